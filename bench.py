@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark on one MI355X: batch 32, 32k context, 32 q / 8 kv heads, INT2 per-channel cache.
+
+One step = append one token per sequence (rotate/clip/quantize write, with group demotion when a
+128-token group completes) + one decode attention (query rotation, split-K partials over the INT2
+pages and the bf16 band, merge + un-rotation).  Inputs are resident in HBM before timing.
+
+Prints ONE JSON line.  `value` is KV GB/s of the whole step: the decode's algorithmic bytes (codes,
+scales/zeros, bf16 band, query, output) per step / step time.  `roofline` is for the split-K decode
+kernel alone, timed with HIP events on the stream it runs on.  `cpu_baseline` times the CPU oracle's
+read side on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_splitk_batch32_32k_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="batch32_32k")
+    ap.add_argument("--impl", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--split", type=int, default=0, help="quantized tokens per decode work-group (0 = auto)")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--cpu-pairs", type=int, default=3, help="(seq, kv head) pairs in the CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for name in ("kvq_decode.hip", "kvq_internal.h"):
+        with open(os.path.join(ROOT, "decode_attention_15_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def decode_bytes(wl, lens, S0, W):
+    """Algorithmic bytes one decode step reads/writes: INT2 codes + bf16 scale/zero of every group
+    (72 B per token and kv head), bf16 band tokens (512 B), query (bf16) and output (fp32)."""
+    kv = 0
+    for T in lens:
+        ng = max(0, (T - S0 - W) // 128)
+        kv += wl.n_kv_heads * (ng * 128 * 72 + (T - 128 * ng) * 512)
+    qo = len(lens) * wl.n_q_heads * 128 * (2 + 4)
+    return kv, qo
+
+
+def cpu_baseline(wl, args, T, rk, rv):
+    """Oracle read side (dequantize, inverse-rotate, fp64 attention) on a few (seq, kv head) pairs."""
+    import numpy as np
+    import oracle as O
+    import synth
+    from threadpoolctl import threadpool_limits
+    pairs = [(b, (3 * b + 1) % wl.n_kv_heads) for b in range(args.cpu_pairs)]
+    q = synth.queries(wl, 10 ** 6)
+    total_s = 0.0
+    total_bytes = 0
+    with threadpool_limits(limits=1):
+        for b, h in pairs:
+            k = synth.kv_tokens(wl, b, 0, T, "k")[:, h].copy()
+            v = synth.kv_tokens(wl, b, 0, T, "v")[:, h].copy()
+            st = O.int2_state(k, v, T, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v, rk, rv)
+            t0 = time.perf_counter()
+            Kh, Vh = O.int2_keys_values(st, rk, rv)
+            O.attend(O.query_values(q[b, h * wl.gq:(h + 1) * wl.gq]), Kh, Vh)
+            total_s += time.perf_counter() - t0
+            ng = st["n_groups"]
+            total_bytes += ng * 128 * 72 + (T - 128 * ng) * 512 + wl.gq * 128 * 6
+    return {
+        "value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"{len(pairs)} (seq, kv head) pairs of {wl.name} at T={T}: oracle read side "
+                  f"(dequantize, x^.R^T, fp64 softmax attention of {wl.gq} q heads); cache state built untimed; "
+                  f"{total_s:.2f} s",
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this path runs on one GPU; multi-GPU runs are not part of this build",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import decode_attention_15_amd as K
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    assert wl.scheme == "int2_channel", "the headline bench is the INT2 workload"
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    B, n_kv, n_q = wl.batch, wl.n_kv_heads, wl.n_q_heads
+    n_steps = args.warmup + args.steps
+    T_end = wl.seq_len
+    T_start = T_end - n_steps
+    impl = {"auto": K.DECODE_AUTO, "valu": K.DECODE_VALU, "mfma": K.DECODE_MFMA}[args.impl]
+    cfg = K.make_config(n_kv, n_q, K.INT2_CHANNEL, K.ROT_DENSE, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v,
+                        args.split, impl)
+    rk = K.build_oscar_rotation(synth.rotation_gaussian(wl, "k")).astype(np.float32)
+    rv = K.build_oscar_rotation(synth.rotation_gaussian(wl, "v")).astype(np.float32)
+    max_pages = K.pages_for_len(cfg, T_end)
+    pt, n_pool = synth.page_table(wl, max_pages)
+    cache = K.allocate_cache(cfg, B, torch.from_numpy(pt), torch.from_numpy(rk), torch.from_numpy(rv),
+                             n_pages=n_pool, device=dev)
+    log(f"[bench] {wl.name}: B={B} T={T_start}->{T_end} heads {n_q}/{n_kv}; pages {n_pool} x {K.page_bytes(cfg)} B")
+
+    # prefill with the workload's recipe (N(0,1) x channel gains, bf16), generated on the device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed)
+    gk = torch.from_numpy(synth.channel_gain(wl, "k")).to(dev)
+    gv = torch.from_numpy(synth.channel_gain(wl, "v")).to(dev)
+
+    def draw(n, gain):
+        x = torch.randn((n, n_kv, 128), generator=gen, device=dev, dtype=torch.float32)
+        return (x * gain[None]).to(torch.bfloat16)
+
+    t0 = time.perf_counter()
+    per_call = 4
+    for b0 in range(0, B, per_call):
+        nb = min(per_call, B - b0)
+        counts = np.zeros(B, dtype=np.int64)
+        counts[b0:b0 + nb] = T_start
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev)
+        k = draw(nb * T_start, gk)
+        v = draw(nb * T_start, gv)
+        K.kv_rotate_quant_write(cache, k, v, cu, T_start)
+        del k, v
+    torch.cuda.synchronize()
+    log(f"[bench] prefill written in {time.perf_counter() - t0:.1f} s")
+
+    ks = [draw(B, gk) for _ in range(n_steps)]
+    vs = [draw(B, gv) for _ in range(n_steps)]
+    qs = [torch.randn((B, n_q, 128), generator=gen, device=dev).to(torch.bfloat16) for _ in range(n_steps)]
+    cu1 = torch.arange(B + 1, dtype=torch.int32, device=dev)
+    out = torch.empty((B, n_q, 128), dtype=torch.float32, device=dev)
+    ws = K.workspace_for(cfg, B, T_end, dev)
+
+    def step(i):
+        K.kv_rotate_quant_write(cache, ks[i], vs[i], cu1, 1)
+        K.kv_decode_attn(cache, qs[i], out, T_end, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    lens_before = cache.seq_lens.cpu().numpy().astype(np.int64)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.warmup, n_steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] {args.steps} timed steps: {ms_step:.4f} ms/step")
+    assert int(cache.seq_lens.min().item()) == T_end
+
+    # average algorithmic bytes over the timed steps (lengths after each append)
+    kv_sum = qo_sum = 0
+    for s in range(1, args.steps + 1):
+        kv_b, qo_b = decode_bytes(wl, lens_before + s, wl.n_sink, wl.n_recent)
+        kv_sum += kv_b
+        qo_sum += qo_b
+    step_bytes = (kv_sum + qo_sum) / args.steps
+
+    # split-K decode kernel alone, same launch configuration, HIP events on its stream
+    K.kv_decode_attn_stages(cache, qs[-1], out, T_end, ws, K.STAGE_QPREP)
+    torch.cuda.synchronize()
+    k0 = torch.cuda.Event(enable_timing=True)
+    k1 = torch.cuda.Event(enable_timing=True)
+    k0.record()
+    for _ in range(args.kernel_reps):
+        K.kv_decode_attn_stages(cache, qs[-1], out, T_end, ws, K.STAGE_SPLITK)
+    k1.record()
+    torch.cuda.synchronize()
+    kern_ms = k0.elapsed_time(k1) / args.kernel_reps
+    kv_b, _ = decode_bytes(wl, [T_end] * B, wl.n_sink, wl.n_recent)
+    kern_bytes = kv_b + B * n_q * 128 * 4 * 2  # + the fp32 rotated and band queries it reads
+    achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
+    log(f"[bench] split-K kernel {kern_ms * 1e3:.1f} us, {achieved:.0f} GB/s")
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha") == kernel_source_sha() and tr.get("workload") == wl.name:
+            traffic = tr.get("bytes_per_launch")
+
+    result = {
+        "metric": "INT2 decode-attn KV GB/s (% of HBM peak); decode steps/s at BS=32, 32k ctx",
+        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "ctx": T_end, "n_q_heads": n_q, "n_kv_heads": n_kv,
+                   "head_dim": 128, "scheme": "int2 per-channel, 128-token groups, bf16 scale/zero",
+                   "sink_recent": [wl.n_sink, wl.n_recent], "page_tokens": 64, "split_tokens": args.split,
+                   "decode_impl": args.impl, "step": "append 1 token/seq (write) + decode attention"},
+        "steps_per_s": round(1000.0 / ms_step, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "split-K decode (INT2 pages + bf16 band)", "kernel_us": round(kern_ms * 1e3, 2),
+                     "bytes_per_launch": kern_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(wl, args, T_end, rk, rv)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

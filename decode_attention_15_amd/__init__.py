@@ -1,0 +1,272 @@
+"""Python binding of libkvq: decode attention over a rotated, 2/4-bit quantized, paged KV cache.
+
+Argument marshalling only: every step of the write and decode paths runs in the HIP kernels of
+libkvq.so (see include/kvq.h for the operations, layouts and error behaviour).  The functions take
+torch tensors (device memory and streams) and pass their pointers through the C ABI.  There is no
+CPU fallback: importing this package fails if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# enums (include/kvq.h)
+KVQ_OK, KVQ_EINVAL, KVQ_ERANGE, KVQ_ENOSPACE, KVQ_EUNSUPPORTED, KVQ_EDEVICE = 0, -1, -2, -3, -4, -5
+INT2_CHANNEL, INT4_TOKEN = 0, 1
+F32, BF16 = 0, 1
+ROT_DENSE, ROT_HADAMARD = 0, 1
+DECODE_AUTO, DECODE_VALU, DECODE_MFMA = 0, 1, 2
+STAGE_QPREP, STAGE_SPLITK, STAGE_MERGE, STAGE_ALL = 1, 2, 4, 7
+
+
+class Config(ctypes.Structure):
+    _fields_ = [
+        ("head_dim", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("scheme", ctypes.c_int32), ("rotation", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
+        ("group_tokens", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("n_recent", ctypes.c_int32),
+        ("clip_k", ctypes.c_float), ("clip_v", ctypes.c_float), ("split_tokens", ctypes.c_int32),
+        ("decode_impl", ctypes.c_int32),
+    ]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [
+        ("pages", ctypes.c_void_p), ("n_pages", ctypes.c_int64), ("band", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p), ("max_pages_per_seq", ctypes.c_int32), ("seq_lens", ctypes.c_void_p),
+        ("rot_k", ctypes.c_void_p), ("rot_v", ctypes.c_void_p), ("batch", ctypes.c_int32),
+    ]
+
+
+_P = ctypes.c_void_p
+_CFG = ctypes.POINTER(Config)
+_CACHE = ctypes.POINTER(Cache)
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_lib_page_bytes = _sig("kvq_page_bytes", ctypes.c_size_t, _CFG)
+_lib_band_slots = _sig("kvq_band_slots", ctypes.c_int32, _CFG)
+_lib_band_bytes = _sig("kvq_band_bytes", ctypes.c_size_t, _CFG, ctypes.c_int32)
+_lib_pages_for_len = _sig("kvq_pages_for_len", ctypes.c_int32, _CFG, ctypes.c_int32)
+_lib_ws_bytes = _sig("kvq_decode_workspace_bytes", ctypes.c_size_t, _CFG, ctypes.c_int32, ctypes.c_int32)
+_lib_bpe = _sig("kvq_bits_per_element", ctypes.c_double, _CFG, ctypes.c_int64)
+_lib_check = _sig("kvq_check_config", ctypes.c_int, _CFG)
+_lib_build_oscar = _sig("kvq_build_oscar_rotation", ctypes.c_int, _P, _P)
+_lib_compose_oscar = _sig("kvq_compose_oscar_rotation", ctypes.c_int, _P, _P)
+_lib_build_hadamard = _sig("kvq_build_hadamard_rotation", ctypes.c_int, _P, _P)
+_lib_write = _sig("kv_rotate_quant_write", ctypes.c_int, _CFG, _CACHE, _P, _P, ctypes.c_int32, _P, ctypes.c_int32, _P)
+_lib_decode = _sig("kv_decode_attn", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P, ctypes.c_int32, _P,
+                   ctypes.c_size_t, _P)
+_lib_decode_stages = _sig("kv_decode_attn_stages", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P, ctypes.c_int32,
+                          _P, ctypes.c_size_t, ctypes.c_int32, _P)
+_lib_debug_rotate = _sig("kvq_debug_rotate", ctypes.c_int, _CFG, _CACHE, ctypes.c_int32, _P, ctypes.c_int32,
+                         ctypes.c_int32, ctypes.c_float, _P, _P)
+_lib_strerror = _sig("kvq_strerror", ctypes.c_char_p, ctypes.c_int)
+_lib_version = _sig("kvq_version", ctypes.c_char_p)
+
+EXPORTED = [
+    "kvq_page_bytes", "kvq_band_slots", "kvq_band_bytes", "kvq_pages_for_len", "kvq_decode_workspace_bytes",
+    "kvq_bits_per_element", "kvq_check_config", "kvq_build_oscar_rotation", "kvq_compose_oscar_rotation",
+    "kvq_build_hadamard_rotation", "kv_rotate_quant_write", "kv_decode_attn", "kv_decode_attn_stages",
+    "kvq_debug_rotate",
+    "kvq_strerror", "kvq_version",
+]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {strerror(status)} ({status})")
+        self.status = status
+
+
+def strerror(status: int) -> str:
+    return _lib_strerror(status).decode()
+
+
+def version() -> str:
+    return _lib_version().decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != KVQ_OK:
+        raise KvqError(status, what)
+
+
+def make_config(n_kv_heads: int, n_q_heads: int, scheme: int = INT2_CHANNEL, rotation: int = ROT_DENSE,
+                n_sink: int = 4, n_recent: int = 128, clip_k: float = 0.96, clip_v: float = 0.92,
+                split_tokens: int = 0, decode_impl: int = DECODE_AUTO) -> Config:
+    return Config(128, n_kv_heads, n_q_heads, scheme, rotation, 64, 128, n_sink, n_recent, clip_k, clip_v,
+                  split_tokens, decode_impl)
+
+
+def check_config(cfg: Config) -> int:
+    return _lib_check(ctypes.byref(cfg))
+
+
+def page_bytes(cfg: Config) -> int:
+    return _lib_page_bytes(ctypes.byref(cfg))
+
+
+def band_slots(cfg: Config) -> int:
+    return _lib_band_slots(ctypes.byref(cfg))
+
+
+def band_bytes(cfg: Config, batch: int) -> int:
+    return _lib_band_bytes(ctypes.byref(cfg), batch)
+
+
+def pages_for_len(cfg: Config, seq_len: int) -> int:
+    return _lib_pages_for_len(ctypes.byref(cfg), seq_len)
+
+
+def decode_workspace_bytes(cfg: Config, batch: int, max_seq_len: int) -> int:
+    return _lib_ws_bytes(ctypes.byref(cfg), batch, max_seq_len)
+
+
+def bits_per_element(cfg: Config, seq_len: int) -> float:
+    return _lib_bpe(ctypes.byref(cfg), seq_len)
+
+
+def _host_f64(a):
+    import numpy as np
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def build_oscar_rotation(gaussian):
+    """R = QR(gaussian).Q . H . P_br in fp64 (host)."""
+    import numpy as np
+    g, gp = _host_f64(gaussian)
+    out = np.empty((128, 128), dtype=np.float64)
+    _check(_lib_build_oscar(gp, out.ctypes.data_as(ctypes.c_void_p)), "kvq_build_oscar_rotation")
+    return out
+
+
+def compose_oscar_rotation(U):
+    import numpy as np
+    u, up = _host_f64(U)
+    out = np.empty((128, 128), dtype=np.float64)
+    _check(_lib_compose_oscar(up, out.ctypes.data_as(ctypes.c_void_p)), "kvq_compose_oscar_rotation")
+    return out
+
+
+def build_hadamard_rotation(sign):
+    import numpy as np
+    s = np.ascontiguousarray(sign, dtype=np.float32)
+    out = np.empty((128, 128), dtype=np.float64)
+    _check(_lib_build_hadamard(s.ctypes.data_as(ctypes.c_void_p), out.ctypes.data_as(ctypes.c_void_p)),
+           "kvq_build_hadamard_rotation")
+    return out
+
+
+# ----------------------------------------------------------------------------- device-side objects
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return BF16
+    raise ValueError(f"unsupported dtype {t.dtype}: expected float32 or bfloat16")
+
+
+@dataclass
+class DeviceCache:
+    """Device tensors of one layer's cache and the C struct that points at them."""
+    cfg: Config
+    pages: "object"
+    band: "object"
+    page_table: "object"
+    seq_lens: "object"
+    rot_k: "object"
+    rot_v: "object"
+    batch: int
+
+    def c_struct(self) -> Cache:
+        n_pages = self.pages.numel() // max(1, page_bytes(self.cfg))
+        return Cache(_ptr(self.pages), n_pages, _ptr(self.band), _ptr(self.page_table), self.page_table.shape[1],
+                     _ptr(self.seq_lens), _ptr(self.rot_k), _ptr(self.rot_v), self.batch)
+
+
+def allocate_cache(cfg: Config, batch: int, page_table, rot_k, rot_v, n_pages: Optional[int] = None,
+                   device: str = "cuda") -> DeviceCache:
+    """Allocate pages, band and lengths (torch, device) for a page table [batch, max_pages] (int32)."""
+    import torch
+    _check(check_config(cfg), "config")
+    pt = page_table.to(device=device, dtype=torch.int32).contiguous()
+    if n_pages is None:
+        n_pages = int(pt.max().item()) + 1 if pt.numel() else 1
+    pages = torch.empty(n_pages * page_bytes(cfg), dtype=torch.uint8, device=device)
+    nb = band_bytes(cfg, batch)
+    band = torch.zeros(max(nb, 2) // 2, dtype=torch.int16, device=device)
+    seq_lens = torch.zeros(batch, dtype=torch.int32, device=device)
+    return DeviceCache(cfg, pages, band, pt, seq_lens, rot_k.to(device).float().contiguous(),
+                       rot_v.to(device).float().contiguous(), batch)
+
+
+def kv_rotate_quant_write(cache: DeviceCache, k, v, cu_new, max_new: int, stream=None) -> None:
+    """Append tokens: k, v [total_new, n_kv, 128] (fp32 or bf16), cu_new int32 [batch+1] (device)."""
+    assert k.is_contiguous() and v.is_contiguous() and cu_new.is_contiguous()
+    assert k.shape == v.shape and k.shape[1:] == (cache.cfg.n_kv_heads, 128)
+    assert cu_new.numel() == cache.batch + 1
+    cs = cache.c_struct()
+    _check(_lib_write(ctypes.byref(cache.cfg), ctypes.byref(cs), _ptr(k), _ptr(v), _dtype_code(k), _ptr(cu_new),
+                      int(max_new), _stream(stream)), "kv_rotate_quant_write")
+
+
+def kv_decode_attn(cache: DeviceCache, q, out, max_seq_len: int, workspace, stream=None) -> None:
+    """One decode step: q [batch, n_q, 128] (fp32/bf16) -> out fp32 [batch, n_q, 128]."""
+    assert q.is_contiguous() and out.is_contiguous() and workspace.is_contiguous()
+    assert q.shape == (cache.batch, cache.cfg.n_q_heads, 128) and out.shape == q.shape
+    cs = cache.c_struct()
+    _check(_lib_decode(ctypes.byref(cache.cfg), ctypes.byref(cs), _ptr(q), _dtype_code(q), _ptr(out),
+                       int(max_seq_len), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                       _stream(stream)), "kv_decode_attn")
+
+
+def kv_decode_attn_stages(cache: DeviceCache, q, out, max_seq_len: int, workspace, stages: int, stream=None) -> None:
+    """The decode step limited to some of its kernels (bitmask of STAGE_*), for timing one kernel alone."""
+    cs = cache.c_struct()
+    _check(_lib_decode_stages(ctypes.byref(cache.cfg), ctypes.byref(cs), _ptr(q), _dtype_code(q), _ptr(out),
+                              int(max_seq_len), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              int(stages), _stream(stream)), "kv_decode_attn_stages")
+
+
+def kvq_debug_rotate(cache: DeviceCache, which: int, x, rho: float, out, stream=None) -> None:
+    cs = cache.c_struct()
+    _check(_lib_debug_rotate(ctypes.byref(cache.cfg), ctypes.byref(cs), which, _ptr(x), _dtype_code(x),
+                             x.shape[0], float(rho), _ptr(out), _stream(stream)), "kvq_debug_rotate")
+
+
+def workspace_for(cfg: Config, batch: int, max_seq_len: int, device: str = "cuda"):
+    import torch
+    n = decode_workspace_bytes(cfg, batch, max_seq_len)
+    if n == 0:
+        raise KvqError(KVQ_EINVAL, "decode_workspace_bytes")
+    return torch.empty((n + 3) // 4, dtype=torch.float32, device=device)

@@ -1,0 +1,329 @@
+// Host side of the C ABI: validation, sizes, rotation builders and kernel launches.
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+int gq_of(const kvq_config* c) { return c->n_q_heads / c->n_kv_heads; }
+
+int head_bytes_of(const kvq_config* c) { return c->scheme == KVQ_INT2_CHANNEL ? I2_HEAD_BYTES : I4_HEAD_BYTES; }
+
+int check_config(const kvq_config* c) {
+  if (!c) return KVQ_EINVAL;
+  if (c->head_dim != D || c->page_tokens != PAGE || c->group_tokens != GROUP) return KVQ_EUNSUPPORTED;
+  if (c->scheme != KVQ_INT2_CHANNEL && c->scheme != KVQ_INT4_TOKEN) return KVQ_EUNSUPPORTED;
+  if (c->rotation != KVQ_ROT_DENSE && c->rotation != KVQ_ROT_HADAMARD) return KVQ_EUNSUPPORTED;
+  if (c->n_kv_heads < 1 || c->n_q_heads < 1 || c->n_q_heads % c->n_kv_heads != 0) return KVQ_EINVAL;
+  const int gq = gq_of(c);
+  if (gq != 1 && gq != 2 && gq != 4 && gq != 8) return KVQ_EUNSUPPORTED;
+  if (c->n_sink < 0 || c->n_recent < 0) return KVQ_EINVAL;
+  if (c->scheme == KVQ_INT4_TOKEN && (c->n_sink != 0 || c->n_recent != 0)) return KVQ_EINVAL;
+  if (!(c->clip_k > 0.0f && c->clip_k <= 1.0f) || !(c->clip_v > 0.0f && c->clip_v <= 1.0f)) return KVQ_EINVAL;
+  const int unit = c->scheme == KVQ_INT2_CHANNEL ? GROUP : PAGE;
+  if (c->split_tokens < 0 || c->split_tokens % unit != 0) return KVQ_EINVAL;
+  if (c->decode_impl != KVQ_DECODE_AUTO && c->decode_impl != KVQ_DECODE_VALU && c->decode_impl != KVQ_DECODE_MFMA)
+    return KVQ_EINVAL;
+  if (c->decode_impl == KVQ_DECODE_MFMA) return KVQ_EUNSUPPORTED;
+  return KVQ_OK;
+}
+
+int check_cache(const kvq_config* c, const kvq_cache* k) {
+  if (!k || !k->pages || !k->page_table || !k->seq_lens || !k->rot_k || !k->rot_v) return KVQ_EINVAL;
+  if (k->batch < 1 || k->max_pages_per_seq < 0 || k->n_pages < 0) return KVQ_EINVAL;
+  if (c->scheme == KVQ_INT2_CHANNEL && !k->band) return KVQ_EINVAL;
+  return KVQ_OK;
+}
+
+void clip_params(float rho, int* j, float* f) {
+  const double h = 127.0 * (double)rho;
+  const double fl = floor(h);
+  *j = (int)fl;
+  *f = (float)(h - fl);
+}
+
+// decode work split: groups (INT2) or pages (INT4) per chunk
+int chunk_units(const kvq_config* c, int batch, int max_seq_len) {
+  if (c->split_tokens > 0) return c->split_tokens / (c->scheme == KVQ_INT2_CHANNEL ? GROUP : PAGE);
+  int units;  // quantized groups/pages per sequence
+  if (c->scheme == KVQ_INT2_CHANNEL) units = n_groups_of(max_seq_len, c->n_sink, c->n_recent);
+  else units = (max_seq_len + PAGE - 1) / PAGE;
+  const int pairs = batch * c->n_kv_heads;
+  const int target_wgs = 2048;
+  int chunks = (target_wgs + pairs - 1) / pairs;
+  if (chunks < 1) chunks = 1;
+  int per = (units + chunks - 1) / chunks;
+  per = ((per + 3) / 4) * 4;  // the 4 waves of a work-group share a chunk
+  const int cap = c->scheme == KVQ_INT2_CHANNEL ? 16 : 32;
+  if (per > cap) per = cap;
+  if (per < 4) per = 4;
+  return per;
+}
+
+int max_chunks_of(const kvq_config* c, int max_seq_len, int per) {
+  int units;
+  if (c->scheme == KVQ_INT2_CHANNEL) units = n_groups_of(max_seq_len, c->n_sink, c->n_recent);
+  else units = (max_seq_len + PAGE - 1) / PAGE;
+  return (units + per - 1) / per;
+}
+
+Geo make_geo(const kvq_config* c, const kvq_cache* k) {
+  Geo g;
+  memset(&g, 0, sizeof(g));
+  g.batch = k->batch;
+  g.n_kv = c->n_kv_heads;
+  g.n_q = c->n_q_heads;
+  g.gq = gq_of(c);
+  g.scheme = c->scheme;
+  g.rotation = c->rotation;
+  g.S0 = c->n_sink;
+  g.W = c->n_recent;
+  g.slots = kvq_band_slots(c);
+  g.max_pages = k->max_pages_per_seq;
+  g.head_bytes = head_bytes_of(c);
+  g.page_bytes = (long long)g.head_bytes * c->n_kv_heads;
+  return g;
+}
+
+// ---- fp64 rotation builders ----
+void sylvester_hadamard(double* H) {
+  const double s = 1.0 / sqrt((double)D);
+  for (int i = 0; i < D; ++i)
+    for (int j = 0; j < D; ++j) H[i * D + j] = (__builtin_popcount(i & j) & 1) ? -s : s;
+}
+
+int bit_reverse7(int k) {
+  int r = 0;
+  for (int b = 0; b < 7; ++b) r |= ((k >> b) & 1) << (6 - b);
+  return r;
+}
+
+// Householder QR of the row-major n x n matrix A (overwritten by R); Q returned row-major,
+// with column signs fixed so that diag(R) > 0.
+void householder_qr(std::vector<double>& A, std::vector<double>& Q, int n) {
+  Q.assign((size_t)n * n, 0.0);
+  for (int i = 0; i < n; ++i) Q[(size_t)i * n + i] = 1.0;
+  std::vector<double> v(n);
+  for (int k = 0; k < n; ++k) {
+    double norm2 = 0.0;
+    for (int i = k; i < n; ++i) norm2 += A[(size_t)i * n + k] * A[(size_t)i * n + k];
+    const double norm = sqrt(norm2);
+    if (norm == 0.0) continue;
+    const double alpha = A[(size_t)k * n + k] > 0 ? -norm : norm;
+    for (int i = 0; i < n; ++i) v[i] = i < k ? 0.0 : A[(size_t)i * n + k];
+    v[k] -= alpha;
+    double vn2 = 0.0;
+    for (int i = k; i < n; ++i) vn2 += v[i] * v[i];
+    if (vn2 == 0.0) continue;
+    for (int j = k; j < n; ++j) {
+      double s = 0.0;
+      for (int i = k; i < n; ++i) s += v[i] * A[(size_t)i * n + j];
+      const double f = 2.0 * s / vn2;
+      for (int i = k; i < n; ++i) A[(size_t)i * n + j] -= f * v[i];
+    }
+    for (int i = 0; i < n; ++i) {
+      double s = 0.0;
+      for (int l = k; l < n; ++l) s += Q[(size_t)i * n + l] * v[l];
+      const double f = 2.0 * s / vn2;
+      for (int l = k; l < n; ++l) Q[(size_t)i * n + l] -= f * v[l];
+    }
+  }
+  for (int k = 0; k < n; ++k) {
+    if (A[(size_t)k * n + k] < 0) {
+      for (int i = 0; i < n; ++i) Q[(size_t)i * n + k] = -Q[(size_t)i * n + k];
+      for (int j = 0; j < n; ++j) A[(size_t)k * n + j] = -A[(size_t)k * n + j];
+    }
+  }
+}
+
+void compose_u_h_pbr(const double* U, double* R) {
+  std::vector<double> H((size_t)D * D), UH((size_t)D * D, 0.0);
+  sylvester_hadamard(H.data());
+  for (int i = 0; i < D; ++i)
+    for (int k = 0; k < D; ++k) {
+      const double u = U[i * D + k];
+      for (int j = 0; j < D; ++j) UH[(size_t)i * D + j] += u * H[(size_t)k * D + j];
+    }
+  // (X P_br)[:, beta(k)] = X[:, k]
+  for (int i = 0; i < D; ++i)
+    for (int k = 0; k < D; ++k) R[i * D + bit_reverse7(k)] = UH[(size_t)i * D + k];
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_EDEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+int kvq_check_config(const kvq_config* cfg) { return check_config(cfg); }
+
+size_t kvq_page_bytes(const kvq_config* cfg) {
+  if (check_config(cfg) != KVQ_OK) return 0;
+  return (size_t)head_bytes_of(cfg) * (size_t)cfg->n_kv_heads;
+}
+
+int32_t kvq_band_slots(const kvq_config* cfg) {
+  if (check_config(cfg) != KVQ_OK) return 0;
+  return cfg->scheme == KVQ_INT2_CHANNEL ? cfg->n_sink + cfg->n_recent + GROUP : 0;
+}
+
+size_t kvq_band_bytes(const kvq_config* cfg, int32_t batch) {
+  if (check_config(cfg) != KVQ_OK || batch < 0) return 0;
+  return (size_t)batch * cfg->n_kv_heads * (size_t)kvq_band_slots(cfg) * SLOT_BYTES;
+}
+
+int32_t kvq_pages_for_len(const kvq_config* cfg, int32_t seq_len) {
+  if (check_config(cfg) != KVQ_OK || seq_len < 0) return -1;
+  if (cfg->scheme == KVQ_INT2_CHANNEL) return 2 * n_groups_of(seq_len, cfg->n_sink, cfg->n_recent);
+  return (seq_len + PAGE - 1) / PAGE;
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t batch, int32_t max_seq_len) {
+  if (check_config(cfg) != KVQ_OK || batch < 1 || max_seq_len < 0) return 0;
+  const int per = chunk_units(cfg, batch, max_seq_len);
+  const int n_units = 1 + max_chunks_of(cfg, max_seq_len, per);
+  const size_t nq = (size_t)batch * cfg->n_q_heads;
+  return sizeof(float) * (2 * nq * D + nq * (size_t)n_units * PART_STRIDE);
+}
+
+double kvq_bits_per_element(const kvq_config* cfg, int64_t seq_len) {
+  if (check_config(cfg) != KVQ_OK || seq_len <= 0) return 0.0;
+  double bytes;
+  if (cfg->scheme == KVQ_INT2_CHANNEL) {
+    const int64_t ng = n_groups_of((int)seq_len, cfg->n_sink, cfg->n_recent);
+    // per group and K|V: 128x128 codes at 2 bits + 128 bf16 scales + 128 bf16 zeros
+    bytes = (double)ng * 2.0 * (GROUP * D / 4 + 2 * D * 2) + (double)(seq_len - GROUP * ng) * SLOT_BYTES;
+  } else {
+    bytes = (double)seq_len * 2.0 * (D / 2 + 4);
+  }
+  return bytes * 8.0 / ((double)seq_len * 2.0 * D);
+}
+
+int kvq_build_oscar_rotation(const double* gaussian_host, double* R_out_host) {
+  if (!gaussian_host || !R_out_host) return KVQ_EINVAL;
+  std::vector<double> A(gaussian_host, gaussian_host + D * D), Q;
+  householder_qr(A, Q, D);
+  compose_u_h_pbr(Q.data(), R_out_host);
+  return KVQ_OK;
+}
+
+int kvq_compose_oscar_rotation(const double* U_host, double* R_out_host) {
+  if (!U_host || !R_out_host) return KVQ_EINVAL;
+  compose_u_h_pbr(U_host, R_out_host);
+  return KVQ_OK;
+}
+
+int kvq_build_hadamard_rotation(const float* sign_host, double* R_out_host) {
+  if (!sign_host || !R_out_host) return KVQ_EINVAL;
+  std::vector<double> H((size_t)D * D);
+  sylvester_hadamard(H.data());
+  for (int i = 0; i < D; ++i) {
+    if (sign_host[i] != 1.0f && sign_host[i] != -1.0f) return KVQ_EINVAL;
+    for (int j = 0; j < D; ++j) R_out_host[i * D + j] = (double)sign_host[i] * H[(size_t)i * D + j];
+  }
+  return KVQ_OK;
+}
+
+int kv_rotate_quant_write(const kvq_config* cfg, kvq_cache* cache, const void* k, const void* v, int32_t dtype,
+                          const int32_t* cu_new, int32_t max_new_host, hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if ((st = check_cache(cfg, cache)) != KVQ_OK) return st;
+  if (!k || !v || !cu_new || max_new_host < 0 || (dtype != KVQ_F32 && dtype != KVQ_BF16)) return KVQ_EINVAL;
+  WriteArgs a;
+  memset(&a, 0, sizeof(a));
+  a.g = make_geo(cfg, cache);
+  a.pages = static_cast<uint8_t*>(cache->pages);
+  a.band = static_cast<uint16_t*>(cache->band);
+  a.page_table = cache->page_table;
+  a.seq_lens = cache->seq_lens;
+  a.cu_new = cu_new;
+  a.k = k;
+  a.v = v;
+  a.src_bf16 = dtype == KVQ_BF16;
+  a.rot_k = cache->rot_k;
+  a.rot_v = cache->rot_v;
+  clip_params(cfg->clip_k, &a.clip_j_k, &a.clip_f_k);
+  clip_params(cfg->clip_v, &a.clip_j_v, &a.clip_f_v);
+  a.max_new = max_new_host;
+  hipError_t e = cfg->scheme == KVQ_INT2_CHANNEL ? launch_write_int2(a, stream) : launch_write_int4(a, stream);
+  return to_status(e);
+}
+
+int kv_decode_attn(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t dtype, float* out,
+                   int32_t max_seq_len_host, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return kv_decode_attn_stages(cfg, cache, q, dtype, out, max_seq_len_host, workspace, ws_bytes, KVQ_STAGE_ALL,
+                               stream);
+}
+
+int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t dtype, float* out,
+                          int32_t max_seq_len_host, void* workspace, size_t ws_bytes, int32_t stages,
+                          hipStream_t stream) {
+  if (stages < 0 || stages > KVQ_STAGE_ALL) return KVQ_EINVAL;
+  int st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if ((st = check_cache(cfg, cache)) != KVQ_OK) return st;
+  if (!q || !out || !workspace || max_seq_len_host < 0 || (dtype != KVQ_F32 && dtype != KVQ_BF16))
+    return KVQ_EINVAL;
+  if (kvq_pages_for_len(cfg, max_seq_len_host) > cache->max_pages_per_seq) return KVQ_ERANGE;
+  const size_t need = kvq_decode_workspace_bytes(cfg, cache->batch, max_seq_len_host);
+  if (ws_bytes < need) return KVQ_ENOSPACE;
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.g = make_geo(cfg, cache);
+  const int per = chunk_units(cfg, cache->batch, max_seq_len_host);
+  a.g.gpc = per;
+  a.g.n_units = 1 + max_chunks_of(cfg, max_seq_len_host, per);
+  a.pages = static_cast<const uint8_t*>(cache->pages);
+  a.band = static_cast<const uint16_t*>(cache->band);
+  a.page_table = cache->page_table;
+  a.seq_lens = cache->seq_lens;
+  a.q = q;
+  a.q_bf16 = dtype == KVQ_BF16;
+  a.rot_k = cache->rot_k;
+  a.rot_v = cache->rot_v;
+  a.out = out;
+  const size_t nq = (size_t)cache->batch * cfg->n_q_heads;
+  float* ws = static_cast<float*>(workspace);
+  a.qrot = ws;
+  a.qband = ws + nq * D;
+  a.partials = ws + 2 * nq * D;
+  a.impl = cfg->decode_impl;
+  return to_status(launch_decode(a, stages, stream));
+}
+
+int kvq_debug_rotate(const kvq_config* cfg, const kvq_cache* cache, int32_t which, const void* x, int32_t dtype,
+                     int32_t n, float rho, float* out, hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!cache || !x || !out || n < 0 || (which != 0 && which != 1) || (dtype != KVQ_F32 && dtype != KVQ_BF16))
+    return KVQ_EINVAL;
+  if (!(rho > 0.0f && rho <= 1.0f)) return KVQ_EINVAL;
+  const float* rot = which ? cache->rot_v : cache->rot_k;
+  if (!rot) return KVQ_EINVAL;
+  int j;
+  float f;
+  clip_params(rho, &j, &f);
+  return to_status(launch_debug_rotate(rot, cfg->rotation, x, dtype == KVQ_BF16, n, j, f, out, stream));
+}
+
+const char* kvq_strerror(int status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_EINVAL: return "invalid argument";
+    case KVQ_ERANGE: return "length or page index out of range";
+    case KVQ_ENOSPACE: return "workspace too small";
+    case KVQ_EUNSUPPORTED: return "unsupported configuration";
+    case KVQ_EDEVICE: return "HIP device error";
+    default: return "unknown status";
+  }
+}
+
+const char* kvq_version(void) { return "kvq 0.1 gfx950"; }
+
+}  // extern "C"

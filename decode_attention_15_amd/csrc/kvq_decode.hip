@@ -1,0 +1,601 @@
+// Read path: one decode attention step over the rotated, quantized, paged cache.
+//
+// [OSCAR] summary page §3.4.4 step 4 (dequantize in the rotated frame, inverse-rotate) and §3.4.5
+// (three cache segments, split partials merged with softmax rescaling); [SAW] §4.1 and App. A.4
+// eq. (13)-(14) (query rotated once, logits against dequantized rotated keys, output un-rotated);
+// [NOVA] App. B.5 (query folded once per step, two-stage split-KV decode).
+//
+// Logits are kept in log2 units: the query is pre-scaled by log2(e)/sqrt(128) so exp2 gives e^x.
+// For a per-channel INT2 group with key scales s_c and zeros z_c:
+//   logit_t = sum_c q~_c s_c (code_tc - z_c) = sum_c alpha_c code_tc - beta,
+//   alpha_c = q~_c s_c, beta = sum_c alpha_c z_c,
+// and with value scales/zeros the group's output contribution is
+//   o~_c += s_c (sum_t p_t code_tc - z_c sum_t p_t),
+// so per element the kernel only converts a 2-bit code and multiplies.
+#include <hip/hip_runtime.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr float kInvSqrt128 = 0.08838834764831845f;
+constexpr int kThreads = 256;
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// LDS written by a wave and then read back by other lanes of the same wave.
+__device__ inline void wave_lds_sync() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+__device__ inline float exp2_safe_diff(float a, float b) {
+  // 2^(a-b) with 2^(-inf - -inf) taken as 0
+  return (a == -INFINITY) ? 0.0f : exp2f(a - b);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Query preparation: q~ = (q R_K) * log2e/sqrt(128) for quantized tokens (rotated frame), and
+// q * log2e/sqrt(128) for the bf16 band (original frame).
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void qprep_kernel(DecodeArgs a) {
+  __shared__ float qs[D];
+  const int hq = blockIdx.x, b = blockIdx.y, j = threadIdx.x;
+  const long long base = ((long long)b * a.g.n_q + hq) * D;
+  const float qv = a.q_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[base + j])
+                            : static_cast<const float*>(a.q)[base + j];
+  const float scale = LOG2E * kInvSqrt128;
+  a.qband[base + j] = qv * scale;
+  float r;
+  if (a.g.rotation == KVQ_ROT_DENSE) {
+    qs[j] = qv;
+    __syncthreads();
+    float acc = 0.0f;
+    for (int i = 0; i < D; ++i) acc = fmaf(qs[i], a.rot_k[i * D + j], acc);
+    r = acc;
+  } else {
+    qs[j] = qv * a.rot_k[j];
+    __syncthreads();
+    for (int hh = 1; hh < D; hh <<= 1) {
+      const float x = qs[j], y = qs[j ^ hh];
+      __syncthreads();
+      qs[j] = (j & hh) ? (y - x) : (x + y);
+      __syncthreads();
+    }
+    r = qs[j] * kInvSqrt128;
+  }
+  a.qrot[base + j] = r * scale;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Split-K decode, vector ALU.  Work-group (unit, kv head, seq): unit 0 = bf16 band (sink + tail),
+// unit u >= 1 = quantized chunk u-1.  Each of the 4 waves walks its own groups/pages with an
+// online softmax; the waves are merged in LDS and one partial (m, l, o[128]) per q head written.
+// ---------------------------------------------------------------------------------------------
+template <int GQ>
+struct DecodeLds {
+  float qband[GQ][D];
+  float alpha[4][GQ][D];   // per wave: alpha (INT2) / rotated query (INT4)
+  float p[4][GQ][D];       // per wave: softmax numerators of the current group/page
+  float cm[4][GQ];
+  float cl[4][GQ];
+  float co[4][GQ][D];
+};
+
+template <int GQ>
+__device__ void combine_and_store(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int unit, int wave, int lane,
+                                  const float (&m)[GQ], const float (&l)[GQ], const float (&o)[GQ][2], int c0, int c1) {
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh) {
+    L.co[wave][hh][c0] = o[hh][0];
+    L.co[wave][hh][c1] = o[hh][1];
+    if (lane == 0) {
+      L.cm[wave][hh] = m[hh];
+      L.cl[wave][hh] = l[hh];
+    }
+  }
+  __syncthreads();
+  const Geo& g = a.g;
+  for (int e = threadIdx.x; e < GQ * D; e += kThreads) {
+    const int hh = e / D, c = e % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, L.cm[w][hh]);
+    float acc = 0.0f, lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float sc = exp2_safe_diff(L.cm[w][hh], M);
+      acc += sc * L.co[w][hh][c];
+      lsum += sc * L.cl[w][hh];
+    }
+    float* part = a.partials + (((long long)b * g.n_q + h * GQ + hh) * g.n_units + unit) * PART_STRIDE;
+    part[2 + c] = acc;
+    if (c == 0) {
+      part[0] = M;
+      part[1] = lsum;
+    }
+  }
+}
+
+template <int GQ>
+__device__ inline void softmax_update(float (&m)[GQ], float (&l)[GQ], float (&o)[GQ][2], int hh, float mx_tile,
+                                      float& mnew_out) {
+  const float mnew = fmaxf(m[hh], mx_tile);
+  const float sc = exp2_safe_diff(m[hh], mnew);
+  l[hh] *= sc;
+  o[hh][0] *= sc;
+  o[hh][1] *= sc;
+  m[hh] = mnew;
+  mnew_out = mnew;
+}
+
+template <int GQ>
+__device__ void band_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int T) {
+  const Geo& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < GQ * D; e += kThreads)
+    L.qband[e / D][e % D] = a.qband[((long long)b * g.n_q + h * GQ + e / D) * D + e % D];
+  __syncthreads();
+  const int ng = n_groups_of(T, g.S0, g.W);
+  const int n_sink = T < g.S0 ? T : g.S0;
+  const int tail0 = g.S0 + GROUP * ng;
+  const int n_tail = T > tail0 ? T - tail0 : 0;
+  const int nb = n_sink + n_tail;
+  const uint16_t* band = a.band + ((long long)b * g.n_kv + h) * g.slots * 256;
+  float m[GQ], l[GQ], o[GQ][2];
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.0f;
+    o[hh][0] = o[hh][1] = 0.0f;
+  }
+  auto slot_of = [&](int k) {
+    const int pos = k < n_sink ? k : tail0 + (k - n_sink);
+    return band_slot_of(pos, g.S0, g.W);
+  };
+  for (int blk = wave; blk * 64 < nb; blk += 4) {
+    const int k = blk * 64 + lane;
+    const bool valid = k < nb;
+    float lg[GQ];
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) lg[hh] = 0.0f;
+    if (valid) {
+      const uint4* kr = reinterpret_cast<const uint4*>(band + (long long)slot_of(k) * 256);
+#pragma unroll 1
+      for (int v8 = 0; v8 < 16; ++v8) {
+        const uint4 w = kr[v8];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int p2 = 0; p2 < 4; ++p2) {
+          const float k0 = __uint_as_float(ws[p2] << 16), k1 = __uint_as_float(ws[p2] & 0xffff0000u);
+          const int c = v8 * 8 + p2 * 2;
+#pragma unroll
+          for (int hh = 0; hh < GQ; ++hh) lg[hh] += L.qband[hh][c] * k0 + L.qband[hh][c + 1] * k1;
+        }
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      const float x = valid ? lg[hh] : -INFINITY;
+      float mnew;
+      softmax_update<GQ>(m, l, o, hh, wave_max(x), mnew);
+      const float p = valid ? exp2f(x - mnew) : 0.0f;
+      L.p[wave][hh][lane] = p;
+      l[hh] += wave_sum(p);
+    }
+    wave_lds_sync();
+    const int nk = (nb - blk * 64) < 64 ? (nb - blk * 64) : 64;
+    for (int kk = 0; kk < nk; ++kk) {
+      const uint32_t vv = *reinterpret_cast<const uint32_t*>(band + (long long)slot_of(blk * 64 + kk) * 256 + 128 +
+                                                            2 * lane);
+      const float v0 = __uint_as_float(vv << 16), v1 = __uint_as_float(vv & 0xffff0000u);
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+        const float p = L.p[wave][hh][kk];
+        o[hh][0] += p * v0;
+        o[hh][1] += p * v1;
+      }
+    }
+    wave_lds_sync();
+  }
+  combine_and_store<GQ>(L, a, b, h, 0, wave, lane, m, l, o, 2 * lane, 2 * lane + 1);
+}
+
+template <int GQ>
+__device__ void int2_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
+  const Geo& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ng = n_groups_of(T, g.S0, g.W);
+  const int g_begin = chunk * g.gpc;
+  int g_end = (g_begin + g.gpc) < ng ? (g_begin + g.gpc) : ng;
+  if (g_end > g.max_pages / 2) g_end = g.max_pages / 2;  // never index past the page-table row
+  float qr[GQ][2];
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh) {
+    const float* q = a.qrot + ((long long)b * g.n_q + h * GQ + hh) * D;
+    qr[hh][0] = q[lane];
+    qr[hh][1] = q[lane + 64];
+  }
+  float m[GQ], l[GQ], o[GQ][2];
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.0f;
+    o[hh][0] = o[hh][1] = 0.0f;
+  }
+  const int32_t* pt = a.page_table + (long long)b * g.max_pages;
+  const long long hoff = (long long)h * I2_HEAD_BYTES;
+  for (int gi = g_begin + wave; gi < g_end; gi += 4) {
+    const uint8_t* pg[2] = {a.pages + (long long)pt[2 * gi] * g.page_bytes + hoff,
+                            a.pages + (long long)pt[2 * gi + 1] * g.page_bytes + hoff};
+    const uint16_t* km = reinterpret_cast<const uint16_t*>(pg[0] + I2_META_OFF);
+    const uint16_t* vm = reinterpret_cast<const uint16_t*>(pg[1] + I2_META_OFF);
+    const float sk0 = bf16_to_f32(km[lane]), sk1 = bf16_to_f32(km[lane + 64]);
+    const float zk0 = bf16_to_f32(km[D + lane]), zk1 = bf16_to_f32(km[D + lane + 64]);
+    float beta[GQ];
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      const float a0 = qr[hh][0] * sk0, a1 = qr[hh][1] * sk1;
+      L.alpha[wave][hh][lane] = a0;
+      L.alpha[wave][hh][lane + 64] = a1;
+      beta[hh] = wave_sum(a0 * zk0 + a1 * zk1);
+    }
+    wave_lds_sync();
+    // logits of tokens lane (page 0) and 64 + lane (page 1)
+    float lg[2][GQ];
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const uint4* kp = reinterpret_cast<const uint4*>(pg[pp] + I2_K_OFF + lane * 32);
+      float acc[GQ];
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) acc[hh] = 0.0f;
+#pragma unroll 1
+      for (int half = 0; half < 2; ++half) {
+        const uint4 kk = kp[half];
+        const uint32_t w[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+#pragma unroll 1
+          for (int by = 0; by < 4; ++by) {
+            const uint32_t x = w[wd] >> (8 * by);
+            const float f0 = (float)(x & 3u), f1 = (float)((x >> 2) & 3u), f2 = (float)((x >> 4) & 3u),
+                        f3 = (float)((x >> 6) & 3u);
+            const int c = half * 64 + wd * 16 + by * 4;
+#pragma unroll
+            for (int hh = 0; hh < GQ; ++hh) {
+              const float4 al = *reinterpret_cast<const float4*>(&L.alpha[wave][hh][c]);
+              acc[hh] += al.x * f0 + al.y * f1 + al.z * f2 + al.w * f3;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) lg[pp][hh] = acc[hh] - beta[hh];
+    }
+    float P[GQ];
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      float mnew;
+      softmax_update<GQ>(m, l, o, hh, wave_max(fmaxf(lg[0][hh], lg[1][hh])), mnew);
+      const float p0 = exp2f(lg[0][hh] - mnew), p1 = exp2f(lg[1][hh] - mnew);
+      L.p[wave][hh][lane] = p0;
+      L.p[wave][hh][64 + lane] = p1;
+      P[hh] = wave_sum(p0 + p1);
+      l[hh] += P[hh];
+    }
+    wave_lds_sync();
+    // V: channels lane and lane + 64
+    float u[GQ][2];
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) u[hh][0] = u[hh][1] = 0.0f;
+#pragma unroll 1
+    for (int pp = 0; pp < 2; ++pp) {
+      const uint4 r0 = *reinterpret_cast<const uint4*>(pg[pp] + I2_V_OFF + lane * 16);
+      const uint4 r1 = *reinterpret_cast<const uint4*>(pg[pp] + I2_V_OFF + (lane + 64) * 16);
+      const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w}, w1[4] = {r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+#pragma unroll 1
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t x0 = w0[gg] >> (8 * j), x1 = w1[gg] >> (8 * j);
+          const int i0 = pp * 64 + 16 * j + 4 * gg;
+#pragma unroll
+          for (int hh = 0; hh < GQ; ++hh) {
+            const float4 p4 = *reinterpret_cast<const float4*>(&L.p[wave][hh][i0]);
+            u[hh][0] += p4.x * (float)(x0 & 3u) + p4.y * (float)((x0 >> 2) & 3u) + p4.z * (float)((x0 >> 4) & 3u) +
+                        p4.w * (float)((x0 >> 6) & 3u);
+            u[hh][1] += p4.x * (float)(x1 & 3u) + p4.y * (float)((x1 >> 2) & 3u) + p4.z * (float)((x1 >> 4) & 3u) +
+                        p4.w * (float)((x1 >> 6) & 3u);
+          }
+        }
+      }
+    }
+    const float sv0 = bf16_to_f32(vm[lane]), sv1 = bf16_to_f32(vm[lane + 64]);
+    const float zv0 = bf16_to_f32(vm[D + lane]), zv1 = bf16_to_f32(vm[D + lane + 64]);
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      o[hh][0] += sv0 * (u[hh][0] - zv0 * P[hh]);
+      o[hh][1] += sv1 * (u[hh][1] - zv1 * P[hh]);
+    }
+    wave_lds_sync();
+  }
+  combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, lane, lane + 64);
+}
+
+template <int GQ>
+__device__ void int4_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
+  const Geo& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_pages = (T + PAGE - 1) / PAGE;
+  const int p_begin = chunk * g.gpc;
+  int p_end = (p_begin + g.gpc) < n_pages ? (p_begin + g.gpc) : n_pages;
+  if (p_end > g.max_pages) p_end = g.max_pages;
+  // rotated query of the GQ heads in every wave's alpha slot, and its channel sum
+  float qsum[GQ];
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh) {
+    const float* q = a.qrot + ((long long)b * g.n_q + h * GQ + hh) * D;
+    const float q0 = q[lane], q1 = q[lane + 64];
+    L.alpha[wave][hh][lane] = q0;
+    L.alpha[wave][hh][lane + 64] = q1;
+    qsum[hh] = wave_sum(q0 + q1);
+  }
+  wave_lds_sync();
+  float m[GQ], l[GQ], o[GQ][2];
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.0f;
+    o[hh][0] = o[hh][1] = 0.0f;
+  }
+  const int32_t* pt = a.page_table + (long long)b * g.max_pages;
+  const long long hoff = (long long)h * I4_HEAD_BYTES;
+  for (int pi = p_begin + wave; pi < p_end; pi += 4) {
+    const uint8_t* pg = a.pages + (long long)pt[pi] * g.page_bytes + hoff;
+    const int t = pi * PAGE + lane;
+    const bool valid = t < T;
+    const uint16_t* kmeta = reinterpret_cast<const uint16_t*>(pg + I4_KMETA_OFF + 4 * lane);
+    const uint16_t* vmeta = reinterpret_cast<const uint16_t*>(pg + I4_VMETA_OFF + 4 * lane);
+    const float sk = bf16_to_f32(kmeta[0]), zk = bf16_to_f32(kmeta[1]);
+    const float sv = bf16_to_f32(vmeta[0]), zv = bf16_to_f32(vmeta[1]);
+    float acc[GQ];
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) acc[hh] = 0.0f;
+    const uint4* kp = reinterpret_cast<const uint4*>(pg + I4_K_OFF + lane * 64);
+#pragma unroll 1
+    for (int v16 = 0; v16 < 4; ++v16) {
+      const uint4 w = kp[v16];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        const int c = v16 * 32 + wd * 8;
+        float f[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f[k] = (float)((ws[wd] >> (4 * k)) & 15u);
+#pragma unroll
+        for (int hh = 0; hh < GQ; ++hh) {
+          const float4 a0 = *reinterpret_cast<const float4*>(&L.alpha[wave][hh][c]);
+          const float4 a1 = *reinterpret_cast<const float4*>(&L.alpha[wave][hh][c + 4]);
+          acc[hh] += a0.x * f[0] + a0.y * f[1] + a0.z * f[2] + a0.w * f[3] + a1.x * f[4] + a1.y * f[5] +
+                     a1.z * f[6] + a1.w * f[7];
+        }
+      }
+    }
+    float wz[GQ];
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      const float x = valid ? sk * (acc[hh] - zk * qsum[hh]) : -INFINITY;
+      float mnew;
+      softmax_update<GQ>(m, l, o, hh, wave_max(x), mnew);
+      const float p = valid ? exp2f(x - mnew) : 0.0f;
+      const float w = p * sv;
+      L.p[wave][hh][lane] = w;
+      l[hh] += wave_sum(p);
+      wz[hh] = wave_sum(w * zv);
+    }
+    wave_lds_sync();
+    // V: channels lane and lane + 64, rows of 32 bytes; token 16j + 4g + r in byte 8g + 2j + r/2
+    const uint4* r0p = reinterpret_cast<const uint4*>(pg + I4_V_OFF + lane * 32);
+    const uint4* r1p = reinterpret_cast<const uint4*>(pg + I4_V_OFF + (lane + 64) * 32);
+    const uint4 a0 = r0p[0], a1 = r0p[1], b0 = r1p[0], b1 = r1p[1];
+    const uint32_t w0[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const uint32_t w1[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+#pragma unroll 1
+      for (int j = 0; j < 4; ++j) {
+        // byte pair 8g + 2j lives in word (8g + 2j) / 4 at bit 8 * ((8g + 2j) % 4)
+        const int wi = (8 * gg + 2 * j) >> 2, sh = 8 * ((8 * gg + 2 * j) & 3);
+        const uint32_t x0 = w0[wi] >> sh, x1 = w1[wi] >> sh;
+        const int i0 = 16 * j + 4 * gg;
+#pragma unroll
+        for (int hh = 0; hh < GQ; ++hh) {
+          const float4 p4 = *reinterpret_cast<const float4*>(&L.p[wave][hh][i0]);
+          o[hh][0] += p4.x * (float)(x0 & 15u) + p4.y * (float)((x0 >> 4) & 15u) + p4.z * (float)((x0 >> 8) & 15u) +
+                      p4.w * (float)((x0 >> 12) & 15u);
+          o[hh][1] += p4.x * (float)(x1 & 15u) + p4.y * (float)((x1 >> 4) & 15u) + p4.z * (float)((x1 >> 8) & 15u) +
+                      p4.w * (float)((x1 >> 12) & 15u);
+        }
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      o[hh][0] -= wz[hh];
+      o[hh][1] -= wz[hh];
+    }
+    wave_lds_sync();
+  }
+  combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, lane, lane + 64);
+}
+
+template <int GQ>
+__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
+  __shared__ DecodeLds<GQ> L;
+  const int unit = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const Geo& g = a.g;
+  const int T = a.seq_lens[b];
+  int n_chunks;
+  if (g.scheme == KVQ_INT2_CHANNEL) {
+    const int ng = n_groups_of(T, g.S0, g.W);
+    n_chunks = (ng + g.gpc - 1) / g.gpc;
+  } else {
+    n_chunks = ((T + PAGE - 1) / PAGE + g.gpc - 1) / g.gpc;
+  }
+  if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;  // lengths beyond the launch bound are cut
+  if (unit > n_chunks) return;
+  if (unit == 0) {
+    if (g.scheme == KVQ_INT2_CHANNEL) {
+      band_unit<GQ>(L, a, b, h, T);
+    } else {
+      // no band: an empty partial
+      for (int e = threadIdx.x; e < GQ * PART_STRIDE; e += kThreads) {
+        const int hh = e / PART_STRIDE, k = e % PART_STRIDE;
+        float* part = a.partials + (((long long)b * g.n_q + h * GQ + hh) * g.n_units) * PART_STRIDE;
+        part[k] = (k == 0) ? -INFINITY : 0.0f;
+      }
+    }
+  } else if (g.scheme == KVQ_INT2_CHANNEL) {
+    int2_unit<GQ>(L, a, b, h, T, unit - 1);
+  } else {
+    int4_unit<GQ>(L, a, b, h, T, unit - 1);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Merge: combine the quantized chunks (rotated frame), un-rotate once by R_V^T, combine with the
+// band partial (original frame), normalize.  One work-group per (seq, kv head) covers its GQ heads.
+// ---------------------------------------------------------------------------------------------
+template <int GQ>
+__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
+  extern __shared__ float rt[];        // R_V transposed, [128][129]
+  __shared__ float ob[GQ][D];          // merged rotated-frame numerators
+  __shared__ float un[GQ][2][D];       // un-rotation partial sums (two halves of c)
+  __shared__ float sM[GQ], sL[GQ];
+  const Geo& g = a.g;
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int T = a.seq_lens[b];
+  int n_chunks;
+  if (g.scheme == KVQ_INT2_CHANNEL) {
+    const int ng = n_groups_of(T, g.S0, g.W);
+    n_chunks = (ng + g.gpc - 1) / g.gpc;
+  } else {
+    n_chunks = ((T + PAGE - 1) / PAGE + g.gpc - 1) / g.gpc;
+  }
+  if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;
+  const bool dense = g.rotation == KVQ_ROT_DENSE;
+  if (dense) {
+    for (int e = tid; e < D * D; e += kThreads) {
+      const int j = e / D, c = e % D;
+      rt[c * (D + 1) + j] = a.rot_v[e];  // rt[c][j] = R_V[j][c]
+    }
+  }
+  // merge the quantized chunks per head
+  for (int e = tid; e < GQ * D; e += kThreads) {
+    const int hh = e / D, c = e % D;
+    const float* base = a.partials + ((long long)b * g.n_q + h * GQ + hh) * g.n_units * PART_STRIDE;
+    float M = -INFINITY;
+    for (int u = 1; u <= n_chunks; ++u) M = fmaxf(M, base[u * PART_STRIDE]);
+    float acc = 0.0f, lsum = 0.0f;
+    for (int u = 1; u <= n_chunks; ++u) {
+      const float sc = exp2_safe_diff(base[u * PART_STRIDE], M);
+      acc += sc * base[u * PART_STRIDE + 2 + c];
+      lsum += sc * base[u * PART_STRIDE + 1];
+    }
+    ob[hh][c] = acc;
+    if (c == 0) {
+      sM[hh] = M;
+      sL[hh] = lsum;
+    }
+  }
+  __syncthreads();
+  if (dense) {
+    // o_j = sum_c ob[c] R_V[j][c]; thread (half, j) sums c in [64*half, 64*half+64)
+    const int j = tid & (D - 1), half = tid >> 7;
+    float acc[GQ];
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) acc[hh] = 0.0f;
+    for (int c = half * 64; c < half * 64 + 64; ++c) {
+      const float r = rt[c * (D + 1) + j];
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) acc[hh] = fmaf(ob[hh][c], r, acc[hh]);
+    }
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) un[hh][half][j] = acc[hh];
+    __syncthreads();
+  } else {
+    // o = (ob H) * sign / sqrt(128), FWHT in LDS on each head's 128 values
+    for (int hh2 = 1; hh2 < D; hh2 <<= 1) {
+      float x[GQ / 2 + 1];
+      int n = 0;
+      for (int e = tid; e < GQ * D; e += kThreads) x[n++] = (e % D & hh2) ? (ob[e / D][(e % D) ^ hh2] - ob[e / D][e % D])
+                                                                          : (ob[e / D][e % D] + ob[e / D][(e % D) ^ hh2]);
+      __syncthreads();
+      n = 0;
+      for (int e = tid; e < GQ * D; e += kThreads) ob[e / D][e % D] = x[n++];
+      __syncthreads();
+    }
+    for (int e = tid; e < GQ * D; e += kThreads) {
+      un[e / D][0][e % D] = ob[e / D][e % D] * a.rot_v[e % D] * kInvSqrt128;
+      un[e / D][1][e % D] = 0.0f;
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < GQ * D; e += kThreads) {
+    const int hh = e / D, j = e % D;
+    const long long qi = (long long)b * g.n_q + h * GQ + hh;
+    const float* bp = a.partials + qi * g.n_units * PART_STRIDE;  // unit 0: band
+    const float mb = (T > 0) ? bp[0] : -INFINITY;
+    const float M = sM[hh];
+    const float Mf = fmaxf(M, mb);
+    float res = 0.0f;
+    if (Mf != -INFINITY) {
+      const float si = exp2_safe_diff(M, Mf), sb = exp2_safe_diff(mb, Mf);
+      const float num = (un[hh][0][j] + un[hh][1][j]) * si + (mb == -INFINITY ? 0.0f : bp[2 + j] * sb);
+      const float den = sL[hh] * si + (mb == -INFINITY ? 0.0f : bp[1] * sb);
+      res = num / den;
+    }
+    a.out[qi * D + j] = res;
+  }
+}
+
+template <int GQ>
+hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
+  const Geo& g = a.g;
+  if (stages & KVQ_STAGE_QPREP) hipLaunchKernelGGL(qprep_kernel, dim3(g.n_q, g.batch), dim3(128), 0, s, a);
+  if (stages & KVQ_STAGE_SPLITK)
+    hipLaunchKernelGGL(decode_valu_kernel<GQ>, dim3(g.n_units, g.n_kv, g.batch), dim3(kThreads), 0, s, a);
+  if (stages & KVQ_STAGE_MERGE) {
+    const int merge_lds = D * (D + 1) * (int)sizeof(float);
+    static bool attr = false;
+    if (!attr) {
+      hipError_t e = hipFuncSetAttribute((const void*)merge_kernel<GQ>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         merge_lds);
+      if (e != hipSuccess) return e;
+      attr = true;
+    }
+    hipLaunchKernelGGL(merge_kernel<GQ>, dim3(g.n_kv, g.batch), dim3(kThreads), merge_lds, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int stages, hipStream_t s) {
+  switch (a.g.gq) {
+    case 1: return launch_gq<1>(a, stages, s);
+    case 2: return launch_gq<2>(a, stages, s);
+    case 4: return launch_gq<4>(a, stages, s);
+    case 8: return launch_gq<8>(a, stages, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvq

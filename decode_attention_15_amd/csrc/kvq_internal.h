@@ -1,0 +1,111 @@
+// Internal declarations shared by the libkvq translation units (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int D = 128;            // head dim
+constexpr int PAGE = 64;          // tokens per page
+constexpr int GROUP = 128;        // tokens per INT2 per-channel group
+constexpr int SLOT_BYTES = 512;   // one band token: bf16 K[128] then bf16 V[128]
+
+// INT2 per-channel head block inside a page
+constexpr int I2_K_OFF = 0;
+constexpr int I2_V_OFF = 2048;
+constexpr int I2_META_OFF = 4096;
+constexpr int I2_HEAD_BYTES = 4608;
+// INT4 token-wise head block inside a page
+constexpr int I4_K_OFF = 0;
+constexpr int I4_V_OFF = 4096;
+constexpr int I4_KMETA_OFF = 8192;
+constexpr int I4_VMETA_OFF = 8448;
+constexpr int I4_HEAD_BYTES = 8704;
+
+// 1/sqrt(128) as used by the randomized-Hadamard write: sqrt(2) * 2^-4 rounded once to fp64
+constexpr double INV_SQRT128_F64 = 0x1.6a09e667f3bcdp-4;
+constexpr float LOG2E = 1.4426950408889634f;
+
+// Geometry handed to kernels by value.
+struct Geo {
+  int batch;
+  int n_kv;
+  int n_q;
+  int gq;
+  int scheme;
+  int rotation;
+  int S0;
+  int W;
+  int slots;        // band slots per (seq, kv head)
+  int max_pages;    // page-table row length
+  int head_bytes;
+  long long page_bytes;
+  int gpc;          // groups (INT2) or pages (INT4) per decode chunk
+  int n_units;      // decode partial units per (seq, q head): 1 band unit + chunks
+};
+
+__host__ __device__ inline int n_groups_of(int T, int S0, int W) {
+  int r = T - S0 - W;
+  return r > 0 ? r / GROUP : 0;
+}
+
+__host__ __device__ inline int band_slot_of(int t, int S0, int W) {
+  return t < S0 ? t : S0 + (t - S0) % (W + GROUP);
+}
+
+__device__ inline uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// ---- launchers implemented in kvq_write.hip / kvq_decode.hip ----
+struct WriteArgs {
+  Geo g;
+  uint8_t* pages;
+  uint16_t* band;
+  const int32_t* page_table;
+  int32_t* seq_lens;
+  const int32_t* cu_new;
+  const void* k;
+  const void* v;
+  int src_bf16;
+  const float* rot_k;
+  const float* rot_v;
+  int clip_j_k, clip_j_v;
+  float clip_f_k, clip_f_v;
+  int max_new;
+};
+
+hipError_t launch_write_int2(const WriteArgs& a, hipStream_t s);
+hipError_t launch_write_int4(const WriteArgs& a, hipStream_t s);
+hipError_t launch_debug_rotate(const float* rot, int rotation, const void* x, int src_bf16, int n, int clip_j,
+                               float clip_f, float* out, hipStream_t s);
+
+struct DecodeArgs {
+  Geo g;
+  const uint8_t* pages;
+  const uint16_t* band;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const void* q;
+  int q_bf16;
+  const float* rot_k;
+  const float* rot_v;
+  float* out;
+  float* qrot;      // [batch][n_q][128]
+  float* qband;     // [batch][n_q][128]
+  float* partials;  // [batch][n_q][n_units][PART_STRIDE]
+  int impl;
+};
+
+constexpr int PART_STRIDE = 2 + D;  // m, l, o[128]
+
+hipError_t launch_decode(const DecodeArgs& a, int stages, hipStream_t s);
+
+}  // namespace kvq

@@ -1,0 +1,442 @@
+// Write path: rotate -> clip -> quantize -> pack into pages, plus the bf16 band.
+//
+// [OSCAR] summary page §3.4.4 (steps 1-3) and §3.4.5 (fused prefill write, window demotion);
+// [SAW] §3 eq. (1), §4.1 (fused rotation-quantization write), App. A.1 eq. (3)-(4).
+//
+// Built with -ffp-contract=off: every rounding below is the one the cache format specifies
+// (see include/kvq.h), so a CPU implementation of the same definition gets the same bits.
+#include <hip/hip_runtime.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr unsigned kFull = 0xffffffffu;
+
+__device__ inline float src_as_bf16_value(const void* src, int src_bf16, long long idx) {
+  if (src_bf16) return bf16_to_f32(static_cast<const uint16_t*>(src)[idx]);
+  return bf16_to_f32(f32_to_bf16_rne(static_cast<const float*>(src)[idx]));
+}
+
+__device__ inline uint16_t src_as_bf16_bits(const void* src, int src_bf16, long long idx) {
+  if (src_bf16) return static_cast<const uint16_t*>(src)[idx];
+  return f32_to_bf16_rne(static_cast<const float*>(src)[idx]);
+}
+
+__device__ inline uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)v, m, 64);
+    v = o < v ? o : v;
+  }
+  return v;
+}
+
+__device__ inline float wave_min_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+__device__ inline float wave_max_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+__device__ inline int wave_count(bool p) { return __popcll(__ballot(p)); }
+
+// j-th smallest (0-based) of the 128 non-negative floats held two per lane, as bit patterns
+// (non-negative IEEE floats order like their unsigned bit patterns).  Greedy construction of the
+// largest v with #{x < v} <= j, one bit at a time.
+__device__ inline uint32_t wave_select_u32(uint32_t u0, uint32_t u1, int j) {
+  uint32_t prefix = 0;
+  for (int bit = 30; bit >= 0; --bit) {
+    const uint32_t cand = prefix | (1u << bit);
+    const int cnt = wave_count(u0 < cand) + wave_count(u1 < cand);
+    if (cnt <= j) prefix = cand;
+  }
+  return prefix;
+}
+
+// Per-token clip threshold: linear-interpolation quantile of |x| at (j, f) ([OSCAR] §3.4.4 step 2).
+__device__ inline float clip_tau(float x0, float x1, int j, float f) {
+  const uint32_t u0 = __float_as_uint(x0) & 0x7fffffffu;
+  const uint32_t u1 = __float_as_uint(x1) & 0x7fffffffu;
+  const uint32_t yj = wave_select_u32(u0, u1, j);
+  if (j >= D - 1) return __uint_as_float(yj);
+  uint32_t yj1;
+  if (wave_count(u0 <= yj) + wave_count(u1 <= yj) >= j + 2) {
+    yj1 = yj;
+  } else {
+    const uint32_t m0 = u0 > yj ? u0 : kFull;
+    const uint32_t m1 = u1 > yj ? u1 : kFull;
+    yj1 = wave_min_u32(m0 < m1 ? m0 : m1);
+  }
+  const float y0 = __uint_as_float(yj), y1 = __uint_as_float(yj1);
+  return __fadd_rn(y0, __fmul_rn(f, __fsub_rn(y1, y0)));
+}
+
+// Unnormalized radix-2 Walsh-Hadamard transform of 128 fp64 values held as (e0 = x[lane],
+// e1 = x[lane + 64]); stages h = 1, 2, ..., 64 each map the pair (i, i+h), i & h == 0, to (a+b, a-b).
+__device__ inline void fwht128_wave(double& e0, double& e1, int lane) {
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1) {
+    const double p0 = __shfl_xor(e0, h, 64);
+    const double p1 = __shfl_xor(e1, h, 64);
+    if (lane & h) {
+      e0 = p0 - e0;
+      e1 = p1 - e1;
+    } else {
+      e0 = e0 + p0;
+      e1 = e1 + p1;
+    }
+  }
+  const double a = e0, b = e1;
+  e0 = a + b;
+  e1 = a - b;
+}
+
+// Rotation of one vector whose 128 bf16 values are in LDS (xs) into (y0, y1) = (x~[lane], x~[lane+64]).
+// Dense: fp64 products summed in increasing i, rounded once.  Hadamard: sign flip, FWHT, * 1/sqrt(128).
+__device__ inline void rotate_vec(const float* xs, const float* rot, int rotation, int lane, float& y0,
+                                  float& y1) {
+  if (rotation == KVQ_ROT_DENSE) {
+    double a0 = 0.0, a1 = 0.0;
+    for (int i = 0; i < D; ++i) {
+      const double x = (double)xs[i];
+      a0 = fma(x, (double)rot[i * D + lane], a0);
+      a1 = fma(x, (double)rot[i * D + lane + 64], a1);
+    }
+    y0 = (float)a0;
+    y1 = (float)a1;
+  } else {
+    double e0 = (double)xs[lane] * (double)rot[lane];
+    double e1 = (double)xs[lane + 64] * (double)rot[lane + 64];
+    fwht128_wave(e0, e1, lane);
+    y0 = (float)(e0 * INV_SQRT128_F64);
+    y1 = (float)(e1 * INV_SQRT128_F64);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// INT2 per-channel groups.  One work-group quantizes one (sequence, kv head, K|V, new group):
+// gather 128 bf16 tokens (band or new input) -> rotate -> per-token clip -> per-channel min/max
+// -> bf16 scale/zero -> codes -> K token-major rows / V channel-major rows + metadata.
+// ---------------------------------------------------------------------------------------------
+constexpr int kGroupLds = 2 * GROUP * D * (int)sizeof(float);
+
+__global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
+  extern __shared__ float lds[];
+  float* xs = lds;               // [128 tokens][128] inputs (bf16 values)
+  float* xr = lds + GROUP * D;   // [128 tokens][128] rotated, then clipped
+  __shared__ float red_min[2][D], red_max[2][D];
+  __shared__ float s_sp[D], s_zp[D];
+
+  const Geo& g = a.g;
+  const int lg = blockIdx.x;
+  const int which = blockIdx.y & 1;
+  const int h = blockIdx.y >> 1;
+  const int b = blockIdx.z;
+  const int T0 = a.seq_lens[b];
+  const int c0 = a.cu_new[b];
+  const int n_new = a.cu_new[b + 1] - c0;
+  const int T1 = T0 + n_new;
+  const int grp = n_groups_of(T0, g.S0, g.W) + lg;
+  if (grp >= n_groups_of(T1, g.S0, g.W)) return;
+  if (2 * grp + 1 >= g.max_pages) return;  // beyond the page-table row: nothing is written
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const void* src = which ? a.v : a.k;
+  const float* rot = which ? a.rot_v : a.rot_k;
+  const int t_first = g.S0 + GROUP * grp;
+
+  // 1. gather
+  for (int e = tid; e < GROUP * D; e += 256) {
+    const int tl = e >> 7, c = e & (D - 1);
+    const int t = t_first + tl;
+    float val;
+    if (t < T0) {
+      const long long slot = band_slot_of(t, g.S0, g.W);
+      const long long off = (((long long)b * g.n_kv + h) * g.slots + slot) * 256 + which * 128 + c;
+      val = bf16_to_f32(a.band[off]);
+    } else {
+      const long long row = c0 + (t - T0);
+      val = src_as_bf16_value(src, a.src_bf16, (row * g.n_kv + h) * D + c);
+    }
+    xs[tl * D + c] = val;
+  }
+  __syncthreads();
+
+  // 2. rotation
+  if (g.rotation == KVQ_ROT_DENSE) {
+    const int j = tid & (D - 1);
+    const int tb = (tid >> 7) * 64;
+    for (int t8 = 0; t8 < 64; t8 += 8) {
+      double acc[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = 0.0;
+      for (int i = 0; i < D; ++i) {
+        const double r = (double)rot[i * D + j];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = fma((double)xs[(tb + t8 + k) * D + i], r, acc[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) xr[(tb + t8 + k) * D + j] = (float)acc[k];
+    }
+  } else {
+    for (int tl = wave * 32; tl < wave * 32 + 32; ++tl) {
+      float y0, y1;
+      rotate_vec(xs + tl * D, rot, g.rotation, lane, y0, y1);
+      xr[tl * D + lane] = y0;
+      xr[tl * D + lane + 64] = y1;
+    }
+  }
+  __syncthreads();
+
+  // 3. per-token clip
+  const int cj = which ? a.clip_j_v : a.clip_j_k;
+  const float cf = which ? a.clip_f_v : a.clip_f_k;
+  if (cj < D - 1) {
+    for (int tl = wave * 32; tl < wave * 32 + 32; ++tl) {
+      const float x0 = xr[tl * D + lane], x1 = xr[tl * D + lane + 64];
+      const float tau = clip_tau(x0, x1, cj, cf);
+      xr[tl * D + lane] = fminf(fmaxf(x0, -tau), tau);
+      xr[tl * D + lane + 64] = fminf(fmaxf(x1, -tau), tau);
+    }
+    __syncthreads();
+  }
+
+  // 4. per-channel min/max over the group, bf16 scale and zero
+  {
+    const int c = tid & (D - 1), half = tid >> 7;
+    float mn = INFINITY, mx = -INFINITY;
+    for (int tl = half * 64; tl < half * 64 + 64; ++tl) {
+      const float x = xr[tl * D + c];
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+    }
+    red_min[half][c] = mn;
+    red_max[half][c] = mx;
+  }
+  __syncthreads();
+  if (tid < D) {
+    const float amin = fminf(red_min[0][tid], red_min[1][tid]);
+    const float bmax = fmaxf(red_max[0][tid], red_max[1][tid]);
+    const float s = (bmax > amin) ? __fdiv_rn(__fsub_rn(bmax, amin), 3.0f) : 1.0f;
+    const uint16_t s16 = f32_to_bf16_rne(s);
+    const float sp = bf16_to_f32(s16);
+    const uint16_t z16 = f32_to_bf16_rne(__fdiv_rn(-amin, sp));
+    s_sp[tid] = sp;
+    s_zp[tid] = bf16_to_f32(z16);
+    const long long phys = a.page_table[(long long)b * g.max_pages + 2 * grp + which];
+    uint16_t* meta = reinterpret_cast<uint16_t*>(a.pages + phys * g.page_bytes + (long long)h * I2_HEAD_BYTES +
+                                                 I2_META_OFF);
+    meta[tid] = s16;
+    meta[D + tid] = z16;
+  }
+  __syncthreads();
+
+  // 5. codes and packing
+  auto code2 = [&](float x, int c) -> uint32_t {
+    float t = __fadd_rn(__fdiv_rn(x, s_sp[c]), s_zp[c]);
+    t = fminf(fmaxf(rintf(t), 0.0f), 3.0f);
+    return (uint32_t)t;
+  };
+  if (which == 0) {
+    // K: token-major, token i at 32*i, channel c in byte c/4 bits 2*(c%4)
+    const int tl = tid >> 1, half = tid & 1;
+    uint32_t w4[4];
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int c = half * 64 + wd * 16 + k;
+        w |= code2(xr[tl * D + c], c) << (2 * k);
+      }
+      w4[wd] = w;
+    }
+    const long long phys = a.page_table[(long long)b * g.max_pages + 2 * grp + (tl >> 6)];
+    uint4* dst = reinterpret_cast<uint4*>(a.pages + phys * g.page_bytes + (long long)h * I2_HEAD_BYTES + I2_K_OFF +
+                                          (tl & 63) * 32 + half * 16);
+    *dst = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+  } else {
+    // V: channel-major rows of 16 bytes; token i = 16j + 4g + r in byte 4g + j, bits 2r
+    const int c = tid & (D - 1), ph = tid >> 7;
+    uint32_t w4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll 4
+    for (int i = 0; i < 64; ++i) {
+      const int j = i >> 4, gg = (i >> 2) & 3, r = i & 3;
+      w4[gg] |= code2(xr[(ph * 64 + i) * D + c], c) << (8 * j + 2 * r);
+    }
+    const long long phys = a.page_table[(long long)b * g.max_pages + 2 * grp + ph];
+    uint4* dst = reinterpret_cast<uint4*>(a.pages + phys * g.page_bytes + (long long)h * I2_HEAD_BYTES + I2_V_OFF +
+                                          c * 16);
+    *dst = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+  }
+}
+
+// bf16 band writes: sink tokens and tokens that are still in the tail after the append.
+__global__ __launch_bounds__(256) void band_write_kernel(WriteArgs a) {
+  const Geo& g = a.g;
+  const int r = blockIdx.x, b = blockIdx.y;
+  const int T0 = a.seq_lens[b];
+  const int c0 = a.cu_new[b];
+  const int n_new = a.cu_new[b + 1] - c0;
+  if (r >= n_new) return;
+  const int t = T0 + r;
+  const int ng1 = n_groups_of(T0 + n_new, g.S0, g.W);
+  if (!(t < g.S0 || t >= g.S0 + GROUP * ng1)) return;
+  const long long slot = band_slot_of(t, g.S0, g.W);
+  for (int e = threadIdx.x; e < g.n_kv * 256; e += 256) {
+    const int h = e >> 8, kv = (e >> 7) & 1, c = e & (D - 1);
+    const long long idx = ((long long)(c0 + r) * g.n_kv + h) * D + c;
+    a.band[(((long long)b * g.n_kv + h) * g.slots + slot) * 256 + kv * 128 + c] =
+        src_as_bf16_bits(kv ? a.v : a.k, a.src_bf16, idx);
+  }
+}
+
+__global__ void advance_kernel(int32_t* seq_lens, const int32_t* cu_new, int batch) {
+  for (int b = threadIdx.x; b < batch; b += blockDim.x) seq_lens[b] += cu_new[b + 1] - cu_new[b];
+}
+
+// ---------------------------------------------------------------------------------------------
+// INT4 token-wise ([SAW]).  One work-group owns an aligned quad of 4 tokens of one (sequence,
+// kv head, K|V): each wave rotates and quantizes one new token; the V nibbles of the quad share
+// bytes, so the work-group merges them with the bytes of tokens outside the append.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void int4_quad_kernel(WriteArgs a) {
+  __shared__ float xs[4][D];
+  __shared__ uint8_t codes[4][D];
+  const Geo& g = a.g;
+  const int which = blockIdx.y & 1;
+  const int h = blockIdx.y >> 1;
+  const int b = blockIdx.z;
+  const int T0 = a.seq_lens[b];
+  const int c0 = a.cu_new[b];
+  const int n_new = a.cu_new[b + 1] - c0;
+  const int T1 = T0 + n_new;
+  if (n_new <= 0) return;
+  const int quad = (T0 >> 2) + blockIdx.x;
+  if (quad * 4 >= T1) return;
+  if ((quad * 4) / PAGE >= g.max_pages) return;  // beyond the page-table row: nothing is written
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = quad * 4 + wave;
+  const bool is_new = (t >= T0 && t < T1);
+  const void* src = which ? a.v : a.k;
+  const float* rot = which ? a.rot_v : a.rot_k;
+  const long long phys = a.page_table[(long long)b * g.max_pages + (quad * 4) / PAGE];
+  uint8_t* head = a.pages + phys * g.page_bytes + (long long)h * I4_HEAD_BYTES;
+  if (is_new) {
+    const long long row = c0 + (t - T0);
+    xs[wave][lane] = src_as_bf16_value(src, a.src_bf16, (row * g.n_kv + h) * D + lane);
+    xs[wave][lane + 64] = src_as_bf16_value(src, a.src_bf16, (row * g.n_kv + h) * D + lane + 64);
+  }
+  __syncthreads();
+  if (is_new) {
+    float y0, y1;
+    rotate_vec(xs[wave], rot, g.rotation, lane, y0, y1);
+    const float amin = wave_min_f32(fminf(y0, y1));
+    const float bmax = wave_max_f32(fmaxf(y0, y1));
+    const float s = (bmax > amin) ? __fdiv_rn(__fsub_rn(bmax, amin), 15.0f) : 1.0f;
+    const uint16_t s16 = f32_to_bf16_rne(s);
+    const float sp = bf16_to_f32(s16);
+    const uint16_t z16 = f32_to_bf16_rne(rintf(__fdiv_rn(-amin, sp)));
+    const float zp = bf16_to_f32(z16);
+    auto code4 = [&](float x) -> uint32_t {
+      float q = __fadd_rn(rintf(__fdiv_rn(x, sp)), zp);
+      q = fminf(fmaxf(q, 0.0f), 15.0f);
+      return (uint32_t)q;
+    };
+    codes[wave][lane] = (uint8_t)code4(y0);
+    codes[wave][lane + 64] = (uint8_t)code4(y1);
+    if (lane == 0) {
+      uint16_t* meta = reinterpret_cast<uint16_t*>(head + (which ? I4_VMETA_OFF : I4_KMETA_OFF) + 4 * (t & 63));
+      meta[0] = s16;
+      meta[1] = z16;
+    }
+  }
+  __syncthreads();
+  if (which == 0) {
+    // K rows: token-major, 64 bytes per token; lanes 0..15 of a new token's wave each pack 8 channels
+    if (is_new && lane < 16) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w |= (uint32_t)codes[wave][lane * 8 + k] << (4 * k);
+      *reinterpret_cast<uint32_t*>(head + I4_K_OFF + (t & 63) * 64 + lane * 4) = w;
+    }
+  } else if (tid < D) {
+    // V rows: channel-major, 32 bytes per channel; token i = 16j + 4g + r in byte 8g + 2j + r/2
+    const int c = tid;
+    const int i0 = (quad * 4) & 63;
+    const int j = i0 >> 4, gg = (i0 >> 2) & 3;
+    uint16_t* p = reinterpret_cast<uint16_t*>(head + I4_V_OFF + c * 32 + 8 * gg + 2 * j);
+    uint32_t v = *p;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tr = quad * 4 + r;
+      if (tr >= T0 && tr < T1) v = (v & ~(0xFu << (4 * r))) | ((uint32_t)codes[r][c] << (4 * r));
+    }
+    *p = (uint16_t)v;
+  }
+}
+
+__global__ __launch_bounds__(64) void debug_rotate_kernel(const float* rot, int rotation, const void* x, int src_bf16,
+                                                          int n, int clip_j, float clip_f, float* out) {
+  __shared__ float xs[D];
+  const int v = blockIdx.x, lane = threadIdx.x;
+  if (v >= n) return;
+  xs[lane] = src_as_bf16_value(x, src_bf16, (long long)v * D + lane);
+  xs[lane + 64] = src_as_bf16_value(x, src_bf16, (long long)v * D + lane + 64);
+  __syncthreads();
+  float y0, y1;
+  rotate_vec(xs, rot, rotation, lane, y0, y1);
+  if (clip_j < D - 1) {
+    const float tau = clip_tau(y0, y1, clip_j, clip_f);
+    y0 = fminf(fmaxf(y0, -tau), tau);
+    y1 = fminf(fmaxf(y1, -tau), tau);
+  }
+  out[(long long)v * D + lane] = y0;
+  out[(long long)v * D + lane + 64] = y1;
+}
+
+}  // namespace
+
+hipError_t launch_write_int2(const WriteArgs& a, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)int2_group_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       kGroupLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int max_groups = (a.max_new + GROUP - 1) / GROUP + 1;
+  if (a.max_new > 0) {
+    hipLaunchKernelGGL(int2_group_kernel, dim3(max_groups, a.g.n_kv * 2, a.g.batch), dim3(256), kGroupLds, s, a);
+    hipLaunchKernelGGL(band_write_kernel, dim3(a.max_new, a.g.batch), dim3(256), 0, s, a);
+  }
+  hipLaunchKernelGGL(advance_kernel, dim3(1), dim3(256), 0, s, a.seq_lens, a.cu_new, a.g.batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_int4(const WriteArgs& a, hipStream_t s) {
+  if (a.max_new > 0) {
+    const int quads = (a.max_new + 3) / 4 + 1;
+    hipLaunchKernelGGL(int4_quad_kernel, dim3(quads, a.g.n_kv * 2, a.g.batch), dim3(256), 0, s, a);
+  }
+  hipLaunchKernelGGL(advance_kernel, dim3(1), dim3(256), 0, s, a.seq_lens, a.cu_new, a.g.batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_rotate(const float* rot, int rotation, const void* x, int src_bf16, int n, int clip_j,
+                               float clip_f, float* out, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(debug_rotate_kernel, dim3(n), dim3(64), 0, s, rot, rotation, x, src_bf16, n, clip_j,
+                                clip_f, out);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,201 @@
+/*
+ * kvq.h — C ABI for decode attention over a rotated, 2/4-bit quantized, paged KV cache on MI355X (gfx950).
+ *
+ * The operations follow these pages (cited by title and section):
+ *   [OSCAR] "OSCAR: Offline Spectral Covariance-Aware Rotation for 2-bit KV Cache Quantization"
+ *           (English summary page): §3.4.2 rotation R = U·H·P_br; §3.4.4 per-token clip, asymmetric
+ *           affine INT2, dequantize then inverse-rotate; §3.4.5 fused write kernel, three-segment cache
+ *           [bf16 sink | INT2 history | bf16 recent], FlashDecoding split + merge.
+ *   [SAW]   "SAW-INT4: System-AWare 4-Bit KV-Cache Quantization for Real-World LLM Serving": §3 eq. (1)
+ *           block-diagonal randomized Hadamard; App. A.1 eq. (3)-(4) token-wise INT4; §4.1 and
+ *           App. A.4 eq. (13)-(14) attention with the query rotated once and the output un-rotated.
+ *   [NOVA]  "Spend Bits Where Queries Look: ...", App. B.5: query rotated once per step and a two-stage
+ *           split-KV decode (partials, then combine); "Bit rate": 2 + 32/128 bits per INT2 element.
+ *
+ * Conventions
+ *  - head_dim is 128.  Vectors are rows; a rotation R is applied as x~ = x·R, so the inverse is R^T.
+ *  - Every buffer pointer in kvq_cache and in the calls below is a DEVICE pointer allocated by the
+ *    caller (for example a torch tensor's data_ptr()).  Host pointers are named *_host.  The library
+ *    never allocates or frees device memory and keeps no state between calls.
+ *  - Device work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is asynchronous.
+ *    Argument validation is synchronous and happens before anything is enqueued.
+ *  - Every int-returning call returns KVQ_OK (0) or a negative kvq_status; kvq_strerror() names it.
+ *    No C++ exception crosses the ABI.  A HIP launch error is returned as KVQ_EDEVICE.
+ *  - Calls on the same cache must be ordered (same stream or explicit events); the library does not
+ *    lock.  Page contents are only valid for tokens the write calls have produced.
+ *
+ * Cache layout (all little-endian)
+ *  - Sequence b holds tokens [0, T_b), T_b = seq_lens[b].  With S0 = n_sink, W = n_recent, G = 128:
+ *      INT2 scheme: n_g = max(0, (T - S0 - W) / G) full 128-token groups are quantized; group g
+ *      covers tokens [S0 + 128g, S0 + 128g + 128); tokens [0, min(T, S0)) (sink) and
+ *      [S0 + 128 n_g, T) (tail, W..W+127 tokens once T >= S0+W) are kept as bf16 in the band.
+ *      INT4 scheme: every token is quantized on write (S0 = W = 0, no band).
+ *  - Quantized token u (u = t - S0 for INT2, u = t for INT4) of sequence b lives in logical page
+ *    u / 64 at in-page index i = u % 64; page_table[b * max_pages_per_seq + u / 64] is its physical
+ *    page.  A physical page holds 64 tokens of all n_kv_heads: head h at byte h * head_bytes.
+ *  - INT2 per-channel head block (head_bytes = 4608):
+ *      [0, 2048)     K codes, token-major: token i at 32*i; channel c in byte c/4, bits 2*(c%4).
+ *      [2048, 4096)  V codes, channel-major: channel c at 2048 + 16*c; token i = 16j + 4g + r
+ *                    (j, g, r in 0..3) in byte 4*g + j, bits 2*r.
+ *      [4096, 4608)  group metadata: on the group's even page K scales[128] then K zeros[128], on its
+ *                    odd page V scales[128] then V zeros[128], all bf16.
+ *  - INT4 token-wise head block (head_bytes = 8704):
+ *      [0, 4096)     K codes, token-major: token i at 64*i; channel c in byte c/2, low nibble = even c.
+ *      [4096, 8192)  V codes, channel-major: channel c at 4096 + 32*c; token i = 16j + 4g + r in
+ *                    byte 8*g + 2*j + r/2, low nibble when r is even.
+ *      [8192, 8448)  K per-token (scale, zero) bf16 pairs, token i at 8192 + 4*i.
+ *      [8448, 8704)  V per-token (scale, zero) bf16 pairs.
+ *  - Band (INT2 scheme): per (b, kv head) kvq_band_slots() slots of 512 bytes: bf16 K[128] then
+ *    bf16 V[128], unrotated.  Token t < S0 sits in slot t; a tail token t in slot
+ *    S0 + (t - S0) % (W + 128).  Band base of (b, h) = ((b * n_kv_heads) + h) * slots * 512.
+ *
+ * Numerics of the write path (identical bits on any conforming implementation)
+ *  - Values enter the cache as bf16 (round to nearest even for an fp32 source); the quantizer reads
+ *    those bf16 values, exactly as a token demoted from the bf16 recent window.
+ *  - Dense rotation: x~_j = fp32( fp64 sum over i = 0..127 in increasing i of x_i * R[i][j] ).
+ *    Randomized Hadamard ([SAW]): sign flip, radix-2 butterflies (a+b, a-b) for h = 1..64 in fp64,
+ *    times 1/sqrt(128) (= sqrt(2)*2^-4 in fp64), rounded to fp32.
+ *  - Clip ([OSCAR] §3.4.4): tau = y[j] + f*(y[j+1] - y[j]) in fp32 without fusion, y = sorted |x~|,
+ *    j = floor(127*rho), f = fp32(127*rho - j) (tau = y[127] when j = 127); x = min(max(x~, -tau), tau).
+ *  - INT2 per channel over the group: s = fp32((b-a)/3) (1 if b == a) -> bf16 s'; z = fp32(-a/s') ->
+ *    bf16 z'; code = clamp(rint(fp32(fp32(x/s') + z')), 0, 3), rint ties to even.
+ *  - INT4 per token: s = fp32((b-a)/15) -> bf16 s'; z = rint(fp32(-a/s')) -> bf16 z';
+ *    code = clamp(rint(fp32(x/s')) + z', 0, 15).
+ *  - Dequantized value x^ = s'(code - z').
+ */
+#ifndef KVQ_H_
+#define KVQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_EINVAL = -1,        /* bad configuration value or NULL pointer */
+  KVQ_ERANGE = -2,        /* a length or page index exceeds what the cache/page table holds */
+  KVQ_ENOSPACE = -3,      /* workspace smaller than kvq_decode_workspace_bytes() */
+  KVQ_EUNSUPPORTED = -4,  /* head_dim != 128, unknown scheme/rotation, or a combination not built */
+  KVQ_EDEVICE = -5        /* a HIP call or kernel launch failed */
+} kvq_status;
+
+typedef enum { KVQ_INT2_CHANNEL = 0, KVQ_INT4_TOKEN = 1 } kvq_scheme;
+typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
+typedef enum { KVQ_ROT_DENSE = 0, KVQ_ROT_HADAMARD = 1 } kvq_rotation;
+typedef enum { KVQ_DECODE_AUTO = 0, KVQ_DECODE_VALU = 1, KVQ_DECODE_MFMA = 2 } kvq_decode_impl;
+
+/* Static description of one attention layer's cache. */
+typedef struct {
+  int32_t head_dim;      /* must be 128 */
+  int32_t n_kv_heads;    /* >= 1 */
+  int32_t n_q_heads;     /* multiple of n_kv_heads; q head h reads kv head h / (n_q_heads / n_kv_heads) */
+  int32_t scheme;        /* kvq_scheme */
+  int32_t rotation;      /* kvq_rotation: DENSE (OSCAR R, fp32 128x128) or HADAMARD (SAW, 128 signs) */
+  int32_t page_tokens;   /* must be 64 */
+  int32_t group_tokens;  /* must be 128 (INT2 per-channel group length) */
+  int32_t n_sink;        /* S0 >= 0 (INT2 only; 0 for INT4) */
+  int32_t n_recent;      /* W >= 0 (INT2 only; 0 for INT4) */
+  float clip_k;          /* rho_K in (0, 1]; 1 = no clip (INT2 only) */
+  float clip_v;          /* rho_V in (0, 1] */
+  int32_t split_tokens;  /* quantized tokens per decode work-group: multiple of 128, or 0 = chosen by size */
+  int32_t decode_impl;   /* kvq_decode_impl */
+} kvq_config;
+
+/* Device-resident cache of a batch of sequences.  All pointers are device pointers owned by the caller. */
+typedef struct {
+  void* pages;                /* physical page pool, n_pages * kvq_page_bytes() bytes */
+  int64_t n_pages;
+  void* band;                 /* bf16 band, kvq_band_bytes(cfg, batch) bytes (may be NULL for INT4) */
+  const int32_t* page_table;  /* [batch][max_pages_per_seq] logical -> physical page */
+  int32_t max_pages_per_seq;
+  int32_t* seq_lens;          /* [batch] tokens cached so far; advanced by kv_rotate_quant_write */
+  const float* rot_k;         /* DENSE: R_K fp32 row-major [128][128]; HADAMARD: signs fp32 [128] (+1/-1) */
+  const float* rot_v;         /* same for V */
+  int32_t batch;
+} kvq_cache;
+
+/* ---- sizes (host only, no device access) ---- */
+
+/* Bytes of one physical page (64 tokens x all kv heads), 0 on a bad config. */
+size_t kvq_page_bytes(const kvq_config* cfg);
+/* Band slots per (sequence, kv head): S0 + W + 128 for INT2, 0 for INT4. */
+int32_t kvq_band_slots(const kvq_config* cfg);
+/* Bytes of the band for `batch` sequences. */
+size_t kvq_band_bytes(const kvq_config* cfg, int32_t batch);
+/* Logical pages a sequence of `seq_len` tokens occupies (INT2: 2 per full group, INT4: ceil(seq_len/64)),
+   -1 on a bad config.  Size max_pages_per_seq with the largest length the cache will reach. */
+int32_t kvq_pages_for_len(const kvq_config* cfg, int32_t seq_len);
+/* Workspace bytes kv_decode_attn needs for `batch` sequences of at most `max_seq_len` tokens. */
+size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t batch, int32_t max_seq_len);
+/* Storage bits per cached K/V element for one sequence of `seq_len` tokens ([NOVA] "Bit rate"). */
+double kvq_bits_per_element(const kvq_config* cfg, int64_t seq_len);
+/* Validate a configuration (KVQ_OK or the status a call would return). */
+int kvq_check_config(const kvq_config* cfg);
+
+/* ---- rotation builders (host, fp64) ---- */
+
+/* [OSCAR] §3.4.2: R = U·H·P_br with U the Q factor of a Householder QR of `gaussian_host` (row-major
+   128x128, fp64), signs fixed so that diag of the triangular factor is positive, H the normalized
+   Sylvester Hadamard matrix, and P_br[k][beta(k)] = 1 for the 7-bit bit reversal beta.  U stands in for
+   the calibrated eigenbasis.  Writes R row-major to `R_out_host` (128x128 fp64). */
+int kvq_build_oscar_rotation(const double* gaussian_host, double* R_out_host);
+/* Same construction from a given orthonormal basis U (columns = eigenvectors sorted by decreasing
+   eigenvalue): R = U·H·P_br. */
+int kvq_compose_oscar_rotation(const double* U_host, double* R_out_host);
+/* [SAW] §3: dense form diag(sign)·H of the randomized Hadamard (for reference/inspection). */
+int kvq_build_hadamard_rotation(const float* sign_host, double* R_out_host);
+
+/* ---- the hot path ---- */
+
+/* Append tokens to every sequence of the cache ([OSCAR] §3.4.5 prefill and window-demotion kernels;
+   [SAW] §4.1 fused rotate-quantize write).
+   k, v: device [total_new][n_kv_heads][128], fp32 or bf16 (`dtype`), sequence b's new tokens at rows
+   cu_new[b] .. cu_new[b+1]-1 (cu_new: device int32 [batch+1], non-decreasing, cu_new[0] = 0).
+   max_new_host bounds cu_new[b+1]-cu_new[b] over b (it sizes the launch grids).
+   Token t of sequence b is t = seq_lens[b] + row offset.  INT2: sink/tail tokens go to the band; every
+   128-token group completed by the append is rotated, clipped, quantized and packed (reading band
+   tokens and new tokens as needed).  INT4: every new token is rotated and quantized.  Finally
+   seq_lens[b] += new tokens.  Errors: KVQ_EINVAL (NULL, bad dtype, max_new_host < 0),
+   KVQ_EDEVICE.  Lengths beyond the page table are not checked on the device: the caller sizes
+   max_pages_per_seq with kvq_pages_for_len(). */
+int kv_rotate_quant_write(const kvq_config* cfg, kvq_cache* cache, const void* k, const void* v,
+                          int32_t dtype, const int32_t* cu_new, int32_t max_new_host, hipStream_t stream);
+
+/* One decode attention step ([OSCAR] §3.4.4 step 4 and §3.4.5; [SAW] App. A.4 eq. (13)-(14)).
+   q: device [batch][n_q_heads][128] fp32 or bf16; out: device fp32 [batch][n_q_heads][128].
+   out[b][h] = softmax(q·K^T/sqrt(128))·V over all seq_lens[b] cached tokens, where quantized tokens
+   are read as K^ = X^·R_K^T, V^ = X^·R_V^T: computed as (q·R_K)·X^ for the logits and (p·X^)·R_V^T
+   for the output, with an online softmax over split chunks merged in a second kernel.
+   max_seq_len_host bounds seq_lens (it sizes the grid); workspace: device scratch of ws_bytes >=
+   kvq_decode_workspace_bytes(cfg, batch, max_seq_len_host).  A sequence with seq_len 0 yields zeros.
+   Errors: KVQ_EINVAL, KVQ_ERANGE (max_seq_len_host beyond the page table), KVQ_ENOSPACE, KVQ_EDEVICE. */
+int kv_decode_attn(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t dtype, float* out,
+                   int32_t max_seq_len_host, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* The decode step restricted to some of its three kernels, to time one of them in isolation:
+   `stages` is a bitmask of KVQ_STAGE_QPREP (query rotation), KVQ_STAGE_SPLITK (split-K partials) and
+   KVQ_STAGE_MERGE (merge, un-rotate, normalize); a later stage reads what an earlier call left in the
+   workspace.  kv_decode_attn() equals stages = KVQ_STAGE_ALL.  Same arguments and errors otherwise. */
+enum { KVQ_STAGE_QPREP = 1, KVQ_STAGE_SPLITK = 2, KVQ_STAGE_MERGE = 4, KVQ_STAGE_ALL = 7 };
+int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t dtype, float* out,
+                          int32_t max_seq_len_host, void* workspace, size_t ws_bytes, int32_t stages,
+                          hipStream_t stream);
+
+/* Test hook: the write path's rotation (and clip when rho < 1) of n vectors x [n][128] (fp32 or bf16)
+   to fp32 [n][128], using the cache's K (which = 0) or V (which = 1) rotation.  Not used by the hot path. */
+int kvq_debug_rotate(const kvq_config* cfg, const kvq_cache* cache, int32_t which, const void* x, int32_t dtype,
+                     int32_t n, float rho, float* out, hipStream_t stream);
+
+const char* kvq_strerror(int status);
+/* Library version string. */
+const char* kvq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H_ */

@@ -120,7 +120,7 @@ def outlier_channels(wl: Workload, kv_head: int, which: str) -> np.ndarray:
     return np.sort(r.choice(HEAD_DIM, size=wl.outlier_channels, replace=False))
 
 
-def _channel_gain(wl: Workload, which: str) -> np.ndarray:
+def channel_gain(wl: Workload, which: str) -> np.ndarray:
     """[n_kv, 128] per-channel multiplier: outliers and/or decaying spectrum."""
     g = np.ones((wl.n_kv_heads, HEAD_DIM), dtype=np.float32)
     if wl.spectrum == "decay":
@@ -142,7 +142,7 @@ def kv_tokens(wl: Workload, seq: int, start: int, count: int, which: str) -> np.
     assert which in ("k", "v")
     blk = 1024
     out = np.empty((count, wl.n_kv_heads, HEAD_DIM), dtype=np.float32)
-    gain = _channel_gain(wl, which)
+    gain = channel_gain(wl, which)
     t = start
     while t < start + count:
         b = t // blk
@@ -204,5 +204,5 @@ def step_tokens(wl: Workload, step: int, which: str) -> np.ndarray:
     """One appended token per sequence for decode step `step`: [batch, n_kv, 128]."""
     r = _rng(wl, "step", step, 0 if which == "k" else 1)
     x = r.standard_normal((wl.batch, wl.n_kv_heads, HEAD_DIM), dtype=np.float32)
-    x *= _channel_gain(wl, which)[None]
+    x *= channel_gain(wl, which)[None]
     return to_bf16_bits(x) if wl.src_dtype == "bf16" else x

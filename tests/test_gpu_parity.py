@@ -1,0 +1,273 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Bar: codes, bf16 scales/zeros and band bytes bit-exact; attention outputs within 2e-3 absolute
+(the decode computes in fp32 on the same dequantized values the fp64 oracle uses).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from kvq_cases import (build_cache, oracle_out, read_band, read_int2_group, read_int4_tokens, run_decode,
+                       source_of)
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def K():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import decode_attention_15_amd as K
+    return K
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _host(bc):
+    return bc.cache.pages.cpu().numpy(), bc.cache.band.cpu().numpy().view(np.uint16)
+
+
+def check_int2(bc, b, h, groups=None, pages=None, band=None):
+    if pages is None:
+        pages, band = _host(bc)
+    T = int(bc.lens[b])
+    k, v = source_of(bc.wl, b, T)
+    st = O.int2_state(k[:, h], v[:, h], T, bc.wl.n_sink, bc.wl.n_recent, bc.wl.clip_k, bc.wl.clip_v,
+                      bc.rk, bc.rv, groups=groups)
+    for i, g in enumerate(st["groups"]):
+        got = read_int2_group(bc, pages, b, h, int(g))
+        for key in ("k_codes", "v_codes", "k_s16", "k_z16", "v_s16", "v_z16"):
+            want = st[key][i]
+            if not np.array_equal(got[key], want):
+                bad = np.argwhere(got[key] != want)
+                raise AssertionError(f"b={b} h={h} group={g} {key}: {len(bad)} mismatches, first {bad[:5].tolist()}")
+    bk, bv = read_band(bc, band, b, h, st["band_pos"])
+    assert np.array_equal(bk, st["band_k"]), f"band K b={b} h={h}"
+    assert np.array_equal(bv, st["band_v"]), f"band V b={b} h={h}"
+    return st
+
+
+def check_int4(bc, b, h, pages):
+    T = int(bc.lens[b])
+    k, v = source_of(bc.wl, b, T)
+    st = O.int4_state(k[:, h], v[:, h], T, bc.rk.astype(np.int8), bc.rv.astype(np.int8))
+    got = read_int4_tokens(bc, pages, b, h, T)
+    for key in ("k_codes", "v_codes", "k_s16", "k_z16", "v_s16", "v_z16"):
+        if not np.array_equal(got[key], st[key]):
+            bad = np.argwhere(got[key] != st[key])
+            raise AssertionError(f"b={b} h={h} {key}: {len(bad)} mismatches, first {bad[:5].tolist()}")
+
+
+def check_out(bc, out, q, pairs):
+    worst = 0.0
+    for b, h in pairs:
+        T = int(bc.lens[b])
+        gq = bc.wl.gq
+        got = out[b, h * gq:(h + 1) * gq]
+        if T == 0:
+            assert np.array_equal(got, np.zeros_like(got))
+            continue
+        want = oracle_out(bc, q, b, h, T)
+        err = np.abs(got - want).max()
+        worst = max(worst, err)
+        assert err <= TOL, f"b={b} h={h} T={T}: max |diff| {err:.3e}"
+    return worst
+
+
+# ------------------------------------------------------------------------- stage-wise: rotation
+
+
+@pytest.mark.parametrize("rotation", ["oscar", "saw"])
+@pytest.mark.parametrize("rho", [1.0, 0.96, 0.92])
+def test_debug_rotate_bit_exact(K, rotation, rho):
+    import torch
+    from kvq_cases import config_for, rotations, source_torch
+    wl = synth.WORKLOADS["gqa_b1_32k" if rotation == "oscar" else "saw_int4_b16_16k"]
+    _say(f"debug_rotate {rotation} rho={rho}")
+    rk, rv = rotations(wl)
+    cfg = config_for(K, wl)
+    x = synth.kv_tokens(wl, 0, 0, 300, "k")[:, 0].copy()
+    pt = torch.zeros((1, 1), dtype=torch.int32)
+    cache = K.allocate_cache(cfg, 1, pt, torch.from_numpy(rk), torch.from_numpy(rv), n_pages=1)
+    out = torch.empty((300, 128), dtype=torch.float32, device="cuda")
+    K.kvq_debug_rotate(cache, 0, source_torch(x, "cuda"), rho, out)
+    got = out.cpu().numpy()
+    xv = O.bf16_value(x)
+    want = O.rotate_dense(xv, rk) if rotation == "oscar" else O.rotate_hadamard(xv, rk.astype(np.int8))
+    if rho < 1.0:
+        want = O.clip_tokens(want, rho)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+# ------------------------------------------------------------------------- small, element by element
+
+
+def test_tiny_single_head_full(K):
+    wl = synth.WORKLOADS["tiny_1h_4k"]
+    _say("tiny_1h_4k: prefill 4000 + 96 appends, T=4096")
+    bc = build_cache(K, wl, [4096], append_steps=96)
+    check_int2(bc, 0, 0)
+    q = synth.queries(synth.scaled(wl, batch=1))
+    out = run_decode(K, bc, q)
+    worst = check_out(bc, out, q, [(0, 0)])
+    _say(f"  worst |diff| {worst:.2e}")
+
+
+def test_gqa_ragged_batch(K):
+    wl = synth.WORKLOADS["gqa_b1_32k"]
+    lens = [3000, 131, 700, 0, 260]
+    _say(f"gqa ragged lens={lens}")
+    bc = build_cache(K, wl, lens, append_steps=5)
+    pages, band = _host(bc)
+    for b in range(len(lens)):
+        for h in (0, 3, 7):
+            if lens[b]:
+                check_int2(bc, b, h, pages=pages, band=band)
+    q = synth.queries(synth.scaled(wl, batch=len(lens)))
+    out = run_decode(K, bc, q)
+    check_out(bc, out, q, [(b, h) for b in range(len(lens)) for h in range(8)])
+
+
+def test_prefill_and_appends_give_identical_bytes(K):
+    wl = synth.WORKLOADS["gqa_b1_32k"]
+    lens = [1500, 777]
+    _say("prefill-vs-append invariance")
+    a = build_cache(K, wl, lens)
+    b = build_cache(K, wl, lens, append_steps=300, chunk=200)
+    pa, ba = _host(a)
+    pb, bb = _host(b)
+    assert np.array_equal(a.cache.seq_lens.cpu().numpy(), np.array(lens, np.int32))
+    assert np.array_equal(b.cache.seq_lens.cpu().numpy(), np.array(lens, np.int32))
+    for s in range(2):
+        for h in range(8):
+            ng = O.n_groups(lens[s], 4, 128)
+            for g in range(ng):
+                ga, gb = read_int2_group(a, pa, s, h, g), read_int2_group(b, pb, s, h, g)
+                for key in ga:
+                    assert np.array_equal(ga[key], gb[key]), (s, h, g, key)
+            pos = O.band_positions(lens[s], 4, 128)
+            ka, va = read_band(a, ba, s, h, pos)
+            kb, vb = read_band(b, bb, s, h, pos)
+            assert np.array_equal(ka, kb) and np.array_equal(va, vb)
+
+
+def test_long_context_gq8_small(K):
+    wl = synth.scaled(synth.WORKLOADS["long_b4_131k"], batch=2)
+    lens = [5000, 2222]
+    _say(f"long gq8 small lens={lens}, split 512")
+    bc = build_cache(K, wl, lens, append_steps=3, split_tokens=512)
+    pages, band = _host(bc)
+    for b in range(2):
+        for h in (0, 5):
+            check_int2(bc, b, h, pages=pages, band=band)
+    q = synth.queries(synth.scaled(wl, batch=2))
+    out = run_decode(K, bc, q)
+    check_out(bc, out, q, [(b, h) for b in range(2) for h in range(8)])
+
+
+def test_split_size_does_not_change_the_result(K):
+    wl = synth.WORKLOADS["gqa_b1_32k"]
+    lens = [4000, 1234]
+    _say("split invariance")
+    outs = []
+    q = synth.queries(synth.scaled(wl, batch=2))
+    for split in (128, 512, 2048):
+        bc = build_cache(K, wl, lens, split_tokens=split)
+        outs.append(run_decode(K, bc, q))
+    assert np.abs(outs[0] - outs[1]).max() < 1e-5
+    assert np.abs(outs[0] - outs[2]).max() < 1e-5
+
+
+def test_saw_int4_small(K):
+    wl = synth.WORKLOADS["saw_int4_b16_16k"]
+    lens = [1000, 333, 66]
+    _say(f"saw int4 small lens={lens}")
+    bc = build_cache(K, wl, lens, append_steps=7, chunk=256)
+    pages = bc.cache.pages.cpu().numpy()
+    for b in range(len(lens)):
+        for h in (0, 6):
+            check_int4(bc, b, h, pages)
+    q = synth.queries(synth.scaled(wl, batch=len(lens)))
+    out = run_decode(K, bc, q)
+    check_out(bc, out, q, [(b, h) for b in range(len(lens)) for h in range(8)])
+
+
+def test_decode_is_deterministic(K):
+    wl = synth.WORKLOADS["gqa_b1_32k"]
+    bc = build_cache(K, wl, [2500])
+    q = synth.queries(synth.scaled(wl, batch=1))
+    o1 = run_decode(K, bc, q)
+    o2 = run_decode(K, bc, q)
+    assert np.array_equal(o1, o2)
+
+
+def test_error_codes_from_the_device_calls(K):
+    import torch
+    wl = synth.WORKLOADS["gqa_b1_32k"]
+    bc = build_cache(K, wl, [600])
+    q = torch.zeros((1, 32, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((1, 32, 128), dtype=torch.float32, device="cuda")
+    ws = K.workspace_for(bc.cfg, 1, 600)
+    with pytest.raises(K.KvqError) as e:
+        K.kv_decode_attn(bc.cache, q, out, 600, ws[:10])
+    assert e.value.status == K.KVQ_ENOSPACE
+    with pytest.raises(K.KvqError) as e:
+        K.kv_decode_attn(bc.cache, q, out, 10 ** 6, K.workspace_for(bc.cfg, 1, 10 ** 6))
+    assert e.value.status == K.KVQ_ERANGE
+
+
+# ------------------------------------------------------------------------- full sizes, sampled
+
+
+def test_gqa_b1_32k_full_sampled(K):
+    wl = synth.WORKLOADS["gqa_b1_32k"]
+    _say("gqa_b1_32k full: T=32768")
+    bc = build_cache(K, wl, [32768], append_steps=2)
+    pages, band = _host(bc)
+    for h in (0, 7):
+        check_int2(bc, 0, h, groups=[0, 127, O.n_groups(32768, 4, 128) - 1], pages=pages, band=band)
+    q = synth.queries(wl)
+    out = run_decode(K, bc, q)
+    check_out(bc, out, q, [(0, 2), (0, 7)])
+
+
+def test_batch32_ragged_full_sampled(K):
+    wl = synth.WORKLOADS["batch32_8k_32k"]
+    lens = synth.seq_lens(wl)
+    _say(f"batch32 ragged full: lens {lens.min()}..{lens.max()}")
+    bc = build_cache(K, wl, lens, seqs_per_call=4)
+    pages, band = _host(bc)
+    for b in (0, 31):
+        check_int2(bc, b, 1, groups=[0, O.n_groups(int(lens[b]), 4, 128) - 1], pages=pages, band=band)
+    q = synth.queries(wl)
+    out = run_decode(K, bc, q)
+    check_out(bc, out, q, [(3, 0), (30, 6)])
+
+
+def test_saw_int4_full_sampled(K):
+    wl = synth.WORKLOADS["saw_int4_b16_16k"]
+    _say("saw int4 full: B=16, T=16384, 8192-token prefill chunks")
+    bc = build_cache(K, wl, [16384] * 16, chunk=8192, seqs_per_call=4)
+    pages = bc.cache.pages.cpu().numpy()
+    check_int4(bc, 5, 3, pages)
+    q = synth.queries(wl)
+    out = run_decode(K, bc, q)
+    check_out(bc, out, q, [(0, 0), (15, 7)])
+
+
+def test_long_b4_131k_full_sampled(K):
+    wl = synth.WORKLOADS["long_b4_131k"]
+    _say("long_b4_131k full: B=4, T=131072, split 512")
+    bc = build_cache(K, wl, [131072] * 4, split_tokens=512, seqs_per_call=1)
+    pages, band = _host(bc)
+    check_int2(bc, 2, 4, groups=[0, 500, O.n_groups(131072, 4, 256) - 1], pages=pages, band=band)
+    q = synth.queries(wl)
+    out = run_decode(K, bc, q)
+    check_out(bc, out, q, [(1, 3)])

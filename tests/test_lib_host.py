@@ -1,0 +1,130 @@
+"""Host-side checks of libkvq (no GPU): exported symbols, sizes, bit accounting, validation, builders."""
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import decode_attention_15_amd as K
+import oracle as O
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq?_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert "kv_decode_attn" in names and "kv_rotate_quant_write" in names
+    for n in names:
+        assert hasattr(K._lib, n), n
+    assert sorted(K.EXPORTED) == names
+
+
+def test_version_and_strerror():
+    assert "gfx950" in K.version()
+    for st in (0, -1, -2, -3, -4, -5):
+        assert K.strerror(st) and K.strerror(st) != "unknown status"
+
+
+def test_page_and_band_sizes():
+    cfg = K.make_config(8, 32)
+    assert K.page_bytes(cfg) == 8 * 4608
+    assert K.band_slots(cfg) == 4 + 128 + 128
+    assert K.band_bytes(cfg, 32) == 32 * 8 * 260 * 512
+    cfg4 = K.make_config(8, 32, scheme=K.INT4_TOKEN, rotation=K.ROT_HADAMARD, n_sink=0, n_recent=0,
+                         clip_k=1.0, clip_v=1.0)
+    assert K.page_bytes(cfg4) == 8 * 8704
+    assert K.band_slots(cfg4) == 0
+    # 72 bytes per INT2 token and kv head; 136 for INT4 (codes + bf16 scale/zero)
+    assert K.page_bytes(cfg) / (64 * 8) == 72
+    assert K.page_bytes(cfg4) / (64 * 8) == 136
+
+
+def test_pages_for_len_follows_the_group_layout():
+    cfg = K.make_config(8, 32)
+    for T in (0, 4, 259, 260, 4096, 32768):
+        assert K.pages_for_len(cfg, T) == 2 * O.n_groups(T, 4, 128)
+    cfg4 = K.make_config(8, 32, scheme=K.INT4_TOKEN, rotation=K.ROT_HADAMARD, n_sink=0, n_recent=0)
+    assert K.pages_for_len(cfg4, 16384) == 256 and K.pages_for_len(cfg4, 65) == 2
+
+
+def test_bits_per_element_match_the_pages():
+    g = json.load(open(os.path.join(GOLDEN, "bits_per_element.json")))
+    S0, W = g["band"]
+    cfg = K.make_config(8, 32, n_sink=S0, n_recent=W)
+    # all-quantized region
+    T_big = S0 + W + 128 * 100000
+    region = K.bits_per_element(cfg, T_big)
+    assert abs(region - g["int2_region_bpe"]) < 0.01
+    # at ~128K with the tail exactly W long, the band adds ~0.034 and the total is ~2.28
+    T = S0 + W + 128 * ((g["context"] - S0 - W) // 128)
+    bpe = K.bits_per_element(cfg, T)
+    assert abs(bpe - g["int2_total_bpe_64_256_at_128k"]) < 0.006
+    assert abs((bpe - 2.25) - g["int2_band_extra_bpe_64_256_at_128k"]) < 0.002
+    cfg4 = K.make_config(8, 32, scheme=K.INT4_TOKEN, rotation=K.ROT_HADAMARD, n_sink=0, n_recent=0)
+    assert K.bits_per_element(cfg4, 16384) == pytest.approx(g["int4_bpe"])
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, K.KVQ_EUNSUPPORTED), ("page_tokens", 32, K.KVQ_EUNSUPPORTED),
+    ("scheme", 7, K.KVQ_EUNSUPPORTED), ("rotation", 5, K.KVQ_EUNSUPPORTED),
+    ("n_q_heads", 30, K.KVQ_EINVAL), ("n_kv_heads", 0, K.KVQ_EINVAL), ("clip_k", 0.0, K.KVQ_EINVAL),
+    ("clip_v", 1.5, K.KVQ_EINVAL), ("split_tokens", 100, K.KVQ_EINVAL), ("n_sink", -1, K.KVQ_EINVAL),
+    ("decode_impl", 9, K.KVQ_EINVAL),
+])
+def test_config_validation(field, value, status):
+    cfg = K.make_config(8, 32)
+    assert K.check_config(cfg) == K.KVQ_OK
+    setattr(cfg, field, value)
+    assert K.check_config(cfg) == status
+    assert K.page_bytes(cfg) == 0
+
+
+def test_gqa_ratio_16_is_unsupported_and_int4_rejects_a_band():
+    assert K.check_config(K.make_config(1, 16)) == K.KVQ_EUNSUPPORTED
+    assert K.check_config(K.make_config(8, 32, scheme=K.INT4_TOKEN, n_sink=4)) == K.KVQ_EINVAL
+
+
+def test_calls_reject_null_pointers_before_touching_the_device():
+    import ctypes
+    cfg = K.make_config(8, 32)
+    cache = K.Cache()
+    st = K._lib_write(ctypes.byref(cfg), ctypes.byref(cache), None, None, 0, None, 1, None)
+    assert st == K.KVQ_EINVAL
+    st = K._lib_decode(ctypes.byref(cfg), ctypes.byref(cache), None, 0, None, 10, None, 0, None)
+    assert st == K.KVQ_EINVAL
+
+
+def test_workspace_grows_with_context_and_batch():
+    cfg = K.make_config(8, 32)
+    a = K.decode_workspace_bytes(cfg, 1, 4096)
+    b = K.decode_workspace_bytes(cfg, 1, 32768)
+    c = K.decode_workspace_bytes(cfg, 32, 32768)
+    assert 0 < a < b < c
+    assert K.decode_workspace_bytes(cfg, 0, 10) == 0
+
+
+def test_oscar_builder_matches_the_oracle_construction():
+    wl = synth.WORKLOADS["tiny_1h_4k"]
+    G = synth.rotation_gaussian(wl, "k")
+    R_lib = K.build_oscar_rotation(G)
+    R_or = O.oscar_rotation(G)
+    assert np.abs(R_lib - R_or).max() < 1e-12
+    assert np.abs(R_lib.T @ R_lib - np.eye(128)).max() < 1e-13
+
+
+def test_compose_and_hadamard_builders():
+    U = O.orthonormal_from_gaussian(synth.rotation_gaussian(synth.WORKLOADS["tiny_1h_4k"], "v"))
+    assert np.abs(K.compose_oscar_rotation(U) - U @ O.hadamard() @ O.bit_reversal_matrix()).max() < 1e-13
+    s = synth.sign_vector(synth.WORKLOADS["saw_int4_b16_16k"], "k")
+    assert np.abs(K.build_hadamard_rotation(s.astype(np.float32)) - O.saw_rotation_matrix(s)).max() < 1e-15
+    with pytest.raises(K.KvqError):
+        K.build_hadamard_rotation(np.full(128, 0.5, np.float32))
