@@ -36,8 +36,12 @@ def parse():
     ap.add_argument("--impl", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--split", type=int, default=0, help="quantized tokens per decode work-group (0 = auto)")
     ap.add_argument("--kernel-reps", type=int, default=20)
-    ap.add_argument("--cpu-pairs", type=int, default=3, help="(seq, kv head) pairs in the CPU-baseline sample")
+    ap.add_argument("--cpu-pairs", type=int, default=2, help="distinct (seq, kv head) pairs in the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time of the CPU-baseline sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (torch copy kernel) 5 times: the known-size "
+                         "reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
     return ap.parse_args()
 
 
@@ -65,36 +69,59 @@ def decode_bytes(wl, lens, S0, W):
 
 
 def cpu_baseline(wl, args, T, rk, rv):
-    """Oracle read side (dequantize, inverse-rotate, fp64 attention) on a few (seq, kv head) pairs."""
-    import numpy as np
+    """Oracle read side (dequantize, inverse-rotate, fp64 attention) with one BLAS thread on a few
+    (seq, kv head) pairs of the workload, repeated round-robin until about --cpu-seconds of timed
+    oracle work have run.  The oracle's cache state of each pair is built once, untimed."""
     import oracle as O
     import synth
     from threadpoolctl import threadpool_limits
-    pairs = [(b, (3 * b + 1) % wl.n_kv_heads) for b in range(args.cpu_pairs)]
     q = synth.queries(wl, 10 ** 6)
     total_s = 0.0
     total_bytes = 0
+    runs = 0
     with threadpool_limits(limits=1):
-        for b, h in pairs:
+        states = []
+        for n in range(max(1, args.cpu_pairs)):
+            b, h = n % wl.batch, (3 * n + 1) % wl.n_kv_heads
             k = synth.kv_tokens(wl, b, 0, T, "k")[:, h].copy()
             v = synth.kv_tokens(wl, b, 0, T, "v")[:, h].copy()
-            st = O.int2_state(k, v, T, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v, rk, rv)
+            states.append((b, h, O.int2_state(k, v, T, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v, rk, rv)))
+        while total_s < args.cpu_seconds:
+            b, h, st = states[runs % len(states)]
             t0 = time.perf_counter()
             Kh, Vh = O.int2_keys_values(st, rk, rv)
             O.attend(O.query_values(q[b, h * wl.gq:(h + 1) * wl.gq]), Kh, Vh)
             total_s += time.perf_counter() - t0
             ng = st["n_groups"]
             total_bytes += ng * 128 * 72 + (T - 128 * ng) * 512 + wl.gq * 128 * 6
+            runs += 1
     return {
         "value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": f"{len(pairs)} (seq, kv head) pairs of {wl.name} at T={T}: oracle read side "
-                  f"(dequantize, x^.R^T, fp64 softmax attention of {wl.gq} q heads); cache state built untimed; "
-                  f"{total_s:.2f} s",
+        "sample": f"{runs} decodes of (seq, kv head) pairs of {wl.name} at T={T} ({len(states)} distinct pairs): "
+                  f"oracle read side (dequantize, x^.R^T, fp64 softmax attention of {wl.gq} q heads), one thread; "
+                  f"cache state built untimed; {total_s:.2f} s timed",
     }
+
+
+def calibrate_copy():
+    """A plain device copy of 1 GiB, five times: rocprofv3 reads FETCH_SIZE / WRITE_SIZE of these
+    dispatches to scale the counters (each dispatch reads and writes exactly 2^30 bytes)."""
+    import torch
+    torch.cuda.set_device(0)
+    src = torch.empty(2 ** 30, dtype=torch.uint8, device="cuda").fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": 2 ** 30, "dispatches": 5}), flush=True)
 
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this path runs on one GPU; multi-GPU runs are not part of this build",

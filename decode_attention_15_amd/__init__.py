@@ -18,6 +18,11 @@ LIB_PATH = os.path.join(HERE, "libkvq.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
 
+# torch ships its own HIP runtime (libamdhip64.so.7).  Load it before libkvq.so so that the library's
+# dependency on that soname resolves to the same runtime: a second HIP runtime in the process would
+# not know torch's device memory, streams or device initialisation.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 # enums (include/kvq.h)
@@ -78,19 +83,21 @@ _lib_debug_rotate = _sig("kvq_debug_rotate", ctypes.c_int, _CFG, _CACHE, ctypes.
                          ctypes.c_int32, ctypes.c_float, _P, _P)
 _lib_strerror = _sig("kvq_strerror", ctypes.c_char_p, ctypes.c_int)
 _lib_version = _sig("kvq_version", ctypes.c_char_p)
+_lib_last_error = _sig("kvq_last_error", ctypes.c_char_p)
 
 EXPORTED = [
     "kvq_page_bytes", "kvq_band_slots", "kvq_band_bytes", "kvq_pages_for_len", "kvq_decode_workspace_bytes",
     "kvq_bits_per_element", "kvq_check_config", "kvq_build_oscar_rotation", "kvq_compose_oscar_rotation",
     "kvq_build_hadamard_rotation", "kv_rotate_quant_write", "kv_decode_attn", "kv_decode_attn_stages",
     "kvq_debug_rotate",
-    "kvq_strerror", "kvq_version",
+    "kvq_strerror", "kvq_version", "kvq_last_error",
 ]
 
 
 class KvqError(RuntimeError):
     def __init__(self, status: int, what: str):
-        super().__init__(f"{what}: {strerror(status)} ({status})")
+        detail = f" [{last_error()}]" if status == KVQ_EDEVICE else ""
+        super().__init__(f"{what}: {strerror(status)} ({status}){detail}")
         self.status = status
 
 
@@ -100,6 +107,11 @@ def strerror(status: int) -> str:
 
 def version() -> str:
     return _lib_version().decode()
+
+
+def last_error() -> str:
+    """HIP error text of the last KVQ_EDEVICE failure on this thread ("" if none)."""
+    return _lib_last_error().decode()
 
 
 def _check(status: int, what: str) -> None:

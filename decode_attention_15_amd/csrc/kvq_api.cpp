@@ -1,5 +1,6 @@
 // Host side of the C ABI: validation, sizes, rotation builders and kernel launches.
 #include <math.h>
+#include <stdio.h>
 #include <string.h>
 
 #include <vector>
@@ -154,7 +155,19 @@ void compose_u_h_pbr(const double* U, double* R) {
     for (int k = 0; k < D; ++k) R[i * D + bit_reverse7(k)] = UH[(size_t)i * D + k];
 }
 
-int to_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_EDEVICE; }
+thread_local char g_last_error[256] = "";
+
+// Status of a launch sequence; a failure records the HIP error name for kvq_last_error().
+int to_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return KVQ_OK;
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d): %s", what, hipGetErrorName(e), (int)e,
+           hipGetErrorString(e));
+  return KVQ_EDEVICE;
+}
+
+// Clear an error a previous, unrelated HIP call left behind, so that the status after our launches
+// describes our launches only.  A sticky device error is returned again by the next launch check.
+void clear_stale_error() { (void)hipGetLastError(); }
 
 }  // namespace
 
@@ -251,8 +264,9 @@ int kv_rotate_quant_write(const kvq_config* cfg, kvq_cache* cache, const void* k
   clip_params(cfg->clip_k, &a.clip_j_k, &a.clip_f_k);
   clip_params(cfg->clip_v, &a.clip_j_v, &a.clip_f_v);
   a.max_new = max_new_host;
+  clear_stale_error();
   hipError_t e = cfg->scheme == KVQ_INT2_CHANNEL ? launch_write_int2(a, stream) : launch_write_int4(a, stream);
-  return to_status(e);
+  return to_status(e, "kv_rotate_quant_write");
 }
 
 int kv_decode_attn(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t dtype, float* out,
@@ -294,7 +308,8 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
   a.qband = ws + nq * D;
   a.partials = ws + 2 * nq * D;
   a.impl = cfg->decode_impl;
-  return to_status(launch_decode(a, stages, stream));
+  clear_stale_error();
+  return to_status(launch_decode(a, stages, stream), "kv_decode_attn");
 }
 
 int kvq_debug_rotate(const kvq_config* cfg, const kvq_cache* cache, int32_t which, const void* x, int32_t dtype,
@@ -309,7 +324,9 @@ int kvq_debug_rotate(const kvq_config* cfg, const kvq_cache* cache, int32_t whic
   int j;
   float f;
   clip_params(rho, &j, &f);
-  return to_status(launch_debug_rotate(rot, cfg->rotation, x, dtype == KVQ_BF16, n, j, f, out, stream));
+  clear_stale_error();
+  return to_status(launch_debug_rotate(rot, cfg->rotation, x, dtype == KVQ_BF16, n, j, f, out, stream),
+                   "kvq_debug_rotate");
 }
 
 const char* kvq_strerror(int status) {
@@ -325,5 +342,7 @@ const char* kvq_strerror(int status) {
 }
 
 const char* kvq_version(void) { return "kvq 0.1 gfx950"; }
+
+const char* kvq_last_error(void) { return g_last_error; }
 
 }  // extern "C"

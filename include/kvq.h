@@ -194,6 +194,9 @@ int kvq_debug_rotate(const kvq_config* cfg, const kvq_cache* cache, int32_t whic
 const char* kvq_strerror(int status);
 /* Library version string. */
 const char* kvq_version(void);
+/* Text of the last KVQ_EDEVICE failure on the calling thread (the HIP error name and string, and the
+   call that saw it); "" if none.  The pointer stays valid until the thread's next failing call. */
+const char* kvq_last_error(void);
 
 #ifdef __cplusplus
 }

@@ -128,3 +128,15 @@ def test_compose_and_hadamard_builders():
     assert np.abs(K.build_hadamard_rotation(s.astype(np.float32)) - O.saw_rotation_matrix(s)).max() < 1e-15
     with pytest.raises(K.KvqError):
         K.build_hadamard_rotation(np.full(128, 0.5, np.float32))
+
+
+def test_one_hip_runtime_in_the_process():
+    """The binding loads torch's HIP runtime first, so libkvq binds to it instead of a second copy."""
+    import subprocess
+    import sys
+    code = ("import os, decode_attention_15_amd\n"
+            "m = open(f'/proc/{os.getpid()}/maps').read()\n"
+            "print(len({l.split()[-1] for l in m.splitlines() if 'libamdhip64' in l}))\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip().splitlines()[-1] == "1"
