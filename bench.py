@@ -24,7 +24,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_splitk_batch32_32k_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_int2_batch32_32k_traffic.txt")
 
 
 def parse():
@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batch32_32k")
-    ap.add_argument("--impl", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--impl", default="auto", choices=["auto", "f32", "dot16"])
     ap.add_argument("--split", type=int, default=0, help="quantized tokens per decode work-group (0 = auto)")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--cpu-pairs", type=int, default=2, help="distinct (seq, kv head) pairs in the CPU-baseline sample")
@@ -55,6 +55,23 @@ def kernel_source_sha():
         with open(os.path.join(ROOT, "decode_attention_15_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM bytes per launch of the split-K decode kernel measured by rocprofv3 (FETCH_SIZE + WRITE_SIZE,
+    scaled by a known-size copy), from the committed summary; None unless that measurement was taken on
+    this workload with the kernel source as it is now."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha() or kv.get("workload") != workload:
+        return None
+    return int(float(kv["bytes_per_launch"]))
 
 
 def decode_bytes(wl, lens, S0, W):
@@ -141,7 +158,7 @@ def main():
     n_steps = args.warmup + args.steps
     T_end = wl.seq_len
     T_start = T_end - n_steps
-    impl = {"auto": K.DECODE_AUTO, "valu": K.DECODE_VALU, "mfma": K.DECODE_MFMA}[args.impl]
+    impl = {"auto": K.DECODE_AUTO, "f32": K.DECODE_F32, "dot16": K.DECODE_DOT16}[args.impl]
     cfg = K.make_config(n_kv, n_q, K.INT2_CHANNEL, K.ROT_DENSE, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v,
                         args.split, impl)
     rk = K.build_oscar_rotation(synth.rotation_gaussian(wl, "k")).astype(np.float32)
@@ -228,12 +245,7 @@ def main():
     achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     log(f"[bench] split-K kernel {kern_ms * 1e3:.1f} us, {achieved:.0f} GB/s")
 
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("kernel_source_sha") == kernel_source_sha() and tr.get("workload") == wl.name:
-            traffic = tr.get("bytes_per_launch")
+    traffic = read_traffic(wl.name)
 
     result = {
         "metric": "INT2 decode-attn KV GB/s (% of HBM peak); decode steps/s at BS=32, 32k ctx",

@@ -30,7 +30,7 @@ KVQ_OK, KVQ_EINVAL, KVQ_ERANGE, KVQ_ENOSPACE, KVQ_EUNSUPPORTED, KVQ_EDEVICE = 0,
 INT2_CHANNEL, INT4_TOKEN = 0, 1
 F32, BF16 = 0, 1
 ROT_DENSE, ROT_HADAMARD = 0, 1
-DECODE_AUTO, DECODE_VALU, DECODE_MFMA = 0, 1, 2
+DECODE_AUTO, DECODE_F32, DECODE_MFMA, DECODE_DOT16 = 0, 1, 2, 3
 STAGE_QPREP, STAGE_SPLITK, STAGE_MERGE, STAGE_ALL = 1, 2, 4, 7
 
 

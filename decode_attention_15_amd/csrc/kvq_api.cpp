@@ -28,9 +28,11 @@ int check_config(const kvq_config* c) {
   if (!(c->clip_k > 0.0f && c->clip_k <= 1.0f) || !(c->clip_v > 0.0f && c->clip_v <= 1.0f)) return KVQ_EINVAL;
   const int unit = c->scheme == KVQ_INT2_CHANNEL ? GROUP : PAGE;
   if (c->split_tokens < 0 || c->split_tokens % unit != 0) return KVQ_EINVAL;
-  if (c->decode_impl != KVQ_DECODE_AUTO && c->decode_impl != KVQ_DECODE_VALU && c->decode_impl != KVQ_DECODE_MFMA)
+  if (c->decode_impl != KVQ_DECODE_AUTO && c->decode_impl != KVQ_DECODE_F32 && c->decode_impl != KVQ_DECODE_MFMA &&
+      c->decode_impl != KVQ_DECODE_DOT16)
     return KVQ_EINVAL;
   if (c->decode_impl == KVQ_DECODE_MFMA) return KVQ_EUNSUPPORTED;
+  if (c->decode_impl == KVQ_DECODE_DOT16 && c->scheme != KVQ_INT2_CHANNEL) return KVQ_EUNSUPPORTED;
   return KVQ_OK;
 }
 

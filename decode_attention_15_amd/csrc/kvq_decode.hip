@@ -42,6 +42,39 @@ __device__ inline float exp2_safe_diff(float a, float b) {
   return (a == -INFINITY) ? 0.0f : exp2f(a - b);
 }
 
+// ---- 64-lane reductions with DPP.  Steps: quad xor 1, quad xor 2, half-row mirror, row mirror (every
+// lane then holds its 16-lane row's result), row broadcast 15 into rows 1 and 3, row broadcast 31 into
+// rows 2 and 3; lane 63 ends with the whole wave's result, which is returned to every lane (uniform).
+// The whole wave must be active.
+#define KVQ_DPP(old, v, ctrl, rmask) __builtin_amdgcn_update_dpp((old), (v), (ctrl), (rmask), 0xF, false)
+
+template <typename Op>
+__device__ inline int wave_reduce_bits(int v, int ident, Op op) {
+  v = op(v, KVQ_DPP(ident, v, 0xB1, 0xF));   // quad_perm [1,0,3,2]
+  v = op(v, KVQ_DPP(ident, v, 0x4E, 0xF));   // quad_perm [2,3,0,1]
+  v = op(v, KVQ_DPP(ident, v, 0x141, 0xF));  // row_half_mirror
+  v = op(v, KVQ_DPP(ident, v, 0x140, 0xF));  // row_mirror
+  v = op(v, KVQ_DPP(ident, v, 0x142, 0xA));  // row_bcast15 -> rows 1, 3
+  v = op(v, KVQ_DPP(ident, v, 0x143, 0xC));  // row_bcast31 -> rows 2, 3
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ inline float wave_max_u(float x) {
+  return __int_as_float(wave_reduce_bits(__float_as_int(x), __float_as_int(-INFINITY), [](int a, int b) {
+    return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b)));
+  }));
+}
+
+__device__ inline float wave_sum_u(float x) {
+  return __int_as_float(wave_reduce_bits(__float_as_int(x), 0, [](int a, int b) {
+    return __float_as_int(__int_as_float(a) + __int_as_float(b));
+  }));
+}
+
+__device__ inline uint32_t wave_sum_u32(uint32_t x) {
+  return (uint32_t)wave_reduce_bits((int)x, 0, [](int a, int b) { return (int)((uint32_t)a + (uint32_t)b); });
+}
+
 // ---------------------------------------------------------------------------------------------
 // Query preparation: q~ = (q R_K) * log2e/sqrt(128) for quantized tokens (rotated frame), and
 // q * log2e/sqrt(128) for the bf16 band (original frame).
@@ -330,6 +363,333 @@ __device__ void int2_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
   combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, lane, lane + 64);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Cross-lane reductions used by the 16-bit INT2 decode.
+// seg_reduce<N>: reduce within aligned segments of N lanes (N = 8..64); every lane of a segment gets the
+// segment's result.  Pairings: quad xor 1, quad xor 2, half-row mirror, row mirror (DPP), then xor 16
+// and xor 32 (cross-row exchanges).
+// heads_allreduce<GQ>: GQ values per lane (one per head) reduced over all 64 lanes.  The first log2(GQ)
+// steps exchange half of the remaining values with the lane across bit 5, 4, 3 (each lane keeps the
+// heads whose index bits match its own lane bits), then the one remaining value is reduced within its
+// segment; head h ends in lane h << (6 - log2 GQ) and is read from there (uniform result).
+// ---------------------------------------------------------------------------------------------
+#define KVQ_MOVDPP(x, ctrl) __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), (ctrl), 0xF, 0xF, false))
+
+template <int N, typename Op>
+__device__ inline float seg_reduce(float x, Op op) {
+  x = op(x, KVQ_MOVDPP(x, 0xB1));   // quad_perm [1,0,3,2]
+  x = op(x, KVQ_MOVDPP(x, 0x4E));   // quad_perm [2,3,0,1]
+  x = op(x, KVQ_MOVDPP(x, 0x141));  // row_half_mirror: i <-> 7-i
+  if (N >= 16) x = op(x, KVQ_MOVDPP(x, 0x140));  // row_mirror: i <-> 15-i
+  if (N >= 32) x = op(x, __shfl_xor(x, 16, 64));
+  if (N >= 64) x = op(x, __shfl_xor(x, 32, 64));
+  return x;
+}
+
+template <int GQ>
+struct HeadLog2 {
+  static constexpr int v = GQ == 1 ? 0 : GQ == 2 ? 1 : GQ == 4 ? 2 : 3;
+};
+
+__device__ inline float xor_exchange(float x, int bit) {
+  if (bit == 3) return KVQ_MOVDPP(x, 0x128);  // row_ror:8 == lane xor 8 within a row
+  return __shfl_xor(x, 1 << bit, 64);
+}
+
+template <int GQ, typename Op>
+__device__ inline void heads_allreduce(const float (&v)[GQ], Op op, int lane, float (&out)[GQ]) {
+  constexpr int LG = HeadLog2<GQ>::v;
+  float cur[GQ];
+#pragma unroll
+  for (int i = 0; i < GQ; ++i) cur[i] = v[i];
+#pragma unroll
+  for (int s = 0; s < LG; ++s) {
+    const int bit = 5 - s;
+    const bool up = (lane >> bit) & 1;
+    const int half = GQ >> (s + 1);
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const float send = up ? cur[i] : cur[half + i];
+      const float keep = up ? cur[half + i] : cur[i];
+      cur[i] = op(keep, xor_exchange(send, bit));
+    }
+  }
+  const float x = seg_reduce<(64 >> LG)>(cur[0], op);
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh)
+    out[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), hh << (6 - LG)));
+}
+
+struct OpMax {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct OpAdd {
+  __device__ float operator()(float a, float b) const { return a + b; }
+};
+
+// ---------------------------------------------------------------------------------------------
+// INT2 chunk, 16-bit fixed point on the 4-way byte dot product (v_dot4).  Same algebra as
+// int2_unit, with the two per-group operands quantized to 16 bits:
+//   - alpha_{h,c} = q~_{h,c} s_c is rounded to an integer a_{h,c} = rint(alpha * 32639 / max_c |alpha|)
+//     (per group and head), so that logit_t = A_h (sum_c a_{h,c} code_{t,c} - sum_c a_{h,c} z_c) with
+//     A_h = max|alpha| / 32639; a = 256 hi + lo with signed bytes hi, lo, two signed dot4 per 4 channels.
+//   - p_t = 2^(logit_t - max_group) in (0, 1] is rounded to u_t = rint(65535 p_t), u = 256 hi + lo with
+//     unsigned bytes, two unsigned dot4 per 4 tokens of a channel; the group's output and weight are
+//     2^(max_group - m) / 65535 times s_c (sum_t u_t code_{t,c} - z_c sum_t u_t) and sum_t u_t.
+// Lane roles.  Keys: tokens lane of the group's even and odd page.  Values: channels lane, lane + 64.
+// alpha: lane handles head lane >> (6 - log2 GQ) and 2 GQ consecutive channels of it, so that the per-head
+// maxima and sums are segment reductions.  The integer operands of a group are exchanged through per-wave
+// LDS bytes laid out so that one 16-byte read gives the words that pair with the four byte-lanes of one
+// 32-bit code word:
+//   K code word m of a token holds channels 16m + 4j + k in byte j, bits 2k; (w >> 2k) & 0x03030303 has
+//   channel 16m + 4j + k in byte j, so alpha word (m, k) holds channel 16m + 4j + k in byte j;
+//   V code word g of a channel holds token 16j + 4g + r in byte j, bits 2r, so p word (page, g, k) holds
+//   token 16j + 4g + k of that page in byte j.
+// ---------------------------------------------------------------------------------------------
+template <int GQ>
+__device__ void int2_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
+  constexpr int LG = HeadLog2<GQ>::v;
+  constexpr int LPH = 64 >> LG;   // lanes per head in the alpha step
+  constexpr int NCH = 2 * GQ;     // channels per lane in the alpha step
+  const Geo& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ng = n_groups_of(T, g.S0, g.W);
+  const int g_begin = chunk * g.gpc;
+  int g_end = (g_begin + g.gpc) < ng ? (g_begin + g.gpc) : ng;
+  if (g_end > g.max_pages / 2) g_end = g.max_pages / 2;  // never index past the page-table row
+  const int c0 = lane, c1 = lane + 64;
+  const int ah = lane >> (6 - LG);         // head of this lane in the alpha step
+  const int ac0 = (lane & (LPH - 1)) * NCH;  // its first channel
+  float qa[NCH];
+  {
+    const float* q = a.qrot + ((long long)b * g.n_q + h * GQ + ah) * D + ac0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) qa[i] = q[i];
+  }
+  float m[GQ], l[GQ], o[GQ][2];
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.0f;
+    o[hh][0] = o[hh][1] = 0.0f;
+  }
+  // per-wave operand bytes: [head][limb lo, hi][32 words]
+  uint8_t* abytes = reinterpret_cast<uint8_t*>(&L.alpha[wave][0][0]);
+  uint8_t* pbytes = reinterpret_cast<uint8_t*>(&L.p[wave][0][0]);
+  uint8_t* alo = abytes + ah * 256;
+  uint8_t* ahi = alo + 128;
+  const int pb0 = ((((lane >> 2) & 3) * 4 + (lane & 3)) << 2) + (lane >> 4);  // token lane of the even page
+  const int pb1 = pb0 + 64;                                                    // token lane of the odd page
+  const int32_t* pt = a.page_table + (long long)b * g.max_pages;
+  const long long hoff = (long long)h * I2_HEAD_BYTES;
+  for (int gi = g_begin + wave; gi < g_end; gi += 4) {
+    const uint8_t* pg0 = a.pages + (long long)pt[2 * gi] * g.page_bytes + hoff;
+    const uint8_t* pg1 = a.pages + (long long)pt[2 * gi + 1] * g.page_bytes + hoff;
+    const uint4 k00 = reinterpret_cast<const uint4*>(pg0 + I2_K_OFF + lane * 32)[0];
+    const uint4 k01 = reinterpret_cast<const uint4*>(pg0 + I2_K_OFF + lane * 32)[1];
+    const uint4 k10 = reinterpret_cast<const uint4*>(pg1 + I2_K_OFF + lane * 32)[0];
+    const uint4 k11 = reinterpret_cast<const uint4*>(pg1 + I2_K_OFF + lane * 32)[1];
+    const uint4 v00 = *reinterpret_cast<const uint4*>(pg0 + I2_V_OFF + c0 * 16);
+    const uint4 v01 = *reinterpret_cast<const uint4*>(pg0 + I2_V_OFF + c1 * 16);
+    const uint4 v10 = *reinterpret_cast<const uint4*>(pg1 + I2_V_OFF + c0 * 16);
+    const uint4 v11 = *reinterpret_cast<const uint4*>(pg1 + I2_V_OFF + c1 * 16);
+    const uint32_t* kmeta = reinterpret_cast<const uint32_t*>(pg0 + I2_META_OFF);
+    uint32_t skw[NCH / 2], zkw[NCH / 2];
+#pragma unroll
+    for (int i = 0; i < NCH / 2; ++i) {
+      skw[i] = kmeta[ac0 / 2 + i];
+      zkw[i] = kmeta[(D + ac0) / 2 + i];
+    }
+    const uint16_t* vm = reinterpret_cast<const uint16_t*>(pg1 + I2_META_OFF);
+    const float sv0 = bf16_to_f32(vm[c0]), sv1 = bf16_to_f32(vm[c1]);
+    const float zv0 = bf16_to_f32(vm[D + c0]), zv1 = bf16_to_f32(vm[D + c1]);
+
+    // 1. alpha of this group for head ah, channels ac0.., 16-bit, as byte limbs in LDS
+    float A[GQ], AZ[GQ];
+    {
+      float al[NCH];
+      float amx = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const uint32_t w = skw[i >> 1];
+        al[i] = qa[i] * __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+        amx = fmaxf(amx, fabsf(al[i]));
+      }
+      amx = seg_reduce<LPH>(amx, OpMax());
+      const float inv = amx > 0.0f ? 32639.0f / amx : 0.0f;
+      int ai[NCH];
+      float zs = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        ai[i] = (int)rintf(al[i] * inv);
+        const uint32_t w = zkw[i >> 1];
+        zs = fmaf((float)ai[i], __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16)), zs);
+      }
+      zs = seg_reduce<LPH>(zs, OpAdd());
+      const float Ah = amx * (1.0f / 32639.0f);
+      const float AZh = Ah * zs;
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+        A[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Ah), hh * LPH));
+        AZ[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(AZh), hh * LPH));
+      }
+      // channel c -> alpha word (c >> 4) * 4 + (c & 3), byte (c >> 2) & 3
+      if constexpr (NCH == 16) {
+        // channels 16r .. 16r+15: word r*4 + k holds channels 16r + 4j + k in byte j
+        uint32_t wl[4], wh[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          wl[k] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(ai[12 + k], ai[8 + k], 0x0c0c0400u),
+                                        __builtin_amdgcn_perm(ai[4 + k], ai[k], 0x0c0c0400u), 0x05040100u);
+          const int h0 = (ai[k] + 128) >> 8, h1 = (ai[4 + k] + 128) >> 8, h2 = (ai[8 + k] + 128) >> 8,
+                    h3 = (ai[12 + k] + 128) >> 8;
+          wh[k] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(h3, h2, 0x0c0c0400u),
+                                        __builtin_amdgcn_perm(h1, h0, 0x0c0c0400u), 0x05040100u);
+        }
+        *reinterpret_cast<uint4*>(alo + ac0) = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+        *reinterpret_cast<uint4*>(ahi + ac0) = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+      } else if constexpr (NCH == 8) {
+        // channels 8r .. 8r+7: channels 8r + k and 8r + 4 + k share word ((r >> 1) * 4 + k), bytes j0, j0 + 1
+        const int r = lane & (LPH - 1);
+        const int base = ((r >> 1) * 16) + 2 * (r & 1);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t lo2 = __builtin_amdgcn_perm(ai[4 + k], ai[k], 0x0c0c0400u);
+          const uint32_t hi2 = __builtin_amdgcn_perm((ai[4 + k] + 128) >> 8, (ai[k] + 128) >> 8, 0x0c0c0400u);
+          *reinterpret_cast<uint16_t*>(alo + base + 4 * k) = (uint16_t)lo2;
+          *reinterpret_cast<uint16_t*>(ahi + base + 4 * k) = (uint16_t)hi2;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const int c = ac0 + i;
+          const int off = (((c >> 4) * 4 + (c & 3)) << 2) + ((c >> 2) & 3);
+          alo[off] = (uint8_t)ai[i];
+          ahi[off] = (uint8_t)((ai[i] + 128) >> 8);
+        }
+      }
+    }
+    wave_lds_sync();
+
+    // 2. key dots: token lane of each page against every head
+    int acc[2][GQ][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) acc[t][hh][0] = acc[t][hh][1] = 0;
+    const uint32_t kw[2][8] = {{k00.x, k00.y, k00.z, k00.w, k01.x, k01.y, k01.z, k01.w},
+                               {k10.x, k10.y, k10.z, k10.w, k11.x, k11.y, k11.z, k11.w}};
+#pragma unroll
+    for (int mw = 0; mw < 8; ++mw) {
+      uint32_t e[2][4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) e[t][k] = (kw[t][mw] >> (2 * k)) & 0x03030303u;
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+#pragma unroll
+        for (int lb = 0; lb < 2; ++lb) {
+          const uint4 w = *reinterpret_cast<const uint4*>(abytes + hh * 256 + lb * 128 + mw * 16);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            int r = acc[t][hh][lb];
+            r = __builtin_amdgcn_sdot4((int)w.x, (int)e[t][0], r, false);
+            r = __builtin_amdgcn_sdot4((int)w.y, (int)e[t][1], r, false);
+            r = __builtin_amdgcn_sdot4((int)w.z, (int)e[t][2], r, false);
+            r = __builtin_amdgcn_sdot4((int)w.w, (int)e[t][3], r, false);
+            acc[t][hh][lb] = r;
+          }
+        }
+      }
+    }
+
+    // 3. logits, group max, 16-bit weights as byte limbs in LDS
+    float lg[2][GQ], mg[GQ], Pf[GQ];
+    {
+      float mx[GQ];
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+        lg[0][hh] = fmaf(A[hh], (float)(acc[0][hh][1] * 256 + acc[0][hh][0]), -AZ[hh]);
+        lg[1][hh] = fmaf(A[hh], (float)(acc[1][hh][1] * 256 + acc[1][hh][0]), -AZ[hh]);
+        mx[hh] = fmaxf(lg[0][hh], lg[1][hh]);
+      }
+      heads_allreduce<GQ>(mx, OpMax(), lane, mg);
+    }
+    {
+      float ps[GQ];
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+        // u = floor(65535 p + 0.5): p in (0, 1], u in [0, 65535]
+        const uint32_t u0 = (uint32_t)fmaf(__builtin_amdgcn_exp2f(lg[0][hh] - mg[hh]), 65535.0f, 0.5f);
+        const uint32_t u1 = (uint32_t)fmaf(__builtin_amdgcn_exp2f(lg[1][hh] - mg[hh]), 65535.0f, 0.5f);
+        ps[hh] = (float)(u0 + u1);
+        uint8_t* lo = pbytes + hh * 256;
+        uint8_t* hi = lo + 128;
+        lo[pb0] = (uint8_t)u0;
+        hi[pb0] = (uint8_t)(u0 >> 8);
+        lo[pb1] = (uint8_t)u1;
+        hi[pb1] = (uint8_t)(u1 >> 8);
+      }
+      heads_allreduce<GQ>(ps, OpAdd(), lane, Pf);  // integers below 2^24: exact in fp32
+    }
+    wave_lds_sync();
+
+    // 4. value dots: channels c0, c1 against the weights of every head
+    uint32_t accv[2][GQ][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) accv[c][hh][0] = accv[c][hh][1] = 0u;
+    const uint32_t vw[2][2][4] = {{{v00.x, v00.y, v00.z, v00.w}, {v10.x, v10.y, v10.z, v10.w}},
+                                  {{v01.x, v01.y, v01.z, v01.w}, {v11.x, v11.y, v11.z, v11.w}}};
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+#pragma unroll
+      for (int gw = 0; gw < 4; ++gw) {
+        uint32_t e[2][4];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) e[c][k] = (vw[c][pp][gw] >> (2 * k)) & 0x03030303u;
+#pragma unroll
+        for (int hh = 0; hh < GQ; ++hh) {
+#pragma unroll
+          for (int lb = 0; lb < 2; ++lb) {
+            const uint4 w = *reinterpret_cast<const uint4*>(pbytes + hh * 256 + lb * 128 + (pp * 16 + gw * 4) * 4);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              uint32_t r = accv[c][hh][lb];
+              r = __builtin_amdgcn_udot4(w.x, e[c][0], r, false);
+              r = __builtin_amdgcn_udot4(w.y, e[c][1], r, false);
+              r = __builtin_amdgcn_udot4(w.z, e[c][2], r, false);
+              r = __builtin_amdgcn_udot4(w.w, e[c][3], r, false);
+              accv[c][hh][lb] = r;
+            }
+          }
+        }
+      }
+    }
+
+    // 5. online-softmax update in the rotated value frame
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      const float mnew = fmaxf(m[hh], mg[hh]);
+      const float sc = exp2_safe_diff(m[hh], mnew);
+      const float wg = __builtin_amdgcn_exp2f(mg[hh] - mnew) * (1.0f / 65535.0f);
+      const float U0 = (float)(accv[0][hh][1] * 256u + accv[0][hh][0]);
+      const float U1 = (float)(accv[1][hh][1] * 256u + accv[1][hh][0]);
+      o[hh][0] = fmaf(o[hh][0], sc, (wg * sv0) * fmaf(-zv0, Pf[hh], U0));
+      o[hh][1] = fmaf(o[hh][1], sc, (wg * sv1) * fmaf(-zv1, Pf[hh], U1));
+      l[hh] = fmaf(l[hh], sc, wg * Pf[hh]);
+      m[hh] = mnew;
+    }
+    wave_lds_sync();
+  }
+  combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, c0, c1);
+}
+
 template <int GQ>
 __device__ void int4_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
   const Geo& g = a.g;
@@ -436,7 +796,7 @@ __device__ void int4_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
   combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, lane, lane + 64);
 }
 
-template <int GQ>
+template <int GQ, bool DOT16>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   __shared__ DecodeLds<GQ> L;
   const int unit = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -463,7 +823,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
       }
     }
   } else if (g.scheme == KVQ_INT2_CHANNEL) {
-    int2_unit<GQ>(L, a, b, h, T, unit - 1);
+    if (DOT16) int2_unit_dot16<GQ>(L, a, b, h, T, unit - 1);
+    else int2_unit<GQ>(L, a, b, h, T, unit - 1);
   } else {
     int4_unit<GQ>(L, a, b, h, T, unit - 1);
   }
@@ -475,7 +836,6 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------------------------
 template <int GQ>
 __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
-  extern __shared__ float rt[];        // R_V transposed, [128][129]
   __shared__ float ob[GQ][D];          // merged rotated-frame numerators
   __shared__ float un[GQ][2][D];       // un-rotation partial sums (two halves of c)
   __shared__ float sM[GQ], sL[GQ];
@@ -491,12 +851,6 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
   }
   if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;
   const bool dense = g.rotation == KVQ_ROT_DENSE;
-  if (dense) {
-    for (int e = tid; e < D * D; e += kThreads) {
-      const int j = e / D, c = e % D;
-      rt[c * (D + 1) + j] = a.rot_v[e];  // rt[c][j] = R_V[j][c]
-    }
-  }
   // merge the quantized chunks per head
   for (int e = tid; e < GQ * D; e += kThreads) {
     const int hh = e / D, c = e % D;
@@ -517,15 +871,25 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
   }
   __syncthreads();
   if (dense) {
-    // o_j = sum_c ob[c] R_V[j][c]; thread (half, j) sums c in [64*half, 64*half+64)
+    // o_j = sum_c ob[c] R_V[j][c]; thread (half, j) sums c in [64*half, 64*half+64) of row j of R_V
     const int j = tid & (D - 1), half = tid >> 7;
+    const float4* row = reinterpret_cast<const float4*>(a.rot_v + j * D + half * 64);
+    float4 r[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = row[i];
     float acc[GQ];
 #pragma unroll
-    for (int hh = 0; hh < GQ; ++hh) acc[hh] = 0.0f;
-    for (int c = half * 64; c < half * 64 + 64; ++c) {
-      const float r = rt[c * (D + 1) + j];
+    for (int hh = 0; hh < GQ; ++hh) {
+      const float* x = &ob[hh][half * 64];
+      float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-      for (int hh = 0; hh < GQ; ++hh) acc[hh] = fmaf(ob[hh][c], r, acc[hh]);
+      for (int i = 0; i < 16; ++i) {
+        s0 = fmaf(x[4 * i], r[i].x, s0);
+        s1 = fmaf(x[4 * i + 1], r[i].y, s1);
+        s0 = fmaf(x[4 * i + 2], r[i].z, s0);
+        s1 = fmaf(x[4 * i + 3], r[i].w, s1);
+      }
+      acc[hh] = s0 + s1;
     }
 #pragma unroll
     for (int hh = 0; hh < GQ; ++hh) un[hh][half][j] = acc[hh];
@@ -570,19 +934,13 @@ template <int GQ>
 hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
   const Geo& g = a.g;
   if (stages & KVQ_STAGE_QPREP) hipLaunchKernelGGL(qprep_kernel, dim3(g.n_q, g.batch), dim3(128), 0, s, a);
-  if (stages & KVQ_STAGE_SPLITK)
-    hipLaunchKernelGGL(decode_valu_kernel<GQ>, dim3(g.n_units, g.n_kv, g.batch), dim3(kThreads), 0, s, a);
-  if (stages & KVQ_STAGE_MERGE) {
-    const int merge_lds = D * (D + 1) * (int)sizeof(float);
-    static bool attr = false;
-    if (!attr) {
-      hipError_t e = hipFuncSetAttribute((const void*)merge_kernel<GQ>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         merge_lds);
-      if (e != hipSuccess) return e;
-      attr = true;
-    }
-    hipLaunchKernelGGL(merge_kernel<GQ>, dim3(g.n_kv, g.batch), dim3(kThreads), merge_lds, s, a);
+  if (stages & KVQ_STAGE_SPLITK) {
+    if (a.impl == KVQ_DECODE_F32 || g.scheme != KVQ_INT2_CHANNEL)
+      hipLaunchKernelGGL((decode_valu_kernel<GQ, false>), dim3(g.n_units, g.n_kv, g.batch), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_valu_kernel<GQ, true>), dim3(g.n_units, g.n_kv, g.batch), dim3(kThreads), 0, s, a);
   }
+  if (stages & KVQ_STAGE_MERGE) hipLaunchKernelGGL(merge_kernel<GQ>, dim3(g.n_kv, g.batch), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1,7 +1,9 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
 
-Bar: codes, bf16 scales/zeros and band bytes bit-exact; attention outputs within 2e-3 absolute
-(the decode computes in fp32 on the same dequantized values the fp64 oracle uses).
+Bar: codes, bf16 scales/zeros and band bytes bit-exact; attention outputs within 2e-3 absolute.  The fp32
+decode (DECODE_F32) differs from the fp64 oracle by fp32 rounding only; the default INT2 decode (DOT16)
+also rounds the per-group key coefficients and softmax weights to 16-bit integers, an error well inside
+the bar on these workloads (about 2e-4 at worst in a CPU model of that arithmetic).
 """
 import sys
 
@@ -120,11 +122,12 @@ def test_tiny_single_head_full(K):
     _say(f"  worst |diff| {worst:.2e}")
 
 
-def test_gqa_ragged_batch(K):
+@pytest.mark.parametrize("impl", ["auto", "f32"])
+def test_gqa_ragged_batch(K, impl):
     wl = synth.WORKLOADS["gqa_b1_32k"]
     lens = [3000, 131, 700, 0, 260]
-    _say(f"gqa ragged lens={lens}")
-    bc = build_cache(K, wl, lens, append_steps=5)
+    _say(f"gqa ragged lens={lens} impl={impl}")
+    bc = build_cache(K, wl, lens, append_steps=5, decode_impl=K.DECODE_F32 if impl == "f32" else K.DECODE_AUTO)
     pages, band = _host(bc)
     for b in range(len(lens)):
         for h in (0, 3, 7):
@@ -158,11 +161,13 @@ def test_prefill_and_appends_give_identical_bytes(K):
             assert np.array_equal(ka, kb) and np.array_equal(va, vb)
 
 
-def test_long_context_gq8_small(K):
+@pytest.mark.parametrize("impl", ["auto", "f32"])
+def test_long_context_gq8_small(K, impl):
     wl = synth.scaled(synth.WORKLOADS["long_b4_131k"], batch=2)
     lens = [5000, 2222]
-    _say(f"long gq8 small lens={lens}, split 512")
-    bc = build_cache(K, wl, lens, append_steps=3, split_tokens=512)
+    _say(f"long gq8 small lens={lens}, split 512, impl={impl}")
+    bc = build_cache(K, wl, lens, append_steps=3, split_tokens=512,
+                     decode_impl=K.DECODE_F32 if impl == "f32" else K.DECODE_AUTO)
     pages, band = _host(bc)
     for b in range(2):
         for h in (0, 5):
@@ -197,6 +202,23 @@ def test_saw_int4_small(K):
     q = synth.queries(synth.scaled(wl, batch=len(lens)))
     out = run_decode(K, bc, q)
     check_out(bc, out, q, [(b, h) for b in range(len(lens)) for h in range(8)])
+
+
+def test_dot16_agrees_with_f32(K):
+    """The 16-bit integer-dot decode against the fp32 decode on the same cache (tiny workload: one head,
+    fp32 source with x10 outlier channels, 4096 tokens) and on a GQA cache: both within the oracle bar."""
+    import torch
+    for name, lens in (("tiny_1h_4k", [4096]), ("gqa_b1_32k", [2900, 1000])):
+        wl = synth.WORKLOADS[name]
+        _say(f"dot16 vs f32: {name} lens={lens}")
+        bc = build_cache(K, wl, lens)
+        q = synth.queries(synth.scaled(wl, batch=len(lens)))
+        outs = []
+        for impl in (K.DECODE_F32, K.DECODE_DOT16):
+            bc.cfg.decode_impl = impl
+            outs.append(run_decode(K, bc, q))
+        assert np.abs(outs[0] - outs[1]).max() <= TOL
+        check_out(bc, outs[1], q, [(b, h) for b in range(len(lens)) for h in range(wl.n_kv_heads)])
 
 
 def test_decode_is_deterministic(K):

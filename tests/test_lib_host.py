@@ -78,7 +78,7 @@ def test_bits_per_element_match_the_pages():
     ("scheme", 7, K.KVQ_EUNSUPPORTED), ("rotation", 5, K.KVQ_EUNSUPPORTED),
     ("n_q_heads", 30, K.KVQ_EINVAL), ("n_kv_heads", 0, K.KVQ_EINVAL), ("clip_k", 0.0, K.KVQ_EINVAL),
     ("clip_v", 1.5, K.KVQ_EINVAL), ("split_tokens", 100, K.KVQ_EINVAL), ("n_sink", -1, K.KVQ_EINVAL),
-    ("decode_impl", 9, K.KVQ_EINVAL),
+    ("decode_impl", 9, K.KVQ_EINVAL), ("decode_impl", 2, K.KVQ_EUNSUPPORTED),
 ])
 def test_config_validation(field, value, status):
     cfg = K.make_config(8, 32)
@@ -140,3 +140,11 @@ def test_one_hip_runtime_in_the_process():
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr
     assert r.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_dot16_decode_is_int2_only():
+    cfg4 = K.make_config(8, 32, scheme=K.INT4_TOKEN, rotation=K.ROT_HADAMARD, n_sink=0, n_recent=0,
+                         clip_k=1.0, clip_v=1.0, decode_impl=K.DECODE_DOT16)
+    assert K.check_config(cfg4) == K.KVQ_EUNSUPPORTED
+    cfg4.decode_impl = K.DECODE_F32
+    assert K.check_config(cfg4) == K.KVQ_OK
