@@ -28,9 +28,9 @@ SOURCES = {
 }
 
 
-def _compile(name: str, extra) -> str:
-    src = os.path.join(CSRC, name)
-    obj = os.path.join(BUILD, name + ".o")
+def _compile(name: str, extra, csrc: str = CSRC, build_dir: str = BUILD) -> str:
+    src = os.path.join(csrc, name)
+    obj = os.path.join(build_dir, name + ".o")
     cmd = [HIPCC, *COMMON, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -38,19 +38,20 @@ def _compile(name: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, csrc: str = CSRC, out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile the sources in `csrc` into the shared library `out` (default: the in-tree libkvq.so)."""
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda kv: _compile(*kv), SOURCES.items()))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda kv: _compile(*kv, csrc=csrc, build_dir=build_dir), SOURCES.items()))
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -115,9 +115,18 @@ __global__ __launch_bounds__(128) void qprep_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------------------------
 template <int GQ>
 struct DecodeLds {
-  float qband[GQ][D];
-  float alpha[4][GQ][D];   // per wave: alpha (INT2) / rotated query (INT4)
-  float p[4][GQ][D];       // per wave: softmax numerators of the current group/page
+  union {
+    struct {                     // band unit, fp32 INT2 path, INT4 path
+      float qband[GQ][D];
+      float alpha[4][GQ][D];     // per wave: alpha (INT2) / rotated query (INT4)
+      float p[4][GQ][D];         // per wave: softmax numerators of the current group/page
+    } f;
+    struct {                     // 16-bit INT2 path
+      uint8_t abytes[4][GQ * 256];  // per wave: key-side operand words [head][limb][32]
+      uint8_t pbytes[4][GQ * 256];  // per wave: value-side operand words [head][limb][32]
+      uint4 vstage[4][256];         // per wave: value codes of the current group (both pages, 4 KB)
+    } d;
+  };
   float cm[4][GQ];
   float cl[4][GQ];
   float co[4][GQ][D];
@@ -175,7 +184,7 @@ __device__ void band_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
   const Geo& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < GQ * D; e += kThreads)
-    L.qband[e / D][e % D] = a.qband[((long long)b * g.n_q + h * GQ + e / D) * D + e % D];
+    L.f.qband[e / D][e % D] = a.qband[((long long)b * g.n_q + h * GQ + e / D) * D + e % D];
   __syncthreads();
   const int ng = n_groups_of(T, g.S0, g.W);
   const int n_sink = T < g.S0 ? T : g.S0;
@@ -211,7 +220,7 @@ __device__ void band_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
           const float k0 = __uint_as_float(ws[p2] << 16), k1 = __uint_as_float(ws[p2] & 0xffff0000u);
           const int c = v8 * 8 + p2 * 2;
 #pragma unroll
-          for (int hh = 0; hh < GQ; ++hh) lg[hh] += L.qband[hh][c] * k0 + L.qband[hh][c + 1] * k1;
+          for (int hh = 0; hh < GQ; ++hh) lg[hh] += L.f.qband[hh][c] * k0 + L.f.qband[hh][c + 1] * k1;
         }
       }
     }
@@ -221,7 +230,7 @@ __device__ void band_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
       float mnew;
       softmax_update<GQ>(m, l, o, hh, wave_max(x), mnew);
       const float p = valid ? exp2f(x - mnew) : 0.0f;
-      L.p[wave][hh][lane] = p;
+      L.f.p[wave][hh][lane] = p;
       l[hh] += wave_sum(p);
     }
     wave_lds_sync();
@@ -232,7 +241,7 @@ __device__ void band_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
       const float v0 = __uint_as_float(vv << 16), v1 = __uint_as_float(vv & 0xffff0000u);
 #pragma unroll
       for (int hh = 0; hh < GQ; ++hh) {
-        const float p = L.p[wave][hh][kk];
+        const float p = L.f.p[wave][hh][kk];
         o[hh][0] += p * v0;
         o[hh][1] += p * v1;
       }
@@ -277,8 +286,8 @@ __device__ void int2_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
 #pragma unroll
     for (int hh = 0; hh < GQ; ++hh) {
       const float a0 = qr[hh][0] * sk0, a1 = qr[hh][1] * sk1;
-      L.alpha[wave][hh][lane] = a0;
-      L.alpha[wave][hh][lane + 64] = a1;
+      L.f.alpha[wave][hh][lane] = a0;
+      L.f.alpha[wave][hh][lane + 64] = a1;
       beta[hh] = wave_sum(a0 * zk0 + a1 * zk1);
     }
     wave_lds_sync();
@@ -304,7 +313,7 @@ __device__ void int2_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
             const int c = half * 64 + wd * 16 + by * 4;
 #pragma unroll
             for (int hh = 0; hh < GQ; ++hh) {
-              const float4 al = *reinterpret_cast<const float4*>(&L.alpha[wave][hh][c]);
+              const float4 al = *reinterpret_cast<const float4*>(&L.f.alpha[wave][hh][c]);
               acc[hh] += al.x * f0 + al.y * f1 + al.z * f2 + al.w * f3;
             }
           }
@@ -319,8 +328,8 @@ __device__ void int2_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
       float mnew;
       softmax_update<GQ>(m, l, o, hh, wave_max(fmaxf(lg[0][hh], lg[1][hh])), mnew);
       const float p0 = exp2f(lg[0][hh] - mnew), p1 = exp2f(lg[1][hh] - mnew);
-      L.p[wave][hh][lane] = p0;
-      L.p[wave][hh][64 + lane] = p1;
+      L.f.p[wave][hh][lane] = p0;
+      L.f.p[wave][hh][64 + lane] = p1;
       P[hh] = wave_sum(p0 + p1);
       l[hh] += P[hh];
     }
@@ -342,7 +351,7 @@ __device__ void int2_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
           const int i0 = pp * 64 + 16 * j + 4 * gg;
 #pragma unroll
           for (int hh = 0; hh < GQ; ++hh) {
-            const float4 p4 = *reinterpret_cast<const float4*>(&L.p[wave][hh][i0]);
+            const float4 p4 = *reinterpret_cast<const float4*>(&L.f.p[wave][hh][i0]);
             u[hh][0] += p4.x * (float)(x0 & 3u) + p4.y * (float)((x0 >> 2) & 3u) + p4.z * (float)((x0 >> 4) & 3u) +
                         p4.w * (float)((x0 >> 6) & 3u);
             u[hh][1] += p4.x * (float)(x1 & 3u) + p4.y * (float)((x1 >> 2) & 3u) + p4.z * (float)((x1 >> 4) & 3u) +
@@ -384,6 +393,12 @@ __device__ inline float seg_reduce(float x, Op op) {
   if (N >= 32) x = op(x, __shfl_xor(x, 16, 64));
   if (N >= 64) x = op(x, __shfl_xor(x, 32, 64));
   return x;
+}
+
+// Wave-uniform read of data the kernel never writes, through the scalar cache (constant address space).
+__device__ inline int2 scalar_load_int2(const int2* p) {
+  const __attribute__((address_space(4))) int* q = (const __attribute__((address_space(4))) int*)(uintptr_t)p;
+  return make_int2(q[0], q[1]);
 }
 
 template <int GQ>
@@ -475,25 +490,34 @@ __device__ void int2_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, in
     o[hh][0] = o[hh][1] = 0.0f;
   }
   // per-wave operand bytes: [head][limb lo, hi][32 words]
-  uint8_t* abytes = reinterpret_cast<uint8_t*>(&L.alpha[wave][0][0]);
-  uint8_t* pbytes = reinterpret_cast<uint8_t*>(&L.p[wave][0][0]);
+  uint8_t* abytes = L.d.abytes[wave];
+  uint8_t* pbytes = L.d.pbytes[wave];
+  uint4* vst = L.d.vstage[wave];
   uint8_t* alo = abytes + ah * 256;
   uint8_t* ahi = alo + 128;
   const int pb0 = ((((lane >> 2) & 3) * 4 + (lane & 3)) << 2) + (lane >> 4);  // token lane of the even page
   const int pb1 = pb0 + 64;                                                    // token lane of the odd page
-  const int32_t* pt = a.page_table + (long long)b * g.max_pages;
+  // the page table is read-only here: scalar loads, the next group's entries one iteration ahead
+  const int2* pt = reinterpret_cast<const int2*>(a.page_table + (long long)b * g.max_pages);
   const long long hoff = (long long)h * I2_HEAD_BYTES;
+  int2 pnext = make_int2(0, 0);
+  if (g_begin + wave < g_end) pnext = scalar_load_int2(pt + g_begin + wave);
   for (int gi = g_begin + wave; gi < g_end; gi += 4) {
-    const uint8_t* pg0 = a.pages + (long long)pt[2 * gi] * g.page_bytes + hoff;
-    const uint8_t* pg1 = a.pages + (long long)pt[2 * gi + 1] * g.page_bytes + hoff;
+    const int2 pcur = pnext;
+    if (gi + 4 < g_end) pnext = scalar_load_int2(pt + gi + 4);
+    const uint8_t* pg0 = a.pages + (long long)pcur.x * g.page_bytes + hoff;
+    const uint8_t* pg1 = a.pages + (long long)pcur.y * g.page_bytes + hoff;
     const uint4 k00 = reinterpret_cast<const uint4*>(pg0 + I2_K_OFF + lane * 32)[0];
     const uint4 k01 = reinterpret_cast<const uint4*>(pg0 + I2_K_OFF + lane * 32)[1];
     const uint4 k10 = reinterpret_cast<const uint4*>(pg1 + I2_K_OFF + lane * 32)[0];
     const uint4 k11 = reinterpret_cast<const uint4*>(pg1 + I2_K_OFF + lane * 32)[1];
-    const uint4 v00 = *reinterpret_cast<const uint4*>(pg0 + I2_V_OFF + c0 * 16);
-    const uint4 v01 = *reinterpret_cast<const uint4*>(pg0 + I2_V_OFF + c1 * 16);
-    const uint4 v10 = *reinterpret_cast<const uint4*>(pg1 + I2_V_OFF + c0 * 16);
-    const uint4 v11 = *reinterpret_cast<const uint4*>(pg1 + I2_V_OFF + c1 * 16);
+    // value codes go straight to LDS (no registers held while in flight): 1 KB per instruction,
+    // lane i's 16 bytes at vst + 64 j + i; vst[64 pp' + c'] = row of channel c' (+64 for j odd) of page pp
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (__attribute__((address_space(1))) void*)((j < 2 ? pg0 : pg1) + I2_V_OFF + (j & 1) * 1024 + lane * 16),
+          (__attribute__((address_space(3))) void*)(vst + 64 * j), 16, 0, 0);
     const uint32_t* kmeta = reinterpret_cast<const uint32_t*>(pg0 + I2_META_OFF);
     uint32_t skw[NCH / 2], zkw[NCH / 2];
 #pragma unroll
@@ -580,6 +604,12 @@ __device__ void int2_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, in
       for (int hh = 0; hh < GQ; ++hh) acc[t][hh][0] = acc[t][hh][1] = 0;
     const uint32_t kw[2][8] = {{k00.x, k00.y, k00.z, k00.w, k01.x, k01.y, k01.z, k01.w},
                                {k10.x, k10.y, k10.z, k10.w, k11.x, k11.y, k11.z, k11.w}};
+    // operand words in order (mw, head, limb); the read of the next one is issued before the current dots
+    auto aword = [&](int idx) {
+      const int mw = idx / (2 * GQ), hh = (idx / 2) % GQ, lb = idx & 1;
+      return *reinterpret_cast<const uint4*>(abytes + hh * 256 + lb * 128 + mw * 16);
+    };
+    uint4 wk = aword(0);
 #pragma unroll
     for (int mw = 0; mw < 8; ++mw) {
       uint32_t e[2][4];
@@ -591,7 +621,9 @@ __device__ void int2_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, in
       for (int hh = 0; hh < GQ; ++hh) {
 #pragma unroll
         for (int lb = 0; lb < 2; ++lb) {
-          const uint4 w = *reinterpret_cast<const uint4*>(abytes + hh * 256 + lb * 128 + mw * 16);
+          const int idx = (mw * GQ + hh) * 2 + lb;
+          const uint4 w = wk;
+          if (idx + 1 < 16 * GQ) wk = aword(idx + 1);
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             int r = acc[t][hh][lb];
@@ -642,8 +674,16 @@ __device__ void int2_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, in
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int hh = 0; hh < GQ; ++hh) accv[c][hh][0] = accv[c][hh][1] = 0u;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the value codes have landed in LDS
+    const uint4 v00 = vst[c0], v01 = vst[64 + c0], v10 = vst[128 + c0], v11 = vst[192 + c0];
     const uint32_t vw[2][2][4] = {{{v00.x, v00.y, v00.z, v00.w}, {v10.x, v10.y, v10.z, v10.w}},
                                   {{v01.x, v01.y, v01.z, v01.w}, {v11.x, v11.y, v11.z, v11.w}}};
+    // operand words in order (page, word, head, limb), read one ahead
+    auto pword = [&](int idx) {
+      const int pg = idx / (2 * GQ), hh = (idx / 2) % GQ, lb = idx & 1;  // pg = pp * 4 + gw
+      return *reinterpret_cast<const uint4*>(pbytes + hh * 256 + lb * 128 + pg * 16);
+    };
+    uint4 wv = pword(0);
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
 #pragma unroll
@@ -657,7 +697,9 @@ __device__ void int2_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, in
         for (int hh = 0; hh < GQ; ++hh) {
 #pragma unroll
           for (int lb = 0; lb < 2; ++lb) {
-            const uint4 w = *reinterpret_cast<const uint4*>(pbytes + hh * 256 + lb * 128 + (pp * 16 + gw * 4) * 4);
+            const int idx = ((pp * 4 + gw) * GQ + hh) * 2 + lb;
+            const uint4 w = wv;
+            if (idx + 1 < 16 * GQ) wv = pword(idx + 1);
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
               uint32_t r = accv[c][hh][lb];
@@ -704,8 +746,8 @@ __device__ void int4_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
   for (int hh = 0; hh < GQ; ++hh) {
     const float* q = a.qrot + ((long long)b * g.n_q + h * GQ + hh) * D;
     const float q0 = q[lane], q1 = q[lane + 64];
-    L.alpha[wave][hh][lane] = q0;
-    L.alpha[wave][hh][lane + 64] = q1;
+    L.f.alpha[wave][hh][lane] = q0;
+    L.f.alpha[wave][hh][lane + 64] = q1;
     qsum[hh] = wave_sum(q0 + q1);
   }
   wave_lds_sync();
@@ -742,8 +784,8 @@ __device__ void int4_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
         for (int k = 0; k < 8; ++k) f[k] = (float)((ws[wd] >> (4 * k)) & 15u);
 #pragma unroll
         for (int hh = 0; hh < GQ; ++hh) {
-          const float4 a0 = *reinterpret_cast<const float4*>(&L.alpha[wave][hh][c]);
-          const float4 a1 = *reinterpret_cast<const float4*>(&L.alpha[wave][hh][c + 4]);
+          const float4 a0 = *reinterpret_cast<const float4*>(&L.f.alpha[wave][hh][c]);
+          const float4 a1 = *reinterpret_cast<const float4*>(&L.f.alpha[wave][hh][c + 4]);
           acc[hh] += a0.x * f[0] + a0.y * f[1] + a0.z * f[2] + a0.w * f[3] + a1.x * f[4] + a1.y * f[5] +
                      a1.z * f[6] + a1.w * f[7];
         }
@@ -757,7 +799,7 @@ __device__ void int4_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
       softmax_update<GQ>(m, l, o, hh, wave_max(x), mnew);
       const float p = valid ? exp2f(x - mnew) : 0.0f;
       const float w = p * sv;
-      L.p[wave][hh][lane] = w;
+      L.f.p[wave][hh][lane] = w;
       l[hh] += wave_sum(p);
       wz[hh] = wave_sum(w * zv);
     }
@@ -778,7 +820,7 @@ __device__ void int4_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
         const int i0 = 16 * j + 4 * gg;
 #pragma unroll
         for (int hh = 0; hh < GQ; ++hh) {
-          const float4 p4 = *reinterpret_cast<const float4*>(&L.p[wave][hh][i0]);
+          const float4 p4 = *reinterpret_cast<const float4*>(&L.f.p[wave][hh][i0]);
           o[hh][0] += p4.x * (float)(x0 & 15u) + p4.y * (float)((x0 >> 4) & 15u) + p4.z * (float)((x0 >> 8) & 15u) +
                       p4.w * (float)((x0 >> 12) & 15u);
           o[hh][1] += p4.x * (float)(x1 & 15u) + p4.y * (float)((x1 >> 4) & 15u) + p4.z * (float)((x1 >> 8) & 15u) +
