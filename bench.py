@@ -229,17 +229,23 @@ def main():
         qo_sum += qo_b
     step_bytes = (kv_sum + qo_sum) / args.steps
 
-    # split-K decode kernel alone, same launch configuration, HIP events on its stream
+    # each kernel of the step alone, same launch configuration, HIP events around every launch on the
+    # stream it runs on (torch's current stream, which the binding passes to the library)
+    def time_launches(fn, reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
+
     K.kv_decode_attn_stages(cache, qs[-1], out, T_end, ws, K.STAGE_QPREP)
-    torch.cuda.synchronize()
-    k0 = torch.cuda.Event(enable_timing=True)
-    k1 = torch.cuda.Event(enable_timing=True)
-    k0.record()
-    for _ in range(args.kernel_reps):
-        K.kv_decode_attn_stages(cache, qs[-1], out, T_end, ws, K.STAGE_SPLITK)
-    k1.record()
-    torch.cuda.synchronize()
-    kern_ms = k0.elapsed_time(k1) / args.kernel_reps
+    stage_us = {}
+    for name, st in (("qprep", K.STAGE_QPREP), ("splitk", K.STAGE_SPLITK), ("merge", K.STAGE_MERGE)):
+        stage_us[name] = round(1e3 * time_launches(
+            lambda st=st: K.kv_decode_attn_stages(cache, qs[-1], out, T_end, ws, st), args.kernel_reps), 2)
+    kern_ms = stage_us["splitk"] * 1e-3
     kv_b, _ = decode_bytes(wl, [T_end] * B, wl.n_sink, wl.n_recent)
     kern_bytes = kv_b + B * n_q * 128 * 4 * 2  # + the fp32 rotated and band queries it reads
     achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
@@ -269,6 +275,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "split-K decode (INT2 pages + bf16 band)", "kernel_us": round(kern_ms * 1e3, 2),
                      "bytes_per_launch": kern_bytes},
+        "decode_kernels_us": stage_us,
     }
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle) ...")

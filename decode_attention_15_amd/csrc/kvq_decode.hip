@@ -79,33 +79,48 @@ __device__ inline uint32_t wave_sum_u32(uint32_t x) {
 // Query preparation: q~ = (q R_K) * log2e/sqrt(128) for quantized tokens (rotated frame), and
 // q * log2e/sqrt(128) for the bf16 band (original frame).
 // ---------------------------------------------------------------------------------------------
+template <int GQ>
 __global__ __launch_bounds__(128) void qprep_kernel(DecodeArgs a) {
-  __shared__ float qs[D];
-  const int hq = blockIdx.x, b = blockIdx.y, j = threadIdx.x;
-  const long long base = ((long long)b * a.g.n_q + hq) * D;
-  const float qv = a.q_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[base + j])
-                            : static_cast<const float*>(a.q)[base + j];
+  __shared__ float qs[GQ][D];
+  const int h = blockIdx.x, b = blockIdx.y, j = threadIdx.x;
+  const long long base = ((long long)b * a.g.n_q + h * GQ) * D;
   const float scale = LOG2E * kInvSqrt128;
-  a.qband[base + j] = qv * scale;
-  float r;
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh) {
+    const float qv = a.q_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[base + hh * D + j])
+                              : static_cast<const float*>(a.q)[base + hh * D + j];
+    a.qband[base + hh * D + j] = qv * scale;
+    qs[hh][j] = a.g.rotation == KVQ_ROT_DENSE ? qv : qv * a.rot_k[j];
+  }
+  __syncthreads();
+  float r[GQ];
   if (a.g.rotation == KVQ_ROT_DENSE) {
-    qs[j] = qv;
-    __syncthreads();
-    float acc = 0.0f;
-    for (int i = 0; i < D; ++i) acc = fmaf(qs[i], a.rot_k[i * D + j], acc);
-    r = acc;
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) r[hh] = 0.0f;
+#pragma unroll 16
+    for (int i = 0; i < D; ++i) {
+      const float rk = a.rot_k[i * D + j];
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) r[hh] = fmaf(qs[hh][i], rk, r[hh]);
+    }
   } else {
-    qs[j] = qv * a.rot_k[j];
-    __syncthreads();
-    for (int hh = 1; hh < D; hh <<= 1) {
-      const float x = qs[j], y = qs[j ^ hh];
+    for (int hb = 1; hb < D; hb <<= 1) {
+      float x[GQ];
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+        const float u = qs[hh][j], v = qs[hh][j ^ hb];
+        x[hh] = (j & hb) ? (v - u) : (u + v);
+      }
       __syncthreads();
-      qs[j] = (j & hh) ? (y - x) : (x + y);
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) qs[hh][j] = x[hh];
       __syncthreads();
     }
-    r = qs[j] * kInvSqrt128;
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) r[hh] = qs[hh][j] * kInvSqrt128;
   }
-  a.qrot[base + j] = r * scale;
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh) a.qrot[base + hh * D + j] = r[hh] * scale;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -898,8 +913,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
     const int hh = e / D, c = e % D;
     const float* base = a.partials + ((long long)b * g.n_q + h * GQ + hh) * g.n_units * PART_STRIDE;
     float M = -INFINITY;
+#pragma unroll 8
     for (int u = 1; u <= n_chunks; ++u) M = fmaxf(M, base[u * PART_STRIDE]);
     float acc = 0.0f, lsum = 0.0f;
+#pragma unroll 8
     for (int u = 1; u <= n_chunks; ++u) {
       const float sc = exp2_safe_diff(base[u * PART_STRIDE], M);
       acc += sc * base[u * PART_STRIDE + 2 + c];
@@ -975,7 +992,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
 template <int GQ>
 hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
   const Geo& g = a.g;
-  if (stages & KVQ_STAGE_QPREP) hipLaunchKernelGGL(qprep_kernel, dim3(g.n_q, g.batch), dim3(128), 0, s, a);
+  if (stages & KVQ_STAGE_QPREP) hipLaunchKernelGGL(qprep_kernel<GQ>, dim3(g.n_kv, g.batch), dim3(128), 0, s, a);
   if (stages & KVQ_STAGE_SPLITK) {
     if (a.impl == KVQ_DECODE_F32 || g.scheme != KVQ_INT2_CHANNEL)
       hipLaunchKernelGGL((decode_valu_kernel<GQ, false>), dim3(g.n_units, g.n_kv, g.batch), dim3(kThreads), 0, s, a);
