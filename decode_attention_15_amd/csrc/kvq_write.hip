@@ -13,6 +13,9 @@ namespace kvq {
 namespace {
 
 constexpr unsigned kFull = 0xffffffffu;
+// LDS rows of a group's input tokens are padded by one float so that the 16 rows one matrix-core
+// operand reads sit in different banks
+constexpr int XS_STRIDE = D + 1;
 
 __device__ inline float src_as_bf16_value(const void* src, int src_bf16, long long idx) {
   if (src_bf16) return bf16_to_f32(static_cast<const uint16_t*>(src)[idx]);
@@ -120,17 +123,58 @@ __device__ inline void rotate_vec(const float* xs, const float* rot, int rotatio
   }
 }
 
+// Dense rotation of a 128-token group, X~ = X R (X: 128 tokens x XS_STRIDE in LDS, fp32 values of bf16; R fp32
+// row-major), on the fp64 matrix cores: v_mfma_f64_16x16x4f64 adds its four products to the accumulator
+// one after another in k order, with one fp64 rounding per addition, so the chain over k = 0..127 gives
+// the same bits as the sequential fp64 sum the cache format specifies (every product x_i R[i][j] is exact
+// in fp64).  Operand layout: lane l supplies A[row l % 16][k l / 16] and B[k l / 16][col l % 16]; the
+// result lands in lane l, register r at row l / 16 + 4 r, column l % 16.  Wave w computes tokens
+// [32w, 32w + 32) x all 128 columns: 2 x 8 tiles of 16 x 16, 32 steps of k = 4.
+__device__ inline void rotate_group_mfma(const float* xs, const float* rot, float* xr, int wave, int lane) {
+  typedef double d4 __attribute__((ext_vector_type(4)));
+  const int li = lane & 15, lk = lane >> 4;
+  const int t0 = wave * 32;
+#pragma unroll 1
+  for (int half = 0; half < 2; ++half) {       // columns [64 half, 64 half + 64): 4 column tiles
+    d4 acc[2][4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = d4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int s = 0; s < D / 4; ++s) {
+      const int kk = 4 * s + lk;
+      double av[2], bv[4];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) av[rt] = (double)xs[(t0 + 16 * rt + li) * XS_STRIDE + kk];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) bv[ct] = (double)rot[kk * D + 64 * half + 16 * ct + li];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[rt], bv[ct], acc[rt][ct], 0, 0, 0);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          xr[(t0 + 16 * rt + lk + 4 * r) * D + 64 * half + 16 * ct + li] = (float)acc[rt][ct][r];
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // INT2 per-channel groups.  One work-group quantizes one (sequence, kv head, K|V, new group):
 // gather 128 bf16 tokens (band or new input) -> rotate -> per-token clip -> per-channel min/max
 // -> bf16 scale/zero -> codes -> K token-major rows / V channel-major rows + metadata.
 // ---------------------------------------------------------------------------------------------
-constexpr int kGroupLds = 2 * GROUP * D * (int)sizeof(float);
+constexpr int kGroupLds = (GROUP * XS_STRIDE + GROUP * D) * (int)sizeof(float);
 
 __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
   extern __shared__ float lds[];
-  float* xs = lds;               // [128 tokens][128] inputs (bf16 values)
-  float* xr = lds + GROUP * D;   // [128 tokens][128] rotated, then clipped
+  float* xs = lds;                       // [128 tokens][XS_STRIDE] inputs (bf16 values)
+  float* xr = lds + GROUP * XS_STRIDE;   // [128 tokens][128] rotated, then clipped
   __shared__ float red_min[2][D], red_max[2][D];
   __shared__ float s_sp[D], s_zp[D];
 
@@ -167,30 +211,17 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
       const long long row = c0 + (t - T0);
       val = src_as_bf16_value(src, a.src_bf16, (row * g.n_kv + h) * D + c);
     }
-    xs[tl * D + c] = val;
+    xs[tl * XS_STRIDE + c] = val;
   }
   __syncthreads();
 
   // 2. rotation
   if (g.rotation == KVQ_ROT_DENSE) {
-    const int j = tid & (D - 1);
-    const int tb = (tid >> 7) * 64;
-    for (int t8 = 0; t8 < 64; t8 += 8) {
-      double acc[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = 0.0;
-      for (int i = 0; i < D; ++i) {
-        const double r = (double)rot[i * D + j];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] = fma((double)xs[(tb + t8 + k) * D + i], r, acc[k]);
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) xr[(tb + t8 + k) * D + j] = (float)acc[k];
-    }
+    rotate_group_mfma(xs, rot, xr, wave, lane);
   } else {
     for (int tl = wave * 32; tl < wave * 32 + 32; ++tl) {
       float y0, y1;
-      rotate_vec(xs + tl * D, rot, g.rotation, lane, y0, y1);
+      rotate_vec(xs + tl * XS_STRIDE, rot, g.rotation, lane, y0, y1);
       xr[tl * D + lane] = y0;
       xr[tl * D + lane + 64] = y1;
     }
