@@ -32,7 +32,6 @@ int check_config(const kvq_config* c) {
       c->decode_impl != KVQ_DECODE_DOT16)
     return KVQ_EINVAL;
   if (c->decode_impl == KVQ_DECODE_MFMA) return KVQ_EUNSUPPORTED;
-  if (c->decode_impl == KVQ_DECODE_DOT16 && c->scheme != KVQ_INT2_CHANNEL) return KVQ_EUNSUPPORTED;
   return KVQ_OK;
 }
 

@@ -747,6 +747,215 @@ __device__ void int2_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, in
   combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, c0, c1);
 }
 
+// ---------------------------------------------------------------------------------------------
+// INT4 token-wise page walk, 16-bit fixed point on v_dot4 ([SAW] App. A.1 eq. (3)-(4), App. A.4 eq. (13)):
+//   logit_t = s_t (sum_c q~_c code_tc - z_t sum_c q~_c): the key-side operand is the rotated query
+//   itself, rounded once per work-group to a_c = rint(q~_c 32639 / max|q~|) (A = max|q~| / 32639),
+//   so logit_t = A s_t (sum_c a_c code_tc - z_t sum_c a_c).
+//   out_c = sum_t p_t s'_t (code'_tc - z'_t): the value-side weight w_t = p_t s'_t (p_t = 2^(logit_t -
+//   max over the page) <= 1) is rounded to u_t = rint(65535 w_t / S'), S' = max over the page of s'_t,
+//   so out_c = (S' / 65535) (sum_t u_t code'_tc - sum_t u_t z'_t).
+// Both 16-bit operands are split into two byte limbs as in int2_unit_dot16.  Lane roles: key token lane of
+// the page; value channels lane, lane + 64.  Operand words in LDS:
+//   key code word m (channels 8m .. 8m+7, channel c in byte (c/2) % 4, low nibble = even c):
+//     (w >> 4n) & 0x0F0F0F0F holds channel 8m + 2j + n in byte j -> alpha word (2m + n), byte j;
+//   value code word W of a channel (tokens 16j + 4g + r in byte 8g + 2j + r/2, nibble r % 2, W = 2g + j/2):
+//     (w >> 4n) & 0x0F0F0F0F holds, in byte bw, token 16 (2 (W % 2) + bw / 2) + 4 (W / 2) + 2 (bw % 2) + n
+//     -> weight word (2W + n), byte bw.
+// ---------------------------------------------------------------------------------------------
+template <int GQ>
+__device__ void int4_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
+  constexpr int LG = HeadLog2<GQ>::v;
+  constexpr int LPH = 64 >> LG;
+  constexpr int NCH = 2 * GQ;
+  const Geo& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_pages = (T + PAGE - 1) / PAGE;
+  const int p_begin = chunk * g.gpc;
+  int p_end = (p_begin + g.gpc) < n_pages ? (p_begin + g.gpc) : n_pages;
+  if (p_end > g.max_pages) p_end = g.max_pages;
+  const int c0 = lane, c1 = lane + 64;
+  uint8_t* abytes = L.d.abytes[wave];
+  uint8_t* pbytes = L.d.pbytes[wave];
+
+  // 1. key-side operand: the rotated query of each head, 16-bit, once for all pages of this chunk
+  float A[GQ], QA[GQ];
+  {
+    const int ah = lane >> (6 - LG);
+    const int ac0 = (lane & (LPH - 1)) * NCH;
+    const float* q = a.qrot + ((long long)b * g.n_q + h * GQ + ah) * D + ac0;
+    float qa[NCH];
+    float amx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      qa[i] = q[i];
+      amx = fmaxf(amx, fabsf(qa[i]));
+    }
+    amx = seg_reduce<LPH>(amx, OpMax());
+    const float inv = amx > 0.0f ? 32639.0f / amx : 0.0f;
+    float qsum = 0.0f;
+    uint8_t* lo = abytes + ah * 256;
+    uint8_t* hi = lo + 128;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ai = (int)rintf(qa[i] * inv);
+      qsum += (float)ai;
+      const int c = ac0 + i;
+      const int off = ((((c >> 3) * 2) + (c & 1)) << 2) + ((c >> 1) & 3);
+      lo[off] = (uint8_t)ai;
+      hi[off] = (uint8_t)((ai + 128) >> 8);
+    }
+    qsum = seg_reduce<LPH>(qsum, OpAdd());  // integers of magnitude < 2^22: exact
+    const float Ah = amx * (1.0f / 32639.0f);
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      A[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Ah), hh * LPH));
+      QA[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qsum), hh * LPH));
+    }
+  }
+  wave_lds_sync();
+
+  float m[GQ], l[GQ], o[GQ][2];
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.0f;
+    o[hh][0] = o[hh][1] = 0.0f;
+  }
+  // token lane -> weight word (2W + n), byte bw
+  const int tj = lane >> 4, tg = (lane >> 2) & 3, tr = lane & 3;
+  const int pboff = ((2 * (2 * tg + (tj >> 1)) + (tr & 1)) << 2) + 2 * (tj & 1) + (tr >> 1);
+  const long long hoff = (long long)h * I4_HEAD_BYTES;
+  const int32_t* pt = a.page_table + (long long)b * g.max_pages;
+  for (int pi = p_begin + wave; pi < p_end; pi += 4) {
+    const uint8_t* pg = a.pages + (long long)pt[pi] * g.page_bytes + hoff;
+    const int t = pi * PAGE + lane;
+    const bool valid = t < T;
+    const uint4* kr = reinterpret_cast<const uint4*>(pg + I4_K_OFF + lane * 64);
+    const uint4 k0 = kr[0], k1 = kr[1], k2 = kr[2], k3 = kr[3];
+    const uint4 v00 = reinterpret_cast<const uint4*>(pg + I4_V_OFF + c0 * 32)[0];
+    const uint4 v01 = reinterpret_cast<const uint4*>(pg + I4_V_OFF + c0 * 32)[1];
+    const uint4 v10 = reinterpret_cast<const uint4*>(pg + I4_V_OFF + c1 * 32)[0];
+    const uint4 v11 = reinterpret_cast<const uint4*>(pg + I4_V_OFF + c1 * 32)[1];
+    const uint32_t kmw = *reinterpret_cast<const uint32_t*>(pg + I4_KMETA_OFF + 4 * lane);
+    const uint32_t vmw = *reinterpret_cast<const uint32_t*>(pg + I4_VMETA_OFF + 4 * lane);
+    const float sk = __uint_as_float(kmw << 16), zk = __uint_as_float(kmw & 0xffff0000u);
+    const float sv = __uint_as_float(vmw << 16), zv = __uint_as_float(vmw & 0xffff0000u);
+
+    // 2. key dots
+    int acc[GQ][2];
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) acc[hh][0] = acc[hh][1] = 0;
+    const uint32_t kw[16] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w,
+                             k2.x, k2.y, k2.z, k2.w, k3.x, k3.y, k3.z, k3.w};
+#pragma unroll
+    for (int mp = 0; mp < 8; ++mp) {  // pairs of code words (16 channels)
+      const uint32_t e00 = kw[2 * mp] & 0x0F0F0F0Fu, e01 = (kw[2 * mp] >> 4) & 0x0F0F0F0Fu;
+      const uint32_t e10 = kw[2 * mp + 1] & 0x0F0F0F0Fu, e11 = (kw[2 * mp + 1] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+#pragma unroll
+        for (int lb = 0; lb < 2; ++lb) {
+          const uint4 w = *reinterpret_cast<const uint4*>(abytes + hh * 256 + lb * 128 + mp * 16);
+          int r = acc[hh][lb];
+          r = __builtin_amdgcn_sdot4((int)w.x, (int)e00, r, false);
+          r = __builtin_amdgcn_sdot4((int)w.y, (int)e01, r, false);
+          r = __builtin_amdgcn_sdot4((int)w.z, (int)e10, r, false);
+          r = __builtin_amdgcn_sdot4((int)w.w, (int)e11, r, false);
+          acc[hh][lb] = r;
+        }
+      }
+    }
+
+    // 3. logits, page max, weights
+    float lg[GQ], mg[GQ], psum[GQ], uz[GQ];
+    {
+      float mx[GQ];
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+        // sum_c a_c (code_tc - z_t) in integers (z_t is an integer for INT4), then one conversion
+        const int lint = acc[hh][1] * 256 + acc[hh][0] - (valid ? (int)zk : 0) * (int)QA[hh];
+        lg[hh] = valid ? (A[hh] * sk) * (float)lint : -INFINITY;
+        mx[hh] = lg[hh];
+      }
+      heads_allreduce<GQ>(mx, OpMax(), lane, mg);
+    }
+    const float Sv = seg_reduce<64>(valid ? sv : 0.0f, OpMax());
+    const float rs = Sv > 0.0f ? 65535.0f / Sv : 0.0f;
+    {
+      float pp[GQ], zz[GQ];
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+        // tokens past the end of the sequence: weight 0, and their (unwritten) metadata never read
+        const float p = valid ? __builtin_amdgcn_exp2f(lg[hh] - mg[hh]) : 0.0f;
+        const uint32_t u = valid ? (uint32_t)fmaf(p * sv, rs, 0.5f) : 0u;
+        pp[hh] = p;
+        zz[hh] = valid ? (float)u * zv : 0.0f;
+        uint8_t* lo = pbytes + hh * 256;
+        lo[pboff] = (uint8_t)u;
+        lo[pboff + 128] = (uint8_t)(u >> 8);
+      }
+      heads_allreduce<GQ>(pp, OpAdd(), lane, psum);
+      heads_allreduce<GQ>(zz, OpAdd(), lane, uz);
+    }
+    wave_lds_sync();
+
+    // 4. value dots: channels c0, c1; code word W of each channel against weight words (2W, 2W + 1)
+    uint32_t accv[2][GQ][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) accv[c][hh][0] = accv[c][hh][1] = 0u;
+    const uint32_t vw[2][8] = {{v00.x, v00.y, v00.z, v00.w, v01.x, v01.y, v01.z, v01.w},
+                               {v10.x, v10.y, v10.z, v10.w, v11.x, v11.y, v11.z, v11.w}};
+#pragma unroll
+    for (int wp = 0; wp < 4; ++wp) {  // pairs of code words
+      uint32_t e[2][4];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        e[c][0] = vw[c][2 * wp] & 0x0F0F0F0Fu;
+        e[c][1] = (vw[c][2 * wp] >> 4) & 0x0F0F0F0Fu;
+        e[c][2] = vw[c][2 * wp + 1] & 0x0F0F0F0Fu;
+        e[c][3] = (vw[c][2 * wp + 1] >> 4) & 0x0F0F0F0Fu;
+      }
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+#pragma unroll
+        for (int lb = 0; lb < 2; ++lb) {
+          const uint4 w = *reinterpret_cast<const uint4*>(pbytes + hh * 256 + lb * 128 + wp * 16);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            uint32_t r = accv[c][hh][lb];
+            r = __builtin_amdgcn_udot4(w.x, e[c][0], r, false);
+            r = __builtin_amdgcn_udot4(w.y, e[c][1], r, false);
+            r = __builtin_amdgcn_udot4(w.z, e[c][2], r, false);
+            r = __builtin_amdgcn_udot4(w.w, e[c][3], r, false);
+            accv[c][hh][lb] = r;
+          }
+        }
+      }
+    }
+
+    // 5. online-softmax update (rotated value frame)
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      const float mnew = fmaxf(m[hh], mg[hh]);
+      const float sc = exp2_safe_diff(m[hh], mnew);
+      const float wpg = exp2_safe_diff(mg[hh], mnew);
+      const float ws = wpg * Sv * (1.0f / 65535.0f);
+      const float U0 = (float)(accv[0][hh][1] * 256u + accv[0][hh][0]);
+      const float U1 = (float)(accv[1][hh][1] * 256u + accv[1][hh][0]);
+      o[hh][0] = fmaf(o[hh][0], sc, ws * (U0 - uz[hh]));
+      o[hh][1] = fmaf(o[hh][1], sc, ws * (U1 - uz[hh]));
+      l[hh] = fmaf(l[hh], sc, wpg * psum[hh]);
+      m[hh] = mnew;
+    }
+    wave_lds_sync();
+  }
+  combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, c0, c1);
+}
+
 template <int GQ>
 __device__ void int4_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
   const Geo& g = a.g;
@@ -853,14 +1062,14 @@ __device__ void int4_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
   combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, lane, lane + 64);
 }
 
-template <int GQ, bool DOT16>
+template <int GQ, int SCHEME, bool DOT16>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   __shared__ DecodeLds<GQ> L;
   const int unit = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const Geo& g = a.g;
   const int T = a.seq_lens[b];
   int n_chunks;
-  if (g.scheme == KVQ_INT2_CHANNEL) {
+  if (SCHEME == KVQ_INT2_CHANNEL) {
     const int ng = n_groups_of(T, g.S0, g.W);
     n_chunks = (ng + g.gpc - 1) / g.gpc;
   } else {
@@ -869,7 +1078,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;  // lengths beyond the launch bound are cut
   if (unit > n_chunks) return;
   if (unit == 0) {
-    if (g.scheme == KVQ_INT2_CHANNEL) {
+    if (SCHEME == KVQ_INT2_CHANNEL) {
       band_unit<GQ>(L, a, b, h, T);
     } else {
       // no band: an empty partial
@@ -879,11 +1088,12 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
         part[k] = (k == 0) ? -INFINITY : 0.0f;
       }
     }
-  } else if (g.scheme == KVQ_INT2_CHANNEL) {
+  } else if (SCHEME == KVQ_INT2_CHANNEL) {
     if (DOT16) int2_unit_dot16<GQ>(L, a, b, h, T, unit - 1);
     else int2_unit<GQ>(L, a, b, h, T, unit - 1);
   } else {
-    int4_unit<GQ>(L, a, b, h, T, unit - 1);
+    if (DOT16) int4_unit_dot16<GQ>(L, a, b, h, T, unit - 1);
+    else int4_unit<GQ>(L, a, b, h, T, unit - 1);
   }
 }
 
@@ -994,10 +1204,17 @@ hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
   const Geo& g = a.g;
   if (stages & KVQ_STAGE_QPREP) hipLaunchKernelGGL(qprep_kernel<GQ>, dim3(g.n_kv, g.batch), dim3(128), 0, s, a);
   if (stages & KVQ_STAGE_SPLITK) {
-    if (a.impl == KVQ_DECODE_F32 || g.scheme != KVQ_INT2_CHANNEL)
-      hipLaunchKernelGGL((decode_valu_kernel<GQ, false>), dim3(g.n_units, g.n_kv, g.batch), dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((decode_valu_kernel<GQ, true>), dim3(g.n_units, g.n_kv, g.batch), dim3(kThreads), 0, s, a);
+    const dim3 grid(g.n_units, g.n_kv, g.batch), block(kThreads);
+    // AUTO: the 16-bit integer-dot kernel for INT2, the fp32 kernel for INT4 (faster there: per-token
+    // scales leave the fp32 path no per-group work, and 4-bit codes convert cheaply)
+    const bool dot16 = a.impl == KVQ_DECODE_DOT16 || (a.impl == KVQ_DECODE_AUTO && g.scheme == KVQ_INT2_CHANNEL);
+    if (g.scheme == KVQ_INT2_CHANNEL) {
+      if (dot16) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, false>), grid, block, 0, s, a);
+    } else {
+      if (dot16) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_TOKEN, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_TOKEN, false>), grid, block, 0, s, a);
+    }
   }
   if (stages & KVQ_STAGE_MERGE) hipLaunchKernelGGL(merge_kernel<GQ>, dim3(g.n_kv, g.batch), dim3(kThreads), 0, s, a);
   return hipGetLastError();

@@ -89,9 +89,10 @@ typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
 typedef enum { KVQ_ROT_DENSE = 0, KVQ_ROT_HADAMARD = 1 } kvq_rotation;
 /* Arithmetic of the quantized-token part of the decode (the bf16 band is always fp32):
    F32   - fp32 FMA on the codes, per-group alpha = q~ s and softmax weights exact in fp32;
-   DOT16 - alpha and the group's softmax weights rounded to 16-bit integers (per group and head, scaled
-           to their maximum) and multiplied with the codes on the integer dot-product unit (INT2 only);
-   MFMA  - reserved, not built;  AUTO - DOT16 for INT2, F32 for INT4. */
+   DOT16 - the key-side operand (INT2: alpha = q~ s per group and head; INT4: q~) and the softmax weights
+           (per group or page and head) rounded to 16-bit integers scaled to their maximum, multiplied
+           with the codes on the integer dot-product unit;
+   MFMA  - reserved, not built;  AUTO - DOT16 for INT2, F32 for INT4 (the faster of the two there). */
 typedef enum { KVQ_DECODE_AUTO = 0, KVQ_DECODE_F32 = 1, KVQ_DECODE_MFMA = 2, KVQ_DECODE_DOT16 = 3 } kvq_decode_impl;
 
 /* Static description of one attention layer's cache. */

@@ -142,9 +142,10 @@ def test_one_hip_runtime_in_the_process():
     assert r.stdout.strip().splitlines()[-1] == "1"
 
 
-def test_dot16_decode_is_int2_only():
-    cfg4 = K.make_config(8, 32, scheme=K.INT4_TOKEN, rotation=K.ROT_HADAMARD, n_sink=0, n_recent=0,
-                         clip_k=1.0, clip_v=1.0, decode_impl=K.DECODE_DOT16)
-    assert K.check_config(cfg4) == K.KVQ_EUNSUPPORTED
-    cfg4.decode_impl = K.DECODE_F32
-    assert K.check_config(cfg4) == K.KVQ_OK
+def test_decode_implementations_accepted_for_both_schemes():
+    for scheme, rot, s0, w, ck, cv in ((K.INT2_CHANNEL, K.ROT_DENSE, 4, 128, 0.96, 0.92),
+                                       (K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0)):
+        for impl in (K.DECODE_AUTO, K.DECODE_F32, K.DECODE_DOT16):
+            cfg = K.make_config(8, 32, scheme=scheme, rotation=rot, n_sink=s0, n_recent=w, clip_k=ck, clip_v=cv,
+                                decode_impl=impl)
+            assert K.check_config(cfg) == K.KVQ_OK
