@@ -20,6 +20,10 @@ namespace kvq {
 namespace {
 
 constexpr float kInvSqrt128 = 0.08838834764831845f;
+// Full scale of the 16-bit key-side operand and of the value-side softmax weights in the integer-dot
+// decode: both split into two signed bytes 256 hi + lo, so |x| <= 32639 (hi = (x + 128) >> 8 <= 127).
+constexpr float kAScale = 32639.0f;
+constexpr float kPScale = 32511.0f;
 constexpr int kThreads = 256;
 
 __device__ inline float wave_sum(float v) {
@@ -405,8 +409,14 @@ __device__ inline float seg_reduce(float x, Op op) {
   x = op(x, KVQ_MOVDPP(x, 0x4E));   // quad_perm [2,3,0,1]
   x = op(x, KVQ_MOVDPP(x, 0x141));  // row_half_mirror: i <-> 7-i
   if (N >= 16) x = op(x, KVQ_MOVDPP(x, 0x140));  // row_mirror: i <-> 15-i
-  if (N >= 32) x = op(x, __shfl_xor(x, 16, 64));
-  if (N >= 64) x = op(x, __shfl_xor(x, 32, 64));
+  if (N >= 32) {  // rows 0|1 and 2|3
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  if (N >= 64) {  // halves
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
   return x;
 }
 
@@ -414,6 +424,13 @@ __device__ inline float seg_reduce(float x, Op op) {
 __device__ inline int2 scalar_load_int2(const int2* p) {
   const __attribute__((address_space(4))) int* q = (const __attribute__((address_space(4))) int*)(uintptr_t)p;
   return make_int2(q[0], q[1]);
+}
+
+// Signed 4-way byte dot product with a zero accumulator (VOP3P form: no register to clear first).
+__device__ inline int sdot4_z(uint32_t a, uint32_t b) {
+  int r;
+  asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 template <int GQ>
@@ -435,13 +452,24 @@ __device__ inline void heads_allreduce(const float (&v)[GQ], Op op, int lane, fl
 #pragma unroll
   for (int s = 0; s < LG; ++s) {
     const int bit = 5 - s;
-    const bool up = (lane >> bit) & 1;
     const int half = GQ >> (s + 1);
 #pragma unroll
     for (int i = 0; i < half; ++i) {
-      const float send = up ? cur[i] : cur[half + i];
-      const float keep = up ? cur[half + i] : cur[i];
-      cur[i] = op(keep, xor_exchange(send, bit));
+      if (bit >= 4) {
+        // permlane swap of (cur[i], cur[half + i]) across lane bit `bit`: the first result holds cur[i] of
+        // this lane (bit clear) or cur[half + i] of the partner (bit set), the second the other half; their
+        // combination is head i over the lane pair where the bit is clear, head half + i where it is set
+        const auto r = bit == 5 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(cur[i]),
+                                                                   __float_as_uint(cur[half + i]), false, false)
+                                : __builtin_amdgcn_permlane16_swap(__float_as_uint(cur[i]),
+                                                                   __float_as_uint(cur[half + i]), false, false);
+        cur[i] = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      } else {
+        const bool up = (lane >> bit) & 1;
+        const float send = up ? cur[i] : cur[half + i];
+        const float keep = up ? cur[half + i] : cur[i];
+        cur[i] = op(keep, xor_exchange(send, bit));
+      }
     }
   }
   const float x = seg_reduce<(64 >> LG)>(cur[0], op);
@@ -463,9 +491,10 @@ struct OpAdd {
 //   - alpha_{h,c} = q~_{h,c} s_c is rounded to an integer a_{h,c} = rint(alpha * 32639 / max_c |alpha|)
 //     (per group and head), so that logit_t = A_h (sum_c a_{h,c} code_{t,c} - sum_c a_{h,c} z_c) with
 //     A_h = max|alpha| / 32639; a = 256 hi + lo with signed bytes hi, lo, two signed dot4 per 4 channels.
-//   - p_t = 2^(logit_t - max_group) in (0, 1] is rounded to u_t = rint(65535 p_t), u = 256 hi + lo with
-//     unsigned bytes, two unsigned dot4 per 4 tokens of a channel; the group's output and weight are
-//     2^(max_group - m) / 65535 times s_c (sum_t u_t code_{t,c} - z_c sum_t u_t) and sum_t u_t.
+//   - p_t = 2^(logit_t - max_group) in (0, 1] is rounded to u_t = rint(32511 p_t), u = 256 hi + lo with
+//     signed bytes, two signed dot4 per 4 tokens of a channel; the group's output and weight are
+//     2^(max_group - m) / 32511 times s_c (sum_t u_t code_{t,c} - z_c sum_t u_t) and sum_t u_t.
+//     (Signed dot4 has a tied-accumulator form with no wait state between dependent issues.)
 // Lane roles.  Keys: tokens lane of the group's even and odd page.  Values: channels lane, lane + 64.
 // alpha: lane handles head lane >> (6 - log2 GQ) and 2 GQ consecutive channels of it, so that the per-head
 // maxima and sums are segment reductions.  The integer operands of a group are exchanged through per-wave
@@ -556,7 +585,7 @@ __device__ void int2_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, in
         amx = fmaxf(amx, fabsf(al[i]));
       }
       amx = seg_reduce<LPH>(amx, OpMax());
-      const float inv = amx > 0.0f ? 32639.0f / amx : 0.0f;
+      const float inv = amx > 0.0f ? kAScale / amx : 0.0f;
       int ai[NCH];
       float zs = 0.0f;
 #pragma unroll
@@ -566,7 +595,7 @@ __device__ void int2_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, in
         zs = fmaf((float)ai[i], __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16)), zs);
       }
       zs = seg_reduce<LPH>(zs, OpAdd());
-      const float Ah = amx * (1.0f / 32639.0f);
+      const float Ah = amx * (1.0f / kAScale);
       const float AZh = Ah * zs;
 #pragma unroll
       for (int hh = 0; hh < GQ; ++hh) {
@@ -641,8 +670,7 @@ __device__ void int2_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, in
           if (idx + 1 < 16 * GQ) wk = aword(idx + 1);
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            int r = acc[t][hh][lb];
-            r = __builtin_amdgcn_sdot4((int)w.x, (int)e[t][0], r, false);
+            int r = mw == 0 ? sdot4_z(w.x, e[t][0]) : __builtin_amdgcn_sdot4((int)w.x, (int)e[t][0], acc[t][hh][lb], false);
             r = __builtin_amdgcn_sdot4((int)w.y, (int)e[t][1], r, false);
             r = __builtin_amdgcn_sdot4((int)w.z, (int)e[t][2], r, false);
             r = __builtin_amdgcn_sdot4((int)w.w, (int)e[t][3], r, false);
@@ -668,27 +696,27 @@ __device__ void int2_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, in
       float ps[GQ];
 #pragma unroll
       for (int hh = 0; hh < GQ; ++hh) {
-        // u = floor(65535 p + 0.5): p in (0, 1], u in [0, 65535]
-        const uint32_t u0 = (uint32_t)fmaf(__builtin_amdgcn_exp2f(lg[0][hh] - mg[hh]), 65535.0f, 0.5f);
-        const uint32_t u1 = (uint32_t)fmaf(__builtin_amdgcn_exp2f(lg[1][hh] - mg[hh]), 65535.0f, 0.5f);
+        // u = floor(kPScale p + 0.5): p in (0, 1], u in [0, kPScale]; u = 256 hi + lo with signed bytes
+        const int u0 = (int)fmaf(__builtin_amdgcn_exp2f(lg[0][hh] - mg[hh]), kPScale, 0.5f);
+        const int u1 = (int)fmaf(__builtin_amdgcn_exp2f(lg[1][hh] - mg[hh]), kPScale, 0.5f);
         ps[hh] = (float)(u0 + u1);
         uint8_t* lo = pbytes + hh * 256;
         uint8_t* hi = lo + 128;
         lo[pb0] = (uint8_t)u0;
-        hi[pb0] = (uint8_t)(u0 >> 8);
+        hi[pb0] = (uint8_t)((u0 + 128) >> 8);
         lo[pb1] = (uint8_t)u1;
-        hi[pb1] = (uint8_t)(u1 >> 8);
+        hi[pb1] = (uint8_t)((u1 + 128) >> 8);
       }
       heads_allreduce<GQ>(ps, OpAdd(), lane, Pf);  // integers below 2^24: exact in fp32
     }
     wave_lds_sync();
 
     // 4. value dots: channels c0, c1 against the weights of every head
-    uint32_t accv[2][GQ][2];
+    int accv[2][GQ][2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int hh = 0; hh < GQ; ++hh) accv[c][hh][0] = accv[c][hh][1] = 0u;
+      for (int hh = 0; hh < GQ; ++hh) accv[c][hh][0] = accv[c][hh][1] = 0;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the value codes have landed in LDS
     const uint4 v00 = vst[c0], v01 = vst[64 + c0], v10 = vst[128 + c0], v11 = vst[192 + c0];
     const uint32_t vw[2][2][4] = {{{v00.x, v00.y, v00.z, v00.w}, {v10.x, v10.y, v10.z, v10.w}},
@@ -717,11 +745,11 @@ __device__ void int2_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, in
             if (idx + 1 < 16 * GQ) wv = pword(idx + 1);
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-              uint32_t r = accv[c][hh][lb];
-              r = __builtin_amdgcn_udot4(w.x, e[c][0], r, false);
-              r = __builtin_amdgcn_udot4(w.y, e[c][1], r, false);
-              r = __builtin_amdgcn_udot4(w.z, e[c][2], r, false);
-              r = __builtin_amdgcn_udot4(w.w, e[c][3], r, false);
+              const int first = pp == 0 && gw == 0;
+              int r = first ? sdot4_z(w.x, e[c][0]) : __builtin_amdgcn_sdot4((int)w.x, (int)e[c][0], accv[c][hh][lb], false);
+              r = __builtin_amdgcn_sdot4((int)w.y, (int)e[c][1], r, false);
+              r = __builtin_amdgcn_sdot4((int)w.z, (int)e[c][2], r, false);
+              r = __builtin_amdgcn_sdot4((int)w.w, (int)e[c][3], r, false);
               accv[c][hh][lb] = r;
             }
           }
@@ -734,9 +762,9 @@ __device__ void int2_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, in
     for (int hh = 0; hh < GQ; ++hh) {
       const float mnew = fmaxf(m[hh], mg[hh]);
       const float sc = exp2_safe_diff(m[hh], mnew);
-      const float wg = __builtin_amdgcn_exp2f(mg[hh] - mnew) * (1.0f / 65535.0f);
-      const float U0 = (float)(accv[0][hh][1] * 256u + accv[0][hh][0]);
-      const float U1 = (float)(accv[1][hh][1] * 256u + accv[1][hh][0]);
+      const float wg = __builtin_amdgcn_exp2f(mg[hh] - mnew) * (1.0f / kPScale);
+      const float U0 = (float)(accv[0][hh][1] * 256 + accv[0][hh][0]);
+      const float U1 = (float)(accv[1][hh][1] * 256 + accv[1][hh][0]);
       o[hh][0] = fmaf(o[hh][0], sc, (wg * sv0) * fmaf(-zv0, Pf[hh], U0));
       o[hh][1] = fmaf(o[hh][1], sc, (wg * sv1) * fmaf(-zv1, Pf[hh], U1));
       l[hh] = fmaf(l[hh], sc, wg * Pf[hh]);
@@ -793,7 +821,7 @@ __device__ void int4_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, in
       amx = fmaxf(amx, fabsf(qa[i]));
     }
     amx = seg_reduce<LPH>(amx, OpMax());
-    const float inv = amx > 0.0f ? 32639.0f / amx : 0.0f;
+    const float inv = amx > 0.0f ? kAScale / amx : 0.0f;
     float qsum = 0.0f;
     uint8_t* lo = abytes + ah * 256;
     uint8_t* hi = lo + 128;
@@ -807,7 +835,7 @@ __device__ void int4_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, in
       hi[off] = (uint8_t)((ai + 128) >> 8);
     }
     qsum = seg_reduce<LPH>(qsum, OpAdd());  // integers of magnitude < 2^22: exact
-    const float Ah = amx * (1.0f / 32639.0f);
+    const float Ah = amx * (1.0f / kAScale);
 #pragma unroll
     for (int hh = 0; hh < GQ; ++hh) {
       A[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Ah), hh * LPH));
