@@ -84,47 +84,56 @@ __device__ inline uint32_t wave_sum_u32(uint32_t x) {
 // q * log2e/sqrt(128) for the bf16 band (original frame).
 // ---------------------------------------------------------------------------------------------
 template <int GQ>
-__global__ __launch_bounds__(128) void qprep_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(512) void qprep_kernel(DecodeArgs a) {
   __shared__ float qs[GQ][D];
-  const int h = blockIdx.x, b = blockIdx.y, j = threadIdx.x;
+  __shared__ float part[4][GQ][D];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int j = tid & (D - 1), qtr = tid >> 7;  // column j, quarter qtr of the 128 input channels
   const long long base = ((long long)b * a.g.n_q + h * GQ) * D;
   const float scale = LOG2E * kInvSqrt128;
-#pragma unroll
-  for (int hh = 0; hh < GQ; ++hh) {
-    const float qv = a.q_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[base + hh * D + j])
-                              : static_cast<const float*>(a.q)[base + hh * D + j];
-    a.qband[base + hh * D + j] = qv * scale;
-    qs[hh][j] = a.g.rotation == KVQ_ROT_DENSE ? qv : qv * a.rot_k[j];
+  for (int e = tid; e < GQ * D; e += 512) {
+    const int hh = e / D, c = e % D;
+    const float qv = a.q_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[base + e])
+                              : static_cast<const float*>(a.q)[base + e];
+    a.qband[base + e] = qv * scale;
+    qs[hh][c] = a.g.rotation == KVQ_ROT_DENSE ? qv : qv * a.rot_k[c];
   }
   __syncthreads();
-  float r[GQ];
   if (a.g.rotation == KVQ_ROT_DENSE) {
+    float r[GQ];
 #pragma unroll
     for (int hh = 0; hh < GQ; ++hh) r[hh] = 0.0f;
-#pragma unroll 16
-    for (int i = 0; i < D; ++i) {
-      const float rk = a.rot_k[i * D + j];
+    float rk[32];
 #pragma unroll
-      for (int hh = 0; hh < GQ; ++hh) r[hh] = fmaf(qs[hh][i], rk, r[hh]);
+    for (int i = 0; i < 32; ++i) rk[i] = a.rot_k[(qtr * 32 + i) * D + j];
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) r[hh] = fmaf(qs[hh][qtr * 32 + i], rk[i], r[hh]);
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) part[qtr][hh][j] = r[hh];
+    __syncthreads();
+    for (int e = tid; e < GQ * D; e += 512) {
+      const int hh = e / D, c = e % D;
+      a.qrot[base + e] = ((part[0][hh][c] + part[1][hh][c]) + (part[2][hh][c] + part[3][hh][c])) * scale;
     }
   } else {
+    // randomized Hadamard: FWHT in LDS, one element per thread
     for (int hb = 1; hb < D; hb <<= 1) {
-      float x[GQ];
-#pragma unroll
-      for (int hh = 0; hh < GQ; ++hh) {
-        const float u = qs[hh][j], v = qs[hh][j ^ hb];
-        x[hh] = (j & hb) ? (v - u) : (u + v);
+      float x[GQ / 4 + 1];
+      int n = 0;
+      for (int e = tid; e < GQ * D; e += 512) {
+        const int hh = e / D, c = e % D;
+        const float u = qs[hh][c], v = qs[hh][c ^ hb];
+        x[n++] = (c & hb) ? (v - u) : (u + v);
       }
       __syncthreads();
-#pragma unroll
-      for (int hh = 0; hh < GQ; ++hh) qs[hh][j] = x[hh];
+      n = 0;
+      for (int e = tid; e < GQ * D; e += 512) qs[e / D][e % D] = x[n++];
       __syncthreads();
     }
-#pragma unroll
-    for (int hh = 0; hh < GQ; ++hh) r[hh] = qs[hh][j] * kInvSqrt128;
+    for (int e = tid; e < GQ * D; e += 512) a.qrot[base + e] = qs[e / D][e % D] * kInvSqrt128 * scale;
   }
-#pragma unroll
-  for (int hh = 0; hh < GQ; ++hh) a.qrot[base + hh * D + j] = r[hh] * scale;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1230,7 +1239,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
 template <int GQ>
 hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
   const Geo& g = a.g;
-  if (stages & KVQ_STAGE_QPREP) hipLaunchKernelGGL(qprep_kernel<GQ>, dim3(g.n_kv, g.batch), dim3(128), 0, s, a);
+  if (stages & KVQ_STAGE_QPREP) hipLaunchKernelGGL(qprep_kernel<GQ>, dim3(g.n_kv, g.batch), dim3(512), 0, s, a);
   if (stages & KVQ_STAGE_SPLITK) {
     const dim3 grid(g.n_units, g.n_kv, g.batch), block(kThreads);
     // AUTO: the 16-bit integer-dot kernel for INT2, the fp32 kernel for INT4 (faster there: per-token
