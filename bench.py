@@ -35,7 +35,6 @@ def parse():
     ap.add_argument("--workload", default="batch32_32k")
     ap.add_argument("--impl", default="auto", choices=["auto", "f32", "dot16"])
     ap.add_argument("--split", type=int, default=0, help="quantized tokens per decode work-group (0 = auto)")
-    ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--cpu-pairs", type=int, default=2, help="distinct (seq, kv head) pairs in the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time of the CPU-baseline sample")
@@ -200,56 +199,56 @@ def main():
     out = torch.empty((B, n_q, 128), dtype=torch.float32, device=dev)
     ws = K.workspace_for(cfg, B, T_end, dev)
 
-    def step(i):
+    # one step = the append write, then the decode's three kernels (query prep, split-K partials, merge)
+    # launched one by one so that HIP events on their stream (torch's current stream, which the binding
+    # passes to the library) bracket each kernel inside the timed steps
+    names = ("qprep", "splitk", "merge")
+    stages = (K.STAGE_QPREP, K.STAGE_SPLITK, K.STAGE_MERGE)
+
+    def step(i, ev=None):
         K.kv_rotate_quant_write(cache, ks[i], vs[i], cu1, 1)
-        K.kv_decode_attn(cache, qs[i], out, T_end, ws)
+        for n, st in enumerate(stages):
+            if ev is not None:
+                ev[n][0].record()
+            K.kv_decode_attn_stages(cache, qs[i], out, T_end, ws, st)
+            if ev is not None:
+                ev[n][1].record()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in stages]
+           for _ in range(args.steps)]
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     lens_before = cache.seq_lens.cpu().numpy().astype(np.int64)
     torch.cuda.synchronize()
     e0.record()
-    for i in range(args.warmup, n_steps):
-        step(i)
+    for n, i in enumerate(range(args.warmup, n_steps)):
+        step(i, evs[n])
     e1.record()
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
     log(f"[bench] {args.steps} timed steps: {ms_step:.4f} ms/step")
     assert int(cache.seq_lens.min().item()) == T_end
 
-    # average algorithmic bytes over the timed steps (lengths after each append)
+    # algorithmic bytes of each timed step (lengths after that step's append)
     kv_sum = qo_sum = 0
-    for s in range(1, args.steps + 1):
-        kv_b, qo_b = decode_bytes(wl, lens_before + s, wl.n_sink, wl.n_recent)
+    for s_ in range(1, args.steps + 1):
+        kv_b, qo_b = decode_bytes(wl, lens_before + s_, wl.n_sink, wl.n_recent)
         kv_sum += kv_b
         qo_sum += qo_b
     step_bytes = (kv_sum + qo_sum) / args.steps
 
-    # each kernel of the step alone, same launch configuration, HIP events around every launch on the
-    # stream it runs on (torch's current stream, which the binding passes to the library)
-    def time_launches(fn, reps):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for e0, e1 in ev:
-            e0.record()
-            fn()
-            e1.record()
-        torch.cuda.synchronize()
-        return sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
-
-    K.kv_decode_attn_stages(cache, qs[-1], out, T_end, ws, K.STAGE_QPREP)
-    stage_us = {}
-    for name, st in (("qprep", K.STAGE_QPREP), ("splitk", K.STAGE_SPLITK), ("merge", K.STAGE_MERGE)):
-        stage_us[name] = round(1e3 * time_launches(
-            lambda st=st: K.kv_decode_attn_stages(cache, qs[-1], out, T_end, ws, st), args.kernel_reps), 2)
+    # the split-K kernel inside the timed steps: its launches' average duration, and the bytes it reads:
+    # KV bytes of the step + the fp32 rotated and band queries
+    stage_us = {n: round(1e3 * sum(ev[k][0].elapsed_time(ev[k][1]) for ev in evs) / args.steps, 2)
+                for k, n in enumerate(names)}
     kern_ms = stage_us["splitk"] * 1e-3
-    kv_b, _ = decode_bytes(wl, [T_end] * B, wl.n_sink, wl.n_recent)
-    kern_bytes = kv_b + B * n_q * 128 * 4 * 2  # + the fp32 rotated and band queries it reads
+    kern_bytes = int(round(kv_sum / args.steps)) + B * n_q * 128 * 4 * 2
     achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
-    log(f"[bench] split-K kernel {kern_ms * 1e3:.1f} us, {achieved:.0f} GB/s")
+    log(f"[bench] split-K kernel {kern_ms * 1e3:.1f} us, {achieved:.0f} GB/s; kernels {stage_us}")
 
     traffic = read_traffic(wl.name)
 
