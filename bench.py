@@ -1,14 +1,15 @@
 #!/usr/bin/env python3
-"""Decode-step benchmark on one MI355X: batch 32, 32k context, 32 q / 8 kv heads, INT2 per-channel cache.
+"""Decode-step benchmark on one MI355X.  Default workload: batch 32, 32k context, 32 q / 8 kv heads,
+INT2 per-channel cache (`--workload` runs any workload of `synth.WORKLOADS` the same way).
 
 One step = append one token per sequence (rotate/clip/quantize write, with group demotion when a
-128-token group completes) + one decode attention (query rotation, split-K partials over the INT2
+128-token group completes) + one decode attention (query rotation, split-K partials over the quantized
 pages and the bf16 band, merge + un-rotation).  Inputs are resident in HBM before timing.
 
 Prints ONE JSON line.  `value` is KV GB/s of the whole step: the decode's algorithmic bytes (codes,
 scales/zeros, bf16 band, query, output) per step / step time.  `roofline` is for the split-K decode
-kernel alone, timed with HIP events on the stream it runs on.  `cpu_baseline` times the CPU oracle's
-read side on a bounded sample of the same workload.
+kernel alone, timed with HIP events around its launches inside the timed steps, on the stream it runs
+on.  `cpu_baseline` times the CPU oracle's read side on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -74,20 +75,25 @@ def read_traffic(workload):
 
 
 def decode_bytes(wl, lens, S0, W):
-    """Algorithmic bytes one decode step reads/writes: INT2 codes + bf16 scale/zero of every group
-    (72 B per token and kv head), bf16 band tokens (512 B), query (bf16) and output (fp32)."""
+    """Algorithmic bytes one decode step reads/writes.  INT2: codes + bf16 scale/zero of every group
+    (72 B per token and kv head) and bf16 band tokens (512 B); INT4: codes + bf16 scale/zero of every
+    token (136 B per token and kv head).  Plus the query (bf16) and the output (fp32)."""
     kv = 0
     for T in lens:
-        ng = max(0, (T - S0 - W) // 128)
-        kv += wl.n_kv_heads * (ng * 128 * 72 + (T - 128 * ng) * 512)
+        if wl.scheme == "int2_channel":
+            ng = max(0, (T - S0 - W) // 128)
+            kv += wl.n_kv_heads * (ng * 128 * 72 + (T - 128 * ng) * 512)
+        else:
+            kv += wl.n_kv_heads * T * 136
     qo = len(lens) * wl.n_q_heads * 128 * (2 + 4)
     return kv, qo
 
 
 def cpu_baseline(wl, args, T, rk, rv):
-    """Oracle read side (dequantize, inverse-rotate, fp64 attention) with one BLAS thread on a few
-    (seq, kv head) pairs of the workload, repeated round-robin until about --cpu-seconds of timed
-    oracle work have run.  The oracle's cache state of each pair is built once, untimed."""
+    """Oracle read side (dequantize, x^.R^T, fp64 attention) with one BLAS thread on a few (seq, kv head)
+    pairs of the workload at length T, repeated round-robin until about --cpu-seconds of timed oracle
+    work have run.  The oracle's cache state of each pair is built once, untimed."""
+    import numpy as np
     import oracle as O
     import synth
     from threadpoolctl import threadpool_limits
@@ -95,21 +101,32 @@ def cpu_baseline(wl, args, T, rk, rv):
     total_s = 0.0
     total_bytes = 0
     runs = 0
+    int2 = wl.scheme == "int2_channel"
     with threadpool_limits(limits=1):
         states = []
         for n in range(max(1, args.cpu_pairs)):
             b, h = n % wl.batch, (3 * n + 1) % wl.n_kv_heads
             k = synth.kv_tokens(wl, b, 0, T, "k")[:, h].copy()
             v = synth.kv_tokens(wl, b, 0, T, "v")[:, h].copy()
-            states.append((b, h, O.int2_state(k, v, T, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v, rk, rv)))
+            if int2:
+                st = O.int2_state(k, v, T, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v, rk, rv)
+            else:
+                st = O.int4_state(k, v, T, rk.astype(np.int8), rv.astype(np.int8))
+            states.append((b, h, st))
         while total_s < args.cpu_seconds:
             b, h, st = states[runs % len(states)]
             t0 = time.perf_counter()
-            Kh, Vh = O.int2_keys_values(st, rk, rv)
+            if int2:
+                Kh, Vh = O.int2_keys_values(st, rk, rv)
+            else:
+                Kh, Vh = O.int4_keys_values(st, rk.astype(np.int8), rv.astype(np.int8))
             O.attend(O.query_values(q[b, h * wl.gq:(h + 1) * wl.gq]), Kh, Vh)
             total_s += time.perf_counter() - t0
-            ng = st["n_groups"]
-            total_bytes += ng * 128 * 72 + (T - 128 * ng) * 512 + wl.gq * 128 * 6
+            if int2:
+                ng = st["n_groups"]
+                total_bytes += ng * 128 * 72 + (T - 128 * ng) * 512 + wl.gq * 128 * 6
+            else:
+                total_bytes += T * 136 + wl.gq * 128 * 6
             runs += 1
     return {
         "value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
@@ -150,25 +167,34 @@ def main():
     import synth
 
     wl = synth.WORKLOADS[args.workload]
-    assert wl.scheme == "int2_channel", "the headline bench is the INT2 workload"
+    int2 = wl.scheme == "int2_channel"
     dev = "cuda"
     torch.cuda.set_device(0)
     B, n_kv, n_q = wl.batch, wl.n_kv_heads, wl.n_q_heads
     n_steps = args.warmup + args.steps
-    T_end = wl.seq_len
-    T_start = T_end - n_steps
+    lens_end = synth.seq_lens(wl).astype(np.int64)          # lengths after the last timed step
+    lens_start = lens_end - n_steps
+    T_end = int(lens_end.max())
     impl = {"auto": K.DECODE_AUTO, "f32": K.DECODE_F32, "dot16": K.DECODE_DOT16}[args.impl]
-    cfg = K.make_config(n_kv, n_q, K.INT2_CHANNEL, K.ROT_DENSE, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v,
-                        args.split, impl)
-    rk = K.build_oscar_rotation(synth.rotation_gaussian(wl, "k")).astype(np.float32)
-    rv = K.build_oscar_rotation(synth.rotation_gaussian(wl, "v")).astype(np.float32)
+    split = args.split if args.split else (wl.split_tokens if wl.name == "long_b4_131k" else 0)
+    if int2:
+        cfg = K.make_config(n_kv, n_q, K.INT2_CHANNEL, K.ROT_DENSE, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v,
+                            split, impl)
+        rk = K.build_oscar_rotation(synth.rotation_gaussian(wl, "k")).astype(np.float32)
+        rv = K.build_oscar_rotation(synth.rotation_gaussian(wl, "v")).astype(np.float32)
+    else:
+        cfg = K.make_config(n_kv, n_q, K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0, split, impl)
+        rk = synth.sign_vector(wl, "k").astype(np.float32)
+        rv = synth.sign_vector(wl, "v").astype(np.float32)
     max_pages = K.pages_for_len(cfg, T_end)
     pt, n_pool = synth.page_table(wl, max_pages)
     cache = K.allocate_cache(cfg, B, torch.from_numpy(pt), torch.from_numpy(rk), torch.from_numpy(rv),
                              n_pages=n_pool, device=dev)
-    log(f"[bench] {wl.name}: B={B} T={T_start}->{T_end} heads {n_q}/{n_kv}; pages {n_pool} x {K.page_bytes(cfg)} B")
+    log(f"[bench] {wl.name}: B={B} T={int(lens_start.min())}..{T_end} heads {n_q}/{n_kv}; "
+        f"pages {n_pool} x {K.page_bytes(cfg)} B")
 
-    # prefill with the workload's recipe (N(0,1) x channel gains, bf16), generated on the device
+    # prefill with the workload's recipe (N(0,1) x channel gains, bf16), generated on the device, in
+    # chunks of at most 8192 tokens per sequence (the prefill chunk of the INT4 workload)
     gen = torch.Generator(device=dev)
     gen.manual_seed(wl.seed)
     gk = torch.from_numpy(synth.channel_gain(wl, "k")).to(dev)
@@ -180,15 +206,21 @@ def main():
 
     t0 = time.perf_counter()
     per_call = 4
+    chunk = 8192 if not int2 else int(lens_start.max())
     for b0 in range(0, B, per_call):
-        nb = min(per_call, B - b0)
-        counts = np.zeros(B, dtype=np.int64)
-        counts[b0:b0 + nb] = T_start
-        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev)
-        k = draw(nb * T_start, gk)
-        v = draw(nb * T_start, gv)
-        K.kv_rotate_quant_write(cache, k, v, cu, T_start)
-        del k, v
+        sel = slice(b0, min(B, b0 + per_call))
+        done = np.zeros(B, dtype=np.int64)
+        while True:
+            counts = np.zeros(B, dtype=np.int64)
+            counts[sel] = np.minimum(lens_start[sel] - done[sel], chunk)
+            if counts.sum() == 0:
+                break
+            cu = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev)
+            k = draw(int(counts.sum()), gk)
+            v = draw(int(counts.sum()), gv)
+            K.kv_rotate_quant_write(cache, k, v, cu, int(counts.max()))
+            done += counts
+            del k, v
     torch.cuda.synchronize()
     log(f"[bench] prefill written in {time.perf_counter() - t0:.1f} s")
 
@@ -231,7 +263,7 @@ def main():
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
     log(f"[bench] {args.steps} timed steps: {ms_step:.4f} ms/step")
-    assert int(cache.seq_lens.min().item()) == T_end
+    assert np.array_equal(cache.seq_lens.cpu().numpy().astype(np.int64), lens_end)
 
     # algorithmic bytes of each timed step (lengths after that step's append)
     kv_sum = qo_sum = 0
@@ -265,14 +297,18 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "batch": B, "ctx": T_end, "n_q_heads": n_q, "n_kv_heads": n_kv,
-                   "head_dim": 128, "scheme": "int2 per-channel, 128-token groups, bf16 scale/zero",
-                   "sink_recent": [wl.n_sink, wl.n_recent], "page_tokens": 64, "split_tokens": args.split,
+        "config": {"workload": wl.name, "batch": B, "ctx": T_end,
+                   "ctx_range": [int(lens_end.min()), int(lens_end.max())], "n_q_heads": n_q, "n_kv_heads": n_kv,
+                   "head_dim": 128,
+                   "scheme": ("int2 per-channel, 128-token groups, bf16 scale/zero" if int2 else
+                              "int4 per-token, bf16 scale/zero, randomized Hadamard (block 128)"),
+                   "sink_recent": [wl.n_sink, wl.n_recent], "page_tokens": 64, "split_tokens": split,
                    "decode_impl": args.impl, "step": "append 1 token/seq (write) + decode attention"},
         "steps_per_s": round(1000.0 / ms_step, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "split-K decode (INT2 pages + bf16 band)", "kernel_us": round(kern_ms * 1e3, 2),
+                     "kernel": ("split-K decode (INT2 pages + bf16 band)" if int2 else "split-K decode (INT4 pages)"),
+                     "kernel_us": round(kern_ms * 1e3, 2),
                      "bytes_per_launch": kern_bytes},
         "decode_kernels_us": stage_us,
     }

@@ -1135,16 +1135,22 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Merge: combine the quantized chunks (rotated frame), un-rotate once by R_V^T, combine with the
-// band partial (original frame), normalize.  One work-group per (seq, kv head) covers its GQ heads.
+// Merge ([OSCAR] §3.4.5 step 4, the second kernel of the split decode; [NOVA] App. B.5): one work-group
+// per (q head, seq).  The chunk partials (rotated value frame) are combined with their softmax weights
+// 2^(m_u - M), the result is un-rotated once by R_V^T, combined with the band partial (original frame)
+// and normalized.  Weights are computed once per chunk; the weighted sum over chunks spreads
+// (channel quad, chunk slice) over the 256 threads so that the partials' loads are all in flight.
 // ---------------------------------------------------------------------------------------------
+constexpr int kMergeSlices = 8;  // chunk slices of the weighted sum (threads = 32 channel quads x 8 slices)
+
 template <int GQ>
 __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
-  __shared__ float ob[GQ][D];          // merged rotated-frame numerators
-  __shared__ float un[GQ][2][D];       // un-rotation partial sums (two halves of c)
-  __shared__ float sM[GQ], sL[GQ];
+  __shared__ float red[kThreads / 64];
+  __shared__ float4 osum[kMergeSlices][D / 4];
+  __shared__ float ob[D];
+  __shared__ float un[2][D];
   const Geo& g = a.g;
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.seq_lens[b];
   int n_chunks;
   if (g.scheme == KVQ_INT2_CHANNEL) {
@@ -1154,85 +1160,100 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
     n_chunks = ((T + PAGE - 1) / PAGE + g.gpc - 1) / g.gpc;
   }
   if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;
+  const long long qi = (long long)b * g.n_q + hq;
+  const float* base = a.partials + qi * g.n_units * PART_STRIDE;  // unit 0: band, 1..n_chunks: chunks
   const bool dense = g.rotation == KVQ_ROT_DENSE;
-  // merge the quantized chunks per head
-  for (int e = tid; e < GQ * D; e += kThreads) {
-    const int hh = e / D, c = e % D;
-    const float* base = a.partials + ((long long)b * g.n_q + h * GQ + hh) * g.n_units * PART_STRIDE;
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int u = 1; u <= n_chunks; ++u) M = fmaxf(M, base[u * PART_STRIDE]);
-    float acc = 0.0f, lsum = 0.0f;
-#pragma unroll 8
-    for (int u = 1; u <= n_chunks; ++u) {
-      const float sc = exp2_safe_diff(base[u * PART_STRIDE], M);
-      acc += sc * base[u * PART_STRIDE + 2 + c];
-      lsum += sc * base[u * PART_STRIDE + 1];
+
+  // 1. M = max over chunks of m_u (block reduction)
+  float mx = -INFINITY;
+  for (int u = 1 + tid; u <= n_chunks; u += kThreads) mx = fmaxf(mx, base[u * PART_STRIDE]);
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) M = fmaxf(M, red[w]);
+  __syncthreads();
+  // 2. L = sum_u 2^(m_u - M) l_u
+  float ls = 0.0f;
+  for (int u = 1 + tid; u <= n_chunks; u += kThreads)
+    ls = fmaf(exp2_safe_diff(base[u * PART_STRIDE], M), base[u * PART_STRIDE + 1], ls);
+  ls = wave_sum(ls);
+  if (lane == 0) red[wave] = ls;
+  __syncthreads();
+  float Lq = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) Lq += red[w];
+  // 3. o[c] = sum_u 2^(m_u - M) o_u[c]: thread (channel quad cq, slice sl) sums chunks u = sl + 1 + 8k
+  {
+    const int cq = tid & (D / 4 - 1), sl = tid / (D / 4);
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 4
+    for (int u = 1 + sl; u <= n_chunks; u += kMergeSlices) {
+      const float w = exp2_safe_diff(base[u * PART_STRIDE], M);
+      const float* o = base + u * PART_STRIDE + 2 + 4 * cq;  // 8-byte aligned: two float2 loads
+      const float2 o01 = *reinterpret_cast<const float2*>(o), o23 = *reinterpret_cast<const float2*>(o + 2);
+      acc.x = fmaf(w, o01.x, acc.x);
+      acc.y = fmaf(w, o01.y, acc.y);
+      acc.z = fmaf(w, o23.x, acc.z);
+      acc.w = fmaf(w, o23.y, acc.w);
     }
-    ob[hh][c] = acc;
-    if (c == 0) {
-      sM[hh] = M;
-      sL[hh] = lsum;
-    }
+    osum[sl][cq] = acc;
   }
   __syncthreads();
-  if (dense) {
-    // o_j = sum_c ob[c] R_V[j][c]; thread (half, j) sums c in [64*half, 64*half+64) of row j of R_V
-    const int j = tid & (D - 1), half = tid >> 7;
-    const float4* row = reinterpret_cast<const float4*>(a.rot_v + j * D + half * 64);
-    float4 r[16];
+  if (tid < D) {
+    const int cq = tid >> 2, k = tid & 3;
+    float v = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) r[i] = row[i];
-    float acc[GQ];
-#pragma unroll
-    for (int hh = 0; hh < GQ; ++hh) {
-      const float* x = &ob[hh][half * 64];
-      float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s0 = fmaf(x[4 * i], r[i].x, s0);
-        s1 = fmaf(x[4 * i + 1], r[i].y, s1);
-        s0 = fmaf(x[4 * i + 2], r[i].z, s0);
-        s1 = fmaf(x[4 * i + 3], r[i].w, s1);
-      }
-      acc[hh] = s0 + s1;
+    for (int sl = 0; sl < kMergeSlices; ++sl) {
+      const float4 t = osum[sl][cq];
+      v += k == 0 ? t.x : k == 1 ? t.y : k == 2 ? t.z : t.w;
     }
+    ob[tid] = v;
+  }
+  __syncthreads();
+  // 4. un-rotate: o_j = sum_c ob[c] R_V[j][c] (dense), or the randomized Hadamard's inverse
+  const int j = tid & (D - 1), half = tid >> 7;
+  if (dense) {
+    const float4* row = reinterpret_cast<const float4*>(a.rot_v + j * D + half * 64);
+    float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-    for (int hh = 0; hh < GQ; ++hh) un[hh][half][j] = acc[hh];
+    for (int i = 0; i < 16; ++i) {
+      const float4 r = row[i];
+      s0 = fmaf(ob[half * 64 + 4 * i], r.x, s0);
+      s1 = fmaf(ob[half * 64 + 4 * i + 1], r.y, s1);
+      s0 = fmaf(ob[half * 64 + 4 * i + 2], r.z, s0);
+      s1 = fmaf(ob[half * 64 + 4 * i + 3], r.w, s1);
+    }
+    un[half][j] = s0 + s1;
     __syncthreads();
   } else {
-    // o = (ob H) * sign / sqrt(128), FWHT in LDS on each head's 128 values
-    for (int hh2 = 1; hh2 < D; hh2 <<= 1) {
-      float x[GQ / 2 + 1];
-      int n = 0;
-      for (int e = tid; e < GQ * D; e += kThreads) x[n++] = (e % D & hh2) ? (ob[e / D][(e % D) ^ hh2] - ob[e / D][e % D])
-                                                                          : (ob[e / D][e % D] + ob[e / D][(e % D) ^ hh2]);
+    // (ob H) * sign / sqrt(128): FWHT in LDS
+    for (int hb = 1; hb < D; hb <<= 1) {
+      float x = 0.0f;
+      if (tid < D) x = (tid & hb) ? (ob[tid ^ hb] - ob[tid]) : (ob[tid] + ob[tid ^ hb]);
       __syncthreads();
-      n = 0;
-      for (int e = tid; e < GQ * D; e += kThreads) ob[e / D][e % D] = x[n++];
+      if (tid < D) ob[tid] = x;
       __syncthreads();
     }
-    for (int e = tid; e < GQ * D; e += kThreads) {
-      un[e / D][0][e % D] = ob[e / D][e % D] * a.rot_v[e % D] * kInvSqrt128;
-      un[e / D][1][e % D] = 0.0f;
+    if (tid < D) {
+      un[0][tid] = ob[tid] * a.rot_v[tid] * kInvSqrt128;
+      un[1][tid] = 0.0f;
     }
     __syncthreads();
   }
-  for (int e = tid; e < GQ * D; e += kThreads) {
-    const int hh = e / D, j = e % D;
-    const long long qi = (long long)b * g.n_q + h * GQ + hh;
-    const float* bp = a.partials + qi * g.n_units * PART_STRIDE;  // unit 0: band
-    const float mb = (T > 0) ? bp[0] : -INFINITY;
-    const float M = sM[hh];
+  // 5. combine with the band partial (unit 0, original frame) and normalize
+  if (tid < D) {
+    const float mb = (T > 0) ? base[0] : -INFINITY;
     const float Mf = fmaxf(M, mb);
     float res = 0.0f;
     if (Mf != -INFINITY) {
       const float si = exp2_safe_diff(M, Mf), sb = exp2_safe_diff(mb, Mf);
-      const float num = (un[hh][0][j] + un[hh][1][j]) * si + (mb == -INFINITY ? 0.0f : bp[2 + j] * sb);
-      const float den = sL[hh] * si + (mb == -INFINITY ? 0.0f : bp[1] * sb);
+      const float num = (un[0][tid] + un[1][tid]) * si + (mb == -INFINITY ? 0.0f : base[2 + tid] * sb);
+      const float den = Lq * si + (mb == -INFINITY ? 0.0f : base[1] * sb);
       res = num / den;
     }
-    a.out[qi * D + j] = res;
+    a.out[qi * D + tid] = res;
   }
 }
 
@@ -1253,7 +1274,7 @@ hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
       else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_TOKEN, false>), grid, block, 0, s, a);
     }
   }
-  if (stages & KVQ_STAGE_MERGE) hipLaunchKernelGGL(merge_kernel<GQ>, dim3(g.n_kv, g.batch), dim3(kThreads), 0, s, a);
+  if (stages & KVQ_STAGE_MERGE) hipLaunchKernelGGL(merge_kernel<GQ>, dim3(g.n_q, g.batch), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
