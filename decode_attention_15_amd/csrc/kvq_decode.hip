@@ -239,9 +239,12 @@ __device__ void band_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
     for (int hh = 0; hh < GQ; ++hh) lg[hh] = 0.0f;
     if (valid) {
       const uint4* kr = reinterpret_cast<const uint4*>(band + (long long)slot_of(k) * 256);
-#pragma unroll 1
+      uint4 kw[16];  // the token's whole key row in flight at once
+#pragma unroll
+      for (int v8 = 0; v8 < 16; ++v8) kw[v8] = kr[v8];
+#pragma unroll
       for (int v8 = 0; v8 < 16; ++v8) {
-        const uint4 w = kr[v8];
+        const uint4 w = kw[v8];
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int p2 = 0; p2 < 4; ++p2) {
@@ -263,15 +266,24 @@ __device__ void band_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
     }
     wave_lds_sync();
     const int nk = (nb - blk * 64) < 64 ? (nb - blk * 64) : 64;
-    for (int kk = 0; kk < nk; ++kk) {
-      const uint32_t vv = *reinterpret_cast<const uint32_t*>(band + (long long)slot_of(blk * 64 + kk) * 256 + 128 +
-                                                            2 * lane);
-      const float v0 = __uint_as_float(vv << 16), v1 = __uint_as_float(vv & 0xffff0000u);
+    // value rows 8 tokens at a time, their loads issued together (channels 2 lane, 2 lane + 1)
+    for (int k8 = 0; k8 < nk; k8 += 8) {
+      uint32_t vv[8];
 #pragma unroll
-      for (int hh = 0; hh < GQ; ++hh) {
-        const float p = L.f.p[wave][hh][kk];
-        o[hh][0] += p * v0;
-        o[hh][1] += p * v1;
+      for (int q = 0; q < 8; ++q) {
+        const int kk = k8 + q < nk ? k8 + q : nk - 1;
+        vv[q] = *reinterpret_cast<const uint32_t*>(band + (long long)slot_of(blk * 64 + kk) * 256 + 128 + 2 * lane);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (k8 + q >= nk) break;
+        const float v0 = __uint_as_float(vv[q] << 16), v1 = __uint_as_float(vv[q] & 0xffff0000u);
+#pragma unroll
+        for (int hh = 0; hh < GQ; ++hh) {
+          const float p = L.f.p[wave][hh][k8 + q];
+          o[hh][0] += p * v0;
+          o[hh][1] += p * v1;
+        }
       }
     }
     wave_lds_sync();
