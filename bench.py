@@ -34,7 +34,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batch32_32k")
-    ap.add_argument("--impl", default="auto", choices=["auto", "f32", "dot16"])
+    ap.add_argument("--impl", default="auto", choices=["auto", "f32", "dot16", "dot8"])
     ap.add_argument("--split", type=int, default=0, help="quantized tokens per decode work-group (0 = auto)")
     ap.add_argument("--cpu-pairs", type=int, default=2, help="distinct (seq, kv head) pairs in the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -175,7 +175,7 @@ def main():
     lens_end = synth.seq_lens(wl).astype(np.int64)          # lengths after the last timed step
     lens_start = lens_end - n_steps
     T_end = int(lens_end.max())
-    impl = {"auto": K.DECODE_AUTO, "f32": K.DECODE_F32, "dot16": K.DECODE_DOT16}[args.impl]
+    impl = {"auto": K.DECODE_AUTO, "f32": K.DECODE_F32, "dot16": K.DECODE_DOT16, "dot8": K.DECODE_DOT8}[args.impl]
     split = args.split if args.split else (wl.split_tokens if wl.name == "long_b4_131k" else 0)
     if int2:
         cfg = K.make_config(n_kv, n_q, K.INT2_CHANNEL, K.ROT_DENSE, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v,

@@ -29,9 +29,10 @@ int check_config(const kvq_config* c) {
   const int unit = c->scheme == KVQ_INT2_CHANNEL ? GROUP : PAGE;
   if (c->split_tokens < 0 || c->split_tokens % unit != 0) return KVQ_EINVAL;
   if (c->decode_impl != KVQ_DECODE_AUTO && c->decode_impl != KVQ_DECODE_F32 && c->decode_impl != KVQ_DECODE_MFMA &&
-      c->decode_impl != KVQ_DECODE_DOT16)
+      c->decode_impl != KVQ_DECODE_DOT16 && c->decode_impl != KVQ_DECODE_DOT8)
     return KVQ_EINVAL;
   if (c->decode_impl == KVQ_DECODE_MFMA) return KVQ_EUNSUPPORTED;
+  if (c->decode_impl == KVQ_DECODE_DOT8 && c->scheme != KVQ_INT2_CHANNEL) return KVQ_EUNSUPPORTED;
   return KVQ_OK;
 }
 

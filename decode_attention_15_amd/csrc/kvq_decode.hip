@@ -153,6 +153,8 @@ struct DecodeLds {
       uint8_t abytes[4][GQ * 256];  // per wave: key-side operand words [head][limb][32]
       uint8_t pbytes[4][GQ * 256];  // per wave: value-side operand words [head][limb][32]
       uint4 vstage[4][256];         // per wave: value codes of the current group (both pages, 4 KB)
+      uint4 kstage[4][256];         // per wave: key codes of a group (nibble-digit path)
+      uint4 mstage[4][64];          // per wave: key and value scales/zeros of a group (nibble-digit path)
     } d;
   };
   float cm[4][GQ];
@@ -797,6 +799,361 @@ __device__ void int2_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, in
 }
 
 // ---------------------------------------------------------------------------------------------
+// INT2 chunk, 16-bit fixed point on the 8-way signed nibble dot product (v_dot8).  Same algebra and the
+// same rounding steps as int2_unit_dot16; the 16-bit operands are written as four signed 4-bit digits
+//   x = d0 + 16 d1 + 256 d2 + 4096 d3,  d_k in [-8, 7]  (|x| <= 0x7777 = 30583),
+// read off the biased value x + 0x8888 (whose hex digits are d_k + 8) by flipping bit 3 of every nibble.
+// A 2-bit code fills a nibble after a single mask, so one code word unpacks in three operations (seven
+// for the byte form), and one dot8 multiplies 8 codes with one digit of 8 operands.
+//   K code word m (channel 16m + 4j + k in byte j, bits 2k): (w >> 2n) & 0x33333333 holds channel
+//   16m + 4j + n in the low and 16m + 4j + n + 2 in the high nibble of byte j (n = 0, 1);
+//   V code word g of a channel (token 16j + 4g + r in byte j, bits 2r): (w >> 2n) & 0x33333333 holds
+//   tokens 16j + 4g + n and 16j + 4g + n + 2 in byte j.
+// The digit words of the key-side operand (head, m) and of the weights (head, page, g) put the digits of
+// the same channels / tokens in the same nibbles; per (head, m) or (head, page, g) eight words,
+//   X = [n0 d0, n0 d2, n1 d0, n1 d2],  Y = [n0 d1, n0 d3, n1 d1, n1 d3].
+// Lane roles.  Keys: tokens t and t + 2 of one page (page = lane bit 5, t = 16 j + 4 g + r with j, g, r
+// from lane bits 3-4, 1-2, 0), so that a lane owns both tokens of a weight nibble pair and writes whole
+// bytes.  Values: channels lane, lane + 64.
+// ---------------------------------------------------------------------------------------------
+// Global -> LDS copies of 16 bytes per lane (lane i's bytes land at the LDS address in M0 + 16 i), issued
+// from inline assembly so that the compiler adds no waits of its own for them: the nibble-digit unit keeps
+// every global read of its loop in this form and waits on the vector-memory counter explicitly.  Per-lane
+// 64-bit address, or a uniform base plus a per-lane 32-bit offset.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ inline void dma16(uint32_t lds, const void* gaddr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gaddr) : "memory");
+}
+__device__ inline void dma16_base(uint32_t lds, const void* gbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(gbase)
+               : "memory");
+}
+#define KVQ_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
+
+constexpr float kScale8 = 30583.0f;  // 0x7777: largest magnitude of four signed digits
+constexpr int kBias8 = 0x8888;
+
+__device__ inline int sdot8_z(uint32_t a, uint32_t b) {
+  int r;
+  asm("v_dot8_i32_i4 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ inline int sdot8(uint32_t a, uint32_t b, int c) { return __builtin_amdgcn_sdot8((int)a, (int)b, c, false); }
+
+// Nibble pairs of two biased values (one per 16-bit half, or one each): X has [d0(lo) | d0(hi) << 4,
+// d2(lo) | d2(hi) << 4] per 16-bit half, Y the d1 and d3 pairs; both still biased.
+__device__ inline uint32_t nib_x(uint32_t lo, uint32_t hi) { return (lo & 0x0F0F0F0Fu) | ((hi << 4) & 0xF0F0F0F0u); }
+__device__ inline uint32_t nib_y(uint32_t lo, uint32_t hi) { return ((lo >> 4) & 0x0F0F0F0Fu) | (hi & 0xF0F0F0F0u); }
+
+// 4 x 4 byte transpose: o[k] byte i = x[i] byte k
+__device__ inline uint4 byte_transpose(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
+  const uint32_t a = __builtin_amdgcn_perm(x1, x0, 0x05010400u);  // x0.b0 x1.b0 x0.b1 x1.b1
+  const uint32_t b = __builtin_amdgcn_perm(x1, x0, 0x07030602u);  // x0.b2 x1.b2 x0.b3 x1.b3
+  const uint32_t c = __builtin_amdgcn_perm(x3, x2, 0x05010400u);
+  const uint32_t e = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
+  return make_uint4(__builtin_amdgcn_perm(c, a, 0x05040100u), __builtin_amdgcn_perm(c, a, 0x07060302u),
+                    __builtin_amdgcn_perm(e, b, 0x05040100u), __builtin_amdgcn_perm(e, b, 0x07060302u));
+}
+
+template <int GQ>
+__device__ void int2_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
+  constexpr int LG = HeadLog2<GQ>::v;
+  constexpr int LPH = 64 >> LG;   // lanes per head in the alpha step
+  constexpr int NCH = 2 * GQ;     // channels per lane in the alpha step
+  const Geo& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ng = n_groups_of(T, g.S0, g.W);
+  const int g_begin = chunk * g.gpc;
+  int g_end = (g_begin + g.gpc) < ng ? (g_begin + g.gpc) : ng;
+  if (g_end > g.max_pages / 2) g_end = g.max_pages / 2;  // never index past the page-table row
+  const int c0 = lane, c1 = lane + 64;
+  const int ah = lane >> (6 - LG);           // head of this lane in the alpha step
+  const int ac0 = (lane & (LPH - 1)) * NCH;  // its first channel
+  // key lane: page kp, tokens kt and kt + 2 (nibble selector kr = kt & 1, byte kj, word kg of the values)
+  const int kp = lane >> 5, kj = (lane >> 3) & 3, kg = (lane >> 1) & 3, kr = lane & 1;
+  const int kt = 16 * kj + 4 * kg + kr;
+  float qa[NCH];
+  {
+    const float* q = a.qrot + ((long long)b * g.n_q + h * GQ + ah) * D + ac0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) qa[i] = q[i];
+    // consume the query here, so that the compiler's own wait for these loads sits before the loop and not
+    // inside it (where, not knowing of the copies below, it would wait for all of them)
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) asm volatile("" ::"v"(qa[i]));
+  }
+  float m[GQ], l[GQ], o[GQ][2];
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.0f;
+    o[hh][0] = o[hh][1] = 0.0f;
+  }
+  // per wave: key digit words [head][m][8], weight digit words [head][page * 4 + g][8]; the weight area
+  // first holds the biased 16-bit key operands [head][128] while the key digit words are built
+  uint32_t* adig = reinterpret_cast<uint32_t*>(L.d.abytes[wave]);
+  uint8_t* pdig = L.d.pbytes[wave];
+  uint16_t* aval = reinterpret_cast<uint16_t*>(L.d.pbytes[wave]);
+  uint4* vst = L.d.vstage[wave];
+  const uint4* kst = L.d.kstage[wave];
+  const uint16_t* mst = reinterpret_cast<const uint16_t*>(L.d.mstage[wave]);  // K s, z then V s, z (bf16)
+  const uint32_t vst_a = lds_addr(vst), kst_a = lds_addr(kst), mst_a = lds_addr(mst);
+  const int2* pt = reinterpret_cast<const int2*>(a.page_table + (long long)b * g.max_pages);
+  const long long hoff = (long long)h * I2_HEAD_BYTES;
+  // Software pipeline over this wave's groups: the scales/zeros, key codes and value codes of the next
+  // group are copied to LDS as soon as the current group's copy of each has been read into registers,
+  // so every copy has a whole group's work to land.  Copies of one group in issue order: M (1 copy, both
+  // pages' scales/zeros), K (4), V (4); the waits below count the copies issued after the one needed.
+  auto page_of = [&](int idx) { return a.pages + (long long)idx * g.page_bytes + hoff; };
+  auto issue_m = [&](int2 p) {  // lanes 0-31: key scales/zeros of the even page, 32-63: value ones of the odd page
+    dma16(mst_a, page_of(lane < 32 ? p.x : p.y) + I2_META_OFF + (lane & 31) * 16);
+  };
+  auto issue_k = [&](int2 p) {  // copy j, lane i: 16-byte half j & 1 of token kt + 2 (j >> 1) of page kp
+    const uint8_t* src = page_of(kp ? p.y : p.x) + I2_K_OFF + kt * 32;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(kst_a + 1024 * j, src + (j >> 1) * 64 + (j & 1) * 16);
+  };
+  auto issue_v = [&](int2 p) {  // copy j: 1 KB of value codes, half j & 1 of page j >> 1
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16_base(vst_a + 1024 * j, page_of(j < 2 ? p.x : p.y) + I2_V_OFF + (j & 1) * 1024, lane * 16);
+  };
+  int2 pnext = make_int2(0, 0);
+  if (g_begin + wave < g_end) {
+    const int2 p0 = scalar_load_int2(pt + g_begin + wave);
+    issue_m(p0);
+    issue_k(p0);
+    issue_v(p0);
+  }
+  for (int gi = g_begin + wave; gi < g_end; gi += 4) {
+    const bool has_next = gi + 4 < g_end;  // uniform
+    if (has_next) pnext = scalar_load_int2(pt + gi + 4);
+    KVQ_WAIT_VM(8);  // this group's M copy (its K and V copies may still be in flight)
+    uint32_t skw[NCH / 2], zkw[NCH / 2];
+#pragma unroll
+    for (int i = 0; i < NCH / 2; ++i) {
+      skw[i] = reinterpret_cast<const uint32_t*>(mst)[ac0 / 2 + i];
+      zkw[i] = reinterpret_cast<const uint32_t*>(mst)[(D + ac0) / 2 + i];
+    }
+    const float sv0 = bf16_to_f32(mst[2 * D + c0]), sv1 = bf16_to_f32(mst[2 * D + c1]);
+    const float zv0 = bf16_to_f32(mst[3 * D + c0]), zv1 = bf16_to_f32(mst[3 * D + c1]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next group's copy overwrites it
+    if (has_next) issue_m(pnext);
+
+    // 1. alpha of this group for head ah, channels ac0.., 16-bit, biased, to LDS
+    float A[GQ], AZ[GQ];
+    {
+      float al[NCH];
+      float amx = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const uint32_t w = skw[i >> 1];
+        al[i] = qa[i] * __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+        amx = fmaxf(amx, fabsf(al[i]));
+      }
+      amx = seg_reduce<LPH>(amx, OpMax());
+      const float inv = amx > 0.0f ? kScale8 / amx : 0.0f;
+      int ai[NCH];
+      float zs = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        ai[i] = (int)rintf(al[i] * inv);
+        const uint32_t w = zkw[i >> 1];
+        zs = fmaf((float)ai[i], __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16)), zs);
+      }
+      zs = seg_reduce<LPH>(zs, OpAdd());
+      const float Ah = amx * (1.0f / kScale8);
+      const float AZh = Ah * zs;
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+        A[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Ah), hh * LPH));
+        AZ[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(AZh), hh * LPH));
+      }
+      uint32_t pk[NCH / 2];
+#pragma unroll
+      for (int i = 0; i < NCH / 2; ++i) pk[i] = (uint32_t)(ai[2 * i] + kBias8) | ((uint32_t)(ai[2 * i + 1] + kBias8) << 16);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(aval + ah * D + ac0);
+      if constexpr (NCH >= 4) {
+#pragma unroll
+        for (int i = 0; i < NCH / 2; i += 2) *reinterpret_cast<uint2*>(dst + i) = make_uint2(pk[i], pk[i + 1]);
+      } else {
+        dst[0] = pk[0];
+      }
+    }
+    wave_lds_sync();
+    // 2. key digit words: lane task (head, m, X or Y) reads the 16 channels of word m
+#pragma unroll
+    for (int u = lane; u < 16 * GQ; u += 64) {
+      const int hh = u >> 4, mw = (u >> 1) & 7, isy = u & 1;
+      const uint4* src = reinterpret_cast<const uint4*>(aval + hh * D + 16 * mw);
+      const uint4 d0 = src[0], d1 = src[1];  // channel pairs (16 mw + 2 i, + 1), i = 0..7
+      const uint32_t dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+      uint32_t z[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) z[j] = (isy ? nib_y(dd[2 * j], dd[2 * j + 1]) : nib_x(dd[2 * j], dd[2 * j + 1])) ^ 0x88888888u;
+      reinterpret_cast<uint4*>(adig)[(hh * 8 + mw) * 2 + isy] = byte_transpose(z[0], z[1], z[2], z[3]);
+    }
+    wave_lds_sync();
+
+    // 3. key dots: tokens kt, kt + 2 of page kp against every head
+    if (has_next) KVQ_WAIT_VM(5);  // this group's K copies (then V, next M may be in flight)
+    else KVQ_WAIT_VM(4);
+    const uint4 k00 = kst[c0], k01 = kst[64 + c0], k10 = kst[128 + c0], k11 = kst[192 + c0];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (has_next) issue_k(pnext);
+    int acc[2][GQ][4];
+    const uint32_t kw[2][8] = {{k00.x, k00.y, k00.z, k00.w, k01.x, k01.y, k01.z, k01.w},
+                               {k10.x, k10.y, k10.z, k10.w, k11.x, k11.y, k11.z, k11.w}};
+    auto aword = [&](int idx) { return reinterpret_cast<const uint4*>(adig)[idx]; };  // idx = (mw GQ + hh) 2 + y
+    uint4 wx = aword(0), wy = aword(1);
+#pragma unroll
+    for (int mw = 0; mw < 8; ++mw) {
+      uint32_t nb[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        nb[t][0] = kw[t][mw] & 0x33333333u;
+        nb[t][1] = (kw[t][mw] >> 2) & 0x33333333u;
+      }
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+        const uint4 X = wx, Y = wy;
+        const int nxt = mw * GQ + hh + 1;
+        if (nxt < 8 * GQ) {
+          const int nm = nxt / GQ, nh = nxt % GQ;
+          wx = aword((nh * 8 + nm) * 2);
+          wy = aword((nh * 8 + nm) * 2 + 1);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          int* r = acc[t][hh];
+          if (mw == 0) {
+            r[0] = sdot8_z(X.x, nb[t][0]);
+            r[2] = sdot8_z(X.y, nb[t][0]);
+            r[1] = sdot8_z(Y.x, nb[t][0]);
+            r[3] = sdot8_z(Y.y, nb[t][0]);
+          } else {
+            r[0] = sdot8(X.x, nb[t][0], r[0]);
+            r[2] = sdot8(X.y, nb[t][0], r[2]);
+            r[1] = sdot8(Y.x, nb[t][0], r[1]);
+            r[3] = sdot8(Y.y, nb[t][0], r[3]);
+          }
+          r[0] = sdot8(X.z, nb[t][1], r[0]);
+          r[2] = sdot8(X.w, nb[t][1], r[2]);
+          r[1] = sdot8(Y.z, nb[t][1], r[1]);
+          r[3] = sdot8(Y.w, nb[t][1], r[3]);
+        }
+      }
+    }
+
+    // 4. logits, group max, 16-bit weights as nibble digits in LDS
+    float lg[2][GQ], mg[GQ], Pf[GQ];
+    {
+      float mx[GQ];
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int* r = acc[t][hh];
+          lg[t][hh] = fmaf(A[hh], (float)(((r[3] * 16 + r[2]) * 16 + r[1]) * 16 + r[0]), -AZ[hh]);
+        }
+        mx[hh] = fmaxf(lg[0][hh], lg[1][hh]);
+      }
+      heads_allreduce<GQ>(mx, OpMax(), lane, mg);
+    }
+    {
+      float ps[GQ];
+      uint8_t* pw = pdig + ((kp * 4 + kg) * 8 + kr * 2) * 4 + kj;  // byte kj of word (page, g, X, n0/n1 d0)
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+        // biased weights u + 0x8888, u = floor(kScale8 p + 0.5) in [0, kScale8]
+        const uint32_t u0 = (uint32_t)fmaf(__builtin_amdgcn_exp2f(lg[0][hh] - mg[hh]), kScale8, 0.5f + kBias8);
+        const uint32_t u1 = (uint32_t)fmaf(__builtin_amdgcn_exp2f(lg[1][hh] - mg[hh]), kScale8, 0.5f + kBias8);
+        ps[hh] = (float)(int)(u0 + u1 - 2 * kBias8);
+        const uint32_t x = nib_x(u0, u1) ^ 0x8888u, y = nib_y(u0, u1) ^ 0x8888u;
+        uint8_t* p = pw + hh * 256;
+        p[0] = (uint8_t)x;         // n d0
+        p[4] = (uint8_t)(x >> 8);  // n d2
+        p[16] = (uint8_t)y;        // n d1
+        p[20] = (uint8_t)(y >> 8); // n d3
+      }
+      heads_allreduce<GQ>(ps, OpAdd(), lane, Pf);  // integers below 2^24: exact in fp32
+    }
+    wave_lds_sync();
+
+    // 5. value dots: channels c0, c1 against the weights of every head
+    int accv[2][GQ][4];
+    if (has_next) KVQ_WAIT_VM(5);  // this group's V copies (then the next M and K may be in flight)
+    else KVQ_WAIT_VM(0);
+    const uint4 v00 = vst[c0], v01 = vst[64 + c0], v10 = vst[128 + c0], v11 = vst[192 + c0];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (has_next) issue_v(pnext);
+    const uint32_t vw[2][2][4] = {{{v00.x, v00.y, v00.z, v00.w}, {v10.x, v10.y, v10.z, v10.w}},
+                                  {{v01.x, v01.y, v01.z, v01.w}, {v11.x, v11.y, v11.z, v11.w}}};
+    auto pword = [&](int idx) { return reinterpret_cast<const uint4*>(pdig)[idx]; };  // ((hh 8 + pg) 2 + y)
+    uint4 px = pword(0), py = pword(1);
+#pragma unroll
+    for (int pg = 0; pg < 8; ++pg) {  // pg = page * 4 + g
+      uint32_t nb[2][2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint32_t w = vw[c][pg >> 2][pg & 3];
+        nb[c][0] = w & 0x33333333u;
+        nb[c][1] = (w >> 2) & 0x33333333u;
+      }
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+        const uint4 X = px, Y = py;
+        const int nxt = pg * GQ + hh + 1;
+        if (nxt < 8 * GQ) {
+          const int npg = nxt / GQ, nh = nxt % GQ;
+          px = pword((nh * 8 + npg) * 2);
+          py = pword((nh * 8 + npg) * 2 + 1);
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          int* r = accv[c][hh];
+          if (pg == 0) {
+            r[0] = sdot8_z(X.x, nb[c][0]);
+            r[2] = sdot8_z(X.y, nb[c][0]);
+            r[1] = sdot8_z(Y.x, nb[c][0]);
+            r[3] = sdot8_z(Y.y, nb[c][0]);
+          } else {
+            r[0] = sdot8(X.x, nb[c][0], r[0]);
+            r[2] = sdot8(X.y, nb[c][0], r[2]);
+            r[1] = sdot8(Y.x, nb[c][0], r[1]);
+            r[3] = sdot8(Y.y, nb[c][0], r[3]);
+          }
+          r[0] = sdot8(X.z, nb[c][1], r[0]);
+          r[2] = sdot8(X.w, nb[c][1], r[2]);
+          r[1] = sdot8(Y.z, nb[c][1], r[1]);
+          r[3] = sdot8(Y.w, nb[c][1], r[3]);
+        }
+      }
+    }
+
+    // 6. online-softmax update in the rotated value frame
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      const float mnew = fmaxf(m[hh], mg[hh]);
+      const float sc = exp2_safe_diff(m[hh], mnew);
+      const float wg = __builtin_amdgcn_exp2f(mg[hh] - mnew) * (1.0f / kScale8);
+      const int* r0 = accv[0][hh];
+      const int* r1 = accv[1][hh];
+      const float U0 = (float)(((r0[3] * 16 + r0[2]) * 16 + r0[1]) * 16 + r0[0]);
+      const float U1 = (float)(((r1[3] * 16 + r1[2]) * 16 + r1[1]) * 16 + r1[0]);
+      o[hh][0] = fmaf(o[hh][0], sc, (wg * sv0) * fmaf(-zv0, Pf[hh], U0));
+      o[hh][1] = fmaf(o[hh][1], sc, (wg * sv1) * fmaf(-zv1, Pf[hh], U1));
+      l[hh] = fmaf(l[hh], sc, wg * Pf[hh]);
+      m[hh] = mnew;
+    }
+    wave_lds_sync();
+  }
+  combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, c0, c1);
+}
+
+// ---------------------------------------------------------------------------------------------
 // INT4 token-wise page walk, 16-bit fixed point on v_dot4 ([SAW] App. A.1 eq. (3)-(4), App. A.4 eq. (13)):
 //   logit_t = s_t (sum_c q~_c code_tc - z_t sum_c q~_c): the key-side operand is the rotated query
 //   itself, rounded once per work-group to a_c = rint(q~_c 32639 / max|q~|) (A = max|q~| / 32639),
@@ -1111,7 +1468,8 @@ __device__ void int4_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
   combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, lane, lane + 64);
 }
 
-template <int GQ, int SCHEME, bool DOT16>
+// MODE: 0 fp32, 1 16-bit on the byte dot product, 2 16-bit on the nibble dot product (INT2 only)
+template <int GQ, int SCHEME, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   __shared__ DecodeLds<GQ> L;
   const int unit = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -1138,10 +1496,11 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
       }
     }
   } else if (SCHEME == KVQ_INT2_CHANNEL) {
-    if (DOT16) int2_unit_dot16<GQ>(L, a, b, h, T, unit - 1);
+    if (MODE == 2) int2_unit_dot8<GQ>(L, a, b, h, T, unit - 1);
+    else if (MODE == 1) int2_unit_dot16<GQ>(L, a, b, h, T, unit - 1);
     else int2_unit<GQ>(L, a, b, h, T, unit - 1);
   } else {
-    if (DOT16) int4_unit_dot16<GQ>(L, a, b, h, T, unit - 1);
+    if (MODE == 1) int4_unit_dot16<GQ>(L, a, b, h, T, unit - 1);
     else int4_unit<GQ>(L, a, b, h, T, unit - 1);
   }
 }
@@ -1275,15 +1634,15 @@ hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
   if (stages & KVQ_STAGE_QPREP) hipLaunchKernelGGL(qprep_kernel<GQ>, dim3(g.n_kv, g.batch), dim3(512), 0, s, a);
   if (stages & KVQ_STAGE_SPLITK) {
     const dim3 grid(g.n_units, g.n_kv, g.batch), block(kThreads);
-    // AUTO: the 16-bit integer-dot kernel for INT2, the fp32 kernel for INT4 (faster there: per-token
-    // scales leave the fp32 path no per-group work, and 4-bit codes convert cheaply)
-    const bool dot16 = a.impl == KVQ_DECODE_DOT16 || (a.impl == KVQ_DECODE_AUTO && g.scheme == KVQ_INT2_CHANNEL);
+    // AUTO: 16-bit operands on the nibble dot product for INT2, the fp32 kernel for INT4 (faster there:
+    // per-token scales leave the fp32 path no per-group work, and 4-bit codes convert cheaply)
     if (g.scheme == KVQ_INT2_CHANNEL) {
-      if (dot16) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, true>), grid, block, 0, s, a);
-      else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, false>), grid, block, 0, s, a);
+      if (a.impl == KVQ_DECODE_F32) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 0>), grid, block, 0, s, a);
+      else if (a.impl == KVQ_DECODE_DOT16) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 1>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 2>), grid, block, 0, s, a);
     } else {
-      if (dot16) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_TOKEN, true>), grid, block, 0, s, a);
-      else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_TOKEN, false>), grid, block, 0, s, a);
+      if (a.impl == KVQ_DECODE_DOT16) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_TOKEN, 1>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_TOKEN, 0>), grid, block, 0, s, a);
     }
   }
   if (stages & KVQ_STAGE_MERGE) hipLaunchKernelGGL(merge_kernel<GQ>, dim3(g.n_q, g.batch), dim3(kThreads), 0, s, a);

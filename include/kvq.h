@@ -91,9 +91,17 @@ typedef enum { KVQ_ROT_DENSE = 0, KVQ_ROT_HADAMARD = 1 } kvq_rotation;
    F32   - fp32 FMA on the codes, per-group alpha = q~ s and softmax weights exact in fp32;
    DOT16 - the key-side operand (INT2: alpha = q~ s per group and head; INT4: q~) and the softmax weights
            (per group or page and head) rounded to 16-bit integers scaled to their maximum, multiplied
-           with the codes on the integer dot-product unit;
-   MFMA  - reserved, not built;  AUTO - DOT16 for INT2, F32 for INT4 (the faster of the two there). */
-typedef enum { KVQ_DECODE_AUTO = 0, KVQ_DECODE_F32 = 1, KVQ_DECODE_MFMA = 2, KVQ_DECODE_DOT16 = 3 } kvq_decode_impl;
+           with the codes on the integer dot-product unit as two signed bytes;
+   DOT8  - INT2 only: the same 16-bit operands (full scale 30583) as four signed 4-bit digits on the 8-way
+           nibble dot product, which needs fewer operations to unpack the 2-bit codes;
+   MFMA  - reserved, not built;  AUTO - DOT8 for INT2, F32 for INT4 (the fastest of each). */
+typedef enum {
+  KVQ_DECODE_AUTO = 0,
+  KVQ_DECODE_F32 = 1,
+  KVQ_DECODE_MFMA = 2,
+  KVQ_DECODE_DOT16 = 3,
+  KVQ_DECODE_DOT8 = 4
+} kvq_decode_impl;
 
 /* Static description of one attention layer's cache. */
 typedef struct {

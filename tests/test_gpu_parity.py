@@ -1,7 +1,7 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
 
 Bar: codes, bf16 scales/zeros and band bytes bit-exact; attention outputs within 2e-3 absolute.  The fp32
-decode (DECODE_F32) differs from the fp64 oracle by fp32 rounding only; the default INT2 decode (DOT16)
+decode (DECODE_F32) differs from the fp64 oracle by fp32 rounding only; the integer-dot INT2 decodes (DOT16, DOT8)
 also rounds the per-group key coefficients and softmax weights to 16-bit integers, an error well inside
 the bar on these workloads (about 2e-4 at worst in a CPU model of that arithmetic).
 """
@@ -122,12 +122,12 @@ def test_tiny_single_head_full(K):
     _say(f"  worst |diff| {worst:.2e}")
 
 
-@pytest.mark.parametrize("impl", ["auto", "f32"])
+@pytest.mark.parametrize("impl", ["auto", "f32", "dot16"])
 def test_gqa_ragged_batch(K, impl):
     wl = synth.WORKLOADS["gqa_b1_32k"]
     lens = [3000, 131, 700, 0, 260]
     _say(f"gqa ragged lens={lens} impl={impl}")
-    bc = build_cache(K, wl, lens, append_steps=5, decode_impl=K.DECODE_F32 if impl == "f32" else K.DECODE_AUTO)
+    bc = build_cache(K, wl, lens, append_steps=5, decode_impl={"f32": K.DECODE_F32, "dot16": K.DECODE_DOT16}.get(impl, K.DECODE_AUTO))
     pages, band = _host(bc)
     for b in range(len(lens)):
         for h in (0, 3, 7):
@@ -161,13 +161,13 @@ def test_prefill_and_appends_give_identical_bytes(K):
             assert np.array_equal(ka, kb) and np.array_equal(va, vb)
 
 
-@pytest.mark.parametrize("impl", ["auto", "f32"])
+@pytest.mark.parametrize("impl", ["auto", "f32", "dot16"])
 def test_long_context_gq8_small(K, impl):
     wl = synth.scaled(synth.WORKLOADS["long_b4_131k"], batch=2)
     lens = [5000, 2222]
     _say(f"long gq8 small lens={lens}, split 512, impl={impl}")
     bc = build_cache(K, wl, lens, append_steps=3, split_tokens=512,
-                     decode_impl=K.DECODE_F32 if impl == "f32" else K.DECODE_AUTO)
+                     decode_impl={"f32": K.DECODE_F32, "dot16": K.DECODE_DOT16}.get(impl, K.DECODE_AUTO))
     pages, band = _host(bc)
     for b in range(2):
         for h in (0, 5):
@@ -204,20 +204,24 @@ def test_saw_int4_small(K):
     check_out(bc, out, q, [(b, h) for b in range(len(lens)) for h in range(8)])
 
 
-def test_dot16_agrees_with_f32(K):
-    """The 16-bit integer-dot decode against the fp32 decode on the same cache (tiny workload: one head,
-    fp32 source with x10 outlier channels, 4096 tokens) and on a GQA cache: both within the oracle bar."""
-    import torch
-    for name, lens in (("tiny_1h_4k", [4096]), ("gqa_b1_32k", [2900, 1000])):
+@pytest.mark.parametrize("impl", ["dot16", "dot8"])
+def test_integer_dot_decodes_agree_with_f32(K, impl):
+    """The 16-bit integer-dot decodes (byte limbs, nibble digits) against the fp32 decode on the same cache:
+    one head with an fp32 source and x10 outlier channels (4096 tokens), GQA 4 and GQA 8 caches; both
+    within the oracle bar."""
+    code = {"dot16": K.DECODE_DOT16, "dot8": K.DECODE_DOT8}[impl]
+    for name, lens in (("tiny_1h_4k", [4096]), ("gqa_b1_32k", [2900, 1000]), ("long_b4_131k", [3000, 700])):
         wl = synth.WORKLOADS[name]
-        _say(f"dot16 vs f32: {name} lens={lens}")
+        _say(f"{impl} vs f32: {name} lens={lens}")
         bc = build_cache(K, wl, lens)
         q = synth.queries(synth.scaled(wl, batch=len(lens)))
         outs = []
-        for impl in (K.DECODE_F32, K.DECODE_DOT16):
-            bc.cfg.decode_impl = impl
+        for c in (K.DECODE_F32, code):
+            bc.cfg.decode_impl = c
             outs.append(run_decode(K, bc, q))
-        assert np.abs(outs[0] - outs[1]).max() <= TOL
+        diff = np.abs(outs[0] - outs[1]).max()
+        _say(f"   max |{impl} - f32| = {diff:.2e}")
+        assert diff <= TOL
         check_out(bc, outs[1], q, [(b, h) for b in range(len(lens)) for h in range(wl.n_kv_heads)])
 
 

@@ -145,7 +145,9 @@ def test_one_hip_runtime_in_the_process():
 def test_decode_implementations_accepted_for_both_schemes():
     for scheme, rot, s0, w, ck, cv in ((K.INT2_CHANNEL, K.ROT_DENSE, 4, 128, 0.96, 0.92),
                                        (K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0)):
-        for impl in (K.DECODE_AUTO, K.DECODE_F32, K.DECODE_DOT16):
+        for impl in (K.DECODE_AUTO, K.DECODE_F32, K.DECODE_DOT16, K.DECODE_DOT8):
             cfg = K.make_config(8, 32, scheme=scheme, rotation=rot, n_sink=s0, n_recent=w, clip_k=ck, clip_v=cv,
                                 decode_impl=impl)
-            assert K.check_config(cfg) == K.KVQ_OK
+            # the nibble-digit decode exists for INT2 only
+            want = K.KVQ_EUNSUPPORTED if (impl == K.DECODE_DOT8 and scheme == K.INT4_TOKEN) else K.KVQ_OK
+            assert K.check_config(cfg) == want
