@@ -76,6 +76,10 @@ _lib_check = _sig("kvq_check_config", ctypes.c_int, _CFG)
 _lib_build_oscar = _sig("kvq_build_oscar_rotation", ctypes.c_int, _P, _P)
 _lib_compose_oscar = _sig("kvq_compose_oscar_rotation", ctypes.c_int, _P, _P)
 _lib_build_hadamard = _sig("kvq_build_hadamard_rotation", ctypes.c_int, _P, _P)
+_lib_query_cov = _sig("kvq_query_covariance", ctypes.c_int, _P, ctypes.c_int64, _P)
+_lib_sv_cov = _sig("kvq_score_value_covariance", ctypes.c_int, _P, ctypes.c_int64, _P, ctypes.c_int64, _P)
+_lib_eigenbasis = _sig("kvq_eigenbasis", ctypes.c_int, _P, _P, _P)
+_lib_oscar_from_cov = _sig("kvq_build_oscar_rotation_from_covariance", ctypes.c_int, _P, _P)
 _lib_write = _sig("kv_rotate_quant_write", ctypes.c_int, _CFG, _CACHE, _P, _P, ctypes.c_int32, _P, ctypes.c_int32, _P)
 _lib_decode = _sig("kv_decode_attn", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P, ctypes.c_int32, _P,
                    ctypes.c_size_t, _P)
@@ -90,7 +94,8 @@ _lib_last_error = _sig("kvq_last_error", ctypes.c_char_p)
 EXPORTED = [
     "kvq_page_bytes", "kvq_band_slots", "kvq_band_bytes", "kvq_pages_for_len", "kvq_decode_workspace_bytes",
     "kvq_bits_per_element", "kvq_check_config", "kvq_build_oscar_rotation", "kvq_compose_oscar_rotation",
-    "kvq_build_hadamard_rotation", "kv_rotate_quant_write", "kv_decode_attn", "kv_decode_attn_stages",
+    "kvq_build_hadamard_rotation", "kvq_query_covariance", "kvq_score_value_covariance", "kvq_eigenbasis",
+    "kvq_build_oscar_rotation_from_covariance", "kv_rotate_quant_write", "kv_decode_attn", "kv_decode_attn_stages",
     "kvq_debug_rotate",
     "kvq_strerror", "kvq_version", "kvq_last_error",
 ]
@@ -185,6 +190,54 @@ def build_hadamard_rotation(sign):
     out = np.empty((128, 128), dtype=np.float64)
     _check(_lib_build_hadamard(s.ctypes.data_as(ctypes.c_void_p), out.ctypes.data_as(ctypes.c_void_p)),
            "kvq_build_hadamard_rotation")
+    return out
+
+
+def _vp(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def query_covariance(q):
+    """C_Q = (1/N) sum_n q_n^T q_n of query rows q [N][128] (host fp32 in, fp64 [128][128] out)."""
+    import numpy as np
+    qa = np.ascontiguousarray(q, dtype=np.float32).reshape(-1, 128)
+    out = np.empty((128, 128), dtype=np.float64)
+    _check(_lib_query_cov(_vp(qa), qa.shape[0], _vp(out)), "kvq_query_covariance")
+    return out
+
+
+def score_value_covariance(v, s):
+    """C_S = (1/N) (S V)^T (S V) for values v [n_keys][128] and scores s [N][n_keys]."""
+    import numpy as np
+    va = np.ascontiguousarray(v, dtype=np.float32).reshape(-1, 128)
+    sa = np.ascontiguousarray(s, dtype=np.float32)
+    if sa.ndim != 2 or sa.shape[1] != va.shape[0]:
+        raise ValueError("scores must be [N][n_keys] with n_keys = len(v)")
+    out = np.empty((128, 128), dtype=np.float64)
+    _check(_lib_sv_cov(_vp(va), va.shape[0], _vp(sa), sa.shape[0], _vp(out)), "kvq_score_value_covariance")
+    return out
+
+
+def eigenbasis(C):
+    """(U, lambda): C = U diag(lambda) U^T, lambda descending, columns sign-fixed (largest entry positive)."""
+    import numpy as np
+    ca, cp = _host_f64(C)
+    if ca.shape != (128, 128):
+        raise ValueError("C must be 128 x 128")
+    U = np.empty((128, 128), dtype=np.float64)
+    lam = np.empty(128, dtype=np.float64)
+    _check(_lib_eigenbasis(cp, _vp(U), _vp(lam)), "kvq_eigenbasis")
+    return U, lam
+
+
+def build_oscar_rotation_from_covariance(C):
+    """R = U . H . P_br with U the eigenbasis of the covariance C."""
+    import numpy as np
+    ca, cp = _host_f64(C)
+    if ca.shape != (128, 128):
+        raise ValueError("C must be 128 x 128")
+    out = np.empty((128, 128), dtype=np.float64)
+    _check(_lib_oscar_from_cov(cp, _vp(out)), "kvq_build_oscar_rotation_from_covariance")
     return out
 
 

@@ -25,6 +25,7 @@ SOURCES = {
     "kvq_write.hip": ["-ffp-contract=off"],
     "kvq_decode.hip": [],
     "kvq_api.cpp": ["-x", "hip", "-ffp-contract=off"],
+    "kvq_calib.cpp": ["-x", "hip", "-ffp-contract=off"],
 }
 
 

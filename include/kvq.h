@@ -164,6 +164,26 @@ int kvq_compose_oscar_rotation(const double* U_host, double* R_out_host);
 /* [SAW] §3: dense form diag(sign)·H of the randomized Hadamard (for reference/inspection). */
 int kvq_build_hadamard_rotation(const float* sign_host, double* R_out_host);
 
+/* ---- calibration: the rotation from an attention-aware covariance (host, fp64) ----
+   [OSCAR] §3.2 offline steps 2-3 and §3.4.2 Factor 1: the key rotation's U is the eigenbasis of the query
+   covariance C_Q, the value rotation's U that of the score-weighted value covariance C_S, eigenvectors in
+   columns by decreasing eigenvalue, and R = U·H·P_br.  All buffers are caller-owned host memory; inputs
+   are read only.  Errors: KVQ_EINVAL for NULL pointers, non-positive counts, non-finite inputs or a
+   non-symmetric C (|C_ij - C_ji| > 1e-12 max|C|); KVQ_ERANGE if the eigensolver does not converge. */
+/* C_Q = (1/N) sum_n q_n^T q_n for N = n_rows query rows q [n_rows][128] (fp32); fp64 sums over n in
+   increasing order.  Writes C [128][128] row-major. */
+int kvq_query_covariance(const float* q_host, int64_t n_rows, double* C_out_host);
+/* C_S = (1/N) (S V)^T (S V) for values V [n_keys][128] and attention scores S [n_rows][n_keys] (fp32,
+   row-major), N = n_rows; row n of S V is summed over keys in increasing order in fp64. */
+int kvq_score_value_covariance(const float* v_host, int64_t n_keys, const float* s_host, int64_t n_rows,
+                               double* C_out_host);
+/* Symmetric eigendecomposition C = U diag(lambda) U^T (cyclic Jacobi, fp64): lambda [128] descending,
+   column k of U [128][128] (row-major) the unit eigenvector of lambda[k], its entry of largest magnitude
+   (first such index) positive.  Within a repeated eigenvalue the basis is any orthonormal one. */
+int kvq_eigenbasis(const double* C_host, double* U_out_host, double* lambda_out_host);
+/* R = U·H·P_br with U the eigenbasis of C (kvq_eigenbasis followed by kvq_compose_oscar_rotation). */
+int kvq_build_oscar_rotation_from_covariance(const double* C_host, double* R_out_host);
+
 /* ---- the hot path ---- */
 
 /* Append tokens to every sequence of the cache ([OSCAR] §3.4.5 prefill and window-demotion kernels;

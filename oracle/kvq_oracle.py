@@ -127,6 +127,45 @@ def saw_rotation_matrix(sign: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# Rotation from a calibration covariance ([OSCAR] §3.2 offline steps 2-3,
+# §3.4.2 Factor 1)
+# ----------------------------------------------------------------------------
+
+
+def query_covariance(q) -> np.ndarray:
+    """C_Q = (1/N) sum_n q_n^T q_n over N query rows ([OSCAR] §3.2 step 2(a)), fp64."""
+    q = np.asarray(q, dtype=np.float64).reshape(-1, D)
+    return q.T @ q / q.shape[0]
+
+
+def score_value_covariance(v, s) -> np.ndarray:
+    """C_S = (1/N) V^T S^T S V for values V [n_keys][d] and scores S [N][n_keys] ([OSCAR] §3.2 step 2(b))."""
+    X = np.asarray(s, dtype=np.float64) @ np.asarray(v, dtype=np.float64).reshape(-1, D)
+    return X.T @ X / X.shape[0]
+
+
+def eigenbasis(C):
+    """C = U diag(lam) U^T with lam descending ([OSCAR] §3.4.2 Factor 1, lambda_1 >= ... >= lambda_d).
+
+    numpy's symmetric eigensolver is the library step.  Each eigenvector's sign is fixed so that its
+    entry of largest magnitude (first such index) is positive.  Returns (U, lam).
+    """
+    lam, V = np.linalg.eigh(np.asarray(C, dtype=np.float64))
+    order = np.argsort(-lam, kind="stable")
+    lam, V = lam[order], V[:, order]
+    top = np.argmax(np.abs(V), axis=0)
+    sign = np.where(V[top, np.arange(V.shape[1])] < 0, -1.0, 1.0)
+    return V * sign[None, :], lam
+
+
+def oscar_rotation_from_covariance(C) -> np.ndarray:
+    """R = U . H_Had . P_br with U the eigenbasis of the calibration covariance ([OSCAR] §3.2 step 3)."""
+    U, _ = eigenbasis(C)
+    d = U.shape[0]
+    return U @ hadamard(d) @ bit_reversal_matrix(d)
+
+
+# ----------------------------------------------------------------------------
 # Write path ([OSCAR] §3.4.4 steps 1-3, §3.4.5 prefill kernel steps 1-6)
 # ----------------------------------------------------------------------------
 

@@ -171,6 +171,23 @@ def rotation_gaussian(wl: Workload, which: str) -> np.ndarray:
     return r.standard_normal((HEAD_DIM, HEAD_DIM))
 
 
+def calibration_activations(n: int, seed: int, n_keys: int = 256):
+    """Seeded calibration data for the covariance-built rotation: queries q [n][128] with a correlated,
+    decaying spectrum (q = z diag(g) G, g_c = (c+1)^-0.5, z and G standard normal), values [n_keys][128]
+    of the same kind, and row-stochastic attention scores [n][n_keys] (softmax of N(0, 2^2) logits).
+    Returns (q, v, scores) as float32."""
+    r = np.random.default_rng(np.random.SeedSequence([0xCA11B, seed]))
+    g = (np.arange(HEAD_DIM) + 1.0) ** -0.5
+    mix_q = g[:, None] * r.standard_normal((HEAD_DIM, HEAD_DIM))
+    mix_v = g[:, None] * r.standard_normal((HEAD_DIM, HEAD_DIM))
+    q = r.standard_normal((n, HEAD_DIM)) @ mix_q
+    v = r.standard_normal((n_keys, HEAD_DIM)) @ mix_v
+    logits = 2.0 * r.standard_normal((n, n_keys))
+    e = np.exp(logits - logits.max(axis=1, keepdims=True))
+    scores = e / e.sum(axis=1, keepdims=True)
+    return q.astype(np.float32), v.astype(np.float32), scores.astype(np.float32)
+
+
 def sign_vector(wl: Workload, which: str) -> np.ndarray:
     """Seeded random signs (+1/-1, int8) of the randomized Hadamard transform."""
     r = _rng(wl, "sign_k" if which == "k" else "sign_v")
