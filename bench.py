@@ -35,6 +35,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batch32_32k")
     ap.add_argument("--impl", default="auto", choices=["auto", "f32", "dot16", "dot8"])
+    ap.add_argument("--scheme", default=None, choices=["int2_channel", "int2_token"],
+                    help="INT2 workloads: quantize per channel over 128-token groups (the workloads' statement) "
+                         "or per token over its 128 channels")
+    ap.add_argument("--key-only", action="store_true", help="rotate K only; V quantized in its own frame")
     ap.add_argument("--split", type=int, default=0, help="quantized tokens per decode work-group (0 = auto)")
     ap.add_argument("--cpu-pairs", type=int, default=2, help="distinct (seq, kv head) pairs in the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -57,7 +61,7 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload):
+def read_traffic(workload, variant=""):
     """HBM bytes per launch of the split-K decode kernel measured by rocprofv3 (FETCH_SIZE + WRITE_SIZE,
     scaled by a known-size copy), from the committed summary; None unless that measurement was taken on
     this workload with the kernel source as it is now."""
@@ -71,6 +75,8 @@ def read_traffic(workload):
                 kv[k.strip()] = v.strip()
     if kv.get("kernel_source_sha") != kernel_source_sha() or kv.get("workload") != workload:
         return None
+    if kv.get("variant", "") != variant:  # scheme / rotation overrides of the workload
+        return None
     return int(float(kv["bytes_per_launch"]))
 
 
@@ -80,7 +86,7 @@ def decode_bytes(wl, lens, S0, W):
     token (136 B per token and kv head).  Plus the query (bf16) and the output (fp32)."""
     kv = 0
     for T in lens:
-        if wl.scheme == "int2_channel":
+        if wl.scheme in ("int2_channel", "int2_token"):
             ng = max(0, (T - S0 - W) // 128)
             kv += wl.n_kv_heads * (ng * 128 * 72 + (T - 128 * ng) * 512)
         else:
@@ -101,7 +107,9 @@ def cpu_baseline(wl, args, T, rk, rv):
     total_s = 0.0
     total_bytes = 0
     runs = 0
-    int2 = wl.scheme == "int2_channel"
+    int2 = wl.scheme in ("int2_channel", "int2_token")
+    axis = "token" if wl.scheme == "int2_token" else "channel"
+    rv = None if wl.key_only else rv
     with threadpool_limits(limits=1):
         states = []
         for n in range(max(1, args.cpu_pairs)):
@@ -109,9 +117,9 @@ def cpu_baseline(wl, args, T, rk, rv):
             k = synth.kv_tokens(wl, b, 0, T, "k")[:, h].copy()
             v = synth.kv_tokens(wl, b, 0, T, "v")[:, h].copy()
             if int2:
-                st = O.int2_state(k, v, T, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v, rk, rv)
+                st = O.int2_state(k, v, T, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v, rk, rv, axis=axis)
             else:
-                st = O.int4_state(k, v, T, rk.astype(np.int8), rv.astype(np.int8))
+                st = O.int4_state(k, v, T, rk.astype(np.int8), None if rv is None else rv.astype(np.int8))
             states.append((b, h, st))
         while total_s < args.cpu_seconds:
             b, h, st = states[runs % len(states)]
@@ -119,7 +127,7 @@ def cpu_baseline(wl, args, T, rk, rv):
             if int2:
                 Kh, Vh = O.int2_keys_values(st, rk, rv)
             else:
-                Kh, Vh = O.int4_keys_values(st, rk.astype(np.int8), rv.astype(np.int8))
+                Kh, Vh = O.int4_keys_values(st, rk.astype(np.int8), None if rv is None else rv.astype(np.int8))
             O.attend(O.query_values(q[b, h * wl.gq:(h + 1) * wl.gq]), Kh, Vh)
             total_s += time.perf_counter() - t0
             if int2:
@@ -167,7 +175,11 @@ def main():
     import synth
 
     wl = synth.WORKLOADS[args.workload]
-    int2 = wl.scheme == "int2_channel"
+    if args.scheme and wl.scheme != "int4_token":
+        wl = synth.scaled(wl, scheme=args.scheme)
+    if args.key_only:
+        wl = synth.scaled(wl, key_only=True)
+    int2 = wl.scheme in ("int2_channel", "int2_token")
     dev = "cuda"
     torch.cuda.set_device(0)
     B, n_kv, n_q = wl.batch, wl.n_kv_heads, wl.n_q_heads
@@ -178,18 +190,19 @@ def main():
     impl = {"auto": K.DECODE_AUTO, "f32": K.DECODE_F32, "dot16": K.DECODE_DOT16, "dot8": K.DECODE_DOT8}[args.impl]
     split = args.split if args.split else (wl.split_tokens if wl.name == "long_b4_131k" else 0)
     if int2:
-        cfg = K.make_config(n_kv, n_q, K.INT2_CHANNEL, K.ROT_DENSE, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v,
-                            split, impl)
+        scheme = K.INT2_CHANNEL if wl.scheme == "int2_channel" else K.INT2_TOKEN
+        cfg = K.make_config(n_kv, n_q, scheme, K.ROT_DENSE, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v,
+                            split, impl, wl.key_only)
         rk = K.build_oscar_rotation(synth.rotation_gaussian(wl, "k")).astype(np.float32)
         rv = K.build_oscar_rotation(synth.rotation_gaussian(wl, "v")).astype(np.float32)
     else:
-        cfg = K.make_config(n_kv, n_q, K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0, split, impl)
+        cfg = K.make_config(n_kv, n_q, K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0, split, impl, wl.key_only)
         rk = synth.sign_vector(wl, "k").astype(np.float32)
         rv = synth.sign_vector(wl, "v").astype(np.float32)
     max_pages = K.pages_for_len(cfg, T_end)
     pt, n_pool = synth.page_table(wl, max_pages)
-    cache = K.allocate_cache(cfg, B, torch.from_numpy(pt), torch.from_numpy(rk), torch.from_numpy(rv),
-                             n_pages=n_pool, device=dev)
+    cache = K.allocate_cache(cfg, B, torch.from_numpy(pt), torch.from_numpy(rk),
+                             None if wl.key_only else torch.from_numpy(rv), n_pages=n_pool, device=dev)
     log(f"[bench] {wl.name}: B={B} T={int(lens_start.min())}..{T_end} heads {n_q}/{n_kv}; "
         f"pages {n_pool} x {K.page_bytes(cfg)} B")
 
@@ -282,7 +295,9 @@ def main():
     achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     log(f"[bench] split-K kernel {kern_ms * 1e3:.1f} us, {achieved:.0f} GB/s; kernels {stage_us}")
 
-    traffic = read_traffic(wl.name)
+    variant = ("" if wl.scheme == synth.WORKLOADS[args.workload].scheme else wl.scheme) + \
+        (" key-only" if wl.key_only else "")
+    traffic = read_traffic(wl.name, variant.strip())
 
     result = {
         "metric": "INT2 decode-attn KV GB/s (% of HBM peak); decode steps/s at BS=32, 32k ctx",
@@ -300,8 +315,10 @@ def main():
         "config": {"workload": wl.name, "batch": B, "ctx": T_end,
                    "ctx_range": [int(lens_end.min()), int(lens_end.max())], "n_q_heads": n_q, "n_kv_heads": n_kv,
                    "head_dim": 128,
-                   "scheme": ("int2 per-channel, 128-token groups, bf16 scale/zero" if int2 else
-                              "int4 per-token, bf16 scale/zero, randomized Hadamard (block 128)"),
+                   "scheme": ({"int2_channel": "int2 per-channel, 128-token groups, bf16 scale/zero",
+                               "int2_token": "int2 per-token over 128 channels, bf16 scale/zero",
+                               "int4_token": "int4 per-token, bf16 scale/zero, randomized Hadamard (block 128)"}
+                              [wl.scheme] + (", key-only rotation" if wl.key_only else "")),
                    "sink_recent": [wl.n_sink, wl.n_recent], "page_tokens": 64, "split_tokens": split,
                    "decode_impl": args.impl, "step": "append 1 token/seq (write) + decode attention"},
         "steps_per_s": round(1000.0 / ms_step, 2),

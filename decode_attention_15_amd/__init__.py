@@ -29,7 +29,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 # enums (include/kvq.h)
 KVQ_OK, KVQ_EINVAL, KVQ_ERANGE, KVQ_ENOSPACE, KVQ_EUNSUPPORTED, KVQ_EDEVICE = 0, -1, -2, -3, -4, -5
-INT2_CHANNEL, INT4_TOKEN = 0, 1
+INT2_CHANNEL, INT4_TOKEN, INT2_TOKEN = 0, 1, 2
 F32, BF16 = 0, 1
 ROT_DENSE, ROT_HADAMARD = 0, 1
 DECODE_AUTO, DECODE_F32, DECODE_MFMA, DECODE_DOT16, DECODE_DOT8 = 0, 1, 2, 3, 4
@@ -42,7 +42,7 @@ class Config(ctypes.Structure):
         ("scheme", ctypes.c_int32), ("rotation", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
         ("group_tokens", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("n_recent", ctypes.c_int32),
         ("clip_k", ctypes.c_float), ("clip_v", ctypes.c_float), ("split_tokens", ctypes.c_int32),
-        ("decode_impl", ctypes.c_int32),
+        ("decode_impl", ctypes.c_int32), ("key_only_rotation", ctypes.c_int32),
     ]
 
 
@@ -128,9 +128,9 @@ def _check(status: int, what: str) -> None:
 
 def make_config(n_kv_heads: int, n_q_heads: int, scheme: int = INT2_CHANNEL, rotation: int = ROT_DENSE,
                 n_sink: int = 4, n_recent: int = 128, clip_k: float = 0.96, clip_v: float = 0.92,
-                split_tokens: int = 0, decode_impl: int = DECODE_AUTO) -> Config:
+                split_tokens: int = 0, decode_impl: int = DECODE_AUTO, key_only_rotation: bool = False) -> Config:
     return Config(128, n_kv_heads, n_q_heads, scheme, rotation, 64, 128, n_sink, n_recent, clip_k, clip_v,
-                  split_tokens, decode_impl)
+                  split_tokens, decode_impl, int(key_only_rotation))
 
 
 def check_config(cfg: Config) -> int:
@@ -283,7 +283,8 @@ class DeviceCache:
 
 def allocate_cache(cfg: Config, batch: int, page_table, rot_k, rot_v, n_pages: Optional[int] = None,
                    device: str = "cuda") -> DeviceCache:
-    """Allocate pages, band and lengths (torch, device) for a page table [batch, max_pages] (int32)."""
+    """Allocate pages, band and lengths (torch, device) for a page table [batch, max_pages] (int32).
+    rot_v may be None under key-only rotation."""
     import torch
     _check(check_config(cfg), "config")
     pt = page_table.to(device=device, dtype=torch.int32).contiguous()
@@ -293,8 +294,8 @@ def allocate_cache(cfg: Config, batch: int, page_table, rot_k, rot_v, n_pages: O
     nb = band_bytes(cfg, batch)
     band = torch.zeros(max(nb, 2) // 2, dtype=torch.int16, device=device)
     seq_lens = torch.zeros(batch, dtype=torch.int32, device=device)
-    return DeviceCache(cfg, pages, band, pt, seq_lens, rot_k.to(device).float().contiguous(),
-                       rot_v.to(device).float().contiguous(), batch)
+    rv = None if rot_v is None else rot_v.to(device).float().contiguous()
+    return DeviceCache(cfg, pages, band, pt, seq_lens, rot_k.to(device).float().contiguous(), rv, batch)
 
 
 def kv_rotate_quant_write(cache: DeviceCache, k, v, cu_new, max_new: int, stream=None) -> None:

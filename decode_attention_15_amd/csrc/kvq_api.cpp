@@ -13,12 +13,12 @@ namespace {
 
 int gq_of(const kvq_config* c) { return c->n_q_heads / c->n_kv_heads; }
 
-int head_bytes_of(const kvq_config* c) { return c->scheme == KVQ_INT2_CHANNEL ? I2_HEAD_BYTES : I4_HEAD_BYTES; }
+int head_bytes_of(const kvq_config* c) { return is_int2(c->scheme) ? I2_HEAD_BYTES : I4_HEAD_BYTES; }
 
 int check_config(const kvq_config* c) {
   if (!c) return KVQ_EINVAL;
   if (c->head_dim != D || c->page_tokens != PAGE || c->group_tokens != GROUP) return KVQ_EUNSUPPORTED;
-  if (c->scheme != KVQ_INT2_CHANNEL && c->scheme != KVQ_INT4_TOKEN) return KVQ_EUNSUPPORTED;
+  if (!is_int2(c->scheme) && c->scheme != KVQ_INT4_TOKEN) return KVQ_EUNSUPPORTED;
   if (c->rotation != KVQ_ROT_DENSE && c->rotation != KVQ_ROT_HADAMARD) return KVQ_EUNSUPPORTED;
   if (c->n_kv_heads < 1 || c->n_q_heads < 1 || c->n_q_heads % c->n_kv_heads != 0) return KVQ_EINVAL;
   const int gq = gq_of(c);
@@ -26,20 +26,25 @@ int check_config(const kvq_config* c) {
   if (c->n_sink < 0 || c->n_recent < 0) return KVQ_EINVAL;
   if (c->scheme == KVQ_INT4_TOKEN && (c->n_sink != 0 || c->n_recent != 0)) return KVQ_EINVAL;
   if (!(c->clip_k > 0.0f && c->clip_k <= 1.0f) || !(c->clip_v > 0.0f && c->clip_v <= 1.0f)) return KVQ_EINVAL;
-  const int unit = c->scheme == KVQ_INT2_CHANNEL ? GROUP : PAGE;
+  const int unit = is_int2(c->scheme) ? GROUP : PAGE;
   if (c->split_tokens < 0 || c->split_tokens % unit != 0) return KVQ_EINVAL;
   if (c->decode_impl != KVQ_DECODE_AUTO && c->decode_impl != KVQ_DECODE_F32 && c->decode_impl != KVQ_DECODE_MFMA &&
       c->decode_impl != KVQ_DECODE_DOT16 && c->decode_impl != KVQ_DECODE_DOT8)
     return KVQ_EINVAL;
   if (c->decode_impl == KVQ_DECODE_MFMA) return KVQ_EUNSUPPORTED;
-  if (c->decode_impl == KVQ_DECODE_DOT8 && c->scheme != KVQ_INT2_CHANNEL) return KVQ_EUNSUPPORTED;
+  if (c->decode_impl == KVQ_DECODE_DOT8 && !is_int2(c->scheme)) return KVQ_EUNSUPPORTED;
+  // per-token INT2 is built on the nibble dot product only
+  if (c->scheme == KVQ_INT2_TOKEN && c->decode_impl != KVQ_DECODE_AUTO && c->decode_impl != KVQ_DECODE_DOT8)
+    return KVQ_EUNSUPPORTED;
+  if (c->key_only_rotation != 0 && c->key_only_rotation != 1) return KVQ_EINVAL;
   return KVQ_OK;
 }
 
 int check_cache(const kvq_config* c, const kvq_cache* k) {
-  if (!k || !k->pages || !k->page_table || !k->seq_lens || !k->rot_k || !k->rot_v) return KVQ_EINVAL;
+  if (!k || !k->pages || !k->page_table || !k->seq_lens || !k->rot_k || (!k->rot_v && !c->key_only_rotation))
+    return KVQ_EINVAL;
   if (k->batch < 1 || k->max_pages_per_seq < 0 || k->n_pages < 0) return KVQ_EINVAL;
-  if (c->scheme == KVQ_INT2_CHANNEL && !k->band) return KVQ_EINVAL;
+  if (is_int2(c->scheme) && !k->band) return KVQ_EINVAL;
   return KVQ_OK;
 }
 
@@ -52,9 +57,9 @@ void clip_params(float rho, int* j, float* f) {
 
 // decode work split: groups (INT2) or pages (INT4) per chunk
 int chunk_units(const kvq_config* c, int batch, int max_seq_len) {
-  if (c->split_tokens > 0) return c->split_tokens / (c->scheme == KVQ_INT2_CHANNEL ? GROUP : PAGE);
+  if (c->split_tokens > 0) return c->split_tokens / (is_int2(c->scheme) ? GROUP : PAGE);
   int units;  // quantized groups/pages per sequence
-  if (c->scheme == KVQ_INT2_CHANNEL) units = n_groups_of(max_seq_len, c->n_sink, c->n_recent);
+  if (is_int2(c->scheme)) units = n_groups_of(max_seq_len, c->n_sink, c->n_recent);
   else units = (max_seq_len + PAGE - 1) / PAGE;
   const int pairs = batch * c->n_kv_heads;
   const int target_wgs = 2048;
@@ -62,7 +67,7 @@ int chunk_units(const kvq_config* c, int batch, int max_seq_len) {
   if (chunks < 1) chunks = 1;
   int per = (units + chunks - 1) / chunks;
   per = ((per + 3) / 4) * 4;  // the 4 waves of a work-group share a chunk
-  const int cap = c->scheme == KVQ_INT2_CHANNEL ? 16 : 32;
+  const int cap = is_int2(c->scheme) ? 16 : 32;
   if (per > cap) per = cap;
   if (per < 4) per = 4;
   return per;
@@ -70,7 +75,7 @@ int chunk_units(const kvq_config* c, int batch, int max_seq_len) {
 
 int max_chunks_of(const kvq_config* c, int max_seq_len, int per) {
   int units;
-  if (c->scheme == KVQ_INT2_CHANNEL) units = n_groups_of(max_seq_len, c->n_sink, c->n_recent);
+  if (is_int2(c->scheme)) units = n_groups_of(max_seq_len, c->n_sink, c->n_recent);
   else units = (max_seq_len + PAGE - 1) / PAGE;
   return (units + per - 1) / per;
 }
@@ -84,6 +89,7 @@ Geo make_geo(const kvq_config* c, const kvq_cache* k) {
   g.gq = gq_of(c);
   g.scheme = c->scheme;
   g.rotation = c->rotation;
+  g.key_only = c->key_only_rotation;
   g.S0 = c->n_sink;
   g.W = c->n_recent;
   g.slots = kvq_band_slots(c);
@@ -184,7 +190,7 @@ size_t kvq_page_bytes(const kvq_config* cfg) {
 
 int32_t kvq_band_slots(const kvq_config* cfg) {
   if (check_config(cfg) != KVQ_OK) return 0;
-  return cfg->scheme == KVQ_INT2_CHANNEL ? cfg->n_sink + cfg->n_recent + GROUP : 0;
+  return is_int2(cfg->scheme) ? cfg->n_sink + cfg->n_recent + GROUP : 0;
 }
 
 size_t kvq_band_bytes(const kvq_config* cfg, int32_t batch) {
@@ -194,7 +200,7 @@ size_t kvq_band_bytes(const kvq_config* cfg, int32_t batch) {
 
 int32_t kvq_pages_for_len(const kvq_config* cfg, int32_t seq_len) {
   if (check_config(cfg) != KVQ_OK || seq_len < 0) return -1;
-  if (cfg->scheme == KVQ_INT2_CHANNEL) return 2 * n_groups_of(seq_len, cfg->n_sink, cfg->n_recent);
+  if (is_int2(cfg->scheme)) return 2 * n_groups_of(seq_len, cfg->n_sink, cfg->n_recent);
   return (seq_len + PAGE - 1) / PAGE;
 }
 
@@ -209,7 +215,7 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t batch, int32_t 
 double kvq_bits_per_element(const kvq_config* cfg, int64_t seq_len) {
   if (check_config(cfg) != KVQ_OK || seq_len <= 0) return 0.0;
   double bytes;
-  if (cfg->scheme == KVQ_INT2_CHANNEL) {
+  if (is_int2(cfg->scheme)) {
     const int64_t ng = n_groups_of((int)seq_len, cfg->n_sink, cfg->n_recent);
     // per group and K|V: 128x128 codes at 2 bits + 128 bf16 scales + 128 bf16 zeros
     bytes = (double)ng * 2.0 * (GROUP * D / 4 + 2 * D * 2) + (double)(seq_len - GROUP * ng) * SLOT_BYTES;
@@ -267,7 +273,7 @@ int kv_rotate_quant_write(const kvq_config* cfg, kvq_cache* cache, const void* k
   clip_params(cfg->clip_v, &a.clip_j_v, &a.clip_f_v);
   a.max_new = max_new_host;
   clear_stale_error();
-  hipError_t e = cfg->scheme == KVQ_INT2_CHANNEL ? launch_write_int2(a, stream) : launch_write_int4(a, stream);
+  hipError_t e = is_int2(cfg->scheme) ? launch_write_int2(a, stream) : launch_write_int4(a, stream);
   return to_status(e, "kv_rotate_quant_write");
 }
 

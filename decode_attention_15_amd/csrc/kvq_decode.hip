@@ -857,6 +857,175 @@ __device__ inline uint4 byte_transpose(uint32_t x0, uint32_t x1, uint32_t x2, ui
                     __builtin_amdgcn_perm(e, b, 0x05040100u), __builtin_amdgcn_perm(e, b, 0x07060302u));
 }
 
+// Per-wave state of the nibble-digit units: LDS areas, lane roles and the group copy pipeline.
+// Copies of one group in issue order: M (1 copy: the even page's metadata to lanes 0-31, the odd page's
+// to lanes 32-63), K (4: copy j, lane i = half j & 1 of token kt + 2 (j >> 1) of page kp), V (4: 1 KB
+// of value codes each, half j & 1 of page j >> 1).  The next group's copy of each is issued as soon as
+// the current one has been read into registers, so every copy has a whole group's work to land; the
+// waits count the copies issued after the one needed.
+template <int GQ>
+struct Dot8Wave {
+  uint32_t* adig;       // key digit words [head][m][8]
+  uint8_t* pdig;        // weight digit words [head][page * 4 + g][8]
+  uint16_t* aval;       // biased 16-bit key operands [head][128] (aliases pdig while the digits are built)
+  const uint4* vst;     // value codes of a group (4 KB)
+  const uint4* kst;     // key codes of a group, lane-ordered (4 KB)
+  const uint16_t* mst;  // metadata of a group's two pages (1 KB)
+  uint32_t vst_a, kst_a, mst_a;
+  const uint8_t* pages;
+  long long page_bytes, hoff;
+  int lane, kp, kt;
+
+  __device__ Dot8Wave(DecodeLds<GQ>& L, const DecodeArgs& a, int h, int wave, int lane_) {
+    adig = reinterpret_cast<uint32_t*>(L.d.abytes[wave]);
+    pdig = L.d.pbytes[wave];
+    aval = reinterpret_cast<uint16_t*>(L.d.pbytes[wave]);
+    vst = L.d.vstage[wave];
+    kst = L.d.kstage[wave];
+    mst = reinterpret_cast<const uint16_t*>(L.d.mstage[wave]);
+    vst_a = lds_addr(vst);
+    kst_a = lds_addr(kst);
+    mst_a = lds_addr(mst);
+    pages = a.pages;
+    page_bytes = a.g.page_bytes;
+    hoff = (long long)h * I2_HEAD_BYTES;
+    lane = lane_;
+    kp = lane >> 5;
+    kt = 16 * ((lane >> 3) & 3) + 4 * ((lane >> 1) & 3) + (lane & 1);
+  }
+  __device__ const uint8_t* page_of(int idx) const { return pages + (long long)idx * page_bytes + hoff; }
+  __device__ void issue_m(int2 p) const { dma16(mst_a, page_of(lane < 32 ? p.x : p.y) + I2_META_OFF + (lane & 31) * 16); }
+  __device__ void issue_k(int2 p) const {
+    const uint8_t* src = page_of(kp ? p.y : p.x) + I2_K_OFF + kt * 32;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(kst_a + 1024 * j, src + (j >> 1) * 64 + (j & 1) * 16);
+  }
+  __device__ void issue_v(int2 p) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dma16_base(vst_a + 1024 * j, page_of(j < 2 ? p.x : p.y) + I2_V_OFF + (j & 1) * 1024, lane * 16);
+  }
+};
+
+// Biased 16-bit key operands of head ah, channels ac0 .. ac0 + NCH - 1 (ai in [-30583, 30583]) to aval.
+template <int GQ, int NCH>
+__device__ __forceinline__ void store_key_operands(uint16_t* aval, int ah, int ac0, const int (&ai)[NCH]) {
+  uint32_t pk[NCH / 2];
+#pragma unroll
+  for (int i = 0; i < NCH / 2; ++i) pk[i] = (uint32_t)(ai[2 * i] + kBias8) | ((uint32_t)(ai[2 * i + 1] + kBias8) << 16);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(aval + ah * D + ac0);
+  if constexpr (NCH >= 4) {
+#pragma unroll
+    for (int i = 0; i < NCH / 2; i += 2) *reinterpret_cast<uint2*>(dst + i) = make_uint2(pk[i], pk[i + 1]);
+  } else {
+    dst[0] = pk[0];
+  }
+}
+
+// Key digit words from the biased operands: lane task (head, m, X or Y) reads the 16 channels of word m.
+template <int GQ>
+__device__ __forceinline__ void build_key_digits(uint32_t* adig, const uint16_t* aval, int lane) {
+#pragma unroll
+  for (int u = lane; u < 16 * GQ; u += 64) {
+    const int hh = u >> 4, mw = (u >> 1) & 7, isy = u & 1;
+    const uint4* src = reinterpret_cast<const uint4*>(aval + hh * D + 16 * mw);
+    const uint4 d0 = src[0], d1 = src[1];  // channel pairs (16 mw + 2 i, + 1), i = 0..7
+    const uint32_t dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+    uint32_t z[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z[j] = (isy ? nib_y(dd[2 * j], dd[2 * j + 1]) : nib_x(dd[2 * j], dd[2 * j + 1])) ^ 0x88888888u;
+    reinterpret_cast<uint4*>(adig)[(hh * 8 + mw) * 2 + isy] = byte_transpose(z[0], z[1], z[2], z[3]);
+  }
+}
+
+// One 32-bit code word (nibble vectors nb[0], nb[1]) against the digit words X, Y of one head.
+__device__ __forceinline__ void dot8_word(int (&r)[4], uint4 X, uint4 Y, const uint32_t (&nb)[2], bool first) {
+  if (first) {
+    r[0] = sdot8_z(X.x, nb[0]);
+    r[2] = sdot8_z(X.y, nb[0]);
+    r[1] = sdot8_z(Y.x, nb[0]);
+    r[3] = sdot8_z(Y.y, nb[0]);
+  } else {
+    r[0] = sdot8(X.x, nb[0], r[0]);
+    r[2] = sdot8(X.y, nb[0], r[2]);
+    r[1] = sdot8(Y.x, nb[0], r[1]);
+    r[3] = sdot8(Y.y, nb[0], r[3]);
+  }
+  r[0] = sdot8(X.z, nb[1], r[0]);
+  r[2] = sdot8(X.w, nb[1], r[2]);
+  r[1] = sdot8(Y.z, nb[1], r[1]);
+  r[3] = sdot8(Y.w, nb[1], r[3]);
+}
+
+__device__ __forceinline__ int digits_value(const int (&r)[4]) { return ((r[3] * 16 + r[2]) * 16 + r[1]) * 16 + r[0]; }
+
+// acc[t][head] = digit sums of tokens kt, kt + 2 (code words kw[t][0..7]) against the key digit words.
+template <int GQ>
+__device__ __forceinline__ void key_dots(const uint32_t* adig, const uint32_t (&kw)[2][8], int (&acc)[2][GQ][4]) {
+  auto aword = [&](int idx) { return reinterpret_cast<const uint4*>(adig)[idx]; };  // idx = (hh 8 + mw) 2 + y
+  uint4 wx = aword(0), wy = aword(1);
+#pragma unroll
+  for (int mw = 0; mw < 8; ++mw) {
+    uint32_t nb[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      nb[t][0] = kw[t][mw] & 0x33333333u;
+      nb[t][1] = (kw[t][mw] >> 2) & 0x33333333u;
+    }
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      const uint4 X = wx, Y = wy;
+      const int nxt = mw * GQ + hh + 1;
+      if (nxt < 8 * GQ) {
+        const int nm = nxt / GQ, nh = nxt % GQ;
+        wx = aword((nh * 8 + nm) * 2);
+        wy = aword((nh * 8 + nm) * 2 + 1);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) dot8_word(acc[t][hh], X, Y, nb[t], mw == 0);
+    }
+  }
+}
+
+// accv[c][head] = digit sums of channels lane, lane + 64 (code words vw[c][page][g]) against the weights.
+template <int GQ>
+__device__ __forceinline__ void value_dots(const uint8_t* pdig, const uint32_t (&vw)[2][2][4], int (&accv)[2][GQ][4]) {
+  auto pword = [&](int idx) { return reinterpret_cast<const uint4*>(pdig)[idx]; };  // ((hh 8 + pg) 2 + y)
+  uint4 px = pword(0), py = pword(1);
+#pragma unroll
+  for (int pg = 0; pg < 8; ++pg) {  // pg = page * 4 + g
+    uint32_t nb[2][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint32_t w = vw[c][pg >> 2][pg & 3];
+      nb[c][0] = w & 0x33333333u;
+      nb[c][1] = (w >> 2) & 0x33333333u;
+    }
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      const uint4 X = px, Y = py;
+      const int nxt = pg * GQ + hh + 1;
+      if (nxt < 8 * GQ) {
+        const int npg = nxt / GQ, nh = nxt % GQ;
+        px = pword((nh * 8 + npg) * 2);
+        py = pword((nh * 8 + npg) * 2 + 1);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) dot8_word(accv[c][hh], X, Y, nb[c], pg == 0);
+    }
+  }
+}
+
+// Weight digits of the lane's tokens kt, kt + 2 (biased weights u0, u1) for one head: byte kj of the
+// words (page kp, g, n = kt & 1, digit 0..3).  pw = pdig + head * 256 + ((kp 4 + g) 8 + n 2) 4 + kj.
+__device__ __forceinline__ void store_weight_digits(uint8_t* pw, uint32_t u0, uint32_t u1) {
+  const uint32_t x = nib_x(u0, u1) ^ 0x8888u, y = nib_y(u0, u1) ^ 0x8888u;
+  pw[0] = (uint8_t)x;          // n d0
+  pw[4] = (uint8_t)(x >> 8);   // n d2
+  pw[16] = (uint8_t)y;         // n d1
+  pw[20] = (uint8_t)(y >> 8);  // n d3
+}
+
 template <int GQ>
 __device__ void int2_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
   constexpr int LG = HeadLog2<GQ>::v;
@@ -872,9 +1041,9 @@ __device__ void int2_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int
   const int c0 = lane, c1 = lane + 64;
   const int ah = lane >> (6 - LG);           // head of this lane in the alpha step
   const int ac0 = (lane & (LPH - 1)) * NCH;  // its first channel
-  // key lane: page kp, tokens kt and kt + 2 (nibble selector kr = kt & 1, byte kj, word kg of the values)
-  const int kp = lane >> 5, kj = (lane >> 3) & 3, kg = (lane >> 1) & 3, kr = lane & 1;
-  const int kt = 16 * kj + 4 * kg + kr;
+  Dot8Wave<GQ> W(L, a, h, wave, lane);
+  // weight digit bytes of this lane's tokens: word (page kp, g, n) byte j of each head
+  uint8_t* pw = W.pdig + ((W.kp * 4 + ((lane >> 1) & 3)) * 8 + (lane & 1) * 2) * 4 + ((lane >> 3) & 3);
   float qa[NCH];
   {
     const float* q = a.qrot + ((long long)b * g.n_q + h * GQ + ah) * D + ac0;
@@ -892,40 +1061,13 @@ __device__ void int2_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int
     l[hh] = 0.0f;
     o[hh][0] = o[hh][1] = 0.0f;
   }
-  // per wave: key digit words [head][m][8], weight digit words [head][page * 4 + g][8]; the weight area
-  // first holds the biased 16-bit key operands [head][128] while the key digit words are built
-  uint32_t* adig = reinterpret_cast<uint32_t*>(L.d.abytes[wave]);
-  uint8_t* pdig = L.d.pbytes[wave];
-  uint16_t* aval = reinterpret_cast<uint16_t*>(L.d.pbytes[wave]);
-  uint4* vst = L.d.vstage[wave];
-  const uint4* kst = L.d.kstage[wave];
-  const uint16_t* mst = reinterpret_cast<const uint16_t*>(L.d.mstage[wave]);  // K s, z then V s, z (bf16)
-  const uint32_t vst_a = lds_addr(vst), kst_a = lds_addr(kst), mst_a = lds_addr(mst);
   const int2* pt = reinterpret_cast<const int2*>(a.page_table + (long long)b * g.max_pages);
-  const long long hoff = (long long)h * I2_HEAD_BYTES;
-  // Software pipeline over this wave's groups: the scales/zeros, key codes and value codes of the next
-  // group are copied to LDS as soon as the current group's copy of each has been read into registers,
-  // so every copy has a whole group's work to land.  Copies of one group in issue order: M (1 copy, both
-  // pages' scales/zeros), K (4), V (4); the waits below count the copies issued after the one needed.
-  auto page_of = [&](int idx) { return a.pages + (long long)idx * g.page_bytes + hoff; };
-  auto issue_m = [&](int2 p) {  // lanes 0-31: key scales/zeros of the even page, 32-63: value ones of the odd page
-    dma16(mst_a, page_of(lane < 32 ? p.x : p.y) + I2_META_OFF + (lane & 31) * 16);
-  };
-  auto issue_k = [&](int2 p) {  // copy j, lane i: 16-byte half j & 1 of token kt + 2 (j >> 1) of page kp
-    const uint8_t* src = page_of(kp ? p.y : p.x) + I2_K_OFF + kt * 32;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(kst_a + 1024 * j, src + (j >> 1) * 64 + (j & 1) * 16);
-  };
-  auto issue_v = [&](int2 p) {  // copy j: 1 KB of value codes, half j & 1 of page j >> 1
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma16_base(vst_a + 1024 * j, page_of(j < 2 ? p.x : p.y) + I2_V_OFF + (j & 1) * 1024, lane * 16);
-  };
   int2 pnext = make_int2(0, 0);
   if (g_begin + wave < g_end) {
     const int2 p0 = scalar_load_int2(pt + g_begin + wave);
-    issue_m(p0);
-    issue_k(p0);
-    issue_v(p0);
+    W.issue_m(p0);
+    W.issue_k(p0);
+    W.issue_v(p0);
   }
   for (int gi = g_begin + wave; gi < g_end; gi += 4) {
     const bool has_next = gi + 4 < g_end;  // uniform
@@ -934,13 +1076,13 @@ __device__ void int2_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int
     uint32_t skw[NCH / 2], zkw[NCH / 2];
 #pragma unroll
     for (int i = 0; i < NCH / 2; ++i) {
-      skw[i] = reinterpret_cast<const uint32_t*>(mst)[ac0 / 2 + i];
-      zkw[i] = reinterpret_cast<const uint32_t*>(mst)[(D + ac0) / 2 + i];
+      skw[i] = reinterpret_cast<const uint32_t*>(W.mst)[ac0 / 2 + i];
+      zkw[i] = reinterpret_cast<const uint32_t*>(W.mst)[(D + ac0) / 2 + i];
     }
-    const float sv0 = bf16_to_f32(mst[2 * D + c0]), sv1 = bf16_to_f32(mst[2 * D + c1]);
-    const float zv0 = bf16_to_f32(mst[3 * D + c0]), zv1 = bf16_to_f32(mst[3 * D + c1]);
+    const float sv0 = bf16_to_f32(W.mst[2 * D + c0]), sv1 = bf16_to_f32(W.mst[2 * D + c1]);
+    const float zv0 = bf16_to_f32(W.mst[3 * D + c0]), zv1 = bf16_to_f32(W.mst[3 * D + c1]);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next group's copy overwrites it
-    if (has_next) issue_m(pnext);
+    if (has_next) W.issue_m(pnext);
 
     // 1. alpha of this group for head ah, channels ac0.., 16-bit, biased, to LDS
     float A[GQ], AZ[GQ];
@@ -971,81 +1113,23 @@ __device__ void int2_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int
         A[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Ah), hh * LPH));
         AZ[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(AZh), hh * LPH));
       }
-      uint32_t pk[NCH / 2];
-#pragma unroll
-      for (int i = 0; i < NCH / 2; ++i) pk[i] = (uint32_t)(ai[2 * i] + kBias8) | ((uint32_t)(ai[2 * i + 1] + kBias8) << 16);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(aval + ah * D + ac0);
-      if constexpr (NCH >= 4) {
-#pragma unroll
-        for (int i = 0; i < NCH / 2; i += 2) *reinterpret_cast<uint2*>(dst + i) = make_uint2(pk[i], pk[i + 1]);
-      } else {
-        dst[0] = pk[0];
-      }
+      store_key_operands<GQ, NCH>(W.aval, ah, ac0, ai);
     }
     wave_lds_sync();
-    // 2. key digit words: lane task (head, m, X or Y) reads the 16 channels of word m
-#pragma unroll
-    for (int u = lane; u < 16 * GQ; u += 64) {
-      const int hh = u >> 4, mw = (u >> 1) & 7, isy = u & 1;
-      const uint4* src = reinterpret_cast<const uint4*>(aval + hh * D + 16 * mw);
-      const uint4 d0 = src[0], d1 = src[1];  // channel pairs (16 mw + 2 i, + 1), i = 0..7
-      const uint32_t dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-      uint32_t z[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) z[j] = (isy ? nib_y(dd[2 * j], dd[2 * j + 1]) : nib_x(dd[2 * j], dd[2 * j + 1])) ^ 0x88888888u;
-      reinterpret_cast<uint4*>(adig)[(hh * 8 + mw) * 2 + isy] = byte_transpose(z[0], z[1], z[2], z[3]);
-    }
+    // 2. key digit words
+    build_key_digits<GQ>(W.adig, W.aval, lane);
     wave_lds_sync();
 
     // 3. key dots: tokens kt, kt + 2 of page kp against every head
     if (has_next) KVQ_WAIT_VM(5);  // this group's K copies (then V, next M may be in flight)
     else KVQ_WAIT_VM(4);
-    const uint4 k00 = kst[c0], k01 = kst[64 + c0], k10 = kst[128 + c0], k11 = kst[192 + c0];
+    const uint4 k00 = W.kst[c0], k01 = W.kst[64 + c0], k10 = W.kst[128 + c0], k11 = W.kst[192 + c0];
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (has_next) issue_k(pnext);
+    if (has_next) W.issue_k(pnext);
     int acc[2][GQ][4];
     const uint32_t kw[2][8] = {{k00.x, k00.y, k00.z, k00.w, k01.x, k01.y, k01.z, k01.w},
                                {k10.x, k10.y, k10.z, k10.w, k11.x, k11.y, k11.z, k11.w}};
-    auto aword = [&](int idx) { return reinterpret_cast<const uint4*>(adig)[idx]; };  // idx = (mw GQ + hh) 2 + y
-    uint4 wx = aword(0), wy = aword(1);
-#pragma unroll
-    for (int mw = 0; mw < 8; ++mw) {
-      uint32_t nb[2][2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        nb[t][0] = kw[t][mw] & 0x33333333u;
-        nb[t][1] = (kw[t][mw] >> 2) & 0x33333333u;
-      }
-#pragma unroll
-      for (int hh = 0; hh < GQ; ++hh) {
-        const uint4 X = wx, Y = wy;
-        const int nxt = mw * GQ + hh + 1;
-        if (nxt < 8 * GQ) {
-          const int nm = nxt / GQ, nh = nxt % GQ;
-          wx = aword((nh * 8 + nm) * 2);
-          wy = aword((nh * 8 + nm) * 2 + 1);
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          int* r = acc[t][hh];
-          if (mw == 0) {
-            r[0] = sdot8_z(X.x, nb[t][0]);
-            r[2] = sdot8_z(X.y, nb[t][0]);
-            r[1] = sdot8_z(Y.x, nb[t][0]);
-            r[3] = sdot8_z(Y.y, nb[t][0]);
-          } else {
-            r[0] = sdot8(X.x, nb[t][0], r[0]);
-            r[2] = sdot8(X.y, nb[t][0], r[2]);
-            r[1] = sdot8(Y.x, nb[t][0], r[1]);
-            r[3] = sdot8(Y.y, nb[t][0], r[3]);
-          }
-          r[0] = sdot8(X.z, nb[t][1], r[0]);
-          r[2] = sdot8(X.w, nb[t][1], r[2]);
-          r[1] = sdot8(Y.z, nb[t][1], r[1]);
-          r[3] = sdot8(Y.w, nb[t][1], r[3]);
-        }
-      }
-    }
+    key_dots<GQ>(W.adig, kw, acc);
 
     // 4. logits, group max, 16-bit weights as nibble digits in LDS
     float lg[2][GQ], mg[GQ], Pf[GQ];
@@ -1054,84 +1138,35 @@ __device__ void int2_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int
 #pragma unroll
       for (int hh = 0; hh < GQ; ++hh) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int* r = acc[t][hh];
-          lg[t][hh] = fmaf(A[hh], (float)(((r[3] * 16 + r[2]) * 16 + r[1]) * 16 + r[0]), -AZ[hh]);
-        }
+        for (int t = 0; t < 2; ++t) lg[t][hh] = fmaf(A[hh], (float)digits_value(acc[t][hh]), -AZ[hh]);
         mx[hh] = fmaxf(lg[0][hh], lg[1][hh]);
       }
       heads_allreduce<GQ>(mx, OpMax(), lane, mg);
     }
     {
       float ps[GQ];
-      uint8_t* pw = pdig + ((kp * 4 + kg) * 8 + kr * 2) * 4 + kj;  // byte kj of word (page, g, X, n0/n1 d0)
 #pragma unroll
       for (int hh = 0; hh < GQ; ++hh) {
         // biased weights u + 0x8888, u = floor(kScale8 p + 0.5) in [0, kScale8]
         const uint32_t u0 = (uint32_t)fmaf(__builtin_amdgcn_exp2f(lg[0][hh] - mg[hh]), kScale8, 0.5f + kBias8);
         const uint32_t u1 = (uint32_t)fmaf(__builtin_amdgcn_exp2f(lg[1][hh] - mg[hh]), kScale8, 0.5f + kBias8);
         ps[hh] = (float)(int)(u0 + u1 - 2 * kBias8);
-        const uint32_t x = nib_x(u0, u1) ^ 0x8888u, y = nib_y(u0, u1) ^ 0x8888u;
-        uint8_t* p = pw + hh * 256;
-        p[0] = (uint8_t)x;         // n d0
-        p[4] = (uint8_t)(x >> 8);  // n d2
-        p[16] = (uint8_t)y;        // n d1
-        p[20] = (uint8_t)(y >> 8); // n d3
+        store_weight_digits(pw + hh * 256, u0, u1);
       }
       heads_allreduce<GQ>(ps, OpAdd(), lane, Pf);  // integers below 2^24: exact in fp32
     }
     wave_lds_sync();
 
     // 5. value dots: channels c0, c1 against the weights of every head
-    int accv[2][GQ][4];
     if (has_next) KVQ_WAIT_VM(5);  // this group's V copies (then the next M and K may be in flight)
     else KVQ_WAIT_VM(0);
-    const uint4 v00 = vst[c0], v01 = vst[64 + c0], v10 = vst[128 + c0], v11 = vst[192 + c0];
+    const uint4 v00 = W.vst[c0], v01 = W.vst[64 + c0], v10 = W.vst[128 + c0], v11 = W.vst[192 + c0];
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (has_next) issue_v(pnext);
+    if (has_next) W.issue_v(pnext);
+    int accv[2][GQ][4];
     const uint32_t vw[2][2][4] = {{{v00.x, v00.y, v00.z, v00.w}, {v10.x, v10.y, v10.z, v10.w}},
                                   {{v01.x, v01.y, v01.z, v01.w}, {v11.x, v11.y, v11.z, v11.w}}};
-    auto pword = [&](int idx) { return reinterpret_cast<const uint4*>(pdig)[idx]; };  // ((hh 8 + pg) 2 + y)
-    uint4 px = pword(0), py = pword(1);
-#pragma unroll
-    for (int pg = 0; pg < 8; ++pg) {  // pg = page * 4 + g
-      uint32_t nb[2][2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const uint32_t w = vw[c][pg >> 2][pg & 3];
-        nb[c][0] = w & 0x33333333u;
-        nb[c][1] = (w >> 2) & 0x33333333u;
-      }
-#pragma unroll
-      for (int hh = 0; hh < GQ; ++hh) {
-        const uint4 X = px, Y = py;
-        const int nxt = pg * GQ + hh + 1;
-        if (nxt < 8 * GQ) {
-          const int npg = nxt / GQ, nh = nxt % GQ;
-          px = pword((nh * 8 + npg) * 2);
-          py = pword((nh * 8 + npg) * 2 + 1);
-        }
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          int* r = accv[c][hh];
-          if (pg == 0) {
-            r[0] = sdot8_z(X.x, nb[c][0]);
-            r[2] = sdot8_z(X.y, nb[c][0]);
-            r[1] = sdot8_z(Y.x, nb[c][0]);
-            r[3] = sdot8_z(Y.y, nb[c][0]);
-          } else {
-            r[0] = sdot8(X.x, nb[c][0], r[0]);
-            r[2] = sdot8(X.y, nb[c][0], r[2]);
-            r[1] = sdot8(Y.x, nb[c][0], r[1]);
-            r[3] = sdot8(Y.y, nb[c][0], r[3]);
-          }
-          r[0] = sdot8(X.z, nb[c][1], r[0]);
-          r[2] = sdot8(X.w, nb[c][1], r[2]);
-          r[1] = sdot8(Y.z, nb[c][1], r[1]);
-          r[3] = sdot8(Y.w, nb[c][1], r[3]);
-        }
-      }
-    }
+    value_dots<GQ>(W.pdig, vw, accv);
 
     // 6. online-softmax update in the rotated value frame
 #pragma unroll
@@ -1139,13 +1174,175 @@ __device__ void int2_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int
       const float mnew = fmaxf(m[hh], mg[hh]);
       const float sc = exp2_safe_diff(m[hh], mnew);
       const float wg = __builtin_amdgcn_exp2f(mg[hh] - mnew) * (1.0f / kScale8);
-      const int* r0 = accv[0][hh];
-      const int* r1 = accv[1][hh];
-      const float U0 = (float)(((r0[3] * 16 + r0[2]) * 16 + r0[1]) * 16 + r0[0]);
-      const float U1 = (float)(((r1[3] * 16 + r1[2]) * 16 + r1[1]) * 16 + r1[0]);
+      const float U0 = (float)digits_value(accv[0][hh]);
+      const float U1 = (float)digits_value(accv[1][hh]);
       o[hh][0] = fmaf(o[hh][0], sc, (wg * sv0) * fmaf(-zv0, Pf[hh], U0));
       o[hh][1] = fmaf(o[hh][1], sc, (wg * sv1) * fmaf(-zv1, Pf[hh], U1));
       l[hh] = fmaf(l[hh], sc, wg * Pf[hh]);
+      m[hh] = mnew;
+    }
+    wave_lds_sync();
+  }
+  combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, c0, c1);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Per-token INT2 chunk ([OSCAR] §3.4.4 step 3 taken per token over its 128 channels) on the nibble dot
+// product.  With the key scale s_t and zero z_t of token t,
+//   logit_t = s_t (sum_c q~_c code_tc - z_t sum_c q~_c),
+// so the key-side operand is the rotated query itself, rounded once per work-group to 16 bits,
+// a_c = rint(30583 q~_c / max|q~|), A = max|q~| / 30583: logit_t = A s_t (sum_c a_c code_tc - z_t sum_c a_c),
+// and its digit words are built once before the walk.  Values: the group adds
+//   sum_t p_t s'_t (code'_tc - z'_t) = (S' / 30583) (sum_t u_t code'_tc - sum_t u_t z'_t)
+// to the output, with the weights p_t s'_t rounded to u_t = rint(30583 p_t s'_t / S'), S' the group's
+// largest value scale (p_t <= 1 relative to the group's largest logit), and sum_t p_t to the softmax sum.
+// Lane roles, digit words and the copy pipeline as in int2_unit_dot8; the metadata of a page holds its
+// tokens' K scales, K zeros, V scales, V zeros (64 bf16 each).
+// ---------------------------------------------------------------------------------------------
+template <int GQ>
+__device__ void int2tok_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
+  constexpr int LG = HeadLog2<GQ>::v;
+  constexpr int LPH = 64 >> LG;
+  constexpr int NCH = 2 * GQ;
+  const Geo& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ng = n_groups_of(T, g.S0, g.W);
+  const int g_begin = chunk * g.gpc;
+  int g_end = (g_begin + g.gpc) < ng ? (g_begin + g.gpc) : ng;
+  if (g_end > g.max_pages / 2) g_end = g.max_pages / 2;  // never index past the page-table row
+  const int c0 = lane, c1 = lane + 64;
+  const int ah = lane >> (6 - LG);
+  const int ac0 = (lane & (LPH - 1)) * NCH;
+  Dot8Wave<GQ> W(L, a, h, wave, lane);
+  uint8_t* pw = W.pdig + ((W.kp * 4 + ((lane >> 1) & 3)) * 8 + (lane & 1) * 2) * 4 + ((lane >> 3) & 3);
+  const int mt0 = W.kp * 256 + (W.kt & 63);  // metadata index of token kt (page kp): K s; +64 K z; +128, +192 V
+
+  // 0. the key-side operand, once: rotated query of head ah, channels ac0.., as digit words
+  float A[GQ], FS[GQ];  // A_h and sum_c a_c (an integer below 2^22: exact in fp32)
+  {
+    float qa[NCH];
+    const float* q = a.qrot + ((long long)b * g.n_q + h * GQ + ah) * D + ac0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) qa[i] = q[i];
+    float amx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) amx = fmaxf(amx, fabsf(qa[i]));
+    amx = seg_reduce<LPH>(amx, OpMax());
+    const float inv = amx > 0.0f ? kScale8 / amx : 0.0f;
+    int ai[NCH];
+    int isum = 0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      ai[i] = (int)rintf(qa[i] * inv);
+      isum += ai[i];
+    }
+    const float fs = seg_reduce<LPH>((float)isum, OpAdd());
+    const float Ah = amx * (1.0f / kScale8);
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      A[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Ah), hh * LPH));
+      FS[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fs), hh * LPH));
+    }
+    store_key_operands<GQ, NCH>(W.aval, ah, ac0, ai);
+    wave_lds_sync();
+    build_key_digits<GQ>(W.adig, W.aval, lane);
+    wave_lds_sync();
+  }
+  float m[GQ], l[GQ], o[GQ][2];
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.0f;
+    o[hh][0] = o[hh][1] = 0.0f;
+  }
+  const int2* pt = reinterpret_cast<const int2*>(a.page_table + (long long)b * g.max_pages);
+  int2 pnext = make_int2(0, 0);
+  if (g_begin + wave < g_end) {
+    const int2 p0 = scalar_load_int2(pt + g_begin + wave);
+    W.issue_m(p0);
+    W.issue_k(p0);
+    W.issue_v(p0);
+  }
+  for (int gi = g_begin + wave; gi < g_end; gi += 4) {
+    const bool has_next = gi + 4 < g_end;  // uniform
+    if (has_next) pnext = scalar_load_int2(pt + gi + 4);
+    KVQ_WAIT_VM(8);  // this group's M copy
+    float sk[2], zk[2], svt[2], zvt[2];  // tokens kt, kt + 2
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      sk[t] = bf16_to_f32(W.mst[mt0 + 2 * t]);
+      zk[t] = bf16_to_f32(W.mst[mt0 + 2 * t + 64]);
+      svt[t] = bf16_to_f32(W.mst[mt0 + 2 * t + 128]);
+      zvt[t] = bf16_to_f32(W.mst[mt0 + 2 * t + 192]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (has_next) W.issue_m(pnext);
+
+    // 1. key dots
+    if (has_next) KVQ_WAIT_VM(5);
+    else KVQ_WAIT_VM(4);
+    const uint4 k00 = W.kst[c0], k01 = W.kst[64 + c0], k10 = W.kst[128 + c0], k11 = W.kst[192 + c0];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (has_next) W.issue_k(pnext);
+    int acc[2][GQ][4];
+    const uint32_t kw[2][8] = {{k00.x, k00.y, k00.z, k00.w, k01.x, k01.y, k01.z, k01.w},
+                               {k10.x, k10.y, k10.z, k10.w, k11.x, k11.y, k11.z, k11.w}};
+    key_dots<GQ>(W.adig, kw, acc);
+
+    // 2. logits, group max, weights p_t s'_t / S' as digits, sum_t p_t and sum_t u_t z'_t
+    float lg[2][GQ], mg[GQ], Pl[GQ], Zs[GQ];
+    {
+      float mx[GQ];
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          lg[t][hh] = (A[hh] * sk[t]) * fmaf(-zk[t], FS[hh], (float)digits_value(acc[t][hh]));
+        mx[hh] = fmaxf(lg[0][hh], lg[1][hh]);
+      }
+      heads_allreduce<GQ>(mx, OpMax(), lane, mg);
+    }
+    const float smax = seg_reduce<64>(fmaxf(svt[0], svt[1]), OpMax());  // S' (uniform)
+    const float sinv = smax > 0.0f ? 1.0f / smax : 0.0f;
+    {
+      float ps[GQ], zs[GQ];
+      const float w0 = svt[0] * sinv, w1 = svt[1] * sinv;  // in [0, 1]
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+        const float p0 = __builtin_amdgcn_exp2f(lg[0][hh] - mg[hh]), p1 = __builtin_amdgcn_exp2f(lg[1][hh] - mg[hh]);
+        const uint32_t u0 = (uint32_t)fmaf(p0 * w0, kScale8, 0.5f + kBias8);
+        const uint32_t u1 = (uint32_t)fmaf(p1 * w1, kScale8, 0.5f + kBias8);
+        ps[hh] = p0 + p1;
+        zs[hh] = fmaf((float)(int)(u0 - kBias8), zvt[0], (float)(int)(u1 - kBias8) * zvt[1]);
+        store_weight_digits(pw + hh * 256, u0, u1);
+      }
+      heads_allreduce<GQ>(ps, OpAdd(), lane, Pl);
+      heads_allreduce<GQ>(zs, OpAdd(), lane, Zs);
+    }
+    wave_lds_sync();
+
+    // 3. value dots
+    if (has_next) KVQ_WAIT_VM(5);
+    else KVQ_WAIT_VM(0);
+    const uint4 v00 = W.vst[c0], v01 = W.vst[64 + c0], v10 = W.vst[128 + c0], v11 = W.vst[192 + c0];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (has_next) W.issue_v(pnext);
+    int accv[2][GQ][4];
+    const uint32_t vw[2][2][4] = {{{v00.x, v00.y, v00.z, v00.w}, {v10.x, v10.y, v10.z, v10.w}},
+                                  {{v01.x, v01.y, v01.z, v01.w}, {v11.x, v11.y, v11.z, v11.w}}};
+    value_dots<GQ>(W.pdig, vw, accv);
+
+    // 4. online-softmax update in the rotated value frame
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      const float mnew = fmaxf(m[hh], mg[hh]);
+      const float sc = exp2_safe_diff(m[hh], mnew);
+      const float eg = __builtin_amdgcn_exp2f(mg[hh] - mnew);
+      const float wg = eg * smax * (1.0f / kScale8);
+      o[hh][0] = fmaf(o[hh][0], sc, wg * ((float)digits_value(accv[0][hh]) - Zs[hh]));
+      o[hh][1] = fmaf(o[hh][1], sc, wg * ((float)digits_value(accv[1][hh]) - Zs[hh]));
+      l[hh] = fmaf(l[hh], sc, eg * Pl[hh]);
       m[hh] = mnew;
     }
     wave_lds_sync();
@@ -1476,7 +1673,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   const Geo& g = a.g;
   const int T = a.seq_lens[b];
   int n_chunks;
-  if (SCHEME == KVQ_INT2_CHANNEL) {
+  if (is_int2(SCHEME)) {
     const int ng = n_groups_of(T, g.S0, g.W);
     n_chunks = (ng + g.gpc - 1) / g.gpc;
   } else {
@@ -1485,7 +1682,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;  // lengths beyond the launch bound are cut
   if (unit > n_chunks) return;
   if (unit == 0) {
-    if (SCHEME == KVQ_INT2_CHANNEL) {
+    if (is_int2(SCHEME)) {
       band_unit<GQ>(L, a, b, h, T);
     } else {
       // no band: an empty partial
@@ -1495,6 +1692,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
         part[k] = (k == 0) ? -INFINITY : 0.0f;
       }
     }
+  } else if (SCHEME == KVQ_INT2_TOKEN) {
+    int2tok_unit_dot8<GQ>(L, a, b, h, T, unit - 1);
   } else if (SCHEME == KVQ_INT2_CHANNEL) {
     if (MODE == 2) int2_unit_dot8<GQ>(L, a, b, h, T, unit - 1);
     else if (MODE == 1) int2_unit_dot16<GQ>(L, a, b, h, T, unit - 1);
@@ -1524,7 +1723,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.seq_lens[b];
   int n_chunks;
-  if (g.scheme == KVQ_INT2_CHANNEL) {
+  if (is_int2(g.scheme)) {
     const int ng = n_groups_of(T, g.S0, g.W);
     n_chunks = (ng + g.gpc - 1) / g.gpc;
   } else {
@@ -1583,9 +1782,16 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
     ob[tid] = v;
   }
   __syncthreads();
-  // 4. un-rotate: o_j = sum_c ob[c] R_V[j][c] (dense), or the randomized Hadamard's inverse
+  // 4. un-rotate: o_j = sum_c ob[c] R_V[j][c] (dense), or the randomized Hadamard's inverse; nothing
+  // under key-only rotation (the values were never rotated)
   const int j = tid & (D - 1), half = tid >> 7;
-  if (dense) {
+  if (g.key_only) {
+    if (tid < D) {
+      un[0][tid] = ob[tid];
+      un[1][tid] = 0.0f;
+    }
+    __syncthreads();
+  } else if (dense) {
     const float4* row = reinterpret_cast<const float4*>(a.rot_v + j * D + half * 64);
     float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
@@ -1636,7 +1842,9 @@ hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
     const dim3 grid(g.n_units, g.n_kv, g.batch), block(kThreads);
     // AUTO: 16-bit operands on the nibble dot product for INT2, the fp32 kernel for INT4 (faster there:
     // per-token scales leave the fp32 path no per-group work, and 4-bit codes convert cheaply)
-    if (g.scheme == KVQ_INT2_CHANNEL) {
+    if (g.scheme == KVQ_INT2_TOKEN) {
+      hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_TOKEN, 2>), grid, block, 0, s, a);
+    } else if (g.scheme == KVQ_INT2_CHANNEL) {
       if (a.impl == KVQ_DECODE_F32) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 0>), grid, block, 0, s, a);
       else if (a.impl == KVQ_DECODE_DOT16) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 1>), grid, block, 0, s, a);
       else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 2>), grid, block, 0, s, a);

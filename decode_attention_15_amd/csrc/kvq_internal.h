@@ -37,6 +37,7 @@ struct Geo {
   int gq;
   int scheme;
   int rotation;
+  int key_only;     // 1: V neither rotated on write nor un-rotated on read
   int S0;
   int W;
   int slots;        // band slots per (seq, kv head)
@@ -46,6 +47,9 @@ struct Geo {
   int gpc;          // groups (INT2) or pages (INT4) per decode chunk
   int n_units;      // decode partial units per (seq, q head): 1 band unit + chunks
 };
+
+// both INT2 schemes share the page layout, the band and the group demotion
+__host__ __device__ inline bool is_int2(int scheme) { return scheme == KVQ_INT2_CHANNEL || scheme == KVQ_INT2_TOKEN; }
 
 __host__ __device__ inline int n_groups_of(int T, int S0, int W) {
   int r = T - S0 - W;

@@ -165,9 +165,10 @@ __device__ inline void rotate_group_mfma(const float* xs, const float* rot, floa
 }
 
 // ---------------------------------------------------------------------------------------------
-// INT2 per-channel groups.  One work-group quantizes one (sequence, kv head, K|V, new group):
-// gather 128 bf16 tokens (band or new input) -> rotate -> per-token clip -> per-channel min/max
-// -> bf16 scale/zero -> codes -> K token-major rows / V channel-major rows + metadata.
+// INT2 groups.  One work-group quantizes one (sequence, kv head, K|V, new group):
+// gather 128 bf16 tokens (band or new input) -> rotate -> per-token clip -> min/max per channel over
+// the group (KVQ_INT2_CHANNEL) or per token over its channels (KVQ_INT2_TOKEN) -> bf16 scale/zero
+// -> codes -> K token-major rows / V channel-major rows + metadata.
 // ---------------------------------------------------------------------------------------------
 constexpr int kGroupLds = (GROUP * XS_STRIDE + GROUP * D) * (int)sizeof(float);
 
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
   float* xs = lds;                       // [128 tokens][XS_STRIDE] inputs (bf16 values)
   float* xr = lds + GROUP * XS_STRIDE;   // [128 tokens][128] rotated, then clipped
   __shared__ float red_min[2][D], red_max[2][D];
-  __shared__ float s_sp[D], s_zp[D];
+  __shared__ float s_sp[D], s_zp[D];  // per channel, or per token of the group
 
   const Geo& g = a.g;
   const int lg = blockIdx.x;
@@ -215,8 +216,11 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
   }
   __syncthreads();
 
-  // 2. rotation
-  if (g.rotation == KVQ_ROT_DENSE) {
+  // 2. rotation (none for V under key-only rotation: the bf16 values themselves)
+  const bool tokenwise = g.scheme == KVQ_INT2_TOKEN;
+  if (which == 1 && g.key_only) {
+    for (int e = tid; e < GROUP * D; e += 256) xr[e] = xs[(e >> 7) * XS_STRIDE + (e & (D - 1))];
+  } else if (g.rotation == KVQ_ROT_DENSE) {
     rotate_group_mfma(xs, rot, xr, wave, lane);
   } else {
     for (int tl = wave * 32; tl < wave * 32 + 32; ++tl) {
@@ -241,8 +245,28 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
     __syncthreads();
   }
 
-  // 4. per-channel min/max over the group, bf16 scale and zero
-  {
+  // 4. min/max per channel over the group (or per token over its channels), bf16 scale and zero
+  if (tokenwise) {
+    for (int tl = wave * 32; tl < wave * 32 + 32; ++tl) {
+      const float x0 = xr[tl * D + lane], x1 = xr[tl * D + lane + 64];
+      const float amin = wave_min_f32(fminf(x0, x1));
+      const float bmax = wave_max_f32(fmaxf(x0, x1));
+      const float s = (bmax > amin) ? __fdiv_rn(__fsub_rn(bmax, amin), 3.0f) : 1.0f;
+      const uint16_t s16 = f32_to_bf16_rne(s);
+      const float sp = bf16_to_f32(s16);
+      const uint16_t z16 = f32_to_bf16_rne(__fdiv_rn(-amin, sp));
+      if (lane == 0) {
+        s_sp[tl] = sp;
+        s_zp[tl] = bf16_to_f32(z16);
+        // page of the token: its K (which = 0) or V (which = 1) scales[64] then zeros[64]
+        const long long phys = a.page_table[(long long)b * g.max_pages + 2 * grp + (tl >> 6)];
+        uint16_t* meta = reinterpret_cast<uint16_t*>(a.pages + phys * g.page_bytes + (long long)h * I2_HEAD_BYTES +
+                                                     I2_META_OFF) + which * 128;
+        meta[tl & 63] = s16;
+        meta[64 + (tl & 63)] = z16;
+      }
+    }
+  } else {
     const int c = tid & (D - 1), half = tid >> 7;
     float mn = INFINITY, mx = -INFINITY;
     for (int tl = half * 64; tl < half * 64 + 64; ++tl) {
@@ -254,7 +278,7 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
     red_max[half][c] = mx;
   }
   __syncthreads();
-  if (tid < D) {
+  if (!tokenwise && tid < D) {
     const float amin = fminf(red_min[0][tid], red_min[1][tid]);
     const float bmax = fmaxf(red_max[0][tid], red_max[1][tid]);
     const float s = (bmax > amin) ? __fdiv_rn(__fsub_rn(bmax, amin), 3.0f) : 1.0f;
@@ -272,8 +296,9 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
   __syncthreads();
 
   // 5. codes and packing
-  auto code2 = [&](float x, int c) -> uint32_t {
-    float t = __fadd_rn(__fdiv_rn(x, s_sp[c]), s_zp[c]);
+  auto code2 = [&](float x, int c, int tl) -> uint32_t {
+    const int i = tokenwise ? tl : c;
+    float t = __fadd_rn(__fdiv_rn(x, s_sp[i]), s_zp[i]);
     t = fminf(fmaxf(rintf(t), 0.0f), 3.0f);
     return (uint32_t)t;
   };
@@ -287,7 +312,7 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const int c = half * 64 + wd * 16 + k;
-        w |= code2(xr[tl * D + c], c) << (2 * k);
+        w |= code2(xr[tl * D + c], c, tl) << (2 * k);
       }
       w4[wd] = w;
     }
@@ -302,7 +327,7 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
 #pragma unroll 4
     for (int i = 0; i < 64; ++i) {
       const int j = i >> 4, gg = (i >> 2) & 3, r = i & 3;
-      w4[gg] |= code2(xr[(ph * 64 + i) * D + c], c) << (8 * j + 2 * r);
+      w4[gg] |= code2(xr[(ph * 64 + i) * D + c], c, ph * 64 + i) << (8 * j + 2 * r);
     }
     const long long phys = a.page_table[(long long)b * g.max_pages + 2 * grp + ph];
     uint4* dst = reinterpret_cast<uint4*>(a.pages + phys * g.page_bytes + (long long)h * I2_HEAD_BYTES + I2_V_OFF +
@@ -370,7 +395,12 @@ __global__ __launch_bounds__(256) void int4_quad_kernel(WriteArgs a) {
   __syncthreads();
   if (is_new) {
     float y0, y1;
-    rotate_vec(xs[wave], rot, g.rotation, lane, y0, y1);
+    if (which == 1 && g.key_only) {  // key-only rotation: V quantized in its own frame
+      y0 = xs[wave][lane];
+      y1 = xs[wave][lane + 64];
+    } else {
+      rotate_vec(xs[wave], rot, g.rotation, lane, y0, y1);
+    }
     const float amin = wave_min_f32(fminf(y0, y1));
     const float bmax = wave_max_f32(fmaxf(y0, y1));
     const float s = (bmax > amin) ? __fdiv_rn(__fsub_rn(bmax, amin), 15.0f) : 1.0f;

@@ -26,26 +26,28 @@
  *
  * Cache layout (all little-endian)
  *  - Sequence b holds tokens [0, T_b), T_b = seq_lens[b].  With S0 = n_sink, W = n_recent, G = 128:
- *      INT2 scheme: n_g = max(0, (T - S0 - W) / G) full 128-token groups are quantized; group g
+ *      INT2 schemes: n_g = max(0, (T - S0 - W) / G) full 128-token groups are quantized; group g
  *      covers tokens [S0 + 128g, S0 + 128g + 128); tokens [0, min(T, S0)) (sink) and
  *      [S0 + 128 n_g, T) (tail, W..W+127 tokens once T >= S0+W) are kept as bf16 in the band.
  *      INT4 scheme: every token is quantized on write (S0 = W = 0, no band).
  *  - Quantized token u (u = t - S0 for INT2, u = t for INT4) of sequence b lives in logical page
  *    u / 64 at in-page index i = u % 64; page_table[b * max_pages_per_seq + u / 64] is its physical
  *    page.  A physical page holds 64 tokens of all n_kv_heads: head h at byte h * head_bytes.
- *  - INT2 per-channel head block (head_bytes = 4608):
+ *  - INT2 head block (head_bytes = 4608), both INT2 schemes:
  *      [0, 2048)     K codes, token-major: token i at 32*i; channel c in byte c/4, bits 2*(c%4).
  *      [2048, 4096)  V codes, channel-major: channel c at 2048 + 16*c; token i = 16j + 4g + r
  *                    (j, g, r in 0..3) in byte 4*g + j, bits 2*r.
- *      [4096, 4608)  group metadata: on the group's even page K scales[128] then K zeros[128], on its
- *                    odd page V scales[128] then V zeros[128], all bf16.
+ *      [4096, 4608)  per channel (KVQ_INT2_CHANNEL): group metadata, on the group's even page K
+ *                    scales[128] then K zeros[128], on its odd page V scales[128] then V zeros[128];
+ *                    per token (KVQ_INT2_TOKEN): the page's own tokens, K scales[64], K zeros[64],
+ *                    V scales[64], V zeros[64]; all bf16.
  *  - INT4 token-wise head block (head_bytes = 8704):
  *      [0, 4096)     K codes, token-major: token i at 64*i; channel c in byte c/2, low nibble = even c.
  *      [4096, 8192)  V codes, channel-major: channel c at 4096 + 32*c; token i = 16j + 4g + r in
  *                    byte 8*g + 2*j + r/2, low nibble when r is even.
  *      [8192, 8448)  K per-token (scale, zero) bf16 pairs, token i at 8192 + 4*i.
  *      [8448, 8704)  V per-token (scale, zero) bf16 pairs.
- *  - Band (INT2 scheme): per (b, kv head) kvq_band_slots() slots of 512 bytes: bf16 K[128] then
+ *  - Band (INT2 schemes): per (b, kv head) kvq_band_slots() slots of 512 bytes: bf16 K[128] then
  *    bf16 V[128], unrotated.  Token t < S0 sits in slot t; a tail token t in slot
  *    S0 + (t - S0) % (W + 128).  Band base of (b, h) = ((b * n_kv_heads) + h) * slots * 512.
  *
@@ -58,7 +60,10 @@
  *  - Clip ([OSCAR] §3.4.4): tau = y[j] + f*(y[j+1] - y[j]) in fp32 without fusion, y = sorted |x~|,
  *    j = floor(127*rho), f = fp32(127*rho - j) (tau = y[127] when j = 127); x = min(max(x~, -tau), tau).
  *  - INT2 per channel over the group: s = fp32((b-a)/3) (1 if b == a) -> bf16 s'; z = fp32(-a/s') ->
- *    bf16 z'; code = clamp(rint(fp32(fp32(x/s') + z')), 0, 3), rint ties to even.
+ *    bf16 z'; code = clamp(rint(fp32(fp32(x/s') + z')), 0, 3), rint ties to even.  INT2 per token:
+ *    the same with a, b the min and max of the token's 128 (clipped) channels.
+ *  - Key-only rotation (key_only_rotation = 1): V is quantized in its own frame (no rotation, the
+ *    bf16 values exactly) and the output is not un-rotated; K is rotated as above.
  *  - INT4 per token: s = fp32((b-a)/15) -> bf16 s'; z = rint(fp32(-a/s')) -> bf16 z';
  *    code = clamp(rint(fp32(x/s')) + z', 0, 15).
  *  - Dequantized value x^ = s'(code - z').
@@ -84,7 +89,12 @@ typedef enum {
   KVQ_EDEVICE = -5        /* a HIP call or kernel launch failed */
 } kvq_status;
 
-typedef enum { KVQ_INT2_CHANNEL = 0, KVQ_INT4_TOKEN = 1 } kvq_scheme;
+/* INT2_CHANNEL: asymmetric INT2 per channel over 128-token groups (the workloads' statement);
+   INT4_TOKEN:   [SAW] token-wise asymmetric INT4, integer zero point, no band;
+   INT2_TOKEN:   [OSCAR] §3.4.4 step 3 as the English page states it: asymmetric INT2 per token over its
+                 128 channels (one group per head), real zero point; same pages, band and demotion as
+                 INT2_CHANNEL, with per-token scales/zeros in the page metadata. */
+typedef enum { KVQ_INT2_CHANNEL = 0, KVQ_INT4_TOKEN = 1, KVQ_INT2_TOKEN = 2 } kvq_scheme;
 typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
 typedef enum { KVQ_ROT_DENSE = 0, KVQ_ROT_HADAMARD = 1 } kvq_rotation;
 /* Arithmetic of the quantized-token part of the decode (the bf16 band is always fp32):
@@ -93,8 +103,10 @@ typedef enum { KVQ_ROT_DENSE = 0, KVQ_ROT_HADAMARD = 1 } kvq_rotation;
            (per group or page and head) rounded to 16-bit integers scaled to their maximum, multiplied
            with the codes on the integer dot-product unit as two signed bytes;
    DOT8  - INT2 only: the same 16-bit operands (full scale 30583) as four signed 4-bit digits on the 8-way
-           nibble dot product, which needs fewer operations to unpack the 2-bit codes;
-   MFMA  - reserved, not built;  AUTO - DOT8 for INT2, F32 for INT4 (the fastest of each). */
+           nibble dot product, which needs fewer operations to unpack the 2-bit codes (INT2_TOKEN:
+           the rotated query once per work-group, the weights p_t s_t per group);
+   MFMA  - reserved, not built;  AUTO - DOT8 for INT2, F32 for INT4 (the fastest of each).
+   INT2_TOKEN is built with DOT8 only (F32 and DOT16 return KVQ_EUNSUPPORTED for it). */
 typedef enum {
   KVQ_DECODE_AUTO = 0,
   KVQ_DECODE_F32 = 1,
@@ -111,13 +123,16 @@ typedef struct {
   int32_t scheme;        /* kvq_scheme */
   int32_t rotation;      /* kvq_rotation: DENSE (OSCAR R, fp32 128x128) or HADAMARD (SAW, 128 signs) */
   int32_t page_tokens;   /* must be 64 */
-  int32_t group_tokens;  /* must be 128 (INT2 per-channel group length) */
-  int32_t n_sink;        /* S0 >= 0 (INT2 only; 0 for INT4) */
-  int32_t n_recent;      /* W >= 0 (INT2 only; 0 for INT4) */
+  int32_t group_tokens;  /* must be 128 (INT2 demotion group length) */
+  int32_t n_sink;        /* S0 >= 0 (INT2 schemes; 0 for INT4) */
+  int32_t n_recent;      /* W >= 0 (INT2 schemes; 0 for INT4) */
   float clip_k;          /* rho_K in (0, 1]; 1 = no clip (INT2 only) */
   float clip_v;          /* rho_V in (0, 1] */
   int32_t split_tokens;  /* quantized tokens per decode work-group: multiple of 128, or 0 = chosen by size */
   int32_t decode_impl;   /* kvq_decode_impl */
+  int32_t key_only_rotation;  /* 0: K and V rotated (V by R_V on write, outputs un-rotated by R_V^T);
+                                 1: only K rotated ([SAW] App. C default), V kept in its own frame and
+                                 kvq_cache.rot_v unused (may be NULL) */
 } kvq_config;
 
 /* Device-resident cache of a batch of sequences.  All pointers are device pointers owned by the caller. */
@@ -129,7 +144,7 @@ typedef struct {
   int32_t max_pages_per_seq;
   int32_t* seq_lens;          /* [batch] tokens cached so far; advanced by kv_rotate_quant_write */
   const float* rot_k;         /* DENSE: R_K fp32 row-major [128][128]; HADAMARD: signs fp32 [128] (+1/-1) */
-  const float* rot_v;         /* same for V */
+  const float* rot_v;         /* same for V (unused and may be NULL with key_only_rotation) */
   int32_t batch;
 } kvq_cache;
 

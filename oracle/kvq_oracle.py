@@ -27,7 +27,9 @@ Readings taken where the pages leave a step open (each listed in the design doc):
       f = fp32(h - j), tau = y[j] + f*(y[j+1]-y[j]) in fp32 with each operation
       rounded (no fused multiply-add); tau = y[127] when j = 127.
   R4  INT2 axis: per channel over 128-token groups (the workload's statement);
-      the clip stays per token, before the group min/max.
+      the clip stays per token, before the group min/max.  The per-token reading of
+      the English page (min/max over a token's 128 channels) is the second INT2
+      scheme; both demote whole 128-token groups (R7).
   R5  Scale and zero ([OSCAR] §3.4.4 step 3): s = (b-a)/3 in fp32 (s = 1 if b == a),
       stored as bf16; z = -a/s' with the stored s', stored as bf16; the encoder
       uses the stored s', z' so encode and decode agree.  Code
@@ -261,6 +263,28 @@ def quantize_int2_channel_group(xc: np.ndarray):
     return q, s16, z16
 
 
+def quantize_int2_token(x: np.ndarray):
+    """Asymmetric affine INT2 per token over its 128 channels ([OSCAR] §3.4.4 step 3 as the English page
+    states it: per-token min-max over a group of G = 128 channels; R5's rounding, per token).
+
+    x: [N tokens, 128 channels] float32 (clipped, rotated).
+    Returns codes uint8 [N, 128], s16 and z16 bf16 bits [N].
+    """
+    x = np.asarray(x, dtype=np.float32)
+    a = x.min(axis=1)
+    b = x.max(axis=1)
+    s = np.where(b > a, ((b - a).astype(F32) / F32(3)).astype(F32), F32(1)).astype(F32)
+    s16 = bf16_rne(s)
+    sp = bf16_value(s16)
+    z = ((-a).astype(F32) / sp).astype(F32)
+    z16 = bf16_rne(z)
+    zp = bf16_value(z16)
+    t = (x / sp[:, None]).astype(F32)
+    t = (t + zp[:, None]).astype(F32)
+    q = np.clip(np.rint(t), 0, 3).astype(np.uint8)
+    return q, s16, z16
+
+
 def quantize_int4_token(x: np.ndarray):
     """Token-wise asymmetric INT4 ([SAW] App. A.1 eq. (3)-(4); reading R6).
 
@@ -305,17 +329,21 @@ def band_positions(T: int, n_sink: int, n_recent: int) -> np.ndarray:
 
 
 def int2_state(k_src, v_src, T: int, n_sink: int, n_recent: int, clip_k: float, clip_v: float,
-               R_K32: np.ndarray, R_V32: np.ndarray, groups=None) -> Dict[str, np.ndarray]:
-    """Quantized state of one (seq, kv head) holding tokens [0, T) under the INT2 scheme.
+               R_K32: np.ndarray, R_V32: Optional[np.ndarray], groups=None, axis: str = "channel"
+               ) -> Dict[str, np.ndarray]:
+    """Quantized state of one (seq, kv head) holding tokens [0, T) under an INT2 scheme.
 
     k_src/v_src: [>=T, 128] float32 or bf16 bits.  `groups` limits the groups computed
-    (for sampled checks on large caches); default all.
+    (for sampled checks on large caches); default all.  axis: "channel" (R4: per channel over
+    the group) or "token" (per token over its channels).  R_V32 = None: key-only rotation, the
+    values are quantized in their own frame.
     """
+    quant = quantize_int2_channel_group if axis == "channel" else quantize_int2_token
     kb = source_to_bf16(np.asarray(k_src)[:T])
     vb = source_to_bf16(np.asarray(v_src)[:T])
     ng = n_groups(T, n_sink, n_recent)
     gl = list(range(ng)) if groups is None else list(groups)
-    out = {"n_groups": ng, "groups": np.array(gl, dtype=np.int64),
+    out = {"n_groups": ng, "groups": np.array(gl, dtype=np.int64), "axis": axis,
            "band_pos": band_positions(T, n_sink, n_recent)}
     out["band_k"] = kb[out["band_pos"]]
     out["band_v"] = vb[out["band_pos"]]
@@ -323,9 +351,9 @@ def int2_state(k_src, v_src, T: int, n_sink: int, n_recent: int, clip_k: float, 
     for g in gl:
         t0 = n_sink + GROUP * g
         xk = rotate_dense(bf16_value(kb[t0:t0 + GROUP]), R_K32)
-        xv = rotate_dense(bf16_value(vb[t0:t0 + GROUP]), R_V32)
-        qk, sk, zk = quantize_int2_channel_group(clip_tokens(xk, clip_k))
-        qv, sv, zv = quantize_int2_channel_group(clip_tokens(xv, clip_v))
+        xv = bf16_value(vb[t0:t0 + GROUP]) if R_V32 is None else rotate_dense(bf16_value(vb[t0:t0 + GROUP]), R_V32)
+        qk, sk, zk = quant(clip_tokens(xk, clip_k))
+        qv, sv, zv = quant(clip_tokens(xv, clip_v))
         kc.append(qk); vc.append(qv); ks.append(sk); kz.append(zk); vs.append(sv); vz.append(zv)
     e8 = np.zeros((0, GROUP, D), np.uint8)
     e16 = np.zeros((0, D), np.uint16)
@@ -338,14 +366,16 @@ def int2_state(k_src, v_src, T: int, n_sink: int, n_recent: int, clip_k: float, 
     return out
 
 
-def int4_state(k_src, v_src, T: int, sign_k: np.ndarray, sign_v: np.ndarray,
+def int4_state(k_src, v_src, T: int, sign_k: np.ndarray, sign_v: Optional[np.ndarray],
                tokens=None) -> Dict[str, np.ndarray]:
-    """Token-wise INT4 state of one (seq, kv head) after the randomized Hadamard ([SAW])."""
+    """Token-wise INT4 state of one (seq, kv head) after the randomized Hadamard ([SAW]); sign_v = None:
+    key-only rotation ([SAW] App. C), values quantized in their own frame."""
     idx = np.arange(T) if tokens is None else np.asarray(tokens)
     kb = source_to_bf16(np.asarray(k_src)[idx])
     vb = source_to_bf16(np.asarray(v_src)[idx])
     qk, sk, zk = quantize_int4_token(rotate_hadamard(bf16_value(kb), sign_k))
-    qv, sv, zv = quantize_int4_token(rotate_hadamard(bf16_value(vb), sign_v))
+    xv = bf16_value(vb) if sign_v is None else rotate_hadamard(bf16_value(vb), sign_v)
+    qv, sv, zv = quantize_int4_token(xv)
     return {"tokens": idx, "k_codes": qk, "k_s16": sk, "k_z16": zk,
             "v_codes": qv, "v_s16": sv, "v_z16": zv}
 
@@ -366,14 +396,17 @@ def attend(q: np.ndarray, keys: np.ndarray, vals: np.ndarray) -> np.ndarray:
 
 
 def int2_keys_values(state, R_K32, R_V32):
-    """Dequantized, inverse-rotated K^ and V^ of every group plus the bf16 band, fp64."""
+    """Dequantized, inverse-rotated K^ and V^ of every group plus the bf16 band, fp64 (R_V32 = None:
+    the values were not rotated)."""
     RK = np.asarray(R_K32, dtype=np.float32).astype(np.float64)
-    RV = np.asarray(R_V32, dtype=np.float32).astype(np.float64)
+    RV = np.eye(D) if R_V32 is None else np.asarray(R_V32, dtype=np.float32).astype(np.float64)
     keys = [bf16_value(state["band_k"]).astype(np.float64)]
     vals = [bf16_value(state["band_v"]).astype(np.float64)]
+    # per-channel scales broadcast over tokens (rows), per-token ones over channels (columns)
+    bc = (lambda x: x[None, :]) if state.get("axis", "channel") == "channel" else (lambda x: x[:, None])
     for i in range(len(state["groups"])):
-        xk = dequantize(state["k_codes"][i], state["k_s16"][i][None, :], state["k_z16"][i][None, :])
-        xv = dequantize(state["v_codes"][i], state["v_s16"][i][None, :], state["v_z16"][i][None, :])
+        xk = dequantize(state["k_codes"][i], bc(state["k_s16"][i]), bc(state["k_z16"][i]))
+        xv = dequantize(state["v_codes"][i], bc(state["v_s16"][i]), bc(state["v_z16"][i]))
         keys.append(xk @ RK.T)
         vals.append(xv @ RV.T)
     return np.concatenate(keys), np.concatenate(vals)
@@ -381,7 +414,7 @@ def int2_keys_values(state, R_K32, R_V32):
 
 def int4_keys_values(state, sign_k, sign_v):
     RK = np.asarray(sign_k, np.float64)[:, None] * hadamard(D)
-    RV = np.asarray(sign_v, np.float64)[:, None] * hadamard(D)
+    RV = np.eye(D) if sign_v is None else np.asarray(sign_v, np.float64)[:, None] * hadamard(D)
     xk = dequantize(state["k_codes"], state["k_s16"][:, None], state["k_z16"][:, None])
     xv = dequantize(state["v_codes"], state["v_s16"][:, None], state["v_z16"][:, None])
     # the write multiplied by fp64(1/sqrt(128)); H here is exactly orthonormal in fp64
@@ -396,9 +429,9 @@ def query_values(q) -> np.ndarray:
     return q.astype(np.float64)
 
 
-def decode_int2(q_heads, k_src, v_src, T, n_sink, n_recent, clip_k, clip_v, R_K32, R_V32):
-    """Output [g_q, 128] for the query heads sharing one kv head, INT2 scheme, fp64."""
-    st = int2_state(k_src, v_src, T, n_sink, n_recent, clip_k, clip_v, R_K32, R_V32)
+def decode_int2(q_heads, k_src, v_src, T, n_sink, n_recent, clip_k, clip_v, R_K32, R_V32, axis="channel"):
+    """Output [g_q, 128] for the query heads sharing one kv head, INT2 schemes, fp64."""
+    st = int2_state(k_src, v_src, T, n_sink, n_recent, clip_k, clip_v, R_K32, R_V32, axis=axis)
     K, V = int2_keys_values(st, R_K32, R_V32)
     return attend(query_values(q_heads), K, V), st
 

@@ -34,7 +34,7 @@ class Workload:
     batch: int
     n_q_heads: int
     n_kv_heads: int
-    scheme: str                 # "int2_channel" (per-channel, 128-token groups) | "int4_token"
+    scheme: str                 # "int2_channel" (per channel, 128-token groups) | "int2_token" | "int4_token"
     n_sink: int
     n_recent: int
     clip_k: float
@@ -50,6 +50,7 @@ class Workload:
     group_tokens: int = 128
     split_tokens: int = 512
     rotation: str = "oscar"     # "oscar" (QR·H·P_br) | "saw" (diag(sign)·H)
+    key_only: bool = False      # rotate K only; V quantized in its own frame
     seed: int = 1000
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 

@@ -7,6 +7,7 @@ GPU writer and reader agree with each other.
 from __future__ import annotations
 
 from dataclasses import dataclass
+import sys
 from typing import Dict, List, Optional
 
 import numpy as np
@@ -15,27 +16,29 @@ import oracle as O
 import synth
 
 I2_HEAD, I4_HEAD = 4608, 8704
+TOL = 2e-3  # max |output - oracle| for every workload
 
 
 def config_for(K, wl: synth.Workload, split_tokens: int = 0, decode_impl: int = 0):
-    if wl.scheme == "int2_channel":
-        return K.make_config(wl.n_kv_heads, wl.n_q_heads, K.INT2_CHANNEL,
-                             K.ROT_DENSE if wl.rotation == "oscar" else K.ROT_HADAMARD,
-                             wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v, split_tokens, decode_impl)
-    return K.make_config(wl.n_kv_heads, wl.n_q_heads, K.INT4_TOKEN,
-                         K.ROT_DENSE if wl.rotation == "oscar" else K.ROT_HADAMARD,
-                         0, 0, 1.0, 1.0, split_tokens, decode_impl)
+    rot = K.ROT_DENSE if wl.rotation == "oscar" else K.ROT_HADAMARD
+    if wl.scheme in ("int2_channel", "int2_token"):
+        scheme = K.INT2_CHANNEL if wl.scheme == "int2_channel" else K.INT2_TOKEN
+        return K.make_config(wl.n_kv_heads, wl.n_q_heads, scheme, rot, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v,
+                             split_tokens, decode_impl, wl.key_only)
+    return K.make_config(wl.n_kv_heads, wl.n_q_heads, K.INT4_TOKEN, rot, 0, 0, 1.0, 1.0, split_tokens, decode_impl,
+                         wl.key_only)
 
 
 def rotations(wl: synth.Workload):
-    """fp32 rotation inputs from the oracle's builders: dense R (OSCAR) or sign vectors (SAW)."""
+    """fp32 rotation inputs from the oracle's builders: dense R (OSCAR) or sign vectors (SAW); the value
+    rotation is None under key-only rotation."""
     if wl.rotation == "oscar":
         rk = O.oscar_rotation(synth.rotation_gaussian(wl, "k")).astype(np.float32)
         rv = O.oscar_rotation(synth.rotation_gaussian(wl, "v")).astype(np.float32)
     else:
         rk = synth.sign_vector(wl, "k").astype(np.float32)
         rv = synth.sign_vector(wl, "v").astype(np.float32)
-    return rk, rv
+    return rk, (None if wl.key_only else rv)
 
 
 def source_torch(arr, device):
@@ -52,7 +55,7 @@ class BuiltCache:
     cache: object
     lens: np.ndarray
     rk: np.ndarray
-    rv: np.ndarray
+    rv: Optional[np.ndarray]
     max_pages: int
 
 
@@ -69,8 +72,8 @@ def build_cache(K, wl: synth.Workload, lens, append_steps: int = 0, chunk: Optio
     max_pages = max(1, max(K.pages_for_len(cfg, int(t)) for t in lens))
     pt, n_pool = synth.page_table(wl, max_pages, B * max_pages + n_pool_extra)
     rk, rv = rotations(wl)
-    cache = K.allocate_cache(cfg, B, torch.from_numpy(pt), torch.from_numpy(rk), torch.from_numpy(rv),
-                             n_pages=n_pool, device=device)
+    cache = K.allocate_cache(cfg, B, torch.from_numpy(pt), torch.from_numpy(rk),
+                             None if rv is None else torch.from_numpy(rv), n_pages=n_pool, device=device)
     pre = np.maximum(lens - append_steps, 0)
     seqs_per_call = B if seqs_per_call is None else seqs_per_call
     # prefill, a group of sequences per call, optionally chunked
@@ -118,7 +121,8 @@ def _page(pages: np.ndarray, page_bytes: int, phys: int) -> np.ndarray:
 
 
 def read_int2_group(bc: BuiltCache, pages: np.ndarray, b: int, h: int, g: int) -> Dict[str, np.ndarray]:
-    """Logical codes [128 tok, 128 ch] and bf16 scale/zero bits of one group of one (seq, kv head)."""
+    """Logical codes [128 tok, 128 ch] and bf16 scale/zero bits of one group of one (seq, kv head):
+    per channel [128] (INT2_CHANNEL) or per token of the group [128] (INT2_TOKEN)."""
     n_kv = bc.wl.n_kv_heads
     pb = n_kv * I2_HEAD
     pt = bc.cache.page_table.cpu().numpy()
@@ -135,6 +139,10 @@ def read_int2_group(bc: BuiltCache, pages: np.ndarray, b: int, h: int, g: int) -
             j, gg, r = i // 16, (i // 4) % 4, i % 4
             vc[pp * 64 + i, :] = (vb[:, 4 * gg + j] >> (2 * r)) & 3
         meta.append(blk[4096:4608].view(np.uint16))
+    if bc.wl.scheme == "int2_token":
+        # each page: its 64 tokens' K scales, K zeros, V scales, V zeros
+        part = [np.concatenate([meta[0][64 * i:64 * i + 64], meta[1][64 * i:64 * i + 64]]) for i in range(4)]
+        return {"k_codes": kc, "v_codes": vc, "k_s16": part[0], "k_z16": part[1], "v_s16": part[2], "v_z16": part[3]}
     return {"k_codes": kc, "v_codes": vc, "k_s16": meta[0][:128], "k_z16": meta[0][128:],
             "v_s16": meta[1][:128], "v_z16": meta[1][128:]}
 
@@ -187,11 +195,12 @@ def oracle_out(bc: BuiltCache, q: np.ndarray, b: int, h: int, T: int) -> np.ndar
     k, v = source_of(bc.wl, b, T)
     gq = bc.wl.gq
     qh = q[b, h * gq:(h + 1) * gq]
-    if bc.wl.scheme == "int2_channel":
+    if bc.wl.scheme in ("int2_channel", "int2_token"):
         o, _ = O.decode_int2(qh, k[:, h], v[:, h], T, bc.wl.n_sink, bc.wl.n_recent, bc.wl.clip_k, bc.wl.clip_v,
-                             bc.rk, bc.rv)
+                             bc.rk, bc.rv, axis="channel" if bc.wl.scheme == "int2_channel" else "token")
     else:
-        o, _ = O.decode_int4(qh, k[:, h], v[:, h], T, bc.rk.astype(np.int8), bc.rv.astype(np.int8))
+        o, _ = O.decode_int4(qh, k[:, h], v[:, h], T, bc.rk.astype(np.int8),
+                             None if bc.rv is None else bc.rv.astype(np.int8))
     return o
 
 
@@ -204,3 +213,62 @@ def run_decode(K, bc: BuiltCache, q_np: np.ndarray, device: str = "cuda"):
     K.kv_decode_attn(bc.cache, q, out, maxT, ws)
     torch.cuda.synchronize()
     return out.cpu().numpy()
+
+
+# ------------------------------------------------------------------------- checks against the oracle
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _host(bc):
+    return bc.cache.pages.cpu().numpy(), bc.cache.band.cpu().numpy().view(np.uint16)
+
+
+def check_int2(bc, b, h, groups=None, pages=None, band=None):
+    if pages is None:
+        pages, band = _host(bc)
+    T = int(bc.lens[b])
+    k, v = source_of(bc.wl, b, T)
+    st = O.int2_state(k[:, h], v[:, h], T, bc.wl.n_sink, bc.wl.n_recent, bc.wl.clip_k, bc.wl.clip_v,
+                      bc.rk, bc.rv, groups=groups, axis="token" if bc.wl.scheme == "int2_token" else "channel")
+    for i, g in enumerate(st["groups"]):
+        got = read_int2_group(bc, pages, b, h, int(g))
+        for key in ("k_codes", "v_codes", "k_s16", "k_z16", "v_s16", "v_z16"):
+            want = st[key][i]
+            if not np.array_equal(got[key], want):
+                bad = np.argwhere(got[key] != want)
+                raise AssertionError(f"b={b} h={h} group={g} {key}: {len(bad)} mismatches, first {bad[:5].tolist()}")
+    bk, bv = read_band(bc, band, b, h, st["band_pos"])
+    assert np.array_equal(bk, st["band_k"]), f"band K b={b} h={h}"
+    assert np.array_equal(bv, st["band_v"]), f"band V b={b} h={h}"
+    return st
+
+
+def check_int4(bc, b, h, pages):
+    T = int(bc.lens[b])
+    k, v = source_of(bc.wl, b, T)
+    st = O.int4_state(k[:, h], v[:, h], T, bc.rk.astype(np.int8), None if bc.rv is None else bc.rv.astype(np.int8))
+    got = read_int4_tokens(bc, pages, b, h, T)
+    for key in ("k_codes", "v_codes", "k_s16", "k_z16", "v_s16", "v_z16"):
+        if not np.array_equal(got[key], st[key]):
+            bad = np.argwhere(got[key] != st[key])
+            raise AssertionError(f"b={b} h={h} {key}: {len(bad)} mismatches, first {bad[:5].tolist()}")
+
+
+def check_out(bc, out, q, pairs):
+    worst = 0.0
+    for b, h in pairs:
+        T = int(bc.lens[b])
+        gq = bc.wl.gq
+        got = out[b, h * gq:(h + 1) * gq]
+        if T == 0:
+            assert np.array_equal(got, np.zeros_like(got))
+            continue
+        want = oracle_out(bc, q, b, h, T)
+        err = np.abs(got - want).max()
+        worst = max(worst, err)
+        assert err <= TOL, f"b={b} h={h} T={T}: max |diff| {err:.3e}"
+    return worst

@@ -31,7 +31,7 @@ def _say(msg):
 
 
 class _BC:
-    """Minimal stand-in for kvq_cases.BuiltCache: what the layout readers use."""
+    """Minimal stand-in for kvq_cases.BuiltCache: what the layout readers use (wl.scheme, wl.n_kv_heads)."""
 
     def __init__(self, wl, cache):
         self.wl, self.cache = wl, cache
@@ -59,8 +59,9 @@ def _write_and_check(K, wl, kb, vb, clip=(0.96, 0.92), chunks=None, decode=True)
     band = cache.band.cpu().numpy().view(np.uint16)
     bc = _BC(wl, cache)
     worst = 0.0
+    axis = "token" if wl.scheme == "int2_token" else "channel"
     for h in range(wl.n_kv_heads):
-        st = O.int2_state(kb[:, h], vb[:, h], T, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v, rk, rv)
+        st = O.int2_state(kb[:, h], vb[:, h], T, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v, rk, rv, axis=axis)
         for i, g in enumerate(st["groups"]):
             got = read_int2_group(bc, pages, 0, h, int(g))
             for key in ("k_codes", "v_codes", "k_s16", "k_z16", "v_s16", "v_z16"):
@@ -89,9 +90,11 @@ def _bf16(x):
 
 
 WL = synth.scaled(synth.WORKLOADS["gqa_b1_32k"], n_q_heads=8, n_kv_heads=2)
+SCHEMES = pytest.mark.parametrize("scheme", ["int2_channel", "int2_token"])
 
 
-def test_all_zero_groups_and_constant_channels(K):
+@SCHEMES
+def test_all_zero_groups_and_constant_channels(K, scheme):
     T = 4 + 128 + 3 * 128 + 50
     rng = np.random.default_rng(5)
     k = rng.standard_normal((T, 2, 128)).astype(np.float32)
@@ -100,11 +103,12 @@ def test_all_zero_groups_and_constant_channels(K):
     v[4:132] = 0.0
     k[132:260, 0, :] = 0.75            # group 1, head 0: every token the same constant vector
     v[132:260, 1, :] = -2.0
-    _say("all-zero group, constant tokens")
-    _write_and_check(K, WL, _bf16(k), _bf16(v))
+    _say(f"all-zero group, constant tokens ({scheme})")
+    _write_and_check(K, synth.scaled(WL, scheme=scheme), _bf16(k), _bf16(v))
 
 
-def test_large_and_tiny_magnitudes(K):
+@SCHEMES
+def test_large_and_tiny_magnitudes(K, scheme):
     T = 4 + 128 + 2 * 128 + 7
     rng = np.random.default_rng(6)
     k = rng.standard_normal((T, 2, 128)).astype(np.float32)
@@ -113,25 +117,27 @@ def test_large_and_tiny_magnitudes(K):
     v[4:132] *= 1.0e-3
     k[132:260] *= 1.0e-36              # group 1: tiny values; rotated results are fp32 subnormals
     v[132:260] *= 1.0e-37
-    _say("large and tiny magnitudes")
-    _write_and_check(K, WL, _bf16(k), _bf16(v), decode=False)
+    _say(f"large and tiny magnitudes ({scheme})")
+    _write_and_check(K, synth.scaled(WL, scheme=scheme), _bf16(k), _bf16(v), decode=False)
 
 
-def test_no_clip(K):
+@SCHEMES
+def test_no_clip(K, scheme):
     T = 4 + 128 + 2 * 128 + 1
     rng = np.random.default_rng(7)
     k = (rng.standard_normal((T, 2, 128)) * 3).astype(np.float32)
     v = rng.standard_normal((T, 2, 128)).astype(np.float32)
-    _say("clip ratio 1 (no clip)")
-    _write_and_check(K, WL, _bf16(k), _bf16(v), clip=(1.0, 1.0))
+    _say(f"clip ratio 1 (no clip) ({scheme})")
+    _write_and_check(K, synth.scaled(WL, scheme=scheme), _bf16(k), _bf16(v), clip=(1.0, 1.0))
 
 
+@SCHEMES
 @pytest.mark.parametrize("T", [1, 3, 4, 5, 132, 259, 260, 261, 387, 388, 389])
-def test_lengths_at_the_sink_window_group_boundaries(K, T):
+def test_lengths_at_the_sink_window_group_boundaries(K, T, scheme):
     rng = np.random.default_rng(100 + T)
     k = rng.standard_normal((T, 2, 128)).astype(np.float32)
     v = rng.standard_normal((T, 2, 128)).astype(np.float32)
-    _say(f"boundary length T={T}")
+    _say(f"boundary length T={T} ({scheme})")
     # written one token at a time below 8 tokens, else in two uneven chunks
     chunks = [1] * T if T < 8 else [T // 3, T - T // 3]
-    _write_and_check(K, WL, _bf16(k), _bf16(v), chunks=chunks)
+    _write_and_check(K, synth.scaled(WL, scheme=scheme), _bf16(k), _bf16(v), chunks=chunks)

@@ -12,11 +12,10 @@ import pytest
 
 import oracle as O
 import synth
-from kvq_cases import (build_cache, oracle_out, read_band, read_int2_group, read_int4_tokens, run_decode,
-                       source_of)
+from kvq_cases import (TOL, _host, _say, build_cache, check_int2, check_int4, check_out, oracle_out, read_band,
+                       read_int2_group, read_int4_tokens, run_decode, source_of)
 
 pytestmark = pytest.mark.gpu
-TOL = 2e-3
 
 
 @pytest.fixture(scope="module")
@@ -25,62 +24,6 @@ def K():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     import decode_attention_15_amd as K
     return K
-
-
-def _say(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
-
-
-def _host(bc):
-    return bc.cache.pages.cpu().numpy(), bc.cache.band.cpu().numpy().view(np.uint16)
-
-
-def check_int2(bc, b, h, groups=None, pages=None, band=None):
-    if pages is None:
-        pages, band = _host(bc)
-    T = int(bc.lens[b])
-    k, v = source_of(bc.wl, b, T)
-    st = O.int2_state(k[:, h], v[:, h], T, bc.wl.n_sink, bc.wl.n_recent, bc.wl.clip_k, bc.wl.clip_v,
-                      bc.rk, bc.rv, groups=groups)
-    for i, g in enumerate(st["groups"]):
-        got = read_int2_group(bc, pages, b, h, int(g))
-        for key in ("k_codes", "v_codes", "k_s16", "k_z16", "v_s16", "v_z16"):
-            want = st[key][i]
-            if not np.array_equal(got[key], want):
-                bad = np.argwhere(got[key] != want)
-                raise AssertionError(f"b={b} h={h} group={g} {key}: {len(bad)} mismatches, first {bad[:5].tolist()}")
-    bk, bv = read_band(bc, band, b, h, st["band_pos"])
-    assert np.array_equal(bk, st["band_k"]), f"band K b={b} h={h}"
-    assert np.array_equal(bv, st["band_v"]), f"band V b={b} h={h}"
-    return st
-
-
-def check_int4(bc, b, h, pages):
-    T = int(bc.lens[b])
-    k, v = source_of(bc.wl, b, T)
-    st = O.int4_state(k[:, h], v[:, h], T, bc.rk.astype(np.int8), bc.rv.astype(np.int8))
-    got = read_int4_tokens(bc, pages, b, h, T)
-    for key in ("k_codes", "v_codes", "k_s16", "k_z16", "v_s16", "v_z16"):
-        if not np.array_equal(got[key], st[key]):
-            bad = np.argwhere(got[key] != st[key])
-            raise AssertionError(f"b={b} h={h} {key}: {len(bad)} mismatches, first {bad[:5].tolist()}")
-
-
-def check_out(bc, out, q, pairs):
-    worst = 0.0
-    for b, h in pairs:
-        T = int(bc.lens[b])
-        gq = bc.wl.gq
-        got = out[b, h * gq:(h + 1) * gq]
-        if T == 0:
-            assert np.array_equal(got, np.zeros_like(got))
-            continue
-        want = oracle_out(bc, q, b, h, T)
-        err = np.abs(got - want).max()
-        worst = max(worst, err)
-        assert err <= TOL, f"b={b} h={h} T={T}: max |diff| {err:.3e}"
-    return worst
 
 
 # ------------------------------------------------------------------------- stage-wise: rotation

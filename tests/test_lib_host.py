@@ -79,6 +79,7 @@ def test_bits_per_element_match_the_pages():
     ("n_q_heads", 30, K.KVQ_EINVAL), ("n_kv_heads", 0, K.KVQ_EINVAL), ("clip_k", 0.0, K.KVQ_EINVAL),
     ("clip_v", 1.5, K.KVQ_EINVAL), ("split_tokens", 100, K.KVQ_EINVAL), ("n_sink", -1, K.KVQ_EINVAL),
     ("decode_impl", 9, K.KVQ_EINVAL), ("decode_impl", 2, K.KVQ_EUNSUPPORTED),
+    ("key_only_rotation", 2, K.KVQ_EINVAL), ("key_only_rotation", -1, K.KVQ_EINVAL), ("scheme", 3, K.KVQ_EUNSUPPORTED),
 ])
 def test_config_validation(field, value, status):
     cfg = K.make_config(8, 32)
@@ -151,3 +152,18 @@ def test_decode_implementations_accepted_for_both_schemes():
             # the nibble-digit decode exists for INT2 only
             want = K.KVQ_EUNSUPPORTED if (impl == K.DECODE_DOT8 and scheme == K.INT4_TOKEN) else K.KVQ_OK
             assert K.check_config(cfg) == want
+
+
+def test_int2_token_scheme_config():
+    """Per-token INT2: same sink/recent rules and sizes as the per-channel scheme; built on DOT8 only."""
+    for impl, want in ((K.DECODE_AUTO, K.KVQ_OK), (K.DECODE_DOT8, K.KVQ_OK), (K.DECODE_F32, K.KVQ_EUNSUPPORTED),
+                       (K.DECODE_DOT16, K.KVQ_EUNSUPPORTED)):
+        cfg = K.make_config(8, 32, scheme=K.INT2_TOKEN, decode_impl=impl)
+        assert K.check_config(cfg) == want
+    a = K.make_config(8, 32, scheme=K.INT2_TOKEN)
+    c = K.make_config(8, 32, scheme=K.INT2_CHANNEL)
+    for T in (0, 100, 4096, 32768):
+        assert K.pages_for_len(a, T) == K.pages_for_len(c, T)
+        assert K.bits_per_element(a, max(T, 1)) == K.bits_per_element(c, max(T, 1))
+    assert K.page_bytes(a) == K.page_bytes(c) and K.band_bytes(a, 4) == K.band_bytes(c, 4)
+    assert K.check_config(K.make_config(8, 32, key_only_rotation=True)) == K.KVQ_OK

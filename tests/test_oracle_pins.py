@@ -369,3 +369,49 @@ def test_int2_reconstruction_uses_the_transposed_rotation():
     xh = O.dequantize(st["k_codes"][0], st["k_s16"][0][None], st["k_z16"][0][None])
     wrong = np.linalg.norm(xh @ R.astype(np.float64) - ref) / np.linalg.norm(ref)
     assert rel < 0.6 and wrong > 1.0
+
+
+def test_int2_token_quantizer_is_the_channel_quantizer_transposed():
+    """Per-token INT2 applies R5's arithmetic along the other axis: the same codes and scale/zero bits as
+    the (pinned) per-channel quantizer on the transposed group."""
+    r = np.random.default_rng(21)
+    x = (r.standard_normal((128, 128)) * r.uniform(0.1, 5.0, size=(128, 1))).astype(np.float32)
+    x[7] = 0.25  # a constant token: b == a, so s = 1
+    q, s16, z16 = O.quantize_int2_token(x)
+    qc, sc, zc = O.quantize_int2_channel_group(x.T)
+    assert np.array_equal(q, qc.T) and np.array_equal(s16, sc) and np.array_equal(z16, zc)
+    assert O.bf16_value(s16[7]) == 1.0
+
+
+def test_int2_token_codes_on_the_grid():
+    """Tokens built as a + s n with n in {0..3} (s a power of two) get codes n and dequantize exactly."""
+    r = np.random.default_rng(22)
+    n = r.integers(0, 4, size=(64, 128))
+    n[:, 0], n[:, 1] = 0, 3  # every token spans the full range
+    a = -r.integers(1, 8, size=(64, 1)).astype(np.float32)
+    s = (2.0 ** r.integers(-3, 3, size=(64, 1))).astype(np.float32)
+    x = (a + s * n).astype(np.float32)
+    q, s16, z16 = O.quantize_int2_token(x)
+    assert np.array_equal(q, n)
+    assert np.array_equal(O.dequantize(q, s16[:, None], z16[:, None]), x.astype(np.float64))
+
+
+def test_key_only_state_is_the_identity_rotation_state():
+    """R_V = None (key-only rotation) quantizes the bf16 values themselves: the same state as R_V = I,
+    whose fp64 rotation is exact; per channel and per token."""
+    r = np.random.default_rng(23)
+    k = r.standard_normal((600, 128)).astype(np.float32)
+    v = r.standard_normal((600, 128)).astype(np.float32)
+    RK = O.oscar_rotation(r.standard_normal((128, 128))).astype(np.float32)
+    for axis in ("channel", "token"):
+        a = O.int2_state(k, v, 600, 4, 128, 0.96, 0.92, RK, None, axis=axis)
+        b = O.int2_state(k, v, 600, 4, 128, 0.96, 0.92, RK, np.eye(128, dtype=np.float32), axis=axis)
+        for key in ("k_codes", "v_codes", "k_s16", "k_z16", "v_s16", "v_z16"):
+            assert np.array_equal(a[key], b[key])
+        Ka, Va = O.int2_keys_values(a, RK, None)
+        Kb, Vb = O.int2_keys_values(b, RK, np.eye(128, dtype=np.float32))
+        assert np.array_equal(Ka, Kb) and np.array_equal(Va, Vb)
+    sk = np.where(r.integers(0, 2, 128) == 1, 1, -1).astype(np.int8)
+    st = O.int4_state(k, v, 600, sk, None)
+    qv, sv, zv = O.quantize_int4_token(O.bf16_value(O.source_to_bf16(v)))
+    assert np.array_equal(st["v_codes"], qv) and np.array_equal(st["v_s16"], sv)
