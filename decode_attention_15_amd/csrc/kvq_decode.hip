@@ -1706,21 +1706,33 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 // Merge ([OSCAR] §3.4.5 step 4, the second kernel of the split decode; [NOVA] App. B.5): one work-group
-// per (q head, seq).  The chunk partials (rotated value frame) are combined with their softmax weights
-// 2^(m_u - M), the result is un-rotated once by R_V^T, combined with the band partial (original frame)
-// and normalized.  Weights are computed once per chunk; the weighted sum over chunks spreads
-// (channel quad, chunk slice) over the 256 threads so that the partials' loads are all in flight.
+// per (kv head, seq) for its GQ query heads, 256 threads per head up to 4 heads.  Per head, the chunk
+// partials (rotated value frame) are combined with their softmax weights 2^(m_u - M); the results are
+// un-rotated by R_V^T, which the work-group reads once for all its heads (every element by one thread),
+// combined with the band partial (original frame) and normalized.  The weighted sum over chunks spreads
+// (channel quad, chunk slice) over 256 threads so that the partials' loads are all in flight.
 // ---------------------------------------------------------------------------------------------
 constexpr int kMergeSlices = 8;  // chunk slices of the weighted sum (threads = 32 channel quads x 8 slices)
 
-template <int GQ>
-__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
-  __shared__ float red[kThreads / 64];
-  __shared__ float4 osum[kMergeSlices][D / 4];
-  __shared__ float ob[D];
-  __shared__ float un[2][D];
+// HPW: query heads per work-group (all GQ heads of a kv head when there are enough (seq, kv head)
+// pairs to fill the chip, else one, so that long contexts with few sequences still spread their
+// chunk partials over many work-groups).
+template <int HPW>
+struct MergeShape {
+  static constexpr int SUB = HPW < 4 ? HPW : 4;  // 256-thread sub-blocks, one head each at a time
+  static constexpr int NT = 256 * SUB;           // threads
+  static constexpr int PARTS = NT / D;           // channel ranges of the un-rotation
+};
+
+template <int GQ, int HPW>
+__global__ __launch_bounds__(MergeShape<HPW>::NT) void merge_kernel(DecodeArgs a) {
+  constexpr int SUB = MergeShape<HPW>::SUB, NT = MergeShape<HPW>::NT, PARTS = MergeShape<HPW>::PARTS;
+  __shared__ float Ms[HPW], Ls[HPW];
+  __shared__ float4 osum[SUB][kMergeSlices][D / 4];
+  __shared__ float ob[HPW][D];
+  __shared__ float un[PARTS][HPW][D];
   const Geo& g = a.g;
-  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.seq_lens[b];
   int n_chunks;
   if (is_int2(g.scheme)) {
@@ -1730,33 +1742,34 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
     n_chunks = ((T + PAGE - 1) / PAGE + g.gpc - 1) / g.gpc;
   }
   if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;
-  const long long qi = (long long)b * g.n_q + hq;
-  const float* base = a.partials + qi * g.n_units * PART_STRIDE;  // unit 0: band, 1..n_chunks: chunks
-  const bool dense = g.rotation == KVQ_ROT_DENSE;
+  const long long q0 = (long long)b * g.n_q + (long long)blockIdx.x * HPW;  // first q head of this work-group
+  auto part_of = [&](int hh) { return a.partials + (q0 + hh) * g.n_units * PART_STRIDE; };  // unit 0: band
 
-  // 1. M = max over chunks of m_u (block reduction)
-  float mx = -INFINITY;
-  for (int u = 1 + tid; u <= n_chunks; u += kThreads) mx = fmaxf(mx, base[u * PART_STRIDE]);
-  mx = wave_max(mx);
-  if (lane == 0) red[wave] = mx;
+  // 1. per head (one wave each): M = max over chunks of m_u, L = sum_u 2^(m_u - M) l_u
+  for (int hh = wave; hh < HPW; hh += NT / 64) {
+    const float* base = part_of(hh);
+    float mx = -INFINITY;
+    for (int u = 1 + lane; u <= n_chunks; u += 64) mx = fmaxf(mx, base[u * PART_STRIDE]);
+    mx = wave_max(mx);
+    float ls = 0.0f;
+    for (int u = 1 + lane; u <= n_chunks; u += 64)
+      ls = fmaf(exp2_safe_diff(base[u * PART_STRIDE], mx), base[u * PART_STRIDE + 1], ls);
+    ls = wave_sum(ls);
+    if (lane == 0) {
+      Ms[hh] = mx;
+      Ls[hh] = ls;
+    }
+  }
   __syncthreads();
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) M = fmaxf(M, red[w]);
-  __syncthreads();
-  // 2. L = sum_u 2^(m_u - M) l_u
-  float ls = 0.0f;
-  for (int u = 1 + tid; u <= n_chunks; u += kThreads)
-    ls = fmaf(exp2_safe_diff(base[u * PART_STRIDE], M), base[u * PART_STRIDE + 1], ls);
-  ls = wave_sum(ls);
-  if (lane == 0) red[wave] = ls;
-  __syncthreads();
-  float Lq = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) Lq += red[w];
-  // 3. o[c] = sum_u 2^(m_u - M) o_u[c]: thread (channel quad cq, slice sl) sums chunks u = sl + 1 + 8k
-  {
-    const int cq = tid & (D / 4 - 1), sl = tid / (D / 4);
+  // 2. per head: o[c] = sum_u 2^(m_u - M) o_u[c]; sub-block sb takes heads sb, sb + SUB, ..; its thread
+  // (channel quad cq, slice sl) sums chunks u = sl + 1 + 8k
+  const int sb = tid >> 8, lt = tid & 255;
+  const int cq = lt & (D / 4 - 1), sl = lt / (D / 4);
+#pragma unroll 1
+  for (int h0 = 0; h0 < HPW; h0 += SUB) {
+    const int hh = h0 + sb;
+    const float* base = part_of(hh);
+    const float M = Ms[hh];
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll 4
     for (int u = 1 + sl; u <= n_chunks; u += kMergeSlices) {
@@ -1768,69 +1781,89 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
       acc.z = fmaf(w, o23.x, acc.z);
       acc.w = fmaf(w, o23.y, acc.w);
     }
-    osum[sl][cq] = acc;
-  }
-  __syncthreads();
-  if (tid < D) {
-    const int cq = tid >> 2, k = tid & 3;
-    float v = 0.0f;
+    osum[sb][sl][cq] = acc;
+    __syncthreads();
+    if (lt < D) {
+      const int k = lt & 3;
+      float v = 0.0f;
 #pragma unroll
-    for (int sl = 0; sl < kMergeSlices; ++sl) {
-      const float4 t = osum[sl][cq];
-      v += k == 0 ? t.x : k == 1 ? t.y : k == 2 ? t.z : t.w;
+      for (int s2 = 0; s2 < kMergeSlices; ++s2) {
+        const float4 t = osum[sb][s2][lt >> 2];
+        v += k == 0 ? t.x : k == 1 ? t.y : k == 2 ? t.z : t.w;
+      }
+      ob[hh][lt] = v;
     }
-    ob[tid] = v;
+    __syncthreads();
   }
-  __syncthreads();
-  // 4. un-rotate: o_j = sum_c ob[c] R_V[j][c] (dense), or the randomized Hadamard's inverse; nothing
-  // under key-only rotation (the values were never rotated)
-  const int j = tid & (D - 1), half = tid >> 7;
+  // 3. un-rotate every head: o_j = sum_c ob[c] R_V[j][c] (dense: thread (j, part) reads the part-th
+  // range of row j of R_V, once for all heads), the randomized Hadamard's inverse, or nothing under
+  // key-only rotation
   if (g.key_only) {
-    if (tid < D) {
-      un[0][tid] = ob[tid];
-      un[1][tid] = 0.0f;
-    }
-    __syncthreads();
-  } else if (dense) {
-    const float4* row = reinterpret_cast<const float4*>(a.rot_v + j * D + half * 64);
-    float s0 = 0.0f, s1 = 0.0f;
+    for (int e = tid; e < HPW * D; e += NT) {
+      un[0][e / D][e % D] = ob[e / D][e % D];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+      for (int p = 1; p < PARTS; ++p) un[p][e / D][e % D] = 0.0f;
+    }
+  } else if (g.rotation == KVQ_ROT_DENSE) {
+    constexpr int CPP = D / PARTS;  // channels per part
+    const int j = tid & (D - 1), part = tid / D;
+    const float4* row = reinterpret_cast<const float4*>(a.rot_v + j * D + part * CPP);
+    float s0[HPW], s1[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) s0[hh] = s1[hh] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPP / 4; ++i) {
       const float4 r = row[i];
-      s0 = fmaf(ob[half * 64 + 4 * i], r.x, s0);
-      s1 = fmaf(ob[half * 64 + 4 * i + 1], r.y, s1);
-      s0 = fmaf(ob[half * 64 + 4 * i + 2], r.z, s0);
-      s1 = fmaf(ob[half * 64 + 4 * i + 3], r.w, s1);
+      const int c = part * CPP + 4 * i;
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        s0[hh] = fmaf(ob[hh][c], r.x, s0[hh]);
+        s1[hh] = fmaf(ob[hh][c + 1], r.y, s1[hh]);
+        s0[hh] = fmaf(ob[hh][c + 2], r.z, s0[hh]);
+        s1[hh] = fmaf(ob[hh][c + 3], r.w, s1[hh]);
+      }
     }
-    un[half][j] = s0 + s1;
-    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) un[part][hh][j] = s0[hh] + s1[hh];
   } else {
-    // (ob H) * sign / sqrt(128): FWHT in LDS
+    // (ob H) * sign / sqrt(128): FWHT in LDS over all heads at once
     for (int hb = 1; hb < D; hb <<= 1) {
-      float x = 0.0f;
-      if (tid < D) x = (tid & hb) ? (ob[tid ^ hb] - ob[tid]) : (ob[tid] + ob[tid ^ hb]);
+      float x[(HPW * D + NT - 1) / NT];
+      int n = 0;
+      for (int e = tid; e < HPW * D; e += NT) {
+        const int hh = e / D, c = e % D;
+        x[n++] = (c & hb) ? (ob[hh][c ^ hb] - ob[hh][c]) : (ob[hh][c] + ob[hh][c ^ hb]);
+      }
       __syncthreads();
-      if (tid < D) ob[tid] = x;
+      n = 0;
+      for (int e = tid; e < HPW * D; e += NT) ob[e / D][e % D] = x[n++];
       __syncthreads();
     }
-    if (tid < D) {
-      un[0][tid] = ob[tid] * a.rot_v[tid] * kInvSqrt128;
-      un[1][tid] = 0.0f;
+    for (int e = tid; e < HPW * D; e += NT) {
+      un[0][e / D][e % D] = ob[e / D][e % D] * a.rot_v[e % D] * kInvSqrt128;
+#pragma unroll
+      for (int p = 1; p < PARTS; ++p) un[p][e / D][e % D] = 0.0f;
     }
-    __syncthreads();
   }
-  // 5. combine with the band partial (unit 0, original frame) and normalize
-  if (tid < D) {
+  __syncthreads();
+  // 4. combine with the band partial (unit 0, original frame) and normalize
+  for (int e = tid; e < HPW * D; e += NT) {
+    const int hh = e / D, c = e % D;
+    const float* base = part_of(hh);
+    const float M = Ms[hh];
     const float mb = (T > 0) ? base[0] : -INFINITY;
     const float Mf = fmaxf(M, mb);
     float res = 0.0f;
     if (Mf != -INFINITY) {
-      const float si = exp2_safe_diff(M, Mf), sb = exp2_safe_diff(mb, Mf);
-      const float num = (un[0][tid] + un[1][tid]) * si + (mb == -INFINITY ? 0.0f : base[2 + tid] * sb);
-      const float den = Lq * si + (mb == -INFINITY ? 0.0f : base[1] * sb);
+      float o = 0.0f;
+#pragma unroll
+      for (int p = 0; p < PARTS; ++p) o += un[p][hh][c];
+      const float si = exp2_safe_diff(M, Mf), sb2 = exp2_safe_diff(mb, Mf);
+      const float num = o * si + (mb == -INFINITY ? 0.0f : base[2 + c] * sb2);
+      const float den = Ls[hh] * si + (mb == -INFINITY ? 0.0f : base[1] * sb2);
       res = num / den;
     }
-    a.out[qi * D + tid] = res;
+    a.out[(q0 + hh) * D + c] = res;
   }
 }
 
@@ -1853,7 +1886,12 @@ hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
       else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_TOKEN, 0>), grid, block, 0, s, a);
     }
   }
-  if (stages & KVQ_STAGE_MERGE) hipLaunchKernelGGL(merge_kernel<GQ>, dim3(g.n_q, g.batch), dim3(kThreads), 0, s, a);
+  if (stages & KVQ_STAGE_MERGE) {
+    if (g.batch * g.n_kv >= 128)
+      hipLaunchKernelGGL((merge_kernel<GQ, GQ>), dim3(g.n_kv, g.batch), dim3(MergeShape<GQ>::NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((merge_kernel<GQ, 1>), dim3(g.n_q, g.batch), dim3(MergeShape<1>::NT), 0, s, a);
+  }
   return hipGetLastError();
 }
 
