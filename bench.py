@@ -39,6 +39,8 @@ def parse():
                     help="INT2 workloads: quantize per channel over 128-token groups (the workloads' statement) "
                          "or per token over its 128 channels")
     ap.add_argument("--key-only", action="store_true", help="rotate K only; V quantized in its own frame")
+    ap.add_argument("--hadamard-block", type=int, default=0, choices=[0, 16, 32, 64, 128],
+                    help="block order of the randomized Hadamard (workloads with that rotation; 0 = 128)")
     ap.add_argument("--split", type=int, default=0, help="quantized tokens per decode work-group (0 = auto)")
     ap.add_argument("--cpu-pairs", type=int, default=2, help="distinct (seq, kv head) pairs in the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -119,7 +121,8 @@ def cpu_baseline(wl, args, T, rk, rv):
             if int2:
                 st = O.int2_state(k, v, T, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v, rk, rv, axis=axis)
             else:
-                st = O.int4_state(k, v, T, rk.astype(np.int8), None if rv is None else rv.astype(np.int8))
+                st = O.int4_state(k, v, T, rk.astype(np.int8), None if rv is None else rv.astype(np.int8),
+                                  block=wl.hadamard_block)
             states.append((b, h, st))
         while total_s < args.cpu_seconds:
             b, h, st = states[runs % len(states)]
@@ -127,7 +130,8 @@ def cpu_baseline(wl, args, T, rk, rv):
             if int2:
                 Kh, Vh = O.int2_keys_values(st, rk, rv)
             else:
-                Kh, Vh = O.int4_keys_values(st, rk.astype(np.int8), None if rv is None else rv.astype(np.int8))
+                Kh, Vh = O.int4_keys_values(st, rk.astype(np.int8), None if rv is None else rv.astype(np.int8),
+                                            wl.hadamard_block)
             O.attend(O.query_values(q[b, h * wl.gq:(h + 1) * wl.gq]), Kh, Vh)
             total_s += time.perf_counter() - t0
             if int2:
@@ -179,6 +183,8 @@ def main():
         wl = synth.scaled(wl, scheme=args.scheme)
     if args.key_only:
         wl = synth.scaled(wl, key_only=True)
+    if args.hadamard_block and wl.rotation == "saw":
+        wl = synth.scaled(wl, hadamard_block=args.hadamard_block)
     int2 = wl.scheme in ("int2_channel", "int2_token")
     dev = "cuda"
     torch.cuda.set_device(0)
@@ -196,7 +202,8 @@ def main():
         rk = K.build_oscar_rotation(synth.rotation_gaussian(wl, "k")).astype(np.float32)
         rv = K.build_oscar_rotation(synth.rotation_gaussian(wl, "v")).astype(np.float32)
     else:
-        cfg = K.make_config(n_kv, n_q, K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0, split, impl, wl.key_only)
+        cfg = K.make_config(n_kv, n_q, K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0, split, impl, wl.key_only,
+                            wl.hadamard_block)
         rk = synth.sign_vector(wl, "k").astype(np.float32)
         rv = synth.sign_vector(wl, "v").astype(np.float32)
     max_pages = K.pages_for_len(cfg, T_end)
@@ -296,7 +303,8 @@ def main():
     log(f"[bench] split-K kernel {kern_ms * 1e3:.1f} us, {achieved:.0f} GB/s; kernels {stage_us}")
 
     variant = ("" if wl.scheme == synth.WORKLOADS[args.workload].scheme else wl.scheme) + \
-        (" key-only" if wl.key_only else "")
+        (" key-only" if wl.key_only else "") + \
+        (f" hadamard-{wl.hadamard_block}" if wl.rotation == "saw" and wl.hadamard_block != 128 else "")
     traffic = read_traffic(wl.name, variant.strip())
 
     result = {
@@ -317,8 +325,9 @@ def main():
                    "head_dim": 128,
                    "scheme": ({"int2_channel": "int2 per-channel, 128-token groups, bf16 scale/zero",
                                "int2_token": "int2 per-token over 128 channels, bf16 scale/zero",
-                               "int4_token": "int4 per-token, bf16 scale/zero, randomized Hadamard (block 128)"}
-                              [wl.scheme] + (", key-only rotation" if wl.key_only else "")),
+                               "int4_token": "int4 per-token, bf16 scale/zero, randomized Hadamard"}
+                              [wl.scheme] + (", key-only rotation" if wl.key_only else "") +
+                              (f", Hadamard block {wl.hadamard_block}" if wl.rotation == "saw" else "")),
                    "sink_recent": [wl.n_sink, wl.n_recent], "page_tokens": 64, "split_tokens": split,
                    "decode_impl": args.impl, "step": "append 1 token/seq (write) + decode attention"},
         "steps_per_s": round(1000.0 / ms_step, 2),

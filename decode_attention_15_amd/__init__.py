@@ -42,7 +42,7 @@ class Config(ctypes.Structure):
         ("scheme", ctypes.c_int32), ("rotation", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
         ("group_tokens", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("n_recent", ctypes.c_int32),
         ("clip_k", ctypes.c_float), ("clip_v", ctypes.c_float), ("split_tokens", ctypes.c_int32),
-        ("decode_impl", ctypes.c_int32), ("key_only_rotation", ctypes.c_int32),
+        ("decode_impl", ctypes.c_int32), ("key_only_rotation", ctypes.c_int32), ("hadamard_block", ctypes.c_int32),
     ]
 
 
@@ -128,9 +128,10 @@ def _check(status: int, what: str) -> None:
 
 def make_config(n_kv_heads: int, n_q_heads: int, scheme: int = INT2_CHANNEL, rotation: int = ROT_DENSE,
                 n_sink: int = 4, n_recent: int = 128, clip_k: float = 0.96, clip_v: float = 0.92,
-                split_tokens: int = 0, decode_impl: int = DECODE_AUTO, key_only_rotation: bool = False) -> Config:
+                split_tokens: int = 0, decode_impl: int = DECODE_AUTO, key_only_rotation: bool = False,
+                hadamard_block: int = 0) -> Config:
     return Config(128, n_kv_heads, n_q_heads, scheme, rotation, 64, 128, n_sink, n_recent, clip_k, clip_v,
-                  split_tokens, decode_impl, int(key_only_rotation))
+                  split_tokens, decode_impl, int(key_only_rotation), hadamard_block)
 
 
 def check_config(cfg: Config) -> int:

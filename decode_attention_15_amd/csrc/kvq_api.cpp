@@ -37,6 +37,10 @@ int check_config(const kvq_config* c) {
   if (c->scheme == KVQ_INT2_TOKEN && c->decode_impl != KVQ_DECODE_AUTO && c->decode_impl != KVQ_DECODE_DOT8)
     return KVQ_EUNSUPPORTED;
   if (c->key_only_rotation != 0 && c->key_only_rotation != 1) return KVQ_EINVAL;
+  const int hb = c->hadamard_block;
+  if (c->rotation == KVQ_ROT_HADAMARD ? (hb != 0 && hb != 16 && hb != 32 && hb != 64 && hb != 128)
+                                      : (hb != 0 && hb != 128))
+    return KVQ_EINVAL;
   return KVQ_OK;
 }
 
@@ -90,6 +94,13 @@ Geo make_geo(const kvq_config* c, const kvq_cache* k) {
   g.scheme = c->scheme;
   g.rotation = c->rotation;
   g.key_only = c->key_only_rotation;
+  g.hblock = c->hadamard_block ? c->hadamard_block : D;
+  {
+    int k = 0;
+    while ((1 << k) < g.hblock) ++k;
+    // 1/sqrt(2^k): exact for even k, fp64(sqrt 2) scaled by a power of two for odd k
+    g.hscale = (k % 2 == 0) ? ldexp(1.0, -k / 2) : ldexp(sqrt(2.0), -(k + 1) / 2);
+  }
   g.S0 = c->n_sink;
   g.W = c->n_recent;
   g.slots = kvq_band_slots(c);
@@ -333,7 +344,9 @@ int kvq_debug_rotate(const kvq_config* cfg, const kvq_cache* cache, int32_t whic
   float f;
   clip_params(rho, &j, &f);
   clear_stale_error();
-  return to_status(launch_debug_rotate(rot, cfg->rotation, x, dtype == KVQ_BF16, n, j, f, out, stream),
+  const Geo g = make_geo(cfg, cache);
+  return to_status(launch_debug_rotate(rot, cfg->rotation, g.hblock, g.hscale, x, dtype == KVQ_BF16, n, j, f, out,
+                                       stream),
                    "kvq_debug_rotate");
 }
 

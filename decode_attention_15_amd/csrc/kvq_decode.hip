@@ -118,8 +118,8 @@ __global__ __launch_bounds__(512) void qprep_kernel(DecodeArgs a) {
       a.qrot[base + e] = ((part[0][hh][c] + part[1][hh][c]) + (part[2][hh][c] + part[3][hh][c])) * scale;
     }
   } else {
-    // randomized Hadamard: FWHT in LDS, one element per thread
-    for (int hb = 1; hb < D; hb <<= 1) {
+    // randomized (block-diagonal) Hadamard: FWHT within blocks of h channels in LDS
+    for (int hb = 1; hb < a.g.hblock; hb <<= 1) {
       float x[GQ / 4 + 1];
       int n = 0;
       for (int e = tid; e < GQ * D; e += 512) {
@@ -132,7 +132,8 @@ __global__ __launch_bounds__(512) void qprep_kernel(DecodeArgs a) {
       for (int e = tid; e < GQ * D; e += 512) qs[e / D][e % D] = x[n++];
       __syncthreads();
     }
-    for (int e = tid; e < GQ * D; e += 512) a.qrot[base + e] = qs[e / D][e % D] * kInvSqrt128 * scale;
+    const float hs = (float)a.g.hscale;
+    for (int e = tid; e < GQ * D; e += 512) a.qrot[base + e] = qs[e / D][e % D] * hs * scale;
   }
 }
 
@@ -1625,10 +1626,11 @@ __device__ void int4_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
       float mnew;
       softmax_update<GQ>(m, l, o, hh, wave_max(x), mnew);
       const float p = valid ? exp2f(x - mnew) : 0.0f;
-      const float w = p * sv;
+      // slots past the end of the sequence hold unwritten scales/zeros: keep them out of every sum
+      const float w = valid ? p * sv : 0.0f;
       L.f.p[wave][hh][lane] = w;
       l[hh] += wave_sum(p);
-      wz[hh] = wave_sum(w * zv);
+      wz[hh] = wave_sum(valid ? w * zv : 0.0f);
     }
     wave_lds_sync();
     // V: channels lane and lane + 64, rows of 32 bytes; token 16j + 4g + r in byte 8g + 2j + r/2
@@ -1826,8 +1828,8 @@ __global__ __launch_bounds__(MergeShape<HPW>::NT) void merge_kernel(DecodeArgs a
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) un[part][hh][j] = s0[hh] + s1[hh];
   } else {
-    // (ob H) * sign / sqrt(128): FWHT in LDS over all heads at once
-    for (int hb = 1; hb < D; hb <<= 1) {
+    // (ob H_blk) * sign / sqrt(h): FWHT within blocks of h channels in LDS, all heads at once
+    for (int hb = 1; hb < g.hblock; hb <<= 1) {
       float x[(HPW * D + NT - 1) / NT];
       int n = 0;
       for (int e = tid; e < HPW * D; e += NT) {
@@ -1840,7 +1842,7 @@ __global__ __launch_bounds__(MergeShape<HPW>::NT) void merge_kernel(DecodeArgs a
       __syncthreads();
     }
     for (int e = tid; e < HPW * D; e += NT) {
-      un[0][e / D][e % D] = ob[e / D][e % D] * a.rot_v[e % D] * kInvSqrt128;
+      un[0][e / D][e % D] = ob[e / D][e % D] * a.rot_v[e % D] * (float)g.hscale;
 #pragma unroll
       for (int p = 1; p < PARTS; ++p) un[p][e / D][e % D] = 0.0f;
     }

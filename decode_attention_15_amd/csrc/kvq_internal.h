@@ -38,6 +38,8 @@ struct Geo {
   int scheme;
   int rotation;
   int key_only;     // 1: V neither rotated on write nor un-rotated on read
+  int hblock;       // Hadamard block order h (16, 32, 64, 128)
+  double hscale;    // its fp64 normalization 1/sqrt(h)
   int S0;
   int W;
   int slots;        // band slots per (seq, kv head)
@@ -88,8 +90,8 @@ struct WriteArgs {
 
 hipError_t launch_write_int2(const WriteArgs& a, hipStream_t s);
 hipError_t launch_write_int4(const WriteArgs& a, hipStream_t s);
-hipError_t launch_debug_rotate(const float* rot, int rotation, const void* x, int src_bf16, int n, int clip_j,
-                               float clip_f, float* out, hipStream_t s);
+hipError_t launch_debug_rotate(const float* rot, int rotation, int hblock, double hscale, const void* x, int src_bf16,
+                               int n, int clip_j, float clip_f, float* out, hipStream_t s);
 
 struct DecodeArgs {
   Geo g;

@@ -82,10 +82,12 @@ __device__ inline float clip_tau(float x0, float x1, int j, float f) {
 }
 
 // Unnormalized radix-2 Walsh-Hadamard transform of 128 fp64 values held as (e0 = x[lane],
-// e1 = x[lane + 64]); stages h = 1, 2, ..., 64 each map the pair (i, i+h), i & h == 0, to (a+b, a-b).
-__device__ inline void fwht128_wave(double& e0, double& e1, int lane) {
+// e1 = x[lane + 64]), on every block of `block` consecutive values: stages h = 1, 2, ..., block/2 each
+// map the pair (i, i+h), i & h == 0, to (a+b, a-b).
+__device__ inline void fwht_wave(double& e0, double& e1, int lane, int block) {
 #pragma unroll
   for (int h = 1; h < 64; h <<= 1) {
+    if (h >= block) break;
     const double p0 = __shfl_xor(e0, h, 64);
     const double p1 = __shfl_xor(e1, h, 64);
     if (lane & h) {
@@ -96,15 +98,17 @@ __device__ inline void fwht128_wave(double& e0, double& e1, int lane) {
       e1 = e1 + p1;
     }
   }
-  const double a = e0, b = e1;
-  e0 = a + b;
-  e1 = a - b;
+  if (block == 128) {
+    const double a = e0, b = e1;
+    e0 = a + b;
+    e1 = a - b;
+  }
 }
 
 // Rotation of one vector whose 128 bf16 values are in LDS (xs) into (y0, y1) = (x~[lane], x~[lane+64]).
-// Dense: fp64 products summed in increasing i, rounded once.  Hadamard: sign flip, FWHT, * 1/sqrt(128).
-__device__ inline void rotate_vec(const float* xs, const float* rot, int rotation, int lane, float& y0,
-                                  float& y1) {
+// Dense: fp64 products summed in increasing i, rounded once.  Hadamard: sign flip, block FWHT, * 1/sqrt(h).
+__device__ inline void rotate_vec(const float* xs, const float* rot, int rotation, int hblock, double hscale,
+                                  int lane, float& y0, float& y1) {
   if (rotation == KVQ_ROT_DENSE) {
     double a0 = 0.0, a1 = 0.0;
     for (int i = 0; i < D; ++i) {
@@ -117,9 +121,9 @@ __device__ inline void rotate_vec(const float* xs, const float* rot, int rotatio
   } else {
     double e0 = (double)xs[lane] * (double)rot[lane];
     double e1 = (double)xs[lane + 64] * (double)rot[lane + 64];
-    fwht128_wave(e0, e1, lane);
-    y0 = (float)(e0 * INV_SQRT128_F64);
-    y1 = (float)(e1 * INV_SQRT128_F64);
+    fwht_wave(e0, e1, lane, hblock);
+    y0 = (float)(e0 * hscale);
+    y1 = (float)(e1 * hscale);
   }
 }
 
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
   } else {
     for (int tl = wave * 32; tl < wave * 32 + 32; ++tl) {
       float y0, y1;
-      rotate_vec(xs + tl * XS_STRIDE, rot, g.rotation, lane, y0, y1);
+      rotate_vec(xs + tl * XS_STRIDE, rot, g.rotation, g.hblock, g.hscale, lane, y0, y1);
       xr[tl * D + lane] = y0;
       xr[tl * D + lane + 64] = y1;
     }
@@ -399,7 +403,7 @@ __global__ __launch_bounds__(256) void int4_quad_kernel(WriteArgs a) {
       y0 = xs[wave][lane];
       y1 = xs[wave][lane + 64];
     } else {
-      rotate_vec(xs[wave], rot, g.rotation, lane, y0, y1);
+      rotate_vec(xs[wave], rot, g.rotation, g.hblock, g.hscale, lane, y0, y1);
     }
     const float amin = wave_min_f32(fminf(y0, y1));
     const float bmax = wave_max_f32(fmaxf(y0, y1));
@@ -446,8 +450,9 @@ __global__ __launch_bounds__(256) void int4_quad_kernel(WriteArgs a) {
   }
 }
 
-__global__ __launch_bounds__(64) void debug_rotate_kernel(const float* rot, int rotation, const void* x, int src_bf16,
-                                                          int n, int clip_j, float clip_f, float* out) {
+__global__ __launch_bounds__(64) void debug_rotate_kernel(const float* rot, int rotation, int hblock, double hscale,
+                                                          const void* x, int src_bf16, int n, int clip_j, float clip_f,
+                                                          float* out) {
   __shared__ float xs[D];
   const int v = blockIdx.x, lane = threadIdx.x;
   if (v >= n) return;
@@ -455,7 +460,7 @@ __global__ __launch_bounds__(64) void debug_rotate_kernel(const float* rot, int 
   xs[lane + 64] = src_as_bf16_value(x, src_bf16, (long long)v * D + lane + 64);
   __syncthreads();
   float y0, y1;
-  rotate_vec(xs, rot, rotation, lane, y0, y1);
+  rotate_vec(xs, rot, rotation, hblock, hscale, lane, y0, y1);
   if (clip_j < D - 1) {
     const float tau = clip_tau(y0, y1, clip_j, clip_f);
     y0 = fminf(fmaxf(y0, -tau), tau);
@@ -493,10 +498,11 @@ hipError_t launch_write_int4(const WriteArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_debug_rotate(const float* rot, int rotation, const void* x, int src_bf16, int n, int clip_j,
-                               float clip_f, float* out, hipStream_t s) {
-  if (n > 0) hipLaunchKernelGGL(debug_rotate_kernel, dim3(n), dim3(64), 0, s, rot, rotation, x, src_bf16, n, clip_j,
-                                clip_f, out);
+hipError_t launch_debug_rotate(const float* rot, int rotation, int hblock, double hscale, const void* x, int src_bf16,
+                               int n, int clip_j, float clip_f, float* out, hipStream_t s) {
+  if (n > 0)
+    hipLaunchKernelGGL(debug_rotate_kernel, dim3(n), dim3(64), 0, s, rot, rotation, hblock, hscale, x, src_bf16, n,
+                       clip_j, clip_f, out);
   return hipGetLastError();
 }
 

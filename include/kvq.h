@@ -56,7 +56,9 @@
  *    those bf16 values, exactly as a token demoted from the bf16 recent window.
  *  - Dense rotation: x~_j = fp32( fp64 sum over i = 0..127 in increasing i of x_i * R[i][j] ).
  *    Randomized Hadamard ([SAW]): sign flip, radix-2 butterflies (a+b, a-b) for h = 1..64 in fp64,
- *    times 1/sqrt(128) (= sqrt(2)*2^-4 in fp64), rounded to fp32.
+ *    times 1/sqrt(128) (= sqrt(2)*2^-4 in fp64), rounded to fp32.  Block order h < 128: the butterflies
+ *    for h' = 1..h/2 only (each block of h channels separately), times 1/sqrt(h) = 2^(-k/2) for even
+ *    k = log2 h, fp64(sqrt(2)) * 2^(-(k+1)/2) for odd k.
  *  - Clip ([OSCAR] §3.4.4): tau = y[j] + f*(y[j+1] - y[j]) in fp32 without fusion, y = sorted |x~|,
  *    j = floor(127*rho), f = fp32(127*rho - j) (tau = y[127] when j = 127); x = min(max(x~, -tau), tau).
  *  - INT2 per channel over the group: s = fp32((b-a)/3) (1 if b == a) -> bf16 s'; z = fp32(-a/s') ->
@@ -133,6 +135,9 @@ typedef struct {
   int32_t key_only_rotation;  /* 0: K and V rotated (V by R_V on write, outputs un-rotated by R_V^T);
                                  1: only K rotated ([SAW] App. C default), V kept in its own frame and
                                  kvq_cache.rot_v unused (may be NULL) */
+  int32_t hadamard_block;     /* HADAMARD rotation: block order h of [SAW] eq. (1), the same normalized
+                                 h x h Hadamard on each block of h channels after the sign flip:
+                                 16, 32, 64 or 128 (0 = 128); DENSE: 0 or 128 */
 } kvq_config;
 
 /* Device-resident cache of a batch of sequences.  All pointers are device pointers owned by the caller. */

@@ -22,6 +22,8 @@ Readings taken where the pages leave a step open (each listed in the design doc):
       rounded once to fp32.  Randomized Hadamard ([SAW] §3, "applied via FWHT"):
       signs, then the radix-2 butterflies (a+b, a-b) for h = 1, 2, ..., 64 in
       fp64, then a multiply by 1/sqrt(128) = sqrt(2)*2^-4 in fp64, rounded to fp32.
+      Block order h < 128 ([SAW] eq. (1)): butterflies for h' < h only, within each
+      block, and 1/sqrt(h) = 2^(-k/2) (k = log2 h even) or sqrt(2)*2^(-(k+1)/2) (odd).
   R3  Clip ([OSCAR] §3.4.4 step 2): tau = linear-interpolation quantile of |x~|
       over the 128 channels: y sorted ascending, h = 127*rho (double), j = floor(h),
       f = fp32(h - j), tau = y[j] + f*(y[j+1]-y[j]) in fp32 with each operation
@@ -123,9 +125,14 @@ def oscar_rotation(G: np.ndarray) -> np.ndarray:
     return orthonormal_from_gaussian(G) @ hadamard(G.shape[0]) @ bit_reversal_matrix(G.shape[0])
 
 
-def saw_rotation_matrix(sign: np.ndarray) -> np.ndarray:
-    """Dense fp64 form of the randomized Hadamard diag(sign) . H ([SAW] §3, block h = d)."""
-    return np.asarray(sign, dtype=np.float64)[:, None] * hadamard(len(sign))
+def saw_rotation_matrix(sign: np.ndarray, block: int = D) -> np.ndarray:
+    """Dense fp64 form of the randomized block-diagonal Hadamard diag(sign) . diag(H_h, ..., H_h)
+    ([SAW] §3 eq. (1): each block of h channels rotated by the same normalized h x h Hadamard)."""
+    d = len(sign)
+    Hb = np.zeros((d, d))
+    for i in range(0, d, block):
+        Hb[i:i + block, i:i + block] = hadamard(block)
+    return np.asarray(sign, dtype=np.float64)[:, None] * Hb
 
 
 # ----------------------------------------------------------------------------
@@ -188,15 +195,17 @@ def rotate_dense(x: np.ndarray, R32: np.ndarray) -> np.ndarray:
 INV_SQRT128_F64 = float(np.ldexp(np.sqrt(2.0), -4))
 
 
-def fwht_fp64(y: np.ndarray) -> np.ndarray:
-    """Unnormalized radix-2 Walsh-Hadamard transform along the last axis, fp64.
+def fwht_fp64(y: np.ndarray, block: Optional[int] = None) -> np.ndarray:
+    """Unnormalized radix-2 Walsh-Hadamard transform along the last axis, fp64, on every block of
+    `block` consecutive entries (default: the whole axis).
 
-    Stage h (h = 1, 2, ..., d/2) maps each pair (i, i+h) with i & h == 0 to (a+b, a-b).
+    Stage h (h = 1, 2, ..., block/2) maps each pair (i, i+h) with i & h == 0 to (a+b, a-b).
     """
     y = np.array(y, dtype=np.float64, copy=True)
     d = y.shape[-1]
+    block = d if block is None else block
     h = 1
-    while h < d:
+    while h < block:
         yr = y.reshape(y.shape[:-1] + (d // (2 * h), 2, h))
         a = yr[..., 0, :].copy()
         b = yr[..., 1, :].copy()
@@ -206,10 +215,19 @@ def fwht_fp64(y: np.ndarray) -> np.ndarray:
     return y
 
 
-def rotate_hadamard(x: np.ndarray, sign: np.ndarray) -> np.ndarray:
-    """Reading R2 for the randomized Hadamard of [SAW] §3: x . diag(sign) . H, computed via FWHT."""
+def hadamard_scale(block: int) -> float:
+    """fp64 normalization 1/sqrt(h) of an order-h = 2^k Hadamard block (reading R2): 2^(-k/2) exactly for
+    even k, fp64(sqrt(2)) * 2^(-(k+1)/2) for odd k (so h = 128 gives sqrt(2) * 2^-4)."""
+    k = block.bit_length() - 1
+    assert block == 1 << k
+    return 2.0 ** (-k // 2) if k % 2 == 0 else float(np.sqrt(2.0)) * 2.0 ** (-(k + 1) // 2)
+
+
+def rotate_hadamard(x: np.ndarray, sign: np.ndarray, block: int = D) -> np.ndarray:
+    """Reading R2 for the randomized (block-diagonal) Hadamard of [SAW] §3 eq. (1):
+    x . diag(sign) . diag(H_h, ..., H_h), computed per block via FWHT in fp64, rounded once."""
     y = np.asarray(x, dtype=np.float64) * np.asarray(sign, dtype=np.float64)[None, :]
-    return (fwht_fp64(y) * INV_SQRT128_F64).astype(np.float32)
+    return (fwht_fp64(y, block) * hadamard_scale(block)).astype(np.float32)
 
 
 def clip_index(rho: float):
@@ -367,14 +385,14 @@ def int2_state(k_src, v_src, T: int, n_sink: int, n_recent: int, clip_k: float, 
 
 
 def int4_state(k_src, v_src, T: int, sign_k: np.ndarray, sign_v: Optional[np.ndarray],
-               tokens=None) -> Dict[str, np.ndarray]:
+               tokens=None, block: int = D) -> Dict[str, np.ndarray]:
     """Token-wise INT4 state of one (seq, kv head) after the randomized Hadamard ([SAW]); sign_v = None:
     key-only rotation ([SAW] App. C), values quantized in their own frame."""
     idx = np.arange(T) if tokens is None else np.asarray(tokens)
     kb = source_to_bf16(np.asarray(k_src)[idx])
     vb = source_to_bf16(np.asarray(v_src)[idx])
-    qk, sk, zk = quantize_int4_token(rotate_hadamard(bf16_value(kb), sign_k))
-    xv = bf16_value(vb) if sign_v is None else rotate_hadamard(bf16_value(vb), sign_v)
+    qk, sk, zk = quantize_int4_token(rotate_hadamard(bf16_value(kb), sign_k, block))
+    xv = bf16_value(vb) if sign_v is None else rotate_hadamard(bf16_value(vb), sign_v, block)
     qv, sv, zv = quantize_int4_token(xv)
     return {"tokens": idx, "k_codes": qk, "k_s16": sk, "k_z16": zk,
             "v_codes": qv, "v_s16": sv, "v_z16": zv}
@@ -412,9 +430,9 @@ def int2_keys_values(state, R_K32, R_V32):
     return np.concatenate(keys), np.concatenate(vals)
 
 
-def int4_keys_values(state, sign_k, sign_v):
-    RK = np.asarray(sign_k, np.float64)[:, None] * hadamard(D)
-    RV = np.eye(D) if sign_v is None else np.asarray(sign_v, np.float64)[:, None] * hadamard(D)
+def int4_keys_values(state, sign_k, sign_v, block: int = D):
+    RK = saw_rotation_matrix(sign_k, block)
+    RV = np.eye(D) if sign_v is None else saw_rotation_matrix(sign_v, block)
     xk = dequantize(state["k_codes"], state["k_s16"][:, None], state["k_z16"][:, None])
     xv = dequantize(state["v_codes"], state["v_s16"][:, None], state["v_z16"][:, None])
     # the write multiplied by fp64(1/sqrt(128)); H here is exactly orthonormal in fp64
@@ -436,9 +454,9 @@ def decode_int2(q_heads, k_src, v_src, T, n_sink, n_recent, clip_k, clip_v, R_K3
     return attend(query_values(q_heads), K, V), st
 
 
-def decode_int4(q_heads, k_src, v_src, T, sign_k, sign_v):
-    st = int4_state(k_src, v_src, T, sign_k, sign_v)
-    K, V = int4_keys_values(st, sign_k, sign_v)
+def decode_int4(q_heads, k_src, v_src, T, sign_k, sign_v, block: int = D):
+    st = int4_state(k_src, v_src, T, sign_k, sign_v, block=block)
+    K, V = int4_keys_values(st, sign_k, sign_v, block)
     return attend(query_values(q_heads), K, V), st
 
 

@@ -51,6 +51,7 @@ class Workload:
     split_tokens: int = 512
     rotation: str = "oscar"     # "oscar" (QR·H·P_br) | "saw" (diag(sign)·H)
     key_only: bool = False      # rotate K only; V quantized in its own frame
+    hadamard_block: int = 128   # block order h of the randomized Hadamard ("saw" rotation)
     seed: int = 1000
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 

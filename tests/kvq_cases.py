@@ -24,9 +24,9 @@ def config_for(K, wl: synth.Workload, split_tokens: int = 0, decode_impl: int = 
     if wl.scheme in ("int2_channel", "int2_token"):
         scheme = K.INT2_CHANNEL if wl.scheme == "int2_channel" else K.INT2_TOKEN
         return K.make_config(wl.n_kv_heads, wl.n_q_heads, scheme, rot, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v,
-                             split_tokens, decode_impl, wl.key_only)
+                             split_tokens, decode_impl, wl.key_only, wl.hadamard_block if wl.rotation == "saw" else 0)
     return K.make_config(wl.n_kv_heads, wl.n_q_heads, K.INT4_TOKEN, rot, 0, 0, 1.0, 1.0, split_tokens, decode_impl,
-                         wl.key_only)
+                         wl.key_only, wl.hadamard_block if wl.rotation == "saw" else 0)
 
 
 def rotations(wl: synth.Workload):
@@ -74,6 +74,9 @@ def build_cache(K, wl: synth.Workload, lens, append_steps: int = 0, chunk: Optio
     rk, rv = rotations(wl)
     cache = K.allocate_cache(cfg, B, torch.from_numpy(pt), torch.from_numpy(rk),
                              None if rv is None else torch.from_numpy(rv), n_pages=n_pool, device=device)
+    # unwritten bytes are 0xFF (bf16 NaN scales/zeros), so no kernel may read them into a result
+    cache.pages.fill_(255)
+    cache.band.fill_(-1)
     pre = np.maximum(lens - append_steps, 0)
     seqs_per_call = B if seqs_per_call is None else seqs_per_call
     # prefill, a group of sequences per call, optionally chunked
@@ -200,7 +203,7 @@ def oracle_out(bc: BuiltCache, q: np.ndarray, b: int, h: int, T: int) -> np.ndar
                              bc.rk, bc.rv, axis="channel" if bc.wl.scheme == "int2_channel" else "token")
     else:
         o, _ = O.decode_int4(qh, k[:, h], v[:, h], T, bc.rk.astype(np.int8),
-                             None if bc.rv is None else bc.rv.astype(np.int8))
+                             None if bc.rv is None else bc.rv.astype(np.int8), block=bc.wl.hadamard_block)
     return o
 
 
@@ -250,7 +253,8 @@ def check_int2(bc, b, h, groups=None, pages=None, band=None):
 def check_int4(bc, b, h, pages):
     T = int(bc.lens[b])
     k, v = source_of(bc.wl, b, T)
-    st = O.int4_state(k[:, h], v[:, h], T, bc.rk.astype(np.int8), None if bc.rv is None else bc.rv.astype(np.int8))
+    st = O.int4_state(k[:, h], v[:, h], T, bc.rk.astype(np.int8), None if bc.rv is None else bc.rv.astype(np.int8),
+                      block=bc.wl.hadamard_block)
     got = read_int4_tokens(bc, pages, b, h, T)
     for key in ("k_codes", "v_codes", "k_s16", "k_z16", "v_s16", "v_z16"):
         if not np.array_equal(got[key], st[key]):

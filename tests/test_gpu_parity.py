@@ -29,12 +29,14 @@ def K():
 # ------------------------------------------------------------------------- stage-wise: rotation
 
 
-@pytest.mark.parametrize("rotation", ["oscar", "saw"])
+@pytest.mark.parametrize("rotation", ["oscar", "saw", "saw16", "saw32", "saw64"])
 @pytest.mark.parametrize("rho", [1.0, 0.96, 0.92])
 def test_debug_rotate_bit_exact(K, rotation, rho):
     import torch
     from kvq_cases import config_for, rotations, source_torch
     wl = synth.WORKLOADS["gqa_b1_32k" if rotation == "oscar" else "saw_int4_b16_16k"]
+    block = int(rotation[3:]) if rotation.startswith("saw") and len(rotation) > 3 else 128
+    wl = synth.scaled(wl, hadamard_block=block)
     _say(f"debug_rotate {rotation} rho={rho}")
     rk, rv = rotations(wl)
     cfg = config_for(K, wl)
@@ -45,7 +47,7 @@ def test_debug_rotate_bit_exact(K, rotation, rho):
     K.kvq_debug_rotate(cache, 0, source_torch(x, "cuda"), rho, out)
     got = out.cpu().numpy()
     xv = O.bf16_value(x)
-    want = O.rotate_dense(xv, rk) if rotation == "oscar" else O.rotate_hadamard(xv, rk.astype(np.int8))
+    want = O.rotate_dense(xv, rk) if rotation == "oscar" else O.rotate_hadamard(xv, rk.astype(np.int8), block)
     if rho < 1.0:
         want = O.clip_tokens(want, rho)
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))

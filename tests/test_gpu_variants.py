@@ -113,3 +113,21 @@ def test_key_only_equals_an_identity_value_rotation(K):
     for phys in pt[0, :2 * O.n_groups(T, wl.n_sink, wl.n_recent)]:
         assert np.array_equal(pa[phys * pb:(phys + 1) * pb], pi[phys * pb:(phys + 1) * pb])
     assert np.abs(out.cpu().numpy() - run_decode(K, ko, q)).max() < 1e-6
+
+
+@pytest.mark.parametrize("block", [16, 32, 64])
+def test_int4_block_hadamard_orders(K, block):
+    """[SAW] eq. (1) block orders h = 16, 32, 64: codes bit-exact, outputs within the bar, through the
+    write (prefill chunks + appends), the query rotation and the merge's inverse rotation."""
+    wl = synth.scaled(synth.WORKLOADS["saw_int4_b16_16k"], hadamard_block=block)
+    lens = [1300, 511]
+    _say(f"int4 with Hadamard block {block}: lens {lens}, 3 appends")
+    bc = build_cache(K, wl, lens, append_steps=3, chunk=600)
+    pages = bc.cache.pages.cpu().numpy()
+    for b in range(len(lens)):
+        for h in (1, 7):
+            check_int4(bc, b, h, pages)
+    q = synth.queries(synth.scaled(wl, batch=len(lens)))
+    out = run_decode(K, bc, q)
+    worst = check_out(bc, out, q, [(b, h) for b in range(len(lens)) for h in range(8)])
+    _say(f"   max |out - oracle| = {worst:.2e}")

@@ -415,3 +415,49 @@ def test_key_only_state_is_the_identity_rotation_state():
     st = O.int4_state(k, v, 600, sk, None)
     qv, sv, zv = O.quantize_int4_token(O.bf16_value(O.source_to_bf16(v)))
     assert np.array_equal(st["v_codes"], qv) and np.array_equal(st["v_s16"], sv)
+
+
+@pytest.mark.parametrize("block", [16, 32, 64, 128])
+def test_block_hadamard_structure_and_normalization(block):
+    """[SAW] eq. (1): diag(sign) . diag(H_h, ..., H_h) is orthogonal, zero outside its h x h blocks, and
+    every block is the same normalized Hadamard (entries +-1/sqrt(h), signs flipped by row)."""
+    r = np.random.default_rng(block)
+    sign = np.where(r.integers(0, 2, 128) == 1, 1, -1).astype(np.int8)
+    R = O.saw_rotation_matrix(sign, block)
+    assert np.abs(R.T @ R - np.eye(128)).max() < 1e-13
+    blk = np.arange(128) // block
+    assert np.all(R[blk[:, None] != blk[None, :]] == 0)
+    assert np.allclose(np.abs(R[blk[:, None] == blk[None, :]]), 1 / np.sqrt(block), atol=0, rtol=1e-15)
+    Hh = O.hadamard(block)
+    for i in range(0, 128, block):
+        assert np.array_equal(R[i:i + block, i:i + block], sign[i:i + block, None] * Hh)
+    assert O.hadamard_scale(block) == pytest.approx(1 / np.sqrt(block), rel=1e-16)
+
+
+@pytest.mark.parametrize("block", [16, 32, 64])
+def test_block_fwht_matches_an_integer_block_hadamard(block):
+    """With integer inputs every butterfly is exact: the block FWHT equals x . diag(s) . diag(H_int) exactly,
+    then one fp64 multiply by 1/sqrt(h) and one fp32 rounding (reading R2)."""
+    r = np.random.default_rng(40 + block)
+    x = r.integers(-300, 300, size=(20, 128)).astype(np.float32)
+    sign = np.where(r.integers(0, 2, 128) == 1, 1, -1).astype(np.int8)
+    Hint = np.rint(O.hadamard(block) * np.sqrt(block)).astype(np.int64)
+    want = np.zeros((20, 128), np.int64)
+    xs = x.astype(np.int64) * sign[None, :]
+    for i in range(0, 128, block):
+        want[:, i:i + block] = xs[:, i:i + block] @ Hint
+    got = O.rotate_hadamard(x, sign, block)
+    assert np.array_equal(got, (want.astype(np.float64) * O.hadamard_scale(block)).astype(np.float32))
+    # a vector supported on one block stays there
+    e = np.zeros((1, 128), np.float32)
+    e[0, block + 3] = 1.0
+    y = O.rotate_hadamard(e, sign, block)
+    assert np.all(y[0, :block] == 0) and np.all(y[0, 2 * block:] == 0)
+
+
+def test_block_128_is_the_full_hadamard():
+    r = np.random.default_rng(50)
+    x = r.standard_normal((10, 128)).astype(np.float32)
+    sign = np.where(r.integers(0, 2, 128) == 1, 1, -1).astype(np.int8)
+    assert np.array_equal(O.rotate_hadamard(x, sign, 128), O.rotate_hadamard(x, sign))
+    assert O.hadamard_scale(128) == O.INV_SQRT128_F64
