@@ -45,6 +45,11 @@ def parse():
     ap.add_argument("--cpu-pairs", type=int, default=2, help="distinct (seq, kv head) pairs in the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time of the CPU-baseline sample")
+    ap.add_argument("--write-bench", action="store_true",
+                    help="time the fused rotate-quantize write of one prefill chunk per sequence instead of the "
+                         "decode step (the INT4 workload's 8192-token chunk x 8 kv heads; for INT2 workloads a "
+                         "chunk of --write-tokens tokens); prints its own JSON line")
+    ap.add_argument("--write-tokens", type=int, default=8192)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (torch copy kernel) 5 times: the known-size "
                          "reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -162,6 +167,73 @@ def calibrate_copy():
     print(json.dumps({"calibrate_copy_bytes": 2 ** 30, "dispatches": 5}), flush=True)
 
 
+def write_bench(args, K, synth, np, torch):
+    """Fused rotate-quantize write of one prefill chunk per sequence (written at position 0 of an empty
+    cache each time): HIP events around each write call on its stream, K warmup + K timed calls."""
+    wl = synth.WORKLOADS[args.workload]
+    if args.scheme and wl.scheme != "int4_token":
+        wl = synth.scaled(wl, scheme=args.scheme)
+    if args.key_only:
+        wl = synth.scaled(wl, key_only=True)
+    if args.hadamard_block and wl.rotation == "saw":
+        wl = synth.scaled(wl, hadamard_block=args.hadamard_block)
+    n = int(wl.extra.get("prefill_chunk", args.write_tokens))
+    B = 1
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    int2 = wl.scheme in ("int2_channel", "int2_token")
+    if int2:
+        scheme = K.INT2_CHANNEL if wl.scheme == "int2_channel" else K.INT2_TOKEN
+        cfg = K.make_config(wl.n_kv_heads, wl.n_q_heads, scheme, K.ROT_DENSE, wl.n_sink, wl.n_recent, wl.clip_k,
+                            wl.clip_v, 0, 0, wl.key_only)
+        rk = K.build_oscar_rotation(synth.rotation_gaussian(wl, "k")).astype(np.float32)
+        rv = K.build_oscar_rotation(synth.rotation_gaussian(wl, "v")).astype(np.float32)
+    else:
+        cfg = K.make_config(wl.n_kv_heads, wl.n_q_heads, K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0, 0, 0,
+                            wl.key_only, wl.hadamard_block)
+        rk = synth.sign_vector(wl, "k").astype(np.float32)
+        rv = synth.sign_vector(wl, "v").astype(np.float32)
+    mp = K.pages_for_len(cfg, n)
+    pt, n_pool = synth.page_table(synth.scaled(wl, batch=B), max(1, mp))
+    cache = K.allocate_cache(cfg, B, torch.from_numpy(pt), torch.from_numpy(rk),
+                             None if wl.key_only else torch.from_numpy(rv), n_pages=n_pool, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed)
+    k = (torch.randn((n, wl.n_kv_heads, 128), generator=gen, device=dev)).to(torch.bfloat16)
+    v = (torch.randn((n, wl.n_kv_heads, 128), generator=gen, device=dev)).to(torch.bfloat16)
+    cu = torch.tensor([0, n], dtype=torch.int32, device=dev)
+    times = []
+    for i in range(args.warmup + args.steps):
+        cache.seq_lens.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        K.kv_rotate_quant_write(cache, k, v, cu, n)
+        e1.record()
+        e1.synchronize()
+        if i >= args.warmup:
+            times.append(e0.elapsed_time(e1) * 1e-3)
+    t = sorted(times)[len(times) // 2]
+    in_bytes = 2 * n * wl.n_kv_heads * 128 * 2
+    if int2:
+        ng = max(0, (n - wl.n_sink - wl.n_recent) // 128)
+        out_bytes = wl.n_kv_heads * (ng * 128 * 72 + (n - 128 * ng) * 512)
+    else:
+        out_bytes = wl.n_kv_heads * n * 136
+    gbps = (in_bytes + out_bytes) / t / 1e9
+    log(f"[write] {wl.name}: {n} tokens x {wl.n_kv_heads} kv heads, median {t * 1e6:.1f} us, {gbps:.0f} GB/s")
+    print(json.dumps({
+        "metric": "fused rotate-quantize KV write GB/s (bf16 in + packed pages out)", "value": round(gbps, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "us_per_write": round(t * 1e6, 2),
+        "higher_is_better": True, "dtype": "bf16 in, fp64 rotation", "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": n, "n_kv_heads": wl.n_kv_heads, "scheme": wl.scheme,
+                   "rotation": wl.rotation, "hadamard_block": wl.hadamard_block if wl.rotation == "saw" else None,
+                   "key_only": wl.key_only},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": in_bytes + out_bytes},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -178,6 +250,9 @@ def main():
     import decode_attention_15_amd as K
     import synth
 
+    if args.write_bench:
+        write_bench(args, K, synth, np, torch)
+        return
     wl = synth.WORKLOADS[args.workload]
     if args.scheme and wl.scheme != "int4_token":
         wl = synth.scaled(wl, scheme=args.scheme)
