@@ -50,6 +50,10 @@ def parse():
                          "decode step (the INT4 workload's 8192-token chunk x 8 kv heads; for INT2 workloads a "
                          "chunk of --write-tokens tokens); prints its own JSON line")
     ap.add_argument("--write-tokens", type=int, default=8192)
+    ap.add_argument("--prefill-bench", action="store_true",
+                    help="time prefill attention of the last --prefill-chunk tokens of every sequence over the "
+                         "quantized history (INT2 workloads); prints its own JSON line")
+    ap.add_argument("--prefill-chunk", type=int, default=4096)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (torch copy kernel) 5 times: the known-size "
                          "reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -234,6 +238,77 @@ def write_bench(args, K, synth, np, torch):
     }), flush=True)
 
 
+def prefill_bench(args, K, synth, np, torch):
+    """Prefill attention of each sequence's last chunk over its quantized history (the cache written in
+    chunks as in chunked prefill): HIP events around kv_prefill_attn (query rotation + attention kernel)."""
+    wl = synth.WORKLOADS[args.workload]
+    if args.key_only:
+        wl = synth.scaled(wl, key_only=True)
+    if wl.scheme != "int2_channel":
+        sys.exit("prefill attention is built for the per-channel INT2 workloads")
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    B, n_kv, n_q = wl.batch, wl.n_kv_heads, wl.n_q_heads
+    lens = synth.seq_lens(wl).astype(np.int64)
+    n = int(args.prefill_chunk)
+    cfg = K.make_config(n_kv, n_q, K.INT2_CHANNEL, K.ROT_DENSE, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v, 0, 0,
+                        wl.key_only)
+    rk = K.build_oscar_rotation(synth.rotation_gaussian(wl, "k")).astype(np.float32)
+    rv = K.build_oscar_rotation(synth.rotation_gaussian(wl, "v")).astype(np.float32)
+    max_pages = K.pages_for_len(cfg, int(lens.max()))
+    pt, n_pool = synth.page_table(wl, max_pages)
+    cache = K.allocate_cache(cfg, B, torch.from_numpy(pt), torch.from_numpy(rk),
+                             None if wl.key_only else torch.from_numpy(rv), n_pages=n_pool, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed)
+    done = np.zeros(B, dtype=np.int64)
+    while True:  # the cache in chunks of n tokens per sequence, as chunked prefill writes it
+        cnt = np.minimum(lens - done, n)
+        if cnt.sum() == 0:
+            break
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)).to(dev)
+        k = torch.randn((int(cnt.sum()), n_kv, 128), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((int(cnt.sum()), n_kv, 128), generator=gen, device=dev).to(torch.bfloat16)
+        K.kv_rotate_quant_write(cache, k, v, cu, int(cnt.max()))
+        done += cnt
+    chunk = np.minimum(lens, n)
+    total = int(chunk.sum())
+    q = torch.randn((total, n_q, 128), generator=gen, device=dev).to(torch.bfloat16)
+    cu_q = torch.from_numpy(np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)).to(dev)
+    out = torch.empty((total, n_q, 128), dtype=torch.float32, device=dev)
+    ws = K.prefill_workspace_for(cfg, total, dev)
+    torch.cuda.synchronize()
+    times = []
+    for i in range(args.warmup + args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        K.kv_prefill_attn(cache, q, cu_q, int(chunk.max()), out, ws)
+        e1.record()
+        e1.synchronize()
+        if i >= args.warmup:
+            times.append(e0.elapsed_time(e1) * 1e-3)
+    t = sorted(times)[len(times) // 2]
+    # algorithmic work: every (query head, visible token) pair costs 128 MACs for the logit and 128 for the
+    # value sum; visible tokens of the query at position p are p + 1
+    pairs = 0
+    for b in range(B):
+        T, c = int(lens[b]), int(chunk[b])
+        pairs += n_q * (c * (T - c) + c * (c + 1) // 2)
+    ops = pairs * 2 * 2 * 128
+    tops = ops / t / 1e12
+    log(f"[prefill] {wl.name}: chunk {n} over {int(lens.max())}, median {t * 1e3:.3f} ms, {tops:.1f} TOP/s algorithmic")
+    print(json.dumps({
+        "metric": "prefill attention over the quantized history, algorithmic TOP/s", "value": round(tops, 2),
+        "unit": "TOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_call": round(t * 1e3, 4),
+        "higher_is_better": True, "dtype": "int8 limbs (24-bit fixed point) + bf16 band", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "ctx": int(lens.max()), "chunk": n, "n_q_heads": n_q,
+                   "n_kv_heads": n_kv, "key_only": wl.key_only},
+        "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": 5000.0, "unit": "TOP/s",
+                     "frac": round(tops / 5000.0, 5), "traffic": None,
+                     "note": "int8 peak; each algorithmic MAC is three int8 MACs (limbs) here"},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -252,6 +327,9 @@ def main():
 
     if args.write_bench:
         write_bench(args, K, synth, np, torch)
+        return
+    if args.prefill_bench:
+        prefill_bench(args, K, synth, np, torch)
         return
     wl = synth.WORKLOADS[args.workload]
     if args.scheme and wl.scheme != "int4_token":

@@ -76,6 +76,9 @@ _lib_check = _sig("kvq_check_config", ctypes.c_int, _CFG)
 _lib_build_oscar = _sig("kvq_build_oscar_rotation", ctypes.c_int, _P, _P)
 _lib_compose_oscar = _sig("kvq_compose_oscar_rotation", ctypes.c_int, _P, _P)
 _lib_build_hadamard = _sig("kvq_build_hadamard_rotation", ctypes.c_int, _P, _P)
+_lib_prefill_ws = _sig("kvq_prefill_workspace_bytes", ctypes.c_size_t, _CFG, ctypes.c_int32)
+_lib_prefill = _sig("kv_prefill_attn", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P, ctypes.c_int32,
+                    ctypes.c_int32, _P, _P, ctypes.c_size_t, _P)
 _lib_query_cov = _sig("kvq_query_covariance", ctypes.c_int, _P, ctypes.c_int64, _P)
 _lib_sv_cov = _sig("kvq_score_value_covariance", ctypes.c_int, _P, ctypes.c_int64, _P, ctypes.c_int64, _P)
 _lib_eigenbasis = _sig("kvq_eigenbasis", ctypes.c_int, _P, _P, _P)
@@ -95,7 +98,8 @@ EXPORTED = [
     "kvq_page_bytes", "kvq_band_slots", "kvq_band_bytes", "kvq_pages_for_len", "kvq_decode_workspace_bytes",
     "kvq_bits_per_element", "kvq_check_config", "kvq_build_oscar_rotation", "kvq_compose_oscar_rotation",
     "kvq_build_hadamard_rotation", "kvq_query_covariance", "kvq_score_value_covariance", "kvq_eigenbasis",
-    "kvq_build_oscar_rotation_from_covariance", "kv_rotate_quant_write", "kv_decode_attn", "kv_decode_attn_stages",
+    "kvq_build_oscar_rotation_from_covariance", "kvq_prefill_workspace_bytes", "kv_prefill_attn",
+    "kv_rotate_quant_write", "kv_decode_attn", "kv_decode_attn_stages",
     "kvq_debug_rotate",
     "kvq_strerror", "kvq_version", "kvq_last_error",
 ]
@@ -339,3 +343,24 @@ def workspace_for(cfg: Config, batch: int, max_seq_len: int, device: str = "cuda
     if n == 0:
         raise KvqError(KVQ_EINVAL, "decode_workspace_bytes")
     return torch.empty((n + 3) // 4, dtype=torch.float32, device=device)
+
+
+def prefill_workspace_bytes(cfg: Config, total_q: int) -> int:
+    return int(_lib_prefill_ws(ctypes.byref(cfg), int(total_q)))
+
+
+def kv_prefill_attn(cache: DeviceCache, q, cu_q, max_q: int, out, workspace, stream=None) -> None:
+    """Prefill attention of the chunk just written: q [total_q, n_q, 128] (fp32/bf16), cu_q [batch + 1]
+    int32 (device) prefix sums of each sequence's chunk length -> out fp32 [total_q, n_q, 128]."""
+    assert q.is_contiguous() and out.is_contiguous() and workspace.is_contiguous() and cu_q.is_contiguous()
+    assert q.dim() == 3 and q.shape[1:] == (cache.cfg.n_q_heads, 128) and out.shape == q.shape
+    cs = cache.c_struct()
+    _check(_lib_prefill(ctypes.byref(cache.cfg), ctypes.byref(cs), _ptr(q), _dtype_code(q), _ptr(cu_q), int(q.shape[0]),
+                        int(max_q), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                        _stream(stream)), "kv_prefill_attn")
+
+
+def prefill_workspace_for(cfg: Config, total_q: int, device: str = "cuda"):
+    import torch
+    n = prefill_workspace_bytes(cfg, total_q)
+    return torch.empty(max(1, (n + 3) // 4), dtype=torch.float32, device=device)

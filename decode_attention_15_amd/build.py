@@ -24,6 +24,7 @@ SOURCES = {
     # the write path must round exactly as the cache format states: no contraction
     "kvq_write.hip": ["-ffp-contract=off"],
     "kvq_decode.hip": [],
+    "kvq_prefill.hip": [],
     "kvq_api.cpp": ["-x", "hip", "-ffp-contract=off"],
     "kvq_calib.cpp": ["-x", "hip", "-ffp-contract=off"],
 }

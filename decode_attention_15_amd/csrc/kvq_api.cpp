@@ -331,6 +331,46 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
   return to_status(launch_decode(a, stages, stream), "kv_decode_attn");
 }
 
+size_t kvq_prefill_workspace_bytes(const kvq_config* cfg, int32_t total_q) {
+  if (check_config(cfg) != KVQ_OK || total_q < 0) return 0;
+  return sizeof(float) * 2 * (size_t)total_q * cfg->n_q_heads * D;
+}
+
+int kv_prefill_attn(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t dtype, const int32_t* cu_q,
+                    int32_t total_q_host, int32_t max_q_host, float* out, void* workspace, size_t ws_bytes,
+                    hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if ((st = check_cache(cfg, cache)) != KVQ_OK) return st;
+  if (cfg->scheme != KVQ_INT2_CHANNEL || cfg->rotation != KVQ_ROT_DENSE) return KVQ_EUNSUPPORTED;
+  if (!q || !cu_q || !out || total_q_host < 0 || max_q_host < 0 || (dtype != KVQ_F32 && dtype != KVQ_BF16))
+    return KVQ_EINVAL;
+  if (total_q_host == 0) return KVQ_OK;
+  if (!workspace) return KVQ_EINVAL;
+  if (ws_bytes < kvq_prefill_workspace_bytes(cfg, total_q_host)) return KVQ_ENOSPACE;
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.g = make_geo(cfg, cache);
+  a.pages = static_cast<const uint8_t*>(cache->pages);
+  a.band = static_cast<const uint16_t*>(cache->band);
+  a.page_table = cache->page_table;
+  a.seq_lens = cache->seq_lens;
+  a.q = q;
+  a.q_bf16 = dtype == KVQ_BF16;
+  a.rot_k = cache->rot_k;
+  a.rot_v = cache->rot_v;
+  a.out = out;
+  float* ws = static_cast<float*>(workspace);
+  a.qrot = ws;
+  a.qband = ws + (size_t)total_q_host * cfg->n_q_heads * D;
+  a.cu_q = cu_q;
+  a.impl = cfg->decode_impl;
+  clear_stale_error();
+  hipError_t e = launch_qprep_rows(a, total_q_host, stream);
+  if (e == hipSuccess) e = launch_prefill(a, max_q_host, stream);
+  return to_status(e, "kv_prefill_attn");
+}
+
 int kvq_debug_rotate(const kvq_config* cfg, const kvq_cache* cache, int32_t which, const void* x, int32_t dtype,
                      int32_t n, float rho, float* out, hipStream_t stream) {
   int st = check_config(cfg);

@@ -1899,6 +1899,19 @@ hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_qprep_rows(const DecodeArgs& a, int rows, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid(a.g.n_kv, rows);
+  switch (a.g.gq) {
+    case 1: hipLaunchKernelGGL(qprep_kernel<1>, grid, dim3(512), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(qprep_kernel<2>, grid, dim3(512), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(qprep_kernel<4>, grid, dim3(512), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(qprep_kernel<8>, grid, dim3(512), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int stages, hipStream_t s) {
   switch (a.g.gq) {
     case 1: return launch_gq<1>(a, stages, s);

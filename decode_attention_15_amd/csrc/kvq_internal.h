@@ -108,10 +108,14 @@ struct DecodeArgs {
   float* qband;     // [batch][n_q][128]
   float* partials;  // [batch][n_q][n_units][PART_STRIDE]
   int impl;
+  const int32_t* cu_q;  // prefill: [batch + 1] prefix sums of each sequence's chunk queries
 };
 
 constexpr int PART_STRIDE = 2 + D;  // m, l, o[128]
 
 hipError_t launch_decode(const DecodeArgs& a, int stages, hipStream_t s);
+// query rotation of `rows` query rows (q, qrot, qband indexed as [row][n_q][128])
+hipError_t launch_qprep_rows(const DecodeArgs& a, int rows, hipStream_t s);
+hipError_t launch_prefill(const DecodeArgs& a, int max_q, hipStream_t s);
 
 }  // namespace kvq

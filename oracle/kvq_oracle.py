@@ -454,6 +454,33 @@ def decode_int2(q_heads, k_src, v_src, T, n_sink, n_recent, clip_k, clip_v, R_K3
     return attend(query_values(q_heads), K, V), st
 
 
+def token_positions(state, T: int, n_sink: int, n_recent: int) -> np.ndarray:
+    """Positions of the tokens in the order int2_keys_values returns them: band, then groups."""
+    pos = [np.asarray(state["band_pos"], dtype=np.int64)]
+    for g in state["groups"]:
+        pos.append(n_sink + GROUP * int(g) + np.arange(GROUP))
+    return np.concatenate(pos)
+
+
+def attend_causal(q_rows: np.ndarray, q_pos: np.ndarray, keys: np.ndarray, vals: np.ndarray,
+                  key_pos: np.ndarray) -> np.ndarray:
+    """Row i of q_rows [n, g_q, d] attends the keys with position <= q_pos[i] ([NOVA] §3 "Long context":
+    chunked prefill over the cache as it stands after the chunk's write), fp64."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    out = np.zeros(q_rows.shape)
+    for i in range(q_rows.shape[0]):
+        vis = key_pos <= q_pos[i]
+        out[i] = attend(q_rows[i], keys[vis], vals[vis])
+    return out
+
+
+def prefill_int2(q_rows, q_pos, k_src, v_src, T, n_sink, n_recent, clip_k, clip_v, R_K32, R_V32, axis="channel"):
+    """Prefill attention of the chunk's queries over an INT2 cache of length T (chunk included)."""
+    st = int2_state(k_src, v_src, T, n_sink, n_recent, clip_k, clip_v, R_K32, R_V32, axis=axis)
+    K, V = int2_keys_values(st, R_K32, R_V32)
+    return attend_causal(query_values(q_rows), np.asarray(q_pos), K, V, token_positions(st, T, n_sink, n_recent))
+
+
 def decode_int4(q_heads, k_src, v_src, T, sign_k, sign_v, block: int = D):
     st = int4_state(k_src, v_src, T, sign_k, sign_v, block=block)
     K, V = int4_keys_values(st, sign_k, sign_v, block)

@@ -167,6 +167,17 @@ def queries(wl: Workload, step: int = 0) -> np.ndarray:
     return to_bf16_bits(q) if wl.src_dtype == "bf16" else q
 
 
+def prefill_queries(wl: Workload, seq: int, start: int, count: int) -> np.ndarray:
+    """Queries of chunk positions start .. start + count - 1 of sequence `seq`: [count, n_q, 128], float32 or
+    bf16 bits like the cache source (one seeded stream per position, so any chunking draws the same rows)."""
+    rows = []
+    for p in range(start, start + count):
+        r = _rng(wl, "q", 7919, seq, p)
+        rows.append(r.standard_normal((wl.n_q_heads, HEAD_DIM), dtype=np.float32))
+    q = np.stack(rows) if rows else np.zeros((0, wl.n_q_heads, HEAD_DIM), np.float32)
+    return to_bf16_bits(q) if wl.src_dtype == "bf16" else q
+
+
 def rotation_gaussian(wl: Workload, which: str) -> np.ndarray:
     """Seeded 128x128 N(0,1) float64 matrix whose QR factor stands in for a calibrated eigenbasis."""
     r = _rng(wl, "rot_k" if which == "k" else "rot_v")

@@ -461,3 +461,29 @@ def test_block_128_is_the_full_hadamard():
     sign = np.where(r.integers(0, 2, 128) == 1, 1, -1).astype(np.int8)
     assert np.array_equal(O.rotate_hadamard(x, sign, 128), O.rotate_hadamard(x, sign))
     assert O.hadamard_scale(128) == O.INV_SQRT128_F64
+
+
+def test_causal_attention_reduces_to_decode_and_to_prefixes():
+    """Prefill attention: the last query (position T-1) sees the whole cache, so it equals the decode
+    output; a query at position p equals attention over the first p+1 source tokens in an all-bf16
+    cache (no quantized group: S0 + W covers the length)."""
+    r = np.random.default_rng(61)
+    T = 700
+    k = r.standard_normal((T, 128)).astype(np.float32)
+    v = r.standard_normal((T, 128)).astype(np.float32)
+    q = r.standard_normal((5, 4, 128)).astype(np.float32)
+    RK = O.oscar_rotation(r.standard_normal((128, 128))).astype(np.float32)
+    RV = O.oscar_rotation(r.standard_normal((128, 128))).astype(np.float32)
+    pos = np.array([3, 131, 132, 400, T - 1])
+    got = O.prefill_int2(q, pos, k, v, T, 4, 128, 0.96, 0.92, RK, RV)
+    want_last, _ = O.decode_int2(q[-1], k, v, T, 4, 128, 0.96, 0.92, RK, RV)
+    assert np.abs(got[-1] - want_last).max() < 1e-12
+    # all-bf16 cache (W large): causal attention over exact bf16 prefixes
+    got_b = O.prefill_int2(q, pos, k, v, T, 4, 1024, 0.96, 0.92, RK, RV)
+    kb, vb = O.bf16_value(O.bf16_rne(k)).astype(np.float64), O.bf16_value(O.bf16_rne(v)).astype(np.float64)
+    for i, p in enumerate(pos):
+        assert np.abs(got_b[i] - O.attend(q[i], kb[:p + 1], vb[:p + 1])).max() < 1e-12
+    # positions of a state: band first (sink + tail), then the groups
+    st = O.int2_state(k, v, T, 4, 128, 0.96, 0.92, RK, RV)
+    tp = O.token_positions(st, T, 4, 128)
+    assert sorted(tp.tolist()) == list(range(T))
