@@ -35,9 +35,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batch32_32k")
     ap.add_argument("--impl", default="auto", choices=["auto", "f32", "dot16", "dot8"])
-    ap.add_argument("--scheme", default=None, choices=["int2_channel", "int2_token"],
-                    help="INT2 workloads: quantize per channel over 128-token groups (the workloads' statement) "
-                         "or per token over its 128 channels")
+    ap.add_argument("--scheme", default=None, choices=["int2_channel", "int2_token", "int4_channel"],
+                    help="INT2 workloads: quantize per channel over 128-token groups (the workloads' statement), "
+                         "per token over its 128 channels, or per channel with 4-bit codes")
     ap.add_argument("--key-only", action="store_true", help="rotate K only; V quantized in its own frame")
     ap.add_argument("--hadamard-block", type=int, default=0, choices=[0, 16, 32, 64, 128],
                     help="block order of the randomized Hadamard (workloads with that rotation; 0 = 128)")
@@ -91,15 +91,20 @@ def read_traffic(workload, variant=""):
     return int(float(kv["bytes_per_launch"]))
 
 
+GROUPED = {"int2_channel": 0, "int2_token": 2, "int4_channel": 3}  # grouped schemes and their kvq_scheme
+
+
 def decode_bytes(wl, lens, S0, W):
     """Algorithmic bytes one decode step reads/writes.  INT2: codes + bf16 scale/zero of every group
-    (72 B per token and kv head) and bf16 band tokens (512 B); INT4: codes + bf16 scale/zero of every
-    token (136 B per token and kv head).  Plus the query (bf16) and the output (fp32)."""
+    (72 B per token and kv head) and bf16 band tokens (512 B); per-channel INT4 the same with 4-bit
+    codes (136 B per token); INT4 per token: codes + bf16 scale/zero of every token (136 B per token
+    and kv head).  Plus the query (bf16) and the output (fp32)."""
     kv = 0
     for T in lens:
-        if wl.scheme in ("int2_channel", "int2_token"):
+        if wl.scheme in GROUPED:
             ng = max(0, (T - S0 - W) // 128)
-            kv += wl.n_kv_heads * (ng * 128 * 72 + (T - 128 * ng) * 512)
+            per_tok = 136 if wl.scheme == "int4_channel" else 72
+            kv += wl.n_kv_heads * (ng * 128 * per_tok + (T - 128 * ng) * 512)
         else:
             kv += wl.n_kv_heads * T * 136
     qo = len(lens) * wl.n_q_heads * 128 * (2 + 4)
@@ -118,8 +123,8 @@ def cpu_baseline(wl, args, T, rk, rv):
     total_s = 0.0
     total_bytes = 0
     runs = 0
-    int2 = wl.scheme in ("int2_channel", "int2_token")
-    axis = "token" if wl.scheme == "int2_token" else "channel"
+    int2 = wl.scheme in GROUPED
+    axis = {"int2_channel": "channel", "int2_token": "token", "int4_channel": "channel4"}.get(wl.scheme)
     rv = None if wl.key_only else rv
     with threadpool_limits(limits=1):
         states = []
@@ -185,9 +190,9 @@ def write_bench(args, K, synth, np, torch):
     B = 1
     dev = "cuda"
     torch.cuda.set_device(0)
-    int2 = wl.scheme in ("int2_channel", "int2_token")
+    int2 = wl.scheme in GROUPED
     if int2:
-        scheme = K.INT2_CHANNEL if wl.scheme == "int2_channel" else K.INT2_TOKEN
+        scheme = GROUPED[wl.scheme]
         cfg = K.make_config(wl.n_kv_heads, wl.n_q_heads, scheme, K.ROT_DENSE, wl.n_sink, wl.n_recent, wl.clip_k,
                             wl.clip_v, 0, 0, wl.key_only)
         rk = K.build_oscar_rotation(synth.rotation_gaussian(wl, "k")).astype(np.float32)
@@ -338,7 +343,7 @@ def main():
         wl = synth.scaled(wl, key_only=True)
     if args.hadamard_block and wl.rotation == "saw":
         wl = synth.scaled(wl, hadamard_block=args.hadamard_block)
-    int2 = wl.scheme in ("int2_channel", "int2_token")
+    int2 = wl.scheme in GROUPED
     dev = "cuda"
     torch.cuda.set_device(0)
     B, n_kv, n_q = wl.batch, wl.n_kv_heads, wl.n_q_heads
@@ -349,7 +354,7 @@ def main():
     impl = {"auto": K.DECODE_AUTO, "f32": K.DECODE_F32, "dot16": K.DECODE_DOT16, "dot8": K.DECODE_DOT8}[args.impl]
     split = args.split if args.split else (wl.split_tokens if wl.name == "long_b4_131k" else 0)
     if int2:
-        scheme = K.INT2_CHANNEL if wl.scheme == "int2_channel" else K.INT2_TOKEN
+        scheme = GROUPED[wl.scheme]
         cfg = K.make_config(n_kv, n_q, scheme, K.ROT_DENSE, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v,
                             split, impl, wl.key_only)
         rk = K.build_oscar_rotation(synth.rotation_gaussian(wl, "k")).astype(np.float32)
@@ -478,6 +483,7 @@ def main():
                    "head_dim": 128,
                    "scheme": ({"int2_channel": "int2 per-channel, 128-token groups, bf16 scale/zero",
                                "int2_token": "int2 per-token over 128 channels, bf16 scale/zero",
+                               "int4_channel": "int4 per-channel, 128-token groups, bf16 scale/zero",
                                "int4_token": "int4 per-token, bf16 scale/zero, randomized Hadamard"}
                               [wl.scheme] + (", key-only rotation" if wl.key_only else "") +
                               (f", Hadamard block {wl.hadamard_block}" if wl.rotation == "saw" else "")),
@@ -486,7 +492,8 @@ def main():
         "steps_per_s": round(1000.0 / ms_step, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": ("split-K decode (INT2 pages + bf16 band)" if int2 else "split-K decode (INT4 pages)"),
+                     "kernel": ("split-K decode (per-channel INT4 pages + bf16 band)" if wl.scheme == "int4_channel"
+                                else "split-K decode (INT2 pages + bf16 band)" if int2 else "split-K decode (INT4 pages)"),
                      "kernel_us": round(kern_ms * 1e3, 2),
                      "bytes_per_launch": kern_bytes},
         "decode_kernels_us": stage_us,

@@ -13,12 +13,12 @@ namespace {
 
 int gq_of(const kvq_config* c) { return c->n_q_heads / c->n_kv_heads; }
 
-int head_bytes_of(const kvq_config* c) { return is_int2(c->scheme) ? I2_HEAD_BYTES : I4_HEAD_BYTES; }
+int head_bytes_of(const kvq_config* c) { return is_int2(c->scheme) ? I2_HEAD_BYTES : I4_HEAD_BYTES; }  // INT4 per channel: 8704
 
 int check_config(const kvq_config* c) {
   if (!c) return KVQ_EINVAL;
   if (c->head_dim != D || c->page_tokens != PAGE || c->group_tokens != GROUP) return KVQ_EUNSUPPORTED;
-  if (!is_int2(c->scheme) && c->scheme != KVQ_INT4_TOKEN) return KVQ_EUNSUPPORTED;
+  if (!is_grouped(c->scheme) && c->scheme != KVQ_INT4_TOKEN) return KVQ_EUNSUPPORTED;
   if (c->rotation != KVQ_ROT_DENSE && c->rotation != KVQ_ROT_HADAMARD) return KVQ_EUNSUPPORTED;
   if (c->n_kv_heads < 1 || c->n_q_heads < 1 || c->n_q_heads % c->n_kv_heads != 0) return KVQ_EINVAL;
   const int gq = gq_of(c);
@@ -26,15 +26,16 @@ int check_config(const kvq_config* c) {
   if (c->n_sink < 0 || c->n_recent < 0) return KVQ_EINVAL;
   if (c->scheme == KVQ_INT4_TOKEN && (c->n_sink != 0 || c->n_recent != 0)) return KVQ_EINVAL;
   if (!(c->clip_k > 0.0f && c->clip_k <= 1.0f) || !(c->clip_v > 0.0f && c->clip_v <= 1.0f)) return KVQ_EINVAL;
-  const int unit = is_int2(c->scheme) ? GROUP : PAGE;
+  const int unit = is_grouped(c->scheme) ? GROUP : PAGE;
   if (c->split_tokens < 0 || c->split_tokens % unit != 0) return KVQ_EINVAL;
   if (c->decode_impl != KVQ_DECODE_AUTO && c->decode_impl != KVQ_DECODE_F32 && c->decode_impl != KVQ_DECODE_MFMA &&
       c->decode_impl != KVQ_DECODE_DOT16 && c->decode_impl != KVQ_DECODE_DOT8)
     return KVQ_EINVAL;
   if (c->decode_impl == KVQ_DECODE_MFMA) return KVQ_EUNSUPPORTED;
-  if (c->decode_impl == KVQ_DECODE_DOT8 && !is_int2(c->scheme)) return KVQ_EUNSUPPORTED;
-  // per-token INT2 is built on the nibble dot product only
-  if (c->scheme == KVQ_INT2_TOKEN && c->decode_impl != KVQ_DECODE_AUTO && c->decode_impl != KVQ_DECODE_DOT8)
+  if (c->decode_impl == KVQ_DECODE_DOT8 && !is_grouped(c->scheme)) return KVQ_EUNSUPPORTED;
+  // per-token INT2 and per-channel INT4 are built on the nibble dot product only
+  if ((c->scheme == KVQ_INT2_TOKEN || c->scheme == KVQ_INT4_CHANNEL) && c->decode_impl != KVQ_DECODE_AUTO &&
+      c->decode_impl != KVQ_DECODE_DOT8)
     return KVQ_EUNSUPPORTED;
   if (c->key_only_rotation != 0 && c->key_only_rotation != 1) return KVQ_EINVAL;
   const int hb = c->hadamard_block;
@@ -48,7 +49,7 @@ int check_cache(const kvq_config* c, const kvq_cache* k) {
   if (!k || !k->pages || !k->page_table || !k->seq_lens || !k->rot_k || (!k->rot_v && !c->key_only_rotation))
     return KVQ_EINVAL;
   if (k->batch < 1 || k->max_pages_per_seq < 0 || k->n_pages < 0) return KVQ_EINVAL;
-  if (is_int2(c->scheme) && !k->band) return KVQ_EINVAL;
+  if (is_grouped(c->scheme) && !k->band) return KVQ_EINVAL;
   return KVQ_OK;
 }
 
@@ -61,9 +62,9 @@ void clip_params(float rho, int* j, float* f) {
 
 // decode work split: groups (INT2) or pages (INT4) per chunk
 int chunk_units(const kvq_config* c, int batch, int max_seq_len) {
-  if (c->split_tokens > 0) return c->split_tokens / (is_int2(c->scheme) ? GROUP : PAGE);
+  if (c->split_tokens > 0) return c->split_tokens / (is_grouped(c->scheme) ? GROUP : PAGE);
   int units;  // quantized groups/pages per sequence
-  if (is_int2(c->scheme)) units = n_groups_of(max_seq_len, c->n_sink, c->n_recent);
+  if (is_grouped(c->scheme)) units = n_groups_of(max_seq_len, c->n_sink, c->n_recent);
   else units = (max_seq_len + PAGE - 1) / PAGE;
   const int pairs = batch * c->n_kv_heads;
   const int target_wgs = 2048;
@@ -71,7 +72,7 @@ int chunk_units(const kvq_config* c, int batch, int max_seq_len) {
   if (chunks < 1) chunks = 1;
   int per = (units + chunks - 1) / chunks;
   per = ((per + 3) / 4) * 4;  // the 4 waves of a work-group share a chunk
-  const int cap = is_int2(c->scheme) ? 16 : 32;
+  const int cap = is_grouped(c->scheme) ? 16 : 32;
   if (per > cap) per = cap;
   if (per < 4) per = 4;
   return per;
@@ -79,7 +80,7 @@ int chunk_units(const kvq_config* c, int batch, int max_seq_len) {
 
 int max_chunks_of(const kvq_config* c, int max_seq_len, int per) {
   int units;
-  if (is_int2(c->scheme)) units = n_groups_of(max_seq_len, c->n_sink, c->n_recent);
+  if (is_grouped(c->scheme)) units = n_groups_of(max_seq_len, c->n_sink, c->n_recent);
   else units = (max_seq_len + PAGE - 1) / PAGE;
   return (units + per - 1) / per;
 }
@@ -201,7 +202,7 @@ size_t kvq_page_bytes(const kvq_config* cfg) {
 
 int32_t kvq_band_slots(const kvq_config* cfg) {
   if (check_config(cfg) != KVQ_OK) return 0;
-  return is_int2(cfg->scheme) ? cfg->n_sink + cfg->n_recent + GROUP : 0;
+  return is_grouped(cfg->scheme) ? cfg->n_sink + cfg->n_recent + GROUP : 0;
 }
 
 size_t kvq_band_bytes(const kvq_config* cfg, int32_t batch) {
@@ -211,7 +212,7 @@ size_t kvq_band_bytes(const kvq_config* cfg, int32_t batch) {
 
 int32_t kvq_pages_for_len(const kvq_config* cfg, int32_t seq_len) {
   if (check_config(cfg) != KVQ_OK || seq_len < 0) return -1;
-  if (is_int2(cfg->scheme)) return 2 * n_groups_of(seq_len, cfg->n_sink, cfg->n_recent);
+  if (is_grouped(cfg->scheme)) return 2 * n_groups_of(seq_len, cfg->n_sink, cfg->n_recent);
   return (seq_len + PAGE - 1) / PAGE;
 }
 
@@ -226,10 +227,11 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t batch, int32_t 
 double kvq_bits_per_element(const kvq_config* cfg, int64_t seq_len) {
   if (check_config(cfg) != KVQ_OK || seq_len <= 0) return 0.0;
   double bytes;
-  if (is_int2(cfg->scheme)) {
+  if (is_grouped(cfg->scheme)) {
     const int64_t ng = n_groups_of((int)seq_len, cfg->n_sink, cfg->n_recent);
-    // per group and K|V: 128x128 codes at 2 bits + 128 bf16 scales + 128 bf16 zeros
-    bytes = (double)ng * 2.0 * (GROUP * D / 4 + 2 * D * 2) + (double)(seq_len - GROUP * ng) * SLOT_BYTES;
+    // per group and K|V: 128x128 codes at 2 (4) bits + 128 bf16 scales + 128 bf16 zeros
+    const int code_bytes = cfg->scheme == KVQ_INT4_CHANNEL ? GROUP * D / 2 : GROUP * D / 4;
+    bytes = (double)ng * 2.0 * (code_bytes + 2 * D * 2) + (double)(seq_len - GROUP * ng) * SLOT_BYTES;
   } else {
     bytes = (double)seq_len * 2.0 * (D / 2 + 4);
   }
@@ -284,7 +286,7 @@ int kv_rotate_quant_write(const kvq_config* cfg, kvq_cache* cache, const void* k
   clip_params(cfg->clip_v, &a.clip_j_v, &a.clip_f_v);
   a.max_new = max_new_host;
   clear_stale_error();
-  hipError_t e = is_int2(cfg->scheme) ? launch_write_int2(a, stream) : launch_write_int4(a, stream);
+  hipError_t e = is_grouped(cfg->scheme) ? launch_write_int2(a, stream) : launch_write_int4(a, stream);
   return to_status(e, "kv_rotate_quant_write");
 }
 

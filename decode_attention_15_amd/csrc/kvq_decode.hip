@@ -142,7 +142,8 @@ __global__ __launch_bounds__(512) void qprep_kernel(DecodeArgs a) {
 // unit u >= 1 = quantized chunk u-1.  Each of the 4 waves walks its own groups/pages with an
 // online softmax; the waves are merged in LDS and one partial (m, l, o[128]) per q head written.
 // ---------------------------------------------------------------------------------------------
-template <int GQ>
+// STG: code staging per wave and group in units of 4 KB (2 for 4-bit per-channel codes)
+template <int GQ, int STG = 1>
 struct DecodeLds {
   union {
     struct {                     // band unit, fp32 INT2 path, INT4 path
@@ -153,19 +154,20 @@ struct DecodeLds {
     struct {                     // 16-bit INT2 path
       uint8_t abytes[4][GQ * 256];  // per wave: key-side operand words [head][limb][32]
       uint8_t pbytes[4][GQ * 256];  // per wave: value-side operand words [head][limb][32]
-      uint4 vstage[4][256];         // per wave: value codes of the current group (both pages, 4 KB)
-      uint4 kstage[4][256];         // per wave: key codes of a group (nibble-digit path)
+      uint4 vstage[4][256 * STG];   // per wave: value codes of the current group (both pages)
+      uint4 kstage[4][256 * STG];   // per wave: key codes of a group (nibble-digit path)
       uint4 mstage[4][64];          // per wave: key and value scales/zeros of a group (nibble-digit path)
     } d;
+    float co[4][GQ][D];          // the waves' outputs, written once every wave has finished its walk
   };
   float cm[4][GQ];
   float cl[4][GQ];
-  float co[4][GQ][D];
 };
 
-template <int GQ>
-__device__ void combine_and_store(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int unit, int wave, int lane,
+template <int GQ, typename Lds>
+__device__ void combine_and_store(Lds& L, const DecodeArgs& a, int b, int h, int unit, int wave, int lane,
                                   const float (&m)[GQ], const float (&l)[GQ], const float (&o)[GQ][2], int c0, int c1) {
+  __syncthreads();  // co shares its LDS with the walks' buffers
 #pragma unroll
   for (int hh = 0; hh < GQ; ++hh) {
     L.co[wave][hh][c0] = o[hh][0];
@@ -210,8 +212,8 @@ __device__ inline void softmax_update(float (&m)[GQ], float (&l)[GQ], float (&o)
   mnew_out = mnew;
 }
 
-template <int GQ>
-__device__ void band_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int T) {
+template <int GQ, typename Lds>
+__device__ void band_unit(Lds& L, const DecodeArgs& a, int b, int h, int T) {
   const Geo& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < GQ * D; e += kThreads)
@@ -294,8 +296,8 @@ __device__ void band_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
   combine_and_store<GQ>(L, a, b, h, 0, wave, lane, m, l, o, 2 * lane, 2 * lane + 1);
 }
 
-template <int GQ>
-__device__ void int2_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
+template <int GQ, typename Lds>
+__device__ void int2_unit(Lds& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
   const Geo& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ng = n_groups_of(T, g.S0, g.W);
@@ -529,8 +531,8 @@ struct OpAdd {
 //   V code word g of a channel holds token 16j + 4g + r in byte j, bits 2r, so p word (page, g, k) holds
 //   token 16j + 4g + k of that page in byte j.
 // ---------------------------------------------------------------------------------------------
-template <int GQ>
-__device__ void int2_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
+template <int GQ, typename Lds>
+__device__ void int2_unit_dot16(Lds& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
   constexpr int LG = HeadLog2<GQ>::v;
   constexpr int LPH = 64 >> LG;   // lanes per head in the alpha step
   constexpr int NCH = 2 * GQ;     // channels per lane in the alpha step
@@ -860,24 +862,29 @@ __device__ inline uint4 byte_transpose(uint32_t x0, uint32_t x1, uint32_t x2, ui
 
 // Per-wave state of the nibble-digit units: LDS areas, lane roles and the group copy pipeline.
 // Copies of one group in issue order: M (1 copy: the even page's metadata to lanes 0-31, the odd page's
-// to lanes 32-63), K (4: copy j, lane i = half j & 1 of token kt + 2 (j >> 1) of page kp), V (4: 1 KB
-// of value codes each, half j & 1 of page j >> 1).  The next group's copy of each is issued as soon as
-// the current one has been read into registers, so every copy has a whole group's work to land; the
-// waits count the copies issued after the one needed.
-template <int GQ>
+// to lanes 32-63), K (2-bit codes: 4 copies, copy j lane i = half j & 1 of token kt + 2 (j >> 1) of page kp;
+// 4-bit codes: 8 copies, copy j = quarter j & 3 of token kt + 2 (j >> 2)), V (2-bit: 4 copies of 1 KB,
+// half j & 1 of page j >> 1; 4-bit: 8 copies, copy j lane i = half j & 1 of channel i + 64 ((j >> 1) & 1)
+// of page j >> 2).  Every copy lands at stage + 1 KB j + 16 i, so that each lane reads its own 16 bytes.
+// The next group's copy of each is issued as soon as the current one has been read into registers, so
+// every copy has a whole group's work to land; the waits count the copies issued after the one needed.
+template <int GQ, int BITS>
 struct Dot8Wave {
+  static constexpr int NCOPY = 2 * BITS;                            // K (and V) copies per group
+  static constexpr int META = BITS == 4 ? I4C_META_OFF : I2_META_OFF;
   uint32_t* adig;       // key digit words [head][m][8]
   uint8_t* pdig;        // weight digit words [head][page * 4 + g][8]
   uint16_t* aval;       // biased 16-bit key operands [head][128] (aliases pdig while the digits are built)
-  const uint4* vst;     // value codes of a group (4 KB)
-  const uint4* kst;     // key codes of a group, lane-ordered (4 KB)
+  const uint4* vst;     // value codes of a group
+  const uint4* kst;     // key codes of a group, lane-ordered
   const uint16_t* mst;  // metadata of a group's two pages (1 KB)
   uint32_t vst_a, kst_a, mst_a;
   const uint8_t* pages;
   long long page_bytes, hoff;
   int lane, kp, kt;
 
-  __device__ Dot8Wave(DecodeLds<GQ>& L, const DecodeArgs& a, int h, int wave, int lane_) {
+  template <typename Lds>
+  __device__ Dot8Wave(Lds& L, const DecodeArgs& a, int h, int wave, int lane_) {
     adig = reinterpret_cast<uint32_t*>(L.d.abytes[wave]);
     pdig = L.d.pbytes[wave];
     aval = reinterpret_cast<uint16_t*>(L.d.pbytes[wave]);
@@ -889,22 +896,35 @@ struct Dot8Wave {
     mst_a = lds_addr(mst);
     pages = a.pages;
     page_bytes = a.g.page_bytes;
-    hoff = (long long)h * I2_HEAD_BYTES;
+    hoff = (long long)h * a.g.head_bytes;
     lane = lane_;
     kp = lane >> 5;
     kt = 16 * ((lane >> 3) & 3) + 4 * ((lane >> 1) & 3) + (lane & 1);
   }
   __device__ const uint8_t* page_of(int idx) const { return pages + (long long)idx * page_bytes + hoff; }
-  __device__ void issue_m(int2 p) const { dma16(mst_a, page_of(lane < 32 ? p.x : p.y) + I2_META_OFF + (lane & 31) * 16); }
+  __device__ void issue_m(int2 p) const { dma16(mst_a, page_of(lane < 32 ? p.x : p.y) + META + (lane & 31) * 16); }
   __device__ void issue_k(int2 p) const {
-    const uint8_t* src = page_of(kp ? p.y : p.x) + I2_K_OFF + kt * 32;
+    if constexpr (BITS == 4) {
+      const uint8_t* src = page_of(kp ? p.y : p.x) + I4C_K_OFF + kt * 64;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(kst_a + 1024 * j, src + (j >> 1) * 64 + (j & 1) * 16);
+      for (int j = 0; j < 8; ++j) dma16(kst_a + 1024 * j, src + (j >> 2) * 128 + (j & 3) * 16);
+    } else {
+      const uint8_t* src = page_of(kp ? p.y : p.x) + I2_K_OFF + kt * 32;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma16(kst_a + 1024 * j, src + (j >> 1) * 64 + (j & 1) * 16);
+    }
   }
   __device__ void issue_v(int2 p) const {
+    if constexpr (BITS == 4) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dma16_base(vst_a + 1024 * j, page_of(j < 2 ? p.x : p.y) + I2_V_OFF + (j & 1) * 1024, lane * 16);
+      for (int j = 0; j < 8; ++j)
+        dma16_base(vst_a + 1024 * j, page_of(j < 4 ? p.x : p.y) + I4C_V_OFF + ((j >> 1) & 1) * 2048 + (j & 1) * 16,
+                   lane * 32);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dma16_base(vst_a + 1024 * j, page_of(j < 2 ? p.x : p.y) + I2_V_OFF + (j & 1) * 1024, lane * 16);
+    }
   }
 };
 
@@ -960,19 +980,32 @@ __device__ __forceinline__ void dot8_word(int (&r)[4], uint4 X, uint4 Y, const u
 
 __device__ __forceinline__ int digits_value(const int (&r)[4]) { return ((r[3] * 16 + r[2]) * 16 + r[1]) * 16 + r[0]; }
 
-// acc[t][head] = digit sums of tokens kt, kt + 2 (code words kw[t][0..7]) against the key digit words.
-template <int GQ>
-__device__ __forceinline__ void key_dots(const uint32_t* adig, const uint32_t (&kw)[2][8], int (&acc)[2][GQ][4]) {
+// Nibble vectors of code word pair idx: nb[0] holds the codes that pair with the X.x / X.y / Y.x / Y.y digit
+// words, nb[1] those of X.z / X.w / Y.z / Y.w.  2-bit codes: word idx, even then odd code positions
+// (values 0..3); 4-bit codes: words 2 idx and 2 idx + 1, less 8 (values -8..7, the offset is taken out of
+// the zero points).
+template <int BITS, int N>
+__device__ __forceinline__ void code_nibbles(uint32_t (&nb)[2], const uint32_t (&w)[N], int idx) {
+  if constexpr (BITS == 4) {
+    nb[0] = w[2 * idx] ^ 0x88888888u;
+    nb[1] = w[2 * idx + 1] ^ 0x88888888u;
+  } else {
+    nb[0] = w[idx] & 0x33333333u;
+    nb[1] = (w[idx] >> 2) & 0x33333333u;
+  }
+}
+
+// acc[t][head] = digit sums of tokens kt, kt + 2 (code words kw[t]) against the key digit words.
+template <int GQ, int BITS>
+__device__ __forceinline__ void key_dots(const uint32_t* adig, const uint32_t (&kw)[2][4 * BITS],
+                                         int (&acc)[2][GQ][4]) {
   auto aword = [&](int idx) { return reinterpret_cast<const uint4*>(adig)[idx]; };  // idx = (hh 8 + mw) 2 + y
   uint4 wx = aword(0), wy = aword(1);
 #pragma unroll
   for (int mw = 0; mw < 8; ++mw) {
     uint32_t nb[2][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      nb[t][0] = kw[t][mw] & 0x33333333u;
-      nb[t][1] = (kw[t][mw] >> 2) & 0x33333333u;
-    }
+    for (int t = 0; t < 2; ++t) code_nibbles<BITS>(nb[t], kw[t], mw);
 #pragma unroll
     for (int hh = 0; hh < GQ; ++hh) {
       const uint4 X = wx, Y = wy;
@@ -988,20 +1021,17 @@ __device__ __forceinline__ void key_dots(const uint32_t* adig, const uint32_t (&
   }
 }
 
-// accv[c][head] = digit sums of channels lane, lane + 64 (code words vw[c][page][g]) against the weights.
-template <int GQ>
-__device__ __forceinline__ void value_dots(const uint8_t* pdig, const uint32_t (&vw)[2][2][4], int (&accv)[2][GQ][4]) {
+// accv[c][head] = digit sums of channels lane, lane + 64 (code words vw[c][page]) against the weights.
+template <int GQ, int BITS>
+__device__ __forceinline__ void value_dots(const uint8_t* pdig, const uint32_t (&vw)[2][2][2 * BITS],
+                                           int (&accv)[2][GQ][4]) {
   auto pword = [&](int idx) { return reinterpret_cast<const uint4*>(pdig)[idx]; };  // ((hh 8 + pg) 2 + y)
   uint4 px = pword(0), py = pword(1);
 #pragma unroll
   for (int pg = 0; pg < 8; ++pg) {  // pg = page * 4 + g
     uint32_t nb[2][2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const uint32_t w = vw[c][pg >> 2][pg & 3];
-      nb[c][0] = w & 0x33333333u;
-      nb[c][1] = (w >> 2) & 0x33333333u;
-    }
+    for (int c = 0; c < 2; ++c) code_nibbles<BITS>(nb[c], vw[c][pg >> 2], pg & 3);
 #pragma unroll
     for (int hh = 0; hh < GQ; ++hh) {
       const uint4 X = px, Y = py;
@@ -1027,8 +1057,8 @@ __device__ __forceinline__ void store_weight_digits(uint8_t* pw, uint32_t u0, ui
   pw[20] = (uint8_t)(y >> 8);  // n d3
 }
 
-template <int GQ>
-__device__ void int2_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
+template <int GQ, int BITS, typename Lds>
+__device__ void int2_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
   constexpr int LG = HeadLog2<GQ>::v;
   constexpr int LPH = 64 >> LG;   // lanes per head in the alpha step
   constexpr int NCH = 2 * GQ;     // channels per lane in the alpha step
@@ -1042,7 +1072,8 @@ __device__ void int2_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int
   const int c0 = lane, c1 = lane + 64;
   const int ah = lane >> (6 - LG);           // head of this lane in the alpha step
   const int ac0 = (lane & (LPH - 1)) * NCH;  // its first channel
-  Dot8Wave<GQ> W(L, a, h, wave, lane);
+  Dot8Wave<GQ, BITS> W(L, a, h, wave, lane);
+  constexpr float ZOFF = BITS == 4 ? 8.0f : 0.0f;  // 4-bit codes enter the dot products less 8
   // weight digit bytes of this lane's tokens: word (page kp, g, n) byte j of each head
   uint8_t* pw = W.pdig + ((W.kp * 4 + ((lane >> 1) & 3)) * 8 + (lane & 1) * 2) * 4 + ((lane >> 3) & 3);
   float qa[NCH];
@@ -1073,7 +1104,8 @@ __device__ void int2_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int
   for (int gi = g_begin + wave; gi < g_end; gi += 4) {
     const bool has_next = gi + 4 < g_end;  // uniform
     if (has_next) pnext = scalar_load_int2(pt + gi + 4);
-    KVQ_WAIT_VM(8);  // this group's M copy (its K and V copies may still be in flight)
+    if constexpr (BITS == 4) KVQ_WAIT_VM(16);  // this group's M copy (its K and V copies may still be in flight)
+    else KVQ_WAIT_VM(8);
     uint32_t skw[NCH / 2], zkw[NCH / 2];
 #pragma unroll
     for (int i = 0; i < NCH / 2; ++i) {
@@ -1104,7 +1136,7 @@ __device__ void int2_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int
       for (int i = 0; i < NCH; ++i) {
         ai[i] = (int)rintf(al[i] * inv);
         const uint32_t w = zkw[i >> 1];
-        zs = fmaf((float)ai[i], __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16)), zs);
+        zs = fmaf((float)ai[i], __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16)) - ZOFF, zs);
       }
       zs = seg_reduce<LPH>(zs, OpAdd());
       const float Ah = amx * (1.0f / kScale8);
@@ -1122,15 +1154,25 @@ __device__ void int2_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int
     wave_lds_sync();
 
     // 3. key dots: tokens kt, kt + 2 of page kp against every head
-    if (has_next) KVQ_WAIT_VM(5);  // this group's K copies (then V, next M may be in flight)
-    else KVQ_WAIT_VM(4);
-    const uint4 k00 = W.kst[c0], k01 = W.kst[64 + c0], k10 = W.kst[128 + c0], k11 = W.kst[192 + c0];
+    // this group's K copies (then V, next M may be in flight)
+    if constexpr (BITS == 4) {
+      if (has_next) KVQ_WAIT_VM(9);
+      else KVQ_WAIT_VM(8);
+    } else {
+      if (has_next) KVQ_WAIT_VM(5);
+      else KVQ_WAIT_VM(4);
+    }
+    uint32_t kw[2][4 * BITS];
+#pragma unroll
+    for (int j = 0; j < 2 * BITS; ++j) {  // copy j: token j / BITS, words 4 (j % BITS) ..
+      const uint4 kk = W.kst[64 * j + c0];
+      uint32_t* dst = &kw[j / BITS][4 * (j % BITS)];
+      dst[0] = kk.x, dst[1] = kk.y, dst[2] = kk.z, dst[3] = kk.w;
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (has_next) W.issue_k(pnext);
     int acc[2][GQ][4];
-    const uint32_t kw[2][8] = {{k00.x, k00.y, k00.z, k00.w, k01.x, k01.y, k01.z, k01.w},
-                               {k10.x, k10.y, k10.z, k10.w, k11.x, k11.y, k11.z, k11.w}};
-    key_dots<GQ>(W.adig, kw, acc);
+    key_dots<GQ, BITS>(W.adig, kw, acc);
 
     // 4. logits, group max, 16-bit weights as nibble digits in LDS
     float lg[2][GQ], mg[GQ], Pf[GQ];
@@ -1159,15 +1201,26 @@ __device__ void int2_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int
     wave_lds_sync();
 
     // 5. value dots: channels c0, c1 against the weights of every head
-    if (has_next) KVQ_WAIT_VM(5);  // this group's V copies (then the next M and K may be in flight)
-    else KVQ_WAIT_VM(0);
-    const uint4 v00 = W.vst[c0], v01 = W.vst[64 + c0], v10 = W.vst[128 + c0], v11 = W.vst[192 + c0];
+    // this group's V copies (then the next M and K may be in flight)
+    if constexpr (BITS == 4) {
+      if (has_next) KVQ_WAIT_VM(9);
+      else KVQ_WAIT_VM(0);
+    } else {
+      if (has_next) KVQ_WAIT_VM(5);
+      else KVQ_WAIT_VM(0);
+    }
+    uint32_t vw[2][2][2 * BITS];  // [channel c0 | c1][page][word]
+#pragma unroll
+    for (int j = 0; j < 2 * BITS; ++j) {
+      const uint4 vv = W.vst[64 * j + c0];
+      // 2-bit: copy j = page j >> 1, channel j & 1; 4-bit: page j >> 2, channel (j >> 1) & 1, words 4 (j & 1) ..
+      uint32_t* dst = BITS == 4 ? &vw[(j >> 1) & 1][j >> 2][4 * (j & 1)] : &vw[j & 1][j >> 1][0];
+      dst[0] = vv.x, dst[1] = vv.y, dst[2] = vv.z, dst[3] = vv.w;
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (has_next) W.issue_v(pnext);
     int accv[2][GQ][4];
-    const uint32_t vw[2][2][4] = {{{v00.x, v00.y, v00.z, v00.w}, {v10.x, v10.y, v10.z, v10.w}},
-                                  {{v01.x, v01.y, v01.z, v01.w}, {v11.x, v11.y, v11.z, v11.w}}};
-    value_dots<GQ>(W.pdig, vw, accv);
+    value_dots<GQ, BITS>(W.pdig, vw, accv);
 
     // 6. online-softmax update in the rotated value frame
 #pragma unroll
@@ -1177,8 +1230,8 @@ __device__ void int2_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int
       const float wg = __builtin_amdgcn_exp2f(mg[hh] - mnew) * (1.0f / kScale8);
       const float U0 = (float)digits_value(accv[0][hh]);
       const float U1 = (float)digits_value(accv[1][hh]);
-      o[hh][0] = fmaf(o[hh][0], sc, (wg * sv0) * fmaf(-zv0, Pf[hh], U0));
-      o[hh][1] = fmaf(o[hh][1], sc, (wg * sv1) * fmaf(-zv1, Pf[hh], U1));
+      o[hh][0] = fmaf(o[hh][0], sc, (wg * sv0) * fmaf(ZOFF - zv0, Pf[hh], U0));
+      o[hh][1] = fmaf(o[hh][1], sc, (wg * sv1) * fmaf(ZOFF - zv1, Pf[hh], U1));
       l[hh] = fmaf(l[hh], sc, wg * Pf[hh]);
       m[hh] = mnew;
     }
@@ -1200,8 +1253,8 @@ __device__ void int2_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int
 // Lane roles, digit words and the copy pipeline as in int2_unit_dot8; the metadata of a page holds its
 // tokens' K scales, K zeros, V scales, V zeros (64 bf16 each).
 // ---------------------------------------------------------------------------------------------
-template <int GQ>
-__device__ void int2tok_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
+template <int GQ, typename Lds>
+__device__ void int2tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
   constexpr int LG = HeadLog2<GQ>::v;
   constexpr int LPH = 64 >> LG;
   constexpr int NCH = 2 * GQ;
@@ -1215,7 +1268,7 @@ __device__ void int2tok_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, 
   const int c0 = lane, c1 = lane + 64;
   const int ah = lane >> (6 - LG);
   const int ac0 = (lane & (LPH - 1)) * NCH;
-  Dot8Wave<GQ> W(L, a, h, wave, lane);
+  Dot8Wave<GQ, 2> W(L, a, h, wave, lane);
   uint8_t* pw = W.pdig + ((W.kp * 4 + ((lane >> 1) & 3)) * 8 + (lane & 1) * 2) * 4 + ((lane >> 3) & 3);
   const int mt0 = W.kp * 256 + (W.kt & 63);  // metadata index of token kt (page kp): K s; +64 K z; +128, +192 V
 
@@ -1289,7 +1342,7 @@ __device__ void int2tok_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, 
     int acc[2][GQ][4];
     const uint32_t kw[2][8] = {{k00.x, k00.y, k00.z, k00.w, k01.x, k01.y, k01.z, k01.w},
                                {k10.x, k10.y, k10.z, k10.w, k11.x, k11.y, k11.z, k11.w}};
-    key_dots<GQ>(W.adig, kw, acc);
+    key_dots<GQ, 2>(W.adig, kw, acc);
 
     // 2. logits, group max, weights p_t s'_t / S' as digits, sum_t p_t and sum_t u_t z'_t
     float lg[2][GQ], mg[GQ], Pl[GQ], Zs[GQ];
@@ -1332,7 +1385,7 @@ __device__ void int2tok_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, 
     int accv[2][GQ][4];
     const uint32_t vw[2][2][4] = {{{v00.x, v00.y, v00.z, v00.w}, {v10.x, v10.y, v10.z, v10.w}},
                                   {{v01.x, v01.y, v01.z, v01.w}, {v11.x, v11.y, v11.z, v11.w}}};
-    value_dots<GQ>(W.pdig, vw, accv);
+    value_dots<GQ, 2>(W.pdig, vw, accv);
 
     // 4. online-softmax update in the rotated value frame
 #pragma unroll
@@ -1367,8 +1420,8 @@ __device__ void int2tok_unit_dot8(DecodeLds<GQ>& L, const DecodeArgs& a, int b, 
 //     (w >> 4n) & 0x0F0F0F0F holds, in byte bw, token 16 (2 (W % 2) + bw / 2) + 4 (W / 2) + 2 (bw % 2) + n
 //     -> weight word (2W + n), byte bw.
 // ---------------------------------------------------------------------------------------------
-template <int GQ>
-__device__ void int4_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
+template <int GQ, typename Lds>
+__device__ void int4_unit_dot16(Lds& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
   constexpr int LG = HeadLog2<GQ>::v;
   constexpr int LPH = 64 >> LG;
   constexpr int NCH = 2 * GQ;
@@ -1560,8 +1613,8 @@ __device__ void int4_unit_dot16(DecodeLds<GQ>& L, const DecodeArgs& a, int b, in
   combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, c0, c1);
 }
 
-template <int GQ>
-__device__ void int4_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
+template <int GQ, typename Lds>
+__device__ void int4_unit(Lds& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
   const Geo& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_pages = (T + PAGE - 1) / PAGE;
@@ -1667,15 +1720,16 @@ __device__ void int4_unit(DecodeLds<GQ>& L, const DecodeArgs& a, int b, int h, i
   combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, lane, lane + 64);
 }
 
-// MODE: 0 fp32, 1 16-bit on the byte dot product, 2 16-bit on the nibble dot product (INT2 only)
+// MODE: 0 fp32, 1 16-bit on the byte dot product, 2 16-bit on the nibble dot product (grouped schemes)
 template <int GQ, int SCHEME, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
-  __shared__ DecodeLds<GQ> L;
+  __shared__ DecodeLds<GQ, SCHEME == KVQ_INT4_CHANNEL ? 2 : 1> L;
   const int unit = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const Geo& g = a.g;
   const int T = a.seq_lens[b];
+  constexpr bool grouped = is_grouped(SCHEME);
   int n_chunks;
-  if (is_int2(SCHEME)) {
+  if (grouped) {
     const int ng = n_groups_of(T, g.S0, g.W);
     n_chunks = (ng + g.gpc - 1) / g.gpc;
   } else {
@@ -1684,7 +1738,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;  // lengths beyond the launch bound are cut
   if (unit > n_chunks) return;
   if (unit == 0) {
-    if (is_int2(SCHEME)) {
+    if constexpr (grouped) {
       band_unit<GQ>(L, a, b, h, T);
     } else {
       // no band: an empty partial
@@ -1694,14 +1748,16 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
         part[k] = (k == 0) ? -INFINITY : 0.0f;
       }
     }
-  } else if (SCHEME == KVQ_INT2_TOKEN) {
+  } else if constexpr (SCHEME == KVQ_INT4_CHANNEL) {
+    int2_unit_dot8<GQ, 4>(L, a, b, h, T, unit - 1);
+  } else if constexpr (SCHEME == KVQ_INT2_TOKEN) {
     int2tok_unit_dot8<GQ>(L, a, b, h, T, unit - 1);
-  } else if (SCHEME == KVQ_INT2_CHANNEL) {
-    if (MODE == 2) int2_unit_dot8<GQ>(L, a, b, h, T, unit - 1);
-    else if (MODE == 1) int2_unit_dot16<GQ>(L, a, b, h, T, unit - 1);
+  } else if constexpr (SCHEME == KVQ_INT2_CHANNEL) {
+    if constexpr (MODE == 2) int2_unit_dot8<GQ, 2>(L, a, b, h, T, unit - 1);
+    else if constexpr (MODE == 1) int2_unit_dot16<GQ>(L, a, b, h, T, unit - 1);
     else int2_unit<GQ>(L, a, b, h, T, unit - 1);
   } else {
-    if (MODE == 1) int4_unit_dot16<GQ>(L, a, b, h, T, unit - 1);
+    if constexpr (MODE == 1) int4_unit_dot16<GQ>(L, a, b, h, T, unit - 1);
     else int4_unit<GQ>(L, a, b, h, T, unit - 1);
   }
 }
@@ -1737,7 +1793,7 @@ __global__ __launch_bounds__(MergeShape<HPW>::NT) void merge_kernel(DecodeArgs a
   const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.seq_lens[b];
   int n_chunks;
-  if (is_int2(g.scheme)) {
+  if (is_grouped(g.scheme)) {
     const int ng = n_groups_of(T, g.S0, g.W);
     n_chunks = (ng + g.gpc - 1) / g.gpc;
   } else {
@@ -1877,7 +1933,9 @@ hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
     const dim3 grid(g.n_units, g.n_kv, g.batch), block(kThreads);
     // AUTO: 16-bit operands on the nibble dot product for INT2, the fp32 kernel for INT4 (faster there:
     // per-token scales leave the fp32 path no per-group work, and 4-bit codes convert cheaply)
-    if (g.scheme == KVQ_INT2_TOKEN) {
+    if (g.scheme == KVQ_INT4_CHANNEL) {
+      hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_CHANNEL, 2>), grid, block, 0, s, a);
+    } else if (g.scheme == KVQ_INT2_TOKEN) {
       hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_TOKEN, 2>), grid, block, 0, s, a);
     } else if (g.scheme == KVQ_INT2_CHANNEL) {
       if (a.impl == KVQ_DECODE_F32) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 0>), grid, block, 0, s, a);

@@ -24,6 +24,10 @@ constexpr int I4_V_OFF = 4096;
 constexpr int I4_KMETA_OFF = 8192;
 constexpr int I4_VMETA_OFF = 8448;
 constexpr int I4_HEAD_BYTES = 8704;
+// INT4 per-channel head block: the INT4 page size with the INT2 per-channel metadata arrangement
+constexpr int I4C_K_OFF = 0;
+constexpr int I4C_V_OFF = 4096;
+constexpr int I4C_META_OFF = 8192;
 
 // 1/sqrt(128) as used by the randomized-Hadamard write: sqrt(2) * 2^-4 rounded once to fp64
 constexpr double INV_SQRT128_F64 = 0x1.6a09e667f3bcdp-4;
@@ -46,12 +50,13 @@ struct Geo {
   int max_pages;    // page-table row length
   int head_bytes;
   long long page_bytes;
-  int gpc;          // groups (INT2) or pages (INT4) per decode chunk
+  int gpc;          // groups (grouped schemes) or pages (INT4 per token) per decode chunk
   int n_units;      // decode partial units per (seq, q head): 1 band unit + chunks
 };
 
-// both INT2 schemes share the page layout, the band and the group demotion
-__host__ __device__ inline bool is_int2(int scheme) { return scheme == KVQ_INT2_CHANNEL || scheme == KVQ_INT2_TOKEN; }
+// both INT2 schemes share the page layout; they and per-channel INT4 share the band and the group demotion
+__host__ __device__ constexpr bool is_int2(int scheme) { return scheme == KVQ_INT2_CHANNEL || scheme == KVQ_INT2_TOKEN; }
+__host__ __device__ constexpr bool is_grouped(int scheme) { return is_int2(scheme) || scheme == KVQ_INT4_CHANNEL; }
 
 __host__ __device__ inline int n_groups_of(int T, int S0, int W) {
   int r = T - S0 - W;

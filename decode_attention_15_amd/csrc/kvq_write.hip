@@ -169,10 +169,10 @@ __device__ inline void rotate_group_mfma(const float* xs, const float* rot, floa
 }
 
 // ---------------------------------------------------------------------------------------------
-// INT2 groups.  One work-group quantizes one (sequence, kv head, K|V, new group):
-// gather 128 bf16 tokens (band or new input) -> rotate -> per-token clip -> min/max per channel over
-// the group (KVQ_INT2_CHANNEL) or per token over its channels (KVQ_INT2_TOKEN) -> bf16 scale/zero
-// -> codes -> K token-major rows / V channel-major rows + metadata.
+// INT2 groups (and their 4-bit per-channel variant).  One work-group quantizes one (sequence, kv head,
+// K|V, new group): gather 128 bf16 tokens (band or new input) -> rotate -> per-token clip -> min/max per
+// channel over the group (KVQ_INT2_CHANNEL, KVQ_INT4_CHANNEL) or per token over its channels
+// (KVQ_INT2_TOKEN) -> bf16 scale/zero -> codes -> K token-major rows / V channel-major rows + metadata.
 // ---------------------------------------------------------------------------------------------
 constexpr int kGroupLds = (GROUP * XS_STRIDE + GROUP * D) * (int)sizeof(float);
 
@@ -222,6 +222,10 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
 
   // 2. rotation (none for V under key-only rotation: the bf16 values themselves)
   const bool tokenwise = g.scheme == KVQ_INT2_TOKEN;
+  const bool four = g.scheme == KVQ_INT4_CHANNEL;
+  const float levels = four ? 15.0f : 3.0f;
+  const long long hoff = (long long)h * g.head_bytes;
+  const int moff = four ? I4C_META_OFF : I2_META_OFF;
   if (which == 1 && g.key_only) {
     for (int e = tid; e < GROUP * D; e += 256) xr[e] = xs[(e >> 7) * XS_STRIDE + (e & (D - 1))];
   } else if (g.rotation == KVQ_ROT_DENSE) {
@@ -255,7 +259,7 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
       const float x0 = xr[tl * D + lane], x1 = xr[tl * D + lane + 64];
       const float amin = wave_min_f32(fminf(x0, x1));
       const float bmax = wave_max_f32(fmaxf(x0, x1));
-      const float s = (bmax > amin) ? __fdiv_rn(__fsub_rn(bmax, amin), 3.0f) : 1.0f;
+      const float s = (bmax > amin) ? __fdiv_rn(__fsub_rn(bmax, amin), levels) : 1.0f;
       const uint16_t s16 = f32_to_bf16_rne(s);
       const float sp = bf16_to_f32(s16);
       const uint16_t z16 = f32_to_bf16_rne(__fdiv_rn(-amin, sp));
@@ -264,8 +268,7 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
         s_zp[tl] = bf16_to_f32(z16);
         // page of the token: its K (which = 0) or V (which = 1) scales[64] then zeros[64]
         const long long phys = a.page_table[(long long)b * g.max_pages + 2 * grp + (tl >> 6)];
-        uint16_t* meta = reinterpret_cast<uint16_t*>(a.pages + phys * g.page_bytes + (long long)h * I2_HEAD_BYTES +
-                                                     I2_META_OFF) + which * 128;
+        uint16_t* meta = reinterpret_cast<uint16_t*>(a.pages + phys * g.page_bytes + hoff + moff) + which * 128;
         meta[tl & 63] = s16;
         meta[64 + (tl & 63)] = z16;
       }
@@ -285,58 +288,106 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
   if (!tokenwise && tid < D) {
     const float amin = fminf(red_min[0][tid], red_min[1][tid]);
     const float bmax = fmaxf(red_max[0][tid], red_max[1][tid]);
-    const float s = (bmax > amin) ? __fdiv_rn(__fsub_rn(bmax, amin), 3.0f) : 1.0f;
+    const float s = (bmax > amin) ? __fdiv_rn(__fsub_rn(bmax, amin), levels) : 1.0f;
     const uint16_t s16 = f32_to_bf16_rne(s);
     const float sp = bf16_to_f32(s16);
     const uint16_t z16 = f32_to_bf16_rne(__fdiv_rn(-amin, sp));
     s_sp[tid] = sp;
     s_zp[tid] = bf16_to_f32(z16);
     const long long phys = a.page_table[(long long)b * g.max_pages + 2 * grp + which];
-    uint16_t* meta = reinterpret_cast<uint16_t*>(a.pages + phys * g.page_bytes + (long long)h * I2_HEAD_BYTES +
-                                                 I2_META_OFF);
+    uint16_t* meta = reinterpret_cast<uint16_t*>(a.pages + phys * g.page_bytes + hoff + moff);
     meta[tid] = s16;
     meta[D + tid] = z16;
   }
   __syncthreads();
 
   // 5. codes and packing
-  auto code2 = [&](float x, int c, int tl) -> uint32_t {
+  auto code = [&](float x, int c, int tl) -> uint32_t {
     const int i = tokenwise ? tl : c;
     float t = __fadd_rn(__fdiv_rn(x, s_sp[i]), s_zp[i]);
-    t = fminf(fmaxf(rintf(t), 0.0f), 3.0f);
+    t = fminf(fmaxf(rintf(t), 0.0f), levels);
     return (uint32_t)t;
   };
   if (which == 0) {
-    // K: token-major, token i at 32*i, channel c in byte c/4 bits 2*(c%4)
+    // K, token-major; thread (token tl, half): channels 64 half .. 64 half + 63
     const int tl = tid >> 1, half = tid & 1;
-    uint32_t w4[4];
-#pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int c = half * 64 + wd * 16 + k;
-        w |= code2(xr[tl * D + c], c, tl) << (2 * k);
-      }
-      w4[wd] = w;
-    }
     const long long phys = a.page_table[(long long)b * g.max_pages + 2 * grp + (tl >> 6)];
-    uint4* dst = reinterpret_cast<uint4*>(a.pages + phys * g.page_bytes + (long long)h * I2_HEAD_BYTES + I2_K_OFF +
-                                          (tl & 63) * 32 + half * 16);
-    *dst = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-  } else {
-    // V: channel-major rows of 16 bytes; token i = 16j + 4g + r in byte 4g + j, bits 2r
-    const int c = tid & (D - 1), ph = tid >> 7;
-    uint32_t w4[4] = {0u, 0u, 0u, 0u};
-#pragma unroll 4
-    for (int i = 0; i < 64; ++i) {
-      const int j = i >> 4, gg = (i >> 2) & 3, r = i & 3;
-      w4[gg] |= code2(xr[(ph * 64 + i) * D + c], c, ph * 64 + i) << (8 * j + 2 * r);
+    uint8_t* row = a.pages + phys * g.page_bytes + hoff + I2_K_OFF;
+    const float* x = xr + tl * D + half * 64;
+    if (four) {
+      // 64 bytes per token; channel block m (16m .. 16m + 15): word 2m nibble k = channel 16m + 2k,
+      // word 2m + 1 nibble k = channel 16m + 2k + 1
+      uint32_t w8[8];
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int cl = 16 * bi + 2 * k + e;
+            w |= code(x[cl], half * 64 + cl, tl) << (4 * k);
+          }
+          w8[2 * bi + e] = w;
+        }
+      uint4* dst = reinterpret_cast<uint4*>(row + (tl & 63) * 64 + half * 32);
+      dst[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
+      dst[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
+    } else {
+      // 32 bytes per token, channel c in byte c/4 bits 2*(c%4)
+      uint32_t w4[4];
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) w |= code(x[wd * 16 + k], half * 64 + wd * 16 + k, tl) << (2 * k);
+        w4[wd] = w;
+      }
+      *reinterpret_cast<uint4*>(row + (tl & 63) * 32 + half * 16) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }
+  } else {
+    // V, channel-major; thread (channel c, page ph of the group); token i = 16j + 4gg + r of the page
+    const int c = tid & (D - 1), ph = tid >> 7;
     const long long phys = a.page_table[(long long)b * g.max_pages + 2 * grp + ph];
-    uint4* dst = reinterpret_cast<uint4*>(a.pages + phys * g.page_bytes + (long long)h * I2_HEAD_BYTES + I2_V_OFF +
-                                          c * 16);
-    *dst = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    const float* x = xr + ph * 64 * D + c;
+    if (four) {
+      // 32-byte rows: token 16j + 4gg + 2hh + n in word 2gg + n, nibble 2j + hh
+      uint32_t w8[8];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int i = 16 * j + 4 * gg + 2 * hh + n;
+              w |= code(x[i * D], c, ph * 64 + i) << (4 * (2 * j + hh));
+            }
+          w8[2 * gg + n] = w;
+        }
+      uint4* dst = reinterpret_cast<uint4*>(a.pages + phys * g.page_bytes + hoff + I4C_V_OFF + c * 32);
+      dst[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
+      dst[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
+    } else {
+      // 16-byte rows: token 16j + 4gg + r in byte 4gg + j, bits 2r
+      uint32_t w4[4];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * j + 4 * gg + r;
+            w |= code(x[i * D], c, ph * 64 + i) << (8 * j + 2 * r);
+          }
+        w4[gg] = w;
+      }
+      *reinterpret_cast<uint4*>(a.pages + phys * g.page_bytes + hoff + I2_V_OFF + c * 16) =
+          make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
   }
 }
 

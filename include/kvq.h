@@ -26,7 +26,7 @@
  *
  * Cache layout (all little-endian)
  *  - Sequence b holds tokens [0, T_b), T_b = seq_lens[b].  With S0 = n_sink, W = n_recent, G = 128:
- *      INT2 schemes: n_g = max(0, (T - S0 - W) / G) full 128-token groups are quantized; group g
+ *      INT2 schemes and INT4_CHANNEL: n_g = max(0, (T - S0 - W) / G) full 128-token groups are quantized; group g
  *      covers tokens [S0 + 128g, S0 + 128g + 128); tokens [0, min(T, S0)) (sink) and
  *      [S0 + 128 n_g, T) (tail, W..W+127 tokens once T >= S0+W) are kept as bf16 in the band.
  *      INT4 scheme: every token is quantized on write (S0 = W = 0, no band).
@@ -41,13 +41,20 @@
  *                    scales[128] then K zeros[128], on its odd page V scales[128] then V zeros[128];
  *                    per token (KVQ_INT2_TOKEN): the page's own tokens, K scales[64], K zeros[64],
  *                    V scales[64], V zeros[64]; all bf16.
+ *  - INT4 per-channel head block (head_bytes = 8704):
+ *      [0, 4096)     K codes, token-major: token i at 64*i, 16 little-endian 32-bit words; channel
+ *                    16m + 2k + e (k < 8, e in {0, 1}) in word 2m + e, bits 4k .. 4k+3.
+ *      [4096, 8192)  V codes, channel-major: channel c at 4096 + 32*c, 8 words; token i = 16j + 4g + 2h + n
+ *                    (j, g < 4; h, n in {0, 1}) in word 2g + n, bits 4(2j + h) .. 4(2j + h) + 3.
+ *      [8192, 8704)  group metadata as for INT2 per channel: even page K scales[128], K zeros[128];
+ *                    odd page V scales[128], V zeros[128]; bf16.
  *  - INT4 token-wise head block (head_bytes = 8704):
  *      [0, 4096)     K codes, token-major: token i at 64*i; channel c in byte c/2, low nibble = even c.
  *      [4096, 8192)  V codes, channel-major: channel c at 4096 + 32*c; token i = 16j + 4g + r in
  *                    byte 8*g + 2*j + r/2, low nibble when r is even.
  *      [8192, 8448)  K per-token (scale, zero) bf16 pairs, token i at 8192 + 4*i.
  *      [8448, 8704)  V per-token (scale, zero) bf16 pairs.
- *  - Band (INT2 schemes): per (b, kv head) kvq_band_slots() slots of 512 bytes: bf16 K[128] then
+ *  - Band (INT2 schemes, INT4_CHANNEL): per (b, kv head) kvq_band_slots() slots of 512 bytes: bf16 K[128] then
  *    bf16 V[128], unrotated.  Token t < S0 sits in slot t; a tail token t in slot
  *    S0 + (t - S0) % (W + 128).  Band base of (b, h) = ((b * n_kv_heads) + h) * slots * 512.
  *
@@ -63,7 +70,8 @@
  *    j = floor(127*rho), f = fp32(127*rho - j) (tau = y[127] when j = 127); x = min(max(x~, -tau), tau).
  *  - INT2 per channel over the group: s = fp32((b-a)/3) (1 if b == a) -> bf16 s'; z = fp32(-a/s') ->
  *    bf16 z'; code = clamp(rint(fp32(fp32(x/s') + z')), 0, 3), rint ties to even.  INT2 per token:
- *    the same with a, b the min and max of the token's 128 (clipped) channels.
+ *    the same with a, b the min and max of the token's 128 (clipped) channels.  INT4 per channel: the same
+ *    per-channel arithmetic with 15 levels: s = fp32((b-a)/15), code = clamp(rint(fp32(fp32(x/s') + z')), 0, 15).
  *  - Key-only rotation (key_only_rotation = 1): V is quantized in its own frame (no rotation, the
  *    bf16 values exactly) and the output is not un-rotated; K is rotated as above.
  *  - INT4 per token: s = fp32((b-a)/15) -> bf16 s'; z = rint(fp32(-a/s')) -> bf16 z';
@@ -95,8 +103,10 @@ typedef enum {
    INT4_TOKEN:   [SAW] token-wise asymmetric INT4, integer zero point, no band;
    INT2_TOKEN:   [OSCAR] §3.4.4 step 3 as the English page states it: asymmetric INT2 per token over its
                  128 channels (one group per head), real zero point; same pages, band and demotion as
-                 INT2_CHANNEL, with per-token scales/zeros in the page metadata. */
-typedef enum { KVQ_INT2_CHANNEL = 0, KVQ_INT4_TOKEN = 1, KVQ_INT2_TOKEN = 2 } kvq_scheme;
+                 INT2_CHANNEL, with per-token scales/zeros in the page metadata;
+   INT4_CHANNEL: the per-channel scheme with 4-bit codes (15 levels, real zero point), same band and
+                 128-token groups, INT4 page size. */
+typedef enum { KVQ_INT2_CHANNEL = 0, KVQ_INT4_TOKEN = 1, KVQ_INT2_TOKEN = 2, KVQ_INT4_CHANNEL = 3 } kvq_scheme;
 typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
 typedef enum { KVQ_ROT_DENSE = 0, KVQ_ROT_HADAMARD = 1 } kvq_rotation;
 /* Arithmetic of the quantized-token part of the decode (the bf16 band is always fp32):
@@ -107,8 +117,8 @@ typedef enum { KVQ_ROT_DENSE = 0, KVQ_ROT_HADAMARD = 1 } kvq_rotation;
    DOT8  - INT2 only: the same 16-bit operands (full scale 30583) as four signed 4-bit digits on the 8-way
            nibble dot product, which needs fewer operations to unpack the 2-bit codes (INT2_TOKEN:
            the rotated query once per work-group, the weights p_t s_t per group);
-   MFMA  - reserved, not built;  AUTO - DOT8 for INT2, F32 for INT4 (the fastest of each).
-   INT2_TOKEN is built with DOT8 only (F32 and DOT16 return KVQ_EUNSUPPORTED for it). */
+   MFMA  - reserved, not built;  AUTO - DOT8 for INT2 and INT4_CHANNEL, F32 for INT4_TOKEN (the fastest of each).
+   INT2_TOKEN and INT4_CHANNEL are built with DOT8 only (F32 and DOT16 return KVQ_EUNSUPPORTED for them). */
 typedef enum {
   KVQ_DECODE_AUTO = 0,
   KVQ_DECODE_F32 = 1,

@@ -260,8 +260,9 @@ def clip_tokens(xt: np.ndarray, rho: float) -> np.ndarray:
 F32 = np.float32
 
 
-def quantize_int2_channel_group(xc: np.ndarray):
-    """Asymmetric affine INT2 of one 128-token group, per channel ([OSCAR] §3.4.4 step 3; R4, R5).
+def quantize_int2_channel_group(xc: np.ndarray, qmax: int = 3):
+    """Asymmetric affine INT2 of one 128-token group, per channel ([OSCAR] §3.4.4 step 3; R4, R5);
+    qmax = 15 gives the per-channel INT4 variant with the same arithmetic.
 
     xc: [128 tokens, 128 channels] float32 (clipped, rotated).
     Returns codes uint8 [tokens, channels], s16 and z16 bf16 bits [channels].
@@ -269,7 +270,7 @@ def quantize_int2_channel_group(xc: np.ndarray):
     xc = np.asarray(xc, dtype=np.float32)
     a = xc.min(axis=0)
     b = xc.max(axis=0)
-    s = np.where(b > a, ((b - a).astype(F32) / F32(3)).astype(F32), F32(1)).astype(F32)
+    s = np.where(b > a, ((b - a).astype(F32) / F32(qmax)).astype(F32), F32(1)).astype(F32)
     s16 = bf16_rne(s)
     sp = bf16_value(s16)
     z = ((-a).astype(F32) / sp).astype(F32)
@@ -277,7 +278,7 @@ def quantize_int2_channel_group(xc: np.ndarray):
     zp = bf16_value(z16)
     t = (xc / sp[None, :]).astype(F32)
     t = (t + zp[None, :]).astype(F32)
-    q = np.clip(np.rint(t), 0, 3).astype(np.uint8)
+    q = np.clip(np.rint(t), 0, qmax).astype(np.uint8)
     return q, s16, z16
 
 
@@ -356,7 +357,9 @@ def int2_state(k_src, v_src, T: int, n_sink: int, n_recent: int, clip_k: float, 
     the group) or "token" (per token over its channels).  R_V32 = None: key-only rotation, the
     values are quantized in their own frame.
     """
-    quant = quantize_int2_channel_group if axis == "channel" else quantize_int2_token
+    # axis "channel4": the per-channel INT4 variant (same groups, band and arithmetic, 15 levels)
+    quant = {"channel": quantize_int2_channel_group, "token": quantize_int2_token,
+             "channel4": lambda x: quantize_int2_channel_group(x, 15)}[axis]
     kb = source_to_bf16(np.asarray(k_src)[:T])
     vb = source_to_bf16(np.asarray(v_src)[:T])
     ng = n_groups(T, n_sink, n_recent)
@@ -421,7 +424,7 @@ def int2_keys_values(state, R_K32, R_V32):
     keys = [bf16_value(state["band_k"]).astype(np.float64)]
     vals = [bf16_value(state["band_v"]).astype(np.float64)]
     # per-channel scales broadcast over tokens (rows), per-token ones over channels (columns)
-    bc = (lambda x: x[None, :]) if state.get("axis", "channel") == "channel" else (lambda x: x[:, None])
+    bc = (lambda x: x[:, None]) if state.get("axis", "channel") == "token" else (lambda x: x[None, :])
     for i in range(len(state["groups"])):
         xk = dequantize(state["k_codes"][i], bc(state["k_s16"][i]), bc(state["k_z16"][i]))
         xv = dequantize(state["v_codes"][i], bc(state["v_s16"][i]), bc(state["v_z16"][i]))

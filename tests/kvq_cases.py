@@ -17,12 +17,18 @@ import synth
 
 I2_HEAD, I4_HEAD = 4608, 8704
 TOL = 2e-3  # max |output - oracle| for every workload
+# schemes with 128-token groups and a bf16 band, and the oracle's quantizer axis of each
+GROUPED = {"int2_channel": "channel", "int2_token": "token", "int4_channel": "channel4"}
+
+
+def head_bytes(scheme: str) -> int:
+    return I2_HEAD if scheme in ("int2_channel", "int2_token") else I4_HEAD
 
 
 def config_for(K, wl: synth.Workload, split_tokens: int = 0, decode_impl: int = 0):
     rot = K.ROT_DENSE if wl.rotation == "oscar" else K.ROT_HADAMARD
-    if wl.scheme in ("int2_channel", "int2_token"):
-        scheme = K.INT2_CHANNEL if wl.scheme == "int2_channel" else K.INT2_TOKEN
+    if wl.scheme in GROUPED:
+        scheme = {"int2_channel": K.INT2_CHANNEL, "int2_token": K.INT2_TOKEN, "int4_channel": K.INT4_CHANNEL}[wl.scheme]
         return K.make_config(wl.n_kv_heads, wl.n_q_heads, scheme, rot, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v,
                              split_tokens, decode_impl, wl.key_only, wl.hadamard_block if wl.rotation == "saw" else 0)
     return K.make_config(wl.n_kv_heads, wl.n_q_heads, K.INT4_TOKEN, rot, 0, 0, 1.0, 1.0, split_tokens, decode_impl,
@@ -123,9 +129,35 @@ def _page(pages: np.ndarray, page_bytes: int, phys: int) -> np.ndarray:
     return pages[phys * page_bytes:(phys + 1) * page_bytes]
 
 
+def read_int4_channel_group(bc: BuiltCache, pages: np.ndarray, b: int, h: int, g: int) -> Dict[str, np.ndarray]:
+    """INT4_CHANNEL: logical codes [128 tok, 128 ch] and per-channel bf16 scale/zero bits of one group."""
+    pb = bc.wl.n_kv_heads * I4_HEAD
+    pt = bc.cache.page_table.cpu().numpy()
+    kc = np.zeros((128, 128), np.uint8)
+    vc = np.zeros((128, 128), np.uint8)
+    meta = []
+    for pp in range(2):
+        blk = _page(pages, pb, int(pt[b, 2 * g + pp]))[h * I4_HEAD:(h + 1) * I4_HEAD]
+        # K: token i's 16 words; channel 16m + 2k + e in word 2m + e, nibble k
+        kw = blk[0:4096].view(np.uint32).reshape(64, 16)
+        for c in range(128):
+            m, k, e = c // 16, (c % 16) // 2, c % 2
+            kc[pp * 64:(pp + 1) * 64, c] = (kw[:, 2 * m + e] >> (4 * k)) & 15
+        # V: channel c's 8 words; token 16j + 4g + 2hh + n in word 2g + n, nibble 2j + hh
+        vw = blk[4096:8192].view(np.uint32).reshape(128, 8)
+        for i in range(64):
+            j, gg, hh, n = i // 16, (i // 4) % 4, (i // 2) % 2, i % 2
+            vc[pp * 64 + i, :] = (vw[:, 2 * gg + n] >> (4 * (2 * j + hh))) & 15
+        meta.append(blk[8192:8704].view(np.uint16))
+    return {"k_codes": kc, "v_codes": vc, "k_s16": meta[0][:128], "k_z16": meta[0][128:],
+            "v_s16": meta[1][:128], "v_z16": meta[1][128:]}
+
+
 def read_int2_group(bc: BuiltCache, pages: np.ndarray, b: int, h: int, g: int) -> Dict[str, np.ndarray]:
     """Logical codes [128 tok, 128 ch] and bf16 scale/zero bits of one group of one (seq, kv head):
-    per channel [128] (INT2_CHANNEL) or per token of the group [128] (INT2_TOKEN)."""
+    per channel [128] (INT2_CHANNEL, INT4_CHANNEL) or per token of the group [128] (INT2_TOKEN)."""
+    if bc.wl.scheme == "int4_channel":
+        return read_int4_channel_group(bc, pages, b, h, g)
     n_kv = bc.wl.n_kv_heads
     pb = n_kv * I2_HEAD
     pt = bc.cache.page_table.cpu().numpy()
@@ -198,9 +230,9 @@ def oracle_out(bc: BuiltCache, q: np.ndarray, b: int, h: int, T: int) -> np.ndar
     k, v = source_of(bc.wl, b, T)
     gq = bc.wl.gq
     qh = q[b, h * gq:(h + 1) * gq]
-    if bc.wl.scheme in ("int2_channel", "int2_token"):
+    if bc.wl.scheme in GROUPED:
         o, _ = O.decode_int2(qh, k[:, h], v[:, h], T, bc.wl.n_sink, bc.wl.n_recent, bc.wl.clip_k, bc.wl.clip_v,
-                             bc.rk, bc.rv, axis="channel" if bc.wl.scheme == "int2_channel" else "token")
+                             bc.rk, bc.rv, axis=GROUPED[bc.wl.scheme])
     else:
         o, _ = O.decode_int4(qh, k[:, h], v[:, h], T, bc.rk.astype(np.int8),
                              None if bc.rv is None else bc.rv.astype(np.int8), block=bc.wl.hadamard_block)
@@ -236,7 +268,7 @@ def check_int2(bc, b, h, groups=None, pages=None, band=None):
     T = int(bc.lens[b])
     k, v = source_of(bc.wl, b, T)
     st = O.int2_state(k[:, h], v[:, h], T, bc.wl.n_sink, bc.wl.n_recent, bc.wl.clip_k, bc.wl.clip_v,
-                      bc.rk, bc.rv, groups=groups, axis="token" if bc.wl.scheme == "int2_token" else "channel")
+                      bc.rk, bc.rv, groups=groups, axis=GROUPED[bc.wl.scheme])
     for i, g in enumerate(st["groups"]):
         got = read_int2_group(bc, pages, b, h, int(g))
         for key in ("k_codes", "v_codes", "k_s16", "k_z16", "v_s16", "v_z16"):

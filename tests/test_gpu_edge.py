@@ -11,7 +11,7 @@ import pytest
 
 import oracle as O
 import synth
-from kvq_cases import config_for, read_band, read_int2_group, rotations, source_torch
+from kvq_cases import GROUPED, config_for, read_band, read_int2_group, rotations, source_torch
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -59,7 +59,7 @@ def _write_and_check(K, wl, kb, vb, clip=(0.96, 0.92), chunks=None, decode=True)
     band = cache.band.cpu().numpy().view(np.uint16)
     bc = _BC(wl, cache)
     worst = 0.0
-    axis = "token" if wl.scheme == "int2_token" else "channel"
+    axis = GROUPED[wl.scheme]
     for h in range(wl.n_kv_heads):
         st = O.int2_state(kb[:, h], vb[:, h], T, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v, rk, rv, axis=axis)
         for i, g in enumerate(st["groups"]):
@@ -90,7 +90,7 @@ def _bf16(x):
 
 
 WL = synth.scaled(synth.WORKLOADS["gqa_b1_32k"], n_q_heads=8, n_kv_heads=2)
-SCHEMES = pytest.mark.parametrize("scheme", ["int2_channel", "int2_token"])
+SCHEMES = pytest.mark.parametrize("scheme", ["int2_channel", "int2_token", "int4_channel"])
 
 
 @SCHEMES

@@ -1,6 +1,7 @@
 """GPU parity of the scheme variants: per-token INT2 (KVQ_INT2_TOKEN, min/max over a token's 128 channels
-as the English OSCAR summary page states §3.4.4 step 3) and key-only rotation (V quantized in its own
-frame, [SAW] App. C's default) for all three schemes.  Same bar as the main parity tests: codes, bf16
+as the English OSCAR summary page states §3.4.4 step 3), per-channel INT4 (KVQ_INT4_CHANNEL, the
+per-channel groups with 15 levels) and key-only rotation (V quantized in its own frame, [SAW] App. C's
+default) for every scheme.  Same bar as the main parity tests: codes, bf16
 scales/zeros and band bytes bit-exact against the oracle, outputs within 2e-3.
 """
 import numpy as np
@@ -63,7 +64,49 @@ def test_int2_token_gqa_full_sampled(K):
     check_out(bc, out, q, [(0, 1), (0, 6)])
 
 
-@pytest.mark.parametrize("scheme", ["int2_channel", "int2_token"])
+def test_int4_channel_single_head_fp32_source(K):
+    wl = synth.scaled(synth.WORKLOADS["tiny_1h_4k"], scheme="int4_channel")
+    _say("int4 per channel: tiny 1 head, T=4096, fp32 source with x10 outlier channels")
+    _int2_case(K, wl, [4096], [0])
+
+
+def test_int4_channel_gq2_ragged_with_appends(K):
+    wl = synth.scaled(synth.WORKLOADS["gqa_b1_32k"], scheme="int4_channel", n_q_heads=16, n_kv_heads=8)
+    _say("int4 per channel: GQA 2, lens [2900, 1000, 133, 0], 5 appends (demotions on the way)")
+    _int2_case(K, wl, [2900, 1000, 133, 0], [0, 3, 7], append_steps=5)
+
+
+def test_int4_channel_gq4_batch_split(K):
+    wl = synth.scaled(synth.WORKLOADS["batch32_32k"], scheme="int4_channel")
+    lens = [4100, 2000, 260, 1029, 3000, 388]
+    _say(f"int4 per channel: GQA 4, lens {lens}, 800-token prefill chunks, 2 appends")
+    _int2_case(K, wl, lens, [0, 5], append_steps=2, chunk=800)
+
+
+def test_int4_channel_gq8_decaying_spectrum_chunked(K):
+    wl = synth.scaled(synth.WORKLOADS["long_b4_131k"], scheme="int4_channel")
+    _say("int4 per channel: GQA 8, sigma_c = (c+1)^-0.5, lens [3000, 700], 1000-token prefill chunks, split 512")
+    _int2_case(K, wl, [3000, 700], [0, 5], chunk=1000, split=512)
+
+
+def test_int4_channel_batch32_full_sampled(K):
+    """The batch32_32k shape at its full size (32 x 32768 tokens, 8 kv heads, 32 q heads) with per-channel
+    INT4: groups and outputs sampled over sequences and heads."""
+    wl = synth.scaled(synth.WORKLOADS["batch32_32k"], scheme="int4_channel")
+    lens = [32768] * 32
+    _say("int4 per channel: batch32_32k full size, sampled")
+    bc = build_cache(K, wl, lens, append_steps=1, seqs_per_call=4)
+    pages, band = _host(bc)
+    ng = O.n_groups(32768, wl.n_sink, wl.n_recent)
+    for b, h in ((0, 0), (17, 5), (31, 7)):
+        check_int2(bc, b, h, groups=[0, ng // 2, ng - 1], pages=pages, band=band)
+    q = synth.queries(wl)
+    out = run_decode(K, bc, q)
+    worst = check_out(bc, out, q, [(0, 0), (9, 2), (17, 5), (31, 7)])
+    _say(f"   max |out - oracle| = {worst:.2e}")
+
+
+@pytest.mark.parametrize("scheme", ["int2_channel", "int2_token", "int4_channel"])
 def test_key_only_rotation_int2(K, scheme):
     wl = synth.scaled(synth.WORKLOADS["gqa_b1_32k"], scheme=scheme, key_only=True)
     _say(f"key-only rotation, {scheme}: lens [2500, 400], 3 appends")

@@ -79,7 +79,7 @@ def test_bits_per_element_match_the_pages():
     ("n_q_heads", 30, K.KVQ_EINVAL), ("n_kv_heads", 0, K.KVQ_EINVAL), ("clip_k", 0.0, K.KVQ_EINVAL),
     ("clip_v", 1.5, K.KVQ_EINVAL), ("split_tokens", 100, K.KVQ_EINVAL), ("n_sink", -1, K.KVQ_EINVAL),
     ("decode_impl", 9, K.KVQ_EINVAL), ("decode_impl", 2, K.KVQ_EUNSUPPORTED),
-    ("key_only_rotation", 2, K.KVQ_EINVAL), ("key_only_rotation", -1, K.KVQ_EINVAL), ("scheme", 3, K.KVQ_EUNSUPPORTED),
+    ("key_only_rotation", 2, K.KVQ_EINVAL), ("key_only_rotation", -1, K.KVQ_EINVAL), ("scheme", 4, K.KVQ_EUNSUPPORTED),
 ])
 def test_config_validation(field, value, status):
     cfg = K.make_config(8, 32)
@@ -167,3 +167,25 @@ def test_int2_token_scheme_config():
         assert K.bits_per_element(a, max(T, 1)) == K.bits_per_element(c, max(T, 1))
     assert K.page_bytes(a) == K.page_bytes(c) and K.band_bytes(a, 4) == K.band_bytes(c, 4)
     assert K.check_config(K.make_config(8, 32, key_only_rotation=True)) == K.KVQ_OK
+
+
+def test_int4_channel_scheme_config():
+    """Per-channel INT4: the INT2 groups, band and page count on the INT4 page size; built on DOT8 only."""
+    for impl, want in ((K.DECODE_AUTO, K.KVQ_OK), (K.DECODE_DOT8, K.KVQ_OK), (K.DECODE_F32, K.KVQ_EUNSUPPORTED),
+                       (K.DECODE_DOT16, K.KVQ_EUNSUPPORTED)):
+        assert K.check_config(K.make_config(8, 32, scheme=K.INT4_CHANNEL, decode_impl=impl)) == want
+    a = K.make_config(8, 32, scheme=K.INT4_CHANNEL)
+    c = K.make_config(8, 32, scheme=K.INT2_CHANNEL)
+    t = K.make_config(8, 32, scheme=K.INT4_TOKEN, rotation=K.ROT_HADAMARD, n_sink=0, n_recent=0, clip_k=1.0,
+                      clip_v=1.0)
+    assert K.page_bytes(a) == K.page_bytes(t) == 8 * 8704
+    assert K.band_slots(a) == K.band_slots(c) and K.band_bytes(a, 4) == K.band_bytes(c, 4)
+    for T in (0, 100, 4096, 32768):
+        assert K.pages_for_len(a, T) == K.pages_for_len(c, T)
+    # one full group past the band: 128 x 128 codes at 4 bits + 2 x 128 bf16 per K and V
+    T = 4 + 128 + 128
+    want = (2 * (128 * 128 / 2 + 2 * 128 * 2) + (T - 128) * 512) * 8 / (2 * T * 128)
+    assert abs(K.bits_per_element(a, T) - want) < 1e-9
+    for hb in (16, 32, 64):
+        assert K.check_config(K.make_config(8, 32, scheme=K.INT4_CHANNEL, rotation=K.ROT_HADAMARD,
+                                            hadamard_block=hb)) == K.KVQ_OK

@@ -487,3 +487,25 @@ def test_causal_attention_reduces_to_decode_and_to_prefixes():
     st = O.int2_state(k, v, T, 4, 128, 0.96, 0.92, RK, RV)
     tp = O.token_positions(st, T, 4, 128)
     assert sorted(tp.tolist()) == list(range(T))
+
+
+def test_int4_channel_quantizer_closed_forms():
+    """Per-channel INT4 (15 levels): channels built as a + s n, n in {0..15} and s a power of two, give codes
+    n and dequantize exactly; the 3-level instance is the pinned INT2 quantizer."""
+    r = np.random.default_rng(71)
+    n = r.integers(0, 16, size=(128, 128))
+    n[0, :], n[1, :] = 0, 15
+    a = -r.integers(1, 9, size=(1, 128)).astype(np.float32)
+    s = (2.0 ** r.integers(-3, 2, size=(1, 128))).astype(np.float32)
+    x = (a + s * n).astype(np.float32)
+    q, s16, z16 = O.quantize_int2_channel_group(x, 15)
+    assert np.array_equal(q, n)
+    assert np.array_equal(O.dequantize(q, s16[None, :], z16[None, :]), x.astype(np.float64))
+    y = r.standard_normal((128, 128)).astype(np.float32)
+    for got, want in zip(O.quantize_int2_channel_group(y, 3), O.quantize_int2_channel_group(y)):
+        assert np.array_equal(got, want)
+    # the reconstruction error of 4 bits is within half a step of the 15-level grid
+    q, s16, z16 = O.quantize_int2_channel_group(y, 15)
+    err = np.abs(O.dequantize(q, s16[None, :], z16[None, :]) - y)
+    step = O.bf16_value(s16).astype(np.float64)
+    assert np.all(err <= step[None, :] * 0.5 * (1 + 1e-2) + 1e-6)
