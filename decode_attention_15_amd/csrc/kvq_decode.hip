@@ -511,6 +511,85 @@ struct OpAdd {
   __device__ float operator()(float a, float b) const { return a + b; }
 };
 
+// Segment reductions whose cross-lane moves fold into the operation (v_add_f32_dpp, v_max_i32_dpp): the
+// moves read valid lanes only, so the bound-control fill value never enters a result.
+#define KVQ_UPDDPP(x, ctrl) __builtin_amdgcn_update_dpp(0, (x), (ctrl), 0xF, 0xF, true)
+template <int N>
+__device__ inline float seg_sum(float x) {
+  x += __int_as_float(KVQ_UPDDPP(__float_as_int(x), 0xB1));
+  x += __int_as_float(KVQ_UPDDPP(__float_as_int(x), 0x4E));
+  x += __int_as_float(KVQ_UPDDPP(__float_as_int(x), 0x141));
+  if (N >= 16) x += __int_as_float(KVQ_UPDDPP(__float_as_int(x), 0x140));
+  if (N >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if (N >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return x;
+}
+template <int N>
+__device__ inline int seg_max_i(int x) {
+  x = max(x, KVQ_UPDDPP(x, 0xB1));
+  x = max(x, KVQ_UPDDPP(x, 0x4E));
+  x = max(x, KVQ_UPDDPP(x, 0x141));
+  if (N >= 16) x = max(x, KVQ_UPDDPP(x, 0x140));
+  if (N >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+    x = max((int)r[0], (int)r[1]);
+  }
+  if (N >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+    x = max((int)r[0], (int)r[1]);
+  }
+  return x;
+}
+
+// heads_allreduce over integers (max) or floats (sum) with the folded segment steps.
+template <int GQ, typename T, typename Op, typename Seg>
+__device__ inline void heads_allreduce_fast(const T (&v)[GQ], Op op, Seg seg, int lane, T (&out)[GQ]) {
+  constexpr int LG = HeadLog2<GQ>::v;
+  T cur[GQ];
+#pragma unroll
+  for (int i = 0; i < GQ; ++i) cur[i] = v[i];
+#pragma unroll
+  for (int s = 0; s < LG; ++s) {
+    const int bit = 5 - s;
+    const int half = GQ >> (s + 1);
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      if (bit >= 4) {
+        const auto r = bit == 5 ? __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, cur[i]),
+                                                                   __builtin_bit_cast(uint32_t, cur[half + i]), false, false)
+                                : __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, cur[i]),
+                                                                   __builtin_bit_cast(uint32_t, cur[half + i]), false, false);
+        // copy the pair's elements out before reinterpreting them: a bit_cast of the element expressions
+        // themselves reads the first element twice with this compiler
+        const uint32_t r0 = r[0], r1 = r[1];
+        cur[i] = op(__builtin_bit_cast(T, r0), __builtin_bit_cast(T, r1));
+      } else {  // bit 3: lane xor 8 within a row
+        const bool up = (lane >> bit) & 1;
+        const T send = up ? cur[i] : cur[half + i];
+        const T keep = up ? cur[half + i] : cur[i];
+        cur[i] = op(keep, __builtin_bit_cast(T, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0x128, 0xF, 0xF, false)));
+      }
+    }
+  }
+  const T x = seg(cur[0]);
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh)
+    out[hh] = __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), hh << (6 - LG)));
+}
+
+// max of two floats without the sNaN quieting that fmaxf adds for operands of unknown origin
+__device__ inline float fmax_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // ---------------------------------------------------------------------------------------------
 // INT2 chunk, 16-bit fixed point on the 4-way byte dot product (v_dot4).  Same algebra as
 // int2_unit, with the two per-group operands quantized to 16 bits:
@@ -802,12 +881,14 @@ __device__ void int2_unit_dot16(Lds& L, const DecodeArgs& a, int b, int h, int T
 }
 
 // ---------------------------------------------------------------------------------------------
-// INT2 chunk, 16-bit fixed point on the 8-way signed nibble dot product (v_dot8).  Same algebra and the
-// same rounding steps as int2_unit_dot16; the 16-bit operands are written as four signed 4-bit digits
-//   x = d0 + 16 d1 + 256 d2 + 4096 d3,  d_k in [-8, 7]  (|x| <= 0x7777 = 30583),
-// read off the biased value x + 0x8888 (whose hex digits are d_k + 8) by flipping bit 3 of every nibble.
-// A 2-bit code fills a nibble after a single mask, so one code word unpacks in three operations (seven
-// for the byte form), and one dot8 multiplies 8 codes with one digit of 8 operands.
+// INT2 chunk (and per-channel INT4), 16-bit fixed point on the 8-way nibble dot product (v_dot8).  Same
+// algebra as int2_unit_dot16.  The key-side operand a = rint(alpha * 30583 / max|alpha|) is written as four
+// signed 4-bit digits
+//   a = d0 + 16 d1 + 256 d2 + 4096 d3,  d_k in [-8, 7]  (|a| <= 0x7777 = 30583),
+// read off the biased value a + 0x8888 (whose hex digits are d_k + 8) by flipping bit 3 of every nibble;
+// the weights u = rint(65535 p), p in [0, 1], are non-negative and use their four hex digits as they are
+// (unsigned products).  A 2-bit code fills a nibble after a single mask, so one code word unpacks in three
+// operations (seven for the byte form), and one dot8 multiplies 8 codes with one digit of 8 operands.
 //   K code word m (channel 16m + 4j + k in byte j, bits 2k): (w >> 2n) & 0x33333333 holds channel
 //   16m + 4j + n in the low and 16m + 4j + n + 2 in the high nibble of byte j (n = 0, 1);
 //   V code word g of a channel (token 16j + 4g + r in byte j, bits 2r): (w >> 2n) & 0x33333333 holds
@@ -833,10 +914,31 @@ __device__ inline void dma16_base(uint32_t lds, const void* gbase, uint32_t voff
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(gbase)
                : "memory");
 }
+// With an immediate offset: the instruction adds it to the LDS address too, so M0 is set OFF lower and the
+// bytes land at lds + 16 i as with dma16.
+template <int OFF>
+__device__ inline void dma16_off(uint32_t lds, const void* gaddr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:%2" ::"s"(lds - OFF), "v"(gaddr),
+               "i"(OFF)
+               : "memory");
+}
 #define KVQ_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
 
 constexpr float kScale8 = 30583.0f;  // 0x7777: largest magnitude of four signed digits
 constexpr int kBias8 = 0x8888;
+constexpr float kScaleW = 65535.0f;  // value-side weights: four unsigned digits
+// Rounding by a magic addend: for |x| <= 2^21, fp32(x + 1.5 * 2^23 + c) = 1.5 * 2^23 + c + rint(x) exactly
+// (ties to even), and the low 16 bits of its encoding are rint(x) + c when 0 <= rint(x) + c < 2^16.
+constexpr float kRoundA = 12582912.0f + (float)kBias8;  // key side: low half = a + 0x8888
+constexpr float kRoundW = 8388608.0f;                   // weights (x >= 0): 2^23 + u, low half = u
+constexpr uint32_t kRoundWBits = 0x4B000000u;
+
+// ((r3 * 16 + r2) * 16 + r1) * 16 + r0 in three shift-adds
+__device__ __forceinline__ int shl4_add(int hi, int lo) {
+  int r;
+  asm("v_lshl_add_u32 %0, %1, 4, %2" : "=v"(r) : "v"(hi), "v"(lo));
+  return r;
+}
 
 __device__ inline int sdot8_z(uint32_t a, uint32_t b) {
   int r;
@@ -844,6 +946,14 @@ __device__ inline int sdot8_z(uint32_t a, uint32_t b) {
   return r;
 }
 __device__ inline int sdot8(uint32_t a, uint32_t b, int c) { return __builtin_amdgcn_sdot8((int)a, (int)b, c, false); }
+__device__ inline int udot8_z(uint32_t a, uint32_t b) {
+  int r;
+  asm("v_dot8_u32_u4 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ inline int udot8(uint32_t a, uint32_t b, int c) {
+  return (int)__builtin_amdgcn_udot8(a, b, (uint32_t)c, false);
+}
 
 // Nibble pairs of two biased values (one per 16-bit half, or one each): X has [d0(lo) | d0(hi) << 4,
 // d2(lo) | d2(hi) << 4] per 16-bit half, Y the d1 and d3 pairs; both still biased.
@@ -902,16 +1012,30 @@ struct Dot8Wave {
     kt = 16 * ((lane >> 3) & 3) + 4 * ((lane >> 1) & 3) + (lane & 1);
   }
   __device__ const uint8_t* page_of(int idx) const { return pages + (long long)idx * page_bytes + hoff; }
-  __device__ void issue_m(int2 p) const { dma16(mst_a, page_of(lane < 32 ? p.x : p.y) + META + (lane & 31) * 16); }
+  // the lane's page of the pair: both page addresses are wave-uniform, the choice per lane is a select
+  __device__ const uint8_t* lane_page(int2 p, bool second) const {
+    const uint8_t* px = page_of(p.x);
+    const uint8_t* py = page_of(p.y);
+    return second ? py : px;
+  }
+  __device__ void issue_m(int2 p) const { dma16(mst_a, lane_page(p, lane >= 32) + META + (lane & 31) * 16); }
   __device__ void issue_k(int2 p) const {
     if constexpr (BITS == 4) {
-      const uint8_t* src = page_of(kp ? p.y : p.x) + I4C_K_OFF + kt * 64;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dma16(kst_a + 1024 * j, src + (j >> 2) * 128 + (j & 3) * 16);
+      const uint8_t* src = lane_page(p, kp) + I4C_K_OFF + kt * 64;
+      dma16_off<0>(kst_a, src);
+      dma16_off<16>(kst_a + 1024, src);
+      dma16_off<32>(kst_a + 2048, src);
+      dma16_off<48>(kst_a + 3072, src);
+      dma16_off<128>(kst_a + 4096, src);
+      dma16_off<144>(kst_a + 5120, src);
+      dma16_off<160>(kst_a + 6144, src);
+      dma16_off<176>(kst_a + 7168, src);
     } else {
-      const uint8_t* src = page_of(kp ? p.y : p.x) + I2_K_OFF + kt * 32;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dma16(kst_a + 1024 * j, src + (j >> 1) * 64 + (j & 1) * 16);
+      const uint8_t* src = lane_page(p, kp) + I2_K_OFF + kt * 32;
+      dma16_off<0>(kst_a, src);
+      dma16_off<16>(kst_a + 1024, src);
+      dma16_off<64>(kst_a + 2048, src);
+      dma16_off<80>(kst_a + 3072, src);
     }
   }
   __device__ void issue_v(int2 p) const {
@@ -928,67 +1052,79 @@ struct Dot8Wave {
   }
 };
 
-// Biased 16-bit key operands of head ah, channels ac0 .. ac0 + NCH - 1 (ai in [-30583, 30583]) to aval.
-template <int GQ, int NCH>
-__device__ __forceinline__ void store_key_operands(uint16_t* aval, int ah, int ac0, const int (&ai)[NCH]) {
-  uint32_t pk[NCH / 2];
-#pragma unroll
-  for (int i = 0; i < NCH / 2; ++i) pk[i] = (uint32_t)(ai[2 * i] + kBias8) | ((uint32_t)(ai[2 * i + 1] + kBias8) << 16);
+// Packed biased 16-bit key operands of head ah, channels ac0 .. ac0 + 2 NW - 1 (word i: channel pair 2i, 2i + 1)
+// to aval.
+template <int NW>
+__device__ __forceinline__ void store_key_operands(uint16_t* aval, int ah, int ac0, const uint32_t (&pk)[NW]) {
   uint32_t* dst = reinterpret_cast<uint32_t*>(aval + ah * D + ac0);
-  if constexpr (NCH >= 4) {
+  if constexpr (NW >= 2) {
 #pragma unroll
-    for (int i = 0; i < NCH / 2; i += 2) *reinterpret_cast<uint2*>(dst + i) = make_uint2(pk[i], pk[i + 1]);
+    for (int i = 0; i < NW; i += 2) *reinterpret_cast<uint2*>(dst + i) = make_uint2(pk[i], pk[i + 1]);
   } else {
     dst[0] = pk[0];
   }
 }
 
+// Low halves of two magic-rounded encodings as one word: lo16(e0) | lo16(e1) << 16.
+__device__ __forceinline__ uint32_t pack_lo16(float e0, float e1) {
+  return __builtin_amdgcn_perm(__float_as_uint(e1), __float_as_uint(e0), 0x05040100u);
+}
+
 // Key digit words from the biased operands: lane task (head, m, X or Y) reads the 16 channels of word m.
+// X takes digits 0 and 2 (low nibble of each byte), Y digits 1 and 3 (high nibble); the task's choice is a
+// shift amount, so that the wave does not diverge.
 template <int GQ>
 __device__ __forceinline__ void build_key_digits(uint32_t* adig, const uint16_t* aval, int lane) {
 #pragma unroll
   for (int u = lane; u < 16 * GQ; u += 64) {
-    const int hh = u >> 4, mw = (u >> 1) & 7, isy = u & 1;
+    const int hh = u >> 4, mw = (u >> 1) & 7;
+    const uint32_t sl = (u & 1) * 4, sh = 4 - sl;
     const uint4* src = reinterpret_cast<const uint4*>(aval + hh * D + 16 * mw);
     const uint4 d0 = src[0], d1 = src[1];  // channel pairs (16 mw + 2 i, + 1), i = 0..7
     const uint32_t dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
     uint32_t z[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) z[j] = (isy ? nib_y(dd[2 * j], dd[2 * j + 1]) : nib_x(dd[2 * j], dd[2 * j + 1])) ^ 0x88888888u;
-    reinterpret_cast<uint4*>(adig)[(hh * 8 + mw) * 2 + isy] = byte_transpose(z[0], z[1], z[2], z[3]);
+    for (int j = 0; j < 4; ++j)
+      z[j] = (((dd[2 * j] >> sl) & 0x0F0F0F0Fu) | ((dd[2 * j + 1] << sh) & 0xF0F0F0F0u)) ^ 0x88888888u;
+    reinterpret_cast<uint4*>(adig)[(hh * 8 + mw) * 2 + (u & 1)] = byte_transpose(z[0], z[1], z[2], z[3]);
   }
 }
 
-// One 32-bit code word (nibble vectors nb[0], nb[1]) against the digit words X, Y of one head.
+// One 32-bit code word (nibble vectors nb[0], nb[1]) against the digit words X, Y of one head; signed
+// (key side) or unsigned (value side) 4-bit products.
+template <bool SIGNED>
 __device__ __forceinline__ void dot8_word(int (&r)[4], uint4 X, uint4 Y, const uint32_t (&nb)[2], bool first) {
+  auto d = [](uint32_t x, uint32_t y, int c) { return SIGNED ? sdot8(x, y, c) : udot8(x, y, c); };
+  auto dz = [](uint32_t x, uint32_t y) { return SIGNED ? sdot8_z(x, y) : udot8_z(x, y); };
   if (first) {
-    r[0] = sdot8_z(X.x, nb[0]);
-    r[2] = sdot8_z(X.y, nb[0]);
-    r[1] = sdot8_z(Y.x, nb[0]);
-    r[3] = sdot8_z(Y.y, nb[0]);
+    r[0] = dz(X.x, nb[0]);
+    r[2] = dz(X.y, nb[0]);
+    r[1] = dz(Y.x, nb[0]);
+    r[3] = dz(Y.y, nb[0]);
   } else {
-    r[0] = sdot8(X.x, nb[0], r[0]);
-    r[2] = sdot8(X.y, nb[0], r[2]);
-    r[1] = sdot8(Y.x, nb[0], r[1]);
-    r[3] = sdot8(Y.y, nb[0], r[3]);
+    r[0] = d(X.x, nb[0], r[0]);
+    r[2] = d(X.y, nb[0], r[2]);
+    r[1] = d(Y.x, nb[0], r[1]);
+    r[3] = d(Y.y, nb[0], r[3]);
   }
-  r[0] = sdot8(X.z, nb[1], r[0]);
-  r[2] = sdot8(X.w, nb[1], r[2]);
-  r[1] = sdot8(Y.z, nb[1], r[1]);
-  r[3] = sdot8(Y.w, nb[1], r[3]);
+  r[0] = d(X.z, nb[1], r[0]);
+  r[2] = d(X.w, nb[1], r[2]);
+  r[1] = d(Y.z, nb[1], r[1]);
+  r[3] = d(Y.w, nb[1], r[3]);
 }
 
-__device__ __forceinline__ int digits_value(const int (&r)[4]) { return ((r[3] * 16 + r[2]) * 16 + r[1]) * 16 + r[0]; }
+__device__ __forceinline__ int digits_value(const int (&r)[4]) { return shl4_add(shl4_add(shl4_add(r[3], r[2]), r[1]), r[0]); }
 
 // Nibble vectors of code word pair idx: nb[0] holds the codes that pair with the X.x / X.y / Y.x / Y.y digit
 // words, nb[1] those of X.z / X.w / Y.z / Y.w.  2-bit codes: word idx, even then odd code positions
-// (values 0..3); 4-bit codes: words 2 idx and 2 idx + 1, less 8 (values -8..7, the offset is taken out of
-// the zero points).
-template <int BITS, int N>
+// (values 0..3); 4-bit codes: words 2 idx and 2 idx + 1, as they are (values 0..15, unsigned products), or
+// less 8 (values -8..7, signed products; the offset is taken out of the zero points).
+template <int BITS, bool SIGNED, int N>
 __device__ __forceinline__ void code_nibbles(uint32_t (&nb)[2], const uint32_t (&w)[N], int idx) {
   if constexpr (BITS == 4) {
-    nb[0] = w[2 * idx] ^ 0x88888888u;
-    nb[1] = w[2 * idx + 1] ^ 0x88888888u;
+    const uint32_t f = SIGNED ? 0x88888888u : 0u;
+    nb[0] = w[2 * idx] ^ f;
+    nb[1] = w[2 * idx + 1] ^ f;
   } else {
     nb[0] = w[idx] & 0x33333333u;
     nb[1] = (w[idx] >> 2) & 0x33333333u;
@@ -1005,7 +1141,7 @@ __device__ __forceinline__ void key_dots(const uint32_t* adig, const uint32_t (&
   for (int mw = 0; mw < 8; ++mw) {
     uint32_t nb[2][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) code_nibbles<BITS>(nb[t], kw[t], mw);
+    for (int t = 0; t < 2; ++t) code_nibbles<BITS, true>(nb[t], kw[t], mw);
 #pragma unroll
     for (int hh = 0; hh < GQ; ++hh) {
       const uint4 X = wx, Y = wy;
@@ -1016,12 +1152,13 @@ __device__ __forceinline__ void key_dots(const uint32_t* adig, const uint32_t (&
         wy = aword((nh * 8 + nm) * 2 + 1);
       }
 #pragma unroll
-      for (int t = 0; t < 2; ++t) dot8_word(acc[t][hh], X, Y, nb[t], mw == 0);
+      for (int t = 0; t < 2; ++t) dot8_word<true>(acc[t][hh], X, Y, nb[t], mw == 0);
     }
   }
 }
 
-// accv[c][head] = digit sums of channels lane, lane + 64 (code words vw[c][page]) against the weights.
+// accv[c][head] = digit sums of channels lane, lane + 64 (code words vw[c][page]) against the unsigned
+// weight digits.
 template <int GQ, int BITS>
 __device__ __forceinline__ void value_dots(const uint8_t* pdig, const uint32_t (&vw)[2][2][2 * BITS],
                                            int (&accv)[2][GQ][4]) {
@@ -1031,7 +1168,7 @@ __device__ __forceinline__ void value_dots(const uint8_t* pdig, const uint32_t (
   for (int pg = 0; pg < 8; ++pg) {  // pg = page * 4 + g
     uint32_t nb[2][2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) code_nibbles<BITS>(nb[c], vw[c][pg >> 2], pg & 3);
+    for (int c = 0; c < 2; ++c) code_nibbles<BITS, false>(nb[c], vw[c][pg >> 2], pg & 3);
 #pragma unroll
     for (int hh = 0; hh < GQ; ++hh) {
       const uint4 X = px, Y = py;
@@ -1042,15 +1179,16 @@ __device__ __forceinline__ void value_dots(const uint8_t* pdig, const uint32_t (
         py = pword((nh * 8 + npg) * 2 + 1);
       }
 #pragma unroll
-      for (int c = 0; c < 2; ++c) dot8_word(accv[c][hh], X, Y, nb[c], pg == 0);
+      for (int c = 0; c < 2; ++c) dot8_word<false>(accv[c][hh], X, Y, nb[c], pg == 0);
     }
   }
 }
 
-// Weight digits of the lane's tokens kt, kt + 2 (biased weights u0, u1) for one head: byte kj of the
-// words (page kp, g, n = kt & 1, digit 0..3).  pw = pdig + head * 256 + ((kp 4 + g) 8 + n 2) 4 + kj.
+// Weight digits of the lane's tokens kt, kt + 2 (unsigned 16-bit weights in the low halves of u0, u1) for
+// one head: byte kj of the words (page kp, g, n = kt & 1, digit 0..3).
+// pw = pdig + head * 256 + ((kp 4 + g) 8 + n 2) 4 + kj.
 __device__ __forceinline__ void store_weight_digits(uint8_t* pw, uint32_t u0, uint32_t u1) {
-  const uint32_t x = nib_x(u0, u1) ^ 0x8888u, y = nib_y(u0, u1) ^ 0x8888u;
+  const uint32_t x = nib_x(u0, u1), y = nib_y(u0, u1);
   pw[0] = (uint8_t)x;          // n d0
   pw[4] = (uint8_t)(x >> 8);   // n d2
   pw[16] = (uint8_t)y;         // n d1
@@ -1073,7 +1211,7 @@ __device__ void int2_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T,
   const int ah = lane >> (6 - LG);           // head of this lane in the alpha step
   const int ac0 = (lane & (LPH - 1)) * NCH;  // its first channel
   Dot8Wave<GQ, BITS> W(L, a, h, wave, lane);
-  constexpr float ZOFF = BITS == 4 ? 8.0f : 0.0f;  // 4-bit codes enter the dot products less 8
+  constexpr float ZOFF = BITS == 4 ? 8.0f : 0.0f;  // 4-bit key codes enter the dot products less 8
   // weight digit bytes of this lane's tokens: word (page kp, g, n) byte j of each head
   uint8_t* pw = W.pdig + ((W.kp * 4 + ((lane >> 1) & 3)) * 8 + (lane & 1) * 2) * 4 + ((lane >> 3) & 3);
   float qa[NCH];
@@ -1121,24 +1259,28 @@ __device__ void int2_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T,
     float A[GQ], AZ[GQ];
     {
       float al[NCH];
-      float amx = 0.0f;
+      int amx_i = 0;  // max |alpha| as its bit pattern (non-negative floats order as their bits)
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
         const uint32_t w = skw[i >> 1];
         al[i] = qa[i] * __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
-        amx = fmaxf(amx, fabsf(al[i]));
+        amx_i = max(amx_i, __float_as_int(fabsf(al[i])));
       }
-      amx = seg_reduce<LPH>(amx, OpMax());
-      const float inv = amx > 0.0f ? kScale8 / amx : 0.0f;
-      int ai[NCH];
+      const float amx = __int_as_float(seg_max_i<LPH>(amx_i));
+      // a = rint(alpha * inv) in [-30583, 30583] (the reciprocal's 1-ulp error cannot carry the largest past
+      // 30583.5); below 2^-100 the coefficients are taken as zero (their logit terms are below fp32's reach)
+      const float inv = amx > 0x1p-100f ? kScale8 * __builtin_amdgcn_rcpf(amx) : 0.0f;
+      uint32_t pk[NCH / 2];
       float zs = 0.0f;
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        ai[i] = (int)rintf(al[i] * inv);
+      for (int i = 0; i < NCH; i += 2) {
+        const float e0 = fmaf(al[i], inv, kRoundA), e1 = fmaf(al[i + 1], inv, kRoundA);
         const uint32_t w = zkw[i >> 1];
-        zs = fmaf((float)ai[i], __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16)) - ZOFF, zs);
+        zs = fmaf(e0 - kRoundA, __uint_as_float(w << 16) - ZOFF, zs);
+        zs = fmaf(e1 - kRoundA, __uint_as_float(w & 0xffff0000u) - ZOFF, zs);
+        pk[i >> 1] = pack_lo16(e0, e1);  // a + 0x8888 of both channels
       }
-      zs = seg_reduce<LPH>(zs, OpAdd());
+      zs = seg_sum<LPH>(zs);
       const float Ah = amx * (1.0f / kScale8);
       const float AZh = Ah * zs;
 #pragma unroll
@@ -1146,7 +1288,7 @@ __device__ void int2_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T,
         A[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Ah), hh * LPH));
         AZ[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(AZh), hh * LPH));
       }
-      store_key_operands<GQ, NCH>(W.aval, ah, ac0, ai);
+      store_key_operands<NCH / 2>(W.aval, ah, ac0, pk);
     }
     wave_lds_sync();
     // 2. key digit words
@@ -1174,29 +1316,37 @@ __device__ void int2_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T,
     int acc[2][GQ][4];
     key_dots<GQ, BITS>(W.adig, kw, acc);
 
-    // 4. logits, group max, 16-bit weights as nibble digits in LDS
-    float lg[2][GQ], mg[GQ], Pf[GQ];
+    // 4. logits logit_t = A val_t - AZ; their group maximum is that of the integer sums val_t (A >= 0);
+    //    weights p_t = 2^(A (val_t - val_max)) <= 1 as unsigned 16-bit nibble digits in LDS
+    float mg[GQ], Pf[GQ];
     {
-      float mx[GQ];
+      float vf[2][GQ];
+      int mx[GQ], vmax[GQ];
 #pragma unroll
       for (int hh = 0; hh < GQ; ++hh) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) lg[t][hh] = fmaf(A[hh], (float)digits_value(acc[t][hh]), -AZ[hh]);
-        mx[hh] = fmaxf(lg[0][hh], lg[1][hh]);
+        const int v0 = digits_value(acc[0][hh]), v1 = digits_value(acc[1][hh]);
+        vf[0][hh] = (float)v0;
+        vf[1][hh] = (float)v1;
+        mx[hh] = max(v0, v1);
       }
-      heads_allreduce<GQ>(mx, OpMax(), lane, mg);
-    }
-    {
+      heads_allreduce_fast<GQ>(mx, [](int x, int y) { return max(x, y); }, [](int x) { return seg_max_i<(64 >> LG)>(x); },
+                               lane, vmax);
       float ps[GQ];
 #pragma unroll
       for (int hh = 0; hh < GQ; ++hh) {
-        // biased weights u + 0x8888, u = floor(kScale8 p + 0.5) in [0, kScale8]
-        const uint32_t u0 = (uint32_t)fmaf(__builtin_amdgcn_exp2f(lg[0][hh] - mg[hh]), kScale8, 0.5f + kBias8);
-        const uint32_t u1 = (uint32_t)fmaf(__builtin_amdgcn_exp2f(lg[1][hh] - mg[hh]), kScale8, 0.5f + kBias8);
-        ps[hh] = (float)(int)(u0 + u1 - 2 * kBias8);
+        const float vm = (float)vmax[hh];
+        mg[hh] = fmaf(A[hh], vm, -AZ[hh]);
+        const float ref = A[hh] * vm;
+        // u = rint(65535 p) in [0, 65535], in the low half of the magic-rounded encoding (p exceeds 1 by at
+        // most the rounding of ref, far below half a unit of u)
+        const uint32_t u0 = __float_as_uint(fmaf(__builtin_amdgcn_exp2f(fmaf(A[hh], vf[0][hh], -ref)), kScaleW, kRoundW));
+        const uint32_t u1 = __float_as_uint(fmaf(__builtin_amdgcn_exp2f(fmaf(A[hh], vf[1][hh], -ref)), kScaleW, kRoundW));
+        ps[hh] = (float)(int)(u0 + u1 - 2 * kRoundWBits);
         store_weight_digits(pw + hh * 256, u0, u1);
       }
-      heads_allreduce<GQ>(ps, OpAdd(), lane, Pf);  // integers below 2^24: exact in fp32
+      // integers below 2^24: exact in fp32
+      heads_allreduce_fast<GQ>(ps, [](float x, float y) { return x + y; }, [](float x) { return seg_sum<(64 >> LG)>(x); },
+                               lane, Pf);
     }
     wave_lds_sync();
 
@@ -1222,20 +1372,30 @@ __device__ void int2_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T,
     int accv[2][GQ][4];
     value_dots<GQ, BITS>(W.pdig, vw, accv);
 
-    // 6. online-softmax update in the rotated value frame
+    // 6. online-softmax update in the rotated value frame; o and l carry the weights' factor 65535 (both
+    //    are divided by it after the walk), and are rescaled in place so that they keep their registers
 #pragma unroll
     for (int hh = 0; hh < GQ; ++hh) {
-      const float mnew = fmaxf(m[hh], mg[hh]);
-      const float sc = exp2_safe_diff(m[hh], mnew);
-      const float wg = __builtin_amdgcn_exp2f(mg[hh] - mnew) * (1.0f / kScale8);
-      const float U0 = (float)digits_value(accv[0][hh]);
-      const float U1 = (float)digits_value(accv[1][hh]);
-      o[hh][0] = fmaf(o[hh][0], sc, (wg * sv0) * fmaf(ZOFF - zv0, Pf[hh], U0));
-      o[hh][1] = fmaf(o[hh][1], sc, (wg * sv1) * fmaf(ZOFF - zv1, Pf[hh], U1));
-      l[hh] = fmaf(l[hh], sc, wg * Pf[hh]);
+      const float mnew = fmax_raw(m[hh], mg[hh]);          // finite: every group's logits are
+      const float sc = __builtin_amdgcn_exp2f(m[hh] - mnew);  // 0 before the first group (m = -inf)
+      const float eg = __builtin_amdgcn_exp2f(mg[hh] - mnew);
+      const float Y0 = fmaf(-zv0, Pf[hh], (float)digits_value(accv[0][hh]));
+      const float Y1 = fmaf(-zv1, Pf[hh], (float)digits_value(accv[1][hh]));
+      o[hh][0] *= sc;
+      o[hh][0] = fmaf(eg * sv0, Y0, o[hh][0]);
+      o[hh][1] *= sc;
+      o[hh][1] = fmaf(eg * sv1, Y1, o[hh][1]);
+      l[hh] *= sc;
+      l[hh] = fmaf(eg, Pf[hh], l[hh]);
       m[hh] = mnew;
     }
     wave_lds_sync();
+  }
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh) {
+    o[hh][0] *= 1.0f / kScaleW;
+    o[hh][1] *= 1.0f / kScaleW;
+    l[hh] *= 1.0f / kScaleW;
   }
   combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, c0, c1);
 }
@@ -1247,8 +1407,8 @@ __device__ void int2_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T,
 // so the key-side operand is the rotated query itself, rounded once per work-group to 16 bits,
 // a_c = rint(30583 q~_c / max|q~|), A = max|q~| / 30583: logit_t = A s_t (sum_c a_c code_tc - z_t sum_c a_c),
 // and its digit words are built once before the walk.  Values: the group adds
-//   sum_t p_t s'_t (code'_tc - z'_t) = (S' / 30583) (sum_t u_t code'_tc - sum_t u_t z'_t)
-// to the output, with the weights p_t s'_t rounded to u_t = rint(30583 p_t s'_t / S'), S' the group's
+//   sum_t p_t s'_t (code'_tc - z'_t) = (S' / 65535) (sum_t u_t code'_tc - sum_t u_t z'_t)
+// to the output, with the weights p_t s'_t rounded to u_t = rint(65535 p_t s'_t / S'), S' the group's
 // largest value scale (p_t <= 1 relative to the group's largest logit), and sum_t p_t to the softmax sum.
 // Lane roles, digit words and the copy pipeline as in int2_unit_dot8; the metadata of a page holds its
 // tokens' K scales, K zeros, V scales, V zeros (64 bf16 each).
@@ -1283,22 +1443,23 @@ __device__ void int2tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
 #pragma unroll
     for (int i = 0; i < NCH; ++i) amx = fmaxf(amx, fabsf(qa[i]));
     amx = seg_reduce<LPH>(amx, OpMax());
-    const float inv = amx > 0.0f ? kScale8 / amx : 0.0f;
-    int ai[NCH];
-    int isum = 0;
+    const float inv = amx > 0x1p-100f ? kScale8 * __builtin_amdgcn_rcpf(amx) : 0.0f;
+    uint32_t pk[NCH / 2];
+    float fsum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      ai[i] = (int)rintf(qa[i] * inv);
-      isum += ai[i];
+    for (int i = 0; i < NCH; i += 2) {
+      const float e0 = fmaf(qa[i], inv, kRoundA), e1 = fmaf(qa[i + 1], inv, kRoundA);
+      fsum += (e0 - kRoundA) + (e1 - kRoundA);  // integers: exact
+      pk[i >> 1] = pack_lo16(e0, e1);
     }
-    const float fs = seg_reduce<LPH>((float)isum, OpAdd());
+    const float fs = seg_reduce<LPH>(fsum, OpAdd());
     const float Ah = amx * (1.0f / kScale8);
 #pragma unroll
     for (int hh = 0; hh < GQ; ++hh) {
       A[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Ah), hh * LPH));
       FS[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fs), hh * LPH));
     }
-    store_key_operands<GQ, NCH>(W.aval, ah, ac0, ai);
+    store_key_operands<NCH / 2>(W.aval, ah, ac0, pk);
     wave_lds_sync();
     build_key_digits<GQ>(W.adig, W.aval, lane);
     wave_lds_sync();
@@ -1365,10 +1526,10 @@ __device__ void int2tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
 #pragma unroll
       for (int hh = 0; hh < GQ; ++hh) {
         const float p0 = __builtin_amdgcn_exp2f(lg[0][hh] - mg[hh]), p1 = __builtin_amdgcn_exp2f(lg[1][hh] - mg[hh]);
-        const uint32_t u0 = (uint32_t)fmaf(p0 * w0, kScale8, 0.5f + kBias8);
-        const uint32_t u1 = (uint32_t)fmaf(p1 * w1, kScale8, 0.5f + kBias8);
+        const float e0 = fmaf(p0 * w0, kScaleW, kRoundW), e1 = fmaf(p1 * w1, kScaleW, kRoundW);
+        const uint32_t u0 = __float_as_uint(e0), u1 = __float_as_uint(e1);
         ps[hh] = p0 + p1;
-        zs[hh] = fmaf((float)(int)(u0 - kBias8), zvt[0], (float)(int)(u1 - kBias8) * zvt[1]);
+        zs[hh] = fmaf(e0 - kRoundW, zvt[0], (e1 - kRoundW) * zvt[1]);
         store_weight_digits(pw + hh * 256, u0, u1);
       }
       heads_allreduce<GQ>(ps, OpAdd(), lane, Pl);
@@ -1391,9 +1552,9 @@ __device__ void int2tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
 #pragma unroll
     for (int hh = 0; hh < GQ; ++hh) {
       const float mnew = fmaxf(m[hh], mg[hh]);
-      const float sc = exp2_safe_diff(m[hh], mnew);
+      const float sc = __builtin_amdgcn_exp2f(m[hh] - mnew);  // 0 before the first group (m = -inf)
       const float eg = __builtin_amdgcn_exp2f(mg[hh] - mnew);
-      const float wg = eg * smax * (1.0f / kScale8);
+      const float wg = eg * smax * (1.0f / kScaleW);
       o[hh][0] = fmaf(o[hh][0], sc, wg * ((float)digits_value(accv[0][hh]) - Zs[hh]));
       o[hh][1] = fmaf(o[hh][1], sc, wg * ((float)digits_value(accv[1][hh]) - Zs[hh]));
       l[hh] = fmaf(l[hh], sc, eg * Pl[hh]);
