@@ -314,6 +314,11 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
   const int per = chunk_units(cfg, cache->batch, max_seq_len_host);
   a.g.gpc = per;
   a.g.n_units = 1 + max_chunks_of(cfg, max_seq_len_host, per);
+  // an explicit split on the nibble-digit path: one chunk per wave (a work-group takes four), so that every
+  // wave walks several groups with its copies in flight, with one partial per chunk as with any split
+  const bool dot8 = cfg->decode_impl == KVQ_DECODE_DOT8 ||
+                    (cfg->decode_impl == KVQ_DECODE_AUTO && is_grouped(cfg->scheme));
+  a.g.wave_chunks = (cfg->split_tokens > 0 && is_grouped(cfg->scheme) && dot8) ? 1 : 0;
   a.pages = static_cast<const uint8_t*>(cache->pages);
   a.band = static_cast<const uint16_t*>(cache->band);
   a.page_table = cache->page_table;

@@ -200,6 +200,23 @@ __device__ void combine_and_store(Lds& L, const DecodeArgs& a, int b, int h, int
   }
 }
 
+// Partial of one wave's own chunk (wave chunks): no combination with the other waves of the work-group.
+template <int GQ>
+__device__ void store_wave_partial(const DecodeArgs& a, int b, int h, int unit, int lane, const float (&m)[GQ],
+                                   const float (&l)[GQ], const float (&o)[GQ][2], int c0, int c1) {
+  const Geo& g = a.g;
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh) {
+    float* part = a.partials + (((long long)b * g.n_q + h * GQ + hh) * g.n_units + unit) * PART_STRIDE;
+    part[2 + c0] = o[hh][0];
+    part[2 + c1] = o[hh][1];
+    if (lane == 0) {
+      part[0] = m[hh];
+      part[1] = l[hh];
+    }
+  }
+}
+
 template <int GQ>
 __device__ inline void softmax_update(float (&m)[GQ], float (&l)[GQ], float (&o)[GQ][2], int hh, float mx_tile,
                                       float& mnew_out) {
@@ -1204,9 +1221,14 @@ __device__ void int2_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ng = n_groups_of(T, g.S0, g.W);
-  const int g_begin = chunk * g.gpc;
+  // the wave's groups: its own chunk, walked in order (wave chunks), or every fourth group of the work-group's
+  const bool wc = g.wave_chunks != 0;
+  const int chunk_id = wc ? 4 * chunk + wave : chunk;
+  const int g_begin = chunk_id * g.gpc;
   int g_end = (g_begin + g.gpc) < ng ? (g_begin + g.gpc) : ng;
   if (g_end > g.max_pages / 2) g_end = g.max_pages / 2;  // never index past the page-table row
+  const int gstep = wc ? 1 : 4;
+  const int g_first = wc ? g_begin : g_begin + wave;
   const int c0 = lane, c1 = lane + 64;
   const int ah = lane >> (6 - LG);           // head of this lane in the alpha step
   const int ac0 = (lane & (LPH - 1)) * NCH;  // its first channel
@@ -1233,15 +1255,15 @@ __device__ void int2_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T,
   }
   const int2* pt = reinterpret_cast<const int2*>(a.page_table + (long long)b * g.max_pages);
   int2 pnext = make_int2(0, 0);
-  if (g_begin + wave < g_end) {
-    const int2 p0 = scalar_load_int2(pt + g_begin + wave);
+  if (g_first < g_end) {
+    const int2 p0 = scalar_load_int2(pt + g_first);
     W.issue_m(p0);
     W.issue_k(p0);
     W.issue_v(p0);
   }
-  for (int gi = g_begin + wave; gi < g_end; gi += 4) {
-    const bool has_next = gi + 4 < g_end;  // uniform
-    if (has_next) pnext = scalar_load_int2(pt + gi + 4);
+  for (int gi = g_first; gi < g_end; gi += gstep) {
+    const bool has_next = gi + gstep < g_end;  // uniform
+    if (has_next) pnext = scalar_load_int2(pt + gi + gstep);
     if constexpr (BITS == 4) KVQ_WAIT_VM(16);  // this group's M copy (its K and V copies may still be in flight)
     else KVQ_WAIT_VM(8);
     uint32_t skw[NCH / 2], zkw[NCH / 2];
@@ -1397,7 +1419,12 @@ __device__ void int2_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T,
     o[hh][1] *= 1.0f / kScaleW;
     l[hh] *= 1.0f / kScaleW;
   }
-  combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, c0, c1);
+  if (wc) {
+    // every partial a merge reads is written; chunks past the length or the launch bound have none
+    if (g_begin < ng && chunk_id < g.n_units - 1) store_wave_partial<GQ>(a, b, h, 1 + chunk_id, lane, m, l, o, c0, c1);
+  } else {
+    combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, c0, c1);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1422,9 +1449,14 @@ __device__ void int2tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ng = n_groups_of(T, g.S0, g.W);
-  const int g_begin = chunk * g.gpc;
+  // the wave's groups: its own chunk, walked in order (wave chunks), or every fourth group of the work-group's
+  const bool wc = g.wave_chunks != 0;
+  const int chunk_id = wc ? 4 * chunk + wave : chunk;
+  const int g_begin = chunk_id * g.gpc;
   int g_end = (g_begin + g.gpc) < ng ? (g_begin + g.gpc) : ng;
   if (g_end > g.max_pages / 2) g_end = g.max_pages / 2;  // never index past the page-table row
+  const int gstep = wc ? 1 : 4;
+  const int g_first = wc ? g_begin : g_begin + wave;
   const int c0 = lane, c1 = lane + 64;
   const int ah = lane >> (6 - LG);
   const int ac0 = (lane & (LPH - 1)) * NCH;
@@ -1473,15 +1505,15 @@ __device__ void int2tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
   }
   const int2* pt = reinterpret_cast<const int2*>(a.page_table + (long long)b * g.max_pages);
   int2 pnext = make_int2(0, 0);
-  if (g_begin + wave < g_end) {
-    const int2 p0 = scalar_load_int2(pt + g_begin + wave);
+  if (g_first < g_end) {
+    const int2 p0 = scalar_load_int2(pt + g_first);
     W.issue_m(p0);
     W.issue_k(p0);
     W.issue_v(p0);
   }
-  for (int gi = g_begin + wave; gi < g_end; gi += 4) {
-    const bool has_next = gi + 4 < g_end;  // uniform
-    if (has_next) pnext = scalar_load_int2(pt + gi + 4);
+  for (int gi = g_first; gi < g_end; gi += gstep) {
+    const bool has_next = gi + gstep < g_end;  // uniform
+    if (has_next) pnext = scalar_load_int2(pt + gi + gstep);
     KVQ_WAIT_VM(8);  // this group's M copy
     float sk[2], zk[2], svt[2], zvt[2];  // tokens kt, kt + 2
 #pragma unroll
@@ -1562,7 +1594,12 @@ __device__ void int2tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
     }
     wave_lds_sync();
   }
-  combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, c0, c1);
+  if (wc) {
+    // every partial a merge reads is written; chunks past the length or the launch bound have none
+    if (g_begin < ng && chunk_id < g.n_units - 1) store_wave_partial<GQ>(a, b, h, 1 + chunk_id, lane, m, l, o, c0, c1);
+  } else {
+    combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, c0, c1);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1897,7 +1934,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     n_chunks = ((T + PAGE - 1) / PAGE + g.gpc - 1) / g.gpc;
   }
   if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;  // lengths beyond the launch bound are cut
-  if (unit > n_chunks) return;
+  if (unit > (g.wave_chunks ? (n_chunks + 3) / 4 : n_chunks)) return;
   if (unit == 0) {
     if constexpr (grouped) {
       band_unit<GQ>(L, a, b, h, T);
@@ -2091,7 +2128,8 @@ hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
   const Geo& g = a.g;
   if (stages & KVQ_STAGE_QPREP) hipLaunchKernelGGL(qprep_kernel<GQ>, dim3(g.n_kv, g.batch), dim3(512), 0, s, a);
   if (stages & KVQ_STAGE_SPLITK) {
-    const dim3 grid(g.n_units, g.n_kv, g.batch), block(kThreads);
+    // wave chunks: four chunks per work-group
+    const dim3 grid(g.wave_chunks ? 1 + (g.n_units - 1 + 3) / 4 : g.n_units, g.n_kv, g.batch), block(kThreads);
     // AUTO: 16-bit operands on the nibble dot product for INT2, the fp32 kernel for INT4 (faster there:
     // per-token scales leave the fp32 path no per-group work, and 4-bit codes convert cheaply)
     if (g.scheme == KVQ_INT4_CHANNEL) {

@@ -52,6 +52,7 @@ struct Geo {
   long long page_bytes;
   int gpc;          // groups (grouped schemes) or pages (INT4 per token) per decode chunk
   int n_units;      // decode partial units per (seq, q head): 1 band unit + chunks
+  int wave_chunks;  // 1: each wave of a work-group walks a chunk of its own and stores its partial
 };
 
 // both INT2 schemes share the page layout; they and per-channel INT4 share the band and the group demotion

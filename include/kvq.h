@@ -140,7 +140,10 @@ typedef struct {
   int32_t n_recent;      /* W >= 0 (INT2 schemes; 0 for INT4) */
   float clip_k;          /* rho_K in (0, 1]; 1 = no clip (INT2 only) */
   float clip_v;          /* rho_V in (0, 1] */
-  int32_t split_tokens;  /* quantized tokens per decode work-group: multiple of 128, or 0 = chosen by size */
+  int32_t split_tokens;  /* quantized tokens per decode chunk, each merged from one partial: a multiple of 128
+                            (grouped schemes) or 64 (INT4_TOKEN), or 0 = chosen by size (one work-group per
+                            chunk).  Given explicitly on the nibble-digit decode, each wave of a work-group
+                            walks a chunk of its own and a work-group takes four. */
   int32_t decode_impl;   /* kvq_decode_impl */
   int32_t key_only_rotation;  /* 0: K and V rotated (V by R_V on write, outputs un-rotated by R_V^T);
                                  1: only K rotated ([SAW] App. C default), V kept in its own frame and

@@ -122,17 +122,21 @@ def test_long_context_gq8_small(K, impl):
     check_out(bc, out, q, [(b, h) for b in range(2) for h in range(8)])
 
 
-def test_split_size_does_not_change_the_result(K):
-    wl = synth.WORKLOADS["gqa_b1_32k"]
+@pytest.mark.parametrize("scheme", ["int2_channel", "int4_channel"])
+def test_split_size_does_not_change_the_result(K, scheme):
+    """The automatic split (one work-group per chunk) and explicit splits (one wave per chunk, four chunks
+    per work-group, the last work-group partly empty) give the same output up to the order of the merge."""
+    wl = synth.scaled(synth.WORKLOADS["gqa_b1_32k"], scheme=scheme)
     lens = [4000, 1234]
-    _say("split invariance")
+    _say(f"split invariance ({scheme})")
     outs = []
     q = synth.queries(synth.scaled(wl, batch=2))
-    for split in (128, 512, 2048):
+    for split in (0, 128, 256, 512, 2048):
         bc = build_cache(K, wl, lens, split_tokens=split)
         outs.append(run_decode(K, bc, q))
-    assert np.abs(outs[0] - outs[1]).max() < 1e-5
-    assert np.abs(outs[0] - outs[2]).max() < 1e-5
+    for o in outs[1:]:
+        assert np.abs(outs[0] - o).max() < 1e-5
+    check_out(bc, outs[-1], q, [(b, h) for b in range(2) for h in range(8)])
 
 
 def test_saw_int4_small(K):
