@@ -391,23 +391,30 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
   }
 }
 
-// bf16 band writes: sink tokens and tokens that are still in the tail after the append.
+// bf16 band writes: sink tokens and tokens that are still in the tail after the append.  ADVANCE (one
+// new token at most per sequence, so one work-group per sequence reads its length): the work-group also
+// advances that length once all its threads have read it.
+template <bool ADVANCE>
 __global__ __launch_bounds__(256) void band_write_kernel(WriteArgs a) {
   const Geo& g = a.g;
   const int r = blockIdx.x, b = blockIdx.y;
   const int T0 = a.seq_lens[b];
   const int c0 = a.cu_new[b];
   const int n_new = a.cu_new[b + 1] - c0;
-  if (r >= n_new) return;
   const int t = T0 + r;
   const int ng1 = n_groups_of(T0 + n_new, g.S0, g.W);
-  if (!(t < g.S0 || t >= g.S0 + GROUP * ng1)) return;
-  const long long slot = band_slot_of(t, g.S0, g.W);
-  for (int e = threadIdx.x; e < g.n_kv * 256; e += 256) {
-    const int h = e >> 8, kv = (e >> 7) & 1, c = e & (D - 1);
-    const long long idx = ((long long)(c0 + r) * g.n_kv + h) * D + c;
-    a.band[(((long long)b * g.n_kv + h) * g.slots + slot) * 256 + kv * 128 + c] =
-        src_as_bf16_bits(kv ? a.v : a.k, a.src_bf16, idx);
+  if (r < n_new && (t < g.S0 || t >= g.S0 + GROUP * ng1)) {
+    const long long slot = band_slot_of(t, g.S0, g.W);
+    for (int e = threadIdx.x; e < g.n_kv * 256; e += 256) {
+      const int h = e >> 8, kv = (e >> 7) & 1, c = e & (D - 1);
+      const long long idx = ((long long)(c0 + r) * g.n_kv + h) * D + c;
+      a.band[(((long long)b * g.n_kv + h) * g.slots + slot) * 256 + kv * 128 + c] =
+          src_as_bf16_bits(kv ? a.v : a.k, a.src_bf16, idx);
+    }
+  }
+  if constexpr (ADVANCE) {
+    __syncthreads();
+    if (threadIdx.x == 0) a.seq_lens[b] = T0 + n_new;
   }
 }
 
@@ -531,12 +538,17 @@ hipError_t launch_write_int2(const WriteArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int max_groups = (a.max_new + GROUP - 1) / GROUP + 1;
-  if (a.max_new > 0) {
-    hipLaunchKernelGGL(int2_group_kernel, dim3(max_groups, a.g.n_kv * 2, a.g.batch), dim3(256), kGroupLds, s, a);
-    hipLaunchKernelGGL(band_write_kernel, dim3(a.max_new, a.g.batch), dim3(256), 0, s, a);
+  // n new tokens complete at most n / 128 + 1 groups of a sequence
+  const int max_groups = a.max_new / GROUP + 1;
+  if (a.max_new == 0) return hipSuccess;  // nothing appended: the lengths stay
+  hipLaunchKernelGGL(int2_group_kernel, dim3(max_groups, a.g.n_kv * 2, a.g.batch), dim3(256), kGroupLds, s, a);
+  if (a.max_new == 1) {
+    // the decode step's append: the band write advances the lengths itself
+    hipLaunchKernelGGL(band_write_kernel<true>, dim3(1, a.g.batch), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(band_write_kernel<false>, dim3(a.max_new, a.g.batch), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(advance_kernel, dim3(1), dim3(256), 0, s, a.seq_lens, a.cu_new, a.g.batch);
   }
-  hipLaunchKernelGGL(advance_kernel, dim3(1), dim3(256), 0, s, a.seq_lens, a.cu_new, a.g.batch);
   return hipGetLastError();
 }
 
