@@ -232,7 +232,8 @@ __device__ inline void softmax_update(float (&m)[GQ], float (&l)[GQ], float (&o)
 template <int GQ, typename Lds>
 __device__ void band_unit(Lds& L, const DecodeArgs& a, int b, int h, int T) {
   const Geo& g = a.g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the value rows' slots are scalar
   for (int e = tid; e < GQ * D; e += kThreads)
     L.f.qband[e / D][e % D] = a.qband[((long long)b * g.n_q + h * GQ + e / D) * D + e % D];
   __syncthreads();
@@ -288,16 +289,25 @@ __device__ void band_unit(Lds& L, const DecodeArgs& a, int b, int h, int T) {
     }
     wave_lds_sync();
     const int nk = (nb - blk * 64) < 64 ? (nb - blk * 64) : 64;
-    // value rows 8 tokens at a time, their loads issued together (channels 2 lane, 2 lane + 1)
-    for (int k8 = 0; k8 < nk; k8 += 8) {
-      uint32_t vv[8];
+    // value rows (channels 2 lane, 2 lane + 1) 16 tokens at a time, the next 16 in flight while these are
+    // summed, so that the block costs about one memory latency rather than one per batch
+    constexpr int VB = 16;
+    auto load_rows = [&](int k0, uint32_t (&dst)[VB]) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int kk = k8 + q < nk ? k8 + q : nk - 1;
-        vv[q] = *reinterpret_cast<const uint32_t*>(band + (long long)slot_of(blk * 64 + kk) * 256 + 128 + 2 * lane);
+      for (int q = 0; q < VB; ++q) {
+        const int kk = k0 + q < nk ? k0 + q : nk - 1;
+        dst[q] = *reinterpret_cast<const uint32_t*>(band + (long long)slot_of(blk * 64 + kk) * 256 + 128 + 2 * lane);
       }
+    };
+    uint32_t vn[VB];
+    load_rows(0, vn);
+    for (int k8 = 0; k8 < nk; k8 += VB) {
+      uint32_t vv[VB];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < VB; ++q) vv[q] = vn[q];
+      if (k8 + VB < nk) load_rows(k8 + VB, vn);
+#pragma unroll
+      for (int q = 0; q < VB; ++q) {
         if (k8 + q >= nk) break;
         const float v0 = __uint_as_float(vv[q] << 16), v1 = __uint_as_float(vv[q] & 0xffff0000u);
 #pragma unroll
