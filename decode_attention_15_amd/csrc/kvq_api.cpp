@@ -32,7 +32,9 @@ int check_config(const kvq_config* c) {
       c->decode_impl != KVQ_DECODE_DOT16 && c->decode_impl != KVQ_DECODE_DOT8)
     return KVQ_EINVAL;
   if (c->decode_impl == KVQ_DECODE_MFMA) return KVQ_EUNSUPPORTED;
-  if (c->decode_impl == KVQ_DECODE_DOT8 && !is_grouped(c->scheme)) return KVQ_EUNSUPPORTED;
+  // nibble digits for INT4 per token walk page pairs: an explicit split must hold whole pairs
+  if (c->decode_impl == KVQ_DECODE_DOT8 && c->scheme == KVQ_INT4_TOKEN && c->split_tokens % (2 * PAGE) != 0)
+    return KVQ_EUNSUPPORTED;
   // per-token INT2 and per-channel INT4 are built on the nibble dot product only
   if ((c->scheme == KVQ_INT2_TOKEN || c->scheme == KVQ_INT4_CHANNEL) && c->decode_impl != KVQ_DECODE_AUTO &&
       c->decode_impl != KVQ_DECODE_DOT8)
@@ -314,11 +316,13 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
   const int per = chunk_units(cfg, cache->batch, max_seq_len_host);
   a.g.gpc = per;
   a.g.n_units = 1 + max_chunks_of(cfg, max_seq_len_host, per);
+  // the nibble-digit decode: every grouped scheme by default; INT4 per token by default when its chunks
+  // hold whole page pairs
+  const bool dot8 = cfg->decode_impl == KVQ_DECODE_DOT8 ||
+                    (cfg->decode_impl == KVQ_DECODE_AUTO && (is_grouped(cfg->scheme) || per % 2 == 0));
   // an explicit split on the nibble-digit path: one chunk per wave (a work-group takes four), so that every
   // wave walks several groups with its copies in flight, with one partial per chunk as with any split
-  const bool dot8 = cfg->decode_impl == KVQ_DECODE_DOT8 ||
-                    (cfg->decode_impl == KVQ_DECODE_AUTO && is_grouped(cfg->scheme));
-  a.g.wave_chunks = (cfg->split_tokens > 0 && is_grouped(cfg->scheme) && dot8) ? 1 : 0;
+  a.g.wave_chunks = (cfg->split_tokens > 0 && dot8) ? 1 : 0;
   a.pages = static_cast<const uint8_t*>(cache->pages);
   a.band = static_cast<const uint16_t*>(cache->band);
   a.page_table = cache->page_table;
@@ -333,7 +337,7 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
   a.qrot = ws;
   a.qband = ws + nq * D;
   a.partials = ws + 2 * nq * D;
-  a.impl = cfg->decode_impl;
+  a.impl = dot8 ? KVQ_DECODE_DOT8 : cfg->decode_impl;
   clear_stale_error();
   return to_status(launch_decode(a, stages, stream), "kv_decode_attn");
 }

@@ -478,6 +478,9 @@ __device__ inline int2 scalar_load_int2(const int2* p) {
   const __attribute__((address_space(4))) int* q = (const __attribute__((address_space(4))) int*)(uintptr_t)p;
   return make_int2(q[0], q[1]);
 }
+__device__ inline int scalar_load_int(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int*)(uintptr_t)p;
+}
 
 // Signed 4-way byte dot product with a zero accumulator (VOP3P form: no register to clear first).
 __device__ inline int sdot4_z(uint32_t a, uint32_t b) {
@@ -1613,6 +1616,319 @@ __device__ void int2tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
 }
 
 // ---------------------------------------------------------------------------------------------
+// INT4 token-wise chunk ([SAW] App. A.1 eq. (3)-(4), App. A.4 eq. (13)) on the nibble dot product, with
+// the per-token INT2 unit's algebra: the key-side operand is the rotated query, rounded once per
+// work-group to a_c (16-bit, four signed digits), and
+//   logit_t = A s_t (sum_c a_c (code_tc - 8) + (8 - z_t) sum_c a_c)
+// (4-bit key codes enter the signed products less 8); values: the weights p_t s'_t / S' as unsigned
+// 16-bit digits against the codes as they are.  The page layout is the INT4 one as written: a key code
+// word holds 8 consecutive channels (word m, nibble k = channel 8m + k), so the key digit words are built
+// for that order (word (m, d): nibble k = digit d of a_{8m+k}); a value code word of a channel holds
+// tokens 16(2jh + jl) + 4g + r at nibble 4jl + r (word 2g + jh), so a lane owns the two tokens of one byte,
+// t0 = 16j + 4g + 2h and t0 + 1 (j, g, h from lane bits 3-4, 1-2, 0; page = lane bit 5).  Pages are walked
+// in pairs (128 tokens, two pages as the grouped schemes' groups); tokens past the length are masked by
+// selects, and a missing second page of the last pair is replaced by the first (read, never used).
+// ---------------------------------------------------------------------------------------------
+// Key digit words for 8-consecutive-channel code words: task (head, m) reads channels 8m .. 8m + 7.
+template <int GQ>
+__device__ __forceinline__ void build_key_digits_seq(uint32_t* adig, const uint16_t* aval, int lane) {
+#pragma unroll
+  for (int u = lane; u < 16 * GQ; u += 64) {
+    const int hh = u >> 4, m = u & 15;
+    const uint4 v = *reinterpret_cast<const uint4*>(aval + hh * D + 8 * m);  // channel pairs (8m + 2i, + 1)
+    const uint32_t pr[4] = {v.x, v.y, v.z, v.w};
+    uint32_t w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t by[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t t = (pr[i] >> (4 * d)) & 0x000F000Fu;  // digit d of both channels of the pair
+        by[i] = (t | (t >> 12)) & 0xFFu;                      // low nibble channel 8m + 2i, high 8m + 2i + 1
+      }
+      w[d] = (by[0] | (by[1] << 8) | (by[2] << 16) | (by[3] << 24)) ^ 0x88888888u;
+    }
+    reinterpret_cast<uint4*>(adig)[hh * 16 + m] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// acc[t][head][d] = digit-d sums of tokens t0, t0 + 1 (16 code words each) against the key digit words.
+template <int GQ>
+__device__ __forceinline__ void key_dots_seq(const uint32_t* adig, const uint32_t (&kw)[2][16], int (&acc)[2][GQ][4]) {
+  auto aword = [&](int idx) { return reinterpret_cast<const uint4*>(adig)[idx]; };  // idx = hh 16 + m
+  uint4 nxt = aword(0);
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const uint32_t nb[2] = {kw[0][m] ^ 0x88888888u, kw[1][m] ^ 0x88888888u};
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      const uint4 X = nxt;
+      const int k = hh * 16 + m;  // the next word read: (head + 1, m), or (0, m + 1)
+      const int kn = hh + 1 < GQ ? k + 16 : m + 1;
+      if (hh + 1 < GQ || m + 1 < 16) nxt = aword(kn);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if (m == 0) {
+          acc[t][hh][0] = sdot8_z(X.x, nb[t]);
+          acc[t][hh][1] = sdot8_z(X.y, nb[t]);
+          acc[t][hh][2] = sdot8_z(X.z, nb[t]);
+          acc[t][hh][3] = sdot8_z(X.w, nb[t]);
+        } else {
+          acc[t][hh][0] = sdot8(X.x, nb[t], acc[t][hh][0]);
+          acc[t][hh][1] = sdot8(X.y, nb[t], acc[t][hh][1]);
+          acc[t][hh][2] = sdot8(X.z, nb[t], acc[t][hh][2]);
+          acc[t][hh][3] = sdot8(X.w, nb[t], acc[t][hh][3]);
+        }
+      }
+    }
+  }
+}
+
+// accv[c][head][d] = digit-d sums of channels lane, lane + 64 (8 code words per page) against the weights;
+// weight digit words [head][page][word][d].
+template <int GQ>
+__device__ __forceinline__ void value_dots_seq(const uint8_t* pdig, const uint32_t (&vw)[2][2][8], int (&accv)[2][GQ][4]) {
+  auto pword = [&](int idx) { return reinterpret_cast<const uint4*>(pdig)[idx]; };  // idx = (hh 2 + pg) 8 + W
+  uint4 nxt = pword(0);
+#pragma unroll
+  for (int pw = 0; pw < 16; ++pw) {  // pw = page * 8 + word
+    const uint32_t nb[2] = {vw[0][pw >> 3][pw & 7], vw[1][pw >> 3][pw & 7]};
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      const uint4 X = nxt;
+      const int kn = hh + 1 < GQ ? (hh + 1) * 16 + pw : pw + 1;
+      if (hh + 1 < GQ || pw + 1 < 16) nxt = pword(kn);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        if (pw == 0) {
+          accv[c][hh][0] = udot8_z(X.x, nb[c]);
+          accv[c][hh][1] = udot8_z(X.y, nb[c]);
+          accv[c][hh][2] = udot8_z(X.z, nb[c]);
+          accv[c][hh][3] = udot8_z(X.w, nb[c]);
+        } else {
+          accv[c][hh][0] = udot8(X.x, nb[c], accv[c][hh][0]);
+          accv[c][hh][1] = udot8(X.y, nb[c], accv[c][hh][1]);
+          accv[c][hh][2] = udot8(X.z, nb[c], accv[c][hh][2]);
+          accv[c][hh][3] = udot8(X.w, nb[c], accv[c][hh][3]);
+        }
+      }
+    }
+  }
+}
+
+template <int GQ, typename Lds>
+__device__ void int4tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
+  constexpr int LG = HeadLog2<GQ>::v;
+  constexpr int LPH = 64 >> LG;
+  constexpr int NCH = 2 * GQ;
+  const Geo& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int npages = (T + PAGE - 1) / PAGE;
+  const int npairs = (npages + 1) / 2;
+  // the wave's page pairs: its own chunk (wave chunks) or every fourth pair of the work-group's chunk
+  const bool wc = g.wave_chunks != 0;
+  const int chunk_id = wc ? 4 * chunk + wave : chunk;
+  const int pb = chunk_id * g.gpc / 2;  // chunks hold an even number of pages
+  int pe = pb + g.gpc / 2 < npairs ? pb + g.gpc / 2 : npairs;
+  if (2 * pe > g.max_pages + 1) pe = (g.max_pages + 1) / 2;  // never index past the page-table row
+  const int pstep = wc ? 1 : 4;
+  const int p_first = wc ? pb : pb + wave;
+  const int c0 = lane, c1 = lane + 64;
+  const int ah = lane >> (6 - LG);
+  const int ac0 = (lane & (LPH - 1)) * NCH;
+  Dot8Wave<GQ, 4> W(L, a, h, wave, lane);
+  const int kp = lane >> 5;
+  const int jj = (lane >> 3) & 3, gg = (lane >> 1) & 3, hb = lane & 1;
+  const int t0 = 16 * jj + 4 * gg + 2 * hb;  // this lane's tokens t0, t0 + 1 of page kp
+  // weight digit bytes of this lane's token pair: word (head, page kp, 2 gg + jj / 2, d), byte 2 (jj & 1) + hb
+  uint8_t* pw = W.pdig + (kp * 8 + 2 * gg + (jj >> 1)) * 16 + 2 * (jj & 1) + hb;
+  const uint16_t* mk = W.mst + ((kp * 2 + 0) * 64 + t0) * 2;  // K (s, z) of token t0; + 2 for t0 + 1
+  const uint16_t* mv = W.mst + ((kp * 2 + 1) * 64 + t0) * 2;
+
+  auto issue_m = [&](int2 p) {
+    dma16(W.mst_a, W.lane_page(p, lane >= 32) + ((lane & 16) ? I4_VMETA_OFF : I4_KMETA_OFF) + (lane & 15) * 16);
+  };
+  auto issue_k = [&](int2 p) {
+    const uint8_t* src = W.lane_page(p, kp) + I4_K_OFF + t0 * 64;  // tokens t0, t0 + 1: 128 contiguous bytes
+    dma16_off<0>(W.kst_a, src);
+    dma16_off<16>(W.kst_a + 1024, src);
+    dma16_off<32>(W.kst_a + 2048, src);
+    dma16_off<48>(W.kst_a + 3072, src);
+    dma16_off<64>(W.kst_a + 4096, src);
+    dma16_off<80>(W.kst_a + 5120, src);
+    dma16_off<96>(W.kst_a + 6144, src);
+    dma16_off<112>(W.kst_a + 7168, src);
+  };
+  // pages of pair i; the second is the first again when the sequence ends in the first
+  const int32_t* ptr = a.page_table + (long long)b * g.max_pages;
+  // (scalar loads: a vector load here would enter the counter the copy pipeline's waits count)
+  auto pages_of = [&](int i) {
+    const int x = scalar_load_int(ptr + 2 * i);
+    const int y = 2 * i + 1 < npages ? scalar_load_int(ptr + 2 * i + 1) : x;
+    return make_int2(x, y);
+  };
+
+  // 0. the key-side operand, once
+  float A[GQ], FS[GQ];
+  {
+    float qa[NCH];
+    const float* q = a.qrot + ((long long)b * g.n_q + h * GQ + ah) * D + ac0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) qa[i] = q[i];
+    int amx_i = 0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) amx_i = max(amx_i, __float_as_int(fabsf(qa[i])));
+    const float amx = __int_as_float(seg_max_i<LPH>(amx_i));
+    const float inv = amx > 0x1p-100f ? kScale8 * __builtin_amdgcn_rcpf(amx) : 0.0f;
+    uint32_t pk[NCH / 2];
+    float fsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCH; i += 2) {
+      const float e0 = fmaf(qa[i], inv, kRoundA), e1 = fmaf(qa[i + 1], inv, kRoundA);
+      fsum += (e0 - kRoundA) + (e1 - kRoundA);  // integers: exact
+      pk[i >> 1] = pack_lo16(e0, e1);
+    }
+    const float fs = seg_sum<LPH>(fsum);
+    const float Ah = amx * (1.0f / kScale8);
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      A[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Ah), hh * LPH));
+      FS[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fs), hh * LPH));
+    }
+    store_key_operands<NCH / 2>(W.aval, ah, ac0, pk);
+    wave_lds_sync();
+    build_key_digits_seq<GQ>(W.adig, W.aval, lane);
+    wave_lds_sync();
+  }
+  float m[GQ], l[GQ], o[GQ][2];
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.0f;
+    o[hh][0] = o[hh][1] = 0.0f;
+  }
+  int2 pnext = make_int2(0, 0);
+  if (p_first < pe) {
+    const int2 p0 = pages_of(p_first);
+    issue_m(p0);
+    issue_k(p0);
+    W.issue_v(p0);
+  }
+  for (int pi = p_first; pi < pe; pi += pstep) {
+    const bool has_next = pi + pstep < pe;  // uniform
+    if (has_next) pnext = pages_of(pi + pstep);
+    KVQ_WAIT_VM(16);  // this pair's M copy
+    const int tok = pi * 128 + kp * 64 + t0;
+    const bool v0 = tok < T, v1 = tok + 1 < T;
+    float sk[2], zk[2], svt[2], zvt[2];
+    sk[0] = bf16_to_f32(mk[0]);
+    zk[0] = bf16_to_f32(mk[1]);
+    sk[1] = bf16_to_f32(mk[2]);
+    zk[1] = bf16_to_f32(mk[3]);
+    svt[0] = bf16_to_f32(mv[0]);
+    zvt[0] = bf16_to_f32(mv[1]);
+    svt[1] = bf16_to_f32(mv[2]);
+    zvt[1] = bf16_to_f32(mv[3]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (has_next) issue_m(pnext);
+    // tokens past the length: no weight, no value scale or zero (their metadata may be anything)
+    svt[0] = v0 ? svt[0] : 0.0f;
+    zvt[0] = v0 ? zvt[0] : 0.0f;
+    svt[1] = v1 ? svt[1] : 0.0f;
+    zvt[1] = v1 ? zvt[1] : 0.0f;
+
+    // 1. key dots
+    if (has_next) KVQ_WAIT_VM(9);
+    else KVQ_WAIT_VM(8);
+    uint32_t kw[2][16];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint4 kk = W.kst[64 * j + c0];
+      uint32_t* dst = &kw[j >> 2][4 * (j & 3)];
+      dst[0] = kk.x, dst[1] = kk.y, dst[2] = kk.z, dst[3] = kk.w;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (has_next) issue_k(pnext);
+    int acc[2][GQ][4];
+    key_dots_seq<GQ>(W.adig, kw, acc);
+
+    // 2. logits, pair max, weights p_t s'_t / S' as unsigned digits, sum_t p_t and sum_t u_t z'_t
+    float lg[2][GQ], mg[GQ], Pl[GQ], Zs[GQ];
+    {
+      float mx[GQ];
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const float x = (A[hh] * sk[t]) * fmaf(8.0f - zk[t], FS[hh], (float)digits_value(acc[t][hh]));
+          lg[t][hh] = (t == 0 ? v0 : v1) ? x : -INFINITY;
+        }
+        mx[hh] = fmaxf(lg[0][hh], lg[1][hh]);
+      }
+      heads_allreduce<GQ>(mx, OpMax(), lane, mg);
+    }
+    const float smax = __int_as_float(seg_max_i<64>(max(__float_as_int(svt[0]), __float_as_int(svt[1]))));  // S' (uniform)
+    const float sinv = smax > 0.0f ? 1.0f / smax : 0.0f;
+    {
+      float ps[GQ], zs[GQ];
+      const float w0 = svt[0] * sinv, w1 = svt[1] * sinv;  // in [0, 1]
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+        const float p0 = __builtin_amdgcn_exp2f(lg[0][hh] - mg[hh]), p1 = __builtin_amdgcn_exp2f(lg[1][hh] - mg[hh]);
+        const float e0 = fmaf(p0 * w0, kScaleW, kRoundW), e1 = fmaf(p1 * w1, kScaleW, kRoundW);
+        const uint32_t u0 = __float_as_uint(e0), u1 = __float_as_uint(e1);
+        ps[hh] = p0 + p1;
+        zs[hh] = fmaf(e0 - kRoundW, zvt[0], (e1 - kRoundW) * zvt[1]);
+        const uint32_t x = nib_x(u0, u1), y = nib_y(u0, u1);
+        uint8_t* q = pw + hh * 256;
+        q[0] = (uint8_t)x;         // d0
+        q[4] = (uint8_t)y;         // d1
+        q[8] = (uint8_t)(x >> 8);  // d2
+        q[12] = (uint8_t)(y >> 8); // d3
+      }
+      heads_allreduce<GQ>(ps, OpAdd(), lane, Pl);
+      heads_allreduce<GQ>(zs, OpAdd(), lane, Zs);
+    }
+    wave_lds_sync();
+
+    // 3. value dots
+    if (has_next) KVQ_WAIT_VM(9);
+    else KVQ_WAIT_VM(0);
+    uint32_t vw[2][2][8];  // [channel c0 | c1][page][word]
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint4 vv = W.vst[64 * j + c0];
+      uint32_t* dst = &vw[(j >> 1) & 1][j >> 2][4 * (j & 1)];
+      dst[0] = vv.x, dst[1] = vv.y, dst[2] = vv.z, dst[3] = vv.w;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (has_next) W.issue_v(pnext);
+    int accv[2][GQ][4];
+    value_dots_seq<GQ>(W.pdig, vw, accv);
+
+    // 4. online-softmax update in the rotated value frame
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      const float mnew = fmax_raw(m[hh], mg[hh]);
+      const float sc = __builtin_amdgcn_exp2f(m[hh] - mnew);  // 0 before the first pair (m = -inf)
+      const float eg = __builtin_amdgcn_exp2f(mg[hh] - mnew);
+      const float wg = eg * smax * (1.0f / kScaleW);
+      o[hh][0] = fmaf(o[hh][0], sc, wg * ((float)digits_value(accv[0][hh]) - Zs[hh]));
+      o[hh][1] = fmaf(o[hh][1], sc, wg * ((float)digits_value(accv[1][hh]) - Zs[hh]));
+      l[hh] = fmaf(l[hh], sc, eg * Pl[hh]);
+      m[hh] = mnew;
+    }
+    wave_lds_sync();
+  }
+  if (wc) {
+    if (pb < npairs && chunk_id < g.n_units - 1) store_wave_partial<GQ>(a, b, h, 1 + chunk_id, lane, m, l, o, c0, c1);
+  } else {
+    combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, c0, c1);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // INT4 token-wise page walk, 16-bit fixed point on v_dot4 ([SAW] App. A.1 eq. (3)-(4), App. A.4 eq. (13)):
 //   logit_t = s_t (sum_c q~_c code_tc - z_t sum_c q~_c): the key-side operand is the rotated query
 //   itself, rounded once per work-group to a_c = rint(q~_c 32639 / max|q~|) (A = max|q~| / 32639),
@@ -1931,7 +2247,7 @@ __device__ void int4_unit(Lds& L, const DecodeArgs& a, int b, int h, int T, int 
 // MODE: 0 fp32, 1 16-bit on the byte dot product, 2 16-bit on the nibble dot product (grouped schemes)
 template <int GQ, int SCHEME, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
-  __shared__ DecodeLds<GQ, SCHEME == KVQ_INT4_CHANNEL ? 2 : 1> L;
+  __shared__ DecodeLds<GQ, (SCHEME == KVQ_INT4_CHANNEL || (SCHEME == KVQ_INT4_TOKEN && MODE == 2)) ? 2 : 1> L;
   const int unit = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const Geo& g = a.g;
   const int T = a.seq_lens[b];
@@ -1965,7 +2281,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     else if constexpr (MODE == 1) int2_unit_dot16<GQ>(L, a, b, h, T, unit - 1);
     else int2_unit<GQ>(L, a, b, h, T, unit - 1);
   } else {
-    if constexpr (MODE == 1) int4_unit_dot16<GQ>(L, a, b, h, T, unit - 1);
+    if constexpr (MODE == 2) int4tok_unit_dot8<GQ>(L, a, b, h, T, unit - 1);
+    else if constexpr (MODE == 1) int4_unit_dot16<GQ>(L, a, b, h, T, unit - 1);
     else int4_unit<GQ>(L, a, b, h, T, unit - 1);
   }
 }
@@ -2151,7 +2468,9 @@ hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
       else if (a.impl == KVQ_DECODE_DOT16) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 1>), grid, block, 0, s, a);
       else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 2>), grid, block, 0, s, a);
     } else {
-      if (a.impl == KVQ_DECODE_DOT16) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_TOKEN, 1>), grid, block, 0, s, a);
+      // the API resolves AUTO for INT4 per token (nibble digits when the chunks hold whole page pairs)
+      if (a.impl == KVQ_DECODE_DOT8) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_TOKEN, 2>), grid, block, 0, s, a);
+      else if (a.impl == KVQ_DECODE_DOT16) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_TOKEN, 1>), grid, block, 0, s, a);
       else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_TOKEN, 0>), grid, block, 0, s, a);
     }
   }

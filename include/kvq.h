@@ -114,10 +114,12 @@ typedef enum { KVQ_ROT_DENSE = 0, KVQ_ROT_HADAMARD = 1 } kvq_rotation;
    DOT16 - the key-side operand (INT2: alpha = q~ s per group and head; INT4: q~) and the softmax weights
            (per group or page and head) rounded to 16-bit integers scaled to their maximum, multiplied
            with the codes on the integer dot-product unit as two signed bytes;
-   DOT8  - INT2 only: the same 16-bit operands (full scale 30583) as four signed 4-bit digits on the 8-way
-           nibble dot product, which needs fewer operations to unpack the 2-bit codes (INT2_TOKEN:
-           the rotated query once per work-group, the weights p_t s_t per group);
-   MFMA  - reserved, not built;  AUTO - DOT8 for INT2 and INT4_CHANNEL, F32 for INT4_TOKEN (the fastest of each).
+   DOT8  - the key-side operand as a 16-bit integer (full scale 30583) in four signed 4-bit digits and the
+           softmax weights (times the value scales for per-token schemes) as unsigned 16-bit integers (full
+           scale 65535) in four 4-bit digits, on the 8-way nibble dot product; 2-bit codes unpack with a
+           mask, 4-bit codes not at all (per-token schemes: the rotated query once per work-group).  INT4
+           per token walks page pairs, so an explicit split_tokens must be a multiple of 128;
+   MFMA  - reserved, not built;  AUTO - DOT8 (INT4_TOKEN with a split of an odd number of pages: F32).
    INT2_TOKEN and INT4_CHANNEL are built with DOT8 only (F32 and DOT16 return KVQ_EUNSUPPORTED for them). */
 typedef enum {
   KVQ_DECODE_AUTO = 0,

@@ -139,11 +139,18 @@ def test_split_size_does_not_change_the_result(K, scheme):
     check_out(bc, outs[-1], q, [(b, h) for b in range(2) for h in range(8)])
 
 
-def test_saw_int4_small(K):
+@pytest.mark.parametrize("impl,split", [("auto", 0), ("f32", 0), ("dot16", 0), ("dot8", 0), ("auto", 64),
+                                        ("dot8", 128), ("dot8", 256)])
+def test_saw_int4_small(K, impl, split):
+    """INT4 per token on every decode path: the automatic choice (nibble digits over page pairs; the fp32
+    path for a 64-token split, whose chunks hold half pairs), each implementation explicitly, and explicit
+    splits (one pair chunk per wave).  Lengths end inside a pair's second page, inside its first page
+    (the pair's second page missing), and on a page boundary."""
     wl = synth.WORKLOADS["saw_int4_b16_16k"]
-    lens = [1000, 333, 66]
-    _say(f"saw int4 small lens={lens}")
-    bc = build_cache(K, wl, lens, append_steps=7, chunk=256)
+    lens = [1000, 333, 66, 40, 128]
+    _say(f"saw int4 small lens={lens} impl={impl} split={split}")
+    code = {"f32": K.DECODE_F32, "dot16": K.DECODE_DOT16, "dot8": K.DECODE_DOT8}.get(impl, K.DECODE_AUTO)
+    bc = build_cache(K, wl, lens, append_steps=7, chunk=256, decode_impl=code, split_tokens=split)
     pages = bc.cache.pages.cpu().numpy()
     for b in range(len(lens)):
         for h in (0, 6):
@@ -156,10 +163,11 @@ def test_saw_int4_small(K):
 @pytest.mark.parametrize("impl", ["dot16", "dot8"])
 def test_integer_dot_decodes_agree_with_f32(K, impl):
     """The 16-bit integer-dot decodes (byte limbs, nibble digits) against the fp32 decode on the same cache:
-    one head with an fp32 source and x10 outlier channels (4096 tokens), GQA 4 and GQA 8 caches; both
-    within the oracle bar."""
+    one head with an fp32 source and x10 outlier channels (4096 tokens), GQA 4 and GQA 8 INT2 caches and
+    the INT4 per-token cache; both within the oracle bar."""
     code = {"dot16": K.DECODE_DOT16, "dot8": K.DECODE_DOT8}[impl]
-    for name, lens in (("tiny_1h_4k", [4096]), ("gqa_b1_32k", [2900, 1000]), ("long_b4_131k", [3000, 700])):
+    for name, lens in (("tiny_1h_4k", [4096]), ("gqa_b1_32k", [2900, 1000]), ("long_b4_131k", [3000, 700]),
+                       ("saw_int4_b16_16k", [1500, 300])):
         wl = synth.WORKLOADS[name]
         _say(f"{impl} vs f32: {name} lens={lens}")
         bc = build_cache(K, wl, lens)

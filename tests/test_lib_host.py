@@ -149,9 +149,14 @@ def test_decode_implementations_accepted_for_both_schemes():
         for impl in (K.DECODE_AUTO, K.DECODE_F32, K.DECODE_DOT16, K.DECODE_DOT8):
             cfg = K.make_config(8, 32, scheme=scheme, rotation=rot, n_sink=s0, n_recent=w, clip_k=ck, clip_v=cv,
                                 decode_impl=impl)
-            # the nibble-digit decode exists for INT2 only
-            want = K.KVQ_EUNSUPPORTED if (impl == K.DECODE_DOT8 and scheme == K.INT4_TOKEN) else K.KVQ_OK
-            assert K.check_config(cfg) == want
+            assert K.check_config(cfg) == K.KVQ_OK
+    # INT4 per token on the nibble digits walks page pairs: an explicit split must hold whole pairs
+    for split, want in ((64, K.KVQ_EUNSUPPORTED), (192, K.KVQ_EUNSUPPORTED), (128, K.KVQ_OK), (512, K.KVQ_OK)):
+        cfg = K.make_config(8, 32, scheme=K.INT4_TOKEN, rotation=K.ROT_HADAMARD, n_sink=0, n_recent=0, clip_k=1.0,
+                            clip_v=1.0, split_tokens=split, decode_impl=K.DECODE_DOT8)
+        assert K.check_config(cfg) == want
+        cfg.decode_impl = K.DECODE_AUTO  # the automatic choice takes the fp32 path there instead
+        assert K.check_config(cfg) == K.KVQ_OK
 
 
 def test_int2_token_scheme_config():
