@@ -63,19 +63,70 @@ __device__ inline uint32_t wave_select_u32(uint32_t u0, uint32_t u1, int j) {
   return prefix;
 }
 
+// Largest of 64 lanes' non-negative values (below 2^31), every lane: DPP-folded steps within rows, then
+// the row and half swaps.
+#define KVQ_UPDDPP(x, ctrl) __builtin_amdgcn_update_dpp(0, (x), (ctrl), 0xF, 0xF, true)
+__device__ inline int wave_max_i32(int x) {
+  x = max(x, KVQ_UPDDPP(x, 0xB1));   // quad_perm [1,0,3,2]
+  x = max(x, KVQ_UPDDPP(x, 0x4E));   // quad_perm [2,3,0,1]
+  x = max(x, KVQ_UPDDPP(x, 0x141));  // row_half_mirror
+  x = max(x, KVQ_UPDDPP(x, 0x140));  // row_mirror
+  const auto r16 = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  const uint32_t a16 = r16[0], b16 = r16[1];
+  x = max((int)a16, (int)b16);
+  const auto r32 = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  const uint32_t a32 = r32[0], b32 = r32[1];
+  return max((int)a32, (int)b32);
+}
+
+// y_j and y_{j+1} of the 128 non-negative floats (bit patterns, two per lane) for j near the top: the
+// distinct values are visited from the largest down, `above` counting the values greater than the
+// current one, until the current one is the (128 - j)-th largest; y_{j+1} is the same value when its
+// repeats reach past it, else the previously visited value.  At most 128 - j rounds, all wave-uniform.
+__device__ inline void wave_top_select_u32(uint32_t u0, uint32_t u1, int j, uint32_t& yj, uint32_t& yj1) {
+  const int k = D - j;
+  uint32_t cur = kFull, prev = kFull;
+  int above = 0;
+  for (;;) {
+    const uint32_t c0 = u0 < cur ? u0 : 0u, c1 = u1 < cur ? u1 : 0u;
+    const uint32_t m = (uint32_t)wave_max_i32((int)(c0 > c1 ? c0 : c1));
+    const int cnt = wave_count(u0 == m) + wave_count(u1 == m);
+    if (above + cnt >= k) {
+      yj = m;
+      yj1 = (k - 1 > above) ? m : prev;
+      return;
+    }
+    above += cnt;
+    prev = m;
+    cur = m;
+  }
+}
+
+// clip(x, -tau, tau) as two comparisons, each taking its second operand when the two compare equal, so
+// that a zero of either sign clipped at tau = 0 gives +0 as the cache format's definition does
+__device__ inline float clip_to(float x, float tau) {
+  const float y = x > -tau ? x : -tau;
+  return y < tau ? y : tau;
+}
+
 // Per-token clip threshold: linear-interpolation quantile of |x| at (j, f) ([OSCAR] §3.4.4 step 2).
 __device__ inline float clip_tau(float x0, float x1, int j, float f) {
   const uint32_t u0 = __float_as_uint(x0) & 0x7fffffffu;
   const uint32_t u1 = __float_as_uint(x1) & 0x7fffffffu;
-  const uint32_t yj = wave_select_u32(u0, u1, j);
-  if (j >= D - 1) return __uint_as_float(yj);
-  uint32_t yj1;
-  if (wave_count(u0 <= yj) + wave_count(u1 <= yj) >= j + 2) {
-    yj1 = yj;
+  uint32_t yj, yj1;
+  if (j >= D - 1) return __uint_as_float(wave_select_u32(u0, u1, j));
+  if (j >= D - 16) {
+    // near the top (clip ratios from about 0.88): a few rounds over the largest values
+    wave_top_select_u32(u0, u1, j, yj, yj1);
   } else {
-    const uint32_t m0 = u0 > yj ? u0 : kFull;
-    const uint32_t m1 = u1 > yj ? u1 : kFull;
-    yj1 = wave_min_u32(m0 < m1 ? m0 : m1);
+    yj = wave_select_u32(u0, u1, j);
+    if (wave_count(u0 <= yj) + wave_count(u1 <= yj) >= j + 2) {
+      yj1 = yj;
+    } else {
+      const uint32_t m0 = u0 > yj ? u0 : kFull;
+      const uint32_t m1 = u1 > yj ? u1 : kFull;
+      yj1 = wave_min_u32(m0 < m1 ? m0 : m1);
+    }
   }
   const float y0 = __uint_as_float(yj), y1 = __uint_as_float(yj1);
   return __fadd_rn(y0, __fmul_rn(f, __fsub_rn(y1, y0)));
@@ -133,39 +184,39 @@ __device__ inline void rotate_vec(const float* xs, const float* rot, int rotatio
 // the same bits as the sequential fp64 sum the cache format specifies (every product x_i R[i][j] is exact
 // in fp64).  Operand layout: lane l supplies A[row l % 16][k l / 16] and B[k l / 16][col l % 16]; the
 // result lands in lane l, register r at row l / 16 + 4 r, column l % 16.  Wave w computes tokens
-// [32w, 32w + 32) x all 128 columns: 2 x 8 tiles of 16 x 16, 32 steps of k = 4.
-__device__ inline void rotate_group_mfma(const float* xs, const float* rot, float* xr, int wave, int lane) {
+// [32w, 32w + 32) x all 128 columns in one pass (2 x 8 tiles of 16 x 16, 32 steps of k = 4), and since a
+// token's rotated row depends on its own input row only, which no other wave reads, it writes the
+// results over its input rows.
+__device__ inline void rotate_group_mfma(float* xs, const float* rot, int wave, int lane) {
   typedef double d4 __attribute__((ext_vector_type(4)));
   const int li = lane & 15, lk = lane >> 4;
   const int t0 = wave * 32;
-#pragma unroll 1
-  for (int half = 0; half < 2; ++half) {       // columns [64 half, 64 half + 64): 4 column tiles
-    d4 acc[2][4];
+  d4 acc[2][8];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) acc[rt][ct] = d4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 2
+  for (int s = 0; s < D / 4; ++s) {
+    const int kk = 4 * s + lk;
+    double av[2], bv[8];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) av[rt] = (double)xs[(t0 + 16 * rt + li) * XS_STRIDE + kk];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) bv[ct] = (double)rot[kk * D + 16 * ct + li];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = d4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-    for (int s = 0; s < D / 4; ++s) {
-      const int kk = 4 * s + lk;
-      double av[2], bv[4];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) av[rt] = (double)xs[(t0 + 16 * rt + li) * XS_STRIDE + kk];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) bv[ct] = (double)rot[kk * D + 64 * half + 16 * ct + li];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[rt], bv[ct], acc[rt][ct], 0, 0, 0);
-    }
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          xr[(t0 + 16 * rt + lk + 4 * r) * D + 64 * half + 16 * ct + li] = (float)acc[rt][ct][r];
+      for (int ct = 0; ct < 8; ++ct) acc[rt][ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[rt], bv[ct], acc[rt][ct], 0, 0, 0);
   }
+  // every read of these rows was consumed by the matrix cores above (a wave's LDS accesses stay in order)
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        xs[(t0 + 16 * rt + lk + 4 * r) * XS_STRIDE + 16 * ct + li] = (float)acc[rt][ct][r];
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -174,12 +225,12 @@ __device__ inline void rotate_group_mfma(const float* xs, const float* rot, floa
 // channel over the group (KVQ_INT2_CHANNEL, KVQ_INT4_CHANNEL) or per token over its channels
 // (KVQ_INT2_TOKEN) -> bf16 scale/zero -> codes -> K token-major rows / V channel-major rows + metadata.
 // ---------------------------------------------------------------------------------------------
-constexpr int kGroupLds = (GROUP * XS_STRIDE + GROUP * D) * (int)sizeof(float);
+constexpr int kGroupLds = GROUP * XS_STRIDE * (int)sizeof(float);  // two work-groups per CU
 
-__global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void int2_group_kernel(WriteArgs a) {
   extern __shared__ float lds[];
-  float* xs = lds;                       // [128 tokens][XS_STRIDE] inputs (bf16 values)
-  float* xr = lds + GROUP * XS_STRIDE;   // [128 tokens][128] rotated, then clipped
+  float* xs = lds;  // [128 tokens][XS_STRIDE] inputs (bf16 values), rotated and clipped in place
+  float* xr = xs;   // the same rows once rotated
   __shared__ float red_min[2][D], red_max[2][D];
   __shared__ float s_sp[D], s_zp[D];  // per channel, or per token of the group
 
@@ -227,15 +278,15 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
   const long long hoff = (long long)h * g.head_bytes;
   const int moff = four ? I4C_META_OFF : I2_META_OFF;
   if (which == 1 && g.key_only) {
-    for (int e = tid; e < GROUP * D; e += 256) xr[e] = xs[(e >> 7) * XS_STRIDE + (e & (D - 1))];
+    // the values themselves
   } else if (g.rotation == KVQ_ROT_DENSE) {
-    rotate_group_mfma(xs, rot, xr, wave, lane);
+    rotate_group_mfma(xs, rot, wave, lane);
   } else {
     for (int tl = wave * 32; tl < wave * 32 + 32; ++tl) {
-      float y0, y1;
+      float y0, y1;  // each lane reads its own two inputs of the row before writing them
       rotate_vec(xs + tl * XS_STRIDE, rot, g.rotation, g.hblock, g.hscale, lane, y0, y1);
-      xr[tl * D + lane] = y0;
-      xr[tl * D + lane + 64] = y1;
+      xr[tl * XS_STRIDE + lane] = y0;
+      xr[tl * XS_STRIDE + lane + 64] = y1;
     }
   }
   __syncthreads();
@@ -245,10 +296,10 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
   const float cf = which ? a.clip_f_v : a.clip_f_k;
   if (cj < D - 1) {
     for (int tl = wave * 32; tl < wave * 32 + 32; ++tl) {
-      const float x0 = xr[tl * D + lane], x1 = xr[tl * D + lane + 64];
+      const float x0 = xr[tl * XS_STRIDE + lane], x1 = xr[tl * XS_STRIDE + lane + 64];
       const float tau = clip_tau(x0, x1, cj, cf);
-      xr[tl * D + lane] = fminf(fmaxf(x0, -tau), tau);
-      xr[tl * D + lane + 64] = fminf(fmaxf(x1, -tau), tau);
+      xr[tl * XS_STRIDE + lane] = clip_to(x0, tau);
+      xr[tl * XS_STRIDE + lane + 64] = clip_to(x1, tau);
     }
     __syncthreads();
   }
@@ -256,7 +307,7 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
   // 4. min/max per channel over the group (or per token over its channels), bf16 scale and zero
   if (tokenwise) {
     for (int tl = wave * 32; tl < wave * 32 + 32; ++tl) {
-      const float x0 = xr[tl * D + lane], x1 = xr[tl * D + lane + 64];
+      const float x0 = xr[tl * XS_STRIDE + lane], x1 = xr[tl * XS_STRIDE + lane + 64];
       const float amin = wave_min_f32(fminf(x0, x1));
       const float bmax = wave_max_f32(fmaxf(x0, x1));
       const float s = (bmax > amin) ? __fdiv_rn(__fsub_rn(bmax, amin), levels) : 1.0f;
@@ -277,7 +328,7 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
     const int c = tid & (D - 1), half = tid >> 7;
     float mn = INFINITY, mx = -INFINITY;
     for (int tl = half * 64; tl < half * 64 + 64; ++tl) {
-      const float x = xr[tl * D + c];
+      const float x = xr[tl * XS_STRIDE + c];
       mn = fminf(mn, x);
       mx = fmaxf(mx, x);
     }
@@ -313,7 +364,7 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
     const int tl = tid >> 1, half = tid & 1;
     const long long phys = a.page_table[(long long)b * g.max_pages + 2 * grp + (tl >> 6)];
     uint8_t* row = a.pages + phys * g.page_bytes + hoff + I2_K_OFF;
-    const float* x = xr + tl * D + half * 64;
+    const float* x = xr + tl * XS_STRIDE + half * 64;
     if (four) {
       // 64 bytes per token; channel block m (16m .. 16m + 15): word 2m nibble k = channel 16m + 2k,
       // word 2m + 1 nibble k = channel 16m + 2k + 1
@@ -349,7 +400,7 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
     // V, channel-major; thread (channel c, page ph of the group); token i = 16j + 4gg + r of the page
     const int c = tid & (D - 1), ph = tid >> 7;
     const long long phys = a.page_table[(long long)b * g.max_pages + 2 * grp + ph];
-    const float* x = xr + ph * 64 * D + c;
+    const float* x = xr + ph * 64 * XS_STRIDE + c;
     if (four) {
       // 32-byte rows: token 16j + 4gg + 2hh + n in word 2gg + n, nibble 2j + hh
       uint32_t w8[8];
@@ -363,7 +414,7 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
               const int i = 16 * j + 4 * gg + 2 * hh + n;
-              w |= code(x[i * D], c, ph * 64 + i) << (4 * (2 * j + hh));
+              w |= code(x[i * XS_STRIDE], c, ph * 64 + i) << (4 * (2 * j + hh));
             }
           w8[2 * gg + n] = w;
         }
@@ -381,7 +432,7 @@ __global__ __launch_bounds__(256) void int2_group_kernel(WriteArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 16 * j + 4 * gg + r;
-            w |= code(x[i * D], c, ph * 64 + i) << (8 * j + 2 * r);
+            w |= code(x[i * XS_STRIDE], c, ph * 64 + i) << (8 * j + 2 * r);
           }
         w4[gg] = w;
       }
@@ -521,8 +572,8 @@ __global__ __launch_bounds__(64) void debug_rotate_kernel(const float* rot, int 
   rotate_vec(xs, rot, rotation, hblock, hscale, lane, y0, y1);
   if (clip_j < D - 1) {
     const float tau = clip_tau(y0, y1, clip_j, clip_f);
-    y0 = fminf(fmaxf(y0, -tau), tau);
-    y1 = fminf(fmaxf(y1, -tau), tau);
+    y0 = clip_to(y0, tau);
+    y1 = clip_to(y1, tau);
   }
   out[(long long)v * D + lane] = y0;
   out[(long long)v * D + lane + 64] = y1;

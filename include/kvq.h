@@ -67,7 +67,9 @@
  *    for h' = 1..h/2 only (each block of h channels separately), times 1/sqrt(h) = 2^(-k/2) for even
  *    k = log2 h, fp64(sqrt(2)) * 2^(-(k+1)/2) for odd k.
  *  - Clip ([OSCAR] §3.4.4): tau = y[j] + f*(y[j+1] - y[j]) in fp32 without fusion, y = sorted |x~|,
- *    j = floor(127*rho), f = fp32(127*rho - j) (tau = y[127] when j = 127); x = min(max(x~, -tau), tau).
+ *    j = floor(127*rho), f = fp32(127*rho - j) (tau = y[127] when j = 127); x = min(max(x~, -tau), tau),
+ *    each of max and min taking its second operand when the two compare equal (a zero clipped at tau = 0
+ *    is +0).
  *  - INT2 per channel over the group: s = fp32((b-a)/3) (1 if b == a) -> bf16 s'; z = fp32(-a/s') ->
  *    bf16 z'; code = clamp(rint(fp32(fp32(x/s') + z')), 0, 3), rint ties to even.  INT2 per token:
  *    the same with a, b the min and max of the token's 128 (clipped) channels.  INT4 per channel: the same
