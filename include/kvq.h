@@ -76,7 +76,8 @@
  *    per-channel arithmetic with 15 levels: s = fp32((b-a)/15), code = clamp(rint(fp32(fp32(x/s') + z')), 0, 15).
  *  - Key-only rotation (key_only_rotation = 1): V is quantized in its own frame (no rotation, the
  *    bf16 values exactly) and the output is not un-rotated; K is rotated as above.
- *  - INT4 per token: s = fp32((b-a)/15) -> bf16 s'; z = rint(fp32(-a/s')) -> bf16 z';
+ *  - INT4 per token: s = fp32((b-a)/15) -> bf16 s'; z = rint(fp32(-a/s')) + 0 -> bf16 z' (an integer zero
+ *    point has one zero, stored as +0);
  *    code = clamp(rint(fp32(x/s')) + z', 0, 15).
  *  - Dequantized value x^ = s'(code - z').
  */

@@ -38,6 +38,8 @@ Readings taken where the pages leave a step open (each listed in the design doc):
       q = clamp(rint(fp32(fp32(x/s') + z')), 0, 3), rint = half to even.
   R6  INT4 ([SAW] eq. (3)-(4)): per token, s = (max-min)/15 (bf16 stored), integer
       z = rint(-min/s') (bf16 stored), q = clamp(rint(x/s') + z', 0, 15).
+  R18 The integer zero point of R6 has one zero, stored as +0 (a zero minimum, or
+      -min/s' of magnitude below one half, would otherwise give -0 or +0 by sign).
   R7  Layout of a length-T cache: tokens [0, S0) are the bf16 sink; groups
       g = 0..n_g-1 cover [S0+128g, S0+128(g+1)) with n_g = max(0, (T-S0-W)//128);
       the rest is the bf16 tail (W..W+127 tokens once T >= S0+W).
@@ -315,7 +317,9 @@ def quantize_int4_token(x: np.ndarray):
     s = np.where(b > a, ((b - a).astype(F32) / F32(15)).astype(F32), F32(1)).astype(F32)
     s16 = bf16_rne(s)
     sp = bf16_value(s16)
-    z = np.rint(((-a).astype(F32) / sp).astype(F32)).astype(F32)
+    # z is an integer ([SAW] eq. (3)), and an integer has one zero: stored as +0 (reading R18), so the sign
+    # of a zero minimum never reaches the stored bits
+    z = (np.rint(((-a).astype(F32) / sp).astype(F32)).astype(F32) + F32(0)).astype(F32)
     z16 = bf16_rne(z)
     zp = bf16_value(z16)
     r = np.rint((x / sp[:, None]).astype(F32)).astype(F32)

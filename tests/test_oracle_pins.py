@@ -270,6 +270,24 @@ def test_int4_codes_on_the_grid_and_eq4_rounding_order():
     assert q[0, 2] == 3
 
 
+def test_int4_integer_zero_point_has_one_zero():
+    """[SAW] eq. (3): z = round(-min / s) is an integer, so a zero zero point is stored as +0 whatever the
+    sign of a zero minimum, or of -min / s below one half."""
+    rows = np.zeros((5, 128), np.float32)
+    rows[1, :] = -0.0                                 # all -0: b = a, s = 1, -a / s = +0
+    rows[2, 1:] = np.linspace(0.25, 3.75, 127)        # minimum +0: -a / s = -0
+    rows[3, 0], rows[3, 1:] = -0.0, np.linspace(0.25, 3.75, 127)
+    rows[4, 1:] = np.linspace(3.0, 18.0, 127)         # minimum 2^-... > 0 below s / 2: rint(-a / s) = -0
+    rows[4, 0] = 0.5
+    q, s16, z16 = O.quantize_int4_token(rows)
+    assert (z16 == 0).all(), z16                      # bf16 bits of +0
+    assert O.bf16_value(s16)[0] == 1.0 and O.bf16_value(s16)[1] == 1.0
+    assert (q[0] == 0).all() and (q[1] == 0).all()
+    sp = O.bf16_value(s16)[2]
+    assert q[2, 0] == 0 and q[2, -1] == 15 and np.array_equal(q[2], q[3])
+    assert q[4, 0] == int(np.rint(np.float32(0.5) / O.bf16_value(s16)[4]))
+
+
 def test_bf16_rne_against_exact_rounding():
     x = (RNG.standard_normal(2000) * 10.0 ** RNG.integers(-20, 20, 2000)).astype(np.float32)
     got = O.bf16_value(O.bf16_rne(x))
