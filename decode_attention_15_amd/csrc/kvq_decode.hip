@@ -1449,7 +1449,8 @@ __device__ void int2_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T,
 // and its digit words are built once before the walk.  Values: the group adds
 //   sum_t p_t s'_t (code'_tc - z'_t) = (S' / 65535) (sum_t u_t code'_tc - sum_t u_t z'_t)
 // to the output, with the weights p_t s'_t rounded to u_t = rint(65535 p_t s'_t / S'), S' the group's
-// largest value scale (p_t <= 1 relative to the group's largest logit), and sum_t p_t to the softmax sum.
+// largest weight p_t s'_t of the head (p_t <= 1 relative to the group's largest logit), and sum_t p_t to the
+// softmax sum.
 // Lane roles, digit words and the copy pipeline as in int2_unit_dot8; the metadata of a page holds its
 // tokens' K scales, K zeros, V scales, V zeros (64 bf16 each).
 // ---------------------------------------------------------------------------------------------
@@ -1563,17 +1564,26 @@ __device__ void int2tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
       }
       heads_allreduce<GQ>(mx, OpMax(), lane, mg);
     }
-    const float smax = seg_reduce<64>(fmaxf(svt[0], svt[1]), OpMax());  // S' (uniform)
-    const float sinv = smax > 0.0f ? 1.0f / smax : 0.0f;
+    // S'_h: the group's largest weight p_t s'_t of head h (positive: the largest logit has p = 1)
+    float p[2][GQ], Sw[GQ];
     {
-      float ps[GQ], zs[GQ];
-      const float w0 = svt[0] * sinv, w1 = svt[1] * sinv;  // in [0, 1]
+      float sm[GQ];
 #pragma unroll
       for (int hh = 0; hh < GQ; ++hh) {
-        const float p0 = __builtin_amdgcn_exp2f(lg[0][hh] - mg[hh]), p1 = __builtin_amdgcn_exp2f(lg[1][hh] - mg[hh]);
-        const float e0 = fmaf(p0 * w0, kScaleW, kRoundW), e1 = fmaf(p1 * w1, kScaleW, kRoundW);
+        p[0][hh] = __builtin_amdgcn_exp2f(lg[0][hh] - mg[hh]);
+        p[1][hh] = __builtin_amdgcn_exp2f(lg[1][hh] - mg[hh]);
+        sm[hh] = fmaxf(p[0][hh] * svt[0], p[1][hh] * svt[1]);
+      }
+      heads_allreduce<GQ>(sm, OpMax(), lane, Sw);
+    }
+    {
+      float ps[GQ], zs[GQ];
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+        const float r = Sw[hh] > 0.0f ? kScaleW / Sw[hh] : 0.0f;
+        const float e0 = fmaf(p[0][hh] * svt[0], r, kRoundW), e1 = fmaf(p[1][hh] * svt[1], r, kRoundW);
         const uint32_t u0 = __float_as_uint(e0), u1 = __float_as_uint(e1);
-        ps[hh] = p0 + p1;
+        ps[hh] = p[0][hh] + p[1][hh];
         zs[hh] = fmaf(e0 - kRoundW, zvt[0], (e1 - kRoundW) * zvt[1]);
         store_weight_digits(pw + hh * 256, u0, u1);
       }
@@ -1599,7 +1609,7 @@ __device__ void int2tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
       const float mnew = fmaxf(m[hh], mg[hh]);
       const float sc = __builtin_amdgcn_exp2f(m[hh] - mnew);  // 0 before the first group (m = -inf)
       const float eg = __builtin_amdgcn_exp2f(mg[hh] - mnew);
-      const float wg = eg * smax * (1.0f / kScaleW);
+      const float wg = eg * Sw[hh] * (1.0f / kScaleW);
       o[hh][0] = fmaf(o[hh][0], sc, wg * ((float)digits_value(accv[0][hh]) - Zs[hh]));
       o[hh][1] = fmaf(o[hh][1], sc, wg * ((float)digits_value(accv[1][hh]) - Zs[hh]));
       l[hh] = fmaf(l[hh], sc, eg * Pl[hh]);
@@ -1868,17 +1878,26 @@ __device__ void int4tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
       }
       heads_allreduce<GQ>(mx, OpMax(), lane, mg);
     }
-    const float smax = __int_as_float(seg_max_i<64>(max(__float_as_int(svt[0]), __float_as_int(svt[1]))));  // S' (uniform)
-    const float sinv = smax > 0.0f ? 1.0f / smax : 0.0f;
+    // S'_h: the pair's largest weight p_t s'_t of head h (positive: the largest logit has p = 1)
+    float p[2][GQ], Sw[GQ];
     {
-      float ps[GQ], zs[GQ];
-      const float w0 = svt[0] * sinv, w1 = svt[1] * sinv;  // in [0, 1]
+      float sm[GQ];
 #pragma unroll
       for (int hh = 0; hh < GQ; ++hh) {
-        const float p0 = __builtin_amdgcn_exp2f(lg[0][hh] - mg[hh]), p1 = __builtin_amdgcn_exp2f(lg[1][hh] - mg[hh]);
-        const float e0 = fmaf(p0 * w0, kScaleW, kRoundW), e1 = fmaf(p1 * w1, kScaleW, kRoundW);
+        p[0][hh] = __builtin_amdgcn_exp2f(lg[0][hh] - mg[hh]);
+        p[1][hh] = __builtin_amdgcn_exp2f(lg[1][hh] - mg[hh]);
+        sm[hh] = fmaxf(p[0][hh] * svt[0], p[1][hh] * svt[1]);
+      }
+      heads_allreduce<GQ>(sm, OpMax(), lane, Sw);
+    }
+    {
+      float ps[GQ], zs[GQ];
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+        const float r = Sw[hh] > 0.0f ? kScaleW / Sw[hh] : 0.0f;
+        const float e0 = fmaf(p[0][hh] * svt[0], r, kRoundW), e1 = fmaf(p[1][hh] * svt[1], r, kRoundW);
         const uint32_t u0 = __float_as_uint(e0), u1 = __float_as_uint(e1);
-        ps[hh] = p0 + p1;
+        ps[hh] = p[0][hh] + p[1][hh];
         zs[hh] = fmaf(e0 - kRoundW, zvt[0], (e1 - kRoundW) * zvt[1]);
         const uint32_t x = nib_x(u0, u1), y = nib_y(u0, u1);
         uint8_t* q = pw + hh * 256;
@@ -1913,7 +1932,7 @@ __device__ void int4tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
       const float mnew = fmax_raw(m[hh], mg[hh]);
       const float sc = __builtin_amdgcn_exp2f(m[hh] - mnew);  // 0 before the first pair (m = -inf)
       const float eg = __builtin_amdgcn_exp2f(mg[hh] - mnew);
-      const float wg = eg * smax * (1.0f / kScaleW);
+      const float wg = eg * Sw[hh] * (1.0f / kScaleW);
       o[hh][0] = fmaf(o[hh][0], sc, wg * ((float)digits_value(accv[0][hh]) - Zs[hh]));
       o[hh][1] = fmaf(o[hh][1], sc, wg * ((float)digits_value(accv[1][hh]) - Zs[hh]));
       l[hh] = fmaf(l[hh], sc, eg * Pl[hh]);
@@ -1934,7 +1953,7 @@ __device__ void int4tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
 //   itself, rounded once per work-group to a_c = rint(q~_c 32639 / max|q~|) (A = max|q~| / 32639),
 //   so logit_t = A s_t (sum_c a_c code_tc - z_t sum_c a_c).
 //   out_c = sum_t p_t s'_t (code'_tc - z'_t): the value-side weight w_t = p_t s'_t (p_t = 2^(logit_t -
-//   max over the page) <= 1) is rounded to u_t = rint(65535 w_t / S'), S' = max over the page of s'_t,
+//   max over the page) <= 1) is rounded to u_t = rint(65535 w_t / S'), S' = max over the page of w_t,
 //   so out_c = (S' / 65535) (sum_t u_t code'_tc - sum_t u_t z'_t).
 // Both 16-bit operands are split into two byte limbs as in int2_unit_dot16.  Lane roles: key token lane of
 // the page; value channels lane, lane + 64.  Operand words in LDS:
@@ -2062,14 +2081,24 @@ __device__ void int4_unit_dot16(Lds& L, const DecodeArgs& a, int b, int h, int T
       }
       heads_allreduce<GQ>(mx, OpMax(), lane, mg);
     }
-    const float Sv = seg_reduce<64>(valid ? sv : 0.0f, OpMax());
-    const float rs = Sv > 0.0f ? 65535.0f / Sv : 0.0f;
+    // S'_h: the page's largest weight p_t s'_t of head h (positive: the largest logit has p = 1); tokens
+    // past the end of the sequence have weight 0, and their (unwritten) metadata is never read
+    float pexp[GQ], Sw[GQ];
+    {
+      float sm[GQ];
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+        pexp[hh] = valid ? __builtin_amdgcn_exp2f(lg[hh] - mg[hh]) : 0.0f;
+        sm[hh] = valid ? pexp[hh] * sv : 0.0f;
+      }
+      heads_allreduce<GQ>(sm, OpMax(), lane, Sw);
+    }
     {
       float pp[GQ], zz[GQ];
 #pragma unroll
       for (int hh = 0; hh < GQ; ++hh) {
-        // tokens past the end of the sequence: weight 0, and their (unwritten) metadata never read
-        const float p = valid ? __builtin_amdgcn_exp2f(lg[hh] - mg[hh]) : 0.0f;
+        const float p = pexp[hh];
+        const float rs = Sw[hh] > 0.0f ? 65535.0f / Sw[hh] : 0.0f;
         const uint32_t u = valid ? (uint32_t)fmaf(p * sv, rs, 0.5f) : 0u;
         pp[hh] = p;
         zz[hh] = valid ? (float)u * zv : 0.0f;
@@ -2124,7 +2153,7 @@ __device__ void int4_unit_dot16(Lds& L, const DecodeArgs& a, int b, int h, int T
       const float mnew = fmaxf(m[hh], mg[hh]);
       const float sc = exp2_safe_diff(m[hh], mnew);
       const float wpg = exp2_safe_diff(mg[hh], mnew);
-      const float ws = wpg * Sv * (1.0f / 65535.0f);
+      const float ws = wpg * Sw[hh] * (1.0f / 65535.0f);
       const float U0 = (float)(accv[0][hh][1] * 256u + accv[0][hh][0]);
       const float U1 = (float)(accv[1][hh][1] * 256u + accv[1][hh][0]);
       o[hh][0] = fmaf(o[hh][0], sc, ws * (U0 - uz[hh]));

@@ -50,6 +50,33 @@ __device__ inline float wave_max_f32(float v) {
 
 __device__ inline int wave_count(bool p) { return __popcll(__ballot(p)); }
 
+// Integer zero point of the token-wise INT4 scheme, rint(-min / s'); an integer has one zero, stored as +0
+// (adding +0 turns -0 into +0 and leaves every other value as it is), so the sign of a zero minimum
+// cannot reach the stored bits.
+__device__ inline float int_zero_point(float amin, float sp) { return __fadd_rn(rintf(__fdiv_rn(-amin, sp)), 0.0f); }
+
+// Correctly rounded x / s for a scale s stored as bf16 (8-bit significand), from rs = 1 / s in fp64.  The
+// quotient never lies on a midpoint between fp32 neighbours (x = m s with m such a midpoint would need an
+// odd factor above 2^24 in x's 24-bit significand), nor within 2^-33 of one relative to its size (the
+// distance is a multiple of ulp/2 / s' for the significand s' < 2^8 of s); x rs is within 2^-52 of x / s,
+// so rounding it to fp32 gives RN(x / s).  Exhaustively checked over every fp32 significand of x and
+// every bf16 significand of s.
+__device__ inline double rcp_of_bf16(float s) { return 1.0 / (double)s; }
+__device__ inline float div_by_bf16(float x, double rs) { return (float)((double)x * rs); }
+
+// fp64 / fp32 value of lane l ^ 1 (CTRL 0xB1) or l ^ 2 (CTRL 0x4E) of the lane's quad (DPP quad permute)
+template <int CTRL>
+__device__ __forceinline__ double quad_swap_f64(double v) {
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, true);
+  return __hiloint2double(hi, lo);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float quad_swap_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
 // j-th smallest (0-based) of the 128 non-negative floats held two per lane, as bit patterns
 // (non-negative IEEE floats order like their unsigned bit patterns).  Greedy construction of the
 // largest v with #{x < v} <= j, one bit at a time.
@@ -232,7 +259,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
   float* xs = lds;  // [128 tokens][XS_STRIDE] inputs (bf16 values), rotated and clipped in place
   float* xr = xs;   // the same rows once rotated
   __shared__ float red_min[2][D], red_max[2][D];
-  __shared__ float s_sp[D], s_zp[D];  // per channel, or per token of the group
+  __shared__ float s_zp[D];   // zero point per channel, or per token of the group
+  __shared__ double s_rs[D];  // 1 / s' in fp64, likewise
 
   const Geo& g = a.g;
   const int lg = blockIdx.x;
@@ -315,7 +343,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
       const float sp = bf16_to_f32(s16);
       const uint16_t z16 = f32_to_bf16_rne(__fdiv_rn(-amin, sp));
       if (lane == 0) {
-        s_sp[tl] = sp;
+        s_rs[tl] = rcp_of_bf16(sp);
         s_zp[tl] = bf16_to_f32(z16);
         // page of the token: its K (which = 0) or V (which = 1) scales[64] then zeros[64]
         const long long phys = a.page_table[(long long)b * g.max_pages + 2 * grp + (tl >> 6)];
@@ -343,7 +371,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
     const uint16_t s16 = f32_to_bf16_rne(s);
     const float sp = bf16_to_f32(s16);
     const uint16_t z16 = f32_to_bf16_rne(__fdiv_rn(-amin, sp));
-    s_sp[tid] = sp;
+    s_rs[tid] = rcp_of_bf16(sp);
     s_zp[tid] = bf16_to_f32(z16);
     const long long phys = a.page_table[(long long)b * g.max_pages + 2 * grp + which];
     uint16_t* meta = reinterpret_cast<uint16_t*>(a.pages + phys * g.page_bytes + hoff + moff);
@@ -355,7 +383,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
   // 5. codes and packing
   auto code = [&](float x, int c, int tl) -> uint32_t {
     const int i = tokenwise ? tl : c;
-    float t = __fadd_rn(__fdiv_rn(x, s_sp[i]), s_zp[i]);
+    float t = __fadd_rn(div_by_bf16(x, s_rs[i]), s_zp[i]);
     t = fminf(fmaxf(rintf(t), 0.0f), levels);
     return (uint32_t)t;
   };
@@ -519,10 +547,11 @@ __global__ __launch_bounds__(256) void int4_quad_kernel(WriteArgs a) {
     const float s = (bmax > amin) ? __fdiv_rn(__fsub_rn(bmax, amin), 15.0f) : 1.0f;
     const uint16_t s16 = f32_to_bf16_rne(s);
     const float sp = bf16_to_f32(s16);
-    const uint16_t z16 = f32_to_bf16_rne(rintf(__fdiv_rn(-amin, sp)));
+    const uint16_t z16 = f32_to_bf16_rne(int_zero_point(amin, sp));
     const float zp = bf16_to_f32(z16);
+    const double rs = rcp_of_bf16(sp);
     auto code4 = [&](float x) -> uint32_t {
-      float q = __fadd_rn(rintf(__fdiv_rn(x, sp)), zp);
+      float q = __fadd_rn(rintf(div_by_bf16(x, rs)), zp);
       q = fminf(fmaxf(q, 0.0f), 15.0f);
       return (uint32_t)q;
     };
@@ -556,6 +585,172 @@ __global__ __launch_bounds__(256) void int4_quad_kernel(WriteArgs a) {
       if (tr >= T0 && tr < T1) v = (v & ~(0xFu << (4 * r))) | ((uint32_t)codes[r][c] << (4 * r));
     }
     *p = (uint16_t)v;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// INT4 token-wise under the randomized Hadamard of block order HB ([SAW] §3 eq. (1), App. A.1
+// eq. (3)-(4)).  One work-group per (64-token page, kv head, K|V, sequence) that the append reaches; lane
+// l of wave w holds token 16 w + l / 4 of the page and its channels 32 (l % 4) + i, i = 0..31.  The
+// butterfly stages h = 1..16 pair channels of one lane, h = 32 and 64 pair lanes l ^ 1 and l ^ 2 of the
+// quad, and the token's min and max are quad reductions.  K rows (token-major) and the metadata are written
+// by the token's own lanes; the V rows (channel-major, two tokens per byte) are assembled from the page's
+// nibble words in LDS by an 8 x 8 nibble transpose, merged with the stored nibbles of tokens outside the
+// append.  Sources are read 16 bytes at a time (the launcher checks their alignment).
+// ---------------------------------------------------------------------------------------------
+template <int HB>
+__global__ __launch_bounds__(256) void int4_page_kernel(WriteArgs a) {
+  __shared__ uint32_t nib[PAGE * 16];  // [token][word m]: nibble k of word m = channel 8 m + k
+  const Geo& g = a.g;
+  const int which = blockIdx.y & 1;
+  const int h = blockIdx.y >> 1;
+  const int b = blockIdx.z;
+  const int T0 = a.seq_lens[b];
+  const int c0 = a.cu_new[b];
+  const int n_new = a.cu_new[b + 1] - c0;
+  const int T1 = T0 + n_new;
+  if (n_new <= 0) return;
+  const int page = T0 / PAGE + blockIdx.x;
+  if (page * PAGE >= T1 || page >= g.max_pages) return;  // past the append or the page-table row
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tk = 16 * wave + (lane >> 2), qd = lane & 3;
+  const int t = page * PAGE + tk;
+  const bool is_new = t >= T0 && t < T1;
+  const long long phys = a.page_table[(long long)b * g.max_pages + page];
+  uint8_t* head = a.pages + phys * g.page_bytes + (long long)h * I4_HEAD_BYTES;
+
+  float y[32];
+  if (is_new) {
+    const long long base = ((long long)(c0 + t - T0) * g.n_kv + h) * D + 32 * qd;
+    const void* src = which ? a.v : a.k;
+    if (a.src_bf16) {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + base);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint4 w = p[k];
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          y[8 * k + 2 * m] = __uint_as_float(ww[m] << 16);
+          y[8 * k + 2 * m + 1] = __uint_as_float(ww[m] & 0xffff0000u);
+        }
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) + base);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float4 w = p[k];
+        y[4 * k] = bf16_to_f32(f32_to_bf16_rne(w.x));
+        y[4 * k + 1] = bf16_to_f32(f32_to_bf16_rne(w.y));
+        y[4 * k + 2] = bf16_to_f32(f32_to_bf16_rne(w.z));
+        y[4 * k + 3] = bf16_to_f32(f32_to_bf16_rne(w.w));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) y[i] = 0.0f;
+  }
+
+  if (!(which == 1 && g.key_only)) {  // key-only rotation: V quantized in its own frame
+    const float* sg = (which ? a.rot_v : a.rot_k) + 32 * qd;
+    double e[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) e[i] = (double)y[i] * (double)sg[i];
+#pragma unroll
+    for (int hs = 1; hs < 32 && hs < HB; hs <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (i & hs) continue;
+        const double lo = e[i], hi = e[i + hs];
+        e[i] = lo + hi;
+        e[i + hs] = lo - hi;
+      }
+    }
+    // across the quad: the upper channel of a pair takes partner - own, the lower own + partner
+    if constexpr (HB >= 64) {
+      const double sgn = (qd & 1) ? -1.0 : 1.0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) e[i] = fma(sgn, e[i], quad_swap_f64<0xB1>(e[i]));
+    }
+    if constexpr (HB >= 128) {
+      const double sgn = (qd & 2) ? -1.0 : 1.0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) e[i] = fma(sgn, e[i], quad_swap_f64<0x4E>(e[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) y[i] = (float)(e[i] * g.hscale);
+  }
+
+  float amin = y[0], bmax = y[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) {
+    amin = fminf(amin, y[i]);
+    bmax = fmaxf(bmax, y[i]);
+  }
+  amin = fminf(amin, quad_swap_f32<0xB1>(amin));
+  bmax = fmaxf(bmax, quad_swap_f32<0xB1>(bmax));
+  amin = fminf(amin, quad_swap_f32<0x4E>(amin));
+  bmax = fmaxf(bmax, quad_swap_f32<0x4E>(bmax));
+  const float s = (bmax > amin) ? __fdiv_rn(__fsub_rn(bmax, amin), 15.0f) : 1.0f;
+  const uint16_t s16 = f32_to_bf16_rne(s);
+  const float sp = bf16_to_f32(s16);
+  const uint16_t z16 = f32_to_bf16_rne(int_zero_point(amin, sp));
+  const float zp = bf16_to_f32(z16);
+  const double rs = rcp_of_bf16(sp);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    float q = __fadd_rn(rintf(div_by_bf16(y[i], rs)), zp);
+    q = fminf(fmaxf(q, 0.0f), 15.0f);
+    w[i >> 3] |= (uint32_t)q << (4 * (i & 7));
+  }
+  if (is_new && qd == 0)
+    *reinterpret_cast<uint32_t*>(head + (which ? I4_VMETA_OFF : I4_KMETA_OFF) + 4 * tk) =
+        (uint32_t)s16 | ((uint32_t)z16 << 16);
+  if (which == 0) {
+    if (is_new) *reinterpret_cast<uint4*>(head + I4_K_OFF + tk * 64 + 16 * qd) = make_uint4(w[0], w[1], w[2], w[3]);
+    return;
+  }
+  reinterpret_cast<uint4*>(nib)[tk * 4 + qd] = make_uint4(w[0], w[1], w[2], w[3]);
+  __syncthreads();
+  if (tid >= 128) return;
+  // V word wi of channel 8 cb + c: nibble p holds token 32 (wi & 1) + 16 (p >> 2) + 4 (wi >> 1) + (p & 3)
+  const int wi = tid & 7, cb = tid >> 3;
+  const int tbase = 32 * (wi & 1) + 4 * (wi >> 1);
+  uint32_t A[8];
+  uint32_t keep = 0;  // nibbles of tokens outside the append
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int tp = tbase + 16 * (p >> 2) + (p & 3);
+    A[p] = nib[tp * 16 + cb];
+    const int tt = page * PAGE + tp;
+    if (tt < T0 || tt >= T1) keep |= 0xFu << (4 * p);
+  }
+  if (keep == 0xFFFFFFFFu) return;
+  // 8 x 8 nibble transpose: afterwards nibble p of A[c] is nibble c of the word read for token slot p
+#pragma unroll
+  for (int p = 0; p < 8; p += 2) {
+    const uint32_t x = ((A[p] >> 4) ^ A[p + 1]) & 0x0F0F0F0Fu;
+    A[p + 1] ^= x;
+    A[p] ^= x << 4;
+  }
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    if (p & 2) continue;
+    const uint32_t x = ((A[p] >> 8) ^ A[p + 2]) & 0x00FF00FFu;
+    A[p + 2] ^= x;
+    A[p] ^= x << 8;
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t x = ((A[p] >> 16) ^ A[p + 4]) & 0x0000FFFFu;
+    A[p + 4] ^= x;
+    A[p] ^= x << 16;
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    uint32_t* dst = reinterpret_cast<uint32_t*>(head + I4_V_OFF + (8 * cb + c) * 32 + 4 * wi);
+    *dst = keep ? ((A[c] & ~keep) | (*dst & keep)) : A[c];
   }
 }
 
@@ -605,8 +800,20 @@ hipError_t launch_write_int2(const WriteArgs& a, hipStream_t s) {
 
 hipError_t launch_write_int4(const WriteArgs& a, hipStream_t s) {
   if (a.max_new > 0) {
-    const int quads = (a.max_new + 3) / 4 + 1;
-    hipLaunchKernelGGL(int4_quad_kernel, dim3(quads, a.g.n_kv * 2, a.g.batch), dim3(256), 0, s, a);
+    const bool aligned = reinterpret_cast<uintptr_t>(a.k) % 16 == 0 && reinterpret_cast<uintptr_t>(a.v) % 16 == 0;
+    if (a.g.rotation == KVQ_ROT_HADAMARD && aligned) {
+      // n new tokens reach at most (n + 62) / 64 + 1 pages of a sequence
+      const dim3 grid((a.max_new + 62) / PAGE + 1, a.g.n_kv * 2, a.g.batch);
+      switch (a.g.hblock) {
+        case 16: hipLaunchKernelGGL(int4_page_kernel<16>, grid, dim3(256), 0, s, a); break;
+        case 32: hipLaunchKernelGGL(int4_page_kernel<32>, grid, dim3(256), 0, s, a); break;
+        case 64: hipLaunchKernelGGL(int4_page_kernel<64>, grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL(int4_page_kernel<128>, grid, dim3(256), 0, s, a); break;
+      }
+    } else {
+      const int quads = (a.max_new + 3) / 4 + 1;
+      hipLaunchKernelGGL(int4_quad_kernel, dim3(quads, a.g.n_kv * 2, a.g.batch), dim3(256), 0, s, a);
+    }
   }
   hipLaunchKernelGGL(advance_kernel, dim3(1), dim3(256), 0, s, a.seq_lens, a.cu_new, a.g.batch);
   return hipGetLastError();

@@ -141,3 +141,152 @@ def test_lengths_at_the_sink_window_group_boundaries(K, T, scheme):
     # written one token at a time below 8 tokens, else in two uneven chunks
     chunks = [1] * T if T < 8 else [T // 3, T - T // 3]
     _write_and_check(K, synth.scaled(WL, scheme=scheme), _bf16(k), _bf16(v), chunks=chunks)
+
+
+# ------------------------------------------------------------------ INT4 per token ([SAW] App. A.1)
+
+SAW = synth.scaled(synth.WORKLOADS["saw_int4_b16_16k"], n_q_heads=8, n_kv_heads=2, batch=1)
+
+
+def _int4_expected(wl, k, v, rk, rv):
+    """Oracle codes and metadata of every token of one kv head (source [T, 128]), either rotation."""
+    if wl.rotation == "saw":
+        return O.int4_state(k, v, len(k), rk.astype(np.int8), rv.astype(np.int8), block=wl.hadamard_block)
+    xk = O.rotate_dense(O.bf16_value(O.source_to_bf16(k)), rk)
+    xv = O.rotate_dense(O.bf16_value(O.source_to_bf16(v)), rv)
+    qk, sk, zk = O.quantize_int4_token(xk)
+    qv, sv, zv = O.quantize_int4_token(xv)
+    return {"k_codes": qk, "k_s16": sk, "k_z16": zk, "v_codes": qv, "v_s16": sv, "v_z16": zv}
+
+
+def _int4_keys_values(wl, st, rk, rv):
+    if wl.rotation == "saw":
+        return O.int4_keys_values(st, rk.astype(np.int8), rv.astype(np.int8), wl.hadamard_block)
+    xk = O.dequantize(st["k_codes"], st["k_s16"][:, None], st["k_z16"][:, None])
+    xv = O.dequantize(st["v_codes"], st["v_s16"][:, None], st["v_z16"][:, None])
+    return xk @ rk.astype(np.float64).T, xv @ rv.astype(np.float64).T
+
+
+def _int4_write_and_check(K, wl, k, v, chunks, misalign=False, decode=True):
+    """Write K/V [T, n_kv, 128] (bf16 bits or fp32) of one sequence in `chunks`, each chunk's source placed
+    4 bytes past a 16-byte boundary if `misalign`; compare every token's codes and metadata, and the decode
+    output if `decode`."""
+    import torch
+    from kvq_cases import read_int4_tokens
+    T = k.shape[0]
+    cfg = config_for(K, wl)
+    rk, rv = rotations(wl)
+    max_pages = max(1, K.pages_for_len(cfg, T))
+    pt, n_pool = synth.page_table(wl, max_pages, max_pages + 2)
+    cache = K.allocate_cache(cfg, 1, torch.from_numpy(pt), torch.from_numpy(rk), torch.from_numpy(rv), n_pages=n_pool)
+
+    def dev(x):
+        t = source_torch(np.ascontiguousarray(x), "cuda")
+        if not misalign:
+            return t
+        pad = 2 if t.dtype == torch.bfloat16 else 1
+        buf = torch.zeros(t.numel() + pad, dtype=t.dtype, device="cuda")
+        buf[pad:] = t.reshape(-1)
+        out = buf[pad:].view(t.shape)
+        assert out.data_ptr() % 16 != 0
+        return out
+
+    done = 0
+    for n in chunks:
+        cu = torch.tensor([0, n], dtype=torch.int32, device="cuda")
+        K.kv_rotate_quant_write(cache, dev(k[done:done + n]), dev(v[done:done + n]), cu, n)
+        done += n
+    torch.cuda.synchronize()
+    assert done == T and int(cache.seq_lens.item()) == T
+    pages = cache.pages.cpu().numpy()
+    bc = _BC(wl, cache)
+    q = synth.queries(wl)
+    if decode:
+        out = torch.empty((1, wl.n_q_heads, 128), dtype=torch.float32, device="cuda")
+        K.kv_decode_attn(cache, source_torch(q, "cuda"), out, T, K.workspace_for(cfg, 1, T))
+        torch.cuda.synchronize()
+        got_out = out.cpu().numpy()
+    worst = 0.0
+    for h in range(wl.n_kv_heads):
+        st = _int4_expected(wl, k[:, h], v[:, h], rk, rv)
+        got = read_int4_tokens(bc, pages, 0, h, T)
+        for key in ("k_codes", "v_codes", "k_s16", "k_z16", "v_s16", "v_z16"):
+            bad = np.argwhere(got[key] != st[key])
+            assert len(bad) == 0, f"h={h} {key}: {len(bad)} mismatches, first {bad[:5].tolist()}"
+        if not decode:
+            continue
+        Kh, Vh = _int4_keys_values(wl, st, rk, rv)
+        want = O.attend(O.query_values(q[0, h * wl.gq:(h + 1) * wl.gq]), Kh, Vh)
+        err = np.abs(got_out[0, h * wl.gq:(h + 1) * wl.gq] - want).max()
+        worst = max(worst, err)
+        assert err <= TOL, f"h={h}: max |diff| {err:.3e}"
+    return worst
+
+
+def _int4_tokens(T, seed):
+    """Random tokens with degenerate ones mixed in: all zero, all -0, constant, positive only (minimum far
+    above zero, or exactly +0), one-hot."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, 2, 128)).astype(np.float32)
+    x[3] = 0.0
+    x[4] = -0.0
+    x[70:74] = 0.75
+    x[75] = np.abs(x[75]) + 4.0
+    x[76] = np.abs(x[76]); x[76, :, 5] = 0.0
+    x[130] = 0.0; x[130, :, 17] = 3.0
+    return x
+
+
+def _heavy_unattended_token(wl, k, v, t):
+    """Token t of every kv head gets values 10^4 times larger than the rest and a key pointing away from
+    the sum of the head's queries, so each query head gives it a logit near -50: a value scale that
+    dominates its page while its softmax weight is nil."""
+    q = O.query_values(synth.queries(wl)[0])
+    for h in range(wl.n_kv_heads):
+        u = q[h * wl.gq:(h + 1) * wl.gq].sum(axis=0)
+        k[t, h] = (-50.0 * np.sqrt(128.0) / np.abs(q[h * wl.gq:(h + 1) * wl.gq] @ (u / np.linalg.norm(u))).min()
+                   * u / np.linalg.norm(u)).astype(np.float32)
+        v[t, h] *= 1.0e4
+
+
+@pytest.mark.parametrize("block", [16, 128])
+def test_int4_token_degenerate_tokens_and_page_boundaries(K, block):
+    """Codes and metadata bit-exact (zero points of zero tokens stored as +0), with appends that start and
+    end inside pages: single tokens, a chunk ending one short of a page, a chunk crossing two pages."""
+    wl = synth.scaled(SAW, hadamard_block=block)
+    T = 400
+    k, v = _int4_tokens(T, 11), _int4_tokens(T, 12)
+    _heavy_unattended_token(wl, k, v, 200)
+    _say(f"int4 per token, degenerate tokens, block {block}")
+    _int4_write_and_check(K, wl, _bf16(k), _bf16(v), [1, 62, 1, 64, 1, 150, 121])
+
+
+def test_int4_token_large_and_tiny_magnitudes(K):
+    """Codes and metadata bit-exact for tokens at 1e30 and 1e-30 times the rest, and at 1e-38 (fp32
+    subnormal sources after bf16 rounding and rotation)."""
+    T = 200
+    k, v = _int4_tokens(T, 17), _int4_tokens(T, 18)
+    k[10], v[11] = k[10] * 1e30, v[11] * 1e30
+    k[12], v[13] = k[12] * 1e-30, v[13] * 1e-30
+    k[65], v[66] = k[65] * 1e-38, v[66] * 1e-38
+    _say("int4 per token, large and tiny magnitudes")
+    _int4_write_and_check(K, SAW, _bf16(k), _bf16(v), [70, 130], decode=False)
+
+
+def test_int4_token_fp32_and_unaligned_sources(K):
+    """An fp32 source (rounded to bf16 on entry) and bf16 sources 4 bytes past a 16-byte boundary (read a
+    value at a time) store the same bits as the oracle."""
+    T = 300
+    k, v = _int4_tokens(T, 13), _int4_tokens(T, 14)
+    _say("int4 per token, fp32 source")
+    _int4_write_and_check(K, SAW, k, v, [100, 1, 199])
+    _say("int4 per token, unaligned bf16 source")
+    _int4_write_and_check(K, SAW, _bf16(k), _bf16(v), [100, 1, 199], misalign=True)
+
+
+def test_int4_token_dense_rotation(K):
+    """INT4 per token under a dense OSCAR rotation (QR x Hadamard x bit reversal)."""
+    T = 333
+    k, v = _int4_tokens(T, 15), _int4_tokens(T, 16)
+    _say("int4 per token, dense rotation")
+    _int4_write_and_check(K, synth.scaled(SAW, rotation="oscar"), _bf16(k), _bf16(v), [64, 5, 264])
