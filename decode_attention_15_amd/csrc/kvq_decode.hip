@@ -154,8 +154,7 @@ struct DecodeLds {
     struct {                     // 16-bit INT2 path
       uint8_t abytes[4][GQ * 256];  // per wave: key-side operand words [head][limb][32]
       uint8_t pbytes[4][GQ * 256];  // per wave: value-side operand words [head][limb][32]
-      uint4 vstage[4][256 * STG];   // per wave: value codes of the current group (both pages)
-      uint4 kstage[4][256 * STG];   // per wave: key codes of a group (nibble-digit path)
+      uint4 vstage[4][256 * STG];   // per wave: key, then value codes of the current group (both pages)
       uint4 mstage[4][64];          // per wave: key and value scales/zeros of a group (nibble-digit path)
     } d;
     float co[4][GQ][D];          // the waves' outputs, written once every wave has finished its walk
@@ -1016,7 +1015,8 @@ struct Dot8Wave {
   uint8_t* pdig;        // weight digit words [head][page * 4 + g][8]
   uint16_t* aval;       // biased 16-bit key operands [head][128] (aliases pdig while the digits are built)
   const uint4* vst;     // value codes of a group
-  const uint4* kst;     // key codes of a group, lane-ordered
+  const uint4* kst;     // key codes of a group, lane-ordered (the same buffer: keys are read out before the
+                        // group's value codes are copied in)
   const uint16_t* mst;  // metadata of a group's two pages (1 KB)
   uint32_t vst_a, kst_a, mst_a;
   const uint8_t* pages;
@@ -1029,7 +1029,7 @@ struct Dot8Wave {
     pdig = L.d.pbytes[wave];
     aval = reinterpret_cast<uint16_t*>(L.d.pbytes[wave]);
     vst = L.d.vstage[wave];
-    kst = L.d.kstage[wave];
+    kst = L.d.vstage[wave];
     mst = reinterpret_cast<const uint16_t*>(L.d.mstage[wave]);
     vst_a = lds_addr(vst);
     kst_a = lds_addr(kst);
@@ -1267,18 +1267,19 @@ __device__ void int2_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T,
     o[hh][0] = o[hh][1] = 0.0f;
   }
   const int2* pt = reinterpret_cast<const int2*>(a.page_table + (long long)b * g.max_pages);
-  int2 pnext = make_int2(0, 0);
+  // copies in flight, in issue order: this group's M and K; the next group's M is issued once this M is read,
+  // this group's V once its K is read (into the same buffer), the next group's K once this V is read
+  int2 pcur = make_int2(0, 0), pnext = make_int2(0, 0);
   if (g_first < g_end) {
-    const int2 p0 = scalar_load_int2(pt + g_first);
-    W.issue_m(p0);
-    W.issue_k(p0);
-    W.issue_v(p0);
+    pcur = scalar_load_int2(pt + g_first);
+    W.issue_m(pcur);
+    W.issue_k(pcur);
   }
   for (int gi = g_first; gi < g_end; gi += gstep) {
     const bool has_next = gi + gstep < g_end;  // uniform
     if (has_next) pnext = scalar_load_int2(pt + gi + gstep);
-    if constexpr (BITS == 4) KVQ_WAIT_VM(16);  // this group's M copy (its K and V copies may still be in flight)
-    else KVQ_WAIT_VM(8);
+    if constexpr (BITS == 4) KVQ_WAIT_VM(8);  // this group's M copy (its K copies may still be in flight)
+    else KVQ_WAIT_VM(4);
     uint32_t skw[NCH / 2], zkw[NCH / 2];
 #pragma unroll
     for (int i = 0; i < NCH / 2; ++i) {
@@ -1331,14 +1332,9 @@ __device__ void int2_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T,
     wave_lds_sync();
 
     // 3. key dots: tokens kt, kt + 2 of page kp against every head
-    // this group's K copies (then V, next M may be in flight)
-    if constexpr (BITS == 4) {
-      if (has_next) KVQ_WAIT_VM(9);
-      else KVQ_WAIT_VM(8);
-    } else {
-      if (has_next) KVQ_WAIT_VM(5);
-      else KVQ_WAIT_VM(4);
-    }
+    // this group's K copies (the next group's M may be in flight)
+    if (has_next) KVQ_WAIT_VM(1);
+    else KVQ_WAIT_VM(0);
     uint32_t kw[2][4 * BITS];
 #pragma unroll
     for (int j = 0; j < 2 * BITS; ++j) {  // copy j: token j / BITS, words 4 (j % BITS) ..
@@ -1347,7 +1343,7 @@ __device__ void int2_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T,
       dst[0] = kk.x, dst[1] = kk.y, dst[2] = kk.z, dst[3] = kk.w;
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (has_next) W.issue_k(pnext);
+    W.issue_v(pcur);  // into the buffer the key codes have left
     int acc[2][GQ][4];
     key_dots<GQ, BITS>(W.adig, kw, acc);
 
@@ -1386,14 +1382,7 @@ __device__ void int2_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T,
     wave_lds_sync();
 
     // 5. value dots: channels c0, c1 against the weights of every head
-    // this group's V copies (then the next M and K may be in flight)
-    if constexpr (BITS == 4) {
-      if (has_next) KVQ_WAIT_VM(9);
-      else KVQ_WAIT_VM(0);
-    } else {
-      if (has_next) KVQ_WAIT_VM(5);
-      else KVQ_WAIT_VM(0);
-    }
+    KVQ_WAIT_VM(0);  // this group's V copies, the youngest in flight
     uint32_t vw[2][2][2 * BITS];  // [channel c0 | c1][page][word]
 #pragma unroll
     for (int j = 0; j < 2 * BITS; ++j) {
@@ -1403,7 +1392,7 @@ __device__ void int2_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T,
       dst[0] = vv.x, dst[1] = vv.y, dst[2] = vv.z, dst[3] = vv.w;
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (has_next) W.issue_v(pnext);
+    if (has_next) W.issue_k(pnext);
     int accv[2][GQ][4];
     value_dots<GQ, BITS>(W.pdig, vw, accv);
 
@@ -1425,6 +1414,7 @@ __device__ void int2_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int T,
       m[hh] = mnew;
     }
     wave_lds_sync();
+    pcur = pnext;
   }
 #pragma unroll
   for (int hh = 0; hh < GQ; ++hh) {
@@ -1518,17 +1508,17 @@ __device__ void int2tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
     o[hh][0] = o[hh][1] = 0.0f;
   }
   const int2* pt = reinterpret_cast<const int2*>(a.page_table + (long long)b * g.max_pages);
-  int2 pnext = make_int2(0, 0);
+  // copies in flight as in int2_unit_dot8: M and K of a group, its V once its K is read, the next K after V
+  int2 pcur = make_int2(0, 0), pnext = make_int2(0, 0);
   if (g_first < g_end) {
-    const int2 p0 = scalar_load_int2(pt + g_first);
-    W.issue_m(p0);
-    W.issue_k(p0);
-    W.issue_v(p0);
+    pcur = scalar_load_int2(pt + g_first);
+    W.issue_m(pcur);
+    W.issue_k(pcur);
   }
   for (int gi = g_first; gi < g_end; gi += gstep) {
     const bool has_next = gi + gstep < g_end;  // uniform
     if (has_next) pnext = scalar_load_int2(pt + gi + gstep);
-    KVQ_WAIT_VM(8);  // this group's M copy
+    KVQ_WAIT_VM(4);  // this group's M copy (its K copies may still be in flight)
     float sk[2], zk[2], svt[2], zvt[2];  // tokens kt, kt + 2
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -1540,12 +1530,12 @@ __device__ void int2tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (has_next) W.issue_m(pnext);
 
-    // 1. key dots
-    if (has_next) KVQ_WAIT_VM(5);
-    else KVQ_WAIT_VM(4);
+    // 1. key dots (this group's K copies; the next group's M may be in flight)
+    if (has_next) KVQ_WAIT_VM(1);
+    else KVQ_WAIT_VM(0);
     const uint4 k00 = W.kst[c0], k01 = W.kst[64 + c0], k10 = W.kst[128 + c0], k11 = W.kst[192 + c0];
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (has_next) W.issue_k(pnext);
+    W.issue_v(pcur);  // into the buffer the key codes have left
     int acc[2][GQ][4];
     const uint32_t kw[2][8] = {{k00.x, k00.y, k00.z, k00.w, k01.x, k01.y, k01.z, k01.w},
                                {k10.x, k10.y, k10.z, k10.w, k11.x, k11.y, k11.z, k11.w}};
@@ -1593,11 +1583,10 @@ __device__ void int2tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
     wave_lds_sync();
 
     // 3. value dots
-    if (has_next) KVQ_WAIT_VM(5);
-    else KVQ_WAIT_VM(0);
+    KVQ_WAIT_VM(0);  // this group's V copies, the youngest in flight
     const uint4 v00 = W.vst[c0], v01 = W.vst[64 + c0], v10 = W.vst[128 + c0], v11 = W.vst[192 + c0];
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (has_next) W.issue_v(pnext);
+    if (has_next) W.issue_k(pnext);
     int accv[2][GQ][4];
     const uint32_t vw[2][2][4] = {{{v00.x, v00.y, v00.z, v00.w}, {v10.x, v10.y, v10.z, v10.w}},
                                   {{v01.x, v01.y, v01.z, v01.w}, {v11.x, v11.y, v11.z, v11.w}}};
@@ -1616,6 +1605,7 @@ __device__ void int2tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
       m[hh] = mnew;
     }
     wave_lds_sync();
+    pcur = pnext;
   }
   if (wc) {
     // every partial a merge reads is written; chunks past the length or the launch bound have none
@@ -1818,17 +1808,17 @@ __device__ void int4tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
     l[hh] = 0.0f;
     o[hh][0] = o[hh][1] = 0.0f;
   }
-  int2 pnext = make_int2(0, 0);
+  // copies in flight as in int2_unit_dot8: M and K of a pair, its V once its K is read, the next K after V
+  int2 pcur = make_int2(0, 0), pnext = make_int2(0, 0);
   if (p_first < pe) {
-    const int2 p0 = pages_of(p_first);
-    issue_m(p0);
-    issue_k(p0);
-    W.issue_v(p0);
+    pcur = pages_of(p_first);
+    issue_m(pcur);
+    issue_k(pcur);
   }
   for (int pi = p_first; pi < pe; pi += pstep) {
     const bool has_next = pi + pstep < pe;  // uniform
     if (has_next) pnext = pages_of(pi + pstep);
-    KVQ_WAIT_VM(16);  // this pair's M copy
+    KVQ_WAIT_VM(8);  // this pair's M copy (its K copies may still be in flight)
     const int tok = pi * 128 + kp * 64 + t0;
     const bool v0 = tok < T, v1 = tok + 1 < T;
     float sk[2], zk[2], svt[2], zvt[2];
@@ -1848,9 +1838,9 @@ __device__ void int4tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
     svt[1] = v1 ? svt[1] : 0.0f;
     zvt[1] = v1 ? zvt[1] : 0.0f;
 
-    // 1. key dots
-    if (has_next) KVQ_WAIT_VM(9);
-    else KVQ_WAIT_VM(8);
+    // 1. key dots (this pair's K copies; the next pair's M may be in flight)
+    if (has_next) KVQ_WAIT_VM(1);
+    else KVQ_WAIT_VM(0);
     uint32_t kw[2][16];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -1859,7 +1849,7 @@ __device__ void int4tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
       dst[0] = kk.x, dst[1] = kk.y, dst[2] = kk.z, dst[3] = kk.w;
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (has_next) issue_k(pnext);
+    W.issue_v(pcur);  // into the buffer the key codes have left
     int acc[2][GQ][4];
     key_dots_seq<GQ>(W.adig, kw, acc);
 
@@ -1912,8 +1902,7 @@ __device__ void int4tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
     wave_lds_sync();
 
     // 3. value dots
-    if (has_next) KVQ_WAIT_VM(9);
-    else KVQ_WAIT_VM(0);
+    KVQ_WAIT_VM(0);  // this pair's V copies, the youngest in flight
     uint32_t vw[2][2][8];  // [channel c0 | c1][page][word]
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -1922,7 +1911,7 @@ __device__ void int4tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
       dst[0] = vv.x, dst[1] = vv.y, dst[2] = vv.z, dst[3] = vv.w;
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (has_next) W.issue_v(pnext);
+    if (has_next) issue_k(pnext);
     int accv[2][GQ][4];
     value_dots_seq<GQ>(W.pdig, vw, accv);
 
@@ -1939,6 +1928,7 @@ __device__ void int4tok_unit_dot8(Lds& L, const DecodeArgs& a, int b, int h, int
       m[hh] = mnew;
     }
     wave_lds_sync();
+    pcur = pnext;
   }
   if (wc) {
     if (pb < npairs && chunk_id < g.n_units - 1) store_wave_partial<GQ>(a, b, h, 1 + chunk_id, lane, m, l, o, c0, c1);
