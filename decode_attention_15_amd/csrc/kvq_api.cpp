@@ -31,7 +31,8 @@ int check_config(const kvq_config* c) {
   if (c->decode_impl != KVQ_DECODE_AUTO && c->decode_impl != KVQ_DECODE_F32 && c->decode_impl != KVQ_DECODE_MFMA &&
       c->decode_impl != KVQ_DECODE_DOT16 && c->decode_impl != KVQ_DECODE_DOT8)
     return KVQ_EINVAL;
-  if (c->decode_impl == KVQ_DECODE_MFMA) return KVQ_EUNSUPPORTED;
+  // the matrix-core decode is built for INT2 per channel
+  if (c->decode_impl == KVQ_DECODE_MFMA && c->scheme != KVQ_INT2_CHANNEL) return KVQ_EUNSUPPORTED;
   // nibble digits for INT4 per token walk page pairs: an explicit split must hold whole pairs
   if (c->decode_impl == KVQ_DECODE_DOT8 && c->scheme == KVQ_INT4_TOKEN && c->split_tokens % (2 * PAGE) != 0)
     return KVQ_EUNSUPPORTED;
@@ -322,7 +323,8 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
                     (cfg->decode_impl == KVQ_DECODE_AUTO && (is_grouped(cfg->scheme) || per % 2 == 0));
   // an explicit split on the nibble-digit path: one chunk per wave (a work-group takes four), so that every
   // wave walks several groups with its copies in flight, with one partial per chunk as with any split
-  a.g.wave_chunks = (cfg->split_tokens > 0 && dot8) ? 1 : 0;
+  const bool mfma = cfg->decode_impl == KVQ_DECODE_MFMA;
+  a.g.wave_chunks = (cfg->split_tokens > 0 && (dot8 || mfma)) ? 1 : 0;
   a.pages = static_cast<const uint8_t*>(cache->pages);
   a.band = static_cast<const uint16_t*>(cache->band);
   a.page_table = cache->page_table;
@@ -337,7 +339,7 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
   a.qrot = ws;
   a.qband = ws + nq * D;
   a.partials = ws + 2 * nq * D;
-  a.impl = dot8 ? KVQ_DECODE_DOT8 : cfg->decode_impl;
+  a.impl = mfma ? KVQ_DECODE_MFMA : dot8 ? KVQ_DECODE_DOT8 : cfg->decode_impl;
   clear_stale_error();
   return to_status(launch_decode(a, stages, stream), "kv_decode_attn");
 }

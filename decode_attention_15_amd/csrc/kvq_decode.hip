@@ -142,10 +142,33 @@ __global__ __launch_bounds__(512) void qprep_kernel(DecodeArgs a) {
 // unit u >= 1 = quantized chunk u-1.  Each of the 4 waves walks its own groups/pages with an
 // online softmax; the waves are merged in LDS and one partial (m, l, o[128]) per q head written.
 // ---------------------------------------------------------------------------------------------
-// STG: code staging per wave and group in units of 4 KB (2 for 4-bit per-channel codes)
-template <int GQ, int STG = 1>
+// Per-wave LDS of the matrix-core INT2 unit: key and value codes of a group (4 KB each), the metadata of
+// two groups (double-buffered, 1 KB each), and the two operand planes it builds per group, each with rows
+// (head, limb) of 128 bytes in k order (stride 144: consecutive rows start in different banks) and a last
+// row that stays zero for the matrix rows no head fills.
+template <int GQ>
+struct MfmaWave {
+  static constexpr int ROWS = 2 * GQ;
+  static constexpr int RSTRIDE = 144;
+  uint4 kst[256];
+  uint4 vst[256];
+  uint4 mst[2][64];
+  uint8_t aplane[(ROWS + 1) * RSTRIDE];
+  uint8_t wplane[(ROWS + 1) * RSTRIDE];
+};
+template <int GQ, bool MF>
+struct MfmaLds {};
+template <int GQ>
+struct MfmaLds<GQ, true> {
+  MfmaWave<GQ> w[4];
+};
+
+// STG: code staging per wave and group in units of 4 KB (2 for 4-bit per-channel codes); MF: the
+// matrix-core unit's buffers
+template <int GQ, int STG = 1, bool MF = false>
 struct DecodeLds {
   union {
+    MfmaLds<GQ, MF> mf;
     struct {                     // band unit, fp32 INT2 path, INT4 path
       float qband[GQ][D];
       float alpha[4][GQ][D];     // per wave: alpha (INT2) / rotated query (INT4)
@@ -163,19 +186,9 @@ struct DecodeLds {
   float cl[4][GQ];
 };
 
+// The four waves' partials (m, l, o in L.co/cm/cl) combined into the work-group's partial of `unit`.
 template <int GQ, typename Lds>
-__device__ void combine_and_store(Lds& L, const DecodeArgs& a, int b, int h, int unit, int wave, int lane,
-                                  const float (&m)[GQ], const float (&l)[GQ], const float (&o)[GQ][2], int c0, int c1) {
-  __syncthreads();  // co shares its LDS with the walks' buffers
-#pragma unroll
-  for (int hh = 0; hh < GQ; ++hh) {
-    L.co[wave][hh][c0] = o[hh][0];
-    L.co[wave][hh][c1] = o[hh][1];
-    if (lane == 0) {
-      L.cm[wave][hh] = m[hh];
-      L.cl[wave][hh] = l[hh];
-    }
-  }
+__device__ void combine_waves(Lds& L, const DecodeArgs& a, int b, int h, int unit) {
   __syncthreads();
   const Geo& g = a.g;
   for (int e = threadIdx.x; e < GQ * D; e += kThreads) {
@@ -197,6 +210,22 @@ __device__ void combine_and_store(Lds& L, const DecodeArgs& a, int b, int h, int
       part[1] = lsum;
     }
   }
+}
+
+template <int GQ, typename Lds>
+__device__ void combine_and_store(Lds& L, const DecodeArgs& a, int b, int h, int unit, int wave, int lane,
+                                  const float (&m)[GQ], const float (&l)[GQ], const float (&o)[GQ][2], int c0, int c1) {
+  __syncthreads();  // co shares its LDS with the walks' buffers
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh) {
+    L.co[wave][hh][c0] = o[hh][0];
+    L.co[wave][hh][c1] = o[hh][1];
+    if (lane == 0) {
+      L.cm[wave][hh] = m[hh];
+      L.cl[wave][hh] = l[hh];
+    }
+  }
+  combine_waves<GQ>(L, a, b, h, unit);
 }
 
 // Partial of one wave's own chunk (wave chunks): no combination with the other waves of the work-group.
@@ -2263,10 +2292,378 @@ __device__ void int4_unit(Lds& L, const DecodeArgs& a, int b, int h, int T, int 
   combine_and_store<GQ>(L, a, b, h, 1 + chunk, wave, lane, m, l, o, lane, lane + 64);
 }
 
-// MODE: 0 fp32, 1 16-bit on the byte dot product, 2 16-bit on the nibble dot product (grouped schemes)
+// ---------------------------------------------------------------------------------------------
+// INT2 per-channel chunk on the int8 matrix cores (v_mfma_i32_16x16x64_i8).  The fixed-point algebra is
+// that of int2_unit_dot16: per group and head the key-side operand a = rint(alpha 32639 / max|alpha|),
+// alpha = q~ s, and the softmax weights u = rint(32511 p), p = 2^(logit - group max), each as two signed
+// byte limbs 256 hi + lo; with A = max|alpha| / 32639,
+//   logit_t = A (sum_c a_c code_tc - sum_c a_c z_c),
+//   o~_c   += (2^(group max - m) / 32511) s_c (sum_t u_t code_tc - z_c sum_t u_t).
+// Both sums are 16 x 16 x 64 matrix products whose rows are (head, limb) pairs, so the GQA heads that share
+// the kv head also share one pass over the codes ([SAW] App. A.4 eq. 13-14; [NOVA] §2 query groups):
+//   keys    D[(head, limb)][token]   = sum_channels limb(a) code, 8 token tiles x 2 channel halves;
+//   values  D[(head, limb)][channel] = sum_tokens limb(u) code, 8 channel tiles x 2 pages;
+// and sum_t u_t is one more product against a vector of ones.  The limbs are exact int32 sums and the
+// codes stay 2-bit in HBM: each 32-bit code word becomes four int8 vectors, (w >> 2n) & 0x03030303.
+// Matrix rows: head h, limb L at row 4 h + L (GQ <= 4; rows with L >= 2 are zero) or 2 h + L (GQ = 8).
+// Operand layouts (lane l, q = l / 16, c = l % 16): A row c, k = 16 q + byte; B the same k, column c;
+// D column c, rows 4 q + r.  So a lane's key results (head(s) of rows 4 q.., token column c) are its
+// weights' producer lane, and its value results hold head q's channels c + 16 tau.
+//  - key k order (k = 64 sigma + 16 q + 4 n + b): channel 16 (2 q + sigma) + 4 b + n, i.e. lane q expands
+//    code words 2 q, 2 q + 1 of a token (channel 16 m + 4 b + n in byte b, bits 2 n);
+//  - value k order (k = 64 kappa + 16 q + 4 n + b): token 64 kappa + 16 b + 4 q + n of page kappa, i.e. lane
+//    q expands code word q of a channel (token 16 b + 4 q + n in byte b, bits 2 n);
+//  - key tile i, column c: token T(i, c) = 64 (c / 8) + 2 (c % 8) + 16 (i % 4) + i / 4, the token at value
+//    position 8 c + i, so each lane stores its 8 weights of a head as 8 consecutive bytes of the weight plane.
+// Key codes are staged with their rows permuted (token t at row t ^ ((t >> 2) & 3)) so that the 8-byte
+// operand reads of a tile spread over all LDS banks.  All global reads are LDS copies issued one
+// group ahead (metadata, keys, values, in that order), with waits that count the copies.
+// ---------------------------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(4))) int mf_i32x4;
+
+__device__ __forceinline__ mf_i32x4 mfma_i8x64(mf_i32x4 a, mf_i32x4 b, mf_i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+// 16 2-bit codes as 16 int8 values: dword n holds field n of every byte
+__device__ __forceinline__ mf_i32x4 codes_i8(uint32_t w) {
+  return mf_i32x4{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
+                  (int)((w >> 6) & 0x03030303u)};
+}
+__device__ __forceinline__ mf_i32x4 u4_i32x4(uint4 v) { return mf_i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}; }
+// lo + 256 hi of two int32 limb sums (two's complement)
+__device__ __forceinline__ int limbs_sum(int lo, int hi) {
+  int r;
+  asm("v_lshl_add_u32 %0, %1, 8, %2" : "=v"(r) : "v"(hi), "v"(lo));
+  return r;
+}
+// Magic rounding with the limb bias: fp32(x + 1.5 * 2^23 + 128) has rint(x) + 128 in the low half of its
+// encoding (|x| <= 32639), whose low byte xor 0x80 is the signed limb lo = x mod 256 and whose high byte is
+// hi = (x + 128) >> 8 in [-128, 127].
+constexpr float kRoundL = 12582912.0f + 128.0f;
+__device__ __forceinline__ void limbs4(float e0, float e1, float e2, float e3, uint32_t& lo, uint32_t& hi) {
+  const uint32_t p01 = pack_lo16(e0, e1), p23 = pack_lo16(e2, e3);
+  lo = __builtin_amdgcn_perm(p23, p01, 0x06040200u) ^ 0x80808080u;
+  hi = __builtin_amdgcn_perm(p23, p01, 0x07050301u);
+}
+// key k position -> channel (see the k order above)
+__host__ __device__ constexpr int mf_key_channel(int Q) {
+  return 16 * (2 * ((Q & 63) >> 4) + (Q >> 6)) + 4 * (Q & 3) + ((Q & 15) >> 2);
+}
+
+template <int GQ, typename Lds>
+__device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
+  constexpr int LG = HeadLog2<GQ>::v;
+  constexpr int LPH = 64 >> LG;        // lanes per head in the alpha step
+  constexpr int NCH = 2 * GQ;          // key positions per lane in the alpha step
+  constexpr int RPH = GQ == 8 ? 2 : 4;  // matrix rows per head
+  constexpr int HPL = GQ == 8 ? 2 : 1;  // heads per lane in the results
+  constexpr int ROWS = 2 * GQ;
+  constexpr int RS = MfmaWave<GQ>::RSTRIDE;
+  const Geo& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ng = n_groups_of(T, g.S0, g.W);
+  const bool wc = g.wave_chunks != 0;
+  const int chunk_id = wc ? 4 * chunk + wave : chunk;
+  const int g_begin = chunk_id * g.gpc;
+  int g_end = (g_begin + g.gpc) < ng ? (g_begin + g.gpc) : ng;
+  if (g_end > g.max_pages / 2) g_end = g.max_pages / 2;  // never index past the page-table row
+  const int gstep = wc ? 1 : 4;
+  const int g_first = wc ? g_begin : g_begin + wave;
+  MfmaWave<GQ>& W = L.mf.w[wave];
+  const int q4 = lane >> 4, c = lane & 15;
+
+  // the rows no head fills read the zero row of each plane
+  if (lane < 32) {
+    reinterpret_cast<uint32_t*>(W.aplane + ROWS * RS)[lane] = 0u;
+    reinterpret_cast<uint32_t*>(W.wplane + ROWS * RS)[lane] = 0u;
+  }
+  // A-operand row of this lane: matrix row c = (head, limb)
+  const int rh = c / RPH, rl = c % RPH;
+  const int prow = (rl < 2 && rh < GQ) ? 2 * rh + rl : ROWS;
+  const uint8_t* a_rd = W.aplane + prow * RS + 16 * q4;
+  const uint8_t* w_rd = W.wplane + prow * RS + 16 * q4;
+  // key operand reads: tile i at staged row 64 (c / 8) + 4 ((c / 2) % 4) + 16 (i % 4) + (y0 ^ (i / 4))
+  const int y0 = (2 * (c & 1)) ^ ((c >> 1) & 3);
+  const int krow = 64 * (c >> 3) + 4 * ((c >> 1) & 3);
+  const uint8_t* k_rd0 = reinterpret_cast<const uint8_t*>(W.kst) + 32 * (krow + y0) + 8 * q4;
+  const uint8_t* k_rd1 = reinterpret_cast<const uint8_t*>(W.kst) + 32 * (krow + (y0 ^ 1)) + 8 * q4;
+  // value operand reads: channel c + 16 tau, code word q4, page kappa
+  const uint32_t* v_rd = reinterpret_cast<const uint32_t*>(W.vst) + 4 * c + q4;
+  // alpha step: head ah, key positions Q0 .. Q0 + NCH - 1
+  const int ah = lane >> (6 - LG);
+  const int Q0 = (lane & (LPH - 1)) * NCH;
+  // copies: per-lane offsets of the permuted key rows (copy j: page j / 2, 16-byte slots 64 j + lane, i.e.
+  // half lane % 2 of staged row 32 (j % 2) + lane / 2 of that page)
+  uint32_t koff[2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int tl = 32 * jj + ((lane >> 1) ^ ((lane >> 3) & 3));
+    koff[jj] = (uint32_t)(tl * 32 + 16 * (lane & 1));
+  }
+  const uint32_t kst_a = lds_addr(W.kst), vst_a = lds_addr(W.vst);
+  const uint32_t mst_a0 = lds_addr(W.mst[0]), mst_a1 = lds_addr(W.mst[1]);
+  const uint8_t* pages = a.pages;
+  const long long pbytes = g.page_bytes, hoff = (long long)h * g.head_bytes;
+  auto page_of = [&](int idx) { return pages + (long long)idx * pbytes + hoff; };
+  auto issue_m = [&](int2 p, int buf) {
+    const uint8_t* src = (lane >= 32 ? page_of(p.y) : page_of(p.x)) + I2_META_OFF + (lane & 31) * 16;
+    dma16(buf ? mst_a1 : mst_a0, src);
+  };
+  auto issue_k = [&](int2 p) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16_base(kst_a + 1024 * j, page_of(j < 2 ? p.x : p.y) + I2_K_OFF, koff[j & 1]);
+  };
+  auto issue_v = [&](int2 p) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dma16_base(vst_a + 1024 * j, page_of(j < 2 ? p.x : p.y) + I2_V_OFF + (j & 1) * 1024, lane * 16);
+  };
+
+  float qa[NCH];
+  {
+    const float* q = a.qrot + ((long long)b * g.n_q + h * GQ + ah) * D;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) qa[i] = q[mf_key_channel(Q0 + i)];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) asm volatile("" ::"v"(qa[i]));  // the loads' wait stays before the walk
+  }
+  float m[HPL], l[HPL], o[HPL][8];
+#pragma unroll
+  for (int e = 0; e < HPL; ++e) {
+    m[e] = -INFINITY;
+    l[e] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) o[e][t] = 0.0f;
+  }
+  const int2* pt = reinterpret_cast<const int2*>(a.page_table + (long long)b * g.max_pages);
+  int2 pcur = make_int2(0, 0), pnext = make_int2(0, 0);
+  int mb = 0;
+  if (g_first < g_end) {
+    pcur = scalar_load_int2(pt + g_first);
+    issue_m(pcur, 0);
+    issue_k(pcur);
+    issue_v(pcur);
+  }
+  wave_lds_sync();
+  const mf_i32x4 zero4 = {0, 0, 0, 0};
+  const mf_i32x4 ones4 = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+  for (int gi = g_first; gi < g_end; gi += gstep) {
+    const bool has_next = gi + gstep < g_end;  // uniform
+    if (has_next) pnext = scalar_load_int2(pt + gi + gstep);
+    KVQ_WAIT_VM(8);  // this group's metadata (its key and value copies may be in flight)
+    const uint16_t* ms = reinterpret_cast<const uint16_t*>(W.mst[mb]);
+    // 1. key-side operand of head ah at positions Q0 + i: alpha = q~ s, rounded to 16 bits, two limbs
+    float Ah, AZh;
+    {
+      float al[NCH], zk[NCH];
+      if constexpr (NCH >= 8) {
+        // positions i and i + 4 (i % 8 < 4) are channels ch, ch + 1 with ch even: one word per pair
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          if ((i & 4) == 0) {
+            const int ch = mf_key_channel(Q0 + i);
+            const uint32_t sw = reinterpret_cast<const uint32_t*>(ms)[ch >> 1];
+            const uint32_t zw = reinterpret_cast<const uint32_t*>(ms + D)[ch >> 1];
+            al[i] = qa[i] * __uint_as_float(sw << 16);
+            al[i + 4] = qa[i + 4] * __uint_as_float(sw & 0xffff0000u);
+            zk[i] = __uint_as_float(zw << 16);
+            zk[i + 4] = __uint_as_float(zw & 0xffff0000u);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const int ch = mf_key_channel(Q0 + i);
+          al[i] = qa[i] * bf16_to_f32(ms[ch]);
+          zk[i] = bf16_to_f32(ms[D + ch]);
+        }
+      }
+      int amx_i = 0;  // max |alpha| as its bit pattern (non-negative floats order as their bits)
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) amx_i = max(amx_i, __float_as_int(fabsf(al[i])));
+      const float amx = __int_as_float(seg_max_i<LPH>(amx_i));
+      // |rint(alpha inv)| <= 32639: the reciprocal's 1-ulp error cannot carry the largest past 32639.5
+      const float inv = amx > 0x1p-100f ? kAScale * __builtin_amdgcn_rcpf(amx) : 0.0f;
+      float ev[NCH];
+      float zs = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        ev[i] = fmaf(al[i], inv, kRoundL);
+        zs = fmaf(ev[i] - kRoundL, zk[i], zs);  // sum_c a_c z_c with the rounded a
+      }
+      zs = seg_sum<LPH>(zs);
+      Ah = amx * (1.0f / kAScale);
+      AZh = Ah * zs;
+      uint8_t* dst0 = W.aplane + (2 * ah) * RS + Q0;
+      uint8_t* dst1 = dst0 + RS;
+      if constexpr (NCH >= 4) {
+        uint32_t lo[NCH / 4], hi[NCH / 4];
+#pragma unroll
+        for (int k = 0; k < NCH / 4; ++k) limbs4(ev[4 * k], ev[4 * k + 1], ev[4 * k + 2], ev[4 * k + 3], lo[k], hi[k]);
+        if constexpr (NCH == 16) {
+          *reinterpret_cast<uint4*>(dst0) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+          *reinterpret_cast<uint4*>(dst1) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        } else if constexpr (NCH == 8) {
+          *reinterpret_cast<uint2*>(dst0) = make_uint2(lo[0], lo[1]);
+          *reinterpret_cast<uint2*>(dst1) = make_uint2(hi[0], hi[1]);
+        } else {
+          *reinterpret_cast<uint32_t*>(dst0) = lo[0];
+          *reinterpret_cast<uint32_t*>(dst1) = hi[0];
+        }
+      } else {
+        uint32_t lo, hi;
+        limbs4(ev[0], ev[1], ev[0], ev[1], lo, hi);
+        *reinterpret_cast<uint16_t*>(dst0) = (uint16_t)lo;
+        *reinterpret_cast<uint16_t*>(dst1) = (uint16_t)hi;
+      }
+    }
+    // per-head scales of this lane's result heads (head q4 HPL + e is the alpha step's lanes (q4 HPL + e) LPH)
+    float Ae[HPL], AZe[HPL];
+#pragma unroll
+    for (int e = 0; e < HPL; ++e) {
+      const int src = ((q4 * HPL + e) & (GQ - 1)) * LPH;
+      Ae[e] = __shfl(Ah, src, 64);
+      AZe[e] = __shfl(AZh, src, 64);
+    }
+    if (has_next) issue_m(pnext, mb ^ 1);
+    wave_lds_sync();
+
+    // 2. key products: 8 token tiles x 2 channel halves
+    if (has_next) KVQ_WAIT_VM(5);  // this group's key copies (its value copies and the next metadata follow)
+    else KVQ_WAIT_VM(4);
+    uint2 kw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      kw[i] = *reinterpret_cast<const uint2*>((i < 4 ? k_rd0 : k_rd1) + 512 * (i & 3));
+    const mf_i32x4 A0 = u4_i32x4(*reinterpret_cast<const uint4*>(a_rd));
+    const mf_i32x4 A1 = u4_i32x4(*reinterpret_cast<const uint4*>(a_rd + 64));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (has_next) issue_k(pnext);
+    mf_i32x4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc[i] = mfma_i8x64(A0, codes_i8(kw[i].x), zero4);
+      acc[i] = mfma_i8x64(A1, codes_i8(kw[i].y), acc[i]);
+    }
+
+    // 3. logits logit = A val - AZ; the group maximum is that of the integer sums (A >= 0); weights
+    //    u = rint(32511 2^(A (val - val_max))) as limbs at positions 8 c + i of the weight plane
+    float mg[HPL];
+#pragma unroll
+    for (int e = 0; e < HPL; ++e) {
+      int v[8];
+      int vmx = (int)0x80000000u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[i] = limbs_sum(acc[i][2 * e], acc[i][2 * e + 1]);
+        vmx = max(vmx, v[i]);
+      }
+      vmx = seg_max_i<16>(vmx);
+      const float ref = Ae[e] * (float)vmx;
+      mg[e] = ref - AZe[e];
+      float ew[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ew[i] = fmaf(__builtin_amdgcn_exp2f(fmaf(Ae[e], (float)v[i], -ref)), kPScale, kRoundL);
+      uint32_t lo0, hi0, lo1, hi1;
+      limbs4(ew[0], ew[1], ew[2], ew[3], lo0, hi0);
+      limbs4(ew[4], ew[5], ew[6], ew[7], lo1, hi1);
+      const int he = q4 * HPL + e;
+      if (he < GQ) {
+        uint8_t* dst = W.wplane + (2 * he) * RS + 8 * c;
+        *reinterpret_cast<uint2*>(dst) = make_uint2(lo0, lo1);
+        *reinterpret_cast<uint2*>(dst + RS) = make_uint2(hi0, hi1);
+      }
+    }
+    wave_lds_sync();
+
+    // 4. value products: 8 channel tiles x 2 pages, and the weight sums
+    if (has_next) KVQ_WAIT_VM(5);  // this group's value copies (the next metadata and keys follow)
+    else KVQ_WAIT_VM(0);
+    uint32_t vw[8][2];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      vw[t][0] = v_rd[64 * t];
+      vw[t][1] = v_rd[512 + 64 * t];
+    }
+    const mf_i32x4 W0 = u4_i32x4(*reinterpret_cast<const uint4*>(w_rd));
+    const mf_i32x4 W1 = u4_i32x4(*reinterpret_cast<const uint4*>(w_rd + 64));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (has_next) issue_v(pnext);
+    mf_i32x4 accp = mfma_i8x64(W0, ones4, zero4);
+    accp = mfma_i8x64(W1, ones4, accp);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      acc[t] = mfma_i8x64(W0, codes_i8(vw[t][0]), zero4);
+      acc[t] = mfma_i8x64(W1, codes_i8(vw[t][1]), acc[t]);
+    }
+
+    // 5. online-softmax update in the rotated value frame (o and l carry the weights' factor 32511)
+#pragma unroll
+    for (int e = 0; e < HPL; ++e) {
+      const float Pf = (float)limbs_sum(accp[2 * e], accp[2 * e + 1]);
+      const float mnew = fmax_raw(m[e], mg[e]);
+      const float sc = __builtin_amdgcn_exp2f(m[e] - mnew);  // 0 before the first group (m = -inf)
+      const float eg = __builtin_amdgcn_exp2f(mg[e] - mnew);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int ch = c + 16 * t;
+        const float sv = bf16_to_f32(ms[2 * D + ch]), zv = bf16_to_f32(ms[3 * D + ch]);
+        const float Y = fmaf(-zv, Pf, (float)limbs_sum(acc[t][2 * e], acc[t][2 * e + 1]));
+        o[e][t] = fmaf(eg * sv, Y, o[e][t] * sc);
+      }
+      l[e] = fmaf(eg, Pf, l[e] * sc);
+      m[e] = mnew;
+    }
+    mb ^= 1;
+    pcur = pnext;
+  }
+#pragma unroll
+  for (int e = 0; e < HPL; ++e) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) o[e][t] *= 1.0f / kPScale;
+    l[e] *= 1.0f / kPScale;
+  }
+  if (wc) {
+    // every partial a merge reads is written; chunks past the length or the launch bound have none
+    if (g_begin < ng && chunk_id < g.n_units - 1) {
+#pragma unroll
+      for (int e = 0; e < HPL; ++e) {
+        const int he = q4 * HPL + e;
+        if (he < GQ) {
+          float* part = a.partials + (((long long)b * g.n_q + h * GQ + he) * g.n_units + 1 + chunk_id) * PART_STRIDE;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) part[2 + c + 16 * t] = o[e][t];
+          if (c == 0) {
+            part[0] = m[e];
+            part[1] = l[e];
+          }
+        }
+      }
+    }
+  } else {
+    __syncthreads();  // co shares its LDS with the walks' buffers
+#pragma unroll
+    for (int e = 0; e < HPL; ++e) {
+      const int he = q4 * HPL + e;
+      if (he < GQ) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) L.co[wave][he][c + 16 * t] = o[e][t];
+        if (c == 0) {
+          L.cm[wave][he] = m[e];
+          L.cl[wave][he] = l[e];
+        }
+      }
+    }
+    combine_waves<GQ>(L, a, b, h, 1 + chunk);
+  }
+}
+
+// MODE: 0 fp32, 1 16-bit on the byte dot product, 2 16-bit on the nibble dot product (grouped schemes),
+// 3 16-bit on the int8 matrix cores (INT2 per channel)
 template <int GQ, int SCHEME, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
-  __shared__ DecodeLds<GQ, (SCHEME == KVQ_INT4_CHANNEL || (SCHEME == KVQ_INT4_TOKEN && MODE == 2)) ? 2 : 1> L;
+  __shared__ DecodeLds<GQ, (SCHEME == KVQ_INT4_CHANNEL || (SCHEME == KVQ_INT4_TOKEN && MODE == 2)) ? 2 : 1, MODE == 3> L;
   const int unit = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const Geo& g = a.g;
   const int T = a.seq_lens[b];
@@ -2296,7 +2693,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   } else if constexpr (SCHEME == KVQ_INT2_TOKEN) {
     int2tok_unit_dot8<GQ>(L, a, b, h, T, unit - 1);
   } else if constexpr (SCHEME == KVQ_INT2_CHANNEL) {
-    if constexpr (MODE == 2) int2_unit_dot8<GQ, 2>(L, a, b, h, T, unit - 1);
+    if constexpr (MODE == 3) int2_unit_mfma<GQ>(L, a, b, h, T, unit - 1);
+    else if constexpr (MODE == 2) int2_unit_dot8<GQ, 2>(L, a, b, h, T, unit - 1);
     else if constexpr (MODE == 1) int2_unit_dot16<GQ>(L, a, b, h, T, unit - 1);
     else int2_unit<GQ>(L, a, b, h, T, unit - 1);
   } else {
@@ -2483,7 +2881,8 @@ hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
     } else if (g.scheme == KVQ_INT2_TOKEN) {
       hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_TOKEN, 2>), grid, block, 0, s, a);
     } else if (g.scheme == KVQ_INT2_CHANNEL) {
-      if (a.impl == KVQ_DECODE_F32) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 0>), grid, block, 0, s, a);
+      if (a.impl == KVQ_DECODE_MFMA) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 3>), grid, block, 0, s, a);
+      else if (a.impl == KVQ_DECODE_F32) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 0>), grid, block, 0, s, a);
       else if (a.impl == KVQ_DECODE_DOT16) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 1>), grid, block, 0, s, a);
       else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 2>), grid, block, 0, s, a);
     } else {

@@ -37,12 +37,12 @@ class _BC:
         self.wl, self.cache = wl, cache
 
 
-def _write_and_check(K, wl, kb, vb, clip=(0.96, 0.92), chunks=None, decode=True):
+def _write_and_check(K, wl, kb, vb, clip=(0.96, 0.92), chunks=None, decode=True, decode_impl=0):
     """Write bf16 K/V [T, n_kv, 128] for one sequence, compare every group, the band and the decode output."""
     import torch
     T = kb.shape[0]
     wl = synth.scaled(wl, batch=1, clip_k=clip[0], clip_v=clip[1])
-    cfg = config_for(K, wl)
+    cfg = config_for(K, wl, 0, decode_impl)
     rk, rv = rotations(wl)
     max_pages = max(1, K.pages_for_len(cfg, T))
     pt, n_pool = synth.page_table(wl, max_pages, max_pages + 2)
@@ -290,3 +290,40 @@ def test_int4_token_dense_rotation(K):
     k, v = _int4_tokens(T, 15), _int4_tokens(T, 16)
     _say("int4 per token, dense rotation")
     _int4_write_and_check(K, synth.scaled(SAW, rotation="oscar"), _bf16(k), _bf16(v), [64, 5, 264])
+
+
+# ------------------------------------------------------------------ the matrix-core INT2 decode
+
+
+def test_matrix_core_decode_zero_and_constant_groups(K):
+    """All-zero groups (alpha = 0 for every channel: every logit of the group equal) and constant tokens
+    (every code equal) on the matrix-core decode."""
+    T = 4 + 128 + 3 * 128 + 50
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((T, 2, 128)).astype(np.float32)
+    v = rng.standard_normal((T, 2, 128)).astype(np.float32)
+    k[4:132] = 0.0
+    v[4:132] = 0.0
+    k[132:260, 0, :] = 0.75
+    v[132:260, 1, :] = -2.0
+    _say("matrix-core decode: all-zero group, constant tokens")
+    _write_and_check(K, WL, _bf16(k), _bf16(v), decode_impl=K.DECODE_MFMA)
+
+
+def test_matrix_core_decode_no_clip_wide_range(K):
+    T = 4 + 128 + 2 * 128 + 1
+    rng = np.random.default_rng(7)
+    k = (rng.standard_normal((T, 2, 128)) * 3).astype(np.float32)
+    v = rng.standard_normal((T, 2, 128)).astype(np.float32)
+    _say("matrix-core decode: clip ratio 1, keys x3")
+    _write_and_check(K, WL, _bf16(k), _bf16(v), clip=(1.0, 1.0), decode_impl=K.DECODE_MFMA)
+
+
+@pytest.mark.parametrize("T", [1, 5, 132, 259, 260, 261, 387, 388, 389, 516, 517])
+def test_matrix_core_decode_boundary_lengths(K, T):
+    rng = np.random.default_rng(100 + T)
+    k = rng.standard_normal((T, 2, 128)).astype(np.float32)
+    v = rng.standard_normal((T, 2, 128)).astype(np.float32)
+    _say(f"matrix-core decode: boundary length T={T}")
+    chunks = [1] * T if T < 8 else [T // 3, T - T // 3]
+    _write_and_check(K, WL, _bf16(k), _bf16(v), chunks=chunks, decode_impl=K.DECODE_MFMA)

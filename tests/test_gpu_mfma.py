@@ -1,0 +1,125 @@
+"""GPU parity of the matrix-core INT2 decode (DECODE_MFMA): the split-K kernel's per-group sums over
+channels and tokens on v_mfma_i32_16x16x64_i8 with 16-bit two-limb operands, against the fp64 oracle on
+the same seeded caches (bar 2e-3), and against the fp32 and nibble-digit decodes of the same cache.
+
+Cases span every GQA ratio the kernel lays out differently (1, 2 and 4: four matrix rows per head; 8: two),
+both chunk layouts (automatic chunks shared by a work-group's four waves and merged in LDS; explicit
+splits walked one chunk per wave), ragged and empty sequences, appends that demote groups, and the
+batch-32 x 32k and 4 x 131k shapes at full size (sampled heads).
+"""
+import numpy as np
+import pytest
+
+import synth
+from kvq_cases import TOL, _host, _say, build_cache, check_int2, check_out, run_decode
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import decode_attention_15_amd as K
+    return K
+
+
+def _case(K, wl, lens, heads, append_steps=0, chunk=None, split=0, check_codes=True):
+    bc = build_cache(K, wl, lens, append_steps=append_steps, chunk=chunk, split_tokens=split,
+                     decode_impl=K.DECODE_MFMA)
+    if check_codes:
+        pages, band = _host(bc)
+        for b in range(len(lens)):
+            if lens[b]:
+                for h in heads:
+                    check_int2(bc, b, h, pages=pages, band=band)
+    q = synth.queries(synth.scaled(wl, batch=len(lens)))
+    out = run_decode(K, bc, q)
+    worst = check_out(bc, out, q, [(b, h) for b in range(len(lens)) for h in range(wl.n_kv_heads)])
+    _say(f"   worst |mfma - oracle| = {worst:.2e}")
+    return bc, q, out
+
+
+def test_mfma_single_head_fp32_source(K):
+    wl = synth.WORKLOADS["tiny_1h_4k"]
+    _say("mfma: tiny 1 head (GQA 1), T=4096, fp32 source with x10 outlier channels, 96 appends")
+    _case(K, wl, [4096], [0], append_steps=96)
+
+
+def test_mfma_gqa4_ragged_with_appends(K):
+    wl = synth.WORKLOADS["gqa_b1_32k"]
+    lens = [3000, 131, 700, 0, 260, 2051]
+    _say(f"mfma: GQA 4 ragged lens={lens}, 5 appends")
+    _case(K, wl, lens, [0, 3, 7], append_steps=5)
+
+
+def test_mfma_gqa2_ragged(K):
+    wl = synth.scaled(synth.WORKLOADS["gqa_b1_32k"], n_q_heads=16, n_kv_heads=8)
+    lens = [2900, 1000, 133, 0]
+    _say(f"mfma: GQA 2 lens={lens}, 3 appends")
+    _case(K, wl, lens, [0, 5], append_steps=3)
+
+
+@pytest.mark.parametrize("split", [0, 512])
+def test_mfma_gqa8_decaying_spectrum(K, split):
+    wl = synth.scaled(synth.WORKLOADS["long_b4_131k"], batch=2)
+    lens = [5000, 2222]
+    _say(f"mfma: GQA 8, sigma_c = (c+1)^-0.5, lens={lens}, split {split}")
+    _case(K, wl, lens, [0, 5], append_steps=3, split=split)
+
+
+@pytest.mark.parametrize("split", [128, 256, 1024])
+def test_mfma_gqa4_explicit_splits(K, split):
+    """Explicit splits: each wave walks a chunk of its own (one or more groups) and stores its partial."""
+    wl = synth.WORKLOADS["batch32_32k"]
+    lens = [4100, 2000, 260, 1029, 3000, 388, 9000]
+    _say(f"mfma: GQA 4 lens={lens}, split {split}, 800-token prefill chunks")
+    _case(K, wl, lens, [2], chunk=800, split=split, check_codes=False)
+
+
+def test_mfma_agrees_with_the_other_decodes(K):
+    """Same cache, three decodes: the matrix-core one within the oracle bar of the fp32 one, and of the
+    nibble-digit one (both round their per-group operands to 16 bits, differently)."""
+    for name, lens in (("tiny_1h_4k", [4096]), ("gqa_b1_32k", [2900, 1000]), ("long_b4_131k", [3000, 700])):
+        wl = synth.WORKLOADS[name]
+        bc = build_cache(K, wl, lens)
+        q = synth.queries(synth.scaled(wl, batch=len(lens)))
+        outs = {}
+        for nm, c in (("f32", K.DECODE_F32), ("dot8", K.DECODE_DOT8), ("mfma", K.DECODE_MFMA)):
+            bc.cfg.decode_impl = c
+            outs[nm] = run_decode(K, bc, q)
+        d32 = np.abs(outs["mfma"] - outs["f32"]).max()
+        d8 = np.abs(outs["mfma"] - outs["dot8"]).max()
+        _say(f"mfma vs f32 / dot8 on {name} lens={lens}: {d32:.2e} / {d8:.2e}")
+        assert d32 <= TOL and d8 <= TOL
+
+
+def test_mfma_is_deterministic(K):
+    wl = synth.WORKLOADS["gqa_b1_32k"]
+    bc = build_cache(K, wl, [2500, 900], decode_impl=K.DECODE_MFMA)
+    q = synth.queries(synth.scaled(wl, batch=2))
+    assert np.array_equal(run_decode(K, bc, q), run_decode(K, bc, q))
+
+
+def test_mfma_batch32_32k_full_sampled(K):
+    """The bench's workload at full size: 32 sequences x 32768 tokens, 32 q / 8 kv heads."""
+    wl = synth.WORKLOADS["batch32_32k"]
+    lens = synth.seq_lens(wl)
+    _say(f"mfma: batch32_32k full, lens {lens.min()}..{lens.max()}")
+    bc = build_cache(K, wl, lens, seqs_per_call=4, decode_impl=K.DECODE_MFMA)
+    q = synth.queries(wl)
+    out = run_decode(K, bc, q)
+    assert np.isfinite(out).all()
+    worst = check_out(bc, out, q, [(0, 0), (17, 5), (31, 7)])
+    _say(f"   worst |mfma - oracle| = {worst:.2e}")
+
+
+def test_mfma_long_b4_131k_full_sampled(K):
+    wl = synth.WORKLOADS["long_b4_131k"]
+    _say("mfma: long_b4_131k full, B=4, T=131072, split 512")
+    bc = build_cache(K, wl, [131072] * 4, split_tokens=512, seqs_per_call=1, decode_impl=K.DECODE_MFMA)
+    q = synth.queries(wl)
+    out = run_decode(K, bc, q)
+    assert np.isfinite(out).all()
+    worst = check_out(bc, out, q, [(2, 6)])
+    _say(f"   worst |mfma - oracle| = {worst:.2e}")

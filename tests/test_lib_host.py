@@ -78,7 +78,7 @@ def test_bits_per_element_match_the_pages():
     ("scheme", 7, K.KVQ_EUNSUPPORTED), ("rotation", 5, K.KVQ_EUNSUPPORTED),
     ("n_q_heads", 30, K.KVQ_EINVAL), ("n_kv_heads", 0, K.KVQ_EINVAL), ("clip_k", 0.0, K.KVQ_EINVAL),
     ("clip_v", 1.5, K.KVQ_EINVAL), ("split_tokens", 100, K.KVQ_EINVAL), ("n_sink", -1, K.KVQ_EINVAL),
-    ("decode_impl", 9, K.KVQ_EINVAL), ("decode_impl", 2, K.KVQ_EUNSUPPORTED),
+    ("decode_impl", 9, K.KVQ_EINVAL), ("decode_impl", -1, K.KVQ_EINVAL),
     ("key_only_rotation", 2, K.KVQ_EINVAL), ("key_only_rotation", -1, K.KVQ_EINVAL), ("scheme", 4, K.KVQ_EUNSUPPORTED),
 ])
 def test_config_validation(field, value, status):
@@ -157,6 +157,19 @@ def test_decode_implementations_accepted_for_both_schemes():
         assert K.check_config(cfg) == want
         cfg.decode_impl = K.DECODE_AUTO  # the automatic choice takes the fp32 path there instead
         assert K.check_config(cfg) == K.KVQ_OK
+
+
+def test_matrix_core_decode_is_built_for_int2_per_channel_only():
+    for scheme, rot, s0, w, ck, cv, want in (
+            (K.INT2_CHANNEL, K.ROT_DENSE, 4, 128, 0.96, 0.92, K.KVQ_OK),
+            (K.INT2_CHANNEL, K.ROT_HADAMARD, 4, 256, 0.96, 0.92, K.KVQ_OK),
+            (K.INT2_TOKEN, K.ROT_DENSE, 4, 128, 0.96, 0.92, K.KVQ_EUNSUPPORTED),
+            (K.INT4_CHANNEL, K.ROT_DENSE, 4, 128, 0.96, 0.92, K.KVQ_EUNSUPPORTED),
+            (K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0, K.KVQ_EUNSUPPORTED)):
+        for split in (0, 512):
+            cfg = K.make_config(8, 32, scheme=scheme, rotation=rot, n_sink=s0, n_recent=w, clip_k=ck, clip_v=cv,
+                                split_tokens=split, decode_impl=K.DECODE_MFMA)
+            assert K.check_config(cfg) == want, (scheme, split)
 
 
 def test_int2_token_scheme_config():
