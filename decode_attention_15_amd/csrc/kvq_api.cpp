@@ -63,6 +63,11 @@ void clip_params(float rho, int* j, float* f) {
   *f = (float)(h - fl);
 }
 
+// the matrix-core decode: asked for, or the automatic choice for INT2 per channel
+bool uses_mfma(const kvq_config* c) {
+  return c->decode_impl == KVQ_DECODE_MFMA || (c->decode_impl == KVQ_DECODE_AUTO && c->scheme == KVQ_INT2_CHANNEL);
+}
+
 // decode work split: groups (INT2) or pages (INT4) per chunk
 int chunk_units(const kvq_config* c, int batch, int max_seq_len) {
   if (c->split_tokens > 0) return c->split_tokens / (is_grouped(c->scheme) ? GROUP : PAGE);
@@ -70,6 +75,15 @@ int chunk_units(const kvq_config* c, int batch, int max_seq_len) {
   if (is_grouped(c->scheme)) units = n_groups_of(max_seq_len, c->n_sink, c->n_recent);
   else units = (max_seq_len + PAGE - 1) / PAGE;
   const int pairs = batch * c->n_kv_heads;
+  if (uses_mfma(c)) {
+    // one chunk per wave, long enough that a wave's copies stay in flight across many groups, short enough
+    // that the chunks of all (sequence, kv head) pairs fill the GPU about once: ~2048 wave chunks, a power
+    // of two from 1 to 32 groups
+    const long long total = (long long)pairs * units;
+    int per = 1;
+    while (per < 32 && (long long)per * 2048 < total) per *= 2;
+    return per;
+  }
   const int target_wgs = 2048;
   int chunks = (target_wgs + pairs - 1) / pairs;
   if (chunks < 1) chunks = 1;
@@ -319,12 +333,13 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
   a.g.n_units = 1 + max_chunks_of(cfg, max_seq_len_host, per);
   // the nibble-digit decode: every grouped scheme by default; INT4 per token by default when its chunks
   // hold whole page pairs
-  const bool dot8 = cfg->decode_impl == KVQ_DECODE_DOT8 ||
-                    (cfg->decode_impl == KVQ_DECODE_AUTO && (is_grouped(cfg->scheme) || per % 2 == 0));
+  const bool mfma = uses_mfma(cfg);
+  const bool dot8 = !mfma && (cfg->decode_impl == KVQ_DECODE_DOT8 ||
+                              (cfg->decode_impl == KVQ_DECODE_AUTO && (is_grouped(cfg->scheme) || per % 2 == 0)));
   // an explicit split on the nibble-digit path: one chunk per wave (a work-group takes four), so that every
   // wave walks several groups with its copies in flight, with one partial per chunk as with any split
-  const bool mfma = cfg->decode_impl == KVQ_DECODE_MFMA;
-  a.g.wave_chunks = (cfg->split_tokens > 0 && (dot8 || mfma)) ? 1 : 0;
+  // the matrix-core decode always walks one chunk per wave
+  a.g.wave_chunks = (mfma || (cfg->split_tokens > 0 && dot8)) ? 1 : 0;
   a.pages = static_cast<const uint8_t*>(cache->pages);
   a.band = static_cast<const uint16_t*>(cache->band);
   a.page_table = cache->page_table;

@@ -122,8 +122,13 @@ typedef enum { KVQ_ROT_DENSE = 0, KVQ_ROT_HADAMARD = 1 } kvq_rotation;
            scale 65535) in four 4-bit digits, on the 8-way nibble dot product; 2-bit codes unpack with a
            mask, 4-bit codes not at all (per-token schemes: the rotated query once per work-group).  INT4
            per token walks page pairs, so an explicit split_tokens must be a multiple of 128;
-   MFMA  - reserved, not built;  AUTO - DOT8 (INT4_TOKEN with a split of an odd number of pages: F32).
-   INT2_TOKEN and INT4_CHANNEL are built with DOT8 only (F32 and DOT16 return KVQ_EUNSUPPORTED for them). */
+   MFMA  - INT2_CHANNEL only: the DOT16 operands (key-side operand and softmax weights as 16-bit integers, two
+           signed bytes) multiplied with the 2-bit codes on the int8 matrix cores, 16 x 16 x 64 products whose
+           rows are (query head, byte limb) pairs, so the query heads of a kv head share one pass over the codes;
+           every wave walks a chunk of its own (split_tokens = 0: 1 to 32 groups per chunk, chosen by size);
+   AUTO  - MFMA for INT2_CHANNEL, DOT8 for the other schemes (INT4_TOKEN with a split of an odd number of
+           pages: F32).
+   INT2_TOKEN and INT4_CHANNEL are built with DOT8 only (F32, DOT16 and MFMA return KVQ_EUNSUPPORTED for them). */
 typedef enum {
   KVQ_DECODE_AUTO = 0,
   KVQ_DECODE_F32 = 1,
@@ -147,8 +152,9 @@ typedef struct {
   float clip_v;          /* rho_V in (0, 1] */
   int32_t split_tokens;  /* quantized tokens per decode chunk, each merged from one partial: a multiple of 128
                             (grouped schemes) or 64 (INT4_TOKEN), or 0 = chosen by size (one work-group per
-                            chunk).  Given explicitly on the nibble-digit decode, each wave of a work-group
-                            walks a chunk of its own and a work-group takes four. */
+                            chunk; one wave per chunk on the matrix-core decode).  Given explicitly on the
+                            nibble-digit or matrix-core decode, each wave of a work-group walks a chunk of its
+                            own and a work-group takes four. */
   int32_t decode_impl;   /* kvq_decode_impl */
   int32_t key_only_rotation;  /* 0: K and V rotated (V by R_V on write, outputs un-rotated by R_V^T);
                                  1: only K rotated ([SAW] App. C default), V kept in its own frame and
