@@ -2330,12 +2330,10 @@ __device__ __forceinline__ mf_i32x4 codes_i8(uint32_t w) {
                   (int)((w >> 6) & 0x03030303u)};
 }
 __device__ __forceinline__ mf_i32x4 u4_i32x4(uint4 v) { return mf_i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}; }
-// lo + 256 hi of two int32 limb sums (two's complement)
-__device__ __forceinline__ int limbs_sum(int lo, int hi) {
-  int r;
-  asm("v_lshl_add_u32 %0, %1, 8, %2" : "=v"(r) : "v"(hi), "v"(lo));
-  return r;
-}
+// lo + 256 hi of two int32 limb sums (two's complement).  Plain code, not inline assembly: its operands
+// are matrix-core results, and only instructions the compiler emits itself get the wait states that
+// reading those registers needs.
+__device__ __forceinline__ int limbs_sum(int lo, int hi) { return (int)((uint32_t)lo + ((uint32_t)hi << 8)); }
 // Magic rounding with the limb bias: fp32(x + 1.5 * 2^23 + 128) has rint(x) + 128 in the low half of its
 // encoding (|x| <= 32639), whose low byte xor 0x80 is the signed limb lo = x mod 256 and whose high byte is
 // hi = (x + 128) >> 8 in [-128, 127].
