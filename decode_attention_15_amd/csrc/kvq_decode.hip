@@ -142,8 +142,9 @@ __global__ __launch_bounds__(512) void qprep_kernel(DecodeArgs a) {
 // unit u >= 1 = quantized chunk u-1.  Each of the 4 waves walks its own groups/pages with an
 // online softmax; the waves are merged in LDS and one partial (m, l, o[128]) per q head written.
 // ---------------------------------------------------------------------------------------------
-// Per-wave LDS of the matrix-core INT2 unit: key and value codes of a group (4 KB each), the metadata of
-// two groups (double-buffered, 1 KB each), and the two operand planes it builds per group, each with rows
+// Per-wave LDS of the matrix-core INT2 unit: the key, then the value codes of a group (one 4 KB buffer),
+// the metadata of two groups (double-buffered, 1 KB each), and the two operand planes it builds per group,
+// each with rows
 // (head, limb) of 128 bytes in k order (stride 144: consecutive rows start in different banks) and a last
 // row that stays zero for the matrix rows no head fills.
 template <int GQ>
@@ -151,7 +152,6 @@ struct MfmaWave {
   static constexpr int ROWS = 2 * GQ;
   static constexpr int RSTRIDE = 144;
   uint4 kst[256];
-  uint4 vst[256];
   uint4 mst[2][64];
   uint8_t aplane[(ROWS + 1) * RSTRIDE];
   uint8_t wplane[(ROWS + 1) * RSTRIDE];
@@ -1106,7 +1106,7 @@ struct Dot8Wave {
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        dma16_base(vst_a + 1024 * j, page_of(j < 2 ? p.x : p.y) + I2_V_OFF + (j & 1) * 1024, lane * 16);
+        dma16_base(kst_a + 1024 * j, page_of(j < 2 ? p.x : p.y) + I2_V_OFF + (j & 1) * 1024, lane * 16);
     }
   }
 };
@@ -2316,8 +2316,9 @@ __device__ void int4_unit(Lds& L, const DecodeArgs& a, int b, int h, int T, int 
 //  - key tile i, column c: token T(i, c) = 64 (c / 8) + 2 (c % 8) + 16 (i % 4) + i / 4, the token at value
 //    position 8 c + i, so each lane stores its 8 weights of a head as 8 consecutive bytes of the weight plane.
 // Key codes are staged with their rows permuted (token t at row t ^ ((t >> 2) & 3)) so that the 8-byte
-// operand reads of a tile spread over all LDS banks.  All global reads are LDS copies issued one
-// group ahead (metadata, keys, values, in that order), with waits that count the copies.
+// operand reads of a tile spread over all LDS banks.  All global reads are LDS copies: a group's metadata
+// one group ahead, its key codes while the previous group's values are multiplied, and its value codes,
+// into the buffer the keys leave, while its keys are multiplied; the waits count the copies.
 // ---------------------------------------------------------------------------------------------
 typedef __attribute__((ext_vector_type(4))) int mf_i32x4;
 
@@ -2387,7 +2388,7 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   const uint8_t* k_rd0 = reinterpret_cast<const uint8_t*>(W.kst) + 32 * (krow + y0) + 8 * q4;
   const uint8_t* k_rd1 = reinterpret_cast<const uint8_t*>(W.kst) + 32 * (krow + (y0 ^ 1)) + 8 * q4;
   // value operand reads: channel c + 16 tau, code word q4, page kappa
-  const uint32_t* v_rd = reinterpret_cast<const uint32_t*>(W.vst) + 4 * c + q4;
+  const uint32_t* v_rd = reinterpret_cast<const uint32_t*>(W.kst) + 4 * c + q4;
   // alpha step: head ah, key positions Q0 .. Q0 + NCH - 1
   const int ah = lane >> (6 - LG);
   const int Q0 = (lane & (LPH - 1)) * NCH;
@@ -2399,7 +2400,7 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     const int tl = 32 * jj + ((lane >> 1) ^ ((lane >> 3) & 3));
     koff[jj] = (uint32_t)(tl * 32 + 16 * (lane & 1));
   }
-  const uint32_t kst_a = lds_addr(W.kst), vst_a = lds_addr(W.vst);
+  const uint32_t kst_a = lds_addr(W.kst);
   const uint32_t mst_a0 = lds_addr(W.mst[0]), mst_a1 = lds_addr(W.mst[1]);
   const uint8_t* pages = a.pages;
   const long long pbytes = g.page_bytes, hoff = (long long)h * g.head_bytes;
@@ -2415,7 +2416,7 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   auto issue_v = [&](int2 p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      dma16_base(vst_a + 1024 * j, page_of(j < 2 ? p.x : p.y) + I2_V_OFF + (j & 1) * 1024, lane * 16);
+      dma16_base(kst_a + 1024 * j, page_of(j < 2 ? p.x : p.y) + I2_V_OFF + (j & 1) * 1024, lane * 16);
   };
 
   float qa[NCH];
@@ -2441,7 +2442,6 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     pcur = scalar_load_int2(pt + g_first);
     issue_m(pcur, 0);
     issue_k(pcur);
-    issue_v(pcur);
   }
   wave_lds_sync();
   const mf_i32x4 zero4 = {0, 0, 0, 0};
@@ -2449,7 +2449,7 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   for (int gi = g_first; gi < g_end; gi += gstep) {
     const bool has_next = gi + gstep < g_end;  // uniform
     if (has_next) pnext = scalar_load_int2(pt + gi + gstep);
-    KVQ_WAIT_VM(8);  // this group's metadata (its key and value copies may be in flight)
+    KVQ_WAIT_VM(4);  // this group's metadata (its key copies may be in flight)
     const uint16_t* ms = reinterpret_cast<const uint16_t*>(W.mst[mb]);
     // 1. key-side operand of head ah at positions Q0 + i: alpha = q~ s, rounded to 16 bits, two limbs
     float Ah, AZh;
@@ -2528,8 +2528,8 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     wave_lds_sync();
 
     // 2. key products: 8 token tiles x 2 channel halves
-    if (has_next) KVQ_WAIT_VM(5);  // this group's key copies (its value copies and the next metadata follow)
-    else KVQ_WAIT_VM(4);
+    if (has_next) KVQ_WAIT_VM(1);  // this group's key copies (the next metadata follows)
+    else KVQ_WAIT_VM(0);
     uint2 kw[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -2537,7 +2537,7 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     const mf_i32x4 A0 = u4_i32x4(*reinterpret_cast<const uint4*>(a_rd));
     const mf_i32x4 A1 = u4_i32x4(*reinterpret_cast<const uint4*>(a_rd + 64));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (has_next) issue_k(pnext);
+    issue_v(pcur);  // into the buffer the key codes have left
     mf_i32x4 acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -2576,8 +2576,7 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     wave_lds_sync();
 
     // 4. value products: 8 channel tiles x 2 pages, and the weight sums
-    if (has_next) KVQ_WAIT_VM(5);  // this group's value copies (the next metadata and keys follow)
-    else KVQ_WAIT_VM(0);
+    KVQ_WAIT_VM(0);  // this group's value copies, the youngest in flight
     uint32_t vw[8][2];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -2587,7 +2586,7 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     const mf_i32x4 W0 = u4_i32x4(*reinterpret_cast<const uint4*>(w_rd));
     const mf_i32x4 W1 = u4_i32x4(*reinterpret_cast<const uint4*>(w_rd + 64));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (has_next) issue_v(pnext);
+    if (has_next) issue_k(pnext);
     mf_i32x4 accp = mfma_i8x64(W0, ones4, zero4);
     accp = mfma_i8x64(W1, ones4, accp);
 #pragma unroll
@@ -2657,13 +2656,54 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   }
 }
 
-// MODE: 0 fp32, 1 16-bit on the byte dot product, 2 16-bit on the nibble dot product (grouped schemes),
-// 3 16-bit on the int8 matrix cores (INT2 per channel)
+// Work-groups of the split-K launch per (sequence, kv head), besides its band unit.
+__host__ __device__ inline int splitk_wgs_per_pair(const Geo& g) {
+  return g.wave_chunks ? (g.n_units - 1 + 3) / 4 : g.n_units - 1;
+}
+// One-dimensional grid: the quantized-chunk work-groups first, chunk-major (every pair's first chunk
+// work-group, then every pair's second, ...), then the band work-groups.  The hardware hands consecutive
+// work-groups to the eight XCDs in turn, so every XCD gets the same mix of chunk positions (pair-major,
+// a chunk position would stay on one XCD, and the last chunks, which short sequences lack, would leave
+// theirs idle; a band unit inside each pair's run would do the same to the band), and the short band
+// work-groups fill the end of the launch.
+__device__ inline void splitk_unit_of(const Geo& g, int& unit, int& h, int& b) {
+  const int m = splitk_wgs_per_pair(g);
+  const int pairs = g.batch * g.n_kv;
+  const int i = blockIdx.x;
+  int pair;
+  if (i < pairs * m) {
+    pair = i % pairs;
+    unit = 1 + i / pairs;
+  } else {
+    pair = i - pairs * m;
+    unit = 0;
+  }
+  h = pair % g.n_kv;
+  b = pair / g.n_kv;
+}
+
+// Matrix-core INT2 launch: its own kernel so that the register bound allows four waves per SIMD at GQ <= 4.
+template <int GQ>
+__global__ __launch_bounds__(kThreads, GQ <= 4 ? 4 : 2) void decode_mfma_kernel(DecodeArgs a) {
+  __shared__ DecodeLds<GQ, 1, true> L;
+  const Geo& g = a.g;
+  int unit, h, b;
+  splitk_unit_of(g, unit, h, b);
+  const int T = a.seq_lens[b];
+  int n_chunks = (n_groups_of(T, g.S0, g.W) + g.gpc - 1) / g.gpc;
+  if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;  // lengths beyond the launch bound are cut
+  if (unit > (n_chunks + 3) / 4) return;
+  if (unit == 0) band_unit<GQ>(L, a, b, h, T);
+  else int2_unit_mfma<GQ>(L, a, b, h, T, unit - 1);
+}
+
+// MODE: 0 fp32, 1 16-bit on the byte dot product, 2 16-bit on the nibble dot product (grouped schemes)
 template <int GQ, int SCHEME, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
-  __shared__ DecodeLds<GQ, (SCHEME == KVQ_INT4_CHANNEL || (SCHEME == KVQ_INT4_TOKEN && MODE == 2)) ? 2 : 1, MODE == 3> L;
-  const int unit = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  __shared__ DecodeLds<GQ, (SCHEME == KVQ_INT4_CHANNEL || (SCHEME == KVQ_INT4_TOKEN && MODE == 2)) ? 2 : 1> L;
   const Geo& g = a.g;
+  int unit, h, b;
+  splitk_unit_of(g, unit, h, b);
   const int T = a.seq_lens[b];
   constexpr bool grouped = is_grouped(SCHEME);
   int n_chunks;
@@ -2691,8 +2731,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   } else if constexpr (SCHEME == KVQ_INT2_TOKEN) {
     int2tok_unit_dot8<GQ>(L, a, b, h, T, unit - 1);
   } else if constexpr (SCHEME == KVQ_INT2_CHANNEL) {
-    if constexpr (MODE == 3) int2_unit_mfma<GQ>(L, a, b, h, T, unit - 1);
-    else if constexpr (MODE == 2) int2_unit_dot8<GQ, 2>(L, a, b, h, T, unit - 1);
+    if constexpr (MODE == 2) int2_unit_dot8<GQ, 2>(L, a, b, h, T, unit - 1);
     else if constexpr (MODE == 1) int2_unit_dot16<GQ>(L, a, b, h, T, unit - 1);
     else int2_unit<GQ>(L, a, b, h, T, unit - 1);
   } else {
@@ -2871,7 +2910,7 @@ hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
   if (stages & KVQ_STAGE_QPREP) hipLaunchKernelGGL(qprep_kernel<GQ>, dim3(g.n_kv, g.batch), dim3(512), 0, s, a);
   if (stages & KVQ_STAGE_SPLITK) {
     // wave chunks: four chunks per work-group
-    const dim3 grid(g.wave_chunks ? 1 + (g.n_units - 1 + 3) / 4 : g.n_units, g.n_kv, g.batch), block(kThreads);
+    const dim3 grid((1 + splitk_wgs_per_pair(g)) * g.batch * g.n_kv), block(kThreads);
     // AUTO: 16-bit operands on the nibble dot product for INT2, the fp32 kernel for INT4 (faster there:
     // per-token scales leave the fp32 path no per-group work, and 4-bit codes convert cheaply)
     if (g.scheme == KVQ_INT4_CHANNEL) {
@@ -2879,7 +2918,7 @@ hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
     } else if (g.scheme == KVQ_INT2_TOKEN) {
       hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_TOKEN, 2>), grid, block, 0, s, a);
     } else if (g.scheme == KVQ_INT2_CHANNEL) {
-      if (a.impl == KVQ_DECODE_MFMA) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 3>), grid, block, 0, s, a);
+      if (a.impl == KVQ_DECODE_MFMA) hipLaunchKernelGGL(decode_mfma_kernel<GQ>, grid, block, 0, s, a);
       else if (a.impl == KVQ_DECODE_F32) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 0>), grid, block, 0, s, a);
       else if (a.impl == KVQ_DECODE_DOT16) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 1>), grid, block, 0, s, a);
       else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 2>), grid, block, 0, s, a);
