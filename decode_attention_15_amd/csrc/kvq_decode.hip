@@ -1106,7 +1106,7 @@ struct Dot8Wave {
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        dma16_base(kst_a + 1024 * j, page_of(j < 2 ? p.x : p.y) + I2_V_OFF + (j & 1) * 1024, lane * 16);
+        dma16_base(vst_a + 1024 * j, page_of(j < 2 ? p.x : p.y) + I2_V_OFF + (j & 1) * 1024, lane * 16);
     }
   }
 };
