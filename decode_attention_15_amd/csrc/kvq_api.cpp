@@ -31,14 +31,15 @@ int check_config(const kvq_config* c) {
   if (c->decode_impl != KVQ_DECODE_AUTO && c->decode_impl != KVQ_DECODE_F32 && c->decode_impl != KVQ_DECODE_MFMA &&
       c->decode_impl != KVQ_DECODE_DOT16 && c->decode_impl != KVQ_DECODE_DOT8)
     return KVQ_EINVAL;
-  // the matrix-core decode is built for INT2 per channel
-  if (c->decode_impl == KVQ_DECODE_MFMA && c->scheme != KVQ_INT2_CHANNEL) return KVQ_EUNSUPPORTED;
+  // the matrix-core decode is built for both INT2 schemes
+  if (c->decode_impl == KVQ_DECODE_MFMA && !is_int2(c->scheme)) return KVQ_EUNSUPPORTED;
   // nibble digits for INT4 per token walk page pairs: an explicit split must hold whole pairs
   if (c->decode_impl == KVQ_DECODE_DOT8 && c->scheme == KVQ_INT4_TOKEN && c->split_tokens % (2 * PAGE) != 0)
     return KVQ_EUNSUPPORTED;
-  // per-token INT2 and per-channel INT4 are built on the nibble dot product only
+  // per-token INT2 is built on the nibble dot product and the matrix cores, per-channel INT4 on the nibble
+  // dot product
   if ((c->scheme == KVQ_INT2_TOKEN || c->scheme == KVQ_INT4_CHANNEL) && c->decode_impl != KVQ_DECODE_AUTO &&
-      c->decode_impl != KVQ_DECODE_DOT8)
+      c->decode_impl != KVQ_DECODE_DOT8 && !(c->scheme == KVQ_INT2_TOKEN && c->decode_impl == KVQ_DECODE_MFMA))
     return KVQ_EUNSUPPORTED;
   if (c->key_only_rotation != 0 && c->key_only_rotation != 1) return KVQ_EINVAL;
   const int hb = c->hadamard_block;
@@ -63,9 +64,9 @@ void clip_params(float rho, int* j, float* f) {
   *f = (float)(h - fl);
 }
 
-// the matrix-core decode: asked for, or the automatic choice for INT2 per channel
+// the matrix-core decode: asked for, or the automatic choice for both INT2 schemes
 bool uses_mfma(const kvq_config* c) {
-  return c->decode_impl == KVQ_DECODE_MFMA || (c->decode_impl == KVQ_DECODE_AUTO && c->scheme == KVQ_INT2_CHANNEL);
+  return c->decode_impl == KVQ_DECODE_MFMA || (c->decode_impl == KVQ_DECODE_AUTO && is_int2(c->scheme));
 }
 
 // decode work split: groups (INT2) or pages (INT4) per chunk

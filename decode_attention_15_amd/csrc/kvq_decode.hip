@@ -2349,7 +2349,7 @@ __host__ __device__ constexpr int mf_key_channel(int Q) {
   return 16 * (2 * ((Q & 63) >> 4) + (Q >> 6)) + 4 * (Q & 3) + ((Q & 15) >> 2);
 }
 
-template <int GQ, typename Lds>
+template <int GQ, bool TOK, typename Lds>
 __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
   constexpr int LG = HeadLog2<GQ>::v;
   constexpr int LPH = 64 >> LG;        // lanes per head in the alpha step
@@ -2427,6 +2427,68 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
 #pragma unroll
     for (int i = 0; i < NCH; ++i) asm volatile("" ::"v"(qa[i]));  // the loads' wait stays before the walk
   }
+  // key-side operand x (positions Q0 + i of head ah) rounded to 16 bits against its head's largest |x|, as
+  // limbs in the key plane; returns the scale A = max|x| / 32639, and in zsum the sum of the rounded values
+  // times zk (per channel; 1 gives their plain sum)
+  auto key_operand = [&](const float (&x)[NCH], const float (&zk)[NCH], float& zsum) -> float {
+    int amx_i = 0;  // max |x| as its bit pattern (non-negative floats order as their bits)
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) amx_i = max(amx_i, __float_as_int(fabsf(x[i])));
+    const float amx = __int_as_float(seg_max_i<LPH>(amx_i));
+    // |rint(x inv)| <= 32639: the reciprocal's 1-ulp error cannot carry the largest past 32639.5
+    const float inv = amx > 0x1p-100f ? kAScale * __builtin_amdgcn_rcpf(amx) : 0.0f;
+    float ev[NCH];
+    float zs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      ev[i] = fmaf(x[i], inv, kRoundL);
+      zs = fmaf(ev[i] - kRoundL, zk[i], zs);  // with the rounded values: exact products of integers up to 2^15
+    }
+    zsum = seg_sum<LPH>(zs);
+    uint8_t* dst0 = W.aplane + (2 * ah) * RS + Q0;
+    uint8_t* dst1 = dst0 + RS;
+    if constexpr (NCH >= 4) {
+      uint32_t lo[NCH / 4], hi[NCH / 4];
+#pragma unroll
+      for (int k = 0; k < NCH / 4; ++k) limbs4(ev[4 * k], ev[4 * k + 1], ev[4 * k + 2], ev[4 * k + 3], lo[k], hi[k]);
+      if constexpr (NCH == 16) {
+        *reinterpret_cast<uint4*>(dst0) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        *reinterpret_cast<uint4*>(dst1) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      } else if constexpr (NCH == 8) {
+        *reinterpret_cast<uint2*>(dst0) = make_uint2(lo[0], lo[1]);
+        *reinterpret_cast<uint2*>(dst1) = make_uint2(hi[0], hi[1]);
+      } else {
+        *reinterpret_cast<uint32_t*>(dst0) = lo[0];
+        *reinterpret_cast<uint32_t*>(dst1) = hi[0];
+      }
+    } else {
+      uint32_t lo, hi;
+      limbs4(ev[0], ev[1], ev[0], ev[1], lo, hi);
+      *reinterpret_cast<uint16_t*>(dst0) = (uint16_t)lo;
+      *reinterpret_cast<uint16_t*>(dst1) = (uint16_t)hi;
+    }
+    return amx * (1.0f / kAScale);
+  };
+  // per-head values of this lane's result heads (head q4 HPL + e is the key step's lanes (q4 HPL + e) LPH)
+  auto head_value = [&](float v, int e) { return __shfl(v, ((q4 * HPL + e) & (GQ - 1)) * LPH, 64); };
+  // per-token INT2: the key-side operand is the rotated query itself, once per walk
+  float At[HPL], FSt[HPL];
+  mf_i32x4 A0t = {0, 0, 0, 0}, A1t = {0, 0, 0, 0};
+  if constexpr (TOK) {
+    float one[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) one[i] = 1.0f;
+    float fs;
+    const float Ah = key_operand(qa, one, fs);
+#pragma unroll
+    for (int e = 0; e < HPL; ++e) {
+      At[e] = head_value(Ah, e);
+      FSt[e] = head_value(fs, e);
+    }
+    wave_lds_sync();
+    A0t = u4_i32x4(*reinterpret_cast<const uint4*>(a_rd));
+    A1t = u4_i32x4(*reinterpret_cast<const uint4*>(a_rd + 64));
+  }
   float m[HPL], l[HPL], o[HPL][8];
 #pragma unroll
   for (int e = 0; e < HPL; ++e) {
@@ -2451,9 +2513,31 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     if (has_next) pnext = scalar_load_int2(pt + gi + gstep);
     KVQ_WAIT_VM(4);  // this group's metadata (its key copies may be in flight)
     const uint16_t* ms = reinterpret_cast<const uint16_t*>(W.mst[mb]);
-    // 1. key-side operand of head ah at positions Q0 + i: alpha = q~ s, rounded to 16 bits, two limbs
-    float Ah, AZh;
-    {
+    // 1. per channel: key-side operand alpha = q~ s of head ah at positions Q0 + i, two limbs;
+    //    per token: the group's token scales and zeros (tokens T(i, c) of the lane's page c / 8)
+    float Ae[HPL], AZe[HPL];
+    float tks[8], tkz[8], tvs[8], tvz[8];
+    if constexpr (TOK) {
+      // tokens 2 (c % 8) + 16 k + {0, 1} of page c / 8: one word per pair; K s, K z, V s, V z at 0, 64, 128, 192
+      const uint32_t* mw = reinterpret_cast<const uint32_t*>(ms + 256 * (c >> 3) + 2 * (c & 7));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t w0 = mw[8 * k], w1 = mw[8 * k + 32], w2 = mw[8 * k + 64], w3 = mw[8 * k + 96];
+        tks[k] = __uint_as_float(w0 << 16);
+        tks[k + 4] = __uint_as_float(w0 & 0xffff0000u);
+        tkz[k] = __uint_as_float(w1 << 16);
+        tkz[k + 4] = __uint_as_float(w1 & 0xffff0000u);
+        tvs[k] = __uint_as_float(w2 << 16);
+        tvs[k + 4] = __uint_as_float(w2 & 0xffff0000u);
+        tvz[k] = __uint_as_float(w3 << 16);
+        tvz[k + 4] = __uint_as_float(w3 & 0xffff0000u);
+      }
+#pragma unroll
+      for (int e = 0; e < HPL; ++e) {
+        Ae[e] = At[e];
+        AZe[e] = FSt[e];
+      }
+    } else {
       float al[NCH], zk[NCH];
       if constexpr (NCH >= 8) {
         // positions i and i + 4 (i % 8 < 4) are channels ch, ch + 1 with ch even: one word per pair
@@ -2477,52 +2561,14 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
           zk[i] = bf16_to_f32(ms[D + ch]);
         }
       }
-      int amx_i = 0;  // max |alpha| as its bit pattern (non-negative floats order as their bits)
+      float zs;
+      const float Ah = key_operand(al, zk, zs);
+      const float AZh = Ah * zs;
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) amx_i = max(amx_i, __float_as_int(fabsf(al[i])));
-      const float amx = __int_as_float(seg_max_i<LPH>(amx_i));
-      // |rint(alpha inv)| <= 32639: the reciprocal's 1-ulp error cannot carry the largest past 32639.5
-      const float inv = amx > 0x1p-100f ? kAScale * __builtin_amdgcn_rcpf(amx) : 0.0f;
-      float ev[NCH];
-      float zs = 0.0f;
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        ev[i] = fmaf(al[i], inv, kRoundL);
-        zs = fmaf(ev[i] - kRoundL, zk[i], zs);  // sum_c a_c z_c with the rounded a
+      for (int e = 0; e < HPL; ++e) {
+        Ae[e] = head_value(Ah, e);
+        AZe[e] = head_value(AZh, e);
       }
-      zs = seg_sum<LPH>(zs);
-      Ah = amx * (1.0f / kAScale);
-      AZh = Ah * zs;
-      uint8_t* dst0 = W.aplane + (2 * ah) * RS + Q0;
-      uint8_t* dst1 = dst0 + RS;
-      if constexpr (NCH >= 4) {
-        uint32_t lo[NCH / 4], hi[NCH / 4];
-#pragma unroll
-        for (int k = 0; k < NCH / 4; ++k) limbs4(ev[4 * k], ev[4 * k + 1], ev[4 * k + 2], ev[4 * k + 3], lo[k], hi[k]);
-        if constexpr (NCH == 16) {
-          *reinterpret_cast<uint4*>(dst0) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-          *reinterpret_cast<uint4*>(dst1) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-        } else if constexpr (NCH == 8) {
-          *reinterpret_cast<uint2*>(dst0) = make_uint2(lo[0], lo[1]);
-          *reinterpret_cast<uint2*>(dst1) = make_uint2(hi[0], hi[1]);
-        } else {
-          *reinterpret_cast<uint32_t*>(dst0) = lo[0];
-          *reinterpret_cast<uint32_t*>(dst1) = hi[0];
-        }
-      } else {
-        uint32_t lo, hi;
-        limbs4(ev[0], ev[1], ev[0], ev[1], lo, hi);
-        *reinterpret_cast<uint16_t*>(dst0) = (uint16_t)lo;
-        *reinterpret_cast<uint16_t*>(dst1) = (uint16_t)hi;
-      }
-    }
-    // per-head scales of this lane's result heads (head q4 HPL + e is the alpha step's lanes (q4 HPL + e) LPH)
-    float Ae[HPL], AZe[HPL];
-#pragma unroll
-    for (int e = 0; e < HPL; ++e) {
-      const int src = ((q4 * HPL + e) & (GQ - 1)) * LPH;
-      Ae[e] = __shfl(Ah, src, 64);
-      AZe[e] = __shfl(AZh, src, 64);
     }
     if (has_next) issue_m(pnext, mb ^ 1);
     wave_lds_sync();
@@ -2534,8 +2580,8 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       kw[i] = *reinterpret_cast<const uint2*>((i < 4 ? k_rd0 : k_rd1) + 512 * (i & 3));
-    const mf_i32x4 A0 = u4_i32x4(*reinterpret_cast<const uint4*>(a_rd));
-    const mf_i32x4 A1 = u4_i32x4(*reinterpret_cast<const uint4*>(a_rd + 64));
+    const mf_i32x4 A0 = TOK ? A0t : u4_i32x4(*reinterpret_cast<const uint4*>(a_rd));
+    const mf_i32x4 A1 = TOK ? A1t : u4_i32x4(*reinterpret_cast<const uint4*>(a_rd + 64));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     issue_v(pcur);  // into the buffer the key codes have left
     mf_i32x4 acc[8];
@@ -2545,11 +2591,43 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
       acc[i] = mfma_i8x64(A1, codes_i8(kw[i].y), acc[i]);
     }
 
-    // 3. logits logit = A val - AZ; the group maximum is that of the integer sums (A >= 0); weights
-    //    u = rint(32511 2^(A (val - val_max))) as limbs at positions 8 c + i of the weight plane
-    float mg[HPL];
+    // 3. per channel: logit = A val - AZ, the group maximum is that of the integer sums (A >= 0), weights
+    //    u = rint(32511 2^(A (val - val_max))); per token: logit_t = A s_t (val_t - z_t sum_c a_c), weights
+    //    u_t = rint(32511 p_t s'_t / S') with S' the group's largest p_t s'_t of the head, their sums
+    //    P = sum_t p_t and Z = sum_t u_t z'_t; weights as limbs at positions 8 c + i of the weight plane
+    float mg[HPL], Sg[HPL], Pt[HPL], Zt[HPL];
 #pragma unroll
     for (int e = 0; e < HPL; ++e) {
+      float ew[8];
+      if constexpr (TOK) {
+        float lg[8];
+        float lmx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          lg[i] = (Ae[e] * tks[i]) * fmaf(-tkz[i], AZe[e], (float)limbs_sum(acc[i][2 * e], acc[i][2 * e + 1]));
+          lmx = fmaxf(lmx, lg[i]);
+        }
+        mg[e] = seg_reduce<16>(lmx, OpMax());
+        float pw[8], wmx = 0.0f, ps = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float pp = __builtin_amdgcn_exp2f(lg[i] - mg[e]);
+          ps += pp;
+          pw[i] = pp * tvs[i];
+          wmx = fmaxf(wmx, pw[i]);
+        }
+        Sg[e] = seg_reduce<16>(wmx, OpMax());
+        Pt[e] = seg_sum<16>(ps);
+        // below 2^-100 the group's value terms are beyond fp32's reach next to the others: weights 0
+        const float r = Sg[e] > 0x1p-100f ? kPScale * __builtin_amdgcn_rcpf(Sg[e]) : 0.0f;
+        float zs = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ew[i] = fmaf(pw[i], r, kRoundL);
+          zs = fmaf(ew[i] - kRoundL, tvz[i], zs);
+        }
+        Zt[e] = seg_sum<16>(zs);
+      } else {
       int v[8];
       int vmx = (int)0x80000000u;
 #pragma unroll
@@ -2560,9 +2638,9 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
       vmx = seg_max_i<16>(vmx);
       const float ref = Ae[e] * (float)vmx;
       mg[e] = ref - AZe[e];
-      float ew[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) ew[i] = fmaf(__builtin_amdgcn_exp2f(fmaf(Ae[e], (float)v[i], -ref)), kPScale, kRoundL);
+      }
       uint32_t lo0, hi0, lo1, hi1;
       limbs4(ew[0], ew[1], ew[2], ew[3], lo0, hi0);
       limbs4(ew[4], ew[5], ew[6], ew[7], lo1, hi1);
@@ -2587,21 +2665,34 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     const mf_i32x4 W1 = u4_i32x4(*reinterpret_cast<const uint4*>(w_rd + 64));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (has_next) issue_k(pnext);
-    mf_i32x4 accp = mfma_i8x64(W0, ones4, zero4);
-    accp = mfma_i8x64(W1, ones4, accp);
+    mf_i32x4 accp = zero4;
+    if constexpr (!TOK) {
+      accp = mfma_i8x64(W0, ones4, zero4);
+      accp = mfma_i8x64(W1, ones4, accp);
+    }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       acc[t] = mfma_i8x64(W0, codes_i8(vw[t][0]), zero4);
       acc[t] = mfma_i8x64(W1, codes_i8(vw[t][1]), acc[t]);
     }
 
-    // 5. online-softmax update in the rotated value frame (o and l carry the weights' factor 32511)
+    // 5. online-softmax update in the rotated value frame (per channel: o and l carry the weights' factor
+    //    32511; per token: the group adds (S' / 32511) (U_c - Z) to o and P to l)
 #pragma unroll
     for (int e = 0; e < HPL; ++e) {
-      const float Pf = (float)limbs_sum(accp[2 * e], accp[2 * e + 1]);
       const float mnew = fmax_raw(m[e], mg[e]);
       const float sc = __builtin_amdgcn_exp2f(m[e] - mnew);  // 0 before the first group (m = -inf)
       const float eg = __builtin_amdgcn_exp2f(mg[e] - mnew);
+      if constexpr (TOK) {
+        const float wg = eg * Sg[e] * (1.0f / kPScale);
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          o[e][t] = fmaf(o[e][t], sc, wg * ((float)limbs_sum(acc[t][2 * e], acc[t][2 * e + 1]) - Zt[e]));
+        l[e] = fmaf(l[e], sc, eg * Pt[e]);
+        m[e] = mnew;
+        continue;
+      }
+      const float Pf = (float)limbs_sum(accp[2 * e], accp[2 * e + 1]);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int ch = c + 16 * t;
@@ -2615,11 +2706,13 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     mb ^= 1;
     pcur = pnext;
   }
+  if constexpr (!TOK) {
 #pragma unroll
-  for (int e = 0; e < HPL; ++e) {
+    for (int e = 0; e < HPL; ++e) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) o[e][t] *= 1.0f / kPScale;
-    l[e] *= 1.0f / kPScale;
+      for (int t = 0; t < 8; ++t) o[e][t] *= 1.0f / kPScale;
+      l[e] *= 1.0f / kPScale;
+    }
   }
   if (wc) {
     // every partial a merge reads is written; chunks past the length or the launch bound have none
@@ -2683,7 +2776,7 @@ __device__ inline void splitk_unit_of(const Geo& g, int& unit, int& h, int& b) {
 }
 
 // Matrix-core INT2 launch: its own kernel so that the register bound allows four waves per SIMD at GQ <= 4.
-template <int GQ>
+template <int GQ, bool TOK>
 __global__ __launch_bounds__(kThreads, GQ <= 4 ? 4 : 2) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ DecodeLds<GQ, 1, true> L;
   const Geo& g = a.g;
@@ -2694,7 +2787,7 @@ __global__ __launch_bounds__(kThreads, GQ <= 4 ? 4 : 2) void decode_mfma_kernel(
   if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;  // lengths beyond the launch bound are cut
   if (unit > (n_chunks + 3) / 4) return;
   if (unit == 0) band_unit<GQ>(L, a, b, h, T);
-  else int2_unit_mfma<GQ>(L, a, b, h, T, unit - 1);
+  else int2_unit_mfma<GQ, TOK>(L, a, b, h, T, unit - 1);
 }
 
 // MODE: 0 fp32, 1 16-bit on the byte dot product, 2 16-bit on the nibble dot product (grouped schemes)
@@ -2916,9 +3009,10 @@ hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
     if (g.scheme == KVQ_INT4_CHANNEL) {
       hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_CHANNEL, 2>), grid, block, 0, s, a);
     } else if (g.scheme == KVQ_INT2_TOKEN) {
-      hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_TOKEN, 2>), grid, block, 0, s, a);
+      if (a.impl == KVQ_DECODE_MFMA) hipLaunchKernelGGL((decode_mfma_kernel<GQ, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_TOKEN, 2>), grid, block, 0, s, a);
     } else if (g.scheme == KVQ_INT2_CHANNEL) {
-      if (a.impl == KVQ_DECODE_MFMA) hipLaunchKernelGGL(decode_mfma_kernel<GQ>, grid, block, 0, s, a);
+      if (a.impl == KVQ_DECODE_MFMA) hipLaunchKernelGGL((decode_mfma_kernel<GQ, false>), grid, block, 0, s, a);
       else if (a.impl == KVQ_DECODE_F32) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 0>), grid, block, 0, s, a);
       else if (a.impl == KVQ_DECODE_DOT16) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 1>), grid, block, 0, s, a);
       else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 2>), grid, block, 0, s, a);

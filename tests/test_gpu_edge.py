@@ -327,3 +327,20 @@ def test_matrix_core_decode_boundary_lengths(K, T):
     _say(f"matrix-core decode: boundary length T={T}")
     chunks = [1] * T if T < 8 else [T // 3, T - T // 3]
     _write_and_check(K, WL, _bf16(k), _bf16(v), chunks=chunks, decode_impl=K.DECODE_MFMA)
+
+
+@pytest.mark.parametrize("T", [1, 5, 259, 260, 261, 389, 517])
+def test_matrix_core_decode_per_token_boundary_lengths_and_constant_tokens(K, T):
+    """Per-token INT2 on the matrix cores: boundary lengths, with a constant token (s = 1 rule) and an
+    all-zero token inside the first group when there is one."""
+    rng = np.random.default_rng(300 + T)
+    k = rng.standard_normal((T, 2, 128)).astype(np.float32)
+    v = rng.standard_normal((T, 2, 128)).astype(np.float32)
+    if T > 140:
+        k[10, 0, :] = 0.5
+        v[11, 1, :] = 0.0
+        k[12] = 0.0
+    _say(f"matrix-core decode, per-token INT2: T={T}")
+    chunks = [1] * T if T < 8 else [T // 3, T - T // 3]
+    _write_and_check(K, synth.scaled(WL, scheme="int2_token"), _bf16(k), _bf16(v), chunks=chunks,
+                     decode_impl=K.DECODE_MFMA)

@@ -1,6 +1,7 @@
-"""GPU parity of the matrix-core INT2 decode (DECODE_MFMA): the split-K kernel's per-group sums over
-channels and tokens on v_mfma_i32_16x16x64_i8 with 16-bit two-limb operands, against the fp64 oracle on
-the same seeded caches (bar 2e-3), and against the fp32 and nibble-digit decodes of the same cache.
+"""GPU parity of the matrix-core INT2 decode (DECODE_MFMA), both INT2 schemes: the split-K kernel's
+per-group sums over channels and tokens on v_mfma_i32_16x16x64_i8 with 16-bit two-limb operands, against
+the fp64 oracle on the same seeded caches (bar 2e-3), and against the fp32 and nibble-digit decodes of the
+same cache.
 
 Cases span every GQA ratio the kernel lays out differently (1, 2 and 4: four matrix rows per head; 8: two),
 both chunk layouts (automatic chunks shared by a work-group's four waves and merged in LDS; explicit
@@ -122,4 +123,66 @@ def test_mfma_long_b4_131k_full_sampled(K):
     out = run_decode(K, bc, q)
     assert np.isfinite(out).all()
     worst = check_out(bc, out, q, [(2, 6)])
+    _say(f"   worst |mfma - oracle| = {worst:.2e}")
+
+
+# ------------------------------------------------------------------ per-token INT2 on the matrix cores
+
+
+def _tok(wl, **kw):
+    return synth.scaled(wl, scheme="int2_token", **kw)
+
+
+def test_mfma_int2_token_single_head_fp32_source(K):
+    wl = _tok(synth.WORKLOADS["tiny_1h_4k"])
+    _say("mfma per-token INT2: tiny 1 head (GQA 1), T=4096, fp32 source with x10 outlier channels, 40 appends")
+    _case(K, wl, [4096], [0], append_steps=40)
+
+
+def test_mfma_int2_token_gqa4_ragged_with_appends(K):
+    wl = _tok(synth.WORKLOADS["gqa_b1_32k"])
+    lens = [3000, 131, 700, 0, 260, 2051]
+    _say(f"mfma per-token INT2: GQA 4 ragged lens={lens}, 5 appends")
+    _case(K, wl, lens, [0, 3, 7], append_steps=5)
+
+
+def test_mfma_int2_token_gqa2(K):
+    wl = _tok(synth.WORKLOADS["gqa_b1_32k"], n_q_heads=16, n_kv_heads=8)
+    lens = [2900, 1000, 133]
+    _say(f"mfma per-token INT2: GQA 2 lens={lens}")
+    _case(K, wl, lens, [0, 5])
+
+
+@pytest.mark.parametrize("split", [0, 512])
+def test_mfma_int2_token_gqa8_decaying_spectrum(K, split):
+    wl = _tok(synth.WORKLOADS["long_b4_131k"], batch=2)
+    lens = [5000, 2222]
+    _say(f"mfma per-token INT2: GQA 8, sigma_c = (c+1)^-0.5, lens={lens}, split {split}")
+    _case(K, wl, lens, [0, 5], append_steps=3, split=split)
+
+
+def test_mfma_int2_token_agrees_with_dot8(K):
+    for name, lens in (("tiny_1h_4k", [4096]), ("gqa_b1_32k", [2900, 1000]), ("long_b4_131k", [3000, 700])):
+        wl = _tok(synth.WORKLOADS[name])
+        bc = build_cache(K, wl, lens)
+        q = synth.queries(synth.scaled(wl, batch=len(lens)))
+        outs = {}
+        for nm, c in (("dot8", K.DECODE_DOT8), ("mfma", K.DECODE_MFMA)):
+            bc.cfg.decode_impl = c
+            outs[nm] = run_decode(K, bc, q)
+        d8 = np.abs(outs["mfma"] - outs["dot8"]).max()
+        _say(f"per-token mfma vs dot8 on {name} lens={lens}: {d8:.2e}")
+        assert d8 <= TOL
+        check_out(bc, outs["mfma"], q, [(b, h) for b in range(len(lens)) for h in range(wl.n_kv_heads)])
+
+
+def test_mfma_int2_token_batch32_full_sampled(K):
+    wl = _tok(synth.WORKLOADS["batch32_32k"])
+    lens = synth.seq_lens(wl)
+    _say("mfma per-token INT2: batch32_32k full")
+    bc = build_cache(K, wl, lens, seqs_per_call=4, decode_impl=K.DECODE_MFMA)
+    q = synth.queries(wl)
+    out = run_decode(K, bc, q)
+    assert np.isfinite(out).all()
+    worst = check_out(bc, out, q, [(0, 0), (31, 7)])
     _say(f"   worst |mfma - oracle| = {worst:.2e}")

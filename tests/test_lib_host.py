@@ -159,11 +159,11 @@ def test_decode_implementations_accepted_for_both_schemes():
         assert K.check_config(cfg) == K.KVQ_OK
 
 
-def test_matrix_core_decode_is_built_for_int2_per_channel_only():
+def test_matrix_core_decode_is_built_for_the_int2_schemes_only():
     for scheme, rot, s0, w, ck, cv, want in (
             (K.INT2_CHANNEL, K.ROT_DENSE, 4, 128, 0.96, 0.92, K.KVQ_OK),
             (K.INT2_CHANNEL, K.ROT_HADAMARD, 4, 256, 0.96, 0.92, K.KVQ_OK),
-            (K.INT2_TOKEN, K.ROT_DENSE, 4, 128, 0.96, 0.92, K.KVQ_EUNSUPPORTED),
+            (K.INT2_TOKEN, K.ROT_DENSE, 4, 128, 0.96, 0.92, K.KVQ_OK),
             (K.INT4_CHANNEL, K.ROT_DENSE, 4, 128, 0.96, 0.92, K.KVQ_EUNSUPPORTED),
             (K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0, K.KVQ_EUNSUPPORTED)):
         for split in (0, 512):
@@ -173,9 +173,9 @@ def test_matrix_core_decode_is_built_for_int2_per_channel_only():
 
 
 def test_int2_token_scheme_config():
-    """Per-token INT2: same sink/recent rules and sizes as the per-channel scheme; built on DOT8 only."""
-    for impl, want in ((K.DECODE_AUTO, K.KVQ_OK), (K.DECODE_DOT8, K.KVQ_OK), (K.DECODE_F32, K.KVQ_EUNSUPPORTED),
-                       (K.DECODE_DOT16, K.KVQ_EUNSUPPORTED)):
+    """Per-token INT2: same sink/recent rules and sizes as the per-channel scheme; built on DOT8 and MFMA."""
+    for impl, want in ((K.DECODE_AUTO, K.KVQ_OK), (K.DECODE_DOT8, K.KVQ_OK), (K.DECODE_MFMA, K.KVQ_OK),
+                       (K.DECODE_F32, K.KVQ_EUNSUPPORTED), (K.DECODE_DOT16, K.KVQ_EUNSUPPORTED)):
         cfg = K.make_config(8, 32, scheme=K.INT2_TOKEN, decode_impl=impl)
         assert K.check_config(cfg) == want
     a = K.make_config(8, 32, scheme=K.INT2_TOKEN)
