@@ -31,10 +31,12 @@ int check_config(const kvq_config* c) {
   if (c->decode_impl != KVQ_DECODE_AUTO && c->decode_impl != KVQ_DECODE_F32 && c->decode_impl != KVQ_DECODE_MFMA &&
       c->decode_impl != KVQ_DECODE_DOT16 && c->decode_impl != KVQ_DECODE_DOT8)
     return KVQ_EINVAL;
-  // the matrix-core decode is built for both INT2 schemes
-  if (c->decode_impl == KVQ_DECODE_MFMA && !is_int2(c->scheme)) return KVQ_EUNSUPPORTED;
-  // nibble digits for INT4 per token walk page pairs: an explicit split must hold whole pairs
-  if (c->decode_impl == KVQ_DECODE_DOT8 && c->scheme == KVQ_INT4_TOKEN && c->split_tokens % (2 * PAGE) != 0)
+  // the matrix-core decode is built for both INT2 schemes and INT4 per token
+  if (c->decode_impl == KVQ_DECODE_MFMA && !is_int2(c->scheme) && c->scheme != KVQ_INT4_TOKEN)
+    return KVQ_EUNSUPPORTED;
+  // nibble digits and matrix cores for INT4 per token walk page pairs: an explicit split must hold whole pairs
+  if ((c->decode_impl == KVQ_DECODE_DOT8 || c->decode_impl == KVQ_DECODE_MFMA) && c->scheme == KVQ_INT4_TOKEN &&
+      c->split_tokens % (2 * PAGE) != 0)
     return KVQ_EUNSUPPORTED;
   // per-token INT2 is built on the nibble dot product and the matrix cores, per-channel INT4 on the nibble
   // dot product
@@ -64,9 +66,12 @@ void clip_params(float rho, int* j, float* f) {
   *f = (float)(h - fl);
 }
 
-// the matrix-core decode: asked for, or the automatic choice for both INT2 schemes
+// the matrix-core decode: asked for, or the automatic choice for both INT2 schemes and for INT4 per token
+// split into whole page pairs
 bool uses_mfma(const kvq_config* c) {
-  return c->decode_impl == KVQ_DECODE_MFMA || (c->decode_impl == KVQ_DECODE_AUTO && is_int2(c->scheme));
+  if (c->decode_impl == KVQ_DECODE_MFMA) return true;
+  if (c->decode_impl != KVQ_DECODE_AUTO) return false;
+  return is_int2(c->scheme) || (c->scheme == KVQ_INT4_TOKEN && c->split_tokens % (2 * PAGE) == 0);
 }
 
 // decode work split: groups (INT2) or pages (INT4) per chunk
@@ -81,7 +86,7 @@ int chunk_units(const kvq_config* c, int batch, int max_seq_len) {
     // that the chunks of all (sequence, kv head) pairs fill the GPU about once: ~2048 wave chunks, a power
     // of two from 1 to 32 groups
     const long long total = (long long)pairs * units;
-    int per = 1;
+    int per = c->scheme == KVQ_INT4_TOKEN ? 2 : 1;  // INT4 per token: whole page pairs
     while (per < 32 && (long long)per * 2048 < total) per *= 2;
     return per;
   }

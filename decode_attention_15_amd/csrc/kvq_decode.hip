@@ -147,20 +147,20 @@ __global__ __launch_bounds__(512) void qprep_kernel(DecodeArgs a) {
 // each with rows
 // (head, limb) of 128 bytes in k order (stride 144: consecutive rows start in different banks) and a last
 // row that stays zero for the matrix rows no head fills.
-template <int GQ>
+template <int GQ, int KU = 256>
 struct MfmaWave {
   static constexpr int ROWS = 2 * GQ;
   static constexpr int RSTRIDE = 144;
-  uint4 kst[256];
+  uint4 kst[KU];  // 4 KB (2-bit codes of a group) or 8 KB (4-bit codes of a page pair)
   uint4 mst[2][64];
   uint8_t aplane[(ROWS + 1) * RSTRIDE];
   uint8_t wplane[(ROWS + 1) * RSTRIDE];
 };
-template <int GQ, bool MF>
+template <int GQ, bool MF, int KU>
 struct MfmaLds {};
-template <int GQ>
-struct MfmaLds<GQ, true> {
-  MfmaWave<GQ> w[4];
+template <int GQ, int KU>
+struct MfmaLds<GQ, true, KU> {
+  MfmaWave<GQ, KU> w[4];
 };
 
 // STG: code staging per wave and group in units of 4 KB (2 for 4-bit per-channel codes); MF: the
@@ -168,7 +168,7 @@ struct MfmaLds<GQ, true> {
 template <int GQ, int STG = 1, bool MF = false>
 struct DecodeLds {
   union {
-    MfmaLds<GQ, MF> mf;
+    MfmaLds<GQ, MF, 256 * STG> mf;
     struct {                     // band unit, fp32 INT2 path, INT4 path
       float qband[GQ][D];
       float alpha[4][GQ][D];     // per wave: alpha (INT2) / rotated query (INT4)
@@ -2749,6 +2749,302 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// INT4 per-token chunk ([SAW] App. A.1 token-wise INT4, eq. 13-14) on the int8 matrix cores: the per-token
+// INT2 unit's algebra (key-side operand = the rotated query, two limbs, once per walk; logit_t = A s_t
+// (D_t - z_t sum_c a_c); weights u_t = rint(32511 p_t s'_t / S')) over page pairs (128 tokens) of 4-bit
+// codes, each 32-bit code word two int8 vectors ((w >> 4n) & 0x0F0F0F0F).  Tokens past the length take no
+// weight; a missing second page of a pair is the first again (read, never weighted).
+//  - key k order (k = 64 sigma + 16 q + 4 d + b): channel 16 (2 q + sigma) + 8 (d / 2) + 2 b + d % 2, i.e.
+//    lane q reads the 16 bytes 32 q + 16 sigma.. of a token row (channel c in byte c / 2, even c low);
+//  - value k order (k = 64 kappa + 16 q + 4 d + b): token 64 kappa + 16 (2 (d / 2) + b / 2) + 4 q + 2 (b % 2)
+//    + d % 2, i.e. lane q reads code words 2 q, 2 q + 1 of a channel row (token 16 j + 4 g + r in byte
+//    8 g + 2 j + r / 2, even r low);
+//  - key tile i, column c: token T(i, c) = 64 (c / 8) + 32 (c % 2) + 16 ((i / 2) % 2) + 4 ((c / 2) % 4) +
+//    2 (i % 2) + i / 4, the token at value position 8 c + i.
+// Key rows are staged with adjacent tokens swapped where bit 2 of the token is set (row t ^ ((t >> 2) & 1)),
+// so that a tile's 16-byte operand reads use all LDS banks.
+// ---------------------------------------------------------------------------------------------
+// key k position -> channel (4-bit codes)
+__host__ __device__ constexpr int mf_key_channel4(int Q) {
+  return 16 * (2 * ((Q & 63) >> 4) + (Q >> 6)) + 8 * (((Q & 15) >> 2) >> 1) + 2 * (Q & 3) + (((Q & 15) >> 2) & 1);
+}
+// two 32-bit words of 4-bit codes as 16 int8 values: low nibbles of w0, high of w0, low of w1, high of w1
+__device__ __forceinline__ mf_i32x4 nibbles_i8(uint32_t w0, uint32_t w1) {
+  return mf_i32x4{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu), (int)(w1 & 0x0F0F0F0Fu),
+                  (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+}
+
+template <int GQ, typename Lds>
+__device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
+  constexpr int LG = HeadLog2<GQ>::v;
+  constexpr int LPH = 64 >> LG;
+  constexpr int NCH = 2 * GQ;
+  constexpr int RPH = GQ == 8 ? 2 : 4;
+  constexpr int HPL = GQ == 8 ? 2 : 1;
+  constexpr int ROWS = 2 * GQ;
+  constexpr int RS = MfmaWave<GQ, 512>::RSTRIDE;
+  const Geo& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int npages = (T + PAGE - 1) / PAGE;
+  const int npairs = (npages + 1) / 2;
+  const int chunk_id = 4 * chunk + wave;  // one chunk (an even number of pages) per wave
+  const int pb = chunk_id * (g.gpc / 2);
+  int pe = pb + g.gpc / 2 < npairs ? pb + g.gpc / 2 : npairs;
+  if (2 * pe > g.max_pages + 1) pe = (g.max_pages + 1) / 2;  // never index past the page-table row
+  MfmaWave<GQ, 512>& W = L.mf.w[wave];
+  const int q4 = lane >> 4, c = lane & 15;
+
+  if (lane < 32) {
+    reinterpret_cast<uint32_t*>(W.aplane + ROWS * RS)[lane] = 0u;
+    reinterpret_cast<uint32_t*>(W.wplane + ROWS * RS)[lane] = 0u;
+  }
+  const int rh = c / RPH, rl = c % RPH;
+  const int prow = (rl < 2 && rh < GQ) ? 2 * rh + rl : ROWS;
+  const uint8_t* a_rd = W.aplane + prow * RS + 16 * q4;
+  const uint8_t* w_rd = W.wplane + prow * RS + 16 * q4;
+  // key operand reads: tile i at staged row 64 (c / 8) + 32 (c % 2) + 4 ((c / 2) % 4) + (y ^ (i / 4)) plus
+  // 16 ((i / 2) % 2) + 2 (i % 2), with y = (c / 2) % 2
+  const int y = (c >> 1) & 1;
+  const int krow = 64 * (c >> 3) + 32 * (c & 1) + 4 * ((c >> 1) & 3);
+  const uint8_t* k_rd0 = reinterpret_cast<const uint8_t*>(W.kst) + 64 * (krow + y) + 16 * q4;
+  const uint8_t* k_rd1 = reinterpret_cast<const uint8_t*>(W.kst) + 64 * (krow + (y ^ 1)) + 16 * q4;
+  // value operand reads: channel c + 16 tau, code words 2 q4, 2 q4 + 1, page kappa
+  const uint8_t* v_rd = reinterpret_cast<const uint8_t*>(W.kst) + 32 * c + 8 * q4;
+  // this lane's tokens T(i, c) (pair-local), their metadata words: K (s, z) at (2 page) 64 + t, V at + 64
+  const int tok0 = 64 * (c >> 3) + 32 * (c & 1) + 4 * ((c >> 1) & 3);
+  const int ah = lane >> (6 - LG);
+  const int Q0 = (lane & (LPH - 1)) * NCH;
+  // copies: key slots 64 j + lane hold staged row 16 j + lane / 4, quarter lane % 4
+  const uint32_t koff = (uint32_t)(64 * ((lane >> 2) ^ ((lane >> 4) & 1)) + 16 * (lane & 3));
+  const uint32_t kst_a = lds_addr(W.kst);
+  const uint32_t mst_a0 = lds_addr(W.mst[0]), mst_a1 = lds_addr(W.mst[1]);
+  const uint8_t* pages = a.pages;
+  const long long pbytes = g.page_bytes, hoff = (long long)h * g.head_bytes;
+  auto page_of = [&](int idx) { return pages + (long long)idx * pbytes + hoff; };
+  auto issue_m = [&](int2 p, int buf) {
+    const uint8_t* src = (lane >= 32 ? page_of(p.y) : page_of(p.x)) + ((lane & 16) ? I4_VMETA_OFF : I4_KMETA_OFF) +
+                         (lane & 15) * 16;
+    dma16(buf ? mst_a1 : mst_a0, src);
+  };
+  auto issue_k = [&](int2 p) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      dma16_base(kst_a + 1024 * j, page_of(j < 4 ? p.x : p.y) + I4_K_OFF + 1024 * (j & 3), koff);
+  };
+  auto issue_v = [&](int2 p) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      dma16_base(kst_a + 1024 * j, page_of(j < 4 ? p.x : p.y) + I4_V_OFF + 1024 * (j & 3), lane * 16);
+  };
+  const int32_t* ptr = a.page_table + (long long)b * g.max_pages;
+  auto pages_of = [&](int i) {  // scalar loads: a vector load would enter the counter the waits count
+    const int x = scalar_load_int(ptr + 2 * i);
+    const int yy = 2 * i + 1 < npages ? scalar_load_int(ptr + 2 * i + 1) : x;
+    return make_int2(x, yy);
+  };
+
+  // 0. the key-side operand, once: the rotated query of head ah at positions Q0 + i, two limbs
+  float At[HPL], FSt[HPL];
+  mf_i32x4 A0, A1;
+  {
+    float qa[NCH];
+    const float* q = a.qrot + ((long long)b * g.n_q + h * GQ + ah) * D;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) qa[i] = q[mf_key_channel4(Q0 + i)];
+    int amx_i = 0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) amx_i = max(amx_i, __float_as_int(fabsf(qa[i])));
+    const float amx = __int_as_float(seg_max_i<LPH>(amx_i));
+    const float inv = amx > 0x1p-100f ? kAScale * __builtin_amdgcn_rcpf(amx) : 0.0f;
+    float ev[NCH];
+    float fs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      ev[i] = fmaf(qa[i], inv, kRoundL);
+      fs += ev[i] - kRoundL;  // integers: exact
+    }
+    fs = seg_sum<LPH>(fs);
+    const float Ah = amx * (1.0f / kAScale);
+    uint8_t* dst0 = W.aplane + (2 * ah) * RS + Q0;
+    uint8_t* dst1 = dst0 + RS;
+    if constexpr (NCH >= 4) {
+      uint32_t lo[NCH / 4], hi[NCH / 4];
+#pragma unroll
+      for (int k = 0; k < NCH / 4; ++k) limbs4(ev[4 * k], ev[4 * k + 1], ev[4 * k + 2], ev[4 * k + 3], lo[k], hi[k]);
+#pragma unroll
+      for (int k = 0; k < NCH / 4; ++k) {
+        reinterpret_cast<uint32_t*>(dst0)[k] = lo[k];
+        reinterpret_cast<uint32_t*>(dst1)[k] = hi[k];
+      }
+    } else {
+      uint32_t lo, hi;
+      limbs4(ev[0], ev[1], ev[0], ev[1], lo, hi);
+      *reinterpret_cast<uint16_t*>(dst0) = (uint16_t)lo;
+      *reinterpret_cast<uint16_t*>(dst1) = (uint16_t)hi;
+    }
+#pragma unroll
+    for (int e = 0; e < HPL; ++e) {
+      const int src = ((q4 * HPL + e) & (GQ - 1)) * LPH;
+      At[e] = __shfl(Ah, src, 64);
+      FSt[e] = __shfl(fs, src, 64);
+    }
+    wave_lds_sync();
+    A0 = u4_i32x4(*reinterpret_cast<const uint4*>(a_rd));
+    A1 = u4_i32x4(*reinterpret_cast<const uint4*>(a_rd + 64));
+  }
+  float m[HPL], l[HPL], o[HPL][8];
+#pragma unroll
+  for (int e = 0; e < HPL; ++e) {
+    m[e] = -INFINITY;
+    l[e] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) o[e][t] = 0.0f;
+  }
+  int2 pcur = make_int2(0, 0), pnext = make_int2(0, 0);
+  int mb = 0;
+  if (pb < pe) {
+    pcur = pages_of(pb);
+    issue_m(pcur, 0);
+    issue_k(pcur);
+  }
+  wave_lds_sync();
+  const mf_i32x4 zero4 = {0, 0, 0, 0};
+  for (int pi = pb; pi < pe; ++pi) {
+    const bool has_next = pi + 1 < pe;  // uniform
+    if (has_next) pnext = pages_of(pi + 1);
+    KVQ_WAIT_VM(8);  // this pair's metadata (its key copies may be in flight)
+    // 1. the lane's tokens: K and V (scale, zero) words, validity
+    const uint32_t* mw = reinterpret_cast<const uint32_t*>(W.mst[mb]) + 128 * (c >> 3);  // its page's K, then V
+    float tks[8], tkz[8], tvs[8], tvz[8];
+    bool ok[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = tok0 + 16 * ((i >> 1) & 1) + 2 * (i & 1) + (i >> 2);  // T(i, c)
+      const uint32_t wk = mw[t & 63], wv = mw[64 + (t & 63)];
+      ok[i] = pi * 128 + t < T;
+      tks[i] = __uint_as_float(wk << 16);
+      tkz[i] = __uint_as_float(wk & 0xffff0000u);
+      // tokens past the length: no value scale or zero (their metadata may be anything)
+      tvs[i] = ok[i] ? __uint_as_float(wv << 16) : 0.0f;
+      tvz[i] = ok[i] ? __uint_as_float(wv & 0xffff0000u) : 0.0f;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (has_next) issue_m(pnext, mb ^ 1);
+
+    // 2. key products: 8 token tiles x 2 channel halves
+    if (has_next) KVQ_WAIT_VM(1);  // this pair's key copies (the next metadata follows)
+    else KVQ_WAIT_VM(0);
+    uint4 kw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      kw[i] = *reinterpret_cast<const uint4*>((i < 4 ? k_rd0 : k_rd1) + 1024 * ((i >> 1) & 1) + 128 * (i & 1));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    issue_v(pcur);  // into the buffer the key codes have left
+    mf_i32x4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc[i] = mfma_i8x64(A0, nibbles_i8(kw[i].x, kw[i].y), zero4);
+      acc[i] = mfma_i8x64(A1, nibbles_i8(kw[i].z, kw[i].w), acc[i]);
+    }
+
+    // 3. logits, the pair's maximum, weights u_t = rint(32511 p_t s'_t / S'), P = sum p_t, Z = sum u_t z'_t
+    float mg[HPL], Sg[HPL], Pt[HPL], Zt[HPL];
+#pragma unroll
+    for (int e = 0; e < HPL; ++e) {
+      float lg[8];
+      float lmx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = (At[e] * tks[i]) * fmaf(-tkz[i], FSt[e], (float)limbs_sum(acc[i][2 * e], acc[i][2 * e + 1]));
+        lg[i] = ok[i] ? x : -INFINITY;
+        lmx = fmaxf(lmx, lg[i]);
+      }
+      mg[e] = seg_reduce<16>(lmx, OpMax());  // finite: every pair has a token within the length
+      float pw[8], wmx = 0.0f, ps = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float pp = __builtin_amdgcn_exp2f(lg[i] - mg[e]);  // 0 for a token past the length
+        ps += pp;
+        pw[i] = pp * tvs[i];
+        wmx = fmaxf(wmx, pw[i]);
+      }
+      Sg[e] = seg_reduce<16>(wmx, OpMax());
+      Pt[e] = seg_sum<16>(ps);
+      const float r = Sg[e] > 0x1p-100f ? kPScale * __builtin_amdgcn_rcpf(Sg[e]) : 0.0f;
+      float ew[8];
+      float zs = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ew[i] = fmaf(pw[i], r, kRoundL);
+        zs = fmaf(ew[i] - kRoundL, tvz[i], zs);
+      }
+      Zt[e] = seg_sum<16>(zs);
+      uint32_t lo0, hi0, lo1, hi1;
+      limbs4(ew[0], ew[1], ew[2], ew[3], lo0, hi0);
+      limbs4(ew[4], ew[5], ew[6], ew[7], lo1, hi1);
+      const int he = q4 * HPL + e;
+      if (he < GQ) {
+        uint8_t* dst = W.wplane + (2 * he) * RS + 8 * c;
+        *reinterpret_cast<uint2*>(dst) = make_uint2(lo0, lo1);
+        *reinterpret_cast<uint2*>(dst + RS) = make_uint2(hi0, hi1);
+      }
+    }
+    wave_lds_sync();
+
+    // 4. value products: 8 channel tiles x 2 pages
+    KVQ_WAIT_VM(0);  // this pair's value copies, the youngest in flight
+    uint2 vw[8][2];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      vw[t][0] = *reinterpret_cast<const uint2*>(v_rd + 512 * t);
+      vw[t][1] = *reinterpret_cast<const uint2*>(v_rd + 4096 + 512 * t);
+    }
+    const mf_i32x4 W0 = u4_i32x4(*reinterpret_cast<const uint4*>(w_rd));
+    const mf_i32x4 W1 = u4_i32x4(*reinterpret_cast<const uint4*>(w_rd + 64));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (has_next) issue_k(pnext);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      acc[t] = mfma_i8x64(W0, nibbles_i8(vw[t][0].x, vw[t][0].y), zero4);
+      acc[t] = mfma_i8x64(W1, nibbles_i8(vw[t][1].x, vw[t][1].y), acc[t]);
+    }
+
+    // 5. online-softmax update in the rotated value frame: the pair adds (S' / 32511) (U_c - Z) and P
+#pragma unroll
+    for (int e = 0; e < HPL; ++e) {
+      const float mnew = fmax_raw(m[e], mg[e]);
+      const float sc = __builtin_amdgcn_exp2f(m[e] - mnew);  // 0 before the first pair (m = -inf)
+      const float eg = __builtin_amdgcn_exp2f(mg[e] - mnew);
+      const float wg = eg * Sg[e] * (1.0f / kPScale);
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        o[e][t] = fmaf(o[e][t], sc, wg * ((float)limbs_sum(acc[t][2 * e], acc[t][2 * e + 1]) - Zt[e]));
+      l[e] = fmaf(l[e], sc, eg * Pt[e]);
+      m[e] = mnew;
+    }
+    mb ^= 1;
+    pcur = pnext;
+  }
+  // every partial a merge reads is written; chunks past the length or the launch bound have none
+  if (pb < npairs && chunk_id < g.n_units - 1) {
+#pragma unroll
+    for (int e = 0; e < HPL; ++e) {
+      const int he = q4 * HPL + e;
+      if (he < GQ) {
+        float* part = a.partials + (((long long)b * g.n_q + h * GQ + he) * g.n_units + 1 + chunk_id) * PART_STRIDE;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) part[2 + c + 16 * t] = o[e][t];
+        if (c == 0) {
+          part[0] = m[e];
+          part[1] = l[e];
+        }
+      }
+    }
+  }
+}
+
 // Work-groups of the split-K launch per (sequence, kv head), besides its band unit.
 __host__ __device__ inline int splitk_wgs_per_pair(const Geo& g) {
   return g.wave_chunks ? (g.n_units - 1 + 3) / 4 : g.n_units - 1;
@@ -2788,6 +3084,28 @@ __global__ __launch_bounds__(kThreads, GQ <= 4 ? 4 : 2) void decode_mfma_kernel(
   if (unit > (n_chunks + 3) / 4) return;
   if (unit == 0) band_unit<GQ>(L, a, b, h, T);
   else int2_unit_mfma<GQ, TOK>(L, a, b, h, T, unit - 1);
+}
+
+// Matrix-core INT4 per-token launch (page pairs; no band: unit 0 stores an empty partial).
+template <int GQ>
+__global__ __launch_bounds__(kThreads, GQ <= 4 ? 3 : 2) void decode_mfma4_kernel(DecodeArgs a) {
+  __shared__ DecodeLds<GQ, 2, true> L;
+  const Geo& g = a.g;
+  int unit, h, b;
+  splitk_unit_of(g, unit, h, b);
+  const int T = a.seq_lens[b];
+  int n_chunks = ((T + PAGE - 1) / PAGE + g.gpc - 1) / g.gpc;
+  if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;  // lengths beyond the launch bound are cut
+  if (unit > (n_chunks + 3) / 4) return;
+  if (unit == 0) {
+    for (int e = threadIdx.x; e < GQ * PART_STRIDE; e += kThreads) {
+      const int hh = e / PART_STRIDE, k = e % PART_STRIDE;
+      float* part = a.partials + (((long long)b * g.n_q + h * GQ + hh) * g.n_units) * PART_STRIDE;
+      part[k] = (k == 0) ? -INFINITY : 0.0f;
+    }
+  } else {
+    int4tok_unit_mfma<GQ>(L, a, b, h, T, unit - 1);
+  }
 }
 
 // MODE: 0 fp32, 1 16-bit on the byte dot product, 2 16-bit on the nibble dot product (grouped schemes)
@@ -3018,7 +3336,8 @@ hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
       else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 2>), grid, block, 0, s, a);
     } else {
       // the API resolves AUTO for INT4 per token (nibble digits when the chunks hold whole page pairs)
-      if (a.impl == KVQ_DECODE_DOT8) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_TOKEN, 2>), grid, block, 0, s, a);
+      if (a.impl == KVQ_DECODE_MFMA) hipLaunchKernelGGL(decode_mfma4_kernel<GQ>, grid, block, 0, s, a);
+      else if (a.impl == KVQ_DECODE_DOT8) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_TOKEN, 2>), grid, block, 0, s, a);
       else if (a.impl == KVQ_DECODE_DOT16) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_TOKEN, 1>), grid, block, 0, s, a);
       else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_TOKEN, 0>), grid, block, 0, s, a);
     }

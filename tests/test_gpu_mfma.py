@@ -186,3 +186,58 @@ def test_mfma_int2_token_batch32_full_sampled(K):
     assert np.isfinite(out).all()
     worst = check_out(bc, out, q, [(0, 0), (31, 7)])
     _say(f"   worst |mfma - oracle| = {worst:.2e}")
+
+
+# ------------------------------------------------------------------ INT4 per token on the matrix cores
+
+
+@pytest.mark.parametrize("split", [0, 128, 256])
+def test_mfma_int4_token_small(K, split):
+    """Lengths end inside a pair's second page, inside its first page (second page missing) and on a page
+    boundary; automatic and explicit splits."""
+    from kvq_cases import check_int4
+    wl = synth.WORKLOADS["saw_int4_b16_16k"]
+    lens = [1000, 333, 66, 40, 128, 1]
+    _say(f"mfma int4 per token lens={lens} split={split}")
+    bc = build_cache(K, wl, lens, append_steps=7, chunk=256, decode_impl=K.DECODE_MFMA, split_tokens=split)
+    pages = bc.cache.pages.cpu().numpy()
+    for b in (0, 2):
+        check_int4(bc, b, 6, pages)
+    q = synth.queries(synth.scaled(wl, batch=len(lens)))
+    out = run_decode(K, bc, q)
+    worst = check_out(bc, out, q, [(b, h) for b in range(len(lens)) for h in range(8)])
+    _say(f"   worst |mfma - oracle| = {worst:.2e}")
+
+
+@pytest.mark.parametrize("gq,block", [(1, 128), (2, 16), (8, 64)])
+def test_mfma_int4_token_gqa_and_blocks(K, gq, block):
+    wl = synth.scaled(synth.WORKLOADS["saw_int4_b16_16k"], n_q_heads=8 * gq, n_kv_heads=8, hadamard_block=block)
+    lens = [700, 2049]
+    _say(f"mfma int4 per token: GQA {gq}, Hadamard block {block}, lens={lens}")
+    _case(K, wl, lens, [], chunk=512, check_codes=False)
+
+
+def test_mfma_int4_token_agrees_with_the_other_decodes(K):
+    wl = synth.WORKLOADS["saw_int4_b16_16k"]
+    lens = [1500, 300]
+    bc = build_cache(K, wl, lens)
+    q = synth.queries(synth.scaled(wl, batch=len(lens)))
+    outs = {}
+    for nm, c in (("f32", K.DECODE_F32), ("dot8", K.DECODE_DOT8), ("mfma", K.DECODE_MFMA)):
+        bc.cfg.decode_impl = c
+        outs[nm] = run_decode(K, bc, q)
+    d32 = np.abs(outs["mfma"] - outs["f32"]).max()
+    d8 = np.abs(outs["mfma"] - outs["dot8"]).max()
+    _say(f"int4 per token mfma vs f32 / dot8: {d32:.2e} / {d8:.2e}")
+    assert d32 <= TOL and d8 <= TOL
+
+
+def test_mfma_int4_token_full_sampled(K):
+    wl = synth.WORKLOADS["saw_int4_b16_16k"]
+    _say("mfma int4 per token: B=16, T=16384, 8192-token prefill chunks")
+    bc = build_cache(K, wl, [16384] * 16, chunk=8192, seqs_per_call=4, decode_impl=K.DECODE_MFMA)
+    q = synth.queries(wl)
+    out = run_decode(K, bc, q)
+    assert np.isfinite(out).all()
+    worst = check_out(bc, out, q, [(0, 0), (15, 7)])
+    _say(f"   worst |mfma - oracle| = {worst:.2e}")

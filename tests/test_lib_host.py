@@ -150,22 +150,24 @@ def test_decode_implementations_accepted_for_both_schemes():
             cfg = K.make_config(8, 32, scheme=scheme, rotation=rot, n_sink=s0, n_recent=w, clip_k=ck, clip_v=cv,
                                 decode_impl=impl)
             assert K.check_config(cfg) == K.KVQ_OK
-    # INT4 per token on the nibble digits walks page pairs: an explicit split must hold whole pairs
+    # INT4 per token on the nibble digits and the matrix cores walks page pairs: an explicit split must hold
+    # whole pairs
     for split, want in ((64, K.KVQ_EUNSUPPORTED), (192, K.KVQ_EUNSUPPORTED), (128, K.KVQ_OK), (512, K.KVQ_OK)):
-        cfg = K.make_config(8, 32, scheme=K.INT4_TOKEN, rotation=K.ROT_HADAMARD, n_sink=0, n_recent=0, clip_k=1.0,
-                            clip_v=1.0, split_tokens=split, decode_impl=K.DECODE_DOT8)
-        assert K.check_config(cfg) == want
+        for impl in (K.DECODE_DOT8, K.DECODE_MFMA):
+            cfg = K.make_config(8, 32, scheme=K.INT4_TOKEN, rotation=K.ROT_HADAMARD, n_sink=0, n_recent=0,
+                                clip_k=1.0, clip_v=1.0, split_tokens=split, decode_impl=impl)
+            assert K.check_config(cfg) == want
         cfg.decode_impl = K.DECODE_AUTO  # the automatic choice takes the fp32 path there instead
         assert K.check_config(cfg) == K.KVQ_OK
 
 
-def test_matrix_core_decode_is_built_for_the_int2_schemes_only():
+def test_matrix_core_decode_schemes():
     for scheme, rot, s0, w, ck, cv, want in (
             (K.INT2_CHANNEL, K.ROT_DENSE, 4, 128, 0.96, 0.92, K.KVQ_OK),
             (K.INT2_CHANNEL, K.ROT_HADAMARD, 4, 256, 0.96, 0.92, K.KVQ_OK),
             (K.INT2_TOKEN, K.ROT_DENSE, 4, 128, 0.96, 0.92, K.KVQ_OK),
             (K.INT4_CHANNEL, K.ROT_DENSE, 4, 128, 0.96, 0.92, K.KVQ_EUNSUPPORTED),
-            (K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0, K.KVQ_EUNSUPPORTED)):
+            (K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0, K.KVQ_OK)):
         for split in (0, 512):
             cfg = K.make_config(8, 32, scheme=scheme, rotation=rot, n_sink=s0, n_recent=w, clip_k=ck, clip_v=cv,
                                 split_tokens=split, decode_impl=K.DECODE_MFMA)
