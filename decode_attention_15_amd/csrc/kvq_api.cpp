@@ -31,17 +31,14 @@ int check_config(const kvq_config* c) {
   if (c->decode_impl != KVQ_DECODE_AUTO && c->decode_impl != KVQ_DECODE_F32 && c->decode_impl != KVQ_DECODE_MFMA &&
       c->decode_impl != KVQ_DECODE_DOT16 && c->decode_impl != KVQ_DECODE_DOT8)
     return KVQ_EINVAL;
-  // the matrix-core decode is built for both INT2 schemes and INT4 per token
-  if (c->decode_impl == KVQ_DECODE_MFMA && !is_int2(c->scheme) && c->scheme != KVQ_INT4_TOKEN)
-    return KVQ_EUNSUPPORTED;
+  // the matrix-core decode is built for every scheme
   // nibble digits and matrix cores for INT4 per token walk page pairs: an explicit split must hold whole pairs
   if ((c->decode_impl == KVQ_DECODE_DOT8 || c->decode_impl == KVQ_DECODE_MFMA) && c->scheme == KVQ_INT4_TOKEN &&
       c->split_tokens % (2 * PAGE) != 0)
     return KVQ_EUNSUPPORTED;
-  // per-token INT2 is built on the nibble dot product and the matrix cores, per-channel INT4 on the nibble
-  // dot product
+  // per-token INT2 and per-channel INT4 are built on the nibble dot product and the matrix cores
   if ((c->scheme == KVQ_INT2_TOKEN || c->scheme == KVQ_INT4_CHANNEL) && c->decode_impl != KVQ_DECODE_AUTO &&
-      c->decode_impl != KVQ_DECODE_DOT8 && !(c->scheme == KVQ_INT2_TOKEN && c->decode_impl == KVQ_DECODE_MFMA))
+      c->decode_impl != KVQ_DECODE_DOT8 && c->decode_impl != KVQ_DECODE_MFMA)
     return KVQ_EUNSUPPORTED;
   if (c->key_only_rotation != 0 && c->key_only_rotation != 1) return KVQ_EINVAL;
   const int hb = c->hadamard_block;
@@ -66,12 +63,12 @@ void clip_params(float rho, int* j, float* f) {
   *f = (float)(h - fl);
 }
 
-// the matrix-core decode: asked for, or the automatic choice for both INT2 schemes and for INT4 per token
-// split into whole page pairs
+// the matrix-core decode: asked for, or the automatic choice for every scheme (INT4 per token: when split
+// into whole page pairs)
 bool uses_mfma(const kvq_config* c) {
   if (c->decode_impl == KVQ_DECODE_MFMA) return true;
   if (c->decode_impl != KVQ_DECODE_AUTO) return false;
-  return is_int2(c->scheme) || (c->scheme == KVQ_INT4_TOKEN && c->split_tokens % (2 * PAGE) == 0);
+  return is_grouped(c->scheme) || c->split_tokens % (2 * PAGE) == 0;
 }
 
 // decode work split: groups (INT2) or pages (INT4) per chunk

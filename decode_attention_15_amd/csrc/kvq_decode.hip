@@ -2349,7 +2349,19 @@ __host__ __device__ constexpr int mf_key_channel(int Q) {
   return 16 * (2 * ((Q & 63) >> 4) + (Q >> 6)) + 4 * (Q & 3) + ((Q & 15) >> 2);
 }
 
-template <int GQ, bool TOK, typename Lds>
+// two 32-bit words of 4-bit codes as 16 int8 values: low nibbles of w0, high of w0, low of w1, high of w1
+__device__ __forceinline__ mf_i32x4 nibbles_i8(uint32_t w0, uint32_t w1) {
+  return mf_i32x4{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu), (int)(w1 & 0x0F0F0F0Fu),
+                  (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+}
+// key k position -> channel, per-channel INT4 (channel 16 m + 2 k + e in word 2 m + e, nibble k): lane q
+// reads words 4 q + 2 sigma, + 1 of a token row, whose low and high nibbles give channels 16 (2 q + sigma) +
+// 4 b + 2 h + e (b the byte, h = high nibble, e the word's parity); k = 64 sigma + 16 q + 4 (2 e + h) + b
+__host__ __device__ constexpr int mf_key_channel_c4(int Q) {
+  return 16 * (2 * ((Q & 63) >> 4) + (Q >> 6)) + 4 * (Q & 3) + 2 * (((Q & 15) >> 2) & 1) + (((Q & 15) >> 2) >> 1);
+}
+
+template <int GQ, bool TOK, int BITS, typename Lds>
 __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
   constexpr int LG = HeadLog2<GQ>::v;
   constexpr int LPH = 64 >> LG;        // lanes per head in the alpha step
@@ -2357,7 +2369,9 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   constexpr int RPH = GQ == 8 ? 2 : 4;  // matrix rows per head
   constexpr int HPL = GQ == 8 ? 2 : 1;  // heads per lane in the results
   constexpr int ROWS = 2 * GQ;
-  constexpr int RS = MfmaWave<GQ>::RSTRIDE;
+  constexpr int KU = 128 * BITS;  // staging of a group's key or value codes, in 16-byte units
+  constexpr int NCP = KU / 64;    // copies per group and side
+  constexpr int RS = MfmaWave<GQ, KU>::RSTRIDE;
   const Geo& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2369,7 +2383,7 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   if (g_end > g.max_pages / 2) g_end = g.max_pages / 2;  // never index past the page-table row
   const int gstep = wc ? 1 : 4;
   const int g_first = wc ? g_begin : g_begin + wave;
-  MfmaWave<GQ>& W = L.mf.w[wave];
+  MfmaWave<GQ, KU>& W = L.mf.w[wave];
   const int q4 = lane >> 4, c = lane & 15;
 
   // the rows no head fills read the zero row of each plane
@@ -2382,13 +2396,17 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   const int prow = (rl < 2 && rh < GQ) ? 2 * rh + rl : ROWS;
   const uint8_t* a_rd = W.aplane + prow * RS + 16 * q4;
   const uint8_t* w_rd = W.wplane + prow * RS + 16 * q4;
-  // key operand reads: tile i at staged row 64 (c / 8) + 4 ((c / 2) % 4) + 16 (i % 4) + (y0 ^ (i / 4))
+  // key operand reads. 2-bit: tile i at staged row 64 (c / 8) + 4 ((c / 2) % 4) + 16 (i % 4) + (y0 ^ (i / 4)),
+  // 8 bytes 8 q4..; 4-bit: token row T(i, c) = 64 (c / 8) + 4 ((c / 2) % 4) + (c % 2) + 16 (i % 4) + 2 (i / 4)
+  // as it is, 16 bytes 16 q4..
   const int y0 = (2 * (c & 1)) ^ ((c >> 1) & 3);
   const int krow = 64 * (c >> 3) + 4 * ((c >> 1) & 3);
-  const uint8_t* k_rd0 = reinterpret_cast<const uint8_t*>(W.kst) + 32 * (krow + y0) + 8 * q4;
-  const uint8_t* k_rd1 = reinterpret_cast<const uint8_t*>(W.kst) + 32 * (krow + (y0 ^ 1)) + 8 * q4;
-  // value operand reads: channel c + 16 tau, code word q4, page kappa
-  const uint32_t* v_rd = reinterpret_cast<const uint32_t*>(W.kst) + 4 * c + q4;
+  const uint8_t* k_rd0 = BITS == 2 ? reinterpret_cast<const uint8_t*>(W.kst) + 32 * (krow + y0) + 8 * q4
+                                   : reinterpret_cast<const uint8_t*>(W.kst) + 64 * (krow + (c & 1)) + 16 * q4;
+  const uint8_t* k_rd1 = BITS == 2 ? reinterpret_cast<const uint8_t*>(W.kst) + 32 * (krow + (y0 ^ 1)) + 8 * q4
+                                   : k_rd0 + 128;
+  // value operand reads: channel c + 16 tau, code word q4 (2-bit) or words 2 q4, 2 q4 + 1 (4-bit), page kappa
+  const uint32_t* v_rd = reinterpret_cast<const uint32_t*>(W.kst) + (BITS == 2 ? 4 * c + q4 : 8 * c + 2 * q4);
   // alpha step: head ah, key positions Q0 .. Q0 + NCH - 1
   const int ah = lane >> (6 - LG);
   const int Q0 = (lane & (LPH - 1)) * NCH;
@@ -2405,25 +2423,33 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   const uint8_t* pages = a.pages;
   const long long pbytes = g.page_bytes, hoff = (long long)h * g.head_bytes;
   auto page_of = [&](int idx) { return pages + (long long)idx * pbytes + hoff; };
+  constexpr int META = BITS == 2 ? I2_META_OFF : I4C_META_OFF;
+  constexpr int KOFF = BITS == 2 ? I2_K_OFF : I4C_K_OFF, VOFF = BITS == 2 ? I2_V_OFF : I4C_V_OFF;
   auto issue_m = [&](int2 p, int buf) {
-    const uint8_t* src = (lane >= 32 ? page_of(p.y) : page_of(p.x)) + I2_META_OFF + (lane & 31) * 16;
+    const uint8_t* src = (lane >= 32 ? page_of(p.y) : page_of(p.x)) + META + (lane & 31) * 16;
     dma16(buf ? mst_a1 : mst_a0, src);
   };
   auto issue_k = [&](int2 p) {
+    if constexpr (BITS == 2) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16_base(kst_a + 1024 * j, page_of(j < 2 ? p.x : p.y) + I2_K_OFF, koff[j & 1]);
+      for (int j = 0; j < 4; ++j) dma16_base(kst_a + 1024 * j, page_of(j < 2 ? p.x : p.y) + KOFF, koff[j & 1]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NCP; ++j)
+        dma16_base(kst_a + 1024 * j, page_of(j < NCP / 2 ? p.x : p.y) + KOFF + 1024 * (j % (NCP / 2)), lane * 16);
+    }
   };
   auto issue_v = [&](int2 p) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dma16_base(kst_a + 1024 * j, page_of(j < 2 ? p.x : p.y) + I2_V_OFF + (j & 1) * 1024, lane * 16);
+    for (int j = 0; j < NCP; ++j)
+      dma16_base(kst_a + 1024 * j, page_of(j < NCP / 2 ? p.x : p.y) + VOFF + 1024 * (j % (NCP / 2)), lane * 16);
   };
 
   float qa[NCH];
   {
     const float* q = a.qrot + ((long long)b * g.n_q + h * GQ + ah) * D;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) qa[i] = q[mf_key_channel(Q0 + i)];
+    for (int i = 0; i < NCH; ++i) qa[i] = q[BITS == 2 ? mf_key_channel(Q0 + i) : mf_key_channel_c4(Q0 + i)];
 #pragma unroll
     for (int i = 0; i < NCH; ++i) asm volatile("" ::"v"(qa[i]));  // the loads' wait stays before the walk
   }
@@ -2511,7 +2537,9 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   for (int gi = g_first; gi < g_end; gi += gstep) {
     const bool has_next = gi + gstep < g_end;  // uniform
     if (has_next) pnext = scalar_load_int2(pt + gi + gstep);
-    KVQ_WAIT_VM(4);  // this group's metadata (its key copies may be in flight)
+    // this group's metadata (its key copies may be in flight)
+    if constexpr (NCP == 4) KVQ_WAIT_VM(4);
+    else KVQ_WAIT_VM(8);
     const uint16_t* ms = reinterpret_cast<const uint16_t*>(W.mst[mb]);
     // 1. per channel: key-side operand alpha = q~ s of head ah at positions Q0 + i, two limbs;
     //    per token: the group's token scales and zeros (tokens T(i, c) of the lane's page c / 8)
@@ -2539,7 +2567,7 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
       }
     } else {
       float al[NCH], zk[NCH];
-      if constexpr (NCH >= 8) {
+      if constexpr (NCH >= 8 && BITS == 2) {
         // positions i and i + 4 (i % 8 < 4) are channels ch, ch + 1 with ch even: one word per pair
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
@@ -2556,7 +2584,7 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
       } else {
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
-          const int ch = mf_key_channel(Q0 + i);
+          const int ch = BITS == 2 ? mf_key_channel(Q0 + i) : mf_key_channel_c4(Q0 + i);
           al[i] = qa[i] * bf16_to_f32(ms[ch]);
           zk[i] = bf16_to_f32(ms[D + ch]);
         }
@@ -2576,10 +2604,16 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     // 2. key products: 8 token tiles x 2 channel halves
     if (has_next) KVQ_WAIT_VM(1);  // this group's key copies (the next metadata follows)
     else KVQ_WAIT_VM(0);
-    uint2 kw[8];
+    uint4 kw[8];  // 2-bit: .x, .y; 4-bit: all four words
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      kw[i] = *reinterpret_cast<const uint2*>((i < 4 ? k_rd0 : k_rd1) + 512 * (i & 3));
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (BITS == 2) {
+        const uint2 t2 = *reinterpret_cast<const uint2*>((i < 4 ? k_rd0 : k_rd1) + 512 * (i & 3));
+        kw[i] = make_uint4(t2.x, t2.y, 0u, 0u);
+      } else {
+        kw[i] = *reinterpret_cast<const uint4*>((i < 4 ? k_rd0 : k_rd1) + 1024 * (i & 3));
+      }
+    }
     const mf_i32x4 A0 = TOK ? A0t : u4_i32x4(*reinterpret_cast<const uint4*>(a_rd));
     const mf_i32x4 A1 = TOK ? A1t : u4_i32x4(*reinterpret_cast<const uint4*>(a_rd + 64));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -2587,8 +2621,8 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     mf_i32x4 acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      acc[i] = mfma_i8x64(A0, codes_i8(kw[i].x), zero4);
-      acc[i] = mfma_i8x64(A1, codes_i8(kw[i].y), acc[i]);
+      acc[i] = mfma_i8x64(A0, BITS == 2 ? codes_i8(kw[i].x) : nibbles_i8(kw[i].x, kw[i].y), zero4);
+      acc[i] = mfma_i8x64(A1, BITS == 2 ? codes_i8(kw[i].y) : nibbles_i8(kw[i].z, kw[i].w), acc[i]);
     }
 
     // 3. per channel: logit = A val - AZ, the group maximum is that of the integer sums (A >= 0), weights
@@ -2655,11 +2689,16 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
 
     // 4. value products: 8 channel tiles x 2 pages, and the weight sums
     KVQ_WAIT_VM(0);  // this group's value copies, the youngest in flight
-    uint32_t vw[8][2];
+    uint2 vw[8][2];  // 2-bit: .x; 4-bit: both words
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      vw[t][0] = v_rd[64 * t];
-      vw[t][1] = v_rd[512 + 64 * t];
+      if constexpr (BITS == 2) {
+        vw[t][0] = make_uint2(v_rd[64 * t], 0u);
+        vw[t][1] = make_uint2(v_rd[512 + 64 * t], 0u);
+      } else {
+        vw[t][0] = *reinterpret_cast<const uint2*>(v_rd + 128 * t);
+        vw[t][1] = *reinterpret_cast<const uint2*>(v_rd + 1024 + 128 * t);
+      }
     }
     const mf_i32x4 W0 = u4_i32x4(*reinterpret_cast<const uint4*>(w_rd));
     const mf_i32x4 W1 = u4_i32x4(*reinterpret_cast<const uint4*>(w_rd + 64));
@@ -2672,8 +2711,8 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      acc[t] = mfma_i8x64(W0, codes_i8(vw[t][0]), zero4);
-      acc[t] = mfma_i8x64(W1, codes_i8(vw[t][1]), acc[t]);
+      acc[t] = mfma_i8x64(W0, BITS == 2 ? codes_i8(vw[t][0].x) : nibbles_i8(vw[t][0].x, vw[t][0].y), zero4);
+      acc[t] = mfma_i8x64(W1, BITS == 2 ? codes_i8(vw[t][1].x) : nibbles_i8(vw[t][1].x, vw[t][1].y), acc[t]);
     }
 
     // 5. online-softmax update in the rotated value frame (per channel: o and l carry the weights' factor
@@ -2768,11 +2807,6 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
 // key k position -> channel (4-bit codes)
 __host__ __device__ constexpr int mf_key_channel4(int Q) {
   return 16 * (2 * ((Q & 63) >> 4) + (Q >> 6)) + 8 * (((Q & 15) >> 2) >> 1) + 2 * (Q & 3) + (((Q & 15) >> 2) & 1);
-}
-// two 32-bit words of 4-bit codes as 16 int8 values: low nibbles of w0, high of w0, low of w1, high of w1
-__device__ __forceinline__ mf_i32x4 nibbles_i8(uint32_t w0, uint32_t w1) {
-  return mf_i32x4{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu), (int)(w1 & 0x0F0F0F0Fu),
-                  (int)((w1 >> 4) & 0x0F0F0F0Fu)};
 }
 
 template <int GQ, typename Lds>
@@ -3072,9 +3106,9 @@ __device__ inline void splitk_unit_of(const Geo& g, int& unit, int& h, int& b) {
 }
 
 // Matrix-core INT2 launch: its own kernel so that the register bound allows four waves per SIMD at GQ <= 4.
-template <int GQ, bool TOK>
-__global__ __launch_bounds__(kThreads, GQ <= 4 ? 4 : 2) void decode_mfma_kernel(DecodeArgs a) {
-  __shared__ DecodeLds<GQ, 1, true> L;
+template <int GQ, bool TOK, int BITS>
+__global__ __launch_bounds__(kThreads, GQ <= 4 ? (BITS == 2 ? 4 : 3) : 2) void decode_mfma_kernel(DecodeArgs a) {
+  __shared__ DecodeLds<GQ, BITS / 2, true> L;
   const Geo& g = a.g;
   int unit, h, b;
   splitk_unit_of(g, unit, h, b);
@@ -3083,7 +3117,7 @@ __global__ __launch_bounds__(kThreads, GQ <= 4 ? 4 : 2) void decode_mfma_kernel(
   if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;  // lengths beyond the launch bound are cut
   if (unit > (n_chunks + 3) / 4) return;
   if (unit == 0) band_unit<GQ>(L, a, b, h, T);
-  else int2_unit_mfma<GQ, TOK>(L, a, b, h, T, unit - 1);
+  else int2_unit_mfma<GQ, TOK, BITS>(L, a, b, h, T, unit - 1);
 }
 
 // Matrix-core INT4 per-token launch (page pairs; no band: unit 0 stores an empty partial).
@@ -3325,12 +3359,13 @@ hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
     // AUTO: 16-bit operands on the nibble dot product for INT2, the fp32 kernel for INT4 (faster there:
     // per-token scales leave the fp32 path no per-group work, and 4-bit codes convert cheaply)
     if (g.scheme == KVQ_INT4_CHANNEL) {
-      hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_CHANNEL, 2>), grid, block, 0, s, a);
+      if (a.impl == KVQ_DECODE_MFMA) hipLaunchKernelGGL((decode_mfma_kernel<GQ, false, 4>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT4_CHANNEL, 2>), grid, block, 0, s, a);
     } else if (g.scheme == KVQ_INT2_TOKEN) {
-      if (a.impl == KVQ_DECODE_MFMA) hipLaunchKernelGGL((decode_mfma_kernel<GQ, true>), grid, block, 0, s, a);
+      if (a.impl == KVQ_DECODE_MFMA) hipLaunchKernelGGL((decode_mfma_kernel<GQ, true, 2>), grid, block, 0, s, a);
       else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_TOKEN, 2>), grid, block, 0, s, a);
     } else if (g.scheme == KVQ_INT2_CHANNEL) {
-      if (a.impl == KVQ_DECODE_MFMA) hipLaunchKernelGGL((decode_mfma_kernel<GQ, false>), grid, block, 0, s, a);
+      if (a.impl == KVQ_DECODE_MFMA) hipLaunchKernelGGL((decode_mfma_kernel<GQ, false, 2>), grid, block, 0, s, a);
       else if (a.impl == KVQ_DECODE_F32) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 0>), grid, block, 0, s, a);
       else if (a.impl == KVQ_DECODE_DOT16) hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 1>), grid, block, 0, s, a);
       else hipLaunchKernelGGL((decode_valu_kernel<GQ, KVQ_INT2_CHANNEL, 2>), grid, block, 0, s, a);

@@ -122,15 +122,14 @@ typedef enum { KVQ_ROT_DENSE = 0, KVQ_ROT_HADAMARD = 1 } kvq_rotation;
            scale 65535) in four 4-bit digits, on the 8-way nibble dot product; 2-bit codes unpack with a
            mask, 4-bit codes not at all (per-token schemes: the rotated query once per work-group).  INT4
            per token walks page pairs, so an explicit split_tokens must be a multiple of 128;
-   MFMA  - the INT2 schemes and INT4_TOKEN: the DOT16 operands (key-side operand and softmax weights, times the
+   MFMA  - every scheme: the DOT16 operands (key-side operand and softmax weights, times the
            value scales for the per-token schemes, as 16-bit integers, two signed bytes) multiplied with the
            2-bit or 4-bit codes on the int8 matrix cores, 16 x 16 x 64 products whose rows are (query head, byte
            limb) pairs, so the query heads of a kv head share one pass over the codes; every wave walks a chunk
            of its own (split_tokens = 0: 1 to 32 groups, or 2 to 32 pages, per chunk, chosen by size); INT4_TOKEN
            walks page pairs, so an explicit split_tokens must be a multiple of 128;
-   AUTO  - MFMA for INT2_CHANNEL, INT2_TOKEN and INT4_TOKEN (INT4_TOKEN with a split of an odd number of pages:
-           F32), DOT8 for INT4_CHANNEL.
-   INT2_TOKEN is built with MFMA and DOT8, INT4_CHANNEL with DOT8 (the others return KVQ_EUNSUPPORTED). */
+   AUTO  - MFMA (INT4_TOKEN with a split of an odd number of pages: F32).
+   INT2_TOKEN and INT4_CHANNEL are built with MFMA and DOT8 (F32 and DOT16 return KVQ_EUNSUPPORTED for them). */
 typedef enum {
   KVQ_DECODE_AUTO = 0,
   KVQ_DECODE_F32 = 1,

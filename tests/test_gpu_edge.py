@@ -344,3 +344,18 @@ def test_matrix_core_decode_per_token_boundary_lengths_and_constant_tokens(K, T)
     chunks = [1] * T if T < 8 else [T // 3, T - T // 3]
     _write_and_check(K, synth.scaled(WL, scheme="int2_token"), _bf16(k), _bf16(v), chunks=chunks,
                      decode_impl=K.DECODE_MFMA)
+
+
+@pytest.mark.parametrize("T", [5, 260, 389, 517])
+def test_matrix_core_decode_per_channel_int4_edges(K, T):
+    """Per-channel INT4 on the matrix cores: boundary lengths, an all-zero group and constant tokens."""
+    rng = np.random.default_rng(500 + T)
+    k = rng.standard_normal((T, 2, 128)).astype(np.float32)
+    v = rng.standard_normal((T, 2, 128)).astype(np.float32)
+    if T > 260:
+        k[4:132] = 0.0
+        v[132:260, 1, :] = -2.0
+    _say(f"matrix-core decode, per-channel INT4: T={T}")
+    chunks = [1] * T if T < 8 else [T // 3, T - T // 3]
+    _write_and_check(K, synth.scaled(WL, scheme="int4_channel"), _bf16(k), _bf16(v), chunks=chunks,
+                     decode_impl=K.DECODE_MFMA)

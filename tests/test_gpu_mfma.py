@@ -241,3 +241,62 @@ def test_mfma_int4_token_full_sampled(K):
     assert np.isfinite(out).all()
     worst = check_out(bc, out, q, [(0, 0), (15, 7)])
     _say(f"   worst |mfma - oracle| = {worst:.2e}")
+
+
+# ------------------------------------------------------------------ per-channel INT4 on the matrix cores
+
+
+def _c4(wl, **kw):
+    return synth.scaled(wl, scheme="int4_channel", **kw)
+
+
+def test_mfma_int4_channel_single_head_fp32_source(K):
+    _say("mfma per-channel INT4: tiny 1 head, T=4096, fp32 source with x10 outlier channels, 20 appends")
+    _case(K, _c4(synth.WORKLOADS["tiny_1h_4k"]), [4096], [0], append_steps=20)
+
+
+def test_mfma_int4_channel_gqa2_ragged_with_appends(K):
+    wl = _c4(synth.WORKLOADS["gqa_b1_32k"], n_q_heads=16, n_kv_heads=8)
+    lens = [2900, 1000, 133, 0]
+    _say(f"mfma per-channel INT4: GQA 2, lens={lens}, 5 appends")
+    _case(K, wl, lens, [0, 3, 7], append_steps=5)
+
+
+@pytest.mark.parametrize("split", [0, 256])
+def test_mfma_int4_channel_gqa4_batch(K, split):
+    wl = _c4(synth.WORKLOADS["batch32_32k"])
+    lens = [4100, 2000, 260, 1029, 3000, 388]
+    _say(f"mfma per-channel INT4: GQA 4, lens={lens}, split {split}, 800-token prefill chunks, 2 appends")
+    _case(K, wl, lens, [0, 5], append_steps=2, chunk=800, split=split)
+
+
+def test_mfma_int4_channel_gqa8_decaying_spectrum(K):
+    wl = _c4(synth.WORKLOADS["long_b4_131k"], batch=2)
+    _say("mfma per-channel INT4: GQA 8, sigma_c = (c+1)^-0.5, lens [3000, 700], split 512")
+    _case(K, wl, [3000, 700], [0, 5], chunk=1000, split=512)
+
+
+def test_mfma_int4_channel_agrees_with_dot8(K):
+    for name, lens in (("gqa_b1_32k", [2900, 1000]), ("long_b4_131k", [3000, 700])):
+        wl = _c4(synth.WORKLOADS[name])
+        bc = build_cache(K, wl, lens)
+        q = synth.queries(synth.scaled(wl, batch=len(lens)))
+        outs = {}
+        for nm, c in (("dot8", K.DECODE_DOT8), ("mfma", K.DECODE_MFMA)):
+            bc.cfg.decode_impl = c
+            outs[nm] = run_decode(K, bc, q)
+        d8 = np.abs(outs["mfma"] - outs["dot8"]).max()
+        _say(f"per-channel INT4 mfma vs dot8 on {name}: {d8:.2e}")
+        assert d8 <= TOL
+
+
+def test_mfma_int4_channel_batch32_full_sampled(K):
+    wl = _c4(synth.WORKLOADS["batch32_32k"])
+    lens = synth.seq_lens(wl)
+    _say("mfma per-channel INT4: batch32_32k full")
+    bc = build_cache(K, wl, lens, seqs_per_call=4, decode_impl=K.DECODE_MFMA)
+    q = synth.queries(wl)
+    out = run_decode(K, bc, q)
+    assert np.isfinite(out).all()
+    worst = check_out(bc, out, q, [(0, 1), (31, 6)])
+    _say(f"   worst |mfma - oracle| = {worst:.2e}")

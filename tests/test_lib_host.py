@@ -166,7 +166,7 @@ def test_matrix_core_decode_schemes():
             (K.INT2_CHANNEL, K.ROT_DENSE, 4, 128, 0.96, 0.92, K.KVQ_OK),
             (K.INT2_CHANNEL, K.ROT_HADAMARD, 4, 256, 0.96, 0.92, K.KVQ_OK),
             (K.INT2_TOKEN, K.ROT_DENSE, 4, 128, 0.96, 0.92, K.KVQ_OK),
-            (K.INT4_CHANNEL, K.ROT_DENSE, 4, 128, 0.96, 0.92, K.KVQ_EUNSUPPORTED),
+            (K.INT4_CHANNEL, K.ROT_DENSE, 4, 128, 0.96, 0.92, K.KVQ_OK),
             (K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0, K.KVQ_OK)):
         for split in (0, 512):
             cfg = K.make_config(8, 32, scheme=scheme, rotation=rot, n_sink=s0, n_recent=w, clip_k=ck, clip_v=cv,
@@ -190,9 +190,9 @@ def test_int2_token_scheme_config():
 
 
 def test_int4_channel_scheme_config():
-    """Per-channel INT4: the INT2 groups, band and page count on the INT4 page size; built on DOT8 only."""
-    for impl, want in ((K.DECODE_AUTO, K.KVQ_OK), (K.DECODE_DOT8, K.KVQ_OK), (K.DECODE_F32, K.KVQ_EUNSUPPORTED),
-                       (K.DECODE_DOT16, K.KVQ_EUNSUPPORTED)):
+    """Per-channel INT4: the INT2 groups, band and page count on the INT4 page size; built on DOT8 and MFMA."""
+    for impl, want in ((K.DECODE_AUTO, K.KVQ_OK), (K.DECODE_DOT8, K.KVQ_OK), (K.DECODE_MFMA, K.KVQ_OK),
+                       (K.DECODE_F32, K.KVQ_EUNSUPPORTED), (K.DECODE_DOT16, K.KVQ_EUNSUPPORTED)):
         assert K.check_config(K.make_config(8, 32, scheme=K.INT4_CHANNEL, decode_impl=impl)) == want
     a = K.make_config(8, 32, scheme=K.INT4_CHANNEL)
     c = K.make_config(8, 32, scheme=K.INT2_CHANNEL)
