@@ -79,12 +79,12 @@ int chunk_units(const kvq_config* c, int batch, int max_seq_len) {
   else units = (max_seq_len + PAGE - 1) / PAGE;
   const int pairs = batch * c->n_kv_heads;
   if (uses_mfma(c)) {
-    // one chunk per wave, long enough that a wave's copies stay in flight across many groups, short enough
-    // that the chunks of all (sequence, kv head) pairs fill the GPU about once: ~2048 wave chunks, a power
-    // of two from 1 to 32 groups
+    // one chunk per wave, long enough that a wave's copies stay in flight across several groups, short
+    // enough that small launches still spread over the GPU: about 512 wave chunks or more, a power of two
+    // from 1 to 32 groups (measured: batch 1 x 32k takes 4 groups, batch 32 x 32k 32)
     const long long total = (long long)pairs * units;
     int per = c->scheme == KVQ_INT4_TOKEN ? 2 : 1;  // INT4 per token: whole page pairs
-    while (per < 32 && (long long)per * 2048 < total) per *= 2;
+    while (per < 32 && (long long)per * 512 < total) per *= 2;
     return per;
   }
   const int target_wgs = 2048;
