@@ -3192,7 +3192,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 // partials (rotated value frame) are combined with their softmax weights 2^(m_u - M); the results are
 // un-rotated by R_V^T, which the work-group reads once for all its heads (every element by one thread),
 // combined with the band partial (original frame) and normalized.  The weighted sum over chunks spreads
-// (channel quad, chunk slice) over 256 threads so that the partials' loads are all in flight.
+// (channel quad, chunk slice) over 256 threads; each slice keeps a running maximum of its own, so the
+// partials, the band partial and the R_V rows are all loaded before the first wait.
 // ---------------------------------------------------------------------------------------------
 constexpr int kMergeSlices = 8;  // chunk slices of the weighted sum (threads = 32 channel quads x 8 slices)
 
@@ -3209,76 +3210,120 @@ struct MergeShape {
 template <int GQ, int HPW>
 __global__ __launch_bounds__(MergeShape<HPW>::NT) void merge_kernel(DecodeArgs a) {
   constexpr int SUB = MergeShape<HPW>::SUB, NT = MergeShape<HPW>::NT, PARTS = MergeShape<HPW>::PARTS;
+  constexpr int CPP = D / PARTS;  // channels per part of the dense un-rotation
+  static_assert(HPW * D <= NT, "every thread owns at most one output element");
   __shared__ float Ms[HPW], Ls[HPW];
   __shared__ float4 osum[SUB][kMergeSlices][D / 4];
+  __shared__ float sm[SUB][kMergeSlices], sl_sum[SUB][kMergeSlices];
   __shared__ float ob[HPW][D];
   __shared__ float un[PARTS][HPW][D];
   const Geo& g = a.g;
-  const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int T = a.seq_lens[b];
-  int n_chunks;
-  if (is_grouped(g.scheme)) {
-    const int ng = n_groups_of(T, g.S0, g.W);
-    n_chunks = (ng + g.gpc - 1) / g.gpc;
-  } else {
-    n_chunks = ((T + PAGE - 1) / PAGE + g.gpc - 1) / g.gpc;
-  }
-  if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;
+  const int b = blockIdx.y, tid = threadIdx.x;
   const long long q0 = (long long)b * g.n_q + (long long)blockIdx.x * HPW;  // first q head of this work-group
   auto part_of = [&](int hh) { return a.partials + (q0 + hh) * g.n_units * PART_STRIDE; };  // unit 0: band
-
-  // 1. per head (one wave each): M = max over chunks of m_u, L = sum_u 2^(m_u - M) l_u
-  for (int hh = wave; hh < HPW; hh += NT / 64) {
-    const float* base = part_of(hh);
-    float mx = -INFINITY;
-    for (int u = 1 + lane; u <= n_chunks; u += 64) mx = fmaxf(mx, base[u * PART_STRIDE]);
-    mx = wave_max(mx);
-    float ls = 0.0f;
-    for (int u = 1 + lane; u <= n_chunks; u += 64)
-      ls = fmaf(exp2_safe_diff(base[u * PART_STRIDE], mx), base[u * PART_STRIDE + 1], ls);
-    ls = wave_sum(ls);
-    if (lane == 0) {
-      Ms[hh] = mx;
-      Ls[hh] = ls;
-    }
+  // The loads are issued before the first wait, so that a merge of up to eight chunks takes one memory
+  // round trip rather than one per phase: this thread's band-partial element, its range of an R_V row
+  // and the first chunk partial of its slice are read before the sequence length has arrived.
+  const bool owns = tid < HPW * D;
+  const int eh = tid / D, ec = tid % D;  // the output element (head, channel) this thread writes
+  float band_m = -INFINITY, band_l = 0.0f, band_o = 0.0f;
+  if (owns) {
+    const float* bb = part_of(eh);
+    band_m = bb[0];
+    band_l = bb[1];
+    band_o = bb[2 + ec];
   }
-  __syncthreads();
-  // 2. per head: o[c] = sum_u 2^(m_u - M) o_u[c]; sub-block sb takes heads sb, sb + SUB, ..; its thread
-  // (channel quad cq, slice sl) sums chunks u = sl + 1 + 8k
+  const bool dense = !g.key_only && g.rotation == KVQ_ROT_DENSE;
+  const int rj = tid & (D - 1), rpart = tid / D;  // dense un-rotation: row rj, channel range rpart
+  float4 rrow[CPP / 4];
+  if (dense) {
+    const float4* row = reinterpret_cast<const float4*>(a.rot_v + rj * D + rpart * CPP);
+#pragma unroll
+    for (int i = 0; i < CPP / 4; ++i) rrow[i] = row[i];
+  }
+  const int n_max = g.n_units - 1;
+  int n_chunks = 0, seq_len = 0;  // set on the first pass below, once the first partials are in flight
+
+  // 1. per head: M = max_u m_u, L = sum_u 2^(m_u - M) l_u, o[c] = sum_u 2^(m_u - M) o_u[c].  Sub-block sb
+  // takes heads sb, sb + SUB, ..; its thread (channel quad cq, slice sl) folds chunks u = sl + 1 + 8k into
+  // a running (max, sum, o) of its own, and the slices are combined in LDS with their own maxima.
   const int sb = tid >> 8, lt = tid & 255;
   const int cq = lt & (D / 4 - 1), sl = lt / (D / 4);
 #pragma unroll 1
   for (int h0 = 0; h0 < HPW; h0 += SUB) {
     const int hh = h0 + sb;
     const float* base = part_of(hh);
-    const float M = Ms[hh];
+    float mloc = -INFINITY, lloc = 0.0f;
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    auto load = [&](int u, float& mu, float& lu, float2& o01, float2& o23) {
+      const float* pu = base + u * PART_STRIDE;
+      mu = pu[0];
+      lu = pu[1];
+      const float* o = pu + 2 + 4 * cq;  // 8-byte aligned: two float2 loads
+      o01 = *reinterpret_cast<const float2*>(o);
+      o23 = *reinterpret_cast<const float2*>(o + 2);
+    };
+    auto fold = [&](float mu, float lu, float2 o01, float2 o23) {
+      const float mn = fmaxf(mloc, mu);
+      const float sc = exp2_safe_diff(mloc, mn), w = exp2_safe_diff(mu, mn);
+      acc.x = fmaf(w, o01.x, acc.x * sc);
+      acc.y = fmaf(w, o01.y, acc.y * sc);
+      acc.z = fmaf(w, o23.x, acc.z * sc);
+      acc.w = fmaf(w, o23.y, acc.w * sc);
+      lloc = fmaf(w, lu, lloc * sc);
+      mloc = mn;
+    };
+    // the slice's first chunk is read without a branch (an existing unit, unit 0 when the launch has
+    // no chunk units; it is dropped below when past the sequence's chunk count)
+    float mu, lu;
+    float2 o01, o23;
+    const int u1 = 1 + sl;
+    load(u1 <= n_max ? u1 : n_max, mu, lu, o01, o23);
+    if (h0 == 0) {
+      const int T = a.seq_lens[b];
+      if (is_grouped(g.scheme)) {
+        n_chunks = (n_groups_of(T, g.S0, g.W) + g.gpc - 1) / g.gpc;
+      } else {
+        n_chunks = ((T + PAGE - 1) / PAGE + g.gpc - 1) / g.gpc;
+      }
+      if (n_chunks > n_max) n_chunks = n_max;
+      seq_len = T;
+    }
+    if (u1 <= n_chunks) fold(mu, lu, o01, o23);
 #pragma unroll 4
-    for (int u = 1 + sl; u <= n_chunks; u += kMergeSlices) {
-      const float w = exp2_safe_diff(base[u * PART_STRIDE], M);
-      const float* o = base + u * PART_STRIDE + 2 + 4 * cq;  // 8-byte aligned: two float2 loads
-      const float2 o01 = *reinterpret_cast<const float2*>(o), o23 = *reinterpret_cast<const float2*>(o + 2);
-      acc.x = fmaf(w, o01.x, acc.x);
-      acc.y = fmaf(w, o01.y, acc.y);
-      acc.z = fmaf(w, o23.x, acc.z);
-      acc.w = fmaf(w, o23.y, acc.w);
+    for (int u = u1 + kMergeSlices; u <= n_chunks; u += kMergeSlices) {
+      load(u, mu, lu, o01, o23);
+      fold(mu, lu, o01, o23);
     }
     osum[sb][sl][cq] = acc;
+    if (cq == 0) {
+      sm[sb][sl] = mloc;
+      sl_sum[sb][sl] = lloc;
+    }
     __syncthreads();
     if (lt < D) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int s2 = 0; s2 < kMergeSlices; ++s2) M = fmaxf(M, sm[sb][s2]);
       const int k = lt & 3;
-      float v = 0.0f;
+      float v = 0.0f, L = 0.0f;
 #pragma unroll
       for (int s2 = 0; s2 < kMergeSlices; ++s2) {
+        const float w = exp2_safe_diff(sm[sb][s2], M);
         const float4 t = osum[sb][s2][lt >> 2];
-        v += k == 0 ? t.x : k == 1 ? t.y : k == 2 ? t.z : t.w;
+        v = fmaf(w, k == 0 ? t.x : k == 1 ? t.y : k == 2 ? t.z : t.w, v);
+        L = fmaf(w, sl_sum[sb][s2], L);
       }
       ob[hh][lt] = v;
+      if (lt == 0) {
+        Ms[hh] = M;
+        Ls[hh] = L;
+      }
     }
     __syncthreads();
   }
-  // 3. un-rotate every head: o_j = sum_c ob[c] R_V[j][c] (dense: thread (j, part) reads the part-th
-  // range of row j of R_V, once for all heads), the randomized Hadamard's inverse, or nothing under
+  // 2. un-rotate every head: o_j = sum_c ob[c] R_V[j][c] (dense: thread (j, part) holds the part-th
+  // range of row j of R_V, applied to all heads), the randomized Hadamard's inverse, or nothing under
   // key-only rotation
   if (g.key_only) {
     for (int e = tid; e < HPW * D; e += NT) {
@@ -3286,17 +3331,14 @@ __global__ __launch_bounds__(MergeShape<HPW>::NT) void merge_kernel(DecodeArgs a
 #pragma unroll
       for (int p = 1; p < PARTS; ++p) un[p][e / D][e % D] = 0.0f;
     }
-  } else if (g.rotation == KVQ_ROT_DENSE) {
-    constexpr int CPP = D / PARTS;  // channels per part
-    const int j = tid & (D - 1), part = tid / D;
-    const float4* row = reinterpret_cast<const float4*>(a.rot_v + j * D + part * CPP);
+  } else if (dense) {
     float s0[HPW], s1[HPW];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) s0[hh] = s1[hh] = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPP / 4; ++i) {
-      const float4 r = row[i];
-      const int c = part * CPP + 4 * i;
+      const float4 r = rrow[i];
+      const int c = rpart * CPP + 4 * i;
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
         s0[hh] = fmaf(ob[hh][c], r.x, s0[hh]);
@@ -3306,7 +3348,7 @@ __global__ __launch_bounds__(MergeShape<HPW>::NT) void merge_kernel(DecodeArgs a
       }
     }
 #pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) un[part][hh][j] = s0[hh] + s1[hh];
+    for (int hh = 0; hh < HPW; ++hh) un[rpart][hh][rj] = s0[hh] + s1[hh];
   } else {
     // (ob H_blk) * sign / sqrt(h): FWHT within blocks of h channels in LDS, all heads at once
     for (int hb = 1; hb < g.hblock; hb <<= 1) {
@@ -3328,24 +3370,22 @@ __global__ __launch_bounds__(MergeShape<HPW>::NT) void merge_kernel(DecodeArgs a
     }
   }
   __syncthreads();
-  // 4. combine with the band partial (unit 0, original frame) and normalize
-  for (int e = tid; e < HPW * D; e += NT) {
-    const int hh = e / D, c = e % D;
-    const float* base = part_of(hh);
-    const float M = Ms[hh];
-    const float mb = (T > 0) ? base[0] : -INFINITY;
+  // 3. combine with the band partial (unit 0, original frame) and normalize
+  if (owns) {
+    const float M = Ms[eh];
+    const float mb = (seq_len > 0) ? band_m : -INFINITY;
     const float Mf = fmaxf(M, mb);
     float res = 0.0f;
     if (Mf != -INFINITY) {
       float o = 0.0f;
 #pragma unroll
-      for (int p = 0; p < PARTS; ++p) o += un[p][hh][c];
+      for (int p = 0; p < PARTS; ++p) o += un[p][eh][ec];
       const float si = exp2_safe_diff(M, Mf), sb2 = exp2_safe_diff(mb, Mf);
-      const float num = o * si + (mb == -INFINITY ? 0.0f : base[2 + c] * sb2);
-      const float den = Ls[hh] * si + (mb == -INFINITY ? 0.0f : base[1] * sb2);
+      const float num = o * si + (mb == -INFINITY ? 0.0f : band_o * sb2);
+      const float den = Ls[eh] * si + (mb == -INFINITY ? 0.0f : band_l * sb2);
       res = num / den;
     }
-    a.out[(q0 + hh) * D + c] = res;
+    a.out[(q0 + eh) * D + ec] = res;
   }
 }
 
