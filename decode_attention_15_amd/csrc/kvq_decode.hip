@@ -3188,28 +3188,32 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 // Merge ([OSCAR] §3.4.5 step 4, the second kernel of the split decode; [NOVA] App. B.5): one work-group
-// per (kv head, seq) for its GQ query heads, 256 threads per head up to 4 heads.  Per head, the chunk
+// per (kv head, seq) for its GQ query heads, 256 threads per head up to 4 heads (or one work-group of
+// 1024 threads per q head when the pairs are few).  Per head, the chunk
 // partials (rotated value frame) are combined with their softmax weights 2^(m_u - M); the results are
 // un-rotated by R_V^T, which the work-group reads once for all its heads (every element by one thread),
 // combined with the band partial (original frame) and normalized.  The weighted sum over chunks spreads
-// (channel quad, chunk slice) over 256 threads; each slice keeps a running maximum of its own, so the
+// (channel quad, chunk slice) over the threads; each slice keeps a running maximum of its own, so the
 // partials, the band partial and the R_V rows are all loaded before the first wait.
 // ---------------------------------------------------------------------------------------------
-constexpr int kMergeSlices = 8;  // chunk slices of the weighted sum (threads = 32 channel quads x 8 slices)
-
 // HPW: query heads per work-group (all GQ heads of a kv head when there are enough (seq, kv head)
 // pairs to fill the chip, else one, so that long contexts with few sequences still spread their
-// chunk partials over many work-groups).
+// chunk partials over many work-groups).  One head per work-group takes 32 chunk slices (1024
+// threads), so that the many chunks of a long context are read with four times the loads in flight.
 template <int HPW>
 struct MergeShape {
-  static constexpr int SUB = HPW < 4 ? HPW : 4;  // 256-thread sub-blocks, one head each at a time
-  static constexpr int NT = 256 * SUB;           // threads
-  static constexpr int PARTS = NT / D;           // channel ranges of the un-rotation
+  static constexpr int SUB = HPW < 4 ? HPW : 4;     // sub-blocks, one head each at a time
+  static constexpr int SL = HPW == 1 ? 32 : 8;      // chunk slices of a sub-block
+  static constexpr int SUBT = (D / 4) * SL;         // threads of a sub-block: channel quads x slices
+  static constexpr int NT = SUBT * SUB;             // threads
+  static constexpr int PARTS = NT / D;              // channel ranges of the un-rotation
 };
 
 template <int GQ, int HPW>
 __global__ __launch_bounds__(MergeShape<HPW>::NT) void merge_kernel(DecodeArgs a) {
   constexpr int SUB = MergeShape<HPW>::SUB, NT = MergeShape<HPW>::NT, PARTS = MergeShape<HPW>::PARTS;
+  constexpr int kMergeSlices = MergeShape<HPW>::SL, SUBT = MergeShape<HPW>::SUBT;
+  static_assert(NT <= 1024 && SUBT >= D, "work-group shape");
   constexpr int CPP = D / PARTS;  // channels per part of the dense un-rotation
   static_assert(HPW * D <= NT, "every thread owns at most one output element");
   __shared__ float Ms[HPW], Ls[HPW];
@@ -3245,9 +3249,9 @@ __global__ __launch_bounds__(MergeShape<HPW>::NT) void merge_kernel(DecodeArgs a
   int n_chunks = 0, seq_len = 0;  // set on the first pass below, once the first partials are in flight
 
   // 1. per head: M = max_u m_u, L = sum_u 2^(m_u - M) l_u, o[c] = sum_u 2^(m_u - M) o_u[c].  Sub-block sb
-  // takes heads sb, sb + SUB, ..; its thread (channel quad cq, slice sl) folds chunks u = sl + 1 + 8k into
+  // takes heads sb, sb + SUB, ..; its thread (channel quad cq, slice sl) folds chunks u = sl + 1 + SL k into
   // a running (max, sum, o) of its own, and the slices are combined in LDS with their own maxima.
-  const int sb = tid >> 8, lt = tid & 255;
+  const int sb = tid / SUBT, lt = tid % SUBT;
   const int cq = lt & (D / 4 - 1), sl = lt / (D / 4);
 #pragma unroll 1
   for (int h0 = 0; h0 < HPW; h0 += SUB) {
