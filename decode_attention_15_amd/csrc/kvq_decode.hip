@@ -91,21 +91,25 @@ __global__ __launch_bounds__(512) void qprep_kernel(DecodeArgs a) {
   const int j = tid & (D - 1), qtr = tid >> 7;  // column j, quarter qtr of the 128 input channels
   const long long base = ((long long)b * a.g.n_q + h * GQ) * D;
   const float scale = LOG2E * kInvSqrt128;
+  const bool dense = a.g.rotation == KVQ_ROT_DENSE;
+  // this thread's 32 entries of column j of R_K, read together with the queries (one round trip)
+  float rk[32];
+  if (dense) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) rk[i] = a.rot_k[(qtr * 32 + i) * D + j];
+  }
   for (int e = tid; e < GQ * D; e += 512) {
     const int hh = e / D, c = e % D;
     const float qv = a.q_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[base + e])
                               : static_cast<const float*>(a.q)[base + e];
     a.qband[base + e] = qv * scale;
-    qs[hh][c] = a.g.rotation == KVQ_ROT_DENSE ? qv : qv * a.rot_k[c];
+    qs[hh][c] = dense ? qv : qv * a.rot_k[c];
   }
   __syncthreads();
-  if (a.g.rotation == KVQ_ROT_DENSE) {
+  if (dense) {
     float r[GQ];
 #pragma unroll
     for (int hh = 0; hh < GQ; ++hh) r[hh] = 0.0f;
-    float rk[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) rk[i] = a.rot_k[(qtr * 32 + i) * D + j];
 #pragma unroll
     for (int i = 0; i < 32; ++i)
 #pragma unroll
