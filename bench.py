@@ -34,7 +34,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batch32_32k")
-    ap.add_argument("--impl", default="auto", choices=["auto", "f32", "dot16", "dot8", "mfma"])
+    ap.add_argument("--impl", default="auto", choices=["auto", "f32", "mfma"])
     ap.add_argument("--scheme", default=None, choices=["int2_channel", "int2_token", "int4_channel"],
                     help="INT2 workloads: quantize per channel over 128-token groups (the workloads' statement), "
                          "per token over its 128 channels, or per channel with 4-bit codes")
@@ -351,8 +351,7 @@ def main():
     lens_end = synth.seq_lens(wl).astype(np.int64)          # lengths after the last timed step
     lens_start = lens_end - n_steps
     T_end = int(lens_end.max())
-    impl = {"auto": K.DECODE_AUTO, "f32": K.DECODE_F32, "dot16": K.DECODE_DOT16, "dot8": K.DECODE_DOT8,
-            "mfma": K.DECODE_MFMA}[args.impl]
+    impl = {"auto": K.DECODE_AUTO, "f32": K.DECODE_F32, "mfma": K.DECODE_MFMA}[args.impl]
     split = args.split if args.split else (wl.split_tokens if wl.name == "long_b4_131k" else 0)
     if int2:
         scheme = GROUPED[wl.scheme]

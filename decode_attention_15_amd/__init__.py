@@ -32,7 +32,7 @@ KVQ_OK, KVQ_EINVAL, KVQ_ERANGE, KVQ_ENOSPACE, KVQ_EUNSUPPORTED, KVQ_EDEVICE = 0,
 INT2_CHANNEL, INT4_TOKEN, INT2_TOKEN, INT4_CHANNEL = 0, 1, 2, 3
 F32, BF16 = 0, 1
 ROT_DENSE, ROT_HADAMARD = 0, 1
-DECODE_AUTO, DECODE_F32, DECODE_MFMA, DECODE_DOT16, DECODE_DOT8 = 0, 1, 2, 3, 4
+DECODE_AUTO, DECODE_F32, DECODE_MFMA = 0, 1, 2
 STAGE_QPREP, STAGE_SPLITK, STAGE_MERGE, STAGE_ALL = 1, 2, 4, 7
 
 

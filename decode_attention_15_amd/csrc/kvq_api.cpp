@@ -28,17 +28,14 @@ int check_config(const kvq_config* c) {
   if (!(c->clip_k > 0.0f && c->clip_k <= 1.0f) || !(c->clip_v > 0.0f && c->clip_v <= 1.0f)) return KVQ_EINVAL;
   const int unit = is_grouped(c->scheme) ? GROUP : PAGE;
   if (c->split_tokens < 0 || c->split_tokens % unit != 0) return KVQ_EINVAL;
-  if (c->decode_impl != KVQ_DECODE_AUTO && c->decode_impl != KVQ_DECODE_F32 && c->decode_impl != KVQ_DECODE_MFMA &&
-      c->decode_impl != KVQ_DECODE_DOT16 && c->decode_impl != KVQ_DECODE_DOT8)
+  if (c->decode_impl != KVQ_DECODE_AUTO && c->decode_impl != KVQ_DECODE_F32 && c->decode_impl != KVQ_DECODE_MFMA)
     return KVQ_EINVAL;
-  // the matrix-core decode is built for every scheme
-  // nibble digits and matrix cores for INT4 per token walk page pairs: an explicit split must hold whole pairs
-  if ((c->decode_impl == KVQ_DECODE_DOT8 || c->decode_impl == KVQ_DECODE_MFMA) && c->scheme == KVQ_INT4_TOKEN &&
-      c->split_tokens % (2 * PAGE) != 0)
+  // the matrix-core decode is built for every scheme; it walks INT4 per token in page pairs, so an explicit
+  // split must hold whole pairs there
+  if (c->decode_impl == KVQ_DECODE_MFMA && c->scheme == KVQ_INT4_TOKEN && c->split_tokens % (2 * PAGE) != 0)
     return KVQ_EUNSUPPORTED;
-  // per-token INT2 and per-channel INT4 are built on the nibble dot product and the matrix cores
-  if ((c->scheme == KVQ_INT2_TOKEN || c->scheme == KVQ_INT4_CHANNEL) && c->decode_impl != KVQ_DECODE_AUTO &&
-      c->decode_impl != KVQ_DECODE_DOT8 && c->decode_impl != KVQ_DECODE_MFMA)
+  // the fp32 decode (exact cross-check) is built for INT2 per channel and INT4 per token
+  if (c->decode_impl == KVQ_DECODE_F32 && c->scheme != KVQ_INT2_CHANNEL && c->scheme != KVQ_INT4_TOKEN)
     return KVQ_EUNSUPPORTED;
   if (c->key_only_rotation != 0 && c->key_only_rotation != 1) return KVQ_EINVAL;
   const int hb = c->hadamard_block;
@@ -334,15 +331,9 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
   const int per = chunk_units(cfg, cache->batch, max_seq_len_host);
   a.g.gpc = per;
   a.g.n_units = 1 + max_chunks_of(cfg, max_seq_len_host, per);
-  // the nibble-digit decode: every grouped scheme by default; INT4 per token by default when its chunks
-  // hold whole page pairs
+  // the matrix-core decode walks one chunk per wave (four per work-group); the fp32 decode one per work-group
   const bool mfma = uses_mfma(cfg);
-  const bool dot8 = !mfma && (cfg->decode_impl == KVQ_DECODE_DOT8 ||
-                              (cfg->decode_impl == KVQ_DECODE_AUTO && (is_grouped(cfg->scheme) || per % 2 == 0)));
-  // an explicit split on the nibble-digit path: one chunk per wave (a work-group takes four), so that every
-  // wave walks several groups with its copies in flight, with one partial per chunk as with any split
-  // the matrix-core decode always walks one chunk per wave
-  a.g.wave_chunks = (mfma || (cfg->split_tokens > 0 && dot8)) ? 1 : 0;
+  a.g.wave_chunks = mfma ? 1 : 0;
   a.pages = static_cast<const uint8_t*>(cache->pages);
   a.band = static_cast<const uint16_t*>(cache->band);
   a.page_table = cache->page_table;
@@ -357,7 +348,7 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
   a.qrot = ws;
   a.qband = ws + nq * D;
   a.partials = ws + 2 * nq * D;
-  a.impl = mfma ? KVQ_DECODE_MFMA : dot8 ? KVQ_DECODE_DOT8 : cfg->decode_impl;
+  a.impl = mfma ? KVQ_DECODE_MFMA : KVQ_DECODE_F32;
   clear_stale_error();
   return to_status(launch_decode(a, stages, stream), "kv_decode_attn");
 }

@@ -113,29 +113,22 @@ typedef enum { KVQ_INT2_CHANNEL = 0, KVQ_INT4_TOKEN = 1, KVQ_INT2_TOKEN = 2, KVQ
 typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
 typedef enum { KVQ_ROT_DENSE = 0, KVQ_ROT_HADAMARD = 1 } kvq_rotation;
 /* Arithmetic of the quantized-token part of the decode (the bf16 band is always fp32):
-   F32   - fp32 FMA on the codes, per-group alpha = q~ s and softmax weights exact in fp32;
-   DOT16 - the key-side operand (INT2: alpha = q~ s per group and head; INT4: q~) and the softmax weights
-           (per group or page and head) rounded to 16-bit integers scaled to their maximum, multiplied
-           with the codes on the integer dot-product unit as two signed bytes;
-   DOT8  - the key-side operand as a 16-bit integer (full scale 30583) in four signed 4-bit digits and the
-           softmax weights (times the value scales for per-token schemes) as unsigned 16-bit integers (full
-           scale 65535) in four 4-bit digits, on the 8-way nibble dot product; 2-bit codes unpack with a
-           mask, 4-bit codes not at all (per-token schemes: the rotated query once per work-group).  INT4
-           per token walks page pairs, so an explicit split_tokens must be a multiple of 128;
-   MFMA  - every scheme: the DOT16 operands (key-side operand and softmax weights, times the
-           value scales for the per-token schemes, as 16-bit integers, two signed bytes) multiplied with the
-           2-bit or 4-bit codes on the int8 matrix cores, 16 x 16 x 64 products whose rows are (query head, byte
-           limb) pairs, so the query heads of a kv head share one pass over the codes; every wave walks a chunk
-           of its own (split_tokens = 0: 1 to 32 groups, or 2 to 32 pages, per chunk, chosen by size); INT4_TOKEN
-           walks page pairs, so an explicit split_tokens must be a multiple of 128;
-   AUTO  - MFMA (INT4_TOKEN with a split of an odd number of pages: F32).
-   INT2_TOKEN and INT4_CHANNEL are built with MFMA and DOT8 (F32 and DOT16 return KVQ_EUNSUPPORTED for them). */
+   MFMA  - every scheme: the key-side operand (per-channel schemes: alpha = q~ s per group and head; per-token
+           schemes: q~ once per walk) and the softmax weights (times the value scales for the per-token
+           schemes) rounded to integers scaled to their maximum, 4,000,000 for 2-bit codes and 1,000,000 for
+           4-bit codes (22 and 20 bits, so that every int32 sum over 128 codes stays exact), split into three
+           signed byte limbs and multiplied with the 2-bit or 4-bit codes on the int8 matrix cores, 16 x 16 x 64
+           products whose rows are (query head, limb) pairs, so the query heads of a kv head share one pass over
+           the codes; every wave walks a chunk of its own (split_tokens = 0: 1 to 32 groups, or 2 to 32 pages,
+           per chunk, chosen by size); INT4_TOKEN walks page pairs, so an explicit split_tokens must be a
+           multiple of 128;
+   F32   - fp32 FMA on the codes with exact per-group alpha = q~ s and softmax weights: the cross-check of the
+           matrix-core decode, built for INT2_CHANNEL and INT4_TOKEN (other schemes: KVQ_EUNSUPPORTED);
+   AUTO  - MFMA (INT4_TOKEN with a split of an odd number of pages: F32). */
 typedef enum {
   KVQ_DECODE_AUTO = 0,
   KVQ_DECODE_F32 = 1,
-  KVQ_DECODE_MFMA = 2,
-  KVQ_DECODE_DOT16 = 3,
-  KVQ_DECODE_DOT8 = 4
+  KVQ_DECODE_MFMA = 2
 } kvq_decode_impl;
 
 /* Static description of one attention layer's cache. */
@@ -152,10 +145,9 @@ typedef struct {
   float clip_k;          /* rho_K in (0, 1]; 1 = no clip (INT2 only) */
   float clip_v;          /* rho_V in (0, 1] */
   int32_t split_tokens;  /* quantized tokens per decode chunk, each merged from one partial: a multiple of 128
-                            (grouped schemes) or 64 (INT4_TOKEN), or 0 = chosen by size (one work-group per
-                            chunk; one wave per chunk on the matrix-core decode).  Given explicitly on the
-                            nibble-digit or matrix-core decode, each wave of a work-group walks a chunk of its
-                            own and a work-group takes four. */
+                            (grouped schemes) or 64 (INT4_TOKEN), or 0 = chosen by size.  On the matrix-core
+                            decode each wave of a work-group walks a chunk of its own and a work-group takes
+                            four; on the fp32 decode the four waves of a work-group share one chunk. */
   int32_t decode_impl;   /* kvq_decode_impl */
   int32_t key_only_rotation;  /* 0: K and V rotated (V by R_V on write, outputs un-rotated by R_V^T);
                                  1: only K rotated ([SAW] App. C default), V kept in its own frame and

@@ -1,9 +1,9 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
 
 Bar: codes, bf16 scales/zeros and band bytes bit-exact; attention outputs within 2e-3 absolute.  The fp32
-decode (DECODE_F32) differs from the fp64 oracle by fp32 rounding only; the integer-dot INT2 decodes (DOT16, DOT8)
-also rounds the per-group key coefficients and softmax weights to 16-bit integers, an error well inside
-the bar on these workloads (about 2e-4 at worst in a CPU model of that arithmetic).
+decode (DECODE_F32) differs from the fp64 oracle by fp32 rounding only; the default matrix-core decode also
+rounds the key-side operand and the softmax weights to 22-bit (2-bit codes) or 20-bit (4-bit codes) integers,
+far inside the bar.
 """
 import sys
 
@@ -81,12 +81,12 @@ def test_tiny_single_head_full(K):
     _say(f"  worst |diff| {worst:.2e}")
 
 
-@pytest.mark.parametrize("impl", ["auto", "f32", "dot16"])
+@pytest.mark.parametrize("impl", ["auto", "f32"])
 def test_gqa_ragged_batch(K, impl):
     wl = synth.WORKLOADS["gqa_b1_32k"]
     lens = [3000, 131, 700, 0, 260]
     _say(f"gqa ragged lens={lens} impl={impl}")
-    bc = build_cache(K, wl, lens, append_steps=5, decode_impl={"f32": K.DECODE_F32, "dot16": K.DECODE_DOT16}.get(impl, K.DECODE_AUTO))
+    bc = build_cache(K, wl, lens, append_steps=5, decode_impl={"f32": K.DECODE_F32}.get(impl, K.DECODE_AUTO))
     pages, band = _host(bc)
     for b in range(len(lens)):
         for h in (0, 3, 7):
@@ -120,13 +120,13 @@ def test_prefill_and_appends_give_identical_bytes(K):
             assert np.array_equal(ka, kb) and np.array_equal(va, vb)
 
 
-@pytest.mark.parametrize("impl", ["auto", "f32", "dot16"])
+@pytest.mark.parametrize("impl", ["auto", "f32"])
 def test_long_context_gq8_small(K, impl):
     wl = synth.scaled(synth.WORKLOADS["long_b4_131k"], batch=2)
     lens = [5000, 2222]
     _say(f"long gq8 small lens={lens}, split 512, impl={impl}")
     bc = build_cache(K, wl, lens, append_steps=3, split_tokens=512,
-                     decode_impl={"f32": K.DECODE_F32, "dot16": K.DECODE_DOT16}.get(impl, K.DECODE_AUTO))
+                     decode_impl={"f32": K.DECODE_F32}.get(impl, K.DECODE_AUTO))
     pages, band = _host(bc)
     for b in range(2):
         for h in (0, 5):
@@ -153,17 +153,16 @@ def test_split_size_does_not_change_the_result(K, scheme):
     check_out(bc, outs[-1], q, [(b, h) for b in range(2) for h in range(8)])
 
 
-@pytest.mark.parametrize("impl,split", [("auto", 0), ("f32", 0), ("dot16", 0), ("dot8", 0), ("auto", 64),
-                                        ("dot8", 128), ("dot8", 256)])
+@pytest.mark.parametrize("impl,split", [("auto", 0), ("f32", 0), ("auto", 64), ("mfma", 128), ("mfma", 256)])
 def test_saw_int4_small(K, impl, split):
-    """INT4 per token on every decode path: the automatic choice (nibble digits over page pairs; the fp32
+    """INT4 per token on every decode path: the automatic choice (matrix cores over page pairs; the fp32
     path for a 64-token split, whose chunks hold half pairs), each implementation explicitly, and explicit
     splits (one pair chunk per wave).  Lengths end inside a pair's second page, inside its first page
     (the pair's second page missing), and on a page boundary."""
     wl = synth.WORKLOADS["saw_int4_b16_16k"]
     lens = [1000, 333, 66, 40, 128]
     _say(f"saw int4 small lens={lens} impl={impl} split={split}")
-    code = {"f32": K.DECODE_F32, "dot16": K.DECODE_DOT16, "dot8": K.DECODE_DOT8}.get(impl, K.DECODE_AUTO)
+    code = {"f32": K.DECODE_F32, "mfma": K.DECODE_MFMA}.get(impl, K.DECODE_AUTO)
     bc = build_cache(K, wl, lens, append_steps=7, chunk=256, decode_impl=code, split_tokens=split)
     pages = bc.cache.pages.cpu().numpy()
     for b in range(len(lens)):
@@ -174,24 +173,22 @@ def test_saw_int4_small(K, impl, split):
     check_out(bc, out, q, [(b, h) for b in range(len(lens)) for h in range(8)])
 
 
-@pytest.mark.parametrize("impl", ["dot16", "dot8"])
-def test_integer_dot_decodes_agree_with_f32(K, impl):
-    """The 16-bit integer-dot decodes (byte limbs, nibble digits) against the fp32 decode on the same cache:
-    one head with an fp32 source and x10 outlier channels (4096 tokens), GQA 4 and GQA 8 INT2 caches and
-    the INT4 per-token cache; both within the oracle bar."""
-    code = {"dot16": K.DECODE_DOT16, "dot8": K.DECODE_DOT8}[impl]
+def test_matrix_core_decode_agrees_with_f32(K):
+    """The matrix-core decode against the fp32 decode on the same cache: one head with an fp32 source and x10
+    outlier channels (4096 tokens), GQA 4 and GQA 8 INT2 caches and the INT4 per-token cache; both within the
+    oracle bar."""
     for name, lens in (("tiny_1h_4k", [4096]), ("gqa_b1_32k", [2900, 1000]), ("long_b4_131k", [3000, 700]),
                        ("saw_int4_b16_16k", [1500, 300])):
         wl = synth.WORKLOADS[name]
-        _say(f"{impl} vs f32: {name} lens={lens}")
+        _say(f"mfma vs f32: {name} lens={lens}")
         bc = build_cache(K, wl, lens)
         q = synth.queries(synth.scaled(wl, batch=len(lens)))
         outs = []
-        for c in (K.DECODE_F32, code):
+        for c in (K.DECODE_F32, K.DECODE_MFMA):
             bc.cfg.decode_impl = c
             outs.append(run_decode(K, bc, q))
         diff = np.abs(outs[0] - outs[1]).max()
-        _say(f"   max |{impl} - f32| = {diff:.2e}")
+        _say(f"   max |mfma - f32| = {diff:.2e}")
         assert diff <= TOL
         check_out(bc, outs[1], q, [(b, h) for b in range(len(lens)) for h in range(wl.n_kv_heads)])
 

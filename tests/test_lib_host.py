@@ -146,17 +146,20 @@ def test_one_hip_runtime_in_the_process():
 def test_decode_implementations_accepted_for_both_schemes():
     for scheme, rot, s0, w, ck, cv in ((K.INT2_CHANNEL, K.ROT_DENSE, 4, 128, 0.96, 0.92),
                                        (K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0)):
-        for impl in (K.DECODE_AUTO, K.DECODE_F32, K.DECODE_DOT16, K.DECODE_DOT8):
+        for impl in (K.DECODE_AUTO, K.DECODE_F32, K.DECODE_MFMA):
             cfg = K.make_config(8, 32, scheme=scheme, rotation=rot, n_sink=s0, n_recent=w, clip_k=ck, clip_v=cv,
                                 decode_impl=impl)
             assert K.check_config(cfg) == K.KVQ_OK
-    # INT4 per token on the nibble digits and the matrix cores walks page pairs: an explicit split must hold
-    # whole pairs
+        # the retired integer-dot decodes (3, 4) and other values are unknown
+        for impl in (3, 4, -1, 99):
+            cfg = K.make_config(8, 32, scheme=scheme, rotation=rot, n_sink=s0, n_recent=w, clip_k=ck, clip_v=cv,
+                                decode_impl=impl)
+            assert K.check_config(cfg) == K.KVQ_EINVAL
+    # INT4 per token on the matrix cores walks page pairs: an explicit split must hold whole pairs
     for split, want in ((64, K.KVQ_EUNSUPPORTED), (192, K.KVQ_EUNSUPPORTED), (128, K.KVQ_OK), (512, K.KVQ_OK)):
-        for impl in (K.DECODE_DOT8, K.DECODE_MFMA):
-            cfg = K.make_config(8, 32, scheme=K.INT4_TOKEN, rotation=K.ROT_HADAMARD, n_sink=0, n_recent=0,
-                                clip_k=1.0, clip_v=1.0, split_tokens=split, decode_impl=impl)
-            assert K.check_config(cfg) == want
+        cfg = K.make_config(8, 32, scheme=K.INT4_TOKEN, rotation=K.ROT_HADAMARD, n_sink=0, n_recent=0,
+                            clip_k=1.0, clip_v=1.0, split_tokens=split, decode_impl=K.DECODE_MFMA)
+        assert K.check_config(cfg) == want
         cfg.decode_impl = K.DECODE_AUTO  # the automatic choice takes the fp32 path there instead
         assert K.check_config(cfg) == K.KVQ_OK
 
@@ -175,9 +178,8 @@ def test_matrix_core_decode_schemes():
 
 
 def test_int2_token_scheme_config():
-    """Per-token INT2: same sink/recent rules and sizes as the per-channel scheme; built on DOT8 and MFMA."""
-    for impl, want in ((K.DECODE_AUTO, K.KVQ_OK), (K.DECODE_DOT8, K.KVQ_OK), (K.DECODE_MFMA, K.KVQ_OK),
-                       (K.DECODE_F32, K.KVQ_EUNSUPPORTED), (K.DECODE_DOT16, K.KVQ_EUNSUPPORTED)):
+    """Per-token INT2: same sink/recent rules and sizes as the per-channel scheme; built on the matrix cores."""
+    for impl, want in ((K.DECODE_AUTO, K.KVQ_OK), (K.DECODE_MFMA, K.KVQ_OK), (K.DECODE_F32, K.KVQ_EUNSUPPORTED)):
         cfg = K.make_config(8, 32, scheme=K.INT2_TOKEN, decode_impl=impl)
         assert K.check_config(cfg) == want
     a = K.make_config(8, 32, scheme=K.INT2_TOKEN)
@@ -190,9 +192,8 @@ def test_int2_token_scheme_config():
 
 
 def test_int4_channel_scheme_config():
-    """Per-channel INT4: the INT2 groups, band and page count on the INT4 page size; built on DOT8 and MFMA."""
-    for impl, want in ((K.DECODE_AUTO, K.KVQ_OK), (K.DECODE_DOT8, K.KVQ_OK), (K.DECODE_MFMA, K.KVQ_OK),
-                       (K.DECODE_F32, K.KVQ_EUNSUPPORTED), (K.DECODE_DOT16, K.KVQ_EUNSUPPORTED)):
+    """Per-channel INT4: the INT2 groups, band and page count on the INT4 page size; built on the matrix cores."""
+    for impl, want in ((K.DECODE_AUTO, K.KVQ_OK), (K.DECODE_MFMA, K.KVQ_OK), (K.DECODE_F32, K.KVQ_EUNSUPPORTED)):
         assert K.check_config(K.make_config(8, 32, scheme=K.INT4_CHANNEL, decode_impl=impl)) == want
     a = K.make_config(8, 32, scheme=K.INT4_CHANNEL)
     c = K.make_config(8, 32, scheme=K.INT2_CHANNEL)
