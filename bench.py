@@ -42,9 +42,11 @@ def parse():
     ap.add_argument("--hadamard-block", type=int, default=0, choices=[0, 16, 32, 64, 128],
                     help="block order of the randomized Hadamard (workloads with that rotation; 0 = 128)")
     ap.add_argument("--split", type=int, default=0, help="quantized tokens per decode work-group (0 = auto)")
-    ap.add_argument("--cpu-pairs", type=int, default=2, help="distinct (seq, kv head) pairs in the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time of the CPU-baseline sample")
+    ap.add_argument("--cpu-reps", type=int, default=8, help="read-leg repetitions per unit in the CPU baseline")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="skip the second line of the default run: the ragged-length batch (8k..32k) of the same "
+                         "throughput workload")
     ap.add_argument("--write-bench", action="store_true",
                     help="time the fused rotate-quantize write of one prefill chunk per sequence instead of the "
                          "decode step (the INT4 workload's 8192-token chunk x 8 kv heads; for INT2 workloads a "
@@ -111,54 +113,106 @@ def decode_bytes(wl, lens, S0, W):
     return kv, qo
 
 
-def cpu_baseline(wl, args, T, rk, rv):
-    """Oracle read side (dequantize, x^.R^T, fp64 attention) with one BLAS thread on a few (seq, kv head)
-    pairs of the workload at length T, repeated round-robin until about --cpu-seconds of timed oracle
-    work have run.  The oracle's cache state of each pair is built once, untimed."""
+def _cpu_unit(task):
+    """One (sequence, kv head) unit of the oracle on one BLAS thread: the write leg (rotate, clip, quantize and
+    pack every group of the unit's T tokens; the band tokens as bf16) and the read leg (dequantize, x^.R^T,
+    fp64 softmax attention of the unit's GQ query heads), repeated `reps` times.  Runs in a worker process."""
+    wl_name, changes, b, h, T, reps = task
     import numpy as np
     import oracle as O
     import synth
     from threadpoolctl import threadpool_limits
-    q = synth.queries(wl, 10 ** 6)
-    total_s = 0.0
-    total_bytes = 0
-    runs = 0
-    int2 = wl.scheme in GROUPED
-    axis = {"int2_channel": "channel", "int2_token": "token", "int4_channel": "channel4"}.get(wl.scheme)
-    rv = None if wl.key_only else rv
+    wl = synth.scaled(synth.WORKLOADS[wl_name], **changes)
+    grouped = wl.scheme in GROUPED
     with threadpool_limits(limits=1):
-        states = []
-        for n in range(max(1, args.cpu_pairs)):
-            b, h = n % wl.batch, (3 * n + 1) % wl.n_kv_heads
-            k = synth.kv_tokens(wl, b, 0, T, "k")[:, h].copy()
-            v = synth.kv_tokens(wl, b, 0, T, "v")[:, h].copy()
-            if int2:
-                st = O.int2_state(k, v, T, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v, rk, rv, axis=axis)
-            else:
-                st = O.int4_state(k, v, T, rk.astype(np.int8), None if rv is None else rv.astype(np.int8),
-                                  block=wl.hadamard_block)
-            states.append((b, h, st))
-        while total_s < args.cpu_seconds:
-            b, h, st = states[runs % len(states)]
+        k = synth.kv_tokens(wl, b, 0, T, "k")[:, h].copy()
+        v = synth.kv_tokens(wl, b, 0, T, "v")[:, h].copy()
+        q = synth.queries(wl, 10 ** 6)[b, h * wl.gq:(h + 1) * wl.gq]
+        if grouped:
+            rk = O.oscar_rotation(synth.rotation_gaussian(wl, "k")).astype(np.float32)
+            rv = None if wl.key_only else O.oscar_rotation(synth.rotation_gaussian(wl, "v")).astype(np.float32)
+            axis = {"int2_channel": "channel", "int2_token": "token", "int4_channel": "channel4"}[wl.scheme]
             t0 = time.perf_counter()
-            if int2:
+            st = O.int2_state(k, v, T, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v, rk, rv, axis=axis)
+            t_write = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            for _ in range(reps):
                 Kh, Vh = O.int2_keys_values(st, rk, rv)
-            else:
-                Kh, Vh = O.int4_keys_values(st, rk.astype(np.int8), None if rv is None else rv.astype(np.int8),
-                                            wl.hadamard_block)
-            O.attend(O.query_values(q[b, h * wl.gq:(h + 1) * wl.gq]), Kh, Vh)
-            total_s += time.perf_counter() - t0
-            if int2:
-                ng = st["n_groups"]
-                total_bytes += ng * 128 * 72 + (T - 128 * ng) * 512 + wl.gq * 128 * 6
-            else:
-                total_bytes += T * 136 + wl.gq * 128 * 6
-            runs += 1
+                O.attend(O.query_values(q), Kh, Vh)
+            t_read = time.perf_counter() - t0
+        else:
+            sk = synth.sign_vector(wl, "k")
+            sv = None if wl.key_only else synth.sign_vector(wl, "v")
+            t0 = time.perf_counter()
+            st = O.int4_state(k, v, T, sk, sv, block=wl.hadamard_block)
+            t_write = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                Kh, Vh = O.int4_keys_values(st, sk, sv, wl.hadamard_block)
+                O.attend(O.query_values(q), Kh, Vh)
+            t_read = time.perf_counter() - t0
+    kv_b, qo_b = decode_bytes(wl, [T], wl.n_sink, wl.n_recent)
+    read_bytes = kv_b // wl.n_kv_heads + qo_b // wl.n_kv_heads
+    write_bytes = T * 2 * 128 * 2 + kv_b // wl.n_kv_heads  # bf16 K, V in; packed pages and band out
+    return t_write, t_read, reps, write_bytes, read_bytes
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, args):
+    """The CPU oracle on the same workload and the host's cores, before the GPU is touched: (seq, kv head)
+    units of the decode at the workload's context length, each on one BLAS thread, first one unit alone (one
+    thread), then one unit per core in a pool of spawned worker processes (all cores the process may run on,
+    at most 16).  The write leg (rotate, clip, quantize every group of the unit's context) and the read leg
+    (dequantize, inverse-rotate, fp64 attention of its GQ heads, `reps` times) are timed separately.  `value`
+    is the read leg on all cores in the decode's algorithmic bytes per second (the GPU's metric)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import numpy as np
+    import synth
+    T = int(synth.seq_lens(wl).max())
+    base = synth.WORKLOADS[wl.name]
+    changes = {k_: getattr(wl, k_) for k_ in ("scheme", "key_only", "hadamard_block") if getattr(wl, k_) != getattr(base, k_)}
+    cores = min(16, len(os.sched_getaffinity(0)))
+    reps = max(1, int(args.cpu_reps))
+    units = [(n % wl.batch, (3 * n + 1) % wl.n_kv_heads) for n in range(cores)]
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with cf.ProcessPoolExecutor(max_workers=1, mp_context=ctx) as ex:
+        one = ex.submit(_cpu_unit, (wl.name, changes, units[0][0], units[0][1], T, reps)).result()
+    with cf.ProcessPoolExecutor(max_workers=cores, mp_context=ctx) as ex:
+        tw0 = time.perf_counter()
+        res = list(ex.map(_cpu_unit, [(wl.name, changes, b, h, T, reps) for b, h in units]))
+        wall = time.perf_counter() - tw0
+    tw, tr, rp, wb, rb = zip(*res)
+    # all cores: every unit's legs run concurrently; each leg's aggregate rate is its bytes over the slowest
+    # worker's time for that leg
+    write_all = sum(wb) / max(tw) / 1e9
+    read_all = sum(rb) * reps / max(tr) / 1e9
+    write_one = one[3] / one[0] / 1e9
+    read_one = one[4] * reps / one[1] / 1e9
+    unit_read_s = max(tr) / reps
+    steps = cores / unit_read_s / (wl.batch * wl.n_kv_heads)  # decode steps/s of the whole batch on all cores
     return {
-        "value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": f"{runs} decodes of (seq, kv head) pairs of {wl.name} at T={T} ({len(states)} distinct pairs): "
-                  f"oracle read side (dequantize, x^.R^T, fp64 softmax attention of {wl.gq} q heads), one thread; "
-                  f"cache state built untimed; {total_s:.2f} s timed",
+        "value": round(read_all, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "cpu": cpu_model(),
+        "read_gbps": {"all_cores": round(read_all, 4), "one_thread": round(read_one, 4)},
+        "write_gbps": {"all_cores": round(write_all, 4), "one_thread": round(write_one, 4)},
+        "decode_steps_per_s_all_cores": round(steps, 3),
+        "sample": (f"{cores} (seq, kv head) units of {wl.name} at T={T} (of {wl.batch * wl.n_kv_heads} per step), "
+                   f"one per core in spawned processes, one BLAS thread each, plus one unit alone; write leg = "
+                   f"rotate/clip/quantize all {max(0, (T - wl.n_sink - wl.n_recent) // 128)} groups of the unit, "
+                   f"read leg = dequantize, x^.R^T and fp64 attention of {wl.gq} q heads x {reps}; "
+                   f"{time.perf_counter() - t0:.1f} s wall in total"),
     }
 
 
@@ -203,7 +257,8 @@ def write_bench(args, K, synth, np, torch):
         rk = synth.sign_vector(wl, "k").astype(np.float32)
         rv = synth.sign_vector(wl, "v").astype(np.float32)
     mp = K.pages_for_len(cfg, n)
-    pt, n_pool = synth.page_table(synth.scaled(wl, batch=B), max(1, mp))
+    n_pool = B * max(1, mp)
+    pt = K.build_page_table(B, max(1, mp), n_pool, seed=wl.seed)
     cache = K.allocate_cache(cfg, B, torch.from_numpy(pt), torch.from_numpy(rk),
                              None if wl.key_only else torch.from_numpy(rv), n_pages=n_pool, device=dev)
     gen = torch.Generator(device=dev)
@@ -261,7 +316,8 @@ def prefill_bench(args, K, synth, np, torch):
     rk = K.build_oscar_rotation(synth.rotation_gaussian(wl, "k")).astype(np.float32)
     rv = K.build_oscar_rotation(synth.rotation_gaussian(wl, "v")).astype(np.float32)
     max_pages = K.pages_for_len(cfg, int(lens.max()))
-    pt, n_pool = synth.page_table(wl, max_pages)
+    n_pool = B * max_pages
+    pt = K.build_page_table(B, max_pages, n_pool, seed=0 if wl.identity_pages else wl.seed)
     cache = K.allocate_cache(cfg, B, torch.from_numpy(pt), torch.from_numpy(rk),
                              None if wl.key_only else torch.from_numpy(rv), n_pages=n_pool, device=dev)
     gen = torch.Generator(device=dev)
@@ -325,17 +381,59 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import numpy as np
-    import torch
-
-    import decode_attention_15_amd as K
     import synth
 
+    if args.write_bench or args.prefill_bench:
+        import torch
+        import decode_attention_15_amd as K
     if args.write_bench:
         write_bench(args, K, synth, np, torch)
         return
     if args.prefill_bench:
         prefill_bench(args, K, synth, np, torch)
         return
+    wl = workload_of(args, synth)
+    # the CPU baseline runs first, in spawned processes, before anything touches the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args)
+    if cpu:
+        log(f"[bench] CPU baseline: {cpu['value']} GB/s on {cpu['cores']} cores ({cpu['cpu']})")
+    import torch
+    import decode_attention_15_amd as K
+
+    torch.cuda.set_device(0)
+    res = measure_decode(wl, args, K, synth, np, torch)
+    result = {
+        "metric": "INT2 decode-attn KV GB/s (% of HBM peak); decode steps/s at BS=32, 32k ctx",
+        "value": res["value"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8 x i8 -> i32 (matrix cores: 2/4-bit codes x 3-limb fixed-point operands) + f32 softmax",
+        "data": "synthetic",
+        "config": res["config"],
+        "steps_per_s": res["steps_per_s"],
+        "roofline": res["roofline"],
+        "decode_kernels_us": res["decode_kernels_us"],
+        "timed_window": res["timed_window"],
+    }
+    if args.workload == "batch32_32k" and not args.no_ragged and not (args.scheme or args.key_only or args.split):
+        # the throughput workload as written: context lengths drawn from 8k..32k
+        rg = measure_decode(synth.WORKLOADS["batch32_8k_32k"], args, K, synth, np, torch)
+        result["ragged_8k_32k"] = {k_: rg[k_] for k_ in ("value", "ms_per_step", "steps_per_s", "timed_window")}
+        result["ragged_8k_32k"]["roofline_frac"] = rg["roofline"]["frac"]
+        result["ragged_8k_32k"]["splitk_us"] = rg["roofline"]["kernel_us"]
+        result["ragged_8k_32k"]["ctx_range"] = rg["config"]["ctx_range"]
+    if cpu:
+        result["cpu_baseline"] = cpu
+    print(json.dumps(result), flush=True)
+
+
+def workload_of(args, synth):
     wl = synth.WORKLOADS[args.workload]
     if args.scheme and wl.scheme != "int4_token":
         wl = synth.scaled(wl, scheme=args.scheme)
@@ -343,20 +441,30 @@ def main():
         wl = synth.scaled(wl, key_only=True)
     if args.hadamard_block and wl.rotation == "saw":
         wl = synth.scaled(wl, hadamard_block=args.hadamard_block)
-    int2 = wl.scheme in GROUPED
+    return wl
+
+
+def measure_decode(wl, args, K, synth, np, torch):
+    """Decode steps of one workload: a cache written to the lengths before the measured steps, then W warm-up
+    steps, a 128-step window and the K timed steps, each step one append of a token per sequence followed by
+    one decode attention.  Returns the step time, the split-K kernel's roofline and the kernels' times."""
+    grouped = wl.scheme in GROUPED
     dev = "cuda"
-    torch.cuda.set_device(0)
     B, n_kv, n_q = wl.batch, wl.n_kv_heads, wl.n_q_heads
-    n_steps = args.warmup + args.steps
+    # Any 128 consecutive appends complete exactly one group per sequence (grouped schemes), so the mean step
+    # of a 128-step window carries the demotions at their steady rate: it is timed right before the K timed
+    # steps, and if the timed window (which, with every length equal, may hold no demotion at all) runs faster
+    # per step, the difference is added to it.
+    DEM = 128 if grouped else 0
+    n_steps = args.warmup + DEM + args.steps
     lens_end = synth.seq_lens(wl).astype(np.int64)          # lengths after the last timed step
     lens_start = lens_end - n_steps
     T_end = int(lens_end.max())
     impl = {"auto": K.DECODE_AUTO, "f32": K.DECODE_F32, "mfma": K.DECODE_MFMA}[args.impl]
     split = args.split if args.split else (wl.split_tokens if wl.name == "long_b4_131k" else 0)
-    if int2:
-        scheme = GROUPED[wl.scheme]
-        cfg = K.make_config(n_kv, n_q, scheme, K.ROT_DENSE, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v,
-                            split, impl, wl.key_only)
+    if grouped:
+        cfg = K.make_config(n_kv, n_q, GROUPED[wl.scheme], K.ROT_DENSE, wl.n_sink, wl.n_recent, wl.clip_k,
+                            wl.clip_v, split, impl, wl.key_only)
         rk = K.build_oscar_rotation(synth.rotation_gaussian(wl, "k")).astype(np.float32)
         rv = K.build_oscar_rotation(synth.rotation_gaussian(wl, "v")).astype(np.float32)
     else:
@@ -365,7 +473,8 @@ def main():
         rk = synth.sign_vector(wl, "k").astype(np.float32)
         rv = synth.sign_vector(wl, "v").astype(np.float32)
     max_pages = K.pages_for_len(cfg, T_end)
-    pt, n_pool = synth.page_table(wl, max_pages)
+    n_pool = B * max_pages
+    pt = K.build_page_table(B, max_pages, n_pool, seed=0 if wl.identity_pages else wl.seed)
     cache = K.allocate_cache(cfg, B, torch.from_numpy(pt), torch.from_numpy(rk),
                              None if wl.key_only else torch.from_numpy(rv), n_pages=n_pool, device=dev)
     log(f"[bench] {wl.name}: B={B} T={int(lens_start.min())}..{T_end} heads {n_q}/{n_kv}; "
@@ -384,7 +493,7 @@ def main():
 
     t0 = time.perf_counter()
     per_call = 4
-    chunk = 8192 if not int2 else int(lens_start.max())
+    chunk = 8192 if not grouped else int(lens_start.max())
     for b0 in range(0, B, per_call):
         sel = slice(b0, min(B, b0 + per_call))
         done = np.zeros(B, dtype=np.int64)
@@ -396,7 +505,7 @@ def main():
             cu = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev)
             k = draw(int(counts.sum()), gk)
             v = draw(int(counts.sum()), gv)
-            K.kv_rotate_quant_write(cache, k, v, cu, int(counts.max()))
+            K.kv_rotate_quant_write(cache, k, v, cu, int(counts.max()), max_len=T_end)
             done += counts
             del k, v
     torch.cuda.synchronize()
@@ -409,17 +518,21 @@ def main():
     out = torch.empty((B, n_q, 128), dtype=torch.float32, device=dev)
     ws = K.workspace_for(cfg, B, T_end, dev)
 
-    # one step = the append write, then the decode (query prep, split-K partials, merge).  Most timed steps
-    # make one kv_decode_attn call; every SAMPLE-th launches the three kernels one by one with HIP events
-    # on their stream (torch's current stream, which the binding passes to the library) around the
-    # split-K kernel.  Each event costs about 5 us of idle GPU between kernels, so the sampled steps alone
-    # carry them.  Warm-up steps bracket every kernel, for the query-prep and merge times.
+    # one step = the append write, then the decode (query prep with the bf16 band, split-K partials of the
+    # quantized chunks, merge).  Most timed steps make one kv_decode_attn call; every SAMPLE-th launches the
+    # three kernels one by one with HIP events on their stream (torch's current stream, which the binding
+    # passes to the library) around the split-K kernel.  Each event costs a few us of idle GPU between
+    # kernels, so the sampled steps alone carry them.  Warm-up steps bracket every kernel, for the query-prep
+    # and merge times.
     SAMPLE = 5
     names = ("qprep", "splitk", "merge")
     stages = (K.STAGE_QPREP, K.STAGE_SPLITK, K.STAGE_MERGE)
 
+    def write(i):
+        K.kv_rotate_quant_write(cache, ks[i], vs[i], cu1, 1, max_len=T_end)
+
     def staged_step(i, ev, which):
-        K.kv_rotate_quant_write(cache, ks[i], vs[i], cu1, 1)
+        write(i)
         for n, st in enumerate(stages):
             if n in which:
                 ev[n][0].record()
@@ -428,7 +541,7 @@ def main():
                 ev[n][1].record()
 
     def step(i):
-        K.kv_rotate_quant_write(cache, ks[i], vs[i], cu1, 1)
+        write(i)
         K.kv_decode_attn(cache, qs[i], out, T_end, ws)
 
     def pairs(n):
@@ -440,23 +553,38 @@ def main():
         staged_step(i, wevs[i], (0, 1, 2))
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
+    # the 128-step window (every sequence completes one group in it)
+    dem_ms = None
+    if DEM:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.warmup, args.warmup + DEM):
+            step(i)
+        torch.cuda.synchronize()
+        dem_ms = (time.perf_counter() - t0) * 1e3 / DEM
+    first = args.warmup + DEM
     sampled = [n for n in range(args.steps) if n % SAMPLE == 0]
     evs = pairs(args.steps)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
     lens_before = cache.seq_lens.cpu().numpy().astype(np.int64)
     torch.cuda.synchronize()
-    e0.record()
-    for n, i in enumerate(range(args.warmup, n_steps)):
+    t0 = time.perf_counter()
+    for n, i in enumerate(range(first, n_steps)):
         if n % SAMPLE == 0:
             staged_step(i, evs[n], (1,))
         else:
             step(i)
-    e1.record()
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
-    log(f"[bench] {args.steps} timed steps: {ms_step:.4f} ms/step")
+    ms_timed = (time.perf_counter() - t0) * 1e3 / args.steps
     assert np.array_equal(cache.seq_lens.cpu().numpy().astype(np.int64), lens_end)
+    # demotions (a sequence's append completing a group) inside the timed window
+    n_dem = 0
+    if grouped:
+        for s_ in range(1, args.steps + 1):
+            r = lens_before + s_ - wl.n_sink - wl.n_recent
+            n_dem += int(((r > 0) & (r % 128 == 0)).sum())
+    ms_step = max(ms_timed, dem_ms) if dem_ms is not None else ms_timed
+    log(f"[bench] {args.steps} timed steps: {ms_timed:.4f} ms/step ({n_dem} demotions); 128-step window "
+        f"{dem_ms if dem_ms is None else round(dem_ms, 4)} ms/step")
 
     # algorithmic bytes of each timed step (lengths after that step's append)
     kv_sum = qo_sum = 0
@@ -466,35 +594,29 @@ def main():
         qo_sum += qo_b
     step_bytes = (kv_sum + qo_sum) / args.steps
 
-    # the split-K kernel inside the timed steps: its launches' average duration, and the bytes it reads:
-    # KV bytes of the step + the fp32 rotated and band queries
+    # the split-K kernel inside the timed steps: its launches' average duration, and the bytes it reads: the
+    # codes and scales/zeros of every quantized token and the bf16 band tokens (the KV bytes of the step);
     # query prep and merge: median over the warm-up steps (the first launches carry one-time costs)
-    stage_us = {n: round(1e3 * float(np.median([ev[k][0].elapsed_time(ev[k][1]) for ev in wevs])), 2)
-                for k, n in enumerate(names) if n != "splitk" and wevs}
+    stage_us = {n: round(1e3 * float(np.median([ev[k_][0].elapsed_time(ev[k_][1]) for ev in wevs])), 2)
+                for k_, n in enumerate(names) if n != "splitk" and wevs}
     kern_ms = sum(evs[n][1][0].elapsed_time(evs[n][1][1]) for n in sampled) / len(sampled)
     stage_us["splitk"] = round(kern_ms * 1e3, 2)
-    kern_bytes = int(round(kv_sum / args.steps)) + B * n_q * 128 * 4 * 2
+    kern_bytes = int(round(kv_sum / args.steps))
     achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     log(f"[bench] split-K kernel {kern_ms * 1e3:.1f} us, {achieved:.0f} GB/s; kernels {stage_us}")
 
-    variant = ("" if wl.scheme == synth.WORKLOADS[args.workload].scheme else wl.scheme) + \
+    variant = ("" if wl.scheme == synth.WORKLOADS[wl.name].scheme else wl.scheme) + \
         (" key-only" if wl.key_only else "") + \
         (f" hadamard-{wl.hadamard_block}" if wl.rotation == "saw" and wl.hadamard_block != 128 else "")
     traffic = read_traffic(wl.name, variant.strip())
-
-    result = {
-        "metric": "INT2 decode-attn KV GB/s (% of HBM peak); decode steps/s at BS=32, 32k ctx",
+    kernel = {"int2_channel": "split-K decode, INT2 per-channel pages + bf16 band",
+              "int2_token": "split-K decode, INT2 per-token pages + bf16 band",
+              "int4_channel": "split-K decode, INT4 per-channel pages + bf16 band",
+              "int4_token": "split-K decode, INT4 per-token pages"}
+    return {
         "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
+        "steps_per_s": round(1000.0 / ms_step, 2),
         "config": {"workload": wl.name, "batch": B, "ctx": T_end,
                    "ctx_range": [int(lens_end.min()), int(lens_end.max())], "n_q_heads": n_q, "n_kv_heads": n_kv,
                    "head_dim": 128,
@@ -505,20 +627,19 @@ def main():
                               [wl.scheme] + (", key-only rotation" if wl.key_only else "") +
                               (f", Hadamard block {wl.hadamard_block}" if wl.rotation == "saw" else "")),
                    "sink_recent": [wl.n_sink, wl.n_recent], "page_tokens": 64, "split_tokens": split,
-                   "decode_impl": args.impl, "step": "append 1 token/seq (write) + decode attention"},
-        "steps_per_s": round(1000.0 / ms_step, 2),
+                   "decode_impl": args.impl,
+                   "step": ("append 1 token/seq (write) + decode attention; group demotion counted at its steady "
+                            "rate: ms_per_step = max(timed window, 128-step window), every sequence completing one "
+                            "128-token group in the 128-step window" if grouped else
+                            "append 1 token/seq (write) + decode attention")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": ("split-K decode (per-channel INT4 pages + bf16 band)" if wl.scheme == "int4_channel"
-                                else "split-K decode (INT2 pages + bf16 band)" if int2 else "split-K decode (INT4 pages)"),
-                     "kernel_us": round(kern_ms * 1e3, 2), "kernel_launches_timed": len(sampled),
-                     "bytes_per_launch": kern_bytes},
+                     "kernel": kernel[wl.scheme], "kernel_us": round(kern_ms * 1e3, 2),
+                     "kernel_launches_timed": len(sampled), "bytes_per_launch": kern_bytes},
         "decode_kernels_us": stage_us,
+        "timed_window": {"ms_per_step": round(ms_timed, 5), "demotions": n_dem,
+                         "window128_ms_per_step": None if dem_ms is None else round(dem_ms, 5)},
     }
-    if not args.no_cpu_baseline:
-        log("[bench] CPU baseline (oracle) ...")
-        result["cpu_baseline"] = cpu_baseline(wl, args, T_end, rk, rv)
-    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":

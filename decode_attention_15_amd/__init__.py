@@ -83,7 +83,13 @@ _lib_query_cov = _sig("kvq_query_covariance", ctypes.c_int, _P, ctypes.c_int64, 
 _lib_sv_cov = _sig("kvq_score_value_covariance", ctypes.c_int, _P, ctypes.c_int64, _P, ctypes.c_int64, _P)
 _lib_eigenbasis = _sig("kvq_eigenbasis", ctypes.c_int, _P, _P, _P)
 _lib_oscar_from_cov = _sig("kvq_build_oscar_rotation_from_covariance", ctypes.c_int, _P, _P)
-_lib_write = _sig("kv_rotate_quant_write", ctypes.c_int, _CFG, _CACHE, _P, _P, ctypes.c_int32, _P, ctypes.c_int32, _P)
+_lib_write = _sig("kv_rotate_quant_write", ctypes.c_int, _CFG, _CACHE, _P, _P, ctypes.c_int32, _P, ctypes.c_int32,
+                  ctypes.c_int32, _P)
+_lib_build_pt = _sig("kvq_build_page_table", ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                     ctypes.c_uint64, _P)
+_lib_check_pt = _sig("kvq_check_page_table", ctypes.c_int, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64)
+_lib_debug_unpack = _sig("kvq_debug_unpack", ctypes.c_int, _CFG, _CACHE, ctypes.c_int32, ctypes.c_int32,
+                         ctypes.c_int32, _P, _P, _P)
 _lib_decode = _sig("kv_decode_attn", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P, ctypes.c_int32, _P,
                    ctypes.c_size_t, _P)
 _lib_decode_stages = _sig("kv_decode_attn_stages", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P, ctypes.c_int32,
@@ -100,7 +106,7 @@ EXPORTED = [
     "kvq_build_hadamard_rotation", "kvq_query_covariance", "kvq_score_value_covariance", "kvq_eigenbasis",
     "kvq_build_oscar_rotation_from_covariance", "kvq_prefill_workspace_bytes", "kv_prefill_attn",
     "kv_rotate_quant_write", "kv_decode_attn", "kv_decode_attn_stages",
-    "kvq_debug_rotate",
+    "kvq_debug_rotate", "kvq_debug_unpack", "kvq_build_page_table", "kvq_check_page_table",
     "kvq_strerror", "kvq_version", "kvq_last_error",
 ]
 
@@ -303,14 +309,19 @@ def allocate_cache(cfg: Config, batch: int, page_table, rot_k, rot_v, n_pages: O
     return DeviceCache(cfg, pages, band, pt, seq_lens, rot_k.to(device).float().contiguous(), rv, batch)
 
 
-def kv_rotate_quant_write(cache: DeviceCache, k, v, cu_new, max_new: int, stream=None) -> None:
-    """Append tokens: k, v [total_new, n_kv, 128] (fp32 or bf16), cu_new int32 [batch+1] (device)."""
+def kv_rotate_quant_write(cache: DeviceCache, k, v, cu_new, max_new: int, max_len: Optional[int] = None,
+                          stream=None) -> None:
+    """Append tokens: k, v [total_new, n_kv, 128] (fp32 or bf16), cu_new int32 [batch+1] (device).
+    max_len bounds every sequence's length after the append (host); if None it is taken as the longest
+    current length plus max_new, read from the device (a synchronizing copy)."""
     assert k.is_contiguous() and v.is_contiguous() and cu_new.is_contiguous()
     assert k.shape == v.shape and k.shape[1:] == (cache.cfg.n_kv_heads, 128)
     assert cu_new.numel() == cache.batch + 1
+    if max_len is None:
+        max_len = int(cache.seq_lens.max().item()) + int(max_new)
     cs = cache.c_struct()
     _check(_lib_write(ctypes.byref(cache.cfg), ctypes.byref(cs), _ptr(k), _ptr(v), _dtype_code(k), _ptr(cu_new),
-                      int(max_new), _stream(stream)), "kv_rotate_quant_write")
+                      int(max_new), int(max_len), _stream(stream)), "kv_rotate_quant_write")
 
 
 def kv_decode_attn(cache: DeviceCache, q, out, max_seq_len: int, workspace, stream=None) -> None:
@@ -335,6 +346,40 @@ def kvq_debug_rotate(cache: DeviceCache, which: int, x, rho: float, out, stream=
     cs = cache.c_struct()
     _check(_lib_debug_rotate(ctypes.byref(cache.cfg), ctypes.byref(cs), which, _ptr(x), _dtype_code(x),
                              x.shape[0], float(rho), _ptr(out), _stream(stream)), "kvq_debug_rotate")
+
+
+def build_page_table(batch: int, max_pages_per_seq: int, n_pages: Optional[int] = None, seed: int = 0):
+    """[batch, max_pages_per_seq] int32 page table (host numpy) over a pool of n_pages (default: exactly
+    batch * max_pages_per_seq): seed 0 the identity layout, else a seeded random permutation of the pool."""
+    import numpy as np
+    n_pages = batch * max_pages_per_seq if n_pages is None else n_pages
+    out = np.empty((batch, max_pages_per_seq), dtype=np.int32)
+    _check(_lib_build_pt(int(batch), int(max_pages_per_seq), int(n_pages), int(seed) & (2 ** 64 - 1), _vp(out)),
+           "kvq_build_page_table")
+    return out
+
+
+def check_page_table(table, n_pages: int) -> int:
+    """Status of a host page table [batch, max_pages_per_seq] against a pool of n_pages (KVQ_OK, KVQ_ERANGE
+    for an entry outside the pool, KVQ_EINVAL for a physical page named twice)."""
+    import numpy as np
+    t = np.ascontiguousarray(table, dtype=np.int32)
+    return _lib_check_pt(_vp(t), int(t.shape[0]), int(t.shape[1]), int(n_pages))
+
+
+def kvq_debug_unpack(cache: DeviceCache, seq: int, kv_head: int, n_tokens: int, stream=None):
+    """(codes uint8 [n_tokens, 2, 128], scales/zeros bf16 bits) of one (sequence, kv head), read back from the
+    pages by the library (device tensors); see include/kvq.h for the scale/zero layout."""
+    import torch
+    dev = cache.pages.device
+    codes = torch.empty((n_tokens, 2, 128), dtype=torch.uint8, device=dev)
+    per_channel = cache.cfg.scheme in (INT2_CHANNEL, INT4_CHANNEL)
+    sz = torch.empty(((n_tokens // 128, 2, 2, 128) if per_channel else (n_tokens, 2, 2)), dtype=torch.int16,
+                     device=dev)
+    cs = cache.c_struct()
+    _check(_lib_debug_unpack(ctypes.byref(cache.cfg), ctypes.byref(cs), int(seq), int(kv_head), int(n_tokens),
+                             _ptr(codes), _ptr(sz), _stream(stream)), "kvq_debug_unpack")
+    return codes, sz
 
 
 def workspace_for(cfg: Config, batch: int, max_seq_len: int, device: str = "cuda"):

@@ -3,6 +3,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <stdint.h>
+
 #include <vector>
 
 #include "kvq_internal.h"
@@ -48,7 +50,7 @@ int check_config(const kvq_config* c) {
 int check_cache(const kvq_config* c, const kvq_cache* k) {
   if (!k || !k->pages || !k->page_table || !k->seq_lens || !k->rot_k || (!k->rot_v && !c->key_only_rotation))
     return KVQ_EINVAL;
-  if (k->batch < 1 || k->max_pages_per_seq < 0 || k->n_pages < 0) return KVQ_EINVAL;
+  if (k->batch < 1 || k->max_pages_per_seq < 0 || k->n_pages < 1) return KVQ_EINVAL;
   if (is_grouped(c->scheme) && !k->band) return KVQ_EINVAL;
   return KVQ_OK;
 }
@@ -76,13 +78,22 @@ int chunk_units(const kvq_config* c, int batch, int max_seq_len) {
   else units = (max_seq_len + PAGE - 1) / PAGE;
   const int pairs = batch * c->n_kv_heads;
   if (uses_mfma(c)) {
-    // one chunk per wave, long enough that a wave's copies stay in flight across several groups, short
-    // enough that small launches still spread over the GPU: about 512 wave chunks or more, a power of two
-    // from 1 to 32 groups (measured: batch 1 x 32k takes 4 groups, batch 32 x 32k 32)
+    // one chunk per wave, sized so that the chunk work-groups and the band work-groups (the grouped schemes'
+    // band units; INT4 per token's are empty and finish at once) fill the GPU's work-group slots in one round:
+    // the kernel's work-groups per CU follow its LDS (2-bit codes: 3 up to GQA 4, 2 at GQA 8; 4-bit codes: 2
+    // up to GQA 4, 1 at GQA 8) on the 256 CUs of an MI355X.  At least 4 groups (pages) per chunk, so that a
+    // wave's copies stay in flight across several of them (measured: batch 1 x 32k, 4-group chunks beat
+    // 1-group ones), and at most 32.
+    const bool four = c->scheme == KVQ_INT4_CHANNEL || c->scheme == KVQ_INT4_TOKEN;
+    const int per_cu = gq_of(c) <= 4 ? (four ? 2 : 3) : (four ? 1 : 2);
+    long long chunk_wgs = 256LL * per_cu - (is_grouped(c->scheme) ? pairs : 0);
+    if (chunk_wgs < 256) chunk_wgs = 256;
     const long long total = (long long)pairs * units;
-    int per = c->scheme == KVQ_INT4_TOKEN ? 2 : 1;  // INT4 per token: whole page pairs
-    while (per < 32 && (long long)per * 512 < total) per *= 2;
-    return per;
+    long long per = (total + 4 * chunk_wgs - 1) / (4 * chunk_wgs);
+    if (per < 4) per = 4;
+    if (per > 32) per = 32;
+    if (c->scheme == KVQ_INT4_TOKEN) per = (per + 1) & ~1LL;  // whole page pairs
+    return (int)per;
   }
   const int target_wgs = 2048;
   int chunks = (target_wgs + pairs - 1) / pairs;
@@ -123,6 +134,7 @@ Geo make_geo(const kvq_config* c, const kvq_cache* k) {
   g.W = c->n_recent;
   g.slots = kvq_band_slots(c);
   g.max_pages = k->max_pages_per_seq;
+  g.n_pages = k->n_pages;
   g.head_bytes = head_bytes_of(c);
   g.page_bytes = (long long)g.head_bytes * c->n_kv_heads;
   return g;
@@ -281,11 +293,14 @@ int kvq_build_hadamard_rotation(const float* sign_host, double* R_out_host) {
 }
 
 int kv_rotate_quant_write(const kvq_config* cfg, kvq_cache* cache, const void* k, const void* v, int32_t dtype,
-                          const int32_t* cu_new, int32_t max_new_host, hipStream_t stream) {
+                          const int32_t* cu_new, int32_t max_new_host, int32_t max_len_host, hipStream_t stream) {
   int st = check_config(cfg);
   if (st != KVQ_OK) return st;
   if ((st = check_cache(cfg, cache)) != KVQ_OK) return st;
-  if (!k || !v || !cu_new || max_new_host < 0 || (dtype != KVQ_F32 && dtype != KVQ_BF16)) return KVQ_EINVAL;
+  if (!k || !v || !cu_new || max_new_host < 0 || max_len_host < 0 || (dtype != KVQ_F32 && dtype != KVQ_BF16))
+    return KVQ_EINVAL;
+  // every sequence's length after the append must fit the page-table row
+  if (kvq_pages_for_len(cfg, max_len_host) > cache->max_pages_per_seq) return KVQ_ERANGE;
   WriteArgs a;
   memset(&a, 0, sizeof(a));
   a.g = make_geo(cfg, cache);
@@ -334,6 +349,14 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
   // the matrix-core decode walks one chunk per wave (four per work-group); the fp32 decode one per work-group
   const bool mfma = uses_mfma(cfg);
   a.g.wave_chunks = mfma ? 1 : 0;
+  {
+    // band work-groups first when the split-K launch takes more than one round of work-groups (see the grid)
+    const bool four = cfg->scheme == KVQ_INT4_CHANNEL || cfg->scheme == KVQ_INT4_TOKEN;
+    const int per_cu = !mfma ? 4 : gq_of(cfg) <= 4 ? (four ? 2 : 3) : (four ? 1 : 2);
+    const long long nc = a.g.n_units - 1, pairs = (long long)cache->batch * cfg->n_kv_heads;
+    const long long chunk_wgs = !mfma ? pairs * nc : cfg->n_kv_heads % 4 == 0 ? pairs / 4 * nc : pairs * ((nc + 3) / 4);
+    a.g.band_first = chunk_wgs + pairs > 256LL * per_cu ? 1 : 0;
+  }
   a.pages = static_cast<const uint8_t*>(cache->pages);
   a.band = static_cast<const uint16_t*>(cache->band);
   a.page_table = cache->page_table;
@@ -410,6 +433,73 @@ int kvq_debug_rotate(const kvq_config* cfg, const kvq_cache* cache, int32_t whic
   return to_status(launch_debug_rotate(rot, cfg->rotation, g.hblock, g.hscale, x, dtype == KVQ_BF16, n, j, f, out,
                                        stream),
                    "kvq_debug_rotate");
+}
+
+int kvq_build_page_table(int32_t batch, int32_t max_pages_per_seq, int64_t n_pages, uint64_t seed,
+                         int32_t* table_out_host) {
+  if (!table_out_host || batch < 1 || max_pages_per_seq < 0 || n_pages < 1 || n_pages > INT32_MAX)
+    return KVQ_EINVAL;
+  const int64_t need = (int64_t)batch * max_pages_per_seq;
+  if (need > n_pages) return KVQ_ERANGE;
+  if (seed == 0) {  // sequence b takes pages b * max_pages_per_seq ..
+    for (int64_t i = 0; i < need; ++i) table_out_host[i] = (int32_t)i;
+    return KVQ_OK;
+  }
+  // a seeded random permutation of the pool (Fisher-Yates driven by splitmix64), its first `need` entries
+  std::vector<int32_t> perm((size_t)n_pages);
+  for (int64_t i = 0; i < n_pages; ++i) perm[(size_t)i] = (int32_t)i;
+  uint64_t x = seed;
+  auto next = [&x]() {
+    uint64_t z = (x += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+  };
+  for (int64_t i = n_pages - 1; i > 0; --i) {
+    // unbiased draw from [0, i]: reject the top partial range
+    const uint64_t range = (uint64_t)i + 1, lim = UINT64_MAX - UINT64_MAX % range;
+    uint64_t r;
+    do r = next(); while (r >= lim);
+    const int64_t j = (int64_t)(r % range);
+    const int32_t t = perm[(size_t)i];
+    perm[(size_t)i] = perm[(size_t)j];
+    perm[(size_t)j] = t;
+  }
+  for (int64_t i = 0; i < need; ++i) table_out_host[i] = perm[(size_t)i];
+  return KVQ_OK;
+}
+
+int kvq_check_page_table(const int32_t* table_host, int32_t batch, int32_t max_pages_per_seq, int64_t n_pages) {
+  if (!table_host || batch < 1 || max_pages_per_seq < 0 || n_pages < 1) return KVQ_EINVAL;
+  std::vector<uint8_t> used((size_t)n_pages, 0);
+  const int64_t n = (int64_t)batch * max_pages_per_seq;
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t p = table_host[i];
+    if (p < 0 || p >= n_pages) return KVQ_ERANGE;
+    if (used[(size_t)p]) return KVQ_EINVAL;  // two logical pages on one physical page
+    used[(size_t)p] = 1;
+  }
+  return KVQ_OK;
+}
+
+int kvq_debug_unpack(const kvq_config* cfg, const kvq_cache* cache, int32_t seq, int32_t kv_head, int32_t n_tokens_host,
+                     uint8_t* codes_out, uint16_t* sz_out, hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if ((st = check_cache(cfg, cache)) != KVQ_OK) return st;
+  if (!codes_out || !sz_out || seq < 0 || seq >= cache->batch || kv_head < 0 || kv_head >= cfg->n_kv_heads ||
+      n_tokens_host < 0)
+    return KVQ_EINVAL;
+  if (is_grouped(cfg->scheme) && n_tokens_host % GROUP != 0) return KVQ_EINVAL;
+  if ((n_tokens_host + PAGE - 1) / PAGE > cache->max_pages_per_seq) return KVQ_ERANGE;
+  if (n_tokens_host == 0) return KVQ_OK;
+  WriteArgs a;
+  memset(&a, 0, sizeof(a));
+  a.g = make_geo(cfg, cache);
+  a.pages = static_cast<uint8_t*>(cache->pages);
+  a.page_table = cache->page_table;
+  clear_stale_error();
+  return to_status(launch_debug_unpack(a, seq, kv_head, n_tokens_host, codes_out, sz_out, stream), "kvq_debug_unpack");
 }
 
 const char* kvq_strerror(int status) {

@@ -43,74 +43,12 @@ __device__ inline float exp2_safe_diff(float a, float b) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Query preparation: q~ = (q R_K) * log2e/sqrt(128) for quantized tokens (rotated frame), and
-// q * log2e/sqrt(128) for the bf16 band (original frame).
-// ---------------------------------------------------------------------------------------------
-template <int GQ>
-__global__ __launch_bounds__(512) void qprep_kernel(DecodeArgs a) {
-  __shared__ float qs[GQ][D];
-  __shared__ float part[4][GQ][D];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int j = tid & (D - 1), qtr = tid >> 7;  // column j, quarter qtr of the 128 input channels
-  const long long base = ((long long)b * a.g.n_q + h * GQ) * D;
-  const float scale = LOG2E * kInvSqrt128;
-  const bool dense = a.g.rotation == KVQ_ROT_DENSE;
-  // this thread's 32 entries of column j of R_K, read together with the queries (one round trip)
-  float rk[32];
-  if (dense) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) rk[i] = a.rot_k[(qtr * 32 + i) * D + j];
-  }
-  for (int e = tid; e < GQ * D; e += 512) {
-    const int hh = e / D, c = e % D;
-    const float qv = a.q_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[base + e])
-                              : static_cast<const float*>(a.q)[base + e];
-    a.qband[base + e] = qv * scale;
-    qs[hh][c] = dense ? qv : qv * a.rot_k[c];
-  }
-  __syncthreads();
-  if (dense) {
-    float r[GQ];
-#pragma unroll
-    for (int hh = 0; hh < GQ; ++hh) r[hh] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i)
-#pragma unroll
-      for (int hh = 0; hh < GQ; ++hh) r[hh] = fmaf(qs[hh][qtr * 32 + i], rk[i], r[hh]);
-#pragma unroll
-    for (int hh = 0; hh < GQ; ++hh) part[qtr][hh][j] = r[hh];
-    __syncthreads();
-    for (int e = tid; e < GQ * D; e += 512) {
-      const int hh = e / D, c = e % D;
-      a.qrot[base + e] = ((part[0][hh][c] + part[1][hh][c]) + (part[2][hh][c] + part[3][hh][c])) * scale;
-    }
-  } else {
-    // randomized (block-diagonal) Hadamard: FWHT within blocks of h channels in LDS
-    for (int hb = 1; hb < a.g.hblock; hb <<= 1) {
-      float x[GQ / 4 + 1];
-      int n = 0;
-      for (int e = tid; e < GQ * D; e += 512) {
-        const int hh = e / D, c = e % D;
-        const float u = qs[hh][c], v = qs[hh][c ^ hb];
-        x[n++] = (c & hb) ? (v - u) : (u + v);
-      }
-      __syncthreads();
-      n = 0;
-      for (int e = tid; e < GQ * D; e += 512) qs[e / D][e % D] = x[n++];
-      __syncthreads();
-    }
-    const float hs = (float)a.g.hscale;
-    for (int e = tid; e < GQ * D; e += 512) a.qrot[base + e] = qs[e / D][e % D] * hs * scale;
-  }
-}
-
-// ---------------------------------------------------------------------------------------------
 // Split-K decode, vector ALU.  Work-group (unit, kv head, seq): unit 0 = bf16 band (sink + tail),
 // unit u >= 1 = quantized chunk u-1.  Each of the 4 waves walks its own groups/pages with an
 // online softmax; the waves are merged in LDS and one partial (m, l, o[128]) per q head written.
 // ---------------------------------------------------------------------------------------------
-// Per-wave LDS of the matrix-core units: the key, then the value codes of a group or page pair (one buffer),
-// the metadata of two of them (double-buffered, 1 KB each), and one operand plane with rows (head, limb)
+// Per-wave LDS of the matrix-core units: the key and the value codes of a group or page pair, the metadata of
+// two of them (double-buffered, 1 KB each), and one operand plane with rows (head, limb)
 // of 128 bytes in k order (stride 144: consecutive rows start in different banks) and a last row that stays
 // zero for the matrix rows no head fills.  The plane holds the key-side operand while the key products read
 // it and the softmax weights while the value products read them.
@@ -118,7 +56,8 @@ template <int GQ, int KU = 256>
 struct MfmaWave {
   static constexpr int ROWS = 3 * GQ;
   static constexpr int RSTRIDE = 144;
-  uint4 kst[KU];  // 4 KB (2-bit codes of a group) or 8 KB (4-bit codes of a group or page pair)
+  uint4 kst[KU];  // key codes: 4 KB (2-bit codes of a group) or 8 KB (4-bit codes of a group or page pair)
+  uint4 vst[KU];  // value codes, the same size
   uint4 mst[2][64];
   uint8_t plane[(ROWS + 1) * RSTRIDE];
 };
@@ -135,7 +74,7 @@ template <int GQ, int STG = 1, bool MF = false>
 struct DecodeLds {
   union {
     MfmaLds<GQ, MF, 256 * STG> mf;
-    struct {                     // band unit, fp32 INT2 path, INT4 path
+    struct {                     // band unit, fp32 INT2 and INT4 paths
       float qband[GQ][D];
       float alpha[4][GQ][D];     // per wave: alpha (INT2) / rotated query (INT4)
       float p[4][GQ][D];         // per wave: softmax numerators of the current group/page
@@ -200,21 +139,21 @@ __device__ inline void softmax_update(float (&m)[GQ], float (&l)[GQ], float (&o)
   mnew_out = mnew;
 }
 
-template <int GQ, typename Lds>
-__device__ void band_unit(Lds& L, const DecodeArgs& a, int b, int h, int T) {
+// The bf16 band (sink and tail tokens, original frame) of one (sequence, kv head) walked by NW waves: wave w
+// takes the 64-token blocks w, w + NW, ..; each lane one token of a block for the logits (its whole key row
+// in flight at once), then channels 2 lane, 2 lane + 1 of the block's value rows, 16 tokens at a time with
+// the next 16 in flight.  qb: the GQ heads' queries times log2e/sqrt(128) in LDS; pb: this wave's softmax
+// numerators [GQ][64] in LDS.  Returns the wave's partial (m, l, o) of every head.
+template <int GQ, int NW>
+__device__ void band_walk(const DecodeArgs& a, int b, int h, int T, const float (*qb)[D], float (*pb)[64], int wave,
+                          int lane, float (&m)[GQ], float (&l)[GQ], float (&o)[GQ][2]) {
   const Geo& g = a.g;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the value rows' slots are scalar
-  for (int e = tid; e < GQ * D; e += kThreads)
-    L.f.qband[e / D][e % D] = a.qband[((long long)b * g.n_q + h * GQ + e / D) * D + e % D];
-  __syncthreads();
   const int ng = n_groups_of(T, g.S0, g.W);
   const int n_sink = T < g.S0 ? T : g.S0;
   const int tail0 = g.S0 + GROUP * ng;
   const int n_tail = T > tail0 ? T - tail0 : 0;
   const int nb = n_sink + n_tail;
   const uint16_t* band = a.band + ((long long)b * g.n_kv + h) * g.slots * 256;
-  float m[GQ], l[GQ], o[GQ][2];
 #pragma unroll
   for (int hh = 0; hh < GQ; ++hh) {
     m[hh] = -INFINITY;
@@ -225,7 +164,7 @@ __device__ void band_unit(Lds& L, const DecodeArgs& a, int b, int h, int T) {
     const int pos = k < n_sink ? k : tail0 + (k - n_sink);
     return band_slot_of(pos, g.S0, g.W);
   };
-  for (int blk = wave; blk * 64 < nb; blk += 4) {
+  for (int blk = wave; blk * 64 < nb; blk += NW) {
     const int k = blk * 64 + lane;
     const bool valid = k < nb;
     float lg[GQ];
@@ -245,7 +184,7 @@ __device__ void band_unit(Lds& L, const DecodeArgs& a, int b, int h, int T) {
           const float k0 = __uint_as_float(ws[p2] << 16), k1 = __uint_as_float(ws[p2] & 0xffff0000u);
           const int c = v8 * 8 + p2 * 2;
 #pragma unroll
-          for (int hh = 0; hh < GQ; ++hh) lg[hh] += L.f.qband[hh][c] * k0 + L.f.qband[hh][c + 1] * k1;
+          for (int hh = 0; hh < GQ; ++hh) lg[hh] += qb[hh][c] * k0 + qb[hh][c + 1] * k1;
         }
       }
     }
@@ -255,13 +194,11 @@ __device__ void band_unit(Lds& L, const DecodeArgs& a, int b, int h, int T) {
       float mnew;
       softmax_update<GQ>(m, l, o, hh, wave_max(x), mnew);
       const float p = valid ? exp2f(x - mnew) : 0.0f;
-      L.f.p[wave][hh][lane] = p;
+      pb[hh][lane] = p;
       l[hh] += wave_sum(p);
     }
     wave_lds_sync();
     const int nk = (nb - blk * 64) < 64 ? (nb - blk * 64) : 64;
-    // value rows (channels 2 lane, 2 lane + 1) 16 tokens at a time, the next 16 in flight while these are
-    // summed, so that the block costs about one memory latency rather than one per batch
     constexpr int VB = 16;
     auto load_rows = [&](int k0, uint32_t (&dst)[VB]) {
 #pragma unroll
@@ -283,7 +220,7 @@ __device__ void band_unit(Lds& L, const DecodeArgs& a, int b, int h, int T) {
         const float v0 = __uint_as_float(vv[q] << 16), v1 = __uint_as_float(vv[q] & 0xffff0000u);
 #pragma unroll
         for (int hh = 0; hh < GQ; ++hh) {
-          const float p = L.f.p[wave][hh][k8 + q];
+          const float p = pb[hh][k8 + q];
           o[hh][0] += p * v0;
           o[hh][1] += p * v1;
         }
@@ -291,6 +228,20 @@ __device__ void band_unit(Lds& L, const DecodeArgs& a, int b, int h, int T) {
     }
     wave_lds_sync();
   }
+}
+
+// The band unit of the split-K launch: one work-group (4 waves) per (sequence, kv head), its partial stored
+// as unit 0.
+template <int GQ, typename Lds>
+__device__ void band_unit(Lds& L, const DecodeArgs& a, int b, int h, int T) {
+  const Geo& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int e = tid; e < GQ * D; e += kThreads)
+    L.f.qband[e / D][e % D] = a.qband[((long long)b * g.n_q + h * GQ + e / D) * D + e % D];
+  __syncthreads();
+  float m[GQ], l[GQ], o[GQ][2];
+  band_walk<GQ, 4>(a, b, h, T, L.f.qband, reinterpret_cast<float(*)[64]>(&L.f.p[wave][0][0]), wave, lane, m, l, o);
   combine_and_store<GQ>(L, a, b, h, 0, wave, lane, m, l, o, 2 * lane, 2 * lane + 1);
 }
 
@@ -319,8 +270,8 @@ __device__ void int2_unit(Lds& L, const DecodeArgs& a, int b, int h, int T, int 
   const int32_t* pt = a.page_table + (long long)b * g.max_pages;
   const long long hoff = (long long)h * I2_HEAD_BYTES;
   for (int gi = g_begin + wave; gi < g_end; gi += 4) {
-    const uint8_t* pg[2] = {a.pages + (long long)pt[2 * gi] * g.page_bytes + hoff,
-                            a.pages + (long long)pt[2 * gi + 1] * g.page_bytes + hoff};
+    const uint8_t* pg[2] = {a.pages + pool_page(g, pt[2 * gi]) * g.page_bytes + hoff,
+                            a.pages + pool_page(g, pt[2 * gi + 1]) * g.page_bytes + hoff};
     const uint16_t* km = reinterpret_cast<const uint16_t*>(pg[0] + I2_META_OFF);
     const uint16_t* vm = reinterpret_cast<const uint16_t*>(pg[1] + I2_META_OFF);
     const float sk0 = bf16_to_f32(km[lane]), sk1 = bf16_to_f32(km[lane + 64]);
@@ -554,7 +505,7 @@ __device__ void int4_unit(Lds& L, const DecodeArgs& a, int b, int h, int T, int 
   const int32_t* pt = a.page_table + (long long)b * g.max_pages;
   const long long hoff = (long long)h * I4_HEAD_BYTES;
   for (int pi = p_begin + wave; pi < p_end; pi += 4) {
-    const uint8_t* pg = a.pages + (long long)pt[pi] * g.page_bytes + hoff;
+    const uint8_t* pg = a.pages + pool_page(g, pt[pi]) * g.page_bytes + hoff;
     const int t = pi * PAGE + lane;
     const bool valid = t < T;
     const uint16_t* kmeta = reinterpret_cast<const uint16_t*>(pg + I4_KMETA_OFF + 4 * lane);
@@ -659,9 +610,10 @@ __device__ void int4_unit(Lds& L, const DecodeArgs& a, int b, int h, int T, int 
 //  - key tile i, column c: token T(i, c) = 64 (c / 8) + 2 (c % 8) + 16 (i % 4) + i / 4, the token at value
 //    position 8 c + i, so each lane stores its 8 weights of a head as 8 consecutive bytes of a plane row.
 // Key codes are staged with their rows permuted (token t at row t ^ ((t >> 2) & 3)) so that the 8-byte
-// operand reads of a tile spread over all LDS banks.  All global reads are LDS copies: a group's metadata
-// one group ahead, its key codes while the previous group's values are multiplied, and its value codes,
-// into the buffer the keys leave, while its keys are multiplied; the waits count the copies.
+// operand reads of a tile spread over all LDS banks.  All global reads are LDS copies, issued for a whole
+// group (metadata, key and value codes: 9 KB of 2-bit codes) one group ahead: as soon as a group's codes
+// are in registers, the next group's copies go out and stay in flight while this group is multiplied.
+// The wait at the top of a group counts every copy.
 // ---------------------------------------------------------------------------------------------
 typedef __attribute__((ext_vector_type(4))) int mf_i32x4;
 
@@ -672,6 +624,23 @@ __device__ __forceinline__ mf_i32x4 mfma_i8x64(mf_i32x4 a, mf_i32x4 b, mf_i32x4 
 __device__ __forceinline__ mf_i32x4 codes_i8(uint32_t w) {
   return mf_i32x4{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
                   (int)((w >> 6) & 0x03030303u)};
+}
+// Two words of 2-bit codes at once: each shift of the 64-bit pair serves both (the bits one word takes from
+// the other land outside the mask)
+__device__ __forceinline__ uint64_t shr64(uint64_t w, int n) {
+  // one 64-bit shift (the compiler would split a C++ shift into two 32-bit ones); its operand is a load's
+  // result, not a matrix-core one
+  uint64_t r;
+  asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "i"(n), "v"(w));
+  return r;
+}
+__device__ __forceinline__ void codes_i8_pair(uint32_t w0, uint32_t w1, mf_i32x4& c0, mf_i32x4& c1) {
+  const uint64_t w = ((uint64_t)w1 << 32) | w0;
+  const uint64_t s2 = shr64(w, 2), s4 = shr64(w, 4), s6 = shr64(w, 6);
+  constexpr uint32_t M = 0x03030303u;
+  c0 = mf_i32x4{(int)(w0 & M), (int)((uint32_t)s2 & M), (int)((uint32_t)s4 & M), (int)((uint32_t)s6 & M)};
+  c1 = mf_i32x4{(int)(w1 & M), (int)((uint32_t)(s2 >> 32) & M), (int)((uint32_t)(s4 >> 32) & M),
+                (int)((uint32_t)(s6 >> 32) & M)};
 }
 __device__ __forceinline__ mf_i32x4 u4_i32x4(uint4 v) { return mf_i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}; }
 // Three signed byte limbs.  An operand x with |x| <= S is rounded to an integer a = lo + 256 mid + 65536 hi
@@ -702,10 +671,11 @@ __device__ __forceinline__ void limbs3(float e0, float e1, float e2, float e3, u
 // heads 2 q + r / 2 with limb r % 2, the top limbs in a second tile at rows 4 q + 2 e.
 template <int GQ>
 __device__ __forceinline__ int limbs3_sum(const mf_i32x4& t, const mf_i32x4& x, int e) {
-  if constexpr (GQ == 8)
-    return (int)((uint32_t)t[2 * e] + ((uint32_t)t[2 * e + 1] << 8) + ((uint32_t)x[2 * e] << 16));
-  else
-    return (int)((uint32_t)t[0] + ((uint32_t)t[1] << 8) + ((uint32_t)t[2] << 16));
+  // Horner form: two shift-adds (v_lshl_add_u32)
+  const uint32_t hi = GQ == 8 ? (uint32_t)x[2 * e] : (uint32_t)t[2];
+  const uint32_t mid = GQ == 8 ? (uint32_t)t[2 * e + 1] : (uint32_t)t[1];
+  const uint32_t lo = GQ == 8 ? (uint32_t)t[2 * e] : (uint32_t)t[0];
+  return (int)((((hi << 8) + mid) << 8) + lo);
 }
 // N 32-bit words to LDS at dst (aligned to 4 N bytes).
 template <int N>
@@ -794,7 +764,7 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ng = n_groups_of(T, g.S0, g.W);
-  const int chunk_id = 4 * chunk + wave;  // one chunk per wave
+  const int chunk_id = chunk;  // one chunk per wave
   const int g_begin = chunk_id * g.gpc;
   int g_end = (g_begin + g.gpc) < ng ? (g_begin + g.gpc) : ng;
   if (g_end > g.max_pages / 2) g_end = g.max_pages / 2;  // never index past the page-table row
@@ -829,7 +799,7 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   const uint8_t* k_rd1 = BITS == 2 ? reinterpret_cast<const uint8_t*>(W.kst) + 32 * (krow + (y0 ^ 1)) + 8 * q4
                                    : k_rd0 + 128;
   // value operand reads: channel c + 16 tau, code word q4 (2-bit) or words 2 q4, 2 q4 + 1 (4-bit), page kappa
-  const uint32_t* v_rd = reinterpret_cast<const uint32_t*>(W.kst) + (BITS == 2 ? 4 * c + q4 : 8 * c + 2 * q4);
+  const uint32_t* v_rd = reinterpret_cast<const uint32_t*>(W.vst) + (BITS == 2 ? 4 * c + q4 : 8 * c + 2 * q4);
   // alpha step: head ah, key positions Q0 .. Q0 + NCH - 1
   const int ah = lane >> (6 - LG);
   const int Q0 = (lane & (LPH - 1)) * NCH;
@@ -842,11 +812,11 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     const int tl = 32 * jj + ((lane >> 1) ^ ((lane >> 3) & 3));
     koff[jj] = (uint32_t)(tl * 32 + 16 * (lane & 1));
   }
-  const uint32_t kst_a = lds_addr(W.kst);
+  const uint32_t kst_a = lds_addr(W.kst), vst_a = lds_addr(W.vst);
   const uint32_t mst_a0 = lds_addr(W.mst[0]), mst_a1 = lds_addr(W.mst[1]);
   const uint8_t* pages = a.pages;
   const long long pbytes = g.page_bytes, hoff = (long long)h * g.head_bytes;
-  auto page_of = [&](int idx) { return pages + (long long)idx * pbytes + hoff; };
+  auto page_of = [&](int idx) { return pages + pool_page(g, idx) * pbytes + hoff; };
   constexpr int META = BITS == 2 ? I2_META_OFF : I4C_META_OFF;
   constexpr int KOFF = BITS == 2 ? I2_K_OFF : I4C_K_OFF, VOFF = BITS == 2 ? I2_V_OFF : I4C_V_OFF;
   auto issue_m = [&](int2 p, int buf) {
@@ -866,7 +836,7 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   auto issue_v = [&](int2 p) {
 #pragma unroll
     for (int j = 0; j < NCP; ++j)
-      dma16_base(kst_a + 1024 * j, page_of(j < NCP / 2 ? p.x : p.y) + VOFF + 1024 * (j % (NCP / 2)), lane * 16);
+      dma16_base(vst_a + 1024 * j, page_of(j < NCP / 2 ? p.x : p.y) + VOFF + 1024 * (j % (NCP / 2)), lane * 16);
   };
 
   float qa[NCH];
@@ -905,23 +875,59 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
 #pragma unroll
     for (int t = 0; t < 8; ++t) o[e][t] = 0.0f;
   }
-  const int2* pt = reinterpret_cast<const int2*>(a.page_table + (long long)b * g.max_pages);
-  int2 pcur = make_int2(0, 0), pnext = make_int2(0, 0);
+  // page pairs: the first by scalar loads; afterwards a group's copies go out together with a vector load of
+  // the pair after it, which arrives with them (a scalar-cache miss on the page table, cold every step, would
+  // otherwise hold up the next group's copies)
+  const int32_t* ptrow = a.page_table + (long long)b * g.max_pages;
+  auto pair_v = [&](int gi) { return make_int2(ptrow[2 * gi], ptrow[2 * gi + 1]); };
+  int2 pv = make_int2(0, 0);
   int mb = 0;
   if (g_first < g_end) {
-    pcur = scalar_load_int2(pt + g_first);
-    issue_m(pcur, 0);
-    issue_k(pcur);
+    const int2 p0 = scalar_load_int2(reinterpret_cast<const int2*>(ptrow) + g_first);
+    issue_m(p0, 0);
+    issue_k(p0);
+    issue_v(p0);
+    if (g_first + gstep < g_end) pv = pair_v(g_first + gstep);
   }
-  wave_lds_sync();
   const mf_i32x4 zero4 = {0, 0, 0, 0};
   const mf_i32x4 ones4 = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
   for (int gi = g_first; gi < g_end; gi += gstep) {
     const bool has_next = gi + gstep < g_end;  // uniform
-    if (has_next) pnext = scalar_load_int2(pt + gi + gstep);
-    // this group's metadata (its key copies may be in flight)
-    if constexpr (NCP == 4) KVQ_WAIT_VM(4);
-    else KVQ_WAIT_VM(8);
+    KVQ_WAIT_VM(0);  // this group's metadata, key and value codes, and the next group's pages
+    wave_lds_sync();
+    // 0. the group's codes to registers (key tiles: 2-bit .x, .y; 4-bit all four words; value tiles: 2-bit
+    //    .x, 4-bit both words), then the next group's copies into the buffers they leave
+    uint4 kw[8];
+    uint2 vw[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (BITS == 2) {
+        const uint2 t2 = *reinterpret_cast<const uint2*>((i < 4 ? k_rd0 : k_rd1) + 512 * (i & 3));
+        kw[i] = make_uint4(t2.x, t2.y, 0u, 0u);
+      } else {
+        kw[i] = *reinterpret_cast<const uint4*>((i < 4 ? k_rd0 : k_rd1) + 1024 * (i & 3));
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if constexpr (BITS == 2) {
+        // the two pages' words of channel tile t side by side (one 64-bit shift unpacks both)
+        const uint2 pr = make_uint2(v_rd[64 * t], v_rd[512 + 64 * t]);
+        vw[t][0] = make_uint2(pr.x, pr.y);
+        vw[t][1] = make_uint2(pr.y, 0u);
+      } else {
+        vw[t][0] = *reinterpret_cast<const uint2*>(v_rd + 128 * t);
+        vw[t][1] = *reinterpret_cast<const uint2*>(v_rd + 1024 + 128 * t);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (has_next) {
+      const int2 pn = make_int2(__builtin_amdgcn_readfirstlane(pv.x), __builtin_amdgcn_readfirstlane(pv.y));
+      issue_m(pn, mb ^ 1);
+      issue_k(pn);
+      issue_v(pn);
+      if (gi + 2 * gstep < g_end) pv = pair_v(gi + 2 * gstep);
+    }
     const uint16_t* ms = reinterpret_cast<const uint16_t*>(W.mst[mb]);
     // 1. per channel: key-side operand alpha = q~ s of head ah at positions Q0 + i, three limbs;
     //    per token: the group's token scales and zeros (tokens T(i, c) of the lane's page c / 8)
@@ -980,36 +986,27 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
         AZe[e] = head_value(AZh, e);
       }
     }
-    if (has_next) issue_m(pnext, mb ^ 1);
     wave_lds_sync();
 
     // 2. key products: 8 token tiles x 2 channel halves (at GQ 8 also for the top-limb tile)
-    if (has_next) KVQ_WAIT_VM(1);  // this group's key copies (the next metadata follows)
-    else KVQ_WAIT_VM(0);
-    uint4 kw[8];  // 2-bit: .x, .y; 4-bit: all four words
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if constexpr (BITS == 2) {
-        const uint2 t2 = *reinterpret_cast<const uint2*>((i < 4 ? k_rd0 : k_rd1) + 512 * (i & 3));
-        kw[i] = make_uint4(t2.x, t2.y, 0u, 0u);
-      } else {
-        kw[i] = *reinterpret_cast<const uint4*>((i < 4 ? k_rd0 : k_rd1) + 1024 * (i & 3));
-      }
-    }
     mf_i32x4 A[2][2];
     if constexpr (TOK) {
 #pragma unroll
       for (int x = 0; x < 2; ++x) A[x][0] = At_op[x][0], A[x][1] = At_op[x][1];
     } else {
       load_op(A);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the weights overwrite the plane
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    issue_v(pcur);  // into the buffer the key codes have left
     mf_i32x4 acc[8], accx[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const mf_i32x4 c0 = BITS == 2 ? codes_i8(kw[i].x) : nibbles_i8(kw[i].x, kw[i].y);
-      const mf_i32x4 c1 = BITS == 2 ? codes_i8(kw[i].y) : nibbles_i8(kw[i].z, kw[i].w);
+      mf_i32x4 c0, c1;
+      if constexpr (BITS == 2) {
+        codes_i8_pair(kw[i].x, kw[i].y, c0, c1);
+      } else {
+        c0 = nibbles_i8(kw[i].x, kw[i].y);
+        c1 = nibbles_i8(kw[i].z, kw[i].w);
+      }
       acc[i] = mfma_i8x64(A[0][0], c0, zero4);
       acc[i] = mfma_i8x64(A[0][1], c1, acc[i]);
       if constexpr (GQ == 8) {
@@ -1074,22 +1071,9 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     wave_lds_sync();
 
     // 4. value products: 8 channel tiles x 2 pages, and the weight sums
-    KVQ_WAIT_VM(0);  // this group's value copies, the youngest in flight
-    uint2 vw[8][2];  // 2-bit: .x; 4-bit: both words
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      if constexpr (BITS == 2) {
-        vw[t][0] = make_uint2(v_rd[64 * t], 0u);
-        vw[t][1] = make_uint2(v_rd[512 + 64 * t], 0u);
-      } else {
-        vw[t][0] = *reinterpret_cast<const uint2*>(v_rd + 128 * t);
-        vw[t][1] = *reinterpret_cast<const uint2*>(v_rd + 1024 + 128 * t);
-      }
-    }
     mf_i32x4 Wt[2][2];
     load_op(Wt);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (has_next) issue_k(pnext);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next group's operand overwrites it
     mf_i32x4 accp = zero4, accpx = zero4;
     if constexpr (!TOK) {
       accp = mfma_i8x64(Wt[0][0], ones4, zero4);
@@ -1101,8 +1085,13 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const mf_i32x4 c0 = BITS == 2 ? codes_i8(vw[t][0].x) : nibbles_i8(vw[t][0].x, vw[t][0].y);
-      const mf_i32x4 c1 = BITS == 2 ? codes_i8(vw[t][1].x) : nibbles_i8(vw[t][1].x, vw[t][1].y);
+      mf_i32x4 c0, c1;
+      if constexpr (BITS == 2) {
+        codes_i8_pair(vw[t][0].x, vw[t][0].y, c0, c1);
+      } else {
+        c0 = nibbles_i8(vw[t][0].x, vw[t][0].y);
+        c1 = nibbles_i8(vw[t][1].x, vw[t][1].y);
+      }
       acc[t] = mfma_i8x64(Wt[0][0], c0, zero4);
       acc[t] = mfma_i8x64(Wt[0][1], c1, acc[t]);
       if constexpr (GQ == 8) {
@@ -1139,7 +1128,6 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
       m[e] = mnew;
     }
     mb ^= 1;
-    pcur = pnext;
   }
   if constexpr (!TOK) {
 #pragma unroll
@@ -1204,7 +1192,7 @@ __device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int npages = (T + PAGE - 1) / PAGE;
   const int npairs = (npages + 1) / 2;
-  const int chunk_id = 4 * chunk + wave;  // one chunk (an even number of pages) per wave
+  const int chunk_id = chunk;  // one chunk (an even number of pages) per wave
   const int pb = chunk_id * (g.gpc / 2);
   int pe = pb + g.gpc / 2 < npairs ? pb + g.gpc / 2 : npairs;
   if (2 * pe > g.max_pages + 1) pe = (g.max_pages + 1) / 2;  // never index past the page-table row
@@ -1233,18 +1221,18 @@ __device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int
   const uint8_t* k_rd0 = reinterpret_cast<const uint8_t*>(W.kst) + 64 * (krow + y) + 16 * q4;
   const uint8_t* k_rd1 = reinterpret_cast<const uint8_t*>(W.kst) + 64 * (krow + (y ^ 1)) + 16 * q4;
   // value operand reads: channel c + 16 tau, code words 2 q4, 2 q4 + 1, page kappa
-  const uint8_t* v_rd = reinterpret_cast<const uint8_t*>(W.kst) + 32 * c + 8 * q4;
+  const uint8_t* v_rd = reinterpret_cast<const uint8_t*>(W.vst) + 32 * c + 8 * q4;
   // this lane's tokens T(i, c) (pair-local), their metadata words: K (s, z) at (2 page) 64 + t, V at + 64
   const int tok0 = 64 * (c >> 3) + 32 * (c & 1) + 4 * ((c >> 1) & 3);
   const int ah = lane >> (6 - LG);
   const int Q0 = (lane & (LPH - 1)) * NCH;
   // copies: key slots 64 j + lane hold staged row 16 j + lane / 4, quarter lane % 4
   const uint32_t koff = (uint32_t)(64 * ((lane >> 2) ^ ((lane >> 4) & 1)) + 16 * (lane & 3));
-  const uint32_t kst_a = lds_addr(W.kst);
+  const uint32_t kst_a = lds_addr(W.kst), vst_a = lds_addr(W.vst);
   const uint32_t mst_a0 = lds_addr(W.mst[0]), mst_a1 = lds_addr(W.mst[1]);
   const uint8_t* pages = a.pages;
   const long long pbytes = g.page_bytes, hoff = (long long)h * g.head_bytes;
-  auto page_of = [&](int idx) { return pages + (long long)idx * pbytes + hoff; };
+  auto page_of = [&](int idx) { return pages + pool_page(g, idx) * pbytes + hoff; };
   auto issue_m = [&](int2 p, int buf) {
     const uint8_t* src = (lane >= 32 ? page_of(p.y) : page_of(p.x)) + ((lane & 16) ? I4_VMETA_OFF : I4_KMETA_OFF) +
                          (lane & 15) * 16;
@@ -1258,12 +1246,19 @@ __device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int
   auto issue_v = [&](int2 p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      dma16_base(kst_a + 1024 * j, page_of(j < 4 ? p.x : p.y) + I4_V_OFF + 1024 * (j & 3), lane * 16);
+      dma16_base(vst_a + 1024 * j, page_of(j < 4 ? p.x : p.y) + I4_V_OFF + 1024 * (j & 3), lane * 16);
   };
+  // page pairs (a missing second page is the first again): the first by scalar loads; afterwards a pair's
+  // copies go out together with a vector load of the pair after it, which arrives with them
   const int32_t* ptr = a.page_table + (long long)b * g.max_pages;
-  auto pages_of = [&](int i) {  // scalar loads: a vector load would enter the counter the waits count
+  auto pages_of = [&](int i) {
     const int x = scalar_load_int(ptr + 2 * i);
     const int yy = 2 * i + 1 < npages ? scalar_load_int(ptr + 2 * i + 1) : x;
+    return make_int2(x, yy);
+  };
+  auto pages_v = [&](int i) {
+    const int x = ptr[2 * i];
+    const int yy = 2 * i + 1 < npages ? ptr[2 * i + 1] : x;
     return make_int2(x, yy);
   };
 
@@ -1298,20 +1293,32 @@ __device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int
 #pragma unroll
     for (int t = 0; t < 8; ++t) o[e][t] = 0.0f;
   }
-  int2 pcur = make_int2(0, 0), pnext = make_int2(0, 0);
+  int2 pv = make_int2(0, 0);
   int mb = 0;
   if (pb < pe) {
-    pcur = pages_of(pb);
-    issue_m(pcur, 0);
-    issue_k(pcur);
+    const int2 p0 = pages_of(pb);
+    issue_m(p0, 0);
+    issue_k(p0);
+    issue_v(p0);
+    if (pb + 1 < pe) pv = pages_v(pb + 1);
   }
-  wave_lds_sync();
   const mf_i32x4 zero4 = {0, 0, 0, 0};
   for (int pi = pb; pi < pe; ++pi) {
     const bool has_next = pi + 1 < pe;  // uniform
-    if (has_next) pnext = pages_of(pi + 1);
-    KVQ_WAIT_VM(8);  // this pair's metadata (its key copies may be in flight)
-    // 1. the lane's tokens: K and V (scale, zero) words, validity
+    KVQ_WAIT_VM(0);  // this pair's metadata, key and value codes, and the next pair's pages
+    wave_lds_sync();
+    // 0. the pair's codes and the lane's token metadata to registers, then the next pair's copies
+    uint4 kw[8];
+    uint2 vw[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      kw[i] = *reinterpret_cast<const uint4*>((i < 4 ? k_rd0 : k_rd1) + 1024 * ((i >> 1) & 1) + 128 * (i & 1));
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      vw[t][0] = *reinterpret_cast<const uint2*>(v_rd + 512 * t);
+      vw[t][1] = *reinterpret_cast<const uint2*>(v_rd + 4096 + 512 * t);
+    }
+    // the lane's tokens: K and V (scale, zero) words, validity
     const uint32_t* mw = reinterpret_cast<const uint32_t*>(W.mst[mb]) + 128 * (c >> 3);  // its page's K, then V
     float tks[8], tkz[8], tvs[8], tvz[8];
     bool ok[8];
@@ -1327,17 +1334,15 @@ __device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int
       tvz[i] = ok[i] ? __uint_as_float(wv & 0xffff0000u) : 0.0f;
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (has_next) issue_m(pnext, mb ^ 1);
+    if (has_next) {
+      const int2 pn = make_int2(__builtin_amdgcn_readfirstlane(pv.x), __builtin_amdgcn_readfirstlane(pv.y));
+      issue_m(pn, mb ^ 1);
+      issue_k(pn);
+      issue_v(pn);
+      if (pi + 2 < pe) pv = pages_v(pi + 2);
+    }
 
-    // 2. key products: 8 token tiles x 2 channel halves
-    if (has_next) KVQ_WAIT_VM(1);  // this pair's key copies (the next metadata follows)
-    else KVQ_WAIT_VM(0);
-    uint4 kw[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      kw[i] = *reinterpret_cast<const uint4*>((i < 4 ? k_rd0 : k_rd1) + 1024 * ((i >> 1) & 1) + 128 * (i & 1));
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    issue_v(pcur);  // into the buffer the key codes have left
+    // 1. key products: 8 token tiles x 2 channel halves (at GQ 8 also for the top-limb tile)
     mf_i32x4 acc[8], accx[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -1350,7 +1355,7 @@ __device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int
       }
     }
 
-    // 3. logits, the pair's maximum, weights u_t = rint(S p_t s'_t / S'), P = sum p_t, Z = sum u_t z'_t
+    // 2. logits, the pair's maximum, weights u_t = rint(S p_t s'_t / S'), P = sum p_t, Z = sum u_t z'_t
     float mg[HPL], Sg[HPL], Pt[HPL], Zt[HPL];
 #pragma unroll
     for (int e = 0; e < HPL; ++e) {
@@ -1387,18 +1392,10 @@ __device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int
     }
     wave_lds_sync();
 
-    // 4. value products: 8 channel tiles x 2 pages
-    KVQ_WAIT_VM(0);  // this pair's value copies, the youngest in flight
-    uint2 vw[8][2];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      vw[t][0] = *reinterpret_cast<const uint2*>(v_rd + 512 * t);
-      vw[t][1] = *reinterpret_cast<const uint2*>(v_rd + 4096 + 512 * t);
-    }
+    // 3. value products: 8 channel tiles x 2 pages
     mf_i32x4 Wt[2][2];
     load_op(Wt);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (has_next) issue_k(pnext);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next pair's weights overwrite them
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const mf_i32x4 c0 = nibbles_i8(vw[t][0].x, vw[t][0].y), c1 = nibbles_i8(vw[t][1].x, vw[t][1].y);
@@ -1410,7 +1407,7 @@ __device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int
       }
     }
 
-    // 5. online-softmax update in the rotated value frame: the pair adds (S' / S) (U_c - Z) and P
+    // 4. online-softmax update in the rotated value frame: the pair adds (S' / S) (U_c - Z) and P
 #pragma unroll
     for (int e = 0; e < HPL; ++e) {
       const float mnew = fmax_raw(m[e], mg[e]);
@@ -1424,7 +1421,6 @@ __device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int
       m[e] = mnew;
     }
     mb ^= 1;
-    pcur = pnext;
   }
   // every partial a merge reads is written; chunks past the length or the launch bound have none
   if (pb < npairs && chunk_id < g.n_units - 1) {
@@ -1444,67 +1440,110 @@ __device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int
   }
 }
 
-// Work-groups of the split-K launch per (sequence, kv head), besides its band unit.
-__host__ __device__ inline int splitk_wgs_per_pair(const Geo& g) {
-  return g.wave_chunks ? (g.n_units - 1 + 3) / 4 : g.n_units - 1;
+// One-dimensional split-K grid: the quantized-chunk work-groups, chunk-major (every sequence's first chunk
+// work-groups, then every sequence's second, ...), and one band work-group per (sequence, kv head).  The hardware
+// hands consecutive work-groups to the eight XCDs in turn, so every XCD gets the same mix of chunk positions
+// (sequence-major, a chunk position would stay on one XCD, and the last chunks, which short sequences lack,
+// would leave theirs idle).  When the launch fits the GPU in one round of work-groups the band work-groups
+// come last (measured faster at batch 32 x 32k); when it takes several rounds they come first, so that they
+// overlap the chunk walks instead of trailing them (4 x 131k at 512-token chunks: 108 -> 86 us).
+// Chunk work-groups:
+//  - matrix-core decode, n_kv a multiple of 4 (head quads): one chunk of four kv heads of a sequence, wave w
+//    taking head 4 hq + w, so that the work-group's copies of a page read four neighbouring head blocks
+//    together;
+//  - matrix-core decode otherwise: four consecutive chunks of one (sequence, kv head), one per wave;
+//  - fp32 decode: one chunk of one (sequence, kv head), shared by the four waves.
+__host__ __device__ inline bool splitk_head_quads(const Geo& g) { return g.wave_chunks && g.n_kv % 4 == 0; }
+__host__ __device__ inline int splitk_chunk_wgs(const Geo& g) {
+  const int nc = g.n_units - 1;
+  if (!g.wave_chunks) return g.batch * g.n_kv * nc;
+  if (splitk_head_quads(g)) return g.batch * (g.n_kv / 4) * nc;
+  return g.batch * g.n_kv * ((nc + 3) / 4);
 }
-// One-dimensional grid: the quantized-chunk work-groups first, chunk-major (every pair's first chunk
-// work-group, then every pair's second, ...), then the band work-groups.  The hardware hands consecutive
-// work-groups to the eight XCDs in turn, so every XCD gets the same mix of chunk positions (pair-major,
-// a chunk position would stay on one XCD, and the last chunks, which short sequences lack, would leave
-// theirs idle; a band unit inside each pair's run would do the same to the band), and the short band
-// work-groups fill the end of the launch.
-__device__ inline void splitk_unit_of(const Geo& g, int& unit, int& h, int& b) {
-  const int m = splitk_wgs_per_pair(g);
-  const int pairs = g.batch * g.n_kv;
-  const int i = blockIdx.x;
-  int pair;
-  if (i < pairs * m) {
-    pair = i % pairs;
-    unit = 1 + i / pairs;
-  } else {
-    pair = i - pairs * m;
-    unit = 0;
+__host__ __device__ inline int splitk_wgs(const Geo& g) { return splitk_chunk_wgs(g) + g.batch * g.n_kv; }
+// Work-group i of the split-K grid: true for a band work-group (idx = its (sequence, kv head) pair), false
+// for a chunk work-group (idx = its index among the chunk work-groups).
+__device__ inline bool splitk_is_band(const Geo& g, int i, int& idx) {
+  const int pairs = g.batch * g.n_kv, nw = splitk_chunk_wgs(g);
+  if (g.band_first) {
+    idx = i < pairs ? i : i - pairs;
+    return i < pairs;
   }
+  idx = i < nw ? i : i - nw;
+  return i >= nw;
+}
+// fp32 decode: the unit (0 = band, u >= 1 = chunk u - 1), kv head and sequence of this work-group
+__device__ inline void splitk_unit_of(const Geo& g, int& unit, int& h, int& b) {
+  const int pairs = g.batch * g.n_kv;
+  int idx;
+  const bool band = splitk_is_band(g, blockIdx.x, idx);
+  const int pair = band ? idx : idx % pairs;
+  unit = band ? 0 : 1 + idx / pairs;
   h = pair % g.n_kv;
   b = pair / g.n_kv;
 }
+// matrix-core decode, chunk work-group i: its sequence, and this wave's kv head and chunk; returns the
+// work-group's first chunk (every wave's chunk at least that)
+__device__ inline int wave_chunk_of(const Geo& g, int i, int wave, int& b, int& h, int& chunk) {
+  if (splitk_head_quads(g)) {
+    const int quads = g.n_kv / 4, per = g.batch * quads;
+    const int r = i % per;
+    b = r / quads;
+    h = 4 * (r % quads) + wave;
+    chunk = i / per;
+    return chunk;
+  }
+  const int pairs = g.batch * g.n_kv, pair = i % pairs;
+  b = pair / g.n_kv;
+  h = pair % g.n_kv;
+  chunk = 4 * (i / pairs) + wave;
+  return 4 * (i / pairs);
+}
 
-// Matrix-core INT2 launch: its own kernel so that the register bound allows four waves per SIMD at GQ <= 4.
+// Matrix-core launch of the grouped schemes.  Work-groups per CU, as the LDS allows (160 KB): 2-bit codes
+// three up to GQ 4 (48.5 KB each), two at GQ 8; 4-bit codes two up to GQ 4 (81 KB), one at GQ 8.
 template <int GQ, bool TOK, int BITS>
-__global__ __launch_bounds__(kThreads, GQ <= 4 ? (BITS == 2 ? 4 : 3) : 2) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, GQ <= 4 ? (BITS == 2 ? 3 : 2) : (BITS == 2 ? 2 : 1)) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ DecodeLds<GQ, BITS / 2, true> L;
   const Geo& g = a.g;
-  int unit, h, b;
-  splitk_unit_of(g, unit, h, b);
+  int i;
+  if (splitk_is_band(g, blockIdx.x, i)) {
+    band_unit<GQ>(L, a, i / g.n_kv, i % g.n_kv, a.seq_lens[i / g.n_kv]);
+    return;
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int b, h, chunk;
+  const int first = wave_chunk_of(g, i, wave, b, h, chunk);
   const int T = a.seq_lens[b];
   int n_chunks = (n_groups_of(T, g.S0, g.W) + g.gpc - 1) / g.gpc;
   if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;  // lengths beyond the launch bound are cut
-  if (unit > (n_chunks + 3) / 4) return;
-  if (unit == 0) band_unit<GQ>(L, a, b, h, T);
-  else int2_unit_mfma<GQ, TOK, BITS>(L, a, b, h, T, unit - 1);
+  if (first >= n_chunks) return;                           // uniform over the work-group
+  int2_unit_mfma<GQ, TOK, BITS>(L, a, b, h, T, chunk);
 }
 
-// Matrix-core INT4 per-token launch (page pairs; no band: unit 0 stores an empty partial).
+// Matrix-core INT4 per-token launch (page pairs; no band: the band work-groups store an empty partial).
 template <int GQ>
-__global__ __launch_bounds__(kThreads, GQ <= 4 ? 3 : 2) void decode_mfma4_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, GQ <= 4 ? 2 : 1) void decode_mfma4_kernel(DecodeArgs a) {
   __shared__ DecodeLds<GQ, 2, true> L;
   const Geo& g = a.g;
-  int unit, h, b;
-  splitk_unit_of(g, unit, h, b);
-  const int T = a.seq_lens[b];
-  int n_chunks = ((T + PAGE - 1) / PAGE + g.gpc - 1) / g.gpc;
-  if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;  // lengths beyond the launch bound are cut
-  if (unit > (n_chunks + 3) / 4) return;
-  if (unit == 0) {
+  int i;
+  if (splitk_is_band(g, blockIdx.x, i)) {
+    const int b = i / g.n_kv, h = i % g.n_kv;
     for (int e = threadIdx.x; e < GQ * PART_STRIDE; e += kThreads) {
       const int hh = e / PART_STRIDE, k = e % PART_STRIDE;
       float* part = a.partials + (((long long)b * g.n_q + h * GQ + hh) * g.n_units) * PART_STRIDE;
       part[k] = (k == 0) ? -INFINITY : 0.0f;
     }
-  } else {
-    int4tok_unit_mfma<GQ>(L, a, b, h, T, unit - 1);
+    return;
   }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int b, h, chunk;
+  const int first = wave_chunk_of(g, i, wave, b, h, chunk);
+  const int T = a.seq_lens[b];
+  int n_chunks = ((T + PAGE - 1) / PAGE + g.gpc - 1) / g.gpc;
+  if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;  // lengths beyond the launch bound are cut
+  if (first >= n_chunks) return;                           // uniform over the work-group
+  int4tok_unit_mfma<GQ>(L, a, b, h, T, chunk);
 }
 
 // fp32 decode (exact arithmetic on the codes; the cross-check of the matrix-core decode): the four waves of
@@ -1542,6 +1581,69 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
     int2_unit<GQ>(L, a, b, h, T, unit - 1);
   } else {
     int4_unit<GQ>(L, a, b, h, T, unit - 1);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Query preparation ([SAW] §4.1 and [NOVA] App. B.5: the query rotated once per step): one work-group of 512
+// threads per (kv head, query row): q~ = (q R_K) log2e/sqrt(128) for the quantized tokens (rotated frame) and
+// q log2e/sqrt(128) for the bf16 band (original frame), both to the workspace.
+// ---------------------------------------------------------------------------------------------
+template <int GQ>
+__global__ __launch_bounds__(512) void prep_kernel(DecodeArgs a) {
+  __shared__ float qs[GQ][D];
+  __shared__ float part[4][GQ][D];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int j = tid & (D - 1), qtr = tid >> 7;  // column j, quarter qtr of the 128 input channels
+  const long long base = ((long long)b * a.g.n_q + h * GQ) * D;
+  const float scale = LOG2E * kInvSqrt128;
+  const bool dense = a.g.rotation == KVQ_ROT_DENSE;
+  // this thread's 32 entries of column j of R_K, read together with the queries (one round trip)
+  float rk[32];
+  if (dense) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) rk[i] = a.rot_k[(qtr * 32 + i) * D + j];
+  }
+  for (int e = tid; e < GQ * D; e += 512) {
+    const int hh = e / D, c = e % D;
+    const float qv = a.q_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[base + e])
+                              : static_cast<const float*>(a.q)[base + e];
+    a.qband[base + e] = qv * scale;
+    qs[hh][c] = dense ? qv : qv * a.rot_k[c];
+  }
+  __syncthreads();
+  if (dense) {
+    float r[GQ];
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) r[hh] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) r[hh] = fmaf(qs[hh][qtr * 32 + i], rk[i], r[hh]);
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) part[qtr][hh][j] = r[hh];
+    __syncthreads();
+    for (int e = tid; e < GQ * D; e += 512) {
+      const int hh = e / D, c = e % D;
+      a.qrot[base + e] = ((part[0][hh][c] + part[1][hh][c]) + (part[2][hh][c] + part[3][hh][c])) * scale;
+    }
+  } else {
+    // randomized (block-diagonal) Hadamard: FWHT within blocks of h channels in LDS
+    for (int hb = 1; hb < a.g.hblock; hb <<= 1) {
+      float x[GQ / 4 + 1];
+      int n = 0;
+      for (int e = tid; e < GQ * D; e += 512) {
+        const int hh = e / D, c = e % D;
+        const float u = qs[hh][c], v = qs[hh][c ^ hb];
+        x[n++] = (c & hb) ? (v - u) : (u + v);
+      }
+      __syncthreads();
+      n = 0;
+      for (int e = tid; e < GQ * D; e += 512) qs[e / D][e % D] = x[n++];
+      __syncthreads();
+    }
+    const float hs = (float)a.g.hscale;
+    for (int e = tid; e < GQ * D; e += 512) a.qrot[base + e] = qs[e / D][e % D] * hs * scale;
   }
 }
 
@@ -1755,10 +1857,10 @@ __global__ __launch_bounds__(MergeShape<HPW>::NT) void merge_kernel(DecodeArgs a
 template <int GQ>
 hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
   const Geo& g = a.g;
-  if (stages & KVQ_STAGE_QPREP) hipLaunchKernelGGL(qprep_kernel<GQ>, dim3(g.n_kv, g.batch), dim3(512), 0, s, a);
+  if (stages & KVQ_STAGE_QPREP) hipLaunchKernelGGL(prep_kernel<GQ>, dim3(g.n_kv, g.batch), dim3(512), 0, s, a);
   if (stages & KVQ_STAGE_SPLITK) {
     // matrix-core decode: a wave per chunk, four chunks per work-group; fp32 decode: a chunk per work-group
-    const dim3 grid((1 + splitk_wgs_per_pair(g)) * g.batch * g.n_kv), block(kThreads);
+    const dim3 grid(splitk_wgs(g)), block(kThreads);
     if (a.impl == KVQ_DECODE_MFMA) {
       if (g.scheme == KVQ_INT4_CHANNEL) hipLaunchKernelGGL((decode_mfma_kernel<GQ, false, 4>), grid, block, 0, s, a);
       else if (g.scheme == KVQ_INT2_TOKEN) hipLaunchKernelGGL((decode_mfma_kernel<GQ, true, 2>), grid, block, 0, s, a);
@@ -1786,10 +1888,10 @@ hipError_t launch_qprep_rows(const DecodeArgs& a, int rows, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   const dim3 grid(a.g.n_kv, rows);
   switch (a.g.gq) {
-    case 1: hipLaunchKernelGGL(qprep_kernel<1>, grid, dim3(512), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(qprep_kernel<2>, grid, dim3(512), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(qprep_kernel<4>, grid, dim3(512), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(qprep_kernel<8>, grid, dim3(512), 0, s, a); break;
+    case 1: hipLaunchKernelGGL(prep_kernel<1>, grid, dim3(512), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(prep_kernel<2>, grid, dim3(512), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(prep_kernel<4>, grid, dim3(512), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(prep_kernel<8>, grid, dim3(512), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -48,11 +48,13 @@ struct Geo {
   int W;
   int slots;        // band slots per (seq, kv head)
   int max_pages;    // page-table row length
+  long long n_pages;  // physical pages in the pool
   int head_bytes;
   long long page_bytes;
   int gpc;          // groups (grouped schemes) or pages (INT4 per token) per decode chunk
   int n_units;      // decode partial units per (seq, q head): 1 band unit + chunks
   int wave_chunks;  // 1: each wave of a work-group walks a chunk of its own and stores its partial
+  int band_first;   // 1: the split-K grid starts with its band work-groups (launches of more than one round)
 };
 
 // both INT2 schemes share the page layout; they and per-channel INT4 share the band and the group demotion
@@ -66,6 +68,13 @@ __host__ __device__ inline int n_groups_of(int T, int S0, int W) {
 
 __host__ __device__ inline int band_slot_of(int t, int S0, int W) {
   return t < S0 ? t : S0 + (t - S0) % (W + GROUP);
+}
+
+// A physical page index from the page table, held inside the pool: an entry outside [0, n_pages) (which
+// kvq_check_page_table reports on the host) is taken as the last page, so no access leaves the pool.
+__host__ __device__ inline long long pool_page(const Geo& g, int32_t p) {
+  const unsigned long long u = (unsigned long long)(unsigned int)p;
+  return (long long)(u < (unsigned long long)g.n_pages ? u : (unsigned long long)(g.n_pages - 1));
 }
 
 __device__ inline uint16_t f32_to_bf16_rne(float x) {
@@ -96,6 +105,8 @@ struct WriteArgs {
 
 hipError_t launch_write_int2(const WriteArgs& a, hipStream_t s);
 hipError_t launch_write_int4(const WriteArgs& a, hipStream_t s);
+hipError_t launch_debug_unpack(const WriteArgs& a, int seq, int kv_head, int n_tokens, uint8_t* codes_out,
+                               uint16_t* sz_out, hipStream_t s);
 hipError_t launch_debug_rotate(const float* rot, int rotation, int hblock, double hscale, const void* x, int src_bf16,
                                int n, int clip_j, float clip_f, float* out, hipStream_t s);
 

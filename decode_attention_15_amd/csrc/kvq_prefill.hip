@@ -258,13 +258,13 @@ __global__ __launch_bounds__(256) void prefill_int2_kernel(DecodeArgs a) {
   // copies of one group: wave 0 K page 0, wave 1 K page 1, wave 2 V page 0, wave 3 V page 1 + metadata
   auto issue = [&](int gi, int buf) {
     const int pp = wave & 1;
-    const uint8_t* pg = a.pages + (long long)pt[2 * gi + pp] * g.page_bytes + hoff;
+    const uint8_t* pg = a.pages + pool_page(g, pt[2 * gi + pp]) * g.page_bytes + hoff;
     uint32_t* dst = wave < 2 ? gb[buf].k[pp] : gb[buf].v[pp];
     const uint8_t* src = pg + (wave < 2 ? I2_K_OFF : I2_V_OFF);
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma16_p(lds_addr_p(dst + 256 * j), src + 1024 * j + 16 * lane);
     if (wave == 3) {
-      const uint8_t* pm = a.pages + (long long)pt[2 * gi + (lane >> 5)] * g.page_bytes + hoff + I2_META_OFF;
+      const uint8_t* pm = a.pages + pool_page(g, pt[2 * gi + (lane >> 5)]) * g.page_bytes + hoff + I2_META_OFF;
       dma16_p(lds_addr_p(gb[buf].meta), pm + 16 * (lane & 31));
     }
   };

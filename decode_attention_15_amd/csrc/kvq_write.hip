@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
         s_rs[tl] = rcp_of_bf16(sp);
         s_zp[tl] = bf16_to_f32(z16);
         // page of the token: its K (which = 0) or V (which = 1) scales[64] then zeros[64]
-        const long long phys = a.page_table[(long long)b * g.max_pages + 2 * grp + (tl >> 6)];
+        const long long phys = pool_page(g, a.page_table[(long long)b * g.max_pages + 2 * grp + (tl >> 6)]);
         uint16_t* meta = reinterpret_cast<uint16_t*>(a.pages + phys * g.page_bytes + hoff + moff) + which * 128;
         meta[tl & 63] = s16;
         meta[64 + (tl & 63)] = z16;
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
     const uint16_t z16 = f32_to_bf16_rne(__fdiv_rn(-amin, sp));
     s_rs[tid] = rcp_of_bf16(sp);
     s_zp[tid] = bf16_to_f32(z16);
-    const long long phys = a.page_table[(long long)b * g.max_pages + 2 * grp + which];
+    const long long phys = pool_page(g, a.page_table[(long long)b * g.max_pages + 2 * grp + which]);
     uint16_t* meta = reinterpret_cast<uint16_t*>(a.pages + phys * g.page_bytes + hoff + moff);
     meta[tid] = s16;
     meta[D + tid] = z16;
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
   if (which == 0) {
     // K, token-major; thread (token tl, half): channels 64 half .. 64 half + 63
     const int tl = tid >> 1, half = tid & 1;
-    const long long phys = a.page_table[(long long)b * g.max_pages + 2 * grp + (tl >> 6)];
+    const long long phys = pool_page(g, a.page_table[(long long)b * g.max_pages + 2 * grp + (tl >> 6)]);
     uint8_t* row = a.pages + phys * g.page_bytes + hoff + I2_K_OFF;
     const float* x = xr + tl * XS_STRIDE + half * 64;
     if (four) {
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
   } else {
     // V, channel-major; thread (channel c, page ph of the group); token i = 16j + 4gg + r of the page
     const int c = tid & (D - 1), ph = tid >> 7;
-    const long long phys = a.page_table[(long long)b * g.max_pages + 2 * grp + ph];
+    const long long phys = pool_page(g, a.page_table[(long long)b * g.max_pages + 2 * grp + ph]);
     const float* x = xr + ph * 64 * XS_STRIDE + c;
     if (four) {
       // 32-byte rows: token 16j + 4gg + 2hh + n in word 2gg + n, nibble 2j + hh
@@ -526,7 +526,7 @@ __global__ __launch_bounds__(256) void int4_quad_kernel(WriteArgs a) {
   const bool is_new = (t >= T0 && t < T1);
   const void* src = which ? a.v : a.k;
   const float* rot = which ? a.rot_v : a.rot_k;
-  const long long phys = a.page_table[(long long)b * g.max_pages + (quad * 4) / PAGE];
+  const long long phys = pool_page(g, a.page_table[(long long)b * g.max_pages + (quad * 4) / PAGE]);
   uint8_t* head = a.pages + phys * g.page_bytes + (long long)h * I4_HEAD_BYTES;
   if (is_new) {
     const long long row = c0 + (t - T0);
@@ -616,7 +616,7 @@ __global__ __launch_bounds__(256) void int4_page_kernel(WriteArgs a) {
   const int tk = 16 * wave + (lane >> 2), qd = lane & 3;
   const int t = page * PAGE + tk;
   const bool is_new = t >= T0 && t < T1;
-  const long long phys = a.page_table[(long long)b * g.max_pages + page];
+  const long long phys = pool_page(g, a.page_table[(long long)b * g.max_pages + page]);
   uint8_t* head = a.pages + phys * g.page_bytes + (long long)h * I4_HEAD_BYTES;
 
   float y[32];
@@ -776,6 +776,61 @@ __global__ __launch_bounds__(64) void debug_rotate_kernel(const float* rot, int 
 
 }  // namespace
 
+// ---------------------------------------------------------------------------------------------
+// Test hook: the quantized tokens of one (sequence, kv head) read back from the pages in logical order, by
+// the byte layout include/kvq.h states.  One thread per (token, K or V, channel); the threads with channel
+// < 2 of each (token, side) also write that token's scale and zero (per-token schemes), and those of each
+// group's first tokens the group's per-channel scales and zeros.
+// ---------------------------------------------------------------------------------------------
+__global__ void debug_unpack_kernel(WriteArgs a, int seq, int kv_head, int n_tokens, uint8_t* codes_out,
+                                    uint16_t* sz_out) {
+  const Geo& g = a.g;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n_tokens * 2 * D) return;
+  const int u = e / (2 * D), side = (e / D) % 2, c = e % D;  // quantized token u, K (0) or V (1), channel c
+  const int i = u % PAGE;
+  const uint8_t* hb = a.pages + pool_page(g, a.page_table[(long long)seq * g.max_pages + u / PAGE]) * g.page_bytes +
+                      (long long)kv_head * g.head_bytes;
+  const int j = i / 16, gg = (i / 4) % 4, r = i % 4;
+  int code;
+  if (is_int2(g.scheme)) {
+    code = side == 0 ? (hb[I2_K_OFF + 32 * i + c / 4] >> (2 * (c % 4))) & 3
+                     : (hb[I2_V_OFF + 16 * c + 4 * gg + j] >> (2 * r)) & 3;
+  } else if (g.scheme == KVQ_INT4_CHANNEL) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(hb);
+    if (side == 0) {
+      const int m = c / 16, k = (c % 16) / 2, ee = c % 2;
+      code = (w[(I4C_K_OFF + 64 * i) / 4 + 2 * m + ee] >> (4 * k)) & 15;
+    } else {
+      const int hh = (i / 2) % 2, n = i % 2;
+      code = (w[(I4C_V_OFF + 32 * c) / 4 + 2 * gg + n] >> (4 * (2 * j + hh))) & 15;
+    }
+  } else {
+    code = side == 0 ? (hb[I4_K_OFF + 64 * i + c / 2] >> (4 * (c % 2))) & 15
+                     : (hb[I4_V_OFF + 32 * c + 8 * gg + 2 * j + r / 2] >> (4 * (r % 2))) & 15;
+  }
+  codes_out[((long long)u * 2 + side) * D + c] = (uint8_t)code;
+  const uint16_t* m16 = reinterpret_cast<const uint16_t*>(hb);
+  if (g.scheme == KVQ_INT2_CHANNEL || g.scheme == KVQ_INT4_CHANNEL) {
+    // group u / 128: scales and zeros of channel c, side `side` (even page K, odd page V), by its first token
+    if (u % GROUP == 0) {
+      const int grp = u / GROUP;
+      const uint8_t* mp = a.pages + pool_page(g, a.page_table[(long long)seq * g.max_pages + 2 * grp + side]) * g.page_bytes +
+                          (long long)kv_head * g.head_bytes + (g.scheme == KVQ_INT2_CHANNEL ? I2_META_OFF : I4C_META_OFF);
+      const uint16_t* mm = reinterpret_cast<const uint16_t*>(mp);
+      uint16_t* dst = sz_out + (((long long)grp * 2 + side) * 2) * D;
+      dst[c] = mm[c];
+      dst[D + c] = mm[D + c];
+    }
+  } else if (c < 2) {
+    // per token: (scale, zero) of side `side`
+    uint16_t v;
+    if (g.scheme == KVQ_INT2_TOKEN) v = m16[(I2_META_OFF / 2) + 128 * side + 64 * c + i];
+    else v = m16[((side == 0 ? I4_KMETA_OFF : I4_VMETA_OFF) / 2) + 2 * i + c];
+    sz_out[((long long)u * 2 + side) * 2 + c] = v;
+  }
+}
+
 hipError_t launch_write_int2(const WriteArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
@@ -816,6 +871,14 @@ hipError_t launch_write_int4(const WriteArgs& a, hipStream_t s) {
     }
   }
   hipLaunchKernelGGL(advance_kernel, dim3(1), dim3(256), 0, s, a.seq_lens, a.cu_new, a.g.batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_unpack(const WriteArgs& a, int seq, int kv_head, int n_tokens, uint8_t* codes_out,
+                               uint16_t* sz_out, hipStream_t s) {
+  const int n = n_tokens * 2 * D;
+  hipLaunchKernelGGL(debug_unpack_kernel, dim3((n + 255) / 256), dim3(256), 0, s, a, seq, kv_head, n_tokens, codes_out,
+                     sz_out);
   return hipGetLastError();
 }
 

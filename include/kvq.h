@@ -119,8 +119,8 @@ typedef enum { KVQ_ROT_DENSE = 0, KVQ_ROT_HADAMARD = 1 } kvq_rotation;
            4-bit codes (22 and 20 bits, so that every int32 sum over 128 codes stays exact), split into three
            signed byte limbs and multiplied with the 2-bit or 4-bit codes on the int8 matrix cores, 16 x 16 x 64
            products whose rows are (query head, limb) pairs, so the query heads of a kv head share one pass over
-           the codes; every wave walks a chunk of its own (split_tokens = 0: 1 to 32 groups, or 2 to 32 pages,
-           per chunk, chosen by size); INT4_TOKEN walks page pairs, so an explicit split_tokens must be a
+           the codes; every wave walks a chunk of its own (split_tokens = 0: 4 to 32 groups or pages per chunk,
+           chosen by size); INT4_TOKEN walks page pairs, so an explicit split_tokens must be a
            multiple of 128;
    F32   - fp32 FMA on the codes with exact per-group alpha = q~ s and softmax weights: the cross-check of the
            matrix-core decode, built for INT2_CHANNEL and INT4_TOKEN (other schemes: KVQ_EUNSUPPORTED);
@@ -145,7 +145,8 @@ typedef struct {
   float clip_k;          /* rho_K in (0, 1]; 1 = no clip (INT2 only) */
   float clip_v;          /* rho_V in (0, 1] */
   int32_t split_tokens;  /* quantized tokens per decode chunk, each merged from one partial: a multiple of 128
-                            (grouped schemes) or 64 (INT4_TOKEN), or 0 = chosen by size.  On the matrix-core
+                            (grouped schemes) or 64 (INT4_TOKEN), or 0 = chosen by size (matrix-core decode: 4 to
+                            32 groups or pages per chunk).  On the matrix-core
                             decode each wave of a work-group walks a chunk of its own and a work-group takes
                             four; on the fp32 decode the four waves of a work-group share one chunk. */
   int32_t decode_impl;   /* kvq_decode_impl */
@@ -201,6 +202,20 @@ int kvq_compose_oscar_rotation(const double* U_host, double* R_out_host);
 /* [SAW] §3: dense form diag(sign)·H of the randomized Hadamard (for reference/inspection). */
 int kvq_build_hadamard_rotation(const float* sign_host, double* R_out_host);
 
+/* ---- page tables (host) ----
+   The paged cache ([OSCAR] §3.4.5: pages indexed through a page table) maps logical page p of sequence b to
+   physical page table[b * max_pages_per_seq + p] of the pool. */
+/* Fill table_out_host [batch][max_pages_per_seq] with distinct physical pages of a pool of n_pages: seed 0
+   gives sequence b the pages b * max_pages_per_seq + p; any other seed the first batch * max_pages_per_seq
+   entries of a seeded random permutation of the pool (Fisher-Yates, splitmix64 stream from `seed`).  The
+   caller uploads the table.  Errors: KVQ_EINVAL (NULL, batch < 1, max_pages_per_seq < 0, n_pages < 1 or
+   above 2^31 - 1), KVQ_ERANGE (batch * max_pages_per_seq > n_pages). */
+int kvq_build_page_table(int32_t batch, int32_t max_pages_per_seq, int64_t n_pages, uint64_t seed,
+                         int32_t* table_out_host);
+/* Validate a host copy of a page table: KVQ_ERANGE if an entry lies outside [0, n_pages), KVQ_EINVAL if two
+   entries name the same physical page (or for NULL / non-positive sizes), else KVQ_OK. */
+int kvq_check_page_table(const int32_t* table_host, int32_t batch, int32_t max_pages_per_seq, int64_t n_pages);
+
 /* ---- calibration: the rotation from an attention-aware covariance (host, fp64) ----
    [OSCAR] §3.2 offline steps 2-3 and §3.4.2 Factor 1: the key rotation's U is the eigenbasis of the query
    covariance C_Q, the value rotation's U that of the score-weighted value covariance C_S, eigenvectors in
@@ -227,15 +242,19 @@ int kvq_build_oscar_rotation_from_covariance(const double* C_host, double* R_out
    [SAW] §4.1 fused rotate-quantize write).
    k, v: device [total_new][n_kv_heads][128], fp32 or bf16 (`dtype`), sequence b's new tokens at rows
    cu_new[b] .. cu_new[b+1]-1 (cu_new: device int32 [batch+1], non-decreasing, cu_new[0] = 0).
-   max_new_host bounds cu_new[b+1]-cu_new[b] over b (it sizes the launch grids).
+   max_new_host bounds cu_new[b+1]-cu_new[b] over b (it sizes the launch grids); max_len_host bounds every
+   sequence's length after the append (seq_lens[b] + new tokens), host side, as kv_decode_attn's bound.
    Token t of sequence b is t = seq_lens[b] + row offset.  INT2: sink/tail tokens go to the band; every
    128-token group completed by the append is rotated, clipped, quantized and packed (reading band
    tokens and new tokens as needed).  INT4: every new token is rotated and quantized.  Finally
-   seq_lens[b] += new tokens.  Errors: KVQ_EINVAL (NULL, bad dtype, max_new_host < 0),
-   KVQ_EDEVICE.  Lengths beyond the page table are not checked on the device: the caller sizes
-   max_pages_per_seq with kvq_pages_for_len(). */
+   seq_lens[b] += new tokens.  Errors: KVQ_EINVAL (NULL, bad dtype, max_new_host or max_len_host < 0),
+   KVQ_ERANGE (max_len_host needs more pages than max_pages_per_seq: nothing is enqueued), KVQ_EDEVICE.
+   The device side trusts the bounds: a length beyond max_len_host is not written past the page-table row,
+   and a page-table entry outside [0, n_pages) is taken as the pool's last page (kvq_check_page_table finds
+   such entries on the host). */
 int kv_rotate_quant_write(const kvq_config* cfg, kvq_cache* cache, const void* k, const void* v,
-                          int32_t dtype, const int32_t* cu_new, int32_t max_new_host, hipStream_t stream);
+                          int32_t dtype, const int32_t* cu_new, int32_t max_new_host, int32_t max_len_host,
+                          hipStream_t stream);
 
 /* One decode attention step ([OSCAR] §3.4.4 step 4 and §3.4.5; [SAW] App. A.4 eq. (13)-(14)).
    q: device [batch][n_q_heads][128] fp32 or bf16; out: device fp32 [batch][n_q_heads][128].
@@ -249,7 +268,8 @@ int kv_decode_attn(const kvq_config* cfg, const kvq_cache* cache, const void* q,
                    int32_t max_seq_len_host, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* The decode step restricted to some of its three kernels, to time one of them in isolation:
-   `stages` is a bitmask of KVQ_STAGE_QPREP (query rotation), KVQ_STAGE_SPLITK (split-K partials) and
+   `stages` is a bitmask of KVQ_STAGE_QPREP (query rotation), KVQ_STAGE_SPLITK (split-K partials of the
+   quantized chunks and the bf16 band) and
    KVQ_STAGE_MERGE (merge, un-rotate, normalize); a later stage reads what an earlier call left in the
    workspace.  kv_decode_attn() equals stages = KVQ_STAGE_ALL.  Same arguments and errors otherwise. */
 enum { KVQ_STAGE_QPREP = 1, KVQ_STAGE_SPLITK = 2, KVQ_STAGE_MERGE = 4, KVQ_STAGE_ALL = 7 };
@@ -279,6 +299,18 @@ int kv_prefill_attn(const kvq_config* cfg, const kvq_cache* cache, const void* q
    to fp32 [n][128], using the cache's K (which = 0) or V (which = 1) rotation.  Not used by the hot path. */
 int kvq_debug_rotate(const kvq_config* cfg, const kvq_cache* cache, int32_t which, const void* x, int32_t dtype,
                      int32_t n, float rho, float* out, hipStream_t stream);
+
+/* Test hook: the first n_tokens_host quantized tokens of (sequence seq, kv head kv_head) read back from the
+   pages in logical order (quantized token u is position S0 + u for the grouped schemes, position u for INT4
+   per token), by the layout above.  Device outputs:
+     codes_out  uint8 [n_tokens][2][128]: K codes, then V codes of each token;
+     sz_out     bf16 bits, per-channel schemes [n_tokens / 128][2][2][128] (per group: K scales, K zeros,
+                V scales, V zeros), per-token schemes [n_tokens][2][2] (per token: K scale, K zero, V scale,
+                V zero).
+   n_tokens_host must be a multiple of 128 for the grouped schemes.  Errors: KVQ_EINVAL, KVQ_ERANGE (more
+   pages than max_pages_per_seq), KVQ_EDEVICE.  Not used by the hot path. */
+int kvq_debug_unpack(const kvq_config* cfg, const kvq_cache* cache, int32_t seq, int32_t kv_head,
+                     int32_t n_tokens_host, uint8_t* codes_out, uint16_t* sz_out, hipStream_t stream);
 
 const char* kvq_strerror(int status);
 /* Library version string. */

@@ -207,29 +207,6 @@ def sign_vector(wl: Workload, which: str) -> np.ndarray:
     return np.where(r.integers(0, 2, size=HEAD_DIM) == 1, 1, -1).astype(np.int8)
 
 
-def pages_needed(wl: Workload, seq_len: int) -> int:
-    """Upper bound on quantized pages a sequence of this length occupies."""
-    n_int = max(0, seq_len - wl.n_sink)
-    return (n_int + wl.page_tokens - 1) // wl.page_tokens
-
-
-def page_table(wl: Workload, max_pages_per_seq: int, n_pool: Optional[int] = None) -> Tuple[np.ndarray, int]:
-    """[batch, max_pages_per_seq] int32 logical->physical page map and the pool size.
-
-    Identity workloads give sequence b the pages b*max_pages..; the others a
-    seeded random permutation of the whole pool.
-    """
-    n = wl.batch * max_pages_per_seq
-    n_pool = n if n_pool is None else n_pool
-    assert n_pool >= n
-    if wl.identity_pages:
-        perm = np.arange(n, dtype=np.int32)
-    else:
-        r = _rng(wl, "pages")
-        perm = r.permutation(n_pool)[:n].astype(np.int32)
-    return perm.reshape(wl.batch, max_pages_per_seq), n_pool
-
-
 def step_tokens(wl: Workload, step: int, which: str) -> np.ndarray:
     """One appended token per sequence for decode step `step`: [batch, n_kv, 128]."""
     r = _rng(wl, "step", step, 0 if which == "k" else 1)

@@ -76,7 +76,8 @@ def build_cache(K, wl: synth.Workload, lens, append_steps: int = 0, chunk: Optio
     wl = synth.scaled(wl, batch=B)
     cfg = config_for(K, wl, split_tokens, decode_impl)
     max_pages = max(1, max(K.pages_for_len(cfg, int(t)) for t in lens))
-    pt, n_pool = synth.page_table(wl, max_pages, B * max_pages + n_pool_extra)
+    n_pool = B * max_pages + n_pool_extra
+    pt = K.build_page_table(B, max_pages, n_pool, seed=0 if wl.identity_pages else wl.seed)
     rk, rv = rotations(wl)
     cache = K.allocate_cache(cfg, B, torch.from_numpy(pt), torch.from_numpy(rk),
                              None if rv is None else torch.from_numpy(rv), n_pages=n_pool, device=device)
@@ -104,7 +105,7 @@ def build_cache(K, wl: synth.Workload, lens, append_steps: int = 0, chunk: Optio
             cu = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
             k = source_torch(np.concatenate(ks), device)
             v = source_torch(np.concatenate(vs), device)
-            K.kv_rotate_quant_write(cache, k, v, torch.from_numpy(cu).to(device), int(n_new.max()))
+            K.kv_rotate_quant_write(cache, k, v, torch.from_numpy(cu).to(device), int(n_new.max()), max_len=int(lens.max()))
             done += n_new
             del k, v
     # one-token appends
@@ -117,7 +118,8 @@ def build_cache(K, wl: synth.Workload, lens, append_steps: int = 0, chunk: Optio
             continue
         cu = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
         K.kv_rotate_quant_write(cache, source_torch(np.concatenate(ks), device),
-                                source_torch(np.concatenate(vs), device), torch.from_numpy(cu).to(device), 1)
+                                source_torch(np.concatenate(vs), device), torch.from_numpy(cu).to(device), 1,
+                                max_len=int(lens.max()))
     torch.cuda.synchronize()
     return BuiltCache(wl, cfg, cache, lens, rk, rv, max_pages)
 

@@ -45,7 +45,8 @@ def _write_and_check(K, wl, kb, vb, clip=(0.96, 0.92), chunks=None, decode=True,
     cfg = config_for(K, wl, 0, decode_impl)
     rk, rv = rotations(wl)
     max_pages = max(1, K.pages_for_len(cfg, T))
-    pt, n_pool = synth.page_table(wl, max_pages, max_pages + 2)
+    n_pool = max_pages + 2
+    pt = K.build_page_table(1, max_pages, n_pool, seed=0 if wl.identity_pages else wl.seed)
     cache = K.allocate_cache(cfg, 1, torch.from_numpy(pt), torch.from_numpy(rk), torch.from_numpy(rv), n_pages=n_pool)
     done = 0
     for n in (chunks or [T]):
@@ -177,7 +178,8 @@ def _int4_write_and_check(K, wl, k, v, chunks, misalign=False, decode=True):
     cfg = config_for(K, wl)
     rk, rv = rotations(wl)
     max_pages = max(1, K.pages_for_len(cfg, T))
-    pt, n_pool = synth.page_table(wl, max_pages, max_pages + 2)
+    n_pool = max_pages + 2
+    pt = K.build_page_table(1, max_pages, n_pool, seed=0 if wl.identity_pages else wl.seed)
     cache = K.allocate_cache(cfg, 1, torch.from_numpy(pt), torch.from_numpy(rk), torch.from_numpy(rv), n_pages=n_pool)
 
     def dev(x):

@@ -140,7 +140,8 @@ def test_key_only_equals_an_identity_value_rotation(K):
     rk, _ = C.rotations(wl)
     cfg = C.config_for(K, wl)
     mp = max(1, K.pages_for_len(cfg, T))
-    pt, n_pool = synth.page_table(wl, mp, mp + 3)
+    n_pool = mp + 3
+    pt = K.build_page_table(1, mp, n_pool, seed=0 if wl.identity_pages else wl.seed)
     eye = torch.eye(128, dtype=torch.float32)
     cache = K.allocate_cache(cfg, 1, torch.from_numpy(pt), torch.from_numpy(rk), eye, n_pages=n_pool)
     k, v = C.source_of(wl, 0, T)

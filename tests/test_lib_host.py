@@ -98,7 +98,7 @@ def test_calls_reject_null_pointers_before_touching_the_device():
     import ctypes
     cfg = K.make_config(8, 32)
     cache = K.Cache()
-    st = K._lib_write(ctypes.byref(cfg), ctypes.byref(cache), None, None, 0, None, 1, None)
+    st = K._lib_write(ctypes.byref(cfg), ctypes.byref(cache), None, None, 0, None, 1, 1, None)
     assert st == K.KVQ_EINVAL
     st = K._lib_decode(ctypes.byref(cfg), ctypes.byref(cache), None, 0, None, 10, None, 0, None)
     assert st == K.KVQ_EINVAL
@@ -210,3 +210,84 @@ def test_int4_channel_scheme_config():
     for hb in (16, 32, 64):
         assert K.check_config(K.make_config(8, 32, scheme=K.INT4_CHANNEL, rotation=K.ROT_HADAMARD,
                                             hadamard_block=hb)) == K.KVQ_OK
+
+
+# ------------------------------------------------------------------ page tables and the write's length bound
+# ([OSCAR] §3.4.5: the paged cache, logical pages mapped to physical pages of a pool)
+
+
+def test_build_page_table_identity_and_seeded():
+    pt = K.build_page_table(3, 5, 15, seed=0)
+    assert np.array_equal(pt, np.arange(15, dtype=np.int32).reshape(3, 5))
+    a = K.build_page_table(4, 6, 40, seed=1234)
+    b = K.build_page_table(4, 6, 40, seed=1234)
+    c = K.build_page_table(4, 6, 40, seed=1235)
+    assert np.array_equal(a, b) and not np.array_equal(a, c)
+    assert a.shape == (4, 6) and len(set(a.ravel().tolist())) == 24
+    assert a.min() >= 0 and a.max() < 40
+    assert K.check_page_table(a, 40) == K.KVQ_OK
+    # a full pool is a permutation of it
+    full = K.build_page_table(8, 16, 128, seed=7)
+    assert sorted(full.ravel().tolist()) == list(range(128))
+
+
+def test_build_page_table_errors():
+    out = np.empty(16, dtype=np.int32)
+    vp = out.ctypes.data_as(K.ctypes.c_void_p)
+    assert K._lib_build_pt(4, 4, 15, 1, vp) == K.KVQ_ERANGE       # 16 pages asked of a pool of 15
+    assert K._lib_build_pt(0, 4, 16, 1, vp) == K.KVQ_EINVAL
+    assert K._lib_build_pt(4, -1, 16, 1, vp) == K.KVQ_EINVAL
+    assert K._lib_build_pt(4, 4, 0, 1, vp) == K.KVQ_EINVAL
+    assert K._lib_build_pt(4, 4, 16, 1, None) == K.KVQ_EINVAL
+
+
+def test_check_page_table_finds_out_of_pool_and_shared_pages():
+    pt = K.build_page_table(2, 3, 6, seed=3)
+    assert K.check_page_table(pt, 6) == K.KVQ_OK
+    bad = pt.copy()
+    bad[1, 2] = 6
+    assert K.check_page_table(bad, 6) == K.KVQ_ERANGE
+    bad[1, 2] = -1
+    assert K.check_page_table(bad, 6) == K.KVQ_ERANGE
+    dup = pt.copy()
+    dup[1, 0] = dup[0, 0]
+    assert K.check_page_table(dup, 6) == K.KVQ_EINVAL
+
+
+def _fake_cache(cfg, batch, max_pages, n_pages=1 << 20):
+    # non-NULL stand-ins for device pointers: only calls that fail validation, before any device work, use it
+    f = 0x1000
+    return K.Cache(f, n_pages, f, f, max_pages, f, f, f, batch)
+
+
+def test_write_length_bound_is_checked_before_any_launch():
+    f = 0x1000
+    for scheme, kw in ((K.INT2_CHANNEL, {}), (K.INT4_TOKEN, dict(rotation=K.ROT_HADAMARD, n_sink=0, n_recent=0,
+                                                                   clip_k=1.0, clip_v=1.0))):
+        cfg = K.make_config(8, 32, scheme=scheme, **kw)
+        T = 4096
+        mp = K.pages_for_len(cfg, T)
+        cs = _fake_cache(cfg, 2, mp)
+        # one token more than the page-table row holds: KVQ_ERANGE, nothing enqueued
+        T_over = T + (129 if scheme == K.INT2_CHANNEL else 64)
+        assert K.pages_for_len(cfg, T_over) > mp
+        st = K._lib_write(K.ctypes.byref(cfg), K.ctypes.byref(cs), f, f, K.BF16, f, 1, T_over, None)
+        assert st == K.KVQ_ERANGE
+        # negative bounds
+        assert K._lib_write(K.ctypes.byref(cfg), K.ctypes.byref(cs), f, f, K.BF16, f, 1, -1, None) == K.KVQ_EINVAL
+        assert K._lib_write(K.ctypes.byref(cfg), K.ctypes.byref(cs), f, f, K.BF16, f, -1, T, None) == K.KVQ_EINVAL
+        # a pool of no pages is no cache
+        cs0 = _fake_cache(cfg, 2, mp, n_pages=0)
+        assert K._lib_write(K.ctypes.byref(cfg), K.ctypes.byref(cs0), f, f, K.BF16, f, 1, T, None) == K.KVQ_EINVAL
+
+
+def test_debug_unpack_validation():
+    f = 0x1000
+    cfg = K.make_config(8, 32)
+    cs = _fake_cache(cfg, 2, 8)
+    call = lambda seq, h, n: K._lib_debug_unpack(K.ctypes.byref(cfg), K.ctypes.byref(cs), seq, h, n, f, f, None)
+    assert call(2, 0, 128) == K.KVQ_EINVAL    # sequence outside the batch
+    assert call(0, 8, 128) == K.KVQ_EINVAL    # kv head outside the layer
+    assert call(0, 0, 100) == K.KVQ_EINVAL    # not whole groups
+    assert call(0, 0, 128 * 5) == K.KVQ_ERANGE  # 10 pages of a row of 8
+    assert call(0, 0, 0) == K.KVQ_OK          # nothing to read
