@@ -92,6 +92,9 @@ _lib_debug_unpack = _sig("kvq_debug_unpack", ctypes.c_int, _CFG, _CACHE, ctypes.
                          ctypes.c_int32, _P, _P, _P)
 _lib_decode = _sig("kv_decode_attn", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P, ctypes.c_int32, _P,
                    ctypes.c_size_t, _P)
+_lib_decode_noalloc = _sig("kv_decode_attn_noalloc", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P,
+                           ctypes.c_int32, _P)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 _lib_decode_stages = _sig("kv_decode_attn_stages", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P, ctypes.c_int32,
                           _P, ctypes.c_size_t, ctypes.c_int32, _P)
 _lib_debug_rotate = _sig("kvq_debug_rotate", ctypes.c_int, _CFG, _CACHE, ctypes.c_int32, _P, ctypes.c_int32,
@@ -105,7 +108,7 @@ EXPORTED = [
     "kvq_bits_per_element", "kvq_check_config", "kvq_build_oscar_rotation", "kvq_compose_oscar_rotation",
     "kvq_build_hadamard_rotation", "kvq_query_covariance", "kvq_score_value_covariance", "kvq_eigenbasis",
     "kvq_build_oscar_rotation_from_covariance", "kvq_prefill_workspace_bytes", "kv_prefill_attn",
-    "kv_rotate_quant_write", "kv_decode_attn", "kv_decode_attn_stages",
+    "kv_rotate_quant_write", "kv_decode_attn", "kv_decode_attn_stages", "kv_decode_attn_noalloc",
     "kvq_debug_rotate", "kvq_debug_unpack", "kvq_build_page_table", "kvq_check_page_table",
     "kvq_strerror", "kvq_version", "kvq_last_error",
 ]
@@ -332,6 +335,15 @@ def kv_decode_attn(cache: DeviceCache, q, out, max_seq_len: int, workspace, stre
     _check(_lib_decode(ctypes.byref(cache.cfg), ctypes.byref(cs), _ptr(q), _dtype_code(q), _ptr(out),
                        int(max_seq_len), _ptr(workspace), workspace.numel() * workspace.element_size(),
                        _stream(stream)), "kv_decode_attn")
+
+
+def kv_decode_attn_noalloc(cache: DeviceCache, q, out, max_seq_len: int, stream=None) -> None:
+    """kv_decode_attn with the library's own per-GPU scratch as workspace (no allocation)."""
+    assert q.is_contiguous() and out.is_contiguous()
+    assert q.shape == (cache.batch, cache.cfg.n_q_heads, 128) and out.shape == q.shape
+    cs = cache.c_struct()
+    _check(_lib_decode_noalloc(ctypes.byref(cache.cfg), ctypes.byref(cs), _ptr(q), _dtype_code(q), _ptr(out),
+                               int(max_seq_len), _stream(stream)), "kv_decode_attn_noalloc")
 
 
 def kv_decode_attn_stages(cache: DeviceCache, q, out, max_seq_len: int, workspace, stages: int, stream=None) -> None:

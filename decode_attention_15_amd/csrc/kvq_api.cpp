@@ -5,11 +5,18 @@
 
 #include <stdint.h>
 
+#include <mutex>
 #include <vector>
 
 #include "kvq_internal.h"
 
 using namespace kvq;
+
+// Workspace of kv_decode_attn_noalloc: a file-scope device array, one per GPU the library runs on, held until
+// the process ends.  Host code never passes `scratch` itself to a kernel (on the host it names a stand-in,
+// not device memory): the device address comes from hipGetSymbolAddress, once per device, with that device
+// current.
+static __device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -206,6 +213,28 @@ void compose_u_h_pbr(const double* U, double* R) {
 
 thread_local char g_last_error[256] = "";
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on the first call on that device).
+hipError_t scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 // Status of a launch sequence; a failure records the HIP error name for kvq_last_error().
 int to_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return KVQ_OK;
@@ -374,6 +403,29 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
   a.impl = mfma ? KVQ_DECODE_MFMA : KVQ_DECODE_F32;
   clear_stale_error();
   return to_status(launch_decode(a, stages, stream), "kv_decode_attn");
+}
+
+int kv_decode_attn_noalloc(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t dtype, float* out,
+                           int32_t max_seq_len_host, hipStream_t stream) {
+  // every check that needs no device comes first, so that a call that cannot run touches nothing
+  int st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if ((st = check_cache(cfg, cache)) != KVQ_OK) return st;
+  if (!q || !out || max_seq_len_host < 0 || (dtype != KVQ_F32 && dtype != KVQ_BF16)) return KVQ_EINVAL;
+  if (kvq_pages_for_len(cfg, max_seq_len_host) > cache->max_pages_per_seq) return KVQ_ERANGE;
+  const size_t need = kvq_decode_workspace_bytes(cfg, cache->batch, max_seq_len_host);
+  if (need > (size_t)KVQ_NOALLOC_SCRATCH_BYTES) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "kv_decode_attn_noalloc: the decode needs %zu bytes of workspace, the scratch holds %zu",
+             need, (size_t)KVQ_NOALLOC_SCRATCH_BYTES);
+    return KVQ_ENOSPACE;
+  }
+  void* ws = nullptr;
+  clear_stale_error();
+  hipError_t e = scratch_of_current_device(&ws);
+  if (e != hipSuccess) return to_status(e, "kv_decode_attn_noalloc (scratch address)");
+  return kv_decode_attn_stages(cfg, cache, q, dtype, out, max_seq_len_host, ws, (size_t)KVQ_NOALLOC_SCRATCH_BYTES,
+                               KVQ_STAGE_ALL, stream);
 }
 
 size_t kvq_prefill_workspace_bytes(const kvq_config* cfg, int32_t total_q) {

@@ -277,6 +277,19 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
                           int32_t max_seq_len_host, void* workspace, size_t ws_bytes, int32_t stages,
                           hipStream_t stream);
 
+/* kv_decode_attn without a workspace argument, for callers that cannot allocate device memory (code under
+   HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): it calls no hipMalloc, hipFree or
+   allocating routine.  Its workspace is a file-scope device array of KVQ_NOALLOC_SCRATCH_BYTES (64 MiB) that
+   every GPU the library runs on holds until the process ends; its address on the current device is looked up
+   once per device.  Every call on a GPU shares that GPU's array, so calls that overlap on one GPU (other
+   streams or threads) race: the caller orders them.  Nothing in it needs clearing between calls: every
+   partial the merge reads is written by the same call.  Same arguments and results as kv_decode_attn;
+   KVQ_ENOSPACE (checked on the host, nothing enqueued, kvq_last_error() gives the sizes) when
+   kvq_decode_workspace_bytes(cfg, batch, max_seq_len_host) exceeds KVQ_NOALLOC_SCRATCH_BYTES. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+int kv_decode_attn_noalloc(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t dtype, float* out,
+                           int32_t max_seq_len_host, hipStream_t stream);
+
 /* Prefill attention over the quantized history ([NOVA] §3 "Long context": chunked prefill, every chunk
    quantized on write so later chunks attend to a quantized history; [SAW] prefill stage: save, read back,
    attend).  Call after kv_rotate_quant_write has appended the chunk: sequence b's chunk is its last

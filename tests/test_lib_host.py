@@ -291,3 +291,24 @@ def test_debug_unpack_validation():
     assert call(0, 0, 100) == K.KVQ_EINVAL    # not whole groups
     assert call(0, 0, 128 * 5) == K.KVQ_ERANGE  # 10 pages of a row of 8
     assert call(0, 0, 0) == K.KVQ_OK          # nothing to read
+
+
+def test_noalloc_decode_refuses_what_the_scratch_cannot_hold():
+    """kv_decode_attn_noalloc: argument errors and a workspace beyond its fixed scratch are refused on the
+    host, before anything touches the device (the pointers here are never dereferenced)."""
+    f = 0x1000
+    cfg = K.make_config(8, 32, split_tokens=512)
+    T = 32768
+    mp = K.pages_for_len(cfg, T)
+    # batch 32 at 32k tokens and the smallest split fits; batch 64 does not
+    assert K.decode_workspace_bytes(cfg, 32, T) <= K.NOALLOC_SCRATCH_BYTES
+    assert K.decode_workspace_bytes(cfg, 64, T) > K.NOALLOC_SCRATCH_BYTES
+    cs = _fake_cache(cfg, 64, mp)
+    st = K._lib_decode_noalloc(K.ctypes.byref(cfg), K.ctypes.byref(cs), f, K.F32, f, T, None)
+    assert st == K.KVQ_ENOSPACE
+    assert "scratch" in K.last_error()
+    # beyond the page table, null pointers, a bad dtype
+    assert K._lib_decode_noalloc(K.ctypes.byref(cfg), K.ctypes.byref(cs), f, K.F32, f, T + 129, None) == K.KVQ_ERANGE
+    assert K._lib_decode_noalloc(K.ctypes.byref(cfg), K.ctypes.byref(cs), None, K.F32, f, T, None) == K.KVQ_EINVAL
+    assert K._lib_decode_noalloc(K.ctypes.byref(cfg), K.ctypes.byref(cs), f, 7, f, T, None) == K.KVQ_EINVAL
+    assert K._lib_decode_noalloc(K.ctypes.byref(cfg), K.ctypes.byref(cs), f, K.F32, f, -1, None) == K.KVQ_EINVAL
