@@ -92,6 +92,14 @@ _lib_debug_unpack = _sig("kvq_debug_unpack", ctypes.c_int, _CFG, _CACHE, ctypes.
                          ctypes.c_int32, _P, _P, _P)
 _lib_decode = _sig("kv_decode_attn", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P, ctypes.c_int32, _P,
                    ctypes.c_size_t, _P)
+class DecodeShape(ctypes.Structure):
+    _fields_ = [("chunk_units", ctypes.c_int32), ("n_chunks", ctypes.c_int32), ("span", ctypes.c_int32),
+                ("splitk_workgroups", ctypes.c_int32), ("band_first", ctypes.c_int32),
+                ("matrix_cores", ctypes.c_int32)]
+
+
+_lib_decode_shape = _sig("kvq_decode_shape_of", ctypes.c_int, _CFG, ctypes.c_int32, ctypes.c_int32,
+                         ctypes.POINTER(DecodeShape))
 _lib_decode_noalloc = _sig("kv_decode_attn_noalloc", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P,
                            ctypes.c_int32, _P)
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -109,6 +117,7 @@ EXPORTED = [
     "kvq_build_hadamard_rotation", "kvq_query_covariance", "kvq_score_value_covariance", "kvq_eigenbasis",
     "kvq_build_oscar_rotation_from_covariance", "kvq_prefill_workspace_bytes", "kv_prefill_attn",
     "kv_rotate_quant_write", "kv_decode_attn", "kv_decode_attn_stages", "kv_decode_attn_noalloc",
+    "kvq_decode_shape_of",
     "kvq_debug_rotate", "kvq_debug_unpack", "kvq_build_page_table", "kvq_check_page_table",
     "kvq_strerror", "kvq_version", "kvq_last_error",
 ]
@@ -335,6 +344,13 @@ def kv_decode_attn(cache: DeviceCache, q, out, max_seq_len: int, workspace, stre
     _check(_lib_decode(ctypes.byref(cache.cfg), ctypes.byref(cs), _ptr(q), _dtype_code(q), _ptr(out),
                        int(max_seq_len), _ptr(workspace), workspace.numel() * workspace.element_size(),
                        _stream(stream)), "kv_decode_attn")
+
+
+def decode_shape(cfg: Config, batch: int, max_seq_len: int) -> dict:
+    """How kv_decode_attn splits a batch of sequences up to max_seq_len tokens (host only)."""
+    sh = DecodeShape()
+    _check(_lib_decode_shape(ctypes.byref(cfg), int(batch), int(max_seq_len), ctypes.byref(sh)), "decode_shape")
+    return {name: int(getattr(sh, name)) for name, _ in DecodeShape._fields_}
 
 
 def kv_decode_attn_noalloc(cache: DeviceCache, q, out, max_seq_len: int, stream=None) -> None:

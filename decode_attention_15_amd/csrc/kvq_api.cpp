@@ -78,6 +78,14 @@ bool uses_mfma(const kvq_config* c) {
 }
 
 // decode work split: groups (INT2) or pages (INT4) per chunk
+// Split-K work-groups one CU holds at once: the kernel's LDS (160 KB per CU) decides.  Matrix-core decode,
+// 2-bit codes: 3 up to GQA 4, 2 at GQA 8; 4-bit codes: 2 up to GQA 4, 1 at GQA 8.  fp32 decode: 4.
+int wgs_per_cu(const kvq_config* c) {
+  if (!uses_mfma(c)) return 4;
+  const bool four = c->scheme == KVQ_INT4_CHANNEL || c->scheme == KVQ_INT4_TOKEN;
+  return gq_of(c) <= 4 ? (four ? 2 : 3) : (four ? 1 : 2);
+}
+
 int chunk_units(const kvq_config* c, int batch, int max_seq_len) {
   if (c->split_tokens > 0) return c->split_tokens / (is_grouped(c->scheme) ? GROUP : PAGE);
   int units;  // quantized groups/pages per sequence
@@ -86,14 +94,10 @@ int chunk_units(const kvq_config* c, int batch, int max_seq_len) {
   const int pairs = batch * c->n_kv_heads;
   if (uses_mfma(c)) {
     // one chunk per wave, sized so that the chunk work-groups and the band work-groups (the grouped schemes'
-    // band units; INT4 per token's are empty and finish at once) fill the GPU's work-group slots in one round:
-    // the kernel's work-groups per CU follow its LDS (2-bit codes: 3 up to GQA 4, 2 at GQA 8; 4-bit codes: 2
-    // up to GQA 4, 1 at GQA 8) on the 256 CUs of an MI355X.  At least 4 groups (pages) per chunk, so that a
-    // wave's copies stay in flight across several of them (measured: batch 1 x 32k, 4-group chunks beat
-    // 1-group ones), and at most 32.
-    const bool four = c->scheme == KVQ_INT4_CHANNEL || c->scheme == KVQ_INT4_TOKEN;
-    const int per_cu = gq_of(c) <= 4 ? (four ? 2 : 3) : (four ? 1 : 2);
-    long long chunk_wgs = 256LL * per_cu - (is_grouped(c->scheme) ? pairs : 0);
+    // band units; INT4 per token's are empty and finish at once) fill the work-group slots of the 256 CUs of
+    // an MI355X in one round.  At least 4 groups (pages) per chunk, so that a wave's copies stay in flight
+    // across several of them (measured: batch 1 x 32k, 4-group chunks beat 1-group ones), and at most 32.
+    long long chunk_wgs = 256LL * wgs_per_cu(c) - (is_grouped(c->scheme) ? pairs : 0);
     if (chunk_wgs < 256) chunk_wgs = 256;
     const long long total = (long long)pairs * units;
     long long per = (total + 4 * chunk_wgs - 1) / (4 * chunk_wgs);
@@ -113,11 +117,45 @@ int chunk_units(const kvq_config* c, int batch, int max_seq_len) {
   return per;
 }
 
+// Chunks one wave of the matrix-core decode walks.  Automatic chunks are already sized to fill the GPU in one
+// round (one chunk per wave).  An explicit split fixes the chunks the merge combines, which can be many more
+// than the waves of one round: a wave then walks consecutive chunks, its copies running on across their
+// boundaries, with as many chunks per walk as fill the work-group slots of one round, and at most 32
+// groups (pages) per walk.
+int walk_span(const kvq_config* c, int batch, int n_chunks, int per) {
+  if (c->split_tokens <= 0 || n_chunks <= 1) return 1;
+  const long long pairs = (long long)batch * c->n_kv_heads;
+  long long slots = 256LL * wgs_per_cu(c) - (is_grouped(c->scheme) ? pairs : 0);  // chunk work-groups per round
+  if (slots < 256) slots = 256;
+  // walks one work-group takes, and the rows of work-groups (head quads: one row per (sequence, quad))
+  const bool quads = c->n_kv_heads % 4 == 0;
+  const long long rows = quads ? pairs / 4 : pairs, walks_per_wg = quads ? 1 : 4;
+  long long per_row = slots / rows;  // work-groups per row
+  if (per_row < 1) per_row = 1;
+  long long span = (n_chunks + per_row * walks_per_wg - 1) / (per_row * walks_per_wg);
+  const long long cap = 32 / per > 1 ? 32 / per : 1;
+  if (span > cap) span = cap;
+  return (int)(span < 1 ? 1 : span);
+}
+
 int max_chunks_of(const kvq_config* c, int max_seq_len, int per) {
   int units;
   if (is_grouped(c->scheme)) units = n_groups_of(max_seq_len, c->n_sink, c->n_recent);
   else units = (max_seq_len + PAGE - 1) / PAGE;
   return (units + per - 1) / per;
+}
+
+// The decode's chunking and split-K grid for lengths up to max_seq_len (g holds the cache's geometry).
+void set_decode_shape(const kvq_config* c, int max_seq_len, Geo& g) {
+  const int per = chunk_units(c, g.batch, max_seq_len);
+  g.gpc = per;
+  g.n_units = 1 + max_chunks_of(c, max_seq_len, per);
+  // the matrix-core decode: every wave walks `span` chunks of its own; the fp32 decode: one chunk per work-group
+  const bool mfma = uses_mfma(c);
+  g.wave_chunks = mfma ? 1 : 0;
+  g.span = mfma ? walk_span(c, g.batch, g.n_units - 1, per) : 1;
+  // band work-groups first when the split-K launch takes more than one round of work-groups (see the grid)
+  g.band_first = splitk_wgs(g) > 256LL * wgs_per_cu(c) ? 1 : 0;
 }
 
 Geo make_geo(const kvq_config* c, const kvq_cache* k) {
@@ -212,6 +250,7 @@ void compose_u_h_pbr(const double* U, double* R) {
 }
 
 thread_local char g_last_error[256] = "";
+
 
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
@@ -372,20 +411,8 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
   DecodeArgs a;
   memset(&a, 0, sizeof(a));
   a.g = make_geo(cfg, cache);
-  const int per = chunk_units(cfg, cache->batch, max_seq_len_host);
-  a.g.gpc = per;
-  a.g.n_units = 1 + max_chunks_of(cfg, max_seq_len_host, per);
-  // the matrix-core decode walks one chunk per wave (four per work-group); the fp32 decode one per work-group
+  set_decode_shape(cfg, max_seq_len_host, a.g);
   const bool mfma = uses_mfma(cfg);
-  a.g.wave_chunks = mfma ? 1 : 0;
-  {
-    // band work-groups first when the split-K launch takes more than one round of work-groups (see the grid)
-    const bool four = cfg->scheme == KVQ_INT4_CHANNEL || cfg->scheme == KVQ_INT4_TOKEN;
-    const int per_cu = !mfma ? 4 : gq_of(cfg) <= 4 ? (four ? 2 : 3) : (four ? 1 : 2);
-    const long long nc = a.g.n_units - 1, pairs = (long long)cache->batch * cfg->n_kv_heads;
-    const long long chunk_wgs = !mfma ? pairs * nc : cfg->n_kv_heads % 4 == 0 ? pairs / 4 * nc : pairs * ((nc + 3) / 4);
-    a.g.band_first = chunk_wgs + pairs > 256LL * per_cu ? 1 : 0;
-  }
   a.pages = static_cast<const uint8_t*>(cache->pages);
   a.band = static_cast<const uint16_t*>(cache->band);
   a.page_table = cache->page_table;
@@ -403,6 +430,24 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
   a.impl = mfma ? KVQ_DECODE_MFMA : KVQ_DECODE_F32;
   clear_stale_error();
   return to_status(launch_decode(a, stages, stream), "kv_decode_attn");
+}
+
+int kvq_decode_shape_of(const kvq_config* cfg, int32_t batch, int32_t max_seq_len, kvq_decode_shape* out) {
+  int st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!out || batch < 1 || max_seq_len < 0) return KVQ_EINVAL;
+  kvq_cache k;
+  memset(&k, 0, sizeof(k));
+  k.batch = batch;
+  Geo g = make_geo(cfg, &k);
+  set_decode_shape(cfg, max_seq_len, g);
+  out->chunk_units = g.gpc;
+  out->n_chunks = g.n_units - 1;
+  out->span = g.span;
+  out->splitk_workgroups = splitk_wgs(g);
+  out->band_first = g.band_first;
+  out->matrix_cores = g.wave_chunks;
+  return KVQ_OK;
 }
 
 int kv_decode_attn_noalloc(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t dtype, float* out,

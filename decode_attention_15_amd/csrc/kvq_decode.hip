@@ -764,12 +764,12 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ng = n_groups_of(T, g.S0, g.W);
-  const int chunk_id = chunk;  // one chunk per wave
-  const int g_begin = chunk_id * g.gpc;
-  int g_end = (g_begin + g.gpc) < ng ? (g_begin + g.gpc) : ng;
-  if (g_end > g.max_pages / 2) g_end = g.max_pages / 2;  // never index past the page-table row
-  constexpr int gstep = 1;
-  const int g_first = g_begin;
+  // this wave walks chunks chunk .. chunk + span - 1 (groups g_first .. g_end - 1), storing a partial per chunk
+  const int g_first = chunk * g.gpc;
+  int g_end = g_first + g.span * g.gpc;
+  if (g_end > ng) g_end = ng;
+  if (g_end > g.max_pages / 2) g_end = g.max_pages / 2;            // never index past the page-table row
+  if (g_end > (g.n_units - 1) * g.gpc) g_end = (g.n_units - 1) * g.gpc;  // chunks past the launch bound: none
   MfmaWave<GQ, KU>& W = L.mf.w[wave];
   const int q4 = lane >> 4, c = lane & 15;
 
@@ -887,12 +887,35 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     issue_m(p0, 0);
     issue_k(p0);
     issue_v(p0);
-    if (g_first + gstep < g_end) pv = pair_v(g_first + gstep);
+    if (g_first + 1 < g_end) pv = pair_v(g_first + 1);
   }
+  // the partial of chunk ci (per channel, o and l carry the weights' factor S), then a fresh softmax state;
+  // every partial a merge reads is written, chunks past the length have none
+  auto store_partial = [&](int ci) {
+#pragma unroll
+    for (int e = 0; e < HPL; ++e) {
+      const int he = q4 * HPL + e;
+      const float f = TOK ? 1.0f : 1.0f / S;
+      if (he < GQ) {
+        float* part = a.partials + (((long long)b * g.n_q + h * GQ + he) * g.n_units + 1 + ci) * PART_STRIDE;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) part[2 + c + 16 * t] = o[e][t] * f;
+        if (c == 0) {
+          part[0] = m[e];
+          part[1] = l[e] * f;
+        }
+      }
+      m[e] = -INFINITY;
+      l[e] = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) o[e][t] = 0.0f;
+    }
+  };
   const mf_i32x4 zero4 = {0, 0, 0, 0};
   const mf_i32x4 ones4 = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
-  for (int gi = g_first; gi < g_end; gi += gstep) {
-    const bool has_next = gi + gstep < g_end;  // uniform
+  int left = g.gpc;  // groups left in the current chunk
+  for (int gi = g_first; gi < g_end; ++gi) {
+    const bool has_next = gi + 1 < g_end;  // uniform
     KVQ_WAIT_VM(0);  // this group's metadata, key and value codes, and the next group's pages
     wave_lds_sync();
     // 0. the group's codes to registers (key tiles: 2-bit .x, .y; 4-bit all four words; value tiles: 2-bit
@@ -926,7 +949,7 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
       issue_m(pn, mb ^ 1);
       issue_k(pn);
       issue_v(pn);
-      if (gi + 2 * gstep < g_end) pv = pair_v(gi + 2 * gstep);
+      if (gi + 2 < g_end) pv = pair_v(gi + 2);
     }
     const uint16_t* ms = reinterpret_cast<const uint16_t*>(W.mst[mb]);
     // 1. per channel: key-side operand alpha = q~ s of head ah at positions Q0 + i, three limbs;
@@ -1128,29 +1151,9 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
       m[e] = mnew;
     }
     mb ^= 1;
-  }
-  if constexpr (!TOK) {
-#pragma unroll
-    for (int e = 0; e < HPL; ++e) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) o[e][t] *= 1.0f / S;
-      l[e] *= 1.0f / S;
-    }
-  }
-  // every partial a merge reads is written; chunks past the length or the launch bound have none
-  if (g_begin < ng && chunk_id < g.n_units - 1) {
-#pragma unroll
-    for (int e = 0; e < HPL; ++e) {
-      const int he = q4 * HPL + e;
-      if (he < GQ) {
-        float* part = a.partials + (((long long)b * g.n_q + h * GQ + he) * g.n_units + 1 + chunk_id) * PART_STRIDE;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) part[2 + c + 16 * t] = o[e][t];
-        if (c == 0) {
-          part[0] = m[e];
-          part[1] = l[e];
-        }
-      }
+    if (--left == 0 || !has_next) {  // uniform: the end of a chunk
+      store_partial(gi / g.gpc);
+      left = g.gpc;
     }
   }
 }
@@ -1192,10 +1195,14 @@ __device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int npages = (T + PAGE - 1) / PAGE;
   const int npairs = (npages + 1) / 2;
-  const int chunk_id = chunk;  // one chunk (an even number of pages) per wave
-  const int pb = chunk_id * (g.gpc / 2);
-  int pe = pb + g.gpc / 2 < npairs ? pb + g.gpc / 2 : npairs;
-  if (2 * pe > g.max_pages + 1) pe = (g.max_pages + 1) / 2;  // never index past the page-table row
+  // this wave walks chunks chunk .. chunk + span - 1 (an even number of pages each: page pairs pb .. pe - 1),
+  // storing a partial per chunk
+  const int ppc = g.gpc / 2;  // page pairs per chunk
+  const int pb = chunk * ppc;
+  int pe = pb + g.span * ppc;
+  if (pe > npairs) pe = npairs;
+  if (2 * pe > g.max_pages + 1) pe = (g.max_pages + 1) / 2;          // never index past the page-table row
+  if (pe > (g.n_units - 1) * ppc) pe = (g.n_units - 1) * ppc;  // chunks past the launch bound: none
   MfmaWave<GQ, 512>& W = L.mf.w[wave];
   const int q4 = lane >> 4, c = lane & 15;
 
@@ -1302,7 +1309,29 @@ __device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int
     issue_v(p0);
     if (pb + 1 < pe) pv = pages_v(pb + 1);
   }
+  // the partial of chunk ci, then a fresh softmax state; every partial a merge reads is written, chunks past
+  // the length have none
+  auto store_partial = [&](int ci) {
+#pragma unroll
+    for (int e = 0; e < HPL; ++e) {
+      const int he = q4 * HPL + e;
+      if (he < GQ) {
+        float* part = a.partials + (((long long)b * g.n_q + h * GQ + he) * g.n_units + 1 + ci) * PART_STRIDE;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) part[2 + c + 16 * t] = o[e][t];
+        if (c == 0) {
+          part[0] = m[e];
+          part[1] = l[e];
+        }
+      }
+      m[e] = -INFINITY;
+      l[e] = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) o[e][t] = 0.0f;
+    }
+  };
   const mf_i32x4 zero4 = {0, 0, 0, 0};
+  int left = ppc;  // page pairs left in the current chunk
   for (int pi = pb; pi < pe; ++pi) {
     const bool has_next = pi + 1 < pe;  // uniform
     KVQ_WAIT_VM(0);  // this pair's metadata, key and value codes, and the next pair's pages
@@ -1421,21 +1450,9 @@ __device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int
       m[e] = mnew;
     }
     mb ^= 1;
-  }
-  // every partial a merge reads is written; chunks past the length or the launch bound have none
-  if (pb < npairs && chunk_id < g.n_units - 1) {
-#pragma unroll
-    for (int e = 0; e < HPL; ++e) {
-      const int he = q4 * HPL + e;
-      if (he < GQ) {
-        float* part = a.partials + (((long long)b * g.n_q + h * GQ + he) * g.n_units + 1 + chunk_id) * PART_STRIDE;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) part[2 + c + 16 * t] = o[e][t];
-        if (c == 0) {
-          part[0] = m[e];
-          part[1] = l[e];
-        }
-      }
+    if (--left == 0 || !has_next) {  // uniform: the end of a chunk
+      store_partial(pi / ppc);
+      left = ppc;
     }
   }
 }
@@ -1446,21 +1463,8 @@ __device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int
 // (sequence-major, a chunk position would stay on one XCD, and the last chunks, which short sequences lack,
 // would leave theirs idle).  When the launch fits the GPU in one round of work-groups the band work-groups
 // come last (measured faster at batch 32 x 32k); when it takes several rounds they come first, so that they
-// overlap the chunk walks instead of trailing them (4 x 131k at 512-token chunks: 108 -> 86 us).
-// Chunk work-groups:
-//  - matrix-core decode, n_kv a multiple of 4 (head quads): one chunk of four kv heads of a sequence, wave w
-//    taking head 4 hq + w, so that the work-group's copies of a page read four neighbouring head blocks
-//    together;
-//  - matrix-core decode otherwise: four consecutive chunks of one (sequence, kv head), one per wave;
-//  - fp32 decode: one chunk of one (sequence, kv head), shared by the four waves.
-__host__ __device__ inline bool splitk_head_quads(const Geo& g) { return g.wave_chunks && g.n_kv % 4 == 0; }
-__host__ __device__ inline int splitk_chunk_wgs(const Geo& g) {
-  const int nc = g.n_units - 1;
-  if (!g.wave_chunks) return g.batch * g.n_kv * nc;
-  if (splitk_head_quads(g)) return g.batch * (g.n_kv / 4) * nc;
-  return g.batch * g.n_kv * ((nc + 3) / 4);
-}
-__host__ __device__ inline int splitk_wgs(const Geo& g) { return splitk_chunk_wgs(g) + g.batch * g.n_kv; }
+// overlap the chunk walks instead of trailing them.  What a chunk work-group walks: splitk_chunk_wgs.
+//
 // Work-group i of the split-K grid: true for a band work-group (idx = its (sequence, kv head) pair), false
 // for a chunk work-group (idx = its index among the chunk work-groups).
 __device__ inline bool splitk_is_band(const Geo& g, int i, int& idx) {
@@ -1482,22 +1486,22 @@ __device__ inline void splitk_unit_of(const Geo& g, int& unit, int& h, int& b) {
   h = pair % g.n_kv;
   b = pair / g.n_kv;
 }
-// matrix-core decode, chunk work-group i: its sequence, and this wave's kv head and chunk; returns the
-// work-group's first chunk (every wave's chunk at least that)
+// matrix-core decode, chunk work-group i: its sequence, and this wave's kv head and first chunk (it walks
+// chunks chunk .. chunk + span - 1); returns the work-group's first chunk (every wave's at least that)
 __device__ inline int wave_chunk_of(const Geo& g, int i, int wave, int& b, int& h, int& chunk) {
   if (splitk_head_quads(g)) {
     const int quads = g.n_kv / 4, per = g.batch * quads;
     const int r = i % per;
     b = r / quads;
     h = 4 * (r % quads) + wave;
-    chunk = i / per;
+    chunk = g.span * (i / per);
     return chunk;
   }
   const int pairs = g.batch * g.n_kv, pair = i % pairs;
   b = pair / g.n_kv;
   h = pair % g.n_kv;
-  chunk = 4 * (i / pairs) + wave;
-  return 4 * (i / pairs);
+  chunk = g.span * (4 * (i / pairs) + wave);
+  return g.span * 4 * (i / pairs);
 }
 
 // Matrix-core launch of the grouped schemes.  Work-groups per CU, as the LDS allows (160 KB): 2-bit codes

@@ -53,7 +53,8 @@ struct Geo {
   long long page_bytes;
   int gpc;          // groups (grouped schemes) or pages (INT4 per token) per decode chunk
   int n_units;      // decode partial units per (seq, q head): 1 band unit + chunks
-  int wave_chunks;  // 1: each wave of a work-group walks a chunk of its own and stores its partial
+  int wave_chunks;  // 1: each wave of a work-group walks chunks of its own and stores their partials
+  int span;         // matrix-core decode: consecutive chunks one wave walks (a partial stored per chunk)
   int band_first;   // 1: the split-K grid starts with its band work-groups (launches of more than one round)
 };
 
@@ -65,6 +66,22 @@ __host__ __device__ inline int n_groups_of(int T, int S0, int W) {
   int r = T - S0 - W;
   return r > 0 ? r / GROUP : 0;
 }
+
+// Chunk work-groups of the split-K grid (the band work-groups, one per (sequence, kv head), come on top):
+//  - matrix-core decode, n_kv a multiple of 4 (head quads): each walks `span` chunks of four kv heads of a
+//    sequence, wave w taking head 4 hq + w, so that the work-group's copies of a page read four neighbouring
+//    head blocks together;
+//  - matrix-core decode otherwise: four consecutive walks of `span` chunks of one (sequence, kv head), one
+//    per wave;
+//  - fp32 decode: one chunk of one (sequence, kv head), shared by the four waves.
+__host__ __device__ inline bool splitk_head_quads(const Geo& g) { return g.wave_chunks && g.n_kv % 4 == 0; }
+__host__ __device__ inline int splitk_chunk_wgs(const Geo& g) {
+  const int nc = g.n_units - 1;
+  if (!g.wave_chunks) return g.batch * g.n_kv * nc;
+  if (splitk_head_quads(g)) return g.batch * (g.n_kv / 4) * ((nc + g.span - 1) / g.span);
+  return g.batch * g.n_kv * ((nc + 4 * g.span - 1) / (4 * g.span));
+}
+__host__ __device__ inline int splitk_wgs(const Geo& g) { return splitk_chunk_wgs(g) + g.batch * g.n_kv; }
 
 __host__ __device__ inline int band_slot_of(int t, int S0, int W) {
   return t < S0 ? t : S0 + (t - S0) % (W + GROUP);

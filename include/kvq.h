@@ -277,6 +277,22 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
                           int32_t max_seq_len_host, void* workspace, size_t ws_bytes, int32_t stages,
                           hipStream_t stream);
 
+/* How kv_decode_attn splits its work for a batch of sequences up to max_seq_len tokens (host only; no device
+   work): the quantized history of a sequence is cut into chunks of chunk_units groups of 128 tokens (grouped
+   schemes) or pages of 64 tokens (INT4 per token), each chunk giving one softmax partial (m, l, o) that the
+   merge combines ([OSCAR] §3.4.5 step 4, FlashDecoding; [NOVA] App. B.5, two-stage split-KV).  An explicit
+   split_tokens fixes the chunks; 0 lets the library size them to the GPU.  On the matrix cores one wave walks
+   `span` consecutive chunks.  Errors: KVQ_EINVAL (null out, batch < 1, negative length), config errors. */
+typedef struct kvq_decode_shape {
+  int32_t chunk_units;        /* groups (grouped schemes) or pages (INT4 per token) per chunk */
+  int32_t n_chunks;           /* chunks of a sequence of max_seq_len tokens */
+  int32_t span;               /* chunks one wave walks in a row (1 on the fp32 decode) */
+  int32_t splitk_workgroups;  /* work-groups of the split-K launch, band work-groups included */
+  int32_t band_first;         /* 1: the launch starts with its band work-groups */
+  int32_t matrix_cores;       /* 1: the matrix-core decode runs, 0: the fp32 decode */
+} kvq_decode_shape;
+int kvq_decode_shape_of(const kvq_config* cfg, int32_t batch, int32_t max_seq_len, kvq_decode_shape* out);
+
 /* kv_decode_attn without a workspace argument, for callers that cannot allocate device memory (code under
    HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): it calls no hipMalloc, hipFree or
    allocating routine.  Its workspace is a file-scope device array of KVQ_NOALLOC_SCRATCH_BYTES (64 MiB) that

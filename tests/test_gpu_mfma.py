@@ -4,8 +4,8 @@ oracle on the same seeded caches (bar 2e-3), and against the fp32 decode of the 
 
 Cases span every GQA ratio the kernel lays out differently (1, 2 and 4: four matrix rows per head; 8: two
 rows per head plus a tile of top limbs), automatic and explicit splits (every wave walks a chunk of its
-own), ragged and empty sequences, appends that demote groups, and the batch-32 x 32k and 4 x 131k shapes
-at full size (sampled heads).
+own; with more chunks than one round of work-groups holds, several in a row), ragged and empty sequences,
+and appends that demote groups.  The full-size shapes are in test_gpu_fullsize.py.
 """
 import numpy as np
 import pytest
@@ -77,6 +77,40 @@ def test_mfma_gqa4_explicit_splits(K, split):
     _case(K, wl, lens, [2], chunk=800, split=split, check_codes=False)
 
 
+@pytest.mark.parametrize("name,kw,batch,lo,hi", [
+    ("batch32_32k", {}, 32, 3000, 7000),                          # GQA 4, head quads
+    ("long_b4_131k", {}, 16, 7000, 10000),                        # GQA 8, head quads
+    ("saw_int4_b16_16k", {}, 32, 4000, 7000),                     # INT4 per token: page pairs
+    ("batch32_32k", dict(n_q_heads=8, n_kv_heads=2), 64, 9000, 12000),  # two kv heads: four walks per work-group
+])
+def test_mfma_walks_several_chunks(K, name, kw, batch, lo, hi):
+    """An explicit 512-token split with more chunks than one round of work-groups holds: each wave walks
+    several consecutive chunks, storing a partial at every chunk boundary.  Ragged lengths (two of them empty)
+    put the boundaries and the ends of the walks everywhere; the whole output is compared with the fp32
+    decode of the same cache (one chunk per work-group) and sampled heads with the oracle."""
+    wl = synth.scaled(synth.WORKLOADS[name], batch=batch, **kw)
+    rng = np.random.default_rng(batch * 7919 + lo)
+    lens = rng.integers(lo, hi + 1, size=batch)
+    lens[3] = 0
+    lens[batch - 2] = 0
+    bc = build_cache(K, wl, lens, split_tokens=512, decode_impl=K.DECODE_MFMA, seqs_per_call=8)
+    shape = K.decode_shape(bc.cfg, batch, int(lens.max()))
+    _say(f"mfma: {name} {kw} batch {batch}, lens {lens.min()}..{lens.max()}, split 512: {shape}")
+    assert shape["matrix_cores"] == 1 and shape["span"] >= 2
+    q = synth.queries(wl)
+    out = run_decode(K, bc, q)
+    assert np.isfinite(out).all()
+    bc.cfg.decode_impl = K.DECODE_F32
+    ref = run_decode(K, bc, q)
+    bc.cfg.decode_impl = K.DECODE_MFMA
+    d32 = np.abs(out - ref).max()
+    _say(f"   max |mfma - f32| over all heads = {d32:.2e}")
+    assert d32 <= TOL
+    pairs = [(b, h) for b in (0, 3, 5, batch // 2, batch - 1) for h in (0, wl.n_kv_heads - 1)]
+    worst = check_out(bc, out, q, pairs)
+    _say(f"   worst |mfma - oracle| = {worst:.2e}")
+
+
 def test_mfma_agrees_with_f32(K):
     """Same cache, two decodes: the matrix-core one (three-limb operands) close to the exact fp32 one."""
     for name, lens in (("tiny_1h_4k", [4096]), ("gqa_b1_32k", [2900, 1000]), ("long_b4_131k", [3000, 700])):
@@ -97,30 +131,6 @@ def test_mfma_is_deterministic(K):
     bc = build_cache(K, wl, [2500, 900], decode_impl=K.DECODE_MFMA)
     q = synth.queries(synth.scaled(wl, batch=2))
     assert np.array_equal(run_decode(K, bc, q), run_decode(K, bc, q))
-
-
-def test_mfma_batch32_32k_full_sampled(K):
-    """The bench's workload at full size: 32 sequences x 32768 tokens, 32 q / 8 kv heads."""
-    wl = synth.WORKLOADS["batch32_32k"]
-    lens = synth.seq_lens(wl)
-    _say(f"mfma: batch32_32k full, lens {lens.min()}..{lens.max()}")
-    bc = build_cache(K, wl, lens, seqs_per_call=4, decode_impl=K.DECODE_MFMA)
-    q = synth.queries(wl)
-    out = run_decode(K, bc, q)
-    assert np.isfinite(out).all()
-    worst = check_out(bc, out, q, [(0, 0), (17, 5), (31, 7)])
-    _say(f"   worst |mfma - oracle| = {worst:.2e}")
-
-
-def test_mfma_long_b4_131k_full_sampled(K):
-    wl = synth.WORKLOADS["long_b4_131k"]
-    _say("mfma: long_b4_131k full, B=4, T=131072, split 512")
-    bc = build_cache(K, wl, [131072] * 4, split_tokens=512, seqs_per_call=1, decode_impl=K.DECODE_MFMA)
-    q = synth.queries(wl)
-    out = run_decode(K, bc, q)
-    assert np.isfinite(out).all()
-    worst = check_out(bc, out, q, [(2, 6)])
-    _say(f"   worst |mfma - oracle| = {worst:.2e}")
 
 
 # ------------------------------------------------------------------ per-token INT2 on the matrix cores

@@ -230,38 +230,3 @@ def test_gqa_b1_32k_full_sampled(K):
     q = synth.queries(wl)
     out = run_decode(K, bc, q)
     check_out(bc, out, q, [(0, 2), (0, 7)])
-
-
-def test_batch32_ragged_full_sampled(K):
-    wl = synth.WORKLOADS["batch32_8k_32k"]
-    lens = synth.seq_lens(wl)
-    _say(f"batch32 ragged full: lens {lens.min()}..{lens.max()}")
-    bc = build_cache(K, wl, lens, seqs_per_call=4)
-    pages, band = _host(bc)
-    for b in (0, 31):
-        check_int2(bc, b, 1, groups=[0, O.n_groups(int(lens[b]), 4, 128) - 1], pages=pages, band=band)
-    q = synth.queries(wl)
-    out = run_decode(K, bc, q)
-    check_out(bc, out, q, [(3, 0), (30, 6)])
-
-
-def test_saw_int4_full_sampled(K):
-    wl = synth.WORKLOADS["saw_int4_b16_16k"]
-    _say("saw int4 full: B=16, T=16384, 8192-token prefill chunks")
-    bc = build_cache(K, wl, [16384] * 16, chunk=8192, seqs_per_call=4)
-    pages = bc.cache.pages.cpu().numpy()
-    check_int4(bc, 5, 3, pages)
-    q = synth.queries(wl)
-    out = run_decode(K, bc, q)
-    check_out(bc, out, q, [(0, 0), (15, 7)])
-
-
-def test_long_b4_131k_full_sampled(K):
-    wl = synth.WORKLOADS["long_b4_131k"]
-    _say("long_b4_131k full: B=4, T=131072, split 512")
-    bc = build_cache(K, wl, [131072] * 4, split_tokens=512, seqs_per_call=1)
-    pages, band = _host(bc)
-    check_int2(bc, 2, 4, groups=[0, 500, O.n_groups(131072, 4, 256) - 1], pages=pages, band=band)
-    q = synth.queries(wl)
-    out = run_decode(K, bc, q)
-    check_out(bc, out, q, [(1, 3)])
