@@ -488,6 +488,16 @@ def prefill_int2(q_rows, q_pos, k_src, v_src, T, n_sink, n_recent, clip_k, clip_
     return attend_causal(query_values(q_rows), np.asarray(q_pos), K, V, token_positions(st, T, n_sink, n_recent))
 
 
+def prefill_int4(q_rows, q_pos, k_src, v_src, T, sign_k, sign_v, block: int = D):
+    """Prefill attention of the chunk's queries over an INT4 per-token cache of length T (chunk included):
+    the chunk is written (rotated and quantized per token) before its queries read the cache back ([SAW]
+    prefill stage; [NOVA] §3 "Long context"), so every visible token, the chunk's own included, is read
+    dequantized and inverse-rotated."""
+    st = int4_state(k_src, v_src, T, sign_k, sign_v, block=block)
+    K, V = int4_keys_values(st, sign_k, sign_v, block)
+    return attend_causal(query_values(q_rows), np.asarray(q_pos), K, V, np.arange(T))
+
+
 def decode_int4(q_heads, k_src, v_src, T, sign_k, sign_v, block: int = D):
     st = int4_state(k_src, v_src, T, sign_k, sign_v, block=block)
     K, V = int4_keys_values(st, sign_k, sign_v, block)

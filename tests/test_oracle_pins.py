@@ -507,6 +507,33 @@ def test_causal_attention_reduces_to_decode_and_to_prefixes():
     assert sorted(tp.tolist()) == list(range(T))
 
 
+def test_int4_prefill_is_decode_over_each_prefix():
+    """INT4 per token quantizes every token on its own, so the cache after a chunk's write holds the same
+    codes for a prefix as a cache of that prefix alone: the query at position p equals the decode over the
+    first p + 1 tokens (the last query the decode over all T); and a query at position 0 reads exactly the
+    dequantized, inverse-rotated first value, whatever its logit."""
+    r = np.random.default_rng(67)
+    T = 300
+    k = r.standard_normal((T, 128)).astype(np.float32)
+    v = r.standard_normal((T, 128)).astype(np.float32)
+    q = r.standard_normal((5, 4, 128)).astype(np.float32)
+    sk = np.where(r.random(128) < 0.5, -1.0, 1.0).astype(np.float32)
+    sv = np.where(r.random(128) < 0.5, -1.0, 1.0).astype(np.float32)
+    pos = np.array([0, 63, 64, 200, T - 1])
+    for block, svv in ((128, sv), (32, sv), (128, None)):
+        got = O.prefill_int4(q, pos, k, v, T, sk, svv, block)
+        for i, p in enumerate(pos):
+            want, _ = O.decode_int4(q[i], k, v, int(p) + 1, sk, svv, block)
+            assert np.abs(got[i] - want).max() < 1e-12
+        # position 0: the first value back in its own frame, within the rounding of one 15-step code per
+        # rotated channel (the inverse rotation is orthonormal) and of the bf16 source
+        st = O.int4_state(k, v, 1, sk, svv, block=block)
+        step = float(O.bf16_value(st["v_s16"][:1])[0])
+        bound = 0.5 * step * np.sqrt(128) * 1.01 + 2.0 ** -8 * np.linalg.norm(v[0])
+        err = np.linalg.norm(got[0] - v[0].astype(np.float64)[None, :], axis=1).max()  # L2 over channels
+        assert err <= bound, (block, err, bound)
+
+
 def test_int4_channel_quantizer_closed_forms():
     """Per-channel INT4 (15 levels): channels built as a + s n, n in {0..15} and s a power of two, give codes
     n and dequantize exactly; the 3-level instance is the pinned INT2 quantizer."""
