@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--write-tokens", type=int, default=8192)
     ap.add_argument("--prefill-bench", action="store_true",
                     help="time prefill attention of the last --prefill-chunk tokens of every sequence over the "
-                         "quantized history (INT2 workloads); prints its own JSON line")
+                         "quantized history (any workload and scheme); prints its own JSON line")
     ap.add_argument("--prefill-chunk", type=int, default=4096)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (torch copy kernel) 5 times: the known-size "
@@ -301,20 +301,13 @@ def write_bench(args, K, synth, np, torch):
 def prefill_bench(args, K, synth, np, torch):
     """Prefill attention of each sequence's last chunk over its quantized history (the cache written in
     chunks as in chunked prefill): HIP events around kv_prefill_attn (query rotation + attention kernel)."""
-    wl = synth.WORKLOADS[args.workload]
-    if args.key_only:
-        wl = synth.scaled(wl, key_only=True)
-    if wl.scheme != "int2_channel":
-        sys.exit("prefill attention is built for the per-channel INT2 workloads")
+    wl = workload_of(args, synth)
     dev = "cuda"
     torch.cuda.set_device(0)
     B, n_kv, n_q = wl.batch, wl.n_kv_heads, wl.n_q_heads
     lens = synth.seq_lens(wl).astype(np.int64)
     n = int(args.prefill_chunk)
-    cfg = K.make_config(n_kv, n_q, K.INT2_CHANNEL, K.ROT_DENSE, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v, 0, 0,
-                        wl.key_only)
-    rk = K.build_oscar_rotation(synth.rotation_gaussian(wl, "k")).astype(np.float32)
-    rv = K.build_oscar_rotation(synth.rotation_gaussian(wl, "v")).astype(np.float32)
+    cfg, rk, rv = config_of(wl, K, synth, np, 0, K.DECODE_AUTO)
     max_pages = K.pages_for_len(cfg, int(lens.max()))
     n_pool = B * max_pages
     pt = K.build_page_table(B, max_pages, n_pool, seed=0 if wl.identity_pages else wl.seed)
@@ -363,7 +356,8 @@ def prefill_bench(args, K, synth, np, torch):
         "unit": "TOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_call": round(t * 1e3, 4),
         "higher_is_better": True, "dtype": "int8 limbs (24-bit fixed point) + bf16 band", "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "ctx": int(lens.max()), "chunk": n, "n_q_heads": n_q,
-                   "n_kv_heads": n_kv, "key_only": wl.key_only},
+                   "n_kv_heads": n_kv, "scheme": wl.scheme, "key_only": wl.key_only,
+                   "hadamard_block": wl.hadamard_block if wl.rotation == "saw" else None},
         "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": 5000.0, "unit": "TOP/s",
                      "frac": round(tops / 5000.0, 5), "traffic": None,
                      "note": "int8 peak; each algorithmic MAC is three int8 MACs (limbs) here"},
@@ -444,6 +438,22 @@ def workload_of(args, synth):
     return wl
 
 
+def config_of(wl, K, synth, np, split, impl):
+    """The library config of a workload and its rotation inputs (dense R from the library's builder for the
+    grouped schemes, sign vectors for the randomized Hadamard)."""
+    if wl.scheme in GROUPED:
+        cfg = K.make_config(wl.n_kv_heads, wl.n_q_heads, GROUPED[wl.scheme], K.ROT_DENSE, wl.n_sink, wl.n_recent,
+                            wl.clip_k, wl.clip_v, split, impl, wl.key_only)
+        rk = K.build_oscar_rotation(synth.rotation_gaussian(wl, "k")).astype(np.float32)
+        rv = K.build_oscar_rotation(synth.rotation_gaussian(wl, "v")).astype(np.float32)
+    else:
+        cfg = K.make_config(wl.n_kv_heads, wl.n_q_heads, K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0, split, impl,
+                            wl.key_only, wl.hadamard_block)
+        rk = synth.sign_vector(wl, "k").astype(np.float32)
+        rv = synth.sign_vector(wl, "v").astype(np.float32)
+    return cfg, rk, rv
+
+
 def measure_decode(wl, args, K, synth, np, torch):
     """Decode steps of one workload: a cache written to the lengths before the measured steps, then W warm-up
     steps, a 128-step window and the K timed steps, each step one append of a token per sequence followed by
@@ -462,16 +472,7 @@ def measure_decode(wl, args, K, synth, np, torch):
     T_end = int(lens_end.max())
     impl = {"auto": K.DECODE_AUTO, "f32": K.DECODE_F32, "mfma": K.DECODE_MFMA}[args.impl]
     split = args.split if args.split else (wl.split_tokens if wl.name == "long_b4_131k" else 0)
-    if grouped:
-        cfg = K.make_config(n_kv, n_q, GROUPED[wl.scheme], K.ROT_DENSE, wl.n_sink, wl.n_recent, wl.clip_k,
-                            wl.clip_v, split, impl, wl.key_only)
-        rk = K.build_oscar_rotation(synth.rotation_gaussian(wl, "k")).astype(np.float32)
-        rv = K.build_oscar_rotation(synth.rotation_gaussian(wl, "v")).astype(np.float32)
-    else:
-        cfg = K.make_config(n_kv, n_q, K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0, split, impl, wl.key_only,
-                            wl.hadamard_block)
-        rk = synth.sign_vector(wl, "k").astype(np.float32)
-        rv = synth.sign_vector(wl, "v").astype(np.float32)
+    cfg, rk, rv = config_of(wl, K, synth, np, split, impl)
     max_pages = K.pages_for_len(cfg, T_end)
     n_pool = B * max_pages
     pt = K.build_page_table(B, max_pages, n_pool, seed=0 if wl.identity_pages else wl.seed)

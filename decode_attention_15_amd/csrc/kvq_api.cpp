@@ -484,7 +484,6 @@ int kv_prefill_attn(const kvq_config* cfg, const kvq_cache* cache, const void* q
   int st = check_config(cfg);
   if (st != KVQ_OK) return st;
   if ((st = check_cache(cfg, cache)) != KVQ_OK) return st;
-  if (cfg->scheme != KVQ_INT2_CHANNEL || cfg->rotation != KVQ_ROT_DENSE) return KVQ_EUNSUPPORTED;
   if (!q || !cu_q || !out || total_q_host < 0 || max_q_host < 0 || (dtype != KVQ_F32 && dtype != KVQ_BF16))
     return KVQ_EINVAL;
   if (total_q_host == 0) return KVQ_OK;

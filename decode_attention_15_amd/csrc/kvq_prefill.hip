@@ -2,18 +2,23 @@
 // written attend to every cached token at a position not after their own ([NOVA] §3 "Long context":
 // chunked prefill, each chunk quantized on write, so later chunks read a quantized history; [SAW]
 // Fig. "Prefill Stage": save the chunk, read the cache back, attention).  The cache is read as it stands
-// after the chunk's write: bf16 sink/tail tokens and INT2 per-channel groups, in the rotated frame for the
-// groups (query rotated once, output un-rotated once by R_V^T) as in the decode.
+// after the chunk's write, for every scheme: bf16 sink/tail tokens and 128-token groups (INT2 per channel
+// or per token, INT4 per channel), or INT4 per-token pages read in pairs of 128 tokens; quantized tokens in
+// the rotated frame (query rotated once, output un-rotated once) as in the decode.
 //
 // Contractions run on the matrix cores:
-//  - INT2 groups on v_mfma_i32_16x16x64_i8 in 24-bit fixed point: per (query head, group) the key-side
-//    operand a = rint(alpha S / max|alpha|), alpha = q~ s, and the weights u = rint(S p), p = 2^(logit -
-//    group max), S = 8355584, each as three signed byte limbs (65536 hi + 256 mid + lo) against the 2-bit
-//    codes (exact int32 sums per limb).  Outputs can be an order of magnitude above 1 (outlier channels),
-//    so the operands keep more bits than the decode's 16;
+//  - quantized tokens on v_mfma_i32_16x16x64_i8 in 24-bit fixed point, three signed byte limbs (65536 hi +
+//    256 mid + lo) against the 2- or 4-bit codes (exact int32 sums per limb), full scale S = 8355584.
+//    Per channel: per (query head, group) the key-side operand a = rint(alpha S / max|alpha|), alpha = q~ s,
+//    and the weights u = rint(S p), p = 2^(logit - group max).  Per token: the key-side operand is the
+//    rotated query itself (a = rint(q~ S / max|q~|), once per query), logit_t = A s_t (D_t - z_t sum_c a_c),
+//    and the weights u_t = rint(S p_t s'_t / S'), S' the unit's largest p_t s'_t, the value sum adding
+//    (S' / S) (U_c - sum_t u_t z'_t).  Outputs can be an order of magnitude above 1 (outlier channels), so
+//    the operands keep more bits than 16;
 //  - bf16 band tokens on v_mfma_f32_16x16x32_bf16 with the query and the weights split into bf16 hi + lo
 //    (about 16 significant bits) against the exact bf16 values;
-//  - the un-rotation on the same bf16 instruction with both operands split (hi hi + hi lo + lo hi).
+//  - the dense un-rotation on the same bf16 instruction with both operands split (hi hi + hi lo + lo hi);
+//    the randomized Hadamard's un-rotation is a fp32 Walsh-Hadamard transform in registers.
 // Operand layouts (16 x 16 tiles; lane l, q = l / 16): i8: A row l % 16, k = 16 q + byte index; B the
 // same k, column l % 16; bf16: k = 8 q + element index; D: column l % 16, rows 4 q + 0..3.  The k index
 // of a contraction may map to channels or tokens in any order used by both operands; the mappings below
@@ -100,15 +105,91 @@ __device__ inline void dma16_p(uint32_t lds, const void* gaddr) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gaddr) : "memory");
 }
 
-struct GroupBuf {
-  uint32_t k[2][512];   // key codes, page p token t at [p][8 t .. 8 t + 7]
-  uint32_t v[2][512];   // value codes, page p channel c at [p][4 c .. 4 c + 3]
-  uint16_t meta[512];   // K scales[128], K zeros[128] (even page), V scales[128], V zeros[128] (odd page)
+// What the prefill kernel reads of a scheme's pages: code bits, the words of a key row (one token, 128
+// channels) and of a value row (one channel, 64 tokens of a page), the offsets in a kv head's block of a
+// page, and whether the scales and zeros are per channel of a group or per token.
+template <int SCHEME>
+struct PrefillScheme {
+  static constexpr bool GROUPED = SCHEME != KVQ_INT4_TOKEN;  // 128-token groups aligned at S0, bf16 band
+  static constexpr bool TOK = SCHEME == KVQ_INT2_TOKEN || SCHEME == KVQ_INT4_TOKEN;
+  static constexpr int BITS = (SCHEME == KVQ_INT2_CHANNEL || SCHEME == KVQ_INT2_TOKEN) ? 2 : 4;
+  static constexpr int HEAD = BITS == 2 ? I2_HEAD_BYTES : I4_HEAD_BYTES;
+  static constexpr int VOFF = BITS == 2 ? I2_V_OFF : I4_V_OFF;
+  static constexpr int MOFF = BITS == 2 ? I2_META_OFF : I4_KMETA_OFF;  // 512 B per page in every layout
+  static constexpr int KROW = BITS == 2 ? 8 : 16;  // words per key row
+  static constexpr int VROW = BITS == 2 ? 4 : 8;   // words per value row and page
 };
 
-template <int GQ>
-__global__ __launch_bounds__(256) void prefill_int2_kernel(DecodeArgs a) {
-  __shared__ GroupBuf gb[2];
+// Key operand of a token row for the channels of 16-channel block m (k = 16 q + 4 k' + j: dword k', byte j):
+//  - 2-bit codes (channel c in byte c / 4, field c % 4): word m, dword k' = field k' -> channel 16 m + 4 j + k';
+//  - per-channel 4-bit (word 2 m + e holds channels 16 m + 2 k + e in nibble k): low nibbles of words 2 m,
+//    2 m + 1, then their high nibbles -> channel 16 m + 4 j + k';
+//  - per-token 4-bit (channel c in byte c / 2, even c low): words 2 m, 2 m + 1, low then high nibbles of
+//    each -> channel 16 m + 8 (k' / 2) + 2 j + k' % 2.
+template <int SCHEME>
+__device__ inline int key_channel(int m, int e) {  // e = 4 j + k'
+  if constexpr (SCHEME == KVQ_INT4_TOKEN) return 16 * m + 8 * ((e & 3) >> 1) + 2 * (e >> 2) + (e & 1);
+  return 16 * m + e;
+}
+__device__ inline i32x4 nib_lo_lo_hi_hi(uint32_t w0, uint32_t w1) {
+  return i32x4{(int)(w0 & 0x0F0F0F0Fu), (int)(w1 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu),
+               (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+}
+__device__ inline i32x4 nib_lo_hi_lo_hi(uint32_t w0, uint32_t w1) {
+  return i32x4{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu), (int)(w1 & 0x0F0F0F0Fu),
+               (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+}
+template <int SCHEME>
+__device__ inline i32x4 key_codes(const uint32_t* row, int m) {
+  if constexpr (PrefillScheme<SCHEME>::BITS == 2) return unpack_codes(row[m]);
+  else if constexpr (SCHEME == KVQ_INT4_CHANNEL) return nib_lo_lo_hi_hi(row[2 * m], row[2 * m + 1]);
+  else return nib_lo_hi_lo_hi(row[2 * m], row[2 * m + 1]);
+}
+// Value operand of a channel row of one page, lane q (k = 16 q + 4 d + b: dword d, byte b), tokens (of the
+// page) 16 J + 4 q + R:
+//  - 2-bit codes (token 16 j + 4 g + r in byte 4 g + j, field r): word q, dword d = field d -> J = b, R = d;
+//  - per-channel 4-bit (word 2 g + n holds tokens 16 j + 4 g + 2 h + n in nibble 2 j + h): low nibbles of
+//    words 2 q, 2 q + 1, then their high nibbles -> J = b, R = d;
+//  - per-token 4-bit (token 16 j + 4 g + r in byte 8 g + 2 j + r / 2, even r low): words 2 q, 2 q + 1, low
+//    then high nibbles of each -> J = 2 (d / 2) + b / 2, R = 2 (b % 2) + d % 2.
+template <int SCHEME>
+__device__ inline i32x4 value_codes(const uint32_t* row, int q) {
+  if constexpr (PrefillScheme<SCHEME>::BITS == 2) return unpack_codes(row[q]);
+  else if constexpr (SCHEME == KVQ_INT4_CHANNEL) return nib_lo_lo_hi_hi(row[2 * q], row[2 * q + 1]);
+  else return nib_lo_hi_lo_hi(row[2 * q], row[2 * q + 1]);
+}
+template <int SCHEME>
+__device__ inline void value_tok(int d, int b, int& J, int& R) {
+  if constexpr (SCHEME == KVQ_INT4_TOKEN) {
+    J = 2 * (d >> 1) + (b >> 1);
+    R = 2 * (b & 1) + (d & 1);
+  } else {
+    J = b;
+    R = d;
+  }
+}
+
+// The page pair of one 128-token unit: grouped schemes' group (two pages), or two consecutive INT4 pages
+template <int BITS>
+struct GroupBuf {
+  uint32_t k[2][64 * (BITS == 2 ? 8 : 16)];   // page p, token t at [p][KROW t ..]
+  uint32_t v[2][128 * (BITS == 2 ? 4 : 8)];   // page p, channel c at [p][VROW c ..]
+  uint16_t meta[512];                         // the pages' 512-byte metadata blocks, page 0 then page 1
+};
+
+// Signed limbs of the integers x[e] (e = 4 j + k') as the three dwords of an i8 operand per limb
+__device__ inline void limb_operands(const int (&x)[16], i32x4 (&op)[3]) {
+  uint32_t w[4][3];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pack_limbs(x[k], x[4 + k], x[8 + k], x[12 + k], w[k]);
+#pragma unroll
+  for (int lb = 0; lb < 3; ++lb) op[lb] = i32x4{(int)w[0][lb], (int)w[1][lb], (int)w[2][lb], (int)w[3][lb]};
+}
+
+template <int GQ, int SCHEME>
+__global__ __launch_bounds__(256) void prefill_kernel(DecodeArgs a) {
+  using SC = PrefillScheme<SCHEME>;
+  __shared__ GroupBuf<SC::BITS> gb[2];
   const Geo& g = a.g;
   const int b = blockIdx.z, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4;
@@ -127,146 +208,182 @@ __global__ __launch_bounds__(256) void prefill_int2_kernel(DecodeArgs a) {
   const int pos_max = T - nq + last_q;
 
   // ---- band (sink + tail, bf16, original frame): blocks of 64 tokens
-  const int ng = n_groups_of(T, g.S0, g.W);
-  const int n_sink = T < g.S0 ? T : g.S0;
-  const int tail0 = g.S0 + GROUP * ng;
-  const int n_tail = T > tail0 ? T - tail0 : 0;
-  const int nb = n_sink + n_tail;
-  const uint16_t* band = a.band + ((long long)b * g.n_kv + h) * g.slots * 256;
-  auto bpos = [&](int k) { return k < n_sink ? k : tail0 + (k - n_sink); };
-  auto bslot = [&](int k) { return band_slot_of(bpos(k), g.S0, g.W); };
+  const int ng = SC::GROUPED ? n_groups_of(T, g.S0, g.W) : 0;
   float mb = -INFINITY, lb = 0.0f;
   f32x4 ob[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) ob[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  if (nb > 0) {
-    // query (original frame, log2e / sqrt(d) folded in) for channels 32 ks + 8 q + e, as hi/lo operands
-    u32x4 qh[4], ql[4];
-    {
-      const float* qb = a.qband + row;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = qb[32 * ks + 8 * q + e];
-        split8(x, qh[ks], ql[ks]);
-      }
-    }
-    for (int k0 = 0; k0 < nb; k0 += 64) {
-      // S^T (64 tokens x 16 columns): token 16 mt + (l % 16) is the A row; channels 32 ks + 8 q + e
-      float s[4][4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int kk = min(k0 + 16 * mt + (lane & 15), nb - 1);  // rows past the band repeat a valid one
-        const uint16_t* kr = band + (long long)bslot(kk) * 256;
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (SC::GROUPED) {
+    const int n_sink = T < g.S0 ? T : g.S0;
+    const int tail0 = g.S0 + GROUP * ng;
+    const int n_tail = T > tail0 ? T - tail0 : 0;
+    const int nb = n_sink + n_tail;
+    const uint16_t* band = a.band + ((long long)b * g.n_kv + h) * g.slots * 256;
+    auto bpos = [&](int k) { return k < n_sink ? k : tail0 + (k - n_sink); };
+    auto bslot = [&](int k) { return band_slot_of(bpos(k), g.S0, g.W); };
+    if (nb > 0) {
+      // query (original frame, log2e / sqrt(d) folded in) for channels 32 ks + 8 q + e, as hi/lo operands
+      u32x4 qh[4], ql[4];
+      {
+        const float* qb = a.qband + row;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const u32x4 av = *reinterpret_cast<const u32x4*>(kr + 32 * ks + 8 * q);
-          acc = mfma_bf16(av, qh[ks], acc);
-          acc = mfma_bf16(av, ql[ks], acc);
-        }
+          float x[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int k = k0 + 16 * mt + 4 * q + i;
-          s[mt][i] = (k < nb && bpos(k) <= qpos) ? acc[i] : -INFINITY;
+          for (int e = 0; e < 8; ++e) x[e] = qb[32 * ks + 8 * q + e];
+          split8(x, qh[ks], ql[ks]);
         }
       }
-      float bm = -INFINITY;
+      for (int k0 = 0; k0 < nb; k0 += 64) {
+        // S^T (64 tokens x 16 columns): token 16 mt + (l % 16) is the A row; channels 32 ks + 8 q + e
+        float s[4][4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt) {
+          const int kk = min(k0 + 16 * mt + (lane & 15), nb - 1);  // rows past the band repeat a valid one
+          const uint16_t* kr = band + (long long)bslot(kk) * 256;
+          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bm = fmaxf(bm, s[mt][i]);
-      bm = col_max(bm);
-      const float mnew = fmaxf(mb, bm);
-      const float sc = exp2_or_zero(mb, mnew);
-      float p[4][4], ps = 0.0f;
+          for (int ks = 0; ks < 4; ++ks) {
+            const u32x4 av = *reinterpret_cast<const u32x4*>(kr + 32 * ks + 8 * q);
+            acc = mfma_bf16(av, qh[ks], acc);
+            acc = mfma_bf16(av, ql[ks], acc);
+          }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[mt][i] = exp2_or_zero(s[mt][i], mnew);
-          ps += p[mt][i];
+          for (int i = 0; i < 4; ++i) {
+            const int k = k0 + 16 * mt + 4 * q + i;
+            s[mt][i] = (k < nb && bpos(k) <= qpos) ? acc[i] : -INFINITY;
+          }
         }
-      lb = lb * sc + col_sum(ps);
-      mb = mnew;
-      // O_b^T (128 channels x 16 columns) += V^T P^T: k = 8 q + e maps to token 32 ks + 4 q + e (e < 4)
-      // and 32 ks + 16 + 4 q + e - 4 (e >= 4), i.e. this lane's own weights of tiles 2 ks, 2 ks + 1
-      u32x4 ph[2], pl[2];
+        float bm = -INFINITY;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const float x[8] = {p[2 * ks][0], p[2 * ks][1], p[2 * ks][2], p[2 * ks][3],
-                            p[2 * ks + 1][0], p[2 * ks + 1][1], p[2 * ks + 1][2], p[2 * ks + 1][3]};
-        split8(x, ph[ks], pl[ks]);
-      }
-      int slots[2][8];
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+          for (int i = 0; i < 4; ++i) bm = fmaxf(bm, s[mt][i]);
+        bm = col_max(bm);
+        const float mnew = fmaxf(mb, bm);
+        const float sc = exp2_or_zero(mb, mnew);
+        float p[4][4], ps = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int k = k0 + 32 * ks + (e < 4 ? 4 * q + e : 16 + 4 * q + e - 4);
-          slots[ks][e] = bslot(min(k, nb - 1));
-        }
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const int c = 16 * mt + (lane & 15);
-        f32x4 acc = ob[mt] * sc;
+          for (int i = 0; i < 4; ++i) {
+            p[mt][i] = exp2_or_zero(s[mt][i], mnew);
+            ps += p[mt][i];
+          }
+        lb = lb * sc + col_sum(ps);
+        mb = mnew;
+        // O_b^T (128 channels x 16 columns) += V^T P^T: k = 8 q + e maps to token 32 ks + 4 q + e (e < 4)
+        // and 32 ks + 16 + 4 q + e - 4 (e >= 4), i.e. this lane's own weights of tiles 2 ks, 2 ks + 1
+        u32x4 ph[2], pl[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          uint32_t w[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            w[e] = (uint32_t)band[(long long)slots[ks][2 * e] * 256 + 128 + c] |
-                   ((uint32_t)band[(long long)slots[ks][2 * e + 1] * 256 + 128 + c] << 16);
-          const u32x4 av = {w[0], w[1], w[2], w[3]};
-          acc = mfma_bf16(av, ph[ks], acc);
-          acc = mfma_bf16(av, pl[ks], acc);
+          const float x[8] = {p[2 * ks][0], p[2 * ks][1], p[2 * ks][2], p[2 * ks][3],
+                              p[2 * ks + 1][0], p[2 * ks + 1][1], p[2 * ks + 1][2], p[2 * ks + 1][3]};
+          split8(x, ph[ks], pl[ks]);
         }
-        ob[mt] = acc;
+        int slots[2][8];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int k = k0 + 32 * ks + (e < 4 ? 4 * q + e : 16 + 4 * q + e - 4);
+            slots[ks][e] = bslot(min(k, nb - 1));
+          }
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          const int c = 16 * mt + (lane & 15);
+          f32x4 acc = ob[mt] * sc;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              w[e] = (uint32_t)band[(long long)slots[ks][2 * e] * 256 + 128 + c] |
+                     ((uint32_t)band[(long long)slots[ks][2 * e + 1] * 256 + 128 + c] << 16);
+            const u32x4 av = {w[0], w[1], w[2], w[3]};
+            acc = mfma_bf16(av, ph[ks], acc);
+            acc = mfma_bf16(av, pl[ks], acc);
+          }
+          ob[mt] = acc;
+        }
       }
     }
   }
 
-  // ---- INT2 per-channel groups (rotated frame), double-buffered in LDS
-  // rotated query of this column for channels 16 m + 4 j + k' of words m = q and m = 4 + q, in the order
-  // e = 4 j + k' (the byte order of an unpacked code word)
+  // ---- quantized 128-token units (rotated frame), double-buffered in LDS
+  // rotated query of this column for the channels of blocks m = q and m = 4 + q, in the order e = 4 j + k'
+  // (the byte order of an unpacked code word)
   float qr[2][16];
   {
     const float* qp = a.qrot + row;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) qr[ks][e] = qp[16 * (4 * ks + q) + e];
+      for (int e = 0; e < 16; ++e) qr[ks][e] = qp[key_channel<SCHEME>(4 * ks + q, e)];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int e = 0; e < 16; ++e) asm volatile("" ::"v"(qr[ks][e]));  // loads complete before the walk
   }
-  int g_end = ng;
+  // units (groups, or INT4 page pairs) whose first token is after every column's position are invisible
+  const int u0 = SC::GROUPED ? g.S0 : 0;  // position of unit 0's first token
+  const int npages = (T + PAGE - 1) / PAGE;
+  int g_end = SC::GROUPED ? ng : (npages + 1) / 2;
   {
-    // groups whose first token is after every column's position are invisible
-    const int gv = pos_max < g.S0 ? 0 : (pos_max - g.S0) / GROUP + 1;
+    const int gv = pos_max < u0 ? 0 : (pos_max - u0) / GROUP + 1;
     if (gv < g_end) g_end = gv;
-    if (g_end > g.max_pages / 2) g_end = g.max_pages / 2;
+    const int row_units = SC::GROUPED ? g.max_pages / 2 : (g.max_pages + 1) / 2;  // never past the table row
+    if (g_end > row_units) g_end = row_units;
+  }
+  // per token: the key-side operand is the rotated query, once (A = max|q~| / S, FS = sum_c a_c)
+  i32x4 bq_tok[2][3];
+  float A_tok = 0.0f, FS_tok = 0.0f;
+  if constexpr (SC::TOK) {
+    float amx = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) amx = fmaxf(amx, fabsf(qr[ks][e]));
+    amx = col_max(amx);
+    const float inv = amx > 0.0f ? kS24 / amx : 0.0f;
+    float fs = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      int x[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        x[e] = (int)rintf(qr[ks][e] * inv);
+        fs += (float)x[e];
+      }
+      limb_operands(x, bq_tok[ks]);
+    }
+    FS_tok = col_sum(fs);
+    A_tok = amx * (1.0f / kS24);
   }
   float m = -INFINITY, l = 0.0f;
   f32x4 o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const int32_t* pt = a.page_table + (long long)b * g.max_pages;
-  const long long hoff = (long long)h * I2_HEAD_BYTES;
-  // copies of one group: wave 0 K page 0, wave 1 K page 1, wave 2 V page 0, wave 3 V page 1 + metadata
+  const long long hoff = (long long)h * SC::HEAD;
+  // the two pages of unit gi (an INT4 sequence with an odd page count reads its last page twice, the
+  // second copy past the length and never weighted)
+  auto page_of = [&](int gi, int pp) {
+    int idx = 2 * gi + pp;
+    if (!SC::GROUPED && idx >= npages) idx = npages - 1;
+    if (idx >= g.max_pages) idx = g.max_pages - 1;
+    return a.pages + pool_page(g, pt[idx]) * g.page_bytes + hoff;
+  };
+  // copies of one unit: wave 0 K page 0, wave 1 K page 1, wave 2 V page 0, wave 3 V page 1 + metadata
+  constexpr int NCP = SC::BITS == 2 ? 2 : 4;  // 1 KB copies per page and side
   auto issue = [&](int gi, int buf) {
     const int pp = wave & 1;
-    const uint8_t* pg = a.pages + pool_page(g, pt[2 * gi + pp]) * g.page_bytes + hoff;
+    const uint8_t* pg = page_of(gi, pp);
     uint32_t* dst = wave < 2 ? gb[buf].k[pp] : gb[buf].v[pp];
-    const uint8_t* src = pg + (wave < 2 ? I2_K_OFF : I2_V_OFF);
+    const uint8_t* src = pg + (wave < 2 ? 0 : SC::VOFF);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) dma16_p(lds_addr_p(dst + 256 * j), src + 1024 * j + 16 * lane);
-    if (wave == 3) {
-      const uint8_t* pm = a.pages + pool_page(g, pt[2 * gi + (lane >> 5)]) * g.page_bytes + hoff + I2_META_OFF;
-      dma16_p(lds_addr_p(gb[buf].meta), pm + 16 * (lane & 31));
-    }
+    for (int j = 0; j < NCP; ++j) dma16_p(lds_addr_p(dst + 256 * j), src + 1024 * j + 16 * lane);
+    if (wave == 3) dma16_p(lds_addr_p(gb[buf].meta), page_of(gi, lane >> 5) + SC::MOFF + 16 * (lane & 31));
   };
   if (g_end > 0) issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -274,55 +391,64 @@ __global__ __launch_bounds__(256) void prefill_int2_kernel(DecodeArgs a) {
   for (int gi = 0; gi < g_end; ++gi) {
     const int buf = gi & 1;
     if (gi + 1 < g_end) issue(gi + 1, buf ^ 1);
-    const GroupBuf& B = gb[buf];
-    const int gpos = g.S0 + GROUP * gi;
-    // 1. key-side operand of this column: a = rint(alpha 32639 / max |alpha|), alpha = q~ s_k
-    float al[2][16];
-    float amx = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int c = 16 * (4 * ks + q) + 4 * (e >> 2) + (e & 3);  // e = 4 j + k' -> channel 16 m + 4 j + k'
-        al[ks][e] = qr[ks][e] * bf16_to_f32(B.meta[c]);
-        amx = fmaxf(amx, fabsf(al[ks][e]));
-      }
-    amx = col_max(amx);
-    const float inv = amx > 0.0f ? kS24 / amx : 0.0f;
-    int ai[2][16];
-    float zs = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int c = 16 * (4 * ks + q) + 4 * (e >> 2) + (e & 3);
-        ai[ks][e] = (int)rintf(al[ks][e] * inv);
-        zs = fmaf((float)ai[ks][e], bf16_to_f32(B.meta[D + c]), zs);
-      }
-    zs = col_sum(zs);
-    const float Acol = amx * (1.0f / kS24), AZ = Acol * zs;
-    // B operands (limbs lo, mid, hi): dword k' of word m holds channels 16 m + 4 j + k' in byte j (e = 4 j + k')
+    const GroupBuf<SC::BITS>& B = gb[buf];
+    const int gpos = u0 + GROUP * gi;
+    // 1. key-side operand: per channel a = rint(alpha S / max|alpha|), alpha = q~ s_k of this group; per
+    //    token the query's, built once
     i32x4 bq[2][3];
+    float Acol, AZ = 0.0f;
+    if constexpr (SC::TOK) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int* x = ai[ks];
-      uint32_t w[4][3];
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) pack_limbs(x[k], x[4 + k], x[8 + k], x[12 + k], w[k]);
+        for (int lb3 = 0; lb3 < 3; ++lb3) bq[ks][lb3] = bq_tok[ks][lb3];
+      Acol = A_tok;
+    } else {
+      float al[2][16];
+      float amx = 0.0f;
 #pragma unroll
-      for (int lb = 0; lb < 3; ++lb) bq[ks][lb] = i32x4{(int)w[0][lb], (int)w[1][lb], (int)w[2][lb], (int)w[3][lb]};
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int c = key_channel<SCHEME>(4 * ks + q, e);
+          al[ks][e] = qr[ks][e] * bf16_to_f32(B.meta[c]);
+          amx = fmaxf(amx, fabsf(al[ks][e]));
+        }
+      amx = col_max(amx);
+      const float inv = amx > 0.0f ? kS24 / amx : 0.0f;
+      float zs = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        int x[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int c = key_channel<SCHEME>(4 * ks + q, e);
+          x[e] = (int)rintf(al[ks][e] * inv);
+          zs = fmaf((float)x[e], bf16_to_f32(B.meta[D + c]), zs);
+        }
+        limb_operands(x, bq[ks]);
+      }
+      zs = col_sum(zs);
+      Acol = amx * (1.0f / kS24);
+      AZ = Acol * zs;
     }
-    // 2. logits S^T (128 tokens x 16 columns): token 16 mt + (l % 16) is the A row, its code word 4 ks + q
+    // this lane's tokens: 16 mt + 4 q + i of the unit (page mt / 4, token 16 (mt % 4) + 4 q + i of it)
+    auto tok_meta = [&](int mt, int i, int which) {  // which: 0 K scale, 1 K zero, 2 V scale, 3 V zero
+      const int pg = mt >> 2, tt = 16 * (mt & 3) + 4 * q + i;
+      if constexpr (SCHEME == KVQ_INT2_TOKEN) return bf16_to_f32(B.meta[256 * pg + 64 * which + tt]);
+      else return bf16_to_f32(B.meta[256 * pg + 128 * (which >> 1) + 2 * tt + (which & 1)]);
+    };
+    // 2. logits S^T (128 tokens x 16 columns): token 16 mt + (l % 16) is the A row
     float lg[8][4];
     float gm = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
       const int t = 16 * mt + (lane & 15);
-      const uint32_t* kr = B.k[t >> 6] + 8 * (t & 63);
+      const uint32_t* kr = B.k[t >> 6] + SC::KROW * (t & 63);
       i32x4 cl = {0, 0, 0, 0}, cm = {0, 0, 0, 0}, ch = {0, 0, 0, 0};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const i32x4 av = unpack_codes(kr[4 * ks + q]);
+        const i32x4 av = key_codes<SCHEME>(kr, 4 * ks + q);
         cl = mfma_i8(av, bq[ks][0], cl);
         cm = mfma_i8(av, bq[ks][1], cm);
         ch = mfma_i8(av, bq[ks][2], ch);
@@ -330,72 +456,112 @@ __global__ __launch_bounds__(256) void prefill_int2_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = 16 * mt + 4 * q + i;
-        const float x = fmaf(Acol, limbs_value(ch, cm, cl, i), -AZ);
+        float x;
+        if constexpr (SC::TOK) x = (Acol * tok_meta(mt, i, 0)) * fmaf(-tok_meta(mt, i, 1), FS_tok, limbs_value(ch, cm, cl, i));
+        else x = fmaf(Acol, limbs_value(ch, cm, cl, i), -AZ);
         lg[mt][i] = (gpos + tok <= qpos) ? x : -INFINITY;
         gm = fmaxf(gm, lg[mt][i]);
       }
     }
     gm = col_max(gm);
-    // 3. weights u = floor(S p + 0.5), p = 2^(logit - group max), as byte limbs; the B operand of page
-    // kp: k = 16 q + 4 r + j maps to token 64 kp + 16 j + 4 q + r, this lane's logit (tile 4 kp + j, r)
+    // 3. weights as byte limbs.  Per channel u = floor(S p + 0.5), p = 2^(logit - group max); per token
+    //    u_t = floor(S p_t s'_t / S' + 0.5), S' = max_t p_t s'_t of the column, with P = sum_t p_t and
+    //    Z = sum_t u_t z'_t
     int u[8][4];
-    float us = 0.0f;
+    float Pf, Sg = 0.0f, Zt = 0.0f;
+    if constexpr (SC::TOK) {
+      float pw[8][4], wmx = 0.0f, ps = 0.0f;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+      for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u[mt][i] = (int)fmaf(exp2_or_zero(lg[mt][i], gm), kS24, 0.5f);
-        us += (float)u[mt][i];
-      }
-    const float Pf = col_sum(us);
+        for (int i = 0; i < 4; ++i) {
+          const float p = exp2_or_zero(lg[mt][i], gm);
+          ps += p;
+          // tokens past the length (their metadata unwritten) take no weight
+          pw[mt][i] = lg[mt][i] == -INFINITY ? 0.0f : p * tok_meta(mt, i, 2);
+          wmx = fmaxf(wmx, pw[mt][i]);
+        }
+      Sg = col_max(wmx);
+      Pf = col_sum(ps);
+      // below 2^-100 the unit's value terms are beyond fp32's reach next to the others: weights 0
+      const float r = Sg > 0x1p-100f ? kS24 / Sg : 0.0f;
+      float zs = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u[mt][i] = (int)fmaf(pw[mt][i], r, 0.5f);
+          if (lg[mt][i] != -INFINITY) zs = fmaf((float)u[mt][i], tok_meta(mt, i, 3), zs);
+        }
+      Zt = col_sum(zs);
+    } else {
+      float us = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u[mt][i] = (int)fmaf(exp2_or_zero(lg[mt][i], gm), kS24, 0.5f);
+          us += (float)u[mt][i];
+        }
+      Pf = col_sum(us);
+    }
+    // B operand of page kp: dword d, byte bb holds the weight of token 16 J + 4 q + R of the page, i.e. this
+    // lane's logit (tile 4 kp + J, i = R)
     i32x4 uq[2][3];
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp) {
-      uint32_t w[4][3];  // dword r: tokens 16 j + 4 q + r of page kp in byte j
+      int x[16];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pack_limbs(u[4 * kp][r], u[4 * kp + 1][r], u[4 * kp + 2][r], u[4 * kp + 3][r], w[r]);
-#pragma unroll
-      for (int lb = 0; lb < 3; ++lb) uq[kp][lb] = i32x4{(int)w[0][lb], (int)w[1][lb], (int)w[2][lb], (int)w[3][lb]};
+      for (int e = 0; e < 16; ++e) {  // e = 4 bb + d (the order limb_operands packs)
+        int J, R;
+        value_tok<SCHEME>(e & 3, e >> 2, J, R);
+        x[e] = u[4 * kp + J][R];
+      }
+      limb_operands(x, uq[kp]);
     }
-    // 4. values U^T (128 channels x 16 columns): channel 16 mt + (l % 16) is the A row; its code word q of
-    // page kp holds tokens 16 j + 4 q + r (byte j, field r) = k index 16 q + 4 r + j
+    // 4. values U^T (128 channels x 16 columns): channel 16 mt + (l % 16) is the A row
     const float mnew = fmaxf(m, gm);
     const float sc = exp2_or_zero(m, mnew);
-    const float wg = exp2_or_zero(gm, mnew) * (1.0f / kS24);
+    const float eg = exp2_or_zero(gm, mnew);
+    const float wg = SC::TOK ? eg * Sg * (1.0f / kS24) : eg * (1.0f / kS24);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
       const int c = 16 * mt + (lane & 15);
       i32x4 cl = {0, 0, 0, 0}, cm = {0, 0, 0, 0}, ch = {0, 0, 0, 0};
 #pragma unroll
       for (int kp = 0; kp < 2; ++kp) {
-        const i32x4 av = unpack_codes(B.v[kp][4 * c + q]);
+        const i32x4 av = value_codes<SCHEME>(B.v[kp] + SC::VROW * c, q);
         cl = mfma_i8(av, uq[kp][0], cl);
         cm = mfma_i8(av, uq[kp][1], cm);
         ch = mfma_i8(av, uq[kp][2], ch);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int cc = 16 * mt + 4 * q + i;
-        const float sv = bf16_to_f32(B.meta[2 * D + cc]), zv = bf16_to_f32(B.meta[3 * D + cc]);
         const float U = limbs_value(ch, cm, cl, i);
-        o[mt][i] = fmaf(o[mt][i], sc, (wg * sv) * fmaf(-zv, Pf, U));
+        if constexpr (SC::TOK) {
+          o[mt][i] = fmaf(o[mt][i], sc, wg * (U - Zt));
+        } else {
+          const int cc = 16 * mt + 4 * q + i;
+          const float sv = bf16_to_f32(B.meta[2 * D + cc]), zv = bf16_to_f32(B.meta[3 * D + cc]);
+          o[mt][i] = fmaf(o[mt][i], sc, (wg * sv) * fmaf(-zv, Pf, U));
+        }
       }
     }
-    l = fmaf(l, sc, wg * Pf);
+    l = SC::TOK ? fmaf(l, sc, eg * Pf) : fmaf(l, sc, wg * Pf);
     m = mnew;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies of the next group
-    __syncthreads();                                    // everyone's copies landed, this group released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies of the next unit
+    __syncthreads();                                    // everyone's copies landed, this unit released
   }
 
-  // ---- un-rotate (O^T <- R_V O^T) unless values were never rotated; the k index of step ks maps to
-  // channel 32 ks + 4 q + e (e < 4) and 32 ks + 16 + 4 q + e - 4 (e >= 4): this lane's tiles 2 ks, 2 ks + 1
-  // (uniform branch: the matrix instructions read every lane's operands; a column that saw nothing holds
-  // zeros and passes through unchanged)
+  // ---- un-rotate unless values were never rotated (uniform branches: the matrix instructions read every
+  // lane's operands; a column that saw nothing holds zeros and passes through unchanged)
   f32x4 of[8];
   if (g.key_only) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) of[i] = o[i];
-  } else {
+  } else if (g.rotation == KVQ_ROT_DENSE) {
+    // O^T <- R_V O^T; the k index of step ks maps to channel 32 ks + 4 q + e (e < 4) and 32 ks + 16 + 4 q +
+    // e - 4 (e >= 4): this lane's tiles 2 ks, 2 ks + 1
     u32x4 oh[4], ol[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -420,6 +586,57 @@ __global__ __launch_bounds__(256) void prefill_int2_kernel(DecodeArgs a) {
       }
       of[mt] = acc;
     }
+  } else {
+    // randomized Hadamard ([SAW] eq. 1): o H_blk, then the signs and 1/sqrt(h).  Channel 16 mt + 4 q + i:
+    // butterflies over bits 0-1 within a lane's quad, bits 2-3 across lanes q (16 and 32 apart), bits 4-6
+    // across its tiles
+    float x[8][4];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[mt][i] = o[mt][i];
+#pragma unroll
+    for (int st = 0; st < 7; ++st) {  // stage hb = 2^st of the blocks' transform (uniform)
+      const int hb = 1 << st;
+      if (hb >= g.hblock) break;
+      if (hb < 4) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          float y[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) y[i] = (i & hb) ? x[mt][i ^ hb] - x[mt][i] : x[mt][i] + x[mt][i ^ hb];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[mt][i] = y[i];
+        }
+      } else if (hb < 16) {
+        const int lx = 16 * (hb >> 2);  // 16 or 32
+        const bool upper = (q & (hb >> 2)) != 0;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float other = __shfl_xor(x[mt][i], lx, 64);
+            x[mt][i] = upper ? other - x[mt][i] : x[mt][i] + other;
+          }
+      } else {
+        const int tb = hb >> 4;  // 1, 2 or 4
+        float y[8][4];
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) y[mt][i] = (mt & tb) ? x[mt ^ tb][i] - x[mt][i] : x[mt][i] + x[mt ^ tb][i];
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[mt][i] = y[mt][i];
+      }
+    }
+    const float hs = (float)g.hscale;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const float4 sg = *reinterpret_cast<const float4*>(a.rot_v + 16 * mt + 4 * q);
+      of[mt] = f32x4{x[mt][0] * sg.x * hs, x[mt][1] * sg.y * hs, x[mt][2] * sg.z * hs, x[mt][3] * sg.w * hs};
+    }
   }
   // ---- combine with the band and normalize; channels 16 mt + 4 q + i of this column
   if (!cvalid) return;
@@ -435,20 +652,31 @@ __global__ __launch_bounds__(256) void prefill_int2_kernel(DecodeArgs a) {
   }
 }
 
+template <int SCHEME>
+hipError_t launch_prefill_scheme(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  switch (a.g.gq) {
+    case 1: hipLaunchKernelGGL((prefill_kernel<1, SCHEME>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<2, SCHEME>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<4, SCHEME>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<8, SCHEME>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const DecodeArgs& a, int max_q, hipStream_t s) {
   const Geo& g = a.g;
   if (max_q <= 0) return hipSuccess;
   const dim3 grid((max_q * g.gq + kCols - 1) / kCols, g.n_kv, g.batch);
-  switch (g.gq) {
-    case 1: hipLaunchKernelGGL(prefill_int2_kernel<1>, grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(prefill_int2_kernel<2>, grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(prefill_int2_kernel<4>, grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(prefill_int2_kernel<8>, grid, dim3(256), 0, s, a); break;
+  switch (g.scheme) {
+    case KVQ_INT2_CHANNEL: return launch_prefill_scheme<KVQ_INT2_CHANNEL>(a, grid, s);
+    case KVQ_INT2_TOKEN: return launch_prefill_scheme<KVQ_INT2_TOKEN>(a, grid, s);
+    case KVQ_INT4_CHANNEL: return launch_prefill_scheme<KVQ_INT4_CHANNEL>(a, grid, s);
+    case KVQ_INT4_TOKEN: return launch_prefill_scheme<KVQ_INT4_TOKEN>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace kvq

@@ -311,15 +311,16 @@ int kv_decode_attn_noalloc(const kvq_config* cfg, const kvq_cache* cache, const 
    attend).  Call after kv_rotate_quant_write has appended the chunk: sequence b's chunk is its last
    n_b = cu_q[b+1] - cu_q[b] tokens (positions T_b - n_b .. T_b - 1, T_b = seq_lens[b] after the write),
    and its query at position p attends every cached token at a position <= p, as the cache holds it
-   (bf16 band tokens, dequantized groups).  Arithmetic: the decode's 16-bit fixed point for the groups
-   on the int8 matrix cores, bf16 hi/lo splits for the band and the un-rotation.
+   (bf16 band tokens and dequantized groups, or dequantized INT4 per-token pages, the chunk's own tokens
+   included).  Every scheme and rotation.  Arithmetic: 24-bit fixed point (three signed byte limbs) against
+   the codes on the int8 matrix cores, bf16 hi/lo splits for the band and the dense un-rotation, a fp32
+   Walsh-Hadamard transform for the randomized Hadamard's.
      q     [total_q][n_q_heads][128] fp32 or bf16 (dtype), device; rows ordered by sequence then query.
      cu_q  [batch + 1] int32 prefix sums of n_b, device; total_q = cu_q[batch], max_q = max n_b (host).
      out   [total_q][n_q_heads][128] fp32, device, written for every query row.
      workspace of kvq_prefill_workspace_bytes(cfg, total_q) bytes (rotated and band-frame queries).
-   Built for KVQ_INT2_CHANNEL with the dense rotation (key-only rotation included); other schemes return
-   KVQ_EUNSUPPORTED.  KVQ_ENOSPACE for a small workspace; n_b must not exceed T_b (not checked on the
-   device: queries beyond the cache attend nothing and output zeros). */
+   KVQ_ENOSPACE for a small workspace; n_b must not exceed T_b (not checked on the device: queries beyond
+   the cache attend nothing and output zeros). */
 size_t kvq_prefill_workspace_bytes(const kvq_config* cfg, int32_t total_q);
 int kv_prefill_attn(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t dtype, const int32_t* cu_q,
                     int32_t total_q, int32_t max_q, float* out, void* workspace, size_t ws_bytes, hipStream_t stream);

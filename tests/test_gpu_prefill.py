@@ -1,14 +1,16 @@
 """GPU parity of prefill attention over the quantized history ([NOVA] §3 "Long context": chunked prefill;
 [SAW] prefill stage): after a chunk is written, each of its queries attends every cached token at a position
 not after its own, as the cache holds it.  Against the oracle's causal attention on the same seeded inputs,
-within the 2e-3 bar; a one-query chunk also equals the decode step's output.
+within the 2e-3 bar, for every scheme (INT2 per channel and per token, INT4 per channel over 128-token
+groups with the bf16 band; INT4 per token over page pairs, randomized Hadamard of block 128 or 16); a
+one-query chunk also equals the decode step's output.
 """
 import numpy as np
 import pytest
 
 import oracle as O
 import synth
-from kvq_cases import TOL, _say, build_cache, run_decode, source_of, source_torch
+from kvq_cases import GROUPED, TOL, _say, build_cache, run_decode, source_of, source_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -49,8 +51,12 @@ def _check(bc, qs, cu, out, heads, rows=None):
         k, v = source_of(wl, b, T)
         for h in heads:
             qh = qs[cu[b] + sel][:, h * wl.gq:(h + 1) * wl.gq]
-            want = O.prefill_int2(qh, T - n + sel, k[:, h], v[:, h], T, wl.n_sink, wl.n_recent, wl.clip_k, wl.clip_v,
-                                  bc.rk, bc.rv)
+            if wl.scheme in GROUPED:
+                want = O.prefill_int2(qh, T - n + sel, k[:, h], v[:, h], T, wl.n_sink, wl.n_recent, wl.clip_k,
+                                      wl.clip_v, bc.rk, bc.rv, axis=GROUPED[wl.scheme])
+            else:
+                want = O.prefill_int4(qh, T - n + sel, k[:, h], v[:, h], T, bc.rk.astype(np.int8),
+                                      None if bc.rv is None else bc.rv.astype(np.int8), block=wl.hadamard_block)
             got = out[cu[b] + sel][:, h * wl.gq:(h + 1) * wl.gq]
             assert np.isfinite(got).all(), f"b={b} h={h}: non-finite output"
             err = np.abs(got - want).max()
@@ -101,3 +107,68 @@ def test_prefill_gqa_32k_sampled(K):
     qs, cu, out = _prefill(K, bc, [4096])
     assert np.isfinite(out).all()
     _check(bc, qs, cu, out, [0, 7], rows=[0, 1, 127, 128, 1000, 2047, 4095])
+
+
+# ------------------------------------------------------------------------- the other schemes
+
+
+def _wl(name, **kw):
+    return synth.scaled(synth.WORKLOADS[name], **kw)
+
+
+SCHEME_CASES = [
+    # (label, workload, lens, chunk, heads)
+    ("int2 per token, GQ 4", _wl("gqa_b1_32k", scheme="int2_token"), [700, 390], [64, 130], [0, 5]),
+    ("int2 per token, GQ 8", _wl("long_b4_131k", scheme="int2_token", batch=2), [900, 520], [70, 129], [1, 6]),
+    ("int4 per channel, GQ 4", _wl("gqa_b1_32k", scheme="int4_channel"), [700, 1100], [64, 200], [2, 7]),
+    ("int4 per channel, GQ 8", _wl("long_b4_131k", scheme="int4_channel", batch=2), [900, 520], [70, 129], [3]),
+    ("int4 per token, GQ 4", _wl("saw_int4_b16_16k", batch=3), [700, 333, 1025], [64, 129, 200], [0, 6]),
+    ("int4 per token, GQ 4, Hadamard block 16", _wl("saw_int4_b16_16k", batch=2, hadamard_block=16), [640, 97],
+     [128, 97], [4]),
+    ("int4 per token, GQ 8", _wl("saw_int4_b16_16k", batch=2, n_q_heads=64), [515, 190], [131, 63], [1, 7]),
+    ("int4 per token, GQ 1", _wl("saw_int4_b16_16k", batch=1, n_q_heads=8), [300], [300], [2]),
+]
+
+
+@pytest.mark.parametrize("label,wl,lens,chunk,heads", SCHEME_CASES, ids=[c[0] for c in SCHEME_CASES])
+def test_prefill_every_scheme(K, label, wl, lens, chunk, heads):
+    _say(f"prefill {label}: lens={lens} chunk={chunk}")
+    bc = build_cache(K, wl, lens, chunk=None)
+    qs, cu, out = _prefill(K, bc, chunk)
+    _check(bc, qs, cu, out, heads)
+
+
+@pytest.mark.parametrize("name,kw", [("gqa_b1_32k", dict(scheme="int2_token")),
+                                     ("gqa_b1_32k", dict(scheme="int4_channel")),
+                                     ("saw_int4_b16_16k", dict(batch=2))])
+def test_prefill_key_only_every_scheme(K, name, kw):
+    wl = _wl(name, key_only=True, **kw)
+    _say(f"prefill {wl.scheme}, key-only rotation")
+    bc = build_cache(K, wl, [800, 300][:wl.batch] if wl.batch > 1 else [800], chunk=None)
+    qs, cu, out = _prefill(K, bc, [90, 45][:len(bc.lens)])
+    _check(bc, qs, cu, out, [3])
+
+
+@pytest.mark.parametrize("name,kw", [("gqa_b1_32k", dict(scheme="int2_token")),
+                                     ("gqa_b1_32k", dict(scheme="int4_channel")),
+                                     ("saw_int4_b16_16k", dict(batch=2))])
+def test_prefill_of_one_query_is_the_decode_step_every_scheme(K, name, kw):
+    wl = _wl(name, **kw)
+    lens = [1500, 333]
+    bc = build_cache(K, wl, lens)
+    qs, cu, out = _prefill(K, bc, [1, 1])
+    dec = run_decode(K, bc, qs)
+    d = np.abs(out - dec).max()
+    _say(f"prefill {wl.scheme}: one query vs decode {d:.2e}")
+    assert d <= TOL
+    _check(bc, qs, cu, out, range(8))
+
+
+def test_prefill_saw_int4_full_sampled(K):
+    """The INT4 workload at full length: 16384 tokens, the last 8192 a chunk; sampled rows of 2 sequences."""
+    wl = _wl("saw_int4_b16_16k", batch=2)
+    _say("prefill saw_int4: 8192 + 8192 chunk")
+    bc = build_cache(K, wl, [16384, 16384], chunk=8192)
+    qs, cu, out = _prefill(K, bc, [8192, 8192])
+    assert np.isfinite(out).all()
+    _check(bc, qs, cu, out, [0, 5], rows=[0, 1, 63, 64, 127, 128, 4097, 8191])
