@@ -23,12 +23,12 @@ _FUTURES: Dict[str, object] = {}
 
 
 def n_workers() -> int:
-    """Worker count: the cores this process may use, less two for the test process, at most 12."""
+    """Worker count: the cores this process may use, less four for the test process, at most 8."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
-    return max(1, min(12, n - 2))
+    return max(1, min(8, n - 4))
 
 
 def _ready() -> int:

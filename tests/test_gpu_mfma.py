@@ -5,7 +5,7 @@ oracle on the same seeded caches (bar 2e-3), and against the fp32 decode of the 
 Cases span every GQA ratio the kernel lays out differently (1, 2 and 4: four matrix rows per head; 8: two
 rows per head plus a tile of top limbs), automatic and explicit splits (every wave walks a chunk of its
 own; with more chunks than one round of work-groups holds, several in a row), ragged and empty sequences,
-and appends that demote groups.  The full-size shapes are in test_gpu_fullsize.py.
+and appends that demote groups.  The full-size shapes are in test_gpu_wide_parity.py.
 """
 import numpy as np
 import pytest
