@@ -93,7 +93,8 @@ _lib_debug_unpack = _sig("kvq_debug_unpack", ctypes.c_int, _CFG, _CACHE, ctypes.
 _lib_decode = _sig("kv_decode_attn", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P, ctypes.c_int32, _P,
                    ctypes.c_size_t, _P)
 class DecodeShape(ctypes.Structure):
-    _fields_ = [("chunk_units", ctypes.c_int32), ("n_chunks", ctypes.c_int32), ("span", ctypes.c_int32),
+    _fields_ = [("chunk_units", ctypes.c_int32), ("n_chunks", ctypes.c_int32), ("walks", ctypes.c_int32),
+                ("span", ctypes.c_int32),
                 ("splitk_workgroups", ctypes.c_int32), ("band_first", ctypes.c_int32),
                 ("matrix_cores", ctypes.c_int32)]
 

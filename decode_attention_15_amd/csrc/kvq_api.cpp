@@ -117,25 +117,27 @@ int chunk_units(const kvq_config* c, int batch, int max_seq_len) {
   return per;
 }
 
-// Chunks one wave of the matrix-core decode walks.  Automatic chunks are already sized to fill the GPU in one
-// round (one chunk per wave).  An explicit split fixes the chunks the merge combines, which can be many more
-// than the waves of one round: a wave then walks consecutive chunks, its copies running on across their
-// boundaries, with as many chunks per walk as fill the work-group slots of one round, and at most 32
-// groups (pages) per walk.
-int walk_span(const kvq_config* c, int batch, int n_chunks, int per) {
-  if (c->split_tokens <= 0 || n_chunks <= 1) return 1;
+// Walks per (sequence, head quad) — or per (sequence, kv head) when the kv heads do not come in fours — of
+// the matrix-core decode; walk w of n chunks takes chunks w n / walks .. (w + 1) n / walks - 1.  Automatic
+// chunks are already sized to fill the GPU in one round: one chunk per walk.  An explicit split fixes the
+// chunks the merge combines, which can be many more than the waves of one round: then as many walks as fill
+// the work-group slots of one round (a wave walks consecutive chunks, its copies running on across their
+// boundaries), with at most 32 groups (pages) per walk.
+int walks_of(const kvq_config* c, int batch, int n_chunks, int per) {
+  if (c->split_tokens <= 0 || n_chunks <= 1) return n_chunks < 1 ? 1 : n_chunks;
   const long long pairs = (long long)batch * c->n_kv_heads;
   long long slots = 256LL * wgs_per_cu(c) - (is_grouped(c->scheme) ? pairs : 0);  // chunk work-groups per round
   if (slots < 256) slots = 256;
-  // walks one work-group takes, and the rows of work-groups (head quads: one row per (sequence, quad))
+  // rows of work-groups (head quads: one row per (sequence, quad), one walk per work-group; otherwise one row per
+  // (sequence, kv head), four walks per work-group)
   const bool quads = c->n_kv_heads % 4 == 0;
   const long long rows = quads ? pairs / 4 : pairs, walks_per_wg = quads ? 1 : 4;
-  long long per_row = slots / rows;  // work-groups per row
-  if (per_row < 1) per_row = 1;
-  long long span = (n_chunks + per_row * walks_per_wg - 1) / (per_row * walks_per_wg);
-  const long long cap = 32 / per > 1 ? 32 / per : 1;
-  if (span > cap) span = cap;
-  return (int)(span < 1 ? 1 : span);
+  long long walks = slots / rows * walks_per_wg;
+  const long long max_chunks = 32 / per > 1 ? 32 / per : 1;    // chunks per walk
+  const long long min_walks = (n_chunks + max_chunks - 1) / max_chunks;
+  if (walks < min_walks) walks = min_walks;
+  if (walks > n_chunks) walks = n_chunks;
+  return (int)(walks < 1 ? 1 : walks);
 }
 
 int max_chunks_of(const kvq_config* c, int max_seq_len, int per) {
@@ -150,10 +152,10 @@ void set_decode_shape(const kvq_config* c, int max_seq_len, Geo& g) {
   const int per = chunk_units(c, g.batch, max_seq_len);
   g.gpc = per;
   g.n_units = 1 + max_chunks_of(c, max_seq_len, per);
-  // the matrix-core decode: every wave walks `span` chunks of its own; the fp32 decode: one chunk per work-group
+  // the matrix-core decode: every wave walks chunks of its own; the fp32 decode: one chunk per work-group
   const bool mfma = uses_mfma(c);
   g.wave_chunks = mfma ? 1 : 0;
-  g.span = mfma ? walk_span(c, g.batch, g.n_units - 1, per) : 1;
+  g.walks = mfma ? walks_of(c, g.batch, g.n_units - 1, per) : 1;
   // band work-groups first when the split-K launch takes more than one round of work-groups (see the grid)
   g.band_first = splitk_wgs(g) > 256LL * wgs_per_cu(c) ? 1 : 0;
 }
@@ -443,7 +445,8 @@ int kvq_decode_shape_of(const kvq_config* cfg, int32_t batch, int32_t max_seq_le
   set_decode_shape(cfg, max_seq_len, g);
   out->chunk_units = g.gpc;
   out->n_chunks = g.n_units - 1;
-  out->span = g.span;
+  out->walks = g.wave_chunks ? g.walks : out->n_chunks;
+  out->span = g.wave_chunks ? (out->n_chunks + g.walks - 1) / g.walks : 1;
   out->splitk_workgroups = splitk_wgs(g);
   out->band_first = g.band_first;
   out->matrix_cores = g.wave_chunks;

@@ -749,7 +749,7 @@ __host__ __device__ constexpr int mf_key_channel_c4(int Q) {
 }
 
 template <int GQ, bool TOK, int BITS, typename Lds>
-__device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
+__device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T, int c0, int c1) {
   constexpr int LG = HeadLog2<GQ>::v;
   constexpr int LPH = 64 >> LG;        // lanes per head in the alpha step
   constexpr int NCH = 2 * GQ;          // key positions per lane in the alpha step
@@ -764,12 +764,11 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ng = n_groups_of(T, g.S0, g.W);
-  // this wave walks chunks chunk .. chunk + span - 1 (groups g_first .. g_end - 1), storing a partial per chunk
-  const int g_first = chunk * g.gpc;
-  int g_end = g_first + g.span * g.gpc;
+  // this wave walks chunks c0 .. c1 - 1 (groups g_first .. g_end - 1), storing a partial per chunk
+  const int g_first = c0 * g.gpc;
+  int g_end = c1 * g.gpc;
   if (g_end > ng) g_end = ng;
   if (g_end > g.max_pages / 2) g_end = g.max_pages / 2;            // never index past the page-table row
-  if (g_end > (g.n_units - 1) * g.gpc) g_end = (g.n_units - 1) * g.gpc;  // chunks past the launch bound: none
   MfmaWave<GQ, KU>& W = L.mf.w[wave];
   const int q4 = lane >> 4, c = lane & 15;
 
@@ -889,6 +888,8 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     issue_v(p0);
     if (g_first + 1 < g_end) pv = pair_v(g_first + 1);
   }
+  // the partial of chunk ci (per channel, o and l carry the weights' factor S), then a fresh softmax state;
+  // every partial a merge reads is written, chunks past the length have none
   // the partial of chunk ci (per channel, o and l carry the weights' factor S), then a fresh softmax state;
   // every partial a merge reads is written, chunks past the length have none
   auto store_partial = [&](int ci) {
@@ -1181,7 +1182,7 @@ __host__ __device__ constexpr int mf_key_channel4(int Q) {
 }
 
 template <int GQ, typename Lds>
-__device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
+__device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T, int c0, int c1) {
   constexpr int LG = HeadLog2<GQ>::v;
   constexpr int LPH = 64 >> LG;
   constexpr int NCH = 2 * GQ;
@@ -1195,14 +1196,13 @@ __device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int npages = (T + PAGE - 1) / PAGE;
   const int npairs = (npages + 1) / 2;
-  // this wave walks chunks chunk .. chunk + span - 1 (an even number of pages each: page pairs pb .. pe - 1),
-  // storing a partial per chunk
+  // this wave walks chunks c0 .. c1 - 1 (an even number of pages each: page pairs pb .. pe - 1), storing a
+  // partial per chunk
   const int ppc = g.gpc / 2;  // page pairs per chunk
-  const int pb = chunk * ppc;
-  int pe = pb + g.span * ppc;
+  const int pb = c0 * ppc;
+  int pe = c1 * ppc;
   if (pe > npairs) pe = npairs;
   if (2 * pe > g.max_pages + 1) pe = (g.max_pages + 1) / 2;          // never index past the page-table row
-  if (pe > (g.n_units - 1) * ppc) pe = (g.n_units - 1) * ppc;  // chunks past the launch bound: none
   MfmaWave<GQ, 512>& W = L.mf.w[wave];
   const int q4 = lane >> 4, c = lane & 15;
 
@@ -1309,6 +1309,8 @@ __device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int
     issue_v(p0);
     if (pb + 1 < pe) pv = pages_v(pb + 1);
   }
+  // the partial of chunk ci, then a fresh softmax state; every partial a merge reads is written, chunks past
+  // the length have none
   // the partial of chunk ci, then a fresh softmax state; every partial a merge reads is written, chunks past
   // the length have none
   auto store_partial = [&](int ci) {
@@ -1486,22 +1488,29 @@ __device__ inline void splitk_unit_of(const Geo& g, int& unit, int& h, int& b) {
   h = pair % g.n_kv;
   b = pair / g.n_kv;
 }
-// matrix-core decode, chunk work-group i: its sequence, and this wave's kv head and first chunk (it walks
-// chunks chunk .. chunk + span - 1); returns the work-group's first chunk (every wave's at least that)
-__device__ inline int wave_chunk_of(const Geo& g, int i, int wave, int& b, int& h, int& chunk) {
+// matrix-core decode, chunk work-group i: its sequence, and this wave's kv head and walk (chunks c0 .. c1 - 1,
+// empty past the walks); returns the work-group's first chunk (every wave's at least that)
+__device__ inline int wave_chunk_of(const Geo& g, int i, int wave, int& b, int& h, int& c0, int& c1) {
   if (splitk_head_quads(g)) {
     const int quads = g.n_kv / 4, per = g.batch * quads;
     const int r = i % per;
     b = r / quads;
     h = 4 * (r % quads) + wave;
-    chunk = g.span * (i / per);
-    return chunk;
+    walk_chunks(g, i / per, &c0, &c1);
+    return c0;
   }
   const int pairs = g.batch * g.n_kv, pair = i % pairs;
   b = pair / g.n_kv;
   h = pair % g.n_kv;
-  chunk = g.span * (4 * (i / pairs) + wave);
-  return g.span * 4 * (i / pairs);
+  const int w = 4 * (i / pairs) + wave;
+  int first, unused;
+  walk_chunks(g, 4 * (i / pairs), &first, &unused);
+  if (w < g.walks) {
+    walk_chunks(g, w, &c0, &c1);
+  } else {
+    c0 = c1 = g.n_units - 1;
+  }
+  return first;
 }
 
 // Matrix-core launch of the grouped schemes.  Work-groups per CU, as the LDS allows (160 KB): 2-bit codes
@@ -1516,13 +1525,13 @@ __global__ __launch_bounds__(kThreads, GQ <= 4 ? (BITS == 2 ? 3 : 2) : (BITS == 
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int b, h, chunk;
-  const int first = wave_chunk_of(g, i, wave, b, h, chunk);
+  int b, h, c0, c1;
+  const int first = wave_chunk_of(g, i, wave, b, h, c0, c1);
   const int T = a.seq_lens[b];
   int n_chunks = (n_groups_of(T, g.S0, g.W) + g.gpc - 1) / g.gpc;
   if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;  // lengths beyond the launch bound are cut
   if (first >= n_chunks) return;                           // uniform over the work-group
-  int2_unit_mfma<GQ, TOK, BITS>(L, a, b, h, T, chunk);
+  int2_unit_mfma<GQ, TOK, BITS>(L, a, b, h, T, c0, c1);
 }
 
 // Matrix-core INT4 per-token launch (page pairs; no band: the band work-groups store an empty partial).
@@ -1541,13 +1550,13 @@ __global__ __launch_bounds__(kThreads, GQ <= 4 ? 2 : 1) void decode_mfma4_kernel
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int b, h, chunk;
-  const int first = wave_chunk_of(g, i, wave, b, h, chunk);
+  int b, h, c0, c1;
+  const int first = wave_chunk_of(g, i, wave, b, h, c0, c1);
   const int T = a.seq_lens[b];
   int n_chunks = ((T + PAGE - 1) / PAGE + g.gpc - 1) / g.gpc;
   if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;  // lengths beyond the launch bound are cut
   if (first >= n_chunks) return;                           // uniform over the work-group
-  int4tok_unit_mfma<GQ>(L, a, b, h, T, chunk);
+  int4tok_unit_mfma<GQ>(L, a, b, h, T, c0, c1);
 }
 
 // fp32 decode (exact arithmetic on the codes; the cross-check of the matrix-core decode): the four waves of

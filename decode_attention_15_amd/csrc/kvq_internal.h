@@ -54,7 +54,8 @@ struct Geo {
   int gpc;          // groups (grouped schemes) or pages (INT4 per token) per decode chunk
   int n_units;      // decode partial units per (seq, q head): 1 band unit + chunks
   int wave_chunks;  // 1: each wave of a work-group walks chunks of its own and stores their partials
-  int span;         // matrix-core decode: consecutive chunks one wave walks (a partial stored per chunk)
+  int walks;        // matrix-core decode: walks per (sequence, head quad) or per (sequence, kv head); walk w
+                    // of n chunks takes chunks w n / walks .. (w + 1) n / walks - 1 (a partial per chunk)
   int band_first;   // 1: the split-K grid starts with its band work-groups (launches of more than one round)
 };
 
@@ -68,18 +69,23 @@ __host__ __device__ inline int n_groups_of(int T, int S0, int W) {
 }
 
 // Chunk work-groups of the split-K grid (the band work-groups, one per (sequence, kv head), come on top):
-//  - matrix-core decode, n_kv a multiple of 4 (head quads): each walks `span` chunks of four kv heads of a
-//    sequence, wave w taking head 4 hq + w, so that the work-group's copies of a page read four neighbouring
-//    head blocks together;
-//  - matrix-core decode otherwise: four consecutive walks of `span` chunks of one (sequence, kv head), one
-//    per wave;
+//  - matrix-core decode, n_kv a multiple of 4 (head quads): one walk of four kv heads of a sequence, wave w
+//    taking head 4 hq + w, so that the work-group's copies of a page read four neighbouring head blocks
+//    together;
+//  - matrix-core decode otherwise: four consecutive walks of one (sequence, kv head), one per wave;
 //  - fp32 decode: one chunk of one (sequence, kv head), shared by the four waves.
 __host__ __device__ inline bool splitk_head_quads(const Geo& g) { return g.wave_chunks && g.n_kv % 4 == 0; }
 __host__ __device__ inline int splitk_chunk_wgs(const Geo& g) {
   const int nc = g.n_units - 1;
   if (!g.wave_chunks) return g.batch * g.n_kv * nc;
-  if (splitk_head_quads(g)) return g.batch * (g.n_kv / 4) * ((nc + g.span - 1) / g.span);
-  return g.batch * g.n_kv * ((nc + 4 * g.span - 1) / (4 * g.span));
+  if (splitk_head_quads(g)) return g.batch * (g.n_kv / 4) * g.walks;
+  return g.batch * g.n_kv * ((g.walks + 3) / 4);
+}
+// the chunks of walk w (of g.walks) of a sequence's n_units - 1 chunks: [*c0, *c1)
+__host__ __device__ inline void walk_chunks(const Geo& g, int w, int* c0, int* c1) {
+  const long long nc = g.n_units - 1;
+  *c0 = (int)(w * nc / g.walks);
+  *c1 = (int)((w + 1) * nc / g.walks);
 }
 __host__ __device__ inline int splitk_wgs(const Geo& g) { return splitk_chunk_wgs(g) + g.batch * g.n_kv; }
 

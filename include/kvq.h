@@ -281,12 +281,15 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
    work): the quantized history of a sequence is cut into chunks of chunk_units groups of 128 tokens (grouped
    schemes) or pages of 64 tokens (INT4 per token), each chunk giving one softmax partial (m, l, o) that the
    merge combines ([OSCAR] §3.4.5 step 4, FlashDecoding; [NOVA] App. B.5, two-stage split-KV).  An explicit
-   split_tokens fixes the chunks; 0 lets the library size them to the GPU.  On the matrix cores one wave walks
-   `span` consecutive chunks.  Errors: KVQ_EINVAL (null out, batch < 1, negative length), config errors. */
+   split_tokens fixes the chunks; 0 lets the library size them to the GPU.  On the matrix cores a sequence's
+   chunks are split into `walks` runs of consecutive chunks (per head quad, or per kv head when the kv heads
+   do not come in fours), one wave walking each run.  Errors: KVQ_EINVAL (null out, batch < 1, negative
+   length), config errors. */
 typedef struct kvq_decode_shape {
   int32_t chunk_units;        /* groups (grouped schemes) or pages (INT4 per token) per chunk */
   int32_t n_chunks;           /* chunks of a sequence of max_seq_len tokens */
-  int32_t span;               /* chunks one wave walks in a row (1 on the fp32 decode) */
+  int32_t walks;              /* runs of chunks per sequence and head quad (or kv head); n_chunks on the fp32 decode */
+  int32_t span;               /* most chunks in one run (1 on the fp32 decode) */
   int32_t splitk_workgroups;  /* work-groups of the split-K launch, band work-groups included */
   int32_t band_first;         /* 1: the launch starts with its band work-groups */
   int32_t matrix_cores;       /* 1: the matrix-core decode runs, 0: the fp32 decode */

@@ -34,6 +34,11 @@ def n_workers() -> int:
 def _ready() -> int:
     import oracle  # noqa: F401  (the imports a job needs, done once per worker)
     import synth  # noqa: F401
+    # the workers yield to the test process (which runs its own oracle work with a full BLAS pool) and use one
+    # BLAS thread each
+    os.nice(10)
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
     time.sleep(0.5)  # busy while the other workers start, so that every submission starts a process of its own
     return os.getpid()
 

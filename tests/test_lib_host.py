@@ -320,22 +320,27 @@ def test_decode_shape_chunks_and_walks():
     cfg = K.make_config(8, 32)
     sh = K.decode_shape(cfg, 32, 32768)
     ng = 255  # groups of a 32768-token sequence with 4 sink and 128 recent tokens
-    assert sh["matrix_cores"] == 1 and sh["span"] == 1
+    assert sh["matrix_cores"] == 1 and sh["span"] == 1 and sh["walks"] == sh["n_chunks"]
     assert sh["n_chunks"] == -(-ng // sh["chunk_units"]) and 4 <= sh["chunk_units"] <= 32
     assert sh["splitk_workgroups"] == 32 * 2 * sh["n_chunks"] + 256 <= 256 * 3 and sh["band_first"] == 0
-    # 512-token split at 4 x 131k, GQA 8: 256 chunks of 4 groups, walks of 5 chunks fit one round (2 per CU)
+    # 512-token split at 4 x 131k, GQA 8: 256 chunks of 4 groups in 60 walks of 4 or 5 chunks per (sequence,
+    # head quad), filling the 512 slots of one round (2 per CU) with the 32 band work-groups
     cfg8 = K.make_config(8, 64, n_recent=256, split_tokens=512)
     sh = K.decode_shape(cfg8, 4, 131072)
-    assert sh["chunk_units"] == 4 and sh["n_chunks"] == 256 and sh["span"] == 5
-    assert sh["splitk_workgroups"] == 4 * 2 * 52 + 32 <= 512 and sh["band_first"] == 0
+    assert sh["chunk_units"] == 4 and sh["n_chunks"] == 256 and sh["walks"] == 60 and sh["span"] == 5
+    assert sh["splitk_workgroups"] == 4 * 2 * 60 + 32 == 512 and sh["band_first"] == 0
     # the fp32 decode walks one chunk per work-group
     cfg.decode_impl = K.DECODE_F32
     sh = K.decode_shape(cfg, 32, 32768)
-    assert sh["matrix_cores"] == 0 and sh["span"] == 1
+    assert sh["matrix_cores"] == 0 and sh["span"] == 1 and sh["walks"] == sh["n_chunks"]
     assert sh["splitk_workgroups"] == 256 * sh["n_chunks"] + 256
     # explicit split at batch 32: 64 chunks per sequence, 8 in a row (32 groups)
     cfg = K.make_config(8, 32, split_tokens=512)
     sh = K.decode_shape(cfg, 32, 32768)
-    assert sh["n_chunks"] == 64 and sh["span"] == 8 and sh["splitk_workgroups"] == 64 * 8 + 256
+    assert sh["n_chunks"] == 64 and sh["walks"] == 8 and sh["span"] == 8 and sh["splitk_workgroups"] == 64 * 8 + 256
+    # two kv heads (no head quads): four walks per work-group, the last work-group of a row partly idle
+    cfg2 = K.make_config(2, 8, split_tokens=512)
+    sh = K.decode_shape(cfg2, 64, 12000)
+    assert sh["walks"] >= 2 and sh["splitk_workgroups"] == 128 * (-(-sh["walks"] // 4)) + 128
     with pytest.raises(K.KvqError):
         K.decode_shape(cfg, 0, 100)
