@@ -271,7 +271,7 @@ def write_bench(args, K, synth, np, torch):
         cache.seq_lens.zero_()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        K.kv_rotate_quant_write(cache, k, v, cu, n)
+        K.kv_rotate_quant_write(cache, k, v, cu, n, max_len=n)
         e1.record()
         e1.synchronize()
         if i >= args.warmup:
@@ -323,7 +323,7 @@ def prefill_bench(args, K, synth, np, torch):
         cu = torch.from_numpy(np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)).to(dev)
         k = torch.randn((int(cnt.sum()), n_kv, 128), generator=gen, device=dev).to(torch.bfloat16)
         v = torch.randn((int(cnt.sum()), n_kv, 128), generator=gen, device=dev).to(torch.bfloat16)
-        K.kv_rotate_quant_write(cache, k, v, cu, int(cnt.max()))
+        K.kv_rotate_quant_write(cache, k, v, cu, int(cnt.max()), max_len=int(lens.max()))
         done += cnt
     chunk = np.minimum(lens, n)
     total = int(chunk.sum())
