@@ -643,29 +643,10 @@ __device__ __forceinline__ void codes_i8_pair(uint32_t w0, uint32_t w1, mf_i32x4
                 (int)((uint32_t)(s6 >> 32) & M)};
 }
 __device__ __forceinline__ mf_i32x4 u4_i32x4(uint4 v) { return mf_i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}; }
-// Three signed byte limbs.  An operand x with |x| <= S is rounded to an integer a = lo + 256 mid + 65536 hi
-// (lo, mid in [-128, 127], hi in [-64, 63]) by one FMA with the magic addend 2^23 + 0x408080: the result
-// lies in [2^23, 2^24), where fp32 spacing is 1, so it is the exact 2^23 + 0x408080 + rint(x) (ties to even)
-// and the low 23 bits of its encoding are y = a + 0x408080 in [0, 2^23).  Bytes 0 and 1 of y less 128 are
-// lo and mid (xor 0x80 as signed bytes); byte 2 (7 bits) less 64 is hi.  The full scale S keeps every int32
-// sum of 128 products with codes exact: 128 * 3 * 4,000,000 and 128 * 15 * 1,000,000 are below 2^31.
-constexpr float kRound3 = 12615808.0f;  // 2^23 + 0x408080
 template <int BITS>
 struct Limb3 {
   static constexpr float S = BITS == 2 ? 4000000.0f : 1000000.0f;
 };
-__device__ __forceinline__ void limbs3(float e0, float e1, float e2, float e3, uint32_t& lo, uint32_t& mid,
-                                       uint32_t& hi) {
-  const uint32_t u0 = __float_as_uint(e0), u1 = __float_as_uint(e1), u2 = __float_as_uint(e2), u3 = __float_as_uint(e3);
-  const uint32_t a01 = __builtin_amdgcn_perm(u1, u0, 0x05010400u);  // u0.b0 u1.b0 u0.b1 u1.b1
-  const uint32_t a23 = __builtin_amdgcn_perm(u3, u2, 0x05010400u);
-  const uint32_t h01 = __builtin_amdgcn_perm(u1, u0, 0x06020602u);  // u0.b2 u1.b2 (twice)
-  const uint32_t h23 = __builtin_amdgcn_perm(u3, u2, 0x06020602u);
-  lo = __builtin_amdgcn_perm(a23, a01, 0x05040100u) ^ 0x80808080u;
-  mid = __builtin_amdgcn_perm(a23, a01, 0x07060302u) ^ 0x80808080u;
-  const uint32_t y = __builtin_amdgcn_perm(h23, h01, 0x05040100u) ^ 0x40404040u;
-  hi = y | ((y & 0x40404040u) << 1);  // bit 6 extended into bit 7: y2 - 64 as a signed byte
-}
 // A head's value lo + 256 mid + 65536 hi from the matrix-core limb sums of this lane (two's complement; the
 // true value fits in int32).  Rows 4 q + r of a result tile: up to GQ 4 head q with limb r (r < 3); at GQ 8
 // heads 2 q + r / 2 with limb r % 2, the top limbs in a second tile at rows 4 q + 2 e.

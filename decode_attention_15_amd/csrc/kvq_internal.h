@@ -108,6 +108,27 @@ __device__ inline uint16_t f32_to_bf16_rne(float x) {
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
+// Three signed byte limbs.  An operand x with |x| <= S is rounded to an integer a = lo + 256 mid + 65536 hi
+// (lo, mid in [-128, 127], hi in [-64, 63]) by one FMA with the magic addend 2^23 + 0x408080: the result
+// lies in [2^23, 2^24), where fp32 spacing is 1, so it is the exact 2^23 + 0x408080 + rint(x) (ties to even)
+// and the low 23 bits of its encoding are y = a + 0x408080 in [0, 2^23).  Bytes 0 and 1 of y less 128 are
+// lo and mid (xor 0x80 as signed bytes); byte 2 (7 bits) less 64 is hi.  A full scale S of 4,000,000 against
+// 2-bit codes (1,000,000 against 4-bit codes) keeps every int32 sum of 128 products with codes exact:
+// 128 * 3 * 4,000,000 and 128 * 15 * 1,000,000 are below 2^31.
+constexpr float kRound3 = 12615808.0f;  // 2^23 + 0x408080
+__device__ __forceinline__ void limbs3(float e0, float e1, float e2, float e3, uint32_t& lo, uint32_t& mid,
+                                       uint32_t& hi) {
+  const uint32_t u0 = __float_as_uint(e0), u1 = __float_as_uint(e1), u2 = __float_as_uint(e2), u3 = __float_as_uint(e3);
+  const uint32_t a01 = __builtin_amdgcn_perm(u1, u0, 0x05010400u);  // u0.b0 u1.b0 u0.b1 u1.b1
+  const uint32_t a23 = __builtin_amdgcn_perm(u3, u2, 0x05010400u);
+  const uint32_t h01 = __builtin_amdgcn_perm(u1, u0, 0x06020602u);  // u0.b2 u1.b2 (twice)
+  const uint32_t h23 = __builtin_amdgcn_perm(u3, u2, 0x06020602u);
+  lo = __builtin_amdgcn_perm(a23, a01, 0x05040100u) ^ 0x80808080u;
+  mid = __builtin_amdgcn_perm(a23, a01, 0x07060302u) ^ 0x80808080u;
+  const uint32_t y = __builtin_amdgcn_perm(h23, h01, 0x05040100u) ^ 0x40404040u;
+  hi = y | ((y & 0x40404040u) << 1);  // bit 6 extended into bit 7: y2 - 64 as a signed byte
+}
+
 // ---- launchers implemented in kvq_write.hip / kvq_decode.hip ----
 struct WriteArgs {
   Geo g;

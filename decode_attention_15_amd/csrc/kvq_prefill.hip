@@ -7,8 +7,9 @@
 // the rotated frame (query rotated once, output un-rotated once) as in the decode.
 //
 // Contractions run on the matrix cores:
-//  - quantized tokens on v_mfma_i32_16x16x64_i8 in 24-bit fixed point, three signed byte limbs (65536 hi +
-//    256 mid + lo) against the 2- or 4-bit codes (exact int32 sums per limb), full scale S = 8355584.
+//  - quantized tokens on v_mfma_i32_16x16x64_i8 in fixed point, three signed byte limbs (65536 hi + 256 mid +
+//    lo, split by one FMA with a magic addend) against the 2- or 4-bit codes, full scale S = 4,000,000 (2-bit
+//    codes) or 1,000,000 (4-bit codes), so that the limbs' int32 sums recombine exactly in int32.
 //    Per channel: per (query head, group) the key-side operand a = rint(alpha S / max|alpha|), alpha = q~ s,
 //    and the weights u = rint(S p), p = 2^(logit - group max).  Per token: the key-side operand is the
 //    rotated query itself (a = rint(q~ S / max|q~|), once per query), logit_t = A s_t (D_t - z_t sum_c a_c),
@@ -35,9 +36,6 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 
-// full scale of three signed byte limbs (the largest is 127 (65536 + 256 + 1) = 8355711), kept 127 below
-// it: an fp32 product near 2^23 rounds by up to 0.5, and rint(max|alpha| * S / max|alpha|) must not pass it
-constexpr float kS24 = 8355584.0f;
 constexpr int kCols = 64;        // (query, head) columns per work-group, 16 per wave
 
 __device__ inline i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) { return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0); }
@@ -65,22 +63,9 @@ __device__ inline void split8(const float (&x)[8], u32x4& hi, u32x4& lo) {
   lo = u32x4{l[0], l[1], l[2], l[3]};
 }
 
-// signed byte limbs of x = 65536 hi + 256 mid + lo (lo, mid, hi in [-128, 127]): lo = x mod 256,
-// mid = ((x + 128) >> 8) mod 256, hi = (((x + 128) >> 8) + 128) >> 8; four values' limbs per word
-__device__ inline uint32_t pack_bytes(int a0, int a1, int a2, int a3) {
-  return __builtin_amdgcn_perm(__builtin_amdgcn_perm(a3, a2, 0x0c0c0400u), __builtin_amdgcn_perm(a1, a0, 0x0c0c0400u),
-                               0x05040100u);
-}
-__device__ inline int limb_up(int x) { return (x + 128) >> 8; }
-// limbs [lo, mid, hi] of four values as the dwords of three operands
-__device__ inline void pack_limbs(int a0, int a1, int a2, int a3, uint32_t (&w)[3]) {
-  w[0] = pack_bytes(a0, a1, a2, a3);
-  const int b0 = limb_up(a0), b1 = limb_up(a1), b2 = limb_up(a2), b3 = limb_up(a3);
-  w[1] = pack_bytes(b0, b1, b2, b3);
-  w[2] = pack_bytes(limb_up(b0), limb_up(b1), limb_up(b2), limb_up(b3));
-}
+// the value lo + 256 mid + 65536 hi of element i of three limb sums (exact in int32 at the full scales used)
 __device__ inline float limbs_value(const i32x4& h, const i32x4& m, const i32x4& l, int i) {
-  return fmaf((float)h[i], 65536.0f, (float)(m[i] * 256 + l[i]));
+  return (float)(int)(((((uint32_t)h[i] << 8) + (uint32_t)m[i]) << 8) + (uint32_t)l[i]);
 }
 // a 32-bit word of 2-bit codes as four int8 vectors: dword k' holds field k' of every byte
 __device__ inline i32x4 unpack_codes(uint32_t w) {
@@ -177,11 +162,12 @@ struct GroupBuf {
   uint16_t meta[512];                         // the pages' 512-byte metadata blocks, page 0 then page 1
 };
 
-// Signed limbs of the integers x[e] (e = 4 j + k') as the three dwords of an i8 operand per limb
-__device__ inline void limb_operands(const int (&x)[16], i32x4 (&op)[3]) {
+// The limbs of 16 magic-rounded values ef[e] (e = 4 j + k', each fmaf(x, scale, kRound3)) as the three i8
+// operands lo, mid, hi: dword k' holds the limbs of ef[k'], ef[4 + k'], ef[8 + k'], ef[12 + k'] in bytes 0..3
+__device__ inline void limb_operands(const float (&ef)[16], i32x4 (&op)[3]) {
   uint32_t w[4][3];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) pack_limbs(x[k], x[4 + k], x[8 + k], x[12 + k], w[k]);
+  for (int k = 0; k < 4; ++k) limbs3(ef[k], ef[4 + k], ef[8 + k], ef[12 + k], w[k][0], w[k][1], w[k][2]);
 #pragma unroll
   for (int lb = 0; lb < 3; ++lb) op[lb] = i32x4{(int)w[0][lb], (int)w[1][lb], (int)w[2][lb], (int)w[3][lb]};
 }
@@ -189,6 +175,7 @@ __device__ inline void limb_operands(const int (&x)[16], i32x4 (&op)[3]) {
 template <int GQ, int SCHEME>
 __global__ __launch_bounds__(256) void prefill_kernel(DecodeArgs a) {
   using SC = PrefillScheme<SCHEME>;
+  constexpr float S = SC::BITS == 2 ? 4000000.0f : 1000000.0f;  // full scale of the fixed-point operands
   __shared__ GroupBuf<SC::BITS> gb[2];
   const Geo& g = a.g;
   const int b = blockIdx.z, h = blockIdx.y;
@@ -345,20 +332,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) amx = fmaxf(amx, fabsf(qr[ks][e]));
     amx = col_max(amx);
-    const float inv = amx > 0.0f ? kS24 / amx : 0.0f;
+    const float inv = amx > 0x1p-100f ? S / amx : 0.0f;
     float fs = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      int x[16];
+      float ef[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        x[e] = (int)rintf(qr[ks][e] * inv);
-        fs += (float)x[e];
+        ef[e] = fmaf(qr[ks][e], inv, kRound3);
+        fs += ef[e] - kRound3;  // the integer a exactly
       }
-      limb_operands(x, bq_tok[ks]);
+      limb_operands(ef, bq_tok[ks]);
     }
     FS_tok = col_sum(fs);
-    A_tok = amx * (1.0f / kS24);
+    A_tok = amx * (1.0f / S);
   }
   float m = -INFINITY, l = 0.0f;
   f32x4 o[8];
@@ -415,28 +402,44 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeArgs a) {
           amx = fmaxf(amx, fabsf(al[ks][e]));
         }
       amx = col_max(amx);
-      const float inv = amx > 0.0f ? kS24 / amx : 0.0f;
+      const float inv = amx > 0x1p-100f ? S / amx : 0.0f;
       float zs = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        int x[16];
+        float ef[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int c = key_channel<SCHEME>(4 * ks + q, e);
-          x[e] = (int)rintf(al[ks][e] * inv);
-          zs = fmaf((float)x[e], bf16_to_f32(B.meta[D + c]), zs);
+          ef[e] = fmaf(al[ks][e], inv, kRound3);
+          zs = fmaf(ef[e] - kRound3, bf16_to_f32(B.meta[D + c]), zs);
         }
-        limb_operands(x, bq[ks]);
+        limb_operands(ef, bq[ks]);
       }
       zs = col_sum(zs);
-      Acol = amx * (1.0f / kS24);
+      Acol = amx * (1.0f / S);
       AZ = Acol * zs;
     }
     // this lane's tokens: 16 mt + 4 q + i of the unit (page mt / 4, token 16 (mt % 4) + 4 q + i of it)
-    auto tok_meta = [&](int mt, int i, int which) {  // which: 0 K scale, 1 K zero, 2 V scale, 3 V zero
-      const int pg = mt >> 2, tt = 16 * (mt & 3) + 4 * q + i;
-      if constexpr (SCHEME == KVQ_INT2_TOKEN) return bf16_to_f32(B.meta[256 * pg + 64 * which + tt]);
-      else return bf16_to_f32(B.meta[256 * pg + 128 * (which >> 1) + 2 * tt + (which & 1)]);
+    // the scales (s) and zeros (z) of tokens 16 mt + 4 q + 0..3, K (side 0) or V (side 1), by one LDS read:
+    // per-token INT2 keeps a page's 64 K scales, K zeros, V scales, V zeros in runs; INT4 keeps (s, z) pairs
+    auto tok_meta4 = [&](int mt, int side, float (&sv)[4], float (&zv)[4]) {
+      const int pg = mt >> 2, t0 = 16 * (mt & 3) + 4 * q;
+      if constexpr (SCHEME == KVQ_INT2_TOKEN) {
+        const uint2 ws = *reinterpret_cast<const uint2*>(&B.meta[256 * pg + 128 * side + t0]);
+        const uint2 wz = *reinterpret_cast<const uint2*>(&B.meta[256 * pg + 128 * side + 64 + t0]);
+        sv[0] = __uint_as_float(ws.x << 16), sv[1] = __uint_as_float(ws.x & 0xffff0000u);
+        sv[2] = __uint_as_float(ws.y << 16), sv[3] = __uint_as_float(ws.y & 0xffff0000u);
+        zv[0] = __uint_as_float(wz.x << 16), zv[1] = __uint_as_float(wz.x & 0xffff0000u);
+        zv[2] = __uint_as_float(wz.y << 16), zv[3] = __uint_as_float(wz.y & 0xffff0000u);
+      } else {
+        const uint4 w = *reinterpret_cast<const uint4*>(&B.meta[256 * pg + 128 * side + 2 * t0]);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[i] = __uint_as_float(ww[i] << 16);
+          zv[i] = __uint_as_float(ww[i] & 0xffff0000u);
+        }
+      }
     };
     // 2. logits S^T (128 tokens x 16 columns): token 16 mt + (l % 16) is the A row
     float lg[8][4];
@@ -453,11 +456,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeArgs a) {
         cm = mfma_i8(av, bq[ks][1], cm);
         ch = mfma_i8(av, bq[ks][2], ch);
       }
+      float ks4[4], kz4[4];
+      if constexpr (SC::TOK) tok_meta4(mt, 0, ks4, kz4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = 16 * mt + 4 * q + i;
         float x;
-        if constexpr (SC::TOK) x = (Acol * tok_meta(mt, i, 0)) * fmaf(-tok_meta(mt, i, 1), FS_tok, limbs_value(ch, cm, cl, i));
+        if constexpr (SC::TOK) x = (Acol * ks4[i]) * fmaf(-kz4[i], FS_tok, limbs_value(ch, cm, cl, i));
         else x = fmaf(Acol, limbs_value(ch, cm, cl, i), -AZ);
         lg[mt][i] = (gpos + tok <= qpos) ? x : -INFINITY;
         gm = fmaxf(gm, lg[mt][i]);
@@ -467,31 +472,34 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeArgs a) {
     // 3. weights as byte limbs.  Per channel u = floor(S p + 0.5), p = 2^(logit - group max); per token
     //    u_t = floor(S p_t s'_t / S' + 0.5), S' = max_t p_t s'_t of the column, with P = sum_t p_t and
     //    Z = sum_t u_t z'_t
-    int u[8][4];
+    float u[8][4];  // magic-rounded weights
     float Pf, Sg = 0.0f, Zt = 0.0f;
     if constexpr (SC::TOK) {
-      float pw[8][4], wmx = 0.0f, ps = 0.0f;
+      float pw[8][4], vz[8][4], wmx = 0.0f, ps = 0.0f;
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
+      for (int mt = 0; mt < 8; ++mt) {
+        float vs4[4];
+        tok_meta4(mt, 1, vs4, vz[mt]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float p = exp2_or_zero(lg[mt][i], gm);
           ps += p;
           // tokens past the length (their metadata unwritten) take no weight
-          pw[mt][i] = lg[mt][i] == -INFINITY ? 0.0f : p * tok_meta(mt, i, 2);
+          pw[mt][i] = lg[mt][i] == -INFINITY ? 0.0f : p * vs4[i];
           wmx = fmaxf(wmx, pw[mt][i]);
         }
+      }
       Sg = col_max(wmx);
       Pf = col_sum(ps);
       // below 2^-100 the unit's value terms are beyond fp32's reach next to the others: weights 0
-      const float r = Sg > 0x1p-100f ? kS24 / Sg : 0.0f;
+      const float r = Sg > 0x1p-100f ? S / Sg : 0.0f;
       float zs = 0.0f;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          u[mt][i] = (int)fmaf(pw[mt][i], r, 0.5f);
-          if (lg[mt][i] != -INFINITY) zs = fmaf((float)u[mt][i], tok_meta(mt, i, 3), zs);
+          u[mt][i] = fmaf(pw[mt][i], r, kRound3);
+          if (lg[mt][i] != -INFINITY) zs = fmaf(u[mt][i] - kRound3, vz[mt][i], zs);
         }
       Zt = col_sum(zs);
     } else {
@@ -500,8 +508,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeArgs a) {
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          u[mt][i] = (int)fmaf(exp2_or_zero(lg[mt][i], gm), kS24, 0.5f);
-          us += (float)u[mt][i];
+          u[mt][i] = fmaf(exp2_or_zero(lg[mt][i], gm), S, kRound3);
+          us += u[mt][i] - kRound3;
         }
       Pf = col_sum(us);
     }
@@ -510,7 +518,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeArgs a) {
     i32x4 uq[2][3];
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp) {
-      int x[16];
+      float x[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {  // e = 4 bb + d (the order limb_operands packs)
         int J, R;
@@ -523,7 +531,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeArgs a) {
     const float mnew = fmaxf(m, gm);
     const float sc = exp2_or_zero(m, mnew);
     const float eg = exp2_or_zero(gm, mnew);
-    const float wg = SC::TOK ? eg * Sg * (1.0f / kS24) : eg * (1.0f / kS24);
+    const float wg = SC::TOK ? eg * Sg * (1.0f / S) : eg * (1.0f / S);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
       const int c = 16 * mt + (lane & 15);
