@@ -627,21 +627,6 @@ __device__ __forceinline__ mf_i32x4 codes_i8(uint32_t w) {
 }
 // Two words of 2-bit codes at once: each shift of the 64-bit pair serves both (the bits one word takes from
 // the other land outside the mask)
-__device__ __forceinline__ uint64_t shr64(uint64_t w, int n) {
-  // one 64-bit shift (the compiler would split a C++ shift into two 32-bit ones); its operand is a load's
-  // result, not a matrix-core one
-  uint64_t r;
-  asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "i"(n), "v"(w));
-  return r;
-}
-__device__ __forceinline__ void codes_i8_pair(uint32_t w0, uint32_t w1, mf_i32x4& c0, mf_i32x4& c1) {
-  const uint64_t w = ((uint64_t)w1 << 32) | w0;
-  const uint64_t s2 = shr64(w, 2), s4 = shr64(w, 4), s6 = shr64(w, 6);
-  constexpr uint32_t M = 0x03030303u;
-  c0 = mf_i32x4{(int)(w0 & M), (int)((uint32_t)s2 & M), (int)((uint32_t)s4 & M), (int)((uint32_t)s6 & M)};
-  c1 = mf_i32x4{(int)(w1 & M), (int)((uint32_t)(s2 >> 32) & M), (int)((uint32_t)(s4 >> 32) & M),
-                (int)((uint32_t)(s6 >> 32) & M)};
-}
 __device__ __forceinline__ mf_i32x4 u4_i32x4(uint4 v) { return mf_i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}; }
 template <int BITS>
 struct Limb3 {

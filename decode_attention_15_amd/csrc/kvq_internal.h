@@ -108,6 +108,25 @@ __device__ inline uint16_t f32_to_bf16_rne(float x) {
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
+typedef __attribute__((ext_vector_type(4))) int kvq_i32x4;
+// Two words of 2-bit codes as the int8 operands of two matrix products: dword n of each holds field n of every
+// byte ((w >> 2 n) & 0x03030303), both words' fields from one 64-bit shift.
+__device__ __forceinline__ uint64_t shr64(uint64_t w, int n) {
+  // one 64-bit shift (the compiler would split a C++ shift into two 32-bit ones); its operand is a load's
+  // result, not a matrix-core one
+  uint64_t r;
+  asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "i"(n), "v"(w));
+  return r;
+}
+__device__ __forceinline__ void codes_i8_pair(uint32_t w0, uint32_t w1, kvq_i32x4& c0, kvq_i32x4& c1) {
+  const uint64_t w = ((uint64_t)w1 << 32) | w0;
+  const uint64_t s2 = shr64(w, 2), s4 = shr64(w, 4), s6 = shr64(w, 6);
+  constexpr uint32_t M = 0x03030303u;
+  c0 = kvq_i32x4{(int)(w0 & M), (int)((uint32_t)s2 & M), (int)((uint32_t)s4 & M), (int)((uint32_t)s6 & M)};
+  c1 = kvq_i32x4{(int)(w1 & M), (int)((uint32_t)(s2 >> 32) & M), (int)((uint32_t)(s4 >> 32) & M),
+                (int)((uint32_t)(s6 >> 32) & M)};
+}
+
 // Three signed byte limbs.  An operand x with |x| <= S is rounded to an integer a = lo + 256 mid + 65536 hi
 // (lo, mid in [-128, 127], hi in [-64, 63]) by one FMA with the magic addend 2^23 + 0x408080: the result
 // lies in [2^23, 2^24), where fp32 spacing is 1, so it is the exact 2^23 + 0x408080 + rint(x) (ties to even)

@@ -449,12 +449,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeArgs a) {
       const int t = 16 * mt + (lane & 15);
       const uint32_t* kr = B.k[t >> 6] + SC::KROW * (t & 63);
       i32x4 cl = {0, 0, 0, 0}, cm = {0, 0, 0, 0}, ch = {0, 0, 0, 0};
+      i32x4 av[2];
+      if constexpr (SC::BITS == 2) {
+        codes_i8_pair(kr[q], kr[4 + q], av[0], av[1]);
+      } else {
+        av[0] = key_codes<SCHEME>(kr, q);
+        av[1] = key_codes<SCHEME>(kr, 4 + q);
+      }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const i32x4 av = key_codes<SCHEME>(kr, 4 * ks + q);
-        cl = mfma_i8(av, bq[ks][0], cl);
-        cm = mfma_i8(av, bq[ks][1], cm);
-        ch = mfma_i8(av, bq[ks][2], ch);
+        cl = mfma_i8(av[ks], bq[ks][0], cl);
+        cm = mfma_i8(av[ks], bq[ks][1], cm);
+        ch = mfma_i8(av[ks], bq[ks][2], ch);
       }
       float ks4[4], kz4[4];
       if constexpr (SC::TOK) tok_meta4(mt, 0, ks4, kz4);
@@ -536,12 +542,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeArgs a) {
     for (int mt = 0; mt < 8; ++mt) {
       const int c = 16 * mt + (lane & 15);
       i32x4 cl = {0, 0, 0, 0}, cm = {0, 0, 0, 0}, ch = {0, 0, 0, 0};
+      i32x4 av[2];
+      if constexpr (SC::BITS == 2) {
+        codes_i8_pair(B.v[0][SC::VROW * c + q], B.v[1][SC::VROW * c + q], av[0], av[1]);
+      } else {
+        av[0] = value_codes<SCHEME>(B.v[0] + SC::VROW * c, q);
+        av[1] = value_codes<SCHEME>(B.v[1] + SC::VROW * c, q);
+      }
 #pragma unroll
       for (int kp = 0; kp < 2; ++kp) {
-        const i32x4 av = value_codes<SCHEME>(B.v[kp] + SC::VROW * c, q);
-        cl = mfma_i8(av, uq[kp][0], cl);
-        cm = mfma_i8(av, uq[kp][1], cm);
-        ch = mfma_i8(av, uq[kp][2], ch);
+        cl = mfma_i8(av[kp], uq[kp][0], cl);
+        cm = mfma_i8(av[kp], uq[kp][1], cm);
+        ch = mfma_i8(av[kp], uq[kp][2], ch);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
