@@ -24,7 +24,8 @@ SOURCES = {
     # the write path must round exactly as the cache format states: no contraction
     "kvq_write.hip": ["-ffp-contract=off"],
     "kvq_decode.hip": [],
-    "kvq_prefill.hip": [],
+    # matrix-core results straight into VGPRs (no accumulator-register copies in the group loop)
+    "kvq_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "kvq_api.cpp": ["-x", "hip", "-ffp-contract=off"],
     "kvq_calib.cpp": ["-x", "hip", "-ffp-contract=off"],
 }
