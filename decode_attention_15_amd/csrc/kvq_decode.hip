@@ -454,9 +454,11 @@ __device__ inline float fmax_raw(float a, float b) {
 
 // ---------------------------------------------------------------------------------------------
 // Global -> LDS copies of 16 bytes per lane (lane i's bytes land at the LDS address in M0 + 16 i), issued
-// from inline assembly so that the compiler adds no waits of its own for them: the nibble-digit unit keeps
-// every global read of its loop in this form and waits on the vector-memory counter explicitly.  Per-lane
-// 64-bit address, or a uniform base plus a per-lane 32-bit offset.
+// from inline assembly so that the compiler adds no waits of its own for them: the matrix-core units keep
+// every global read of their loops in this form and wait on the vector-memory counter explicitly.  Per-lane
+// 64-bit address, or a uniform base plus a per-lane 32-bit offset.  The blocks write M0, which the compiler
+// does not track: no compiler-emitted instruction in these kernels may use M0 (the tests check the compiled
+// assembly for exactly that).
 __device__ inline uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -465,14 +467,6 @@ __device__ inline void dma16(uint32_t lds, const void* gaddr) {
 }
 __device__ inline void dma16_base(uint32_t lds, const void* gbase, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(gbase)
-               : "memory");
-}
-// With an immediate offset: the instruction adds it to the LDS address too, so M0 is set OFF lower and the
-// bytes land at lds + 16 i as with dma16.
-template <int OFF>
-__device__ inline void dma16_off(uint32_t lds, const void* gaddr) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:%2" ::"s"(lds - OFF), "v"(gaddr),
-               "i"(OFF)
                : "memory");
 }
 #define KVQ_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
@@ -620,13 +614,6 @@ typedef __attribute__((ext_vector_type(4))) int mf_i32x4;
 __device__ __forceinline__ mf_i32x4 mfma_i8x64(mf_i32x4 a, mf_i32x4 b, mf_i32x4 c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
-// 16 2-bit codes as 16 int8 values: dword n holds field n of every byte
-__device__ __forceinline__ mf_i32x4 codes_i8(uint32_t w) {
-  return mf_i32x4{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
-                  (int)((w >> 6) & 0x03030303u)};
-}
-// Two words of 2-bit codes at once: each shift of the 64-bit pair serves both (the bits one word takes from
-// the other land outside the mask)
 __device__ __forceinline__ mf_i32x4 u4_i32x4(uint4 v) { return mf_i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}; }
 template <int BITS>
 struct Limb3 {

@@ -67,11 +67,6 @@ __device__ inline void split8(const float (&x)[8], u32x4& hi, u32x4& lo) {
 __device__ inline float limbs_value(const i32x4& h, const i32x4& m, const i32x4& l, int i) {
   return (float)(int)(((((uint32_t)h[i] << 8) + (uint32_t)m[i]) << 8) + (uint32_t)l[i]);
 }
-// a 32-bit word of 2-bit codes as four int8 vectors: dword k' holds field k' of every byte
-__device__ inline i32x4 unpack_codes(uint32_t w) {
-  return i32x4{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
-               (int)((w >> 6) & 0x03030303u)};
-}
 // reductions over the 4 lanes of a column (lanes l, l ^ 16, l ^ 32, l ^ 48)
 __device__ inline float col_max(float x) {
   x = fmaxf(x, __shfl_xor(x, 16, 64));
@@ -106,7 +101,8 @@ struct PrefillScheme {
 };
 
 // Key operand of a token row for the channels of 16-channel block m (k = 16 q + 4 k' + j: dword k', byte j):
-//  - 2-bit codes (channel c in byte c / 4, field c % 4): word m, dword k' = field k' -> channel 16 m + 4 j + k';
+//  - 2-bit codes (channel c in byte c / 4, field c % 4): word m, dword k' = field k' -> channel 16 m + 4 j + k'
+//    (codes_i8_pair unpacks the two k steps' words m = q and 4 + q together);
 //  - per-channel 4-bit (word 2 m + e holds channels 16 m + 2 k + e in nibble k): low nibbles of words 2 m,
 //    2 m + 1, then their high nibbles -> channel 16 m + 4 j + k';
 //  - per-token 4-bit (channel c in byte c / 2, even c low): words 2 m, 2 m + 1, low then high nibbles of
@@ -125,22 +121,23 @@ __device__ inline i32x4 nib_lo_hi_lo_hi(uint32_t w0, uint32_t w1) {
                (int)((w1 >> 4) & 0x0F0F0F0Fu)};
 }
 template <int SCHEME>
-__device__ inline i32x4 key_codes(const uint32_t* row, int m) {
-  if constexpr (PrefillScheme<SCHEME>::BITS == 2) return unpack_codes(row[m]);
-  else if constexpr (SCHEME == KVQ_INT4_CHANNEL) return nib_lo_lo_hi_hi(row[2 * m], row[2 * m + 1]);
+__device__ inline i32x4 key_codes(const uint32_t* row, int m) {  // 4-bit codes
+  static_assert(PrefillScheme<SCHEME>::BITS == 4, "2-bit words go through codes_i8_pair");
+  if constexpr (SCHEME == KVQ_INT4_CHANNEL) return nib_lo_lo_hi_hi(row[2 * m], row[2 * m + 1]);
   else return nib_lo_hi_lo_hi(row[2 * m], row[2 * m + 1]);
 }
 // Value operand of a channel row of one page, lane q (k = 16 q + 4 d + b: dword d, byte b), tokens (of the
 // page) 16 J + 4 q + R:
-//  - 2-bit codes (token 16 j + 4 g + r in byte 4 g + j, field r): word q, dword d = field d -> J = b, R = d;
+//  - 2-bit codes (token 16 j + 4 g + r in byte 4 g + j, field r): word q, dword d = field d -> J = b, R = d
+//    (codes_i8_pair unpacks the two pages' words together);
 //  - per-channel 4-bit (word 2 g + n holds tokens 16 j + 4 g + 2 h + n in nibble 2 j + h): low nibbles of
 //    words 2 q, 2 q + 1, then their high nibbles -> J = b, R = d;
 //  - per-token 4-bit (token 16 j + 4 g + r in byte 8 g + 2 j + r / 2, even r low): words 2 q, 2 q + 1, low
 //    then high nibbles of each -> J = 2 (d / 2) + b / 2, R = 2 (b % 2) + d % 2.
 template <int SCHEME>
-__device__ inline i32x4 value_codes(const uint32_t* row, int q) {
-  if constexpr (PrefillScheme<SCHEME>::BITS == 2) return unpack_codes(row[q]);
-  else if constexpr (SCHEME == KVQ_INT4_CHANNEL) return nib_lo_lo_hi_hi(row[2 * q], row[2 * q + 1]);
+__device__ inline i32x4 value_codes(const uint32_t* row, int q) {  // 4-bit codes
+  static_assert(PrefillScheme<SCHEME>::BITS == 4, "2-bit words go through codes_i8_pair");
+  if constexpr (SCHEME == KVQ_INT4_CHANNEL) return nib_lo_lo_hi_hi(row[2 * q], row[2 * q + 1]);
   else return nib_lo_hi_lo_hi(row[2 * q], row[2 * q + 1]);
 }
 template <int SCHEME>
