@@ -413,6 +413,7 @@ def main():
         "steps_per_s": res["steps_per_s"],
         "roofline": res["roofline"],
         "decode_kernels_us": res["decode_kernels_us"],
+        "read_probe": res["read_probe"],
         "timed_window": res["timed_window"],
     }
     if args.workload == "batch32_32k" and not args.no_ragged and not (args.scheme or args.key_only or args.split):
@@ -606,6 +607,27 @@ def measure_decode(wl, args, K, synth, np, torch):
     achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     log(f"[bench] split-K kernel {kern_ms * 1e3:.1f} us, {achieved:.0f} GB/s; kernels {stage_us}")
 
+    # the read pattern's ceiling: the library's read probe reads the same quantized head blocks as the split-K
+    # kernel (same walks, work-groups and page order, no band, no arithmetic), timed the same way
+    probe = None
+    shape = K.decode_shape(cfg, B, T_end)
+    if grouped and shape["matrix_cores"]:
+        xo = torch.empty((B, n_kv, shape["walks"]), dtype=torch.int32, device=dev)
+        K.read_probe(cache, xo, T_end)
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for e0, e1 in pev:
+            e0.record()
+            K.read_probe(cache, xo, T_end)
+            e1.record()
+        torch.cuda.synchronize()
+        p_ms = sum(e0.elapsed_time(e1) for e0, e1 in pev) / len(pev)
+        hb = K.page_bytes(cfg) // n_kv
+        q_bytes = sum(max(0, (int(t) - wl.n_sink - wl.n_recent) // 128) * 2 * hb * n_kv for t in lens_end)
+        probe = {"kernel_us": round(p_ms * 1e3, 2), "bytes_per_launch": int(q_bytes),
+                 "achieved": round(q_bytes / (p_ms * 1e-3) / 1e9, 1),
+                 "frac": round(q_bytes / (p_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "launches_timed": len(pev)}
+        log(f"[bench] read probe {probe}")
+
     variant = ("" if wl.scheme == synth.WORKLOADS[wl.name].scheme else wl.scheme) + \
         (" key-only" if wl.key_only else "") + \
         (f" hadamard-{wl.hadamard_block}" if wl.rotation == "saw" and wl.hadamard_block != 128 else "")
@@ -638,6 +660,7 @@ def measure_decode(wl, args, K, synth, np, torch):
                      "kernel": kernel[wl.scheme], "kernel_us": round(kern_ms * 1e3, 2),
                      "kernel_launches_timed": len(sampled), "bytes_per_launch": kern_bytes},
         "decode_kernels_us": stage_us,
+        "read_probe": probe,
         "timed_window": {"ms_per_step": round(ms_timed, 5), "demotions": n_dem,
                          "window128_ms_per_step": None if dem_ms is None else round(dem_ms, 5)},
     }

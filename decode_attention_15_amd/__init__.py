@@ -104,6 +104,7 @@ _lib_decode_shape = _sig("kvq_decode_shape_of", ctypes.c_int, _CFG, ctypes.c_int
 _lib_decode_noalloc = _sig("kv_decode_attn_noalloc", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P,
                            ctypes.c_int32, _P)
 NOALLOC_SCRATCH_BYTES = 64 << 20
+_lib_read_probe = _sig("kvq_read_probe", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P)
 _lib_decode_stages = _sig("kv_decode_attn_stages", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P, ctypes.c_int32,
                           _P, ctypes.c_size_t, ctypes.c_int32, _P)
 _lib_debug_rotate = _sig("kvq_debug_rotate", ctypes.c_int, _CFG, _CACHE, ctypes.c_int32, _P, ctypes.c_int32,
@@ -118,7 +119,7 @@ EXPORTED = [
     "kvq_build_hadamard_rotation", "kvq_query_covariance", "kvq_score_value_covariance", "kvq_eigenbasis",
     "kvq_build_oscar_rotation_from_covariance", "kvq_prefill_workspace_bytes", "kv_prefill_attn",
     "kv_rotate_quant_write", "kv_decode_attn", "kv_decode_attn_stages", "kv_decode_attn_noalloc",
-    "kvq_decode_shape_of",
+    "kvq_decode_shape_of", "kvq_read_probe",
     "kvq_debug_rotate", "kvq_debug_unpack", "kvq_build_page_table", "kvq_check_page_table",
     "kvq_strerror", "kvq_version", "kvq_last_error",
 ]
@@ -352,6 +353,17 @@ def decode_shape(cfg: Config, batch: int, max_seq_len: int) -> dict:
     sh = DecodeShape()
     _check(_lib_decode_shape(ctypes.byref(cfg), int(batch), int(max_seq_len), ctypes.byref(sh)), "decode_shape")
     return {name: int(getattr(sh, name)) for name, _ in DecodeShape._fields_}
+
+
+def read_probe(cache: DeviceCache, xor_out, max_seq_len: int, stream=None) -> None:
+    """The decode's read pattern with no arithmetic: xor_out (uint32-sized int32 [batch, n_kv, walks]) gets the
+    XOR of the 32-bit words each walk of the split-K decode reads."""
+    assert xor_out.is_contiguous() and xor_out.element_size() == 4
+    shape = decode_shape(cache.cfg, cache.batch, max_seq_len)
+    assert xor_out.numel() == cache.batch * cache.cfg.n_kv_heads * shape["walks"]
+    cs = cache.c_struct()
+    _check(_lib_read_probe(ctypes.byref(cache.cfg), ctypes.byref(cs), _ptr(xor_out), int(max_seq_len),
+                           _stream(stream)), "kvq_read_probe")
 
 
 def kv_decode_attn_noalloc(cache: DeviceCache, q, out, max_seq_len: int, stream=None) -> None:

@@ -26,6 +26,8 @@ SOURCES = {
     "kvq_decode.hip": [],
     # matrix-core results straight into VGPRs (no accumulator-register copies in the group loop)
     "kvq_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    # read-bandwidth probe of the decode's read pattern
+    "kvq_probe.hip": [],
     "kvq_api.cpp": ["-x", "hip", "-ffp-contract=off"],
     "kvq_calib.cpp": ["-x", "hip", "-ffp-contract=off"],
 }

@@ -453,6 +453,25 @@ int kvq_decode_shape_of(const kvq_config* cfg, int32_t batch, int32_t max_seq_le
   return KVQ_OK;
 }
 
+int kvq_read_probe(const kvq_config* cfg, const kvq_cache* cache, uint32_t* xor_out, int32_t max_seq_len_host,
+                   hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if ((st = check_cache(cfg, cache)) != KVQ_OK) return st;
+  if (!xor_out || max_seq_len_host < 0) return KVQ_EINVAL;
+  if (!is_grouped(cfg->scheme) || !uses_mfma(cfg)) return KVQ_EUNSUPPORTED;
+  if (kvq_pages_for_len(cfg, max_seq_len_host) > cache->max_pages_per_seq) return KVQ_ERANGE;
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.g = make_geo(cfg, cache);
+  set_decode_shape(cfg, max_seq_len_host, a.g);
+  a.pages = static_cast<const uint8_t*>(cache->pages);
+  a.page_table = cache->page_table;
+  a.seq_lens = cache->seq_lens;
+  clear_stale_error();
+  return to_status(launch_read_probe(a, xor_out, stream), "kvq_read_probe");
+}
+
 int kv_decode_attn_noalloc(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t dtype, float* out,
                            int32_t max_seq_len_host, hipStream_t stream) {
   // every check that needs no device comes first, so that a call that cannot run touches nothing

@@ -843,8 +843,6 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   }
   // the partial of chunk ci (per channel, o and l carry the weights' factor S), then a fresh softmax state;
   // every partial a merge reads is written, chunks past the length have none
-  // the partial of chunk ci (per channel, o and l carry the weights' factor S), then a fresh softmax state;
-  // every partial a merge reads is written, chunks past the length have none
   auto store_partial = [&](int ci) {
 #pragma unroll
     for (int e = 0; e < HPL; ++e) {
@@ -1264,8 +1262,6 @@ __device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int
   }
   // the partial of chunk ci, then a fresh softmax state; every partial a merge reads is written, chunks past
   // the length have none
-  // the partial of chunk ci, then a fresh softmax state; every partial a merge reads is written, chunks past
-  // the length have none
   auto store_partial = [&](int ci) {
 #pragma unroll
     for (int e = 0; e < HPL; ++e) {
@@ -1441,31 +1437,6 @@ __device__ inline void splitk_unit_of(const Geo& g, int& unit, int& h, int& b) {
   h = pair % g.n_kv;
   b = pair / g.n_kv;
 }
-// matrix-core decode, chunk work-group i: its sequence, and this wave's kv head and walk (chunks c0 .. c1 - 1,
-// empty past the walks); returns the work-group's first chunk (every wave's at least that)
-__device__ inline int wave_chunk_of(const Geo& g, int i, int wave, int& b, int& h, int& c0, int& c1) {
-  if (splitk_head_quads(g)) {
-    const int quads = g.n_kv / 4, per = g.batch * quads;
-    const int r = i % per;
-    b = r / quads;
-    h = 4 * (r % quads) + wave;
-    walk_chunks(g, i / per, &c0, &c1);
-    return c0;
-  }
-  const int pairs = g.batch * g.n_kv, pair = i % pairs;
-  b = pair / g.n_kv;
-  h = pair % g.n_kv;
-  const int w = 4 * (i / pairs) + wave;
-  int first, unused;
-  walk_chunks(g, 4 * (i / pairs), &first, &unused);
-  if (w < g.walks) {
-    walk_chunks(g, w, &c0, &c1);
-  } else {
-    c0 = c1 = g.n_units - 1;
-  }
-  return first;
-}
-
 // Matrix-core launch of the grouped schemes.  Work-groups per CU, as the LDS allows (160 KB): 2-bit codes
 // three up to GQ 4 (48.5 KB each), two at GQ 8; 4-bit codes two up to GQ 4 (81 KB), one at GQ 8.
 template <int GQ, bool TOK, int BITS>

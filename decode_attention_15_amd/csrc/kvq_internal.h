@@ -88,6 +88,30 @@ __host__ __device__ inline void walk_chunks(const Geo& g, int w, int* c0, int* c
   *c1 = (int)((w + 1) * nc / g.walks);
 }
 __host__ __device__ inline int splitk_wgs(const Geo& g) { return splitk_chunk_wgs(g) + g.batch * g.n_kv; }
+// matrix-core decode, chunk work-group i: its sequence, and this wave's kv head and walk (chunks c0 .. c1 - 1,
+// empty past the walks); returns the work-group's first chunk (every wave's at least that)
+__device__ inline int wave_chunk_of(const Geo& g, int i, int wave, int& b, int& h, int& c0, int& c1) {
+  if (splitk_head_quads(g)) {
+    const int quads = g.n_kv / 4, per = g.batch * quads;
+    const int r = i % per;
+    b = r / quads;
+    h = 4 * (r % quads) + wave;
+    walk_chunks(g, i / per, &c0, &c1);
+    return c0;
+  }
+  const int pairs = g.batch * g.n_kv, pair = i % pairs;
+  b = pair / g.n_kv;
+  h = pair % g.n_kv;
+  const int w = 4 * (i / pairs) + wave;
+  int first, unused;
+  walk_chunks(g, 4 * (i / pairs), &first, &unused);
+  if (w < g.walks) {
+    walk_chunks(g, w, &c0, &c1);
+  } else {
+    c0 = c1 = g.n_units - 1;
+  }
+  return first;
+}
 
 __host__ __device__ inline int band_slot_of(int t, int S0, int W) {
   return t < S0 ? t : S0 + (t - S0) % (W + GROUP);
@@ -197,5 +221,6 @@ hipError_t launch_decode(const DecodeArgs& a, int stages, hipStream_t s);
 // query rotation of `rows` query rows (q, qrot, qband indexed as [row][n_q][128])
 hipError_t launch_qprep_rows(const DecodeArgs& a, int rows, hipStream_t s);
 hipError_t launch_prefill(const DecodeArgs& a, int max_q, hipStream_t s);
+hipError_t launch_read_probe(const DecodeArgs& a, uint32_t* xor_out, hipStream_t s);
 
 }  // namespace kvq

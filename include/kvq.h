@@ -296,6 +296,19 @@ typedef struct kvq_decode_shape {
 } kvq_decode_shape;
 int kvq_decode_shape_of(const kvq_config* cfg, int32_t batch, int32_t max_seq_len, kvq_decode_shape* out);
 
+/* Read-bandwidth probe of the split-K decode (a measurement hook; it computes no attention).  It reads every
+   quantized head block that kv_decode_attn's split-K kernel reads for lengths up to max_seq_len_host, with the
+   same chunks, walks, work-groups and page-pair order ([OSCAR] §3.4.5, the paged INT2 cache and its chunked
+   decode walk), and only folds the 32-bit words each walk read with XOR: xor_out[(b * n_kv_heads + h) * walks
+   + w] (device, uint32, batch * n_kv_heads * walks words, `walks` from kvq_decode_shape_of) receives walk w's
+   XOR for sequence b and kv head h, 0 for a walk with no quantized group.  The band is not read.  Timing it
+   gives the rate at which the GPU streams the decode's read pattern with no arithmetic beside it.  Grouped
+   schemes on the matrix-core decode only: KVQ_EUNSUPPORTED for INT4 per token or decode_impl = fp32.  Other
+   errors as kv_decode_attn (config, cache, KVQ_EINVAL for a null xor_out or negative length, KVQ_ERANGE when
+   the length needs more pages than the page-table row holds, KVQ_EDEVICE on a launch error). */
+int kvq_read_probe(const kvq_config* cfg, const kvq_cache* cache, uint32_t* xor_out, int32_t max_seq_len_host,
+                   hipStream_t stream);
+
 /* kv_decode_attn without a workspace argument, for callers that cannot allocate device memory (code under
    HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): it calls no hipMalloc, hipFree or
    allocating routine.  Its workspace is a file-scope device array of KVQ_NOALLOC_SCRATCH_BYTES (64 MiB) that

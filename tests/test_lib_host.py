@@ -344,3 +344,21 @@ def test_decode_shape_chunks_and_walks():
     assert sh["walks"] >= 2 and sh["splitk_workgroups"] == 128 * (-(-sh["walks"] // 4)) + 128
     with pytest.raises(K.KvqError):
         K.decode_shape(cfg, 0, 100)
+
+
+def test_read_probe_refuses_on_the_host():
+    """kvq_read_probe: schemes without the matrix-core grouped walk, null output, negative or too long
+    lengths are refused before anything touches the device (the pointers here are never dereferenced)."""
+    f = 0x1000
+    T = 4096
+    cfg = K.make_config(8, 32)
+    cs = _fake_cache(cfg, 2, K.pages_for_len(cfg, T))
+    probe = K._lib_read_probe
+    assert probe(K.ctypes.byref(cfg), K.ctypes.byref(cs), None, T, None) == K.KVQ_EINVAL
+    assert probe(K.ctypes.byref(cfg), K.ctypes.byref(cs), f, -1, None) == K.KVQ_EINVAL
+    assert probe(K.ctypes.byref(cfg), K.ctypes.byref(cs), f, T + 129, None) == K.KVQ_ERANGE
+    cfg.decode_impl = K.DECODE_F32
+    assert probe(K.ctypes.byref(cfg), K.ctypes.byref(cs), f, T, None) == K.KVQ_EUNSUPPORTED
+    cfg4 = K.make_config(8, 32, K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0)
+    cs4 = _fake_cache(cfg4, 2, K.pages_for_len(cfg4, T))
+    assert probe(K.ctypes.byref(cfg4), K.ctypes.byref(cs4), f, T, None) == K.KVQ_EUNSUPPORTED
