@@ -462,14 +462,30 @@ __device__ inline float fmax_raw(float a, float b) {
 __device__ inline uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
+// NT: a non-temporal (streaming) read, for bytes that are read once per step.
+template <bool NT = false>
 __device__ inline void dma16(uint32_t lds, const void* gaddr) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gaddr) : "memory");
+  if constexpr (NT) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds), "v"(gaddr) : "memory");
+  } else {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gaddr) : "memory");
+  }
 }
+template <bool NT = false>
 __device__ inline void dma16_base(uint32_t lds, const void* gbase, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(gbase)
-               : "memory");
+  if constexpr (NT) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(lds), "v"(voff), "s"(gbase)
+                 : "memory");
+  } else {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(gbase)
+                 : "memory");
+  }
 }
 #define KVQ_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
+// The grouped schemes' code and metadata copies stream (measured on MI355X at batch 32 x 32k: the split-K
+// kernel about 10% faster than with default-policy copies); the INT4 per-token walk keeps the default policy
+// (measured slightly slower with streaming copies).
+constexpr bool kStreamCopies = true;
 template <int GQ, typename Lds>
 __device__ void int4_unit(Lds& L, const DecodeArgs& a, int b, int h, int T, int chunk) {
   const Geo& g = a.g;
@@ -773,22 +789,22 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   constexpr int KOFF = BITS == 2 ? I2_K_OFF : I4C_K_OFF, VOFF = BITS == 2 ? I2_V_OFF : I4C_V_OFF;
   auto issue_m = [&](int2 p, int buf) {
     const uint8_t* src = (lane >= 32 ? page_of(p.y) : page_of(p.x)) + META + (lane & 31) * 16;
-    dma16(buf ? mst_a1 : mst_a0, src);
+    dma16<kStreamCopies>(buf ? mst_a1 : mst_a0, src);
   };
   auto issue_k = [&](int2 p) {
     if constexpr (BITS == 2) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma16_base(kst_a + 1024 * j, page_of(j < 2 ? p.x : p.y) + KOFF, koff[j & 1]);
+      for (int j = 0; j < 4; ++j) dma16_base<kStreamCopies>(kst_a + 1024 * j, page_of(j < 2 ? p.x : p.y) + KOFF, koff[j & 1]);
     } else {
 #pragma unroll
       for (int j = 0; j < NCP; ++j)
-        dma16_base(kst_a + 1024 * j, page_of(j < NCP / 2 ? p.x : p.y) + KOFF + 1024 * (j % (NCP / 2)), lane * 16);
+        dma16_base<kStreamCopies>(kst_a + 1024 * j, page_of(j < NCP / 2 ? p.x : p.y) + KOFF + 1024 * (j % (NCP / 2)), lane * 16);
     }
   };
   auto issue_v = [&](int2 p) {
 #pragma unroll
     for (int j = 0; j < NCP; ++j)
-      dma16_base(vst_a + 1024 * j, page_of(j < NCP / 2 ? p.x : p.y) + VOFF + 1024 * (j % (NCP / 2)), lane * 16);
+      dma16_base<kStreamCopies>(vst_a + 1024 * j, page_of(j < NCP / 2 ? p.x : p.y) + VOFF + 1024 * (j % (NCP / 2)), lane * 16);
   };
 
   float qa[NCH];

@@ -1,19 +1,20 @@
 // Read-bandwidth probe of the split-K decode (a measurement hook, no attention arithmetic).
 //
 // The probe reads exactly the quantized head blocks that the matrix-core split-K decode reads for the
-// grouped schemes, with the decode's grid: the same chunks, walks, work-groups (head quads or kv-head rows)
-// and page-pair order, one group (the two pages' head blocks of one kv head) at a time.  Each lane keeps
-// the next group's 16-byte loads in flight while it folds the current group into a running XOR, and each
-// wave stores the XOR of all 32-bit words its walk read.  Timing a launch gives the rate at which the GPU
-// streams this read pattern when nothing else runs; the XOR lets a test confirm that the probe read the
-// bytes the decode reads ([OSCAR] §3.4.5 paged INT2 cache layout; the decode's chunked walk follows
-// [OSCAR] §3.4.5 step 4 and [NOVA] App. B.5, two-stage split-KV).
+// grouped schemes, with the decode's grid (the same chunks, walks, work-groups of head quads or kv-head rows,
+// and page-pair order) and its streaming (non-temporal) read policy, one group (the two pages' head blocks
+// of one kv head) at a time.  Each lane keeps the next group's 16-byte loads in flight while it folds the
+// current group into a running XOR, and each wave stores the XOR of all 32-bit words its walk read.  Timing
+// a launch gives the rate at which the GPU streams this read pattern when nothing else runs; the XOR lets a
+// test confirm that the probe read the bytes the decode reads ([OSCAR] §3.4.5 paged INT2 cache layout; the
+// decode's chunked walk follows [OSCAR] §3.4.5 step 4 and [NOVA] App. B.5, two-stage split-KV).
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
 constexpr int kProbeThreads = 256;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // NK 1 KB wave loads per group: the two pages' head blocks of one kv head (2 x 4608 B for 2-bit codes,
 // 2 x 8704 B for 4-bit codes), lane-contiguous 16-byte pieces
@@ -46,7 +47,8 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(DecodeArgs a,
     for (int k = 0; k < NK; ++k) {
       const long long off = 1024LL * k + 16 * lane;  // inside the 2 hb bytes of the group (NK KB = 2 hb)
       const uint8_t* src = off < hb ? p0 + off : p1 + (off - hb);
-      v[k] = *reinterpret_cast<const uint4*>(src);
+      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));  // streaming, as the decode
+      v[k] = make_uint4(w.x, w.y, w.z, w.w);
     }
   };
   uint32_t acc = 0;
