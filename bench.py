@@ -31,8 +31,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_int2_batch32_32k_traffic.t
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    # measured on MI355X: the first ~70 decode steps of a run take about 10% longer while the GPU settles
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="batch32_32k")
     ap.add_argument("--impl", default="auto", choices=["auto", "f32", "mfma"])
     ap.add_argument("--scheme", default=None, choices=["int2_channel", "int2_token", "int4_channel"],
@@ -521,12 +522,12 @@ def measure_decode(wl, args, K, synth, np, torch):
     ws = K.workspace_for(cfg, B, T_end, dev)
 
     # one step = the append write, then the decode (query prep with the bf16 band, split-K partials of the
-    # quantized chunks, merge).  Most timed steps make one kv_decode_attn call; every SAMPLE-th launches the
-    # three kernels one by one with HIP events on their stream (torch's current stream, which the binding
-    # passes to the library) around the split-K kernel.  Each event costs a few us of idle GPU between
-    # kernels, so the sampled steps alone carry them.  Warm-up steps bracket every kernel, for the query-prep
-    # and merge times.
-    SAMPLE = 5
+    # quantized chunks, merge).  Most timed steps make one kv_decode_attn call; every SAMPLE-th makes one
+    # kv_decode_attn_timed call, whose split-K dispatch itself records two HIP events at the kernel's start
+    # and end (on the call's stream: torch's current stream, which the binding passes to the library), so the
+    # interval is the kernel's own whatever the host does.  Warm-up steps launch the three kernels one by one
+    # with events around each, for the query-prep and merge times.
+    SAMPLE = 10
     names = ("qprep", "splitk", "merge")
     stages = (K.STAGE_QPREP, K.STAGE_SPLITK, K.STAGE_MERGE)
 
@@ -545,6 +546,10 @@ def measure_decode(wl, args, K, synth, np, torch):
     def step(i):
         write(i)
         K.kv_decode_attn(cache, qs[i], out, T_end, ws)
+
+    def timed_step(i, ev):
+        write(i)
+        K.kv_decode_attn_timed(cache, qs[i], out, T_end, ws, ev[0], ev[1])
 
     def pairs(n):
         return [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in stages]
@@ -572,9 +577,10 @@ def measure_decode(wl, args, K, synth, np, torch):
     t0 = time.perf_counter()
     for n, i in enumerate(range(first, n_steps)):
         if n % SAMPLE == 0:
-            staged_step(i, evs[n], (1,))
+            timed_step(i, evs[n][1])
         else:
             step(i)
+    host_ms = (time.perf_counter() - t0) * 1e3 / args.steps  # the host's enqueue time per step
     torch.cuda.synchronize()
     ms_timed = (time.perf_counter() - t0) * 1e3 / args.steps
     assert np.array_equal(cache.seq_lens.cpu().numpy().astype(np.int64), lens_end)
@@ -585,7 +591,8 @@ def measure_decode(wl, args, K, synth, np, torch):
             r = lens_before + s_ - wl.n_sink - wl.n_recent
             n_dem += int(((r > 0) & (r % 128 == 0)).sum())
     ms_step = max(ms_timed, dem_ms) if dem_ms is not None else ms_timed
-    log(f"[bench] {args.steps} timed steps: {ms_timed:.4f} ms/step ({n_dem} demotions); 128-step window "
+    log(f"[bench] {args.steps} timed steps: {ms_timed:.4f} ms/step ({n_dem} demotions; host enqueue "
+        f"{host_ms:.4f} ms/step); 128-step window "
         f"{dem_ms if dem_ms is None else round(dem_ms, 4)} ms/step")
 
     # algorithmic bytes of each timed step (lengths after that step's append)

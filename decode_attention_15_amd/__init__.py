@@ -104,6 +104,8 @@ _lib_decode_shape = _sig("kvq_decode_shape_of", ctypes.c_int, _CFG, ctypes.c_int
 _lib_decode_noalloc = _sig("kv_decode_attn_noalloc", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P,
                            ctypes.c_int32, _P)
 NOALLOC_SCRATCH_BYTES = 64 << 20
+_lib_decode_timed = _sig("kv_decode_attn_timed", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P, ctypes.c_int32,
+                         _P, ctypes.c_size_t, _P, _P, _P)
 _lib_read_probe = _sig("kvq_read_probe", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P)
 _lib_decode_stages = _sig("kv_decode_attn_stages", ctypes.c_int, _CFG, _CACHE, _P, ctypes.c_int32, _P, ctypes.c_int32,
                           _P, ctypes.c_size_t, ctypes.c_int32, _P)
@@ -119,6 +121,7 @@ EXPORTED = [
     "kvq_build_hadamard_rotation", "kvq_query_covariance", "kvq_score_value_covariance", "kvq_eigenbasis",
     "kvq_build_oscar_rotation_from_covariance", "kvq_prefill_workspace_bytes", "kv_prefill_attn",
     "kv_rotate_quant_write", "kv_decode_attn", "kv_decode_attn_stages", "kv_decode_attn_noalloc",
+    "kv_decode_attn_timed",
     "kvq_decode_shape_of", "kvq_read_probe",
     "kvq_debug_rotate", "kvq_debug_unpack", "kvq_build_page_table", "kvq_check_page_table",
     "kvq_strerror", "kvq_version", "kvq_last_error",
@@ -381,6 +384,20 @@ def kv_decode_attn_stages(cache: DeviceCache, q, out, max_seq_len: int, workspac
     _check(_lib_decode_stages(ctypes.byref(cache.cfg), ctypes.byref(cs), _ptr(q), _dtype_code(q), _ptr(out),
                               int(max_seq_len), _ptr(workspace), workspace.numel() * workspace.element_size(),
                               int(stages), _stream(stream)), "kv_decode_attn_stages")
+
+
+def kv_decode_attn_timed(cache: DeviceCache, q, out, max_seq_len: int, workspace, split_begin, split_end,
+                         stream=None) -> None:
+    """kv_decode_attn with torch.cuda.Event(enable_timing=True) events that the split-K dispatch records at
+    the kernel's start and end.  torch creates an event's HIP event at its first record, so an event never
+    recorded before is recorded once here first (a marker on the stream, no device work)."""
+    for ev in (split_begin, split_end):
+        if not ev.cuda_event:
+            ev.record()
+    cs = cache.c_struct()
+    _check(_lib_decode_timed(ctypes.byref(cache.cfg), ctypes.byref(cs), _ptr(q), _dtype_code(q), _ptr(out),
+                             int(max_seq_len), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             split_begin.cuda_event, split_end.cuda_event, _stream(stream)), "kv_decode_attn_timed")
 
 
 def kvq_debug_rotate(cache: DeviceCache, which: int, x, rho: float, out, stream=None) -> None:

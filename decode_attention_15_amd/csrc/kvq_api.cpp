@@ -398,9 +398,10 @@ int kv_decode_attn(const kvq_config* cfg, const kvq_cache* cache, const void* q,
                                stream);
 }
 
-int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t dtype, float* out,
-                          int32_t max_seq_len_host, void* workspace, size_t ws_bytes, int32_t stages,
-                          hipStream_t stream) {
+namespace {
+int decode_with(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t dtype, float* out,
+                int32_t max_seq_len_host, void* workspace, size_t ws_bytes, int32_t stages, hipEvent_t split_begin,
+                hipEvent_t split_end, hipStream_t stream) {
   if (stages < 0 || stages > KVQ_STAGE_ALL) return KVQ_EINVAL;
   int st = check_config(cfg);
   if (st != KVQ_OK) return st;
@@ -431,7 +432,23 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
   a.partials = ws + 2 * nq * D;
   a.impl = mfma ? KVQ_DECODE_MFMA : KVQ_DECODE_F32;
   clear_stale_error();
-  return to_status(launch_decode(a, stages, stream), "kv_decode_attn");
+  return to_status(launch_decode(a, stages, stream, split_begin, split_end), "kv_decode_attn");
+}
+}  // namespace
+
+int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t dtype, float* out,
+                          int32_t max_seq_len_host, void* workspace, size_t ws_bytes, int32_t stages,
+                          hipStream_t stream) {
+  return decode_with(cfg, cache, q, dtype, out, max_seq_len_host, workspace, ws_bytes, stages, nullptr, nullptr,
+                     stream);
+}
+
+int kv_decode_attn_timed(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t dtype, float* out,
+                         int32_t max_seq_len_host, void* workspace, size_t ws_bytes, hipEvent_t split_begin,
+                         hipEvent_t split_end, hipStream_t stream) {
+  if (!split_begin || !split_end) return KVQ_EINVAL;
+  return decode_with(cfg, cache, q, dtype, out, max_seq_len_host, workspace, ws_bytes, KVQ_STAGE_ALL, split_begin,
+                     split_end, stream);
 }
 
 int kvq_decode_shape_of(const kvq_config* cfg, int32_t batch, int32_t max_seq_len, kvq_decode_shape* out) {

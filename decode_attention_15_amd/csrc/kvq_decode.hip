@@ -14,6 +14,8 @@
 // so per element the kernel only converts a 2-bit code and multiplies.
 #include <hip/hip_runtime.h>
 
+#include <hip/hip_ext.h>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -1808,21 +1810,26 @@ __global__ __launch_bounds__(MergeShape<HPW>::NT) void merge_kernel(DecodeArgs a
 }
 
 template <int GQ>
-hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s) {
+hipError_t launch_gq(const DecodeArgs& a, int stages, hipStream_t s, hipEvent_t split_begin, hipEvent_t split_end) {
   const Geo& g = a.g;
   if (stages & KVQ_STAGE_QPREP) hipLaunchKernelGGL(prep_kernel<GQ>, dim3(g.n_kv, g.batch), dim3(512), 0, s, a);
   if (stages & KVQ_STAGE_SPLITK) {
-    // matrix-core decode: a wave per chunk, four chunks per work-group; fp32 decode: a chunk per work-group
+    // matrix-core decode: a wave per chunk, four chunks per work-group; fp32 decode: a chunk per work-group.
+    // With events, the dispatch itself records them at the kernel's start and end (hipExtLaunchKernel).
     const dim3 grid(splitk_wgs(g)), block(kThreads);
+    auto launch = [&](auto kernel) {
+      if (split_begin) hipExtLaunchKernelGGL(kernel, grid, block, 0, s, split_begin, split_end, 0, a);
+      else hipLaunchKernelGGL(kernel, grid, block, 0, s, a);
+    };
     if (a.impl == KVQ_DECODE_MFMA) {
-      if (g.scheme == KVQ_INT4_CHANNEL) hipLaunchKernelGGL((decode_mfma_kernel<GQ, false, 4>), grid, block, 0, s, a);
-      else if (g.scheme == KVQ_INT2_TOKEN) hipLaunchKernelGGL((decode_mfma_kernel<GQ, true, 2>), grid, block, 0, s, a);
-      else if (g.scheme == KVQ_INT2_CHANNEL) hipLaunchKernelGGL((decode_mfma_kernel<GQ, false, 2>), grid, block, 0, s, a);
-      else hipLaunchKernelGGL(decode_mfma4_kernel<GQ>, grid, block, 0, s, a);
+      if (g.scheme == KVQ_INT4_CHANNEL) launch(decode_mfma_kernel<GQ, false, 4>);
+      else if (g.scheme == KVQ_INT2_TOKEN) launch(decode_mfma_kernel<GQ, true, 2>);
+      else if (g.scheme == KVQ_INT2_CHANNEL) launch(decode_mfma_kernel<GQ, false, 2>);
+      else launch(decode_mfma4_kernel<GQ>);
     } else {
       // the API admits the fp32 decode for these two schemes only
-      if (g.scheme == KVQ_INT2_CHANNEL) hipLaunchKernelGGL((decode_f32_kernel<GQ, KVQ_INT2_CHANNEL>), grid, block, 0, s, a);
-      else if (g.scheme == KVQ_INT4_TOKEN) hipLaunchKernelGGL((decode_f32_kernel<GQ, KVQ_INT4_TOKEN>), grid, block, 0, s, a);
+      if (g.scheme == KVQ_INT2_CHANNEL) launch(decode_f32_kernel<GQ, KVQ_INT2_CHANNEL>);
+      else if (g.scheme == KVQ_INT4_TOKEN) launch(decode_f32_kernel<GQ, KVQ_INT4_TOKEN>);
       else return hipErrorInvalidValue;
     }
   }
@@ -1850,12 +1857,12 @@ hipError_t launch_qprep_rows(const DecodeArgs& a, int rows, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int stages, hipStream_t s) {
+hipError_t launch_decode(const DecodeArgs& a, int stages, hipStream_t s, hipEvent_t split_begin, hipEvent_t split_end) {
   switch (a.g.gq) {
-    case 1: return launch_gq<1>(a, stages, s);
-    case 2: return launch_gq<2>(a, stages, s);
-    case 4: return launch_gq<4>(a, stages, s);
-    case 8: return launch_gq<8>(a, stages, s);
+    case 1: return launch_gq<1>(a, stages, s, split_begin, split_end);
+    case 2: return launch_gq<2>(a, stages, s, split_begin, split_end);
+    case 4: return launch_gq<4>(a, stages, s, split_begin, split_end);
+    case 8: return launch_gq<8>(a, stages, s, split_begin, split_end);
     default: return hipErrorInvalidValue;
   }
 }

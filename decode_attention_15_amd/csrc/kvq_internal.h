@@ -217,7 +217,9 @@ struct DecodeArgs {
 
 constexpr int PART_STRIDE = 2 + D;  // m, l, o[128]
 
-hipError_t launch_decode(const DecodeArgs& a, int stages, hipStream_t s);
+// split_begin / split_end (null, or both set): events the split-K dispatch records at the kernel's start and end
+hipError_t launch_decode(const DecodeArgs& a, int stages, hipStream_t s, hipEvent_t split_begin = nullptr,
+                         hipEvent_t split_end = nullptr);
 // query rotation of `rows` query rows (q, qrot, qband indexed as [row][n_q][128])
 hipError_t launch_qprep_rows(const DecodeArgs& a, int rows, hipStream_t s);
 hipError_t launch_prefill(const DecodeArgs& a, int max_q, hipStream_t s);

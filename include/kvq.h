@@ -277,6 +277,15 @@ int kv_decode_attn_stages(const kvq_config* cfg, const kvq_cache* cache, const v
                           int32_t max_seq_len_host, void* workspace, size_t ws_bytes, int32_t stages,
                           hipStream_t stream);
 
+/* kv_decode_attn with two caller-created HIP events (hipEventCreate, timing enabled; the caller owns and
+   destroys them) that the split-K kernel's dispatch itself records at the kernel's start and end
+   (hipExtLaunchKernel), so that hipEventElapsedTime(split_begin, split_end) is the split-K kernel's time
+   whatever the host does around the call (a measurement hook).  Same arguments, results and errors as
+   kv_decode_attn; KVQ_EINVAL for a null event. */
+int kv_decode_attn_timed(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t dtype, float* out,
+                         int32_t max_seq_len_host, void* workspace, size_t ws_bytes, hipEvent_t split_begin,
+                         hipEvent_t split_end, hipStream_t stream);
+
 /* How kv_decode_attn splits its work for a batch of sequences up to max_seq_len tokens (host only; no device
    work): the quantized history of a sequence is cut into chunks of chunk_units groups of 128 tokens (grouped
    schemes) or pages of 64 tokens (INT4 per token), each chunk giving one softmax partial (m, l, o) that the
