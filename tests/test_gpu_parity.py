@@ -202,6 +202,30 @@ def test_decode_is_deterministic(K):
     assert np.array_equal(o1, o2)
 
 
+@pytest.mark.parametrize("name,impl", [("gqa_b1_32k", "auto"), ("gqa_b1_32k", "f32"), ("long_b4_131k", "auto"),
+                                       ("saw_int4_b16_16k", "auto")])
+def test_timed_decode_equals_the_decode(K, name, impl):
+    """kv_decode_attn_timed (events recorded by the split-K dispatch) gives the bytes kv_decode_attn gives,
+    and its events bracket a positive interval."""
+    import torch
+    wl = synth.scaled(synth.WORKLOADS[name], batch=2)
+    decode_impl = {"auto": K.DECODE_AUTO, "f32": K.DECODE_F32}[impl]
+    bc = build_cache(K, wl, [2500, 700], decode_impl=decode_impl)
+    from kvq_cases import source_torch
+    q = source_torch(synth.queries(wl), "cuda")
+    ws = K.workspace_for(bc.cfg, 2, 2500)
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    ref = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    K.kv_decode_attn(bc.cache, q, ref, 2500, ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    K.kv_decode_attn_timed(bc.cache, q, out, 2500, ws, e0, e1)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    ms = e0.elapsed_time(e1)
+    _say(f"timed decode {name} {impl}: split-K {ms * 1e3:.1f} us")
+    assert 0.0 < ms < 100.0
+
+
 def test_error_codes_from_the_device_calls(K):
     import torch
     wl = synth.WORKLOADS["gqa_b1_32k"]
