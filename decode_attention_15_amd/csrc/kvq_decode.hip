@@ -642,7 +642,8 @@ struct Limb3 {
 // heads 2 q + r / 2 with limb r % 2, the top limbs in a second tile at rows 4 q + 2 e.
 template <int GQ>
 __device__ __forceinline__ int limbs3_sum(const mf_i32x4& t, const mf_i32x4& x, int e) {
-  // Horner form: two shift-adds (v_lshl_add_u32)
+  // plain integer arithmetic on the matrix-core results: the compiler places the wait states the matrix
+  // cores need before a vector instruction reads their results (it cannot for inline assembly)
   const uint32_t hi = GQ == 8 ? (uint32_t)x[2 * e] : (uint32_t)t[2];
   const uint32_t mid = GQ == 8 ? (uint32_t)t[2 * e + 1] : (uint32_t)t[1];
   const uint32_t lo = GQ == 8 ? (uint32_t)t[2 * e] : (uint32_t)t[0];

@@ -26,6 +26,8 @@
 // are chosen so that a lane's own results feed the next contraction without moving data between lanes.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -190,6 +192,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeArgs a) {
   // the work-group's last visible position (uniform)
   const int last_q = min(nq - 1, ((int)blockIdx.x * kCols + kCols - 1) / GQ);
   const int pos_max = T - nq + last_q;
+  // every column of the work-group holds a query, the first at position pos_min (uniform)
+  const bool all_cols_valid = ((int)blockIdx.x + 1) * kCols <= nq * GQ;
+  const int pos_min = T - nq + ((int)blockIdx.x * kCols) / GQ;
 
   // ---- band (sink + tail, bf16, original frame): blocks of 64 tokens
   const int ng = SC::GROUPED ? n_groups_of(T, g.S0, g.W) : 0;
@@ -439,82 +444,93 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeArgs a) {
       }
     };
     // 2. logits S^T (128 tokens x 16 columns): token 16 mt + (l % 16) is the A row
-    float lg[8][4];
-    float gm = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const int t = 16 * mt + (lane & 15);
-      const uint32_t* kr = B.k[t >> 6] + SC::KROW * (t & 63);
-      i32x4 cl = {0, 0, 0, 0}, cm = {0, 0, 0, 0}, ch = {0, 0, 0, 0};
-      i32x4 av[2];
-      if constexpr (SC::BITS == 2) {
-        codes_i8_pair(kr[q], kr[4 + q], av[0], av[1]);
-      } else {
-        av[0] = key_codes<SCHEME>(kr, q);
-        av[1] = key_codes<SCHEME>(kr, 4 + q);
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        cl = mfma_i8(av[ks], bq[ks][0], cl);
-        cm = mfma_i8(av[ks], bq[ks][1], cm);
-        ch = mfma_i8(av[ks], bq[ks][2], ch);
-      }
-      float ks4[4], kz4[4];
-      if constexpr (SC::TOK) tok_meta4(mt, 0, ks4, kz4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = 16 * mt + 4 * q + i;
-        float x;
-        if constexpr (SC::TOK) x = (Acol * ks4[i]) * fmaf(-kz4[i], FS_tok, limbs_value(ch, cm, cl, i));
-        else x = fmaf(Acol, limbs_value(ch, cm, cl, i), -AZ);
-        lg[mt][i] = (gpos + tok <= qpos) ? x : -INFINITY;
-        gm = fmaxf(gm, lg[mt][i]);
-      }
-    }
-    gm = col_max(gm);
     // 3. weights as byte limbs.  Per channel u = floor(S p + 0.5), p = 2^(logit - group max); per token
     //    u_t = floor(S p_t s'_t / S' + 0.5), S' = max_t p_t s'_t of the column, with P = sum_t p_t and
     //    Z = sum_t u_t z'_t
+    // FULL: every token of the unit is visible to every column of the work-group (a uniform condition), so
+    // no logit is masked and no weight needs the masked case's checks; the results are the same either way.
+    float gm = -INFINITY;
     float u[8][4];  // magic-rounded weights
     float Pf, Sg = 0.0f, Zt = 0.0f;
-    if constexpr (SC::TOK) {
-      float pw[8][4], vz[8][4], wmx = 0.0f, ps = 0.0f;
+    auto logits_weights = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      float lg[8][4];
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-        float vs4[4];
-        tok_meta4(mt, 1, vs4, vz[mt]);
+        const int t = 16 * mt + (lane & 15);
+        const uint32_t* kr = B.k[t >> 6] + SC::KROW * (t & 63);
+        i32x4 cl = {0, 0, 0, 0}, cm = {0, 0, 0, 0}, ch = {0, 0, 0, 0};
+        i32x4 av[2];
+        if constexpr (SC::BITS == 2) {
+          codes_i8_pair(kr[q], kr[4 + q], av[0], av[1]);
+        } else {
+          av[0] = key_codes<SCHEME>(kr, q);
+          av[1] = key_codes<SCHEME>(kr, 4 + q);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          cl = mfma_i8(av[ks], bq[ks][0], cl);
+          cm = mfma_i8(av[ks], bq[ks][1], cm);
+          ch = mfma_i8(av[ks], bq[ks][2], ch);
+        }
+        float ks4[4], kz4[4];
+        if constexpr (SC::TOK) tok_meta4(mt, 0, ks4, kz4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = exp2_or_zero(lg[mt][i], gm);
-          ps += p;
-          // tokens past the length (their metadata unwritten) take no weight
-          pw[mt][i] = lg[mt][i] == -INFINITY ? 0.0f : p * vs4[i];
-          wmx = fmaxf(wmx, pw[mt][i]);
+          const int tok = 16 * mt + 4 * q + i;
+          float x;
+          if constexpr (SC::TOK) x = (Acol * ks4[i]) * fmaf(-kz4[i], FS_tok, limbs_value(ch, cm, cl, i));
+          else x = fmaf(Acol, limbs_value(ch, cm, cl, i), -AZ);
+          lg[mt][i] = (FULL || gpos + tok <= qpos) ? x : -INFINITY;
+          gm = fmaxf(gm, lg[mt][i]);
         }
       }
-      Sg = col_max(wmx);
-      Pf = col_sum(ps);
-      // below 2^-100 the unit's value terms are beyond fp32's reach next to the others: weights 0
-      const float r = Sg > 0x1p-100f ? S / Sg : 0.0f;
-      float zs = 0.0f;
+      gm = col_max(gm);
+      auto weight = [&](float x) { return FULL ? __builtin_amdgcn_exp2f(x - gm) : exp2_or_zero(x, gm); };
+      if constexpr (SC::TOK) {
+        float pw[8][4], vz[8][4], wmx = 0.0f, ps = 0.0f;
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
+        for (int mt = 0; mt < 8; ++mt) {
+          float vs4[4];
+          tok_meta4(mt, 1, vs4, vz[mt]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          u[mt][i] = fmaf(pw[mt][i], r, kRound3);
-          if (lg[mt][i] != -INFINITY) zs = fmaf(u[mt][i] - kRound3, vz[mt][i], zs);
+          for (int i = 0; i < 4; ++i) {
+            const float p = weight(lg[mt][i]);
+            ps += p;
+            // tokens past the length (their metadata unwritten) take no weight
+            pw[mt][i] = (!FULL && lg[mt][i] == -INFINITY) ? 0.0f : p * vs4[i];
+            wmx = fmaxf(wmx, pw[mt][i]);
+          }
         }
-      Zt = col_sum(zs);
+        Sg = col_max(wmx);
+        Pf = col_sum(ps);
+        // below 2^-100 the unit's value terms are beyond fp32's reach next to the others: weights 0
+        const float r = Sg > 0x1p-100f ? S / Sg : 0.0f;
+        float zs = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            u[mt][i] = fmaf(pw[mt][i], r, kRound3);
+            if (FULL || lg[mt][i] != -INFINITY) zs = fmaf(u[mt][i] - kRound3, vz[mt][i], zs);
+          }
+        Zt = col_sum(zs);
+      } else {
+        float us = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            u[mt][i] = fmaf(weight(lg[mt][i]), S, kRound3);
+            us += u[mt][i] - kRound3;
+          }
+        Pf = col_sum(us);
+      }
+    };
+    if (all_cols_valid && gpos + GROUP - 1 <= pos_min) {
+      logits_weights(std::true_type{});
     } else {
-      float us = 0.0f;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          u[mt][i] = fmaf(exp2_or_zero(lg[mt][i], gm), S, kRound3);
-          us += u[mt][i] - kRound3;
-        }
-      Pf = col_sum(us);
+      logits_weights(std::false_type{});
     }
     // B operand of page kp: dword d, byte bb holds the weight of token 16 J + 4 q + R of the page, i.e. this
     // lane's logit (tile 4 kp + J, i = R)
