@@ -172,6 +172,36 @@ __device__ __forceinline__ void limbs3(float e0, float e1, float e2, float e3, u
   hi = y | ((y & 0x40404040u) << 1);  // bit 6 extended into bit 7: y2 - 64 as a signed byte
 }
 
+// bf16 matrix-core operands: fp32 values split into bf16 hi + lo (hi the round-to-nearest-even bf16 of x, lo
+// that of the remainder: about 16 significant bits together) for v_mfma_f32_16x16x32_bf16, whose products of
+// bf16 values are exact and whose sums are fp32
+typedef __attribute__((ext_vector_type(4))) float kvq_f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int kvq_u32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 kvq_bf16x8;
+__device__ inline kvq_f32x4 mfma_bf16(kvq_u32x4 a, kvq_u32x4 b, kvq_f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(kvq_bf16x8, a), __builtin_bit_cast(kvq_bf16x8, b),
+                                                  c, 0, 0, 0);
+}
+// bf16 round to nearest even as bits (finite inputs)
+__device__ inline uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ inline void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t h0 = bf16_bits(x0), h1 = bf16_bits(x1);
+  const uint32_t l0 = bf16_bits(x0 - __uint_as_float(h0 << 16)), l1 = bf16_bits(x1 - __uint_as_float(h1 << 16));
+  hi = h0 | (h1 << 16);
+  lo = l0 | (l1 << 16);
+}
+// eight floats -> bf16x8 hi and lo operands
+__device__ inline void split8(const float (&x)[8], kvq_u32x4& hi, kvq_u32x4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) split2(x[2 * k], x[2 * k + 1], h[k], l[k]);
+  hi = kvq_u32x4{h[0], h[1], h[2], h[3]};
+  lo = kvq_u32x4{l[0], l[1], l[2], l[3]};
+}
+
 // ---- launchers implemented in kvq_write.hip / kvq_decode.hip ----
 struct WriteArgs {
   Geo g;

@@ -41,29 +41,6 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 constexpr int kCols = 64;        // (query, head) columns per work-group, 16 per wave
 
 __device__ inline i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) { return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0); }
-__device__ inline f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// bf16 round to nearest even as bits (finite inputs), and the split x ~ hi + lo
-__device__ inline uint32_t bf16_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ inline void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const uint32_t h0 = bf16_bits(x0), h1 = bf16_bits(x1);
-  const uint32_t l0 = bf16_bits(x0 - __uint_as_float(h0 << 16)), l1 = bf16_bits(x1 - __uint_as_float(h1 << 16));
-  hi = h0 | (h1 << 16);
-  lo = l0 | (l1 << 16);
-}
-// eight floats -> bf16x8 hi and lo operands
-__device__ inline void split8(const float (&x)[8], u32x4& hi, u32x4& lo) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) split2(x[2 * k], x[2 * k + 1], h[k], l[k]);
-  hi = u32x4{h[0], h[1], h[2], h[3]};
-  lo = u32x4{l[0], l[1], l[2], l[3]};
-}
 
 // the value lo + 256 mid + 65536 hi of element i of three limb sums (exact in int32 at the full scales used)
 __device__ inline float limbs_value(const i32x4& h, const i32x4& m, const i32x4& l, int i) {
