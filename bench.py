@@ -619,7 +619,8 @@ def measure_decode(wl, args, K, synth, np, torch):
     probe = None
     shape = K.decode_shape(cfg, B, T_end)
     if grouped and shape["matrix_cores"]:
-        xo = torch.empty((B, n_kv, shape["walks"]), dtype=torch.int32, device=dev)
+        xo = torch.empty((B, n_kv, shape["max_chunks"] if shape["balanced"] else shape["walks"]), dtype=torch.int32,
+                         device=dev)
         K.read_probe(cache, xo, T_end)
         pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
         for e0, e1 in pev:

@@ -96,7 +96,7 @@ class DecodeShape(ctypes.Structure):
     _fields_ = [("chunk_units", ctypes.c_int32), ("n_chunks", ctypes.c_int32), ("walks", ctypes.c_int32),
                 ("span", ctypes.c_int32),
                 ("splitk_workgroups", ctypes.c_int32), ("band_first", ctypes.c_int32),
-                ("matrix_cores", ctypes.c_int32)]
+                ("matrix_cores", ctypes.c_int32), ("balanced", ctypes.c_int32), ("max_chunks", ctypes.c_int32)]
 
 
 _lib_decode_shape = _sig("kvq_decode_shape_of", ctypes.c_int, _CFG, ctypes.c_int32, ctypes.c_int32,
@@ -359,11 +359,13 @@ def decode_shape(cfg: Config, batch: int, max_seq_len: int) -> dict:
 
 
 def read_probe(cache: DeviceCache, xor_out, max_seq_len: int, stream=None) -> None:
-    """The decode's read pattern with no arithmetic: xor_out (uint32-sized int32 [batch, n_kv, walks]) gets the
-    XOR of the 32-bit words each walk of the split-K decode reads."""
+    """The decode's read pattern with no arithmetic: xor_out (uint32-sized int32 [batch, n_kv, slots]) gets the
+    XOR of the 32-bit words each walk of the split-K decode reads; slots = walks, or max_chunks under balanced
+    chunking."""
     assert xor_out.is_contiguous() and xor_out.element_size() == 4
     shape = decode_shape(cache.cfg, cache.batch, max_seq_len)
-    assert xor_out.numel() == cache.batch * cache.cfg.n_kv_heads * shape["walks"]
+    slots = shape["max_chunks"] if shape["balanced"] else shape["walks"]
+    assert xor_out.numel() == cache.batch * cache.cfg.n_kv_heads * slots
     cs = cache.c_struct()
     _check(_lib_read_probe(ctypes.byref(cache.cfg), ctypes.byref(cs), _ptr(xor_out), int(max_seq_len),
                            _stream(stream)), "kvq_read_probe")

@@ -86,8 +86,18 @@ int wgs_per_cu(const kvq_config* c) {
   return gq_of(c) <= 4 ? (four ? 2 : 3) : (four ? 1 : 2);
 }
 
+// Balanced automatic chunking: the matrix-core decode of the grouped schemes in head quads with no explicit
+// split picks its chunk size on the device from the batch's actual lengths (at least 4 groups), so that a
+// batch of short and long sequences spreads its groups evenly over the work-groups of one round.
+bool balanced_mode(const kvq_config* c) {
+  return uses_mfma(c) && is_grouped(c->scheme) && c->split_tokens <= 0 && c->n_kv_heads % 4 == 0;
+}
+constexpr int kBalancedFloor = 4;  // groups per chunk at least
+constexpr size_t kSchedBytes = 256;  // the workspace's tail: the balanced chunk size
+
 int chunk_units(const kvq_config* c, int batch, int max_seq_len) {
   if (c->split_tokens > 0) return c->split_tokens / (is_grouped(c->scheme) ? GROUP : PAGE);
+  if (balanced_mode(c)) return kBalancedFloor;
   int units;  // quantized groups/pages per sequence
   if (is_grouped(c->scheme)) units = n_groups_of(max_seq_len, c->n_sink, c->n_recent);
   else units = (max_seq_len + PAGE - 1) / PAGE;
@@ -156,6 +166,16 @@ void set_decode_shape(const kvq_config* c, int max_seq_len, Geo& g) {
   const bool mfma = uses_mfma(c);
   g.wave_chunks = mfma ? 1 : 0;
   g.walks = mfma ? walks_of(c, g.batch, g.n_units - 1, per) : 1;
+  g.balanced = balanced_mode(c) ? 1 : 0;
+  if (g.balanced) {
+    // one chunk per work-group: as many chunk work-groups as one round holds beside the band work-groups, and
+    // at least one per (sequence, head quad), so that one chunk per row always fits
+    const long long rows = (long long)g.batch * (c->n_kv_heads / 4);
+    long long slots = 256LL * wgs_per_cu(c) - (long long)g.batch * c->n_kv_heads;
+    if (slots < 256) slots = 256;
+    g.nwg = (int)(rows > slots ? rows : slots);
+    g.walks = g.n_units - 1;  // chunks of one (sequence, head quad) at most
+  }
   // band work-groups first when the split-K launch takes more than one round of work-groups (see the grid)
   g.band_first = splitk_wgs(g) > 256LL * wgs_per_cu(c) ? 1 : 0;
 }
@@ -320,7 +340,7 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t batch, int32_t 
   const int per = chunk_units(cfg, batch, max_seq_len);
   const int n_units = 1 + max_chunks_of(cfg, max_seq_len, per);
   const size_t nq = (size_t)batch * cfg->n_q_heads;
-  return sizeof(float) * (2 * nq * D + nq * (size_t)n_units * PART_STRIDE);
+  return sizeof(float) * (2 * nq * D + nq * (size_t)n_units * PART_STRIDE) + kSchedBytes;
 }
 
 double kvq_bits_per_element(const kvq_config* cfg, int64_t seq_len) {
@@ -430,6 +450,7 @@ int decode_with(const kvq_config* cfg, const kvq_cache* cache, const void* q, in
   a.qrot = ws;
   a.qband = ws + nq * D;
   a.partials = ws + 2 * nq * D;
+  a.sched = reinterpret_cast<int*>(a.partials + nq * (size_t)a.g.n_units * PART_STRIDE);
   a.impl = mfma ? KVQ_DECODE_MFMA : KVQ_DECODE_F32;
   clear_stale_error();
   return to_status(launch_decode(a, stages, stream, split_begin, split_end), "kv_decode_attn");
@@ -467,6 +488,21 @@ int kvq_decode_shape_of(const kvq_config* cfg, int32_t batch, int32_t max_seq_le
   out->splitk_workgroups = splitk_wgs(g);
   out->band_first = g.band_first;
   out->matrix_cores = g.wave_chunks;
+  out->balanced = g.balanced;
+  out->max_chunks = g.n_units - 1;
+  if (g.balanced) {
+    // the device's rule when every sequence has max_seq_len tokens: the smallest G >= the floor whose chunks
+    // fit the chunk work-groups
+    const long long rows = (long long)batch * (cfg->n_kv_heads / 4);
+    const long long ng = n_groups_of(max_seq_len, cfg->n_sink, cfg->n_recent);
+    long long G = (rows * ng + g.nwg - 1) / g.nwg;
+    if (G < g.gpc) G = g.gpc;
+    while (ng > 0 && rows * ((ng + G - 1) / G) > g.nwg) ++G;
+    out->chunk_units = (int32_t)G;
+    out->n_chunks = ng > 0 ? (int32_t)((ng + G - 1) / G) : 0;
+    out->walks = out->n_chunks;
+    out->span = 1;
+  }
   return KVQ_OK;
 }
 

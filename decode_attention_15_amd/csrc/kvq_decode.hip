@@ -843,7 +843,7 @@ __host__ __device__ constexpr int mf_key_channel_c4(int Q) {
 }
 
 template <int GQ, bool TOK, int BITS, typename Lds>
-__device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T, int c0, int c1) {
+__device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T, int c0, int c1, int gpc) {
   constexpr int LG = HeadLog2<GQ>::v;
   constexpr int LPH = 64 >> LG;        // lanes per head in the alpha step
   constexpr int NCH = 2 * GQ;          // key positions per lane in the alpha step
@@ -858,10 +858,12 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ng = n_groups_of(T, g.S0, g.W);
-  // this wave walks chunks c0 .. c1 - 1 (groups g_first .. g_end - 1), storing a partial per chunk
-  const int g_first = c0 * g.gpc;
-  int g_end = c1 * g.gpc;
+  // this wave walks chunks c0 .. c1 - 1 of gpc groups (groups g_first .. g_end - 1), storing a partial per
+  // chunk; groups past the launch bound are cut
+  const int g_first = c0 * gpc;
+  int g_end = c1 * gpc;
   if (g_end > ng) g_end = ng;
+  if (g_end > (g.n_units - 1) * g.gpc) g_end = (g.n_units - 1) * g.gpc;
   if (g_end > g.max_pages / 2) g_end = g.max_pages / 2;            // never index past the page-table row
   MfmaWave<GQ, KU>& W = L.mf.w[wave];
   const int q4 = lane >> 4, c = lane & 15;
@@ -1006,7 +1008,7 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   };
   const mf_i32x4 zero4 = {0, 0, 0, 0};
   const mf_i32x4 ones4 = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
-  int left = g.gpc;  // groups left in the current chunk
+  int left = gpc;  // groups left in the current chunk
   for (int gi = g_first; gi < g_end; ++gi) {
     const bool has_next = gi + 1 < g_end;  // uniform
     KVQ_WAIT_VM(0);  // this group's metadata, key and value codes, and the next group's pages
@@ -1245,8 +1247,8 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     }
     mb ^= 1;
     if (--left == 0 || !has_next) {  // uniform: the end of a chunk
-      store_partial(gi / g.gpc);
-      left = g.gpc;
+      store_partial(gi / gpc);
+      left = gpc;
     }
   }
 }
@@ -1593,13 +1595,23 @@ __global__ __launch_bounds__(kThreads, GQ <= 4 ? (BITS == 2 ? 3 : 2) : (BITS == 
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (g.balanced) {
+    // the chunk size from the batch's lengths (every wave computes it), one chunk per work-group
+    const int lane = threadIdx.x & 63;
+    const int G = balanced_gpc(g, a.seq_lens, lane);
+    if (i == 0 && threadIdx.x == 0) a.sched[0] = G;  // for the merge
+    int b, quad, c;
+    if (!balanced_wg(g, a.seq_lens, i, lane, G, b, quad, c)) return;  // uniform over the work-group
+    int2_unit_mfma<GQ, TOK, BITS>(L, a, b, 4 * quad + wave, a.seq_lens[b], c, c + 1, G);
+    return;
+  }
   int b, h, c0, c1;
   const int first = wave_chunk_of(g, i, wave, b, h, c0, c1);
   const int T = a.seq_lens[b];
   int n_chunks = (n_groups_of(T, g.S0, g.W) + g.gpc - 1) / g.gpc;
   if (n_chunks > g.n_units - 1) n_chunks = g.n_units - 1;  // lengths beyond the launch bound are cut
   if (first >= n_chunks) return;                           // uniform over the work-group
-  int2_unit_mfma<GQ, TOK, BITS>(L, a, b, h, T, c0, c1);
+  int2_unit_mfma<GQ, TOK, BITS>(L, a, b, h, T, c0, c1, g.gpc);
 }
 
 // Matrix-core INT4 per-token launch (page pairs; no band: the band work-groups store an empty partial).
@@ -1788,6 +1800,12 @@ __global__ __launch_bounds__(MergeShape<HPW>::NT) void merge_kernel(DecodeArgs a
     for (int i = 0; i < CPP / 4; ++i) rrow[i] = row[i];
   }
   const int n_max = g.n_units - 1;
+  // balanced chunking: the chunk size the split-K launch chose (read with the first partials)
+  int gb = 1;
+  if (g.balanced) {
+    gb = a.sched[0];
+    if (gb < 1) gb = 1;
+  }
   int n_chunks = 0, seq_len = 0;  // set on the first pass below, once the first partials are in flight
 
   // 1. per head: M = max_u m_u, L = sum_u 2^(m_u - M) l_u, o[c] = sum_u 2^(m_u - M) o_u[c].  Sub-block sb
@@ -1827,7 +1845,9 @@ __global__ __launch_bounds__(MergeShape<HPW>::NT) void merge_kernel(DecodeArgs a
     load(u1 <= n_max ? u1 : n_max, mu, lu, o01, o23);
     if (h0 == 0) {
       const int T = a.seq_lens[b];
-      if (is_grouped(g.scheme)) {
+      if (g.balanced) {
+        n_chunks = (balanced_groups(g, T) + gb - 1) / gb;
+      } else if (is_grouped(g.scheme)) {
         n_chunks = (n_groups_of(T, g.S0, g.W) + g.gpc - 1) / g.gpc;
       } else {
         n_chunks = ((T + PAGE - 1) / PAGE + g.gpc - 1) / g.gpc;

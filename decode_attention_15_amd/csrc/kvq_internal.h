@@ -57,6 +57,8 @@ struct Geo {
   int walks;        // matrix-core decode: walks per (sequence, head quad) or per (sequence, kv head); walk w
                     // of n chunks takes chunks w n / walks .. (w + 1) n / walks - 1 (a partial per chunk)
   int band_first;   // 1: the split-K grid starts with its band work-groups (launches of more than one round)
+  int balanced;     // 1: chunk size chosen on the device from the batch's lengths (gpc is its floor; see below)
+  int nwg;          // balanced: chunk work-groups of the launch
 };
 
 // both INT2 schemes share the page layout; they and per-channel INT4 share the band and the group demotion
@@ -76,6 +78,7 @@ __host__ __device__ inline int n_groups_of(int T, int S0, int W) {
 //  - fp32 decode: one chunk of one (sequence, kv head), shared by the four waves.
 __host__ __device__ inline bool splitk_head_quads(const Geo& g) { return g.wave_chunks && g.n_kv % 4 == 0; }
 __host__ __device__ inline int splitk_chunk_wgs(const Geo& g) {
+  if (g.balanced) return g.nwg;
   const int nc = g.n_units - 1;
   if (!g.wave_chunks) return g.batch * g.n_kv * nc;
   if (splitk_head_quads(g)) return g.batch * (g.n_kv / 4) * g.walks;
@@ -88,6 +91,95 @@ __host__ __device__ inline void walk_chunks(const Geo& g, int w, int* c0, int* c
   *c1 = (int)((w + 1) * nc / g.walks);
 }
 __host__ __device__ inline int splitk_wgs(const Geo& g) { return splitk_chunk_wgs(g) + g.batch * g.n_kv; }
+
+// ---- balanced automatic chunking (g.balanced) ----
+// The chunk size G (groups) is the smallest G >= g.gpc for which the chunks of every (sequence, head quad),
+// ceil(groups / G) each, fit the g.nwg chunk work-groups; chunk work-group i takes one chunk, sequences in
+// order, then chunks, then head quads.  A sequence's groups are cut at the launch bound ((n_units - 1) gpc,
+// so that no chunk index reaches n_units - 1) and at the page-table row.  The functions are wave-level: the
+// calling wave's 64 lanes all take part and all get the results.
+__device__ inline int balanced_groups(const Geo& g, int T) {
+  const int n = n_groups_of(T, g.S0, g.W);
+  int cap = (g.n_units - 1) * g.gpc;
+  if (cap > g.max_pages / 2) cap = g.max_pages / 2;
+  return n < cap ? n : cap;
+}
+__device__ inline int wave_sum_i(int x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+__device__ inline int wave_max_i(int x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const int y = __shfl_xor(x, m, 64);
+    x = x > y ? x : y;
+  }
+  return x;
+}
+// chunk work-groups the batch needs at chunk size G
+__device__ inline int balanced_chunks(const Geo& g, const int32_t* seq_lens, int lane, int G) {
+  int c = 0;
+  for (int b0 = 0; b0 < g.batch; b0 += 64) {
+    const int b = b0 + lane;
+    if (b < g.batch) c += (balanced_groups(g, seq_lens[b]) + G - 1) / G;
+  }
+  return __builtin_amdgcn_readfirstlane(wave_sum_i(c)) * (g.n_kv / 4);
+}
+__device__ inline int balanced_gpc(const Geo& g, const int32_t* seq_lens, int lane) {
+  int s = 0, mx = 0;
+  for (int b0 = 0; b0 < g.batch; b0 += 64) {
+    const int b = b0 + lane;
+    const int n = b < g.batch ? balanced_groups(g, seq_lens[b]) : 0;
+    s += n;
+    mx = mx > n ? mx : n;
+  }
+  s = wave_sum_i(s) * (g.n_kv / 4);
+  mx = wave_max_i(mx);
+  // the results are wave-uniform: say so to the compiler (scalar registers)
+  s = __builtin_amdgcn_readfirstlane(s);
+  mx = __builtin_amdgcn_readfirstlane(mx);
+  int lo = (s + g.nwg - 1) / g.nwg;
+  if (lo < g.gpc) lo = g.gpc;
+  if (balanced_chunks(g, seq_lens, lane, lo) <= g.nwg) return lo;
+  // chunks(lo) > nwg >= chunks(mx): at G = mx every (sequence, head quad) has at most one chunk and the host
+  // gives at least one work-group per (sequence, head quad); the count does not grow with G
+  int hi = mx;
+  while (hi - lo > 1) {
+    const int mid = lo + (hi - lo) / 2;
+    if (balanced_chunks(g, seq_lens, lane, mid) <= g.nwg) hi = mid;
+    else lo = mid;
+  }
+  return hi;
+}
+// chunk work-group i at chunk size G: its sequence b, head quad and chunk c; false when it has none
+__device__ inline bool balanced_wg(const Geo& g, const int32_t* seq_lens, int i, int lane, int G, int& b,
+                                   int& quad, int& c) {
+  const int quads = g.n_kv / 4;
+  int base = 0;
+  for (int b0 = 0; b0 < g.batch; b0 += 64) {
+    const int bb = b0 + lane;
+    const int cnt = bb < g.batch ? (balanced_groups(g, seq_lens[bb]) + G - 1) / G * quads : 0;
+    int incl = cnt;  // inclusive prefix sum over the lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += t;
+    }
+    const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+    if (i < base + total) {
+      const unsigned long long hit = __ballot(incl > i - base);
+      const int l = __ffsll((long long)hit) - 1;  // the first lane whose prefix passes i
+      const int local = i - base - __builtin_amdgcn_readfirstlane(__shfl(incl - cnt, l, 64));
+      b = __builtin_amdgcn_readfirstlane(b0 + l);
+      c = local / quads;
+      quad = local % quads;
+      return true;
+    }
+    base += total;
+  }
+  return false;
+}
 // matrix-core decode, chunk work-group i: its sequence, and this wave's kv head and walk (chunks c0 .. c1 - 1,
 // empty past the walks); returns the work-group's first chunk (every wave's at least that)
 __device__ inline int wave_chunk_of(const Geo& g, int i, int wave, int& b, int& h, int& c0, int& c1) {
@@ -241,6 +333,7 @@ struct DecodeArgs {
   float* qrot;      // [batch][n_q][128]
   float* qband;     // [batch][n_q][128]
   float* partials;  // [batch][n_q][n_units][PART_STRIDE]
+  int* sched;       // balanced chunking: [0] the chunk size G the split-K launch used (the merge reads it)
   int impl;
   const int32_t* cu_q;  // prefill: [batch + 1] prefix sums of each sequence's chunk queries
 };

@@ -23,20 +23,32 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(DecodeArgs a,
   const Geo& g = a.g;
   const int i = blockIdx.x, lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int b, h, c0, c1;
-  (void)wave_chunk_of(g, i, wave, b, h, c0, c1);
-  // this wave's walk index (the output slot); a wave past the walks of its row has none
-  int w;
-  if (splitk_head_quads(g)) {
-    w = i / (g.batch * (g.n_kv / 4));
+  int b, h, c0, c1, gpc = g.gpc;
+  int w;  // this wave's walk index (the output slot)
+  if (g.balanced) {
+    // the decode's balanced chunking: one chunk of G groups per work-group, the chunk index is the slot
+    gpc = balanced_gpc(g, a.seq_lens, lane);
+    int quad, c;
+    if (!balanced_wg(g, a.seq_lens, i, lane, gpc, b, quad, c)) return;
+    h = 4 * quad + wave;
+    c0 = c;
+    c1 = c + 1;
+    w = c;
   } else {
-    w = 4 * (i / (g.batch * g.n_kv)) + wave;
-    if (w >= g.walks) return;
+    (void)wave_chunk_of(g, i, wave, b, h, c0, c1);
+    // a wave past the walks of its row has none
+    if (splitk_head_quads(g)) {
+      w = i / (g.batch * (g.n_kv / 4));
+    } else {
+      w = 4 * (i / (g.batch * g.n_kv)) + wave;
+      if (w >= g.walks) return;
+    }
   }
   const int T = a.seq_lens[b];
   const int ng = n_groups_of(T, g.S0, g.W);
-  int g_first = c0 * g.gpc, g_end = c1 * g.gpc;
+  int g_first = c0 * gpc, g_end = c1 * gpc;
   if (g_end > ng) g_end = ng;
+  if (g_end > (g.n_units - 1) * g.gpc) g_end = (g.n_units - 1) * g.gpc;  // the launch bound
   if (g_end > g.max_pages / 2) g_end = g.max_pages / 2;  // never index past the page-table row
   const int32_t* ptrow = a.page_table + (long long)b * g.max_pages;
   const long long hb = g.head_bytes, hoff = (long long)h * hb;

@@ -292,7 +292,12 @@ int kv_decode_attn_timed(const kvq_config* cfg, const kvq_cache* cache, const vo
    merge combines ([OSCAR] §3.4.5 step 4, FlashDecoding; [NOVA] App. B.5, two-stage split-KV).  An explicit
    split_tokens fixes the chunks; 0 lets the library size them to the GPU.  On the matrix cores a sequence's
    chunks are split into `walks` runs of consecutive chunks (per head quad, or per kv head when the kv heads
-   do not come in fours), one wave walking each run.  Errors: KVQ_EINVAL (null out, batch < 1, negative
+   do not come in fours), one wave walking each run.  Balanced chunking (balanced = 1: the grouped schemes on
+   the matrix cores, kv heads in fours, split_tokens = 0): the decode picks the chunk size on the device from
+   the batch's actual lengths, the smallest G >= 4 groups whose chunks (ceil(groups / G) per sequence and head
+   quad) fit the launch's chunk work-groups, one chunk per work-group; chunk_units, n_chunks and walks then
+   report the choice for a batch whose every sequence has max_seq_len tokens, and max_chunks the most chunks
+   one sequence can have (the workspace's bound).  Errors: KVQ_EINVAL (null out, batch < 1, negative
    length), config errors. */
 typedef struct kvq_decode_shape {
   int32_t chunk_units;        /* groups (grouped schemes) or pages (INT4 per token) per chunk */
@@ -302,6 +307,8 @@ typedef struct kvq_decode_shape {
   int32_t splitk_workgroups;  /* work-groups of the split-K launch, band work-groups included */
   int32_t band_first;         /* 1: the launch starts with its band work-groups */
   int32_t matrix_cores;       /* 1: the matrix-core decode runs, 0: the fp32 decode */
+  int32_t balanced;           /* 1: balanced chunking, the chunk size chosen on the device from the lengths */
+  int32_t max_chunks;         /* chunks of one sequence at most (partials per q head the workspace holds, less 1) */
 } kvq_decode_shape;
 int kvq_decode_shape_of(const kvq_config* cfg, int32_t batch, int32_t max_seq_len, kvq_decode_shape* out);
 
@@ -310,7 +317,9 @@ int kvq_decode_shape_of(const kvq_config* cfg, int32_t batch, int32_t max_seq_le
    same chunks, walks, work-groups and page-pair order ([OSCAR] §3.4.5, the paged INT2 cache and its chunked
    decode walk), and only folds the 32-bit words each walk read with XOR: xor_out[(b * n_kv_heads + h) * walks
    + w] (device, uint32, batch * n_kv_heads * walks words, `walks` from kvq_decode_shape_of) receives walk w's
-   XOR for sequence b and kv head h, 0 for a walk with no quantized group.  The band is not read.  Timing it
+   XOR for sequence b and kv head h, 0 for a walk with no quantized group.  Under balanced chunking the slots
+   are [(b * n_kv_heads + h) * max_chunks + c], chunk c of the decode's choice for the actual lengths, and
+   the slots past a sequence's chunk count are left as they were.  The band is not read.  Timing it
    gives the rate at which the GPU streams the decode's read pattern with no arithmetic beside it.  Grouped
    schemes on the matrix-core decode only: KVQ_EUNSUPPORTED for INT4 per token or decode_impl = fp32.  Other
    errors as kv_decode_attn (config, cache, KVQ_EINVAL for a null xor_out or negative length, KVQ_ERANGE when

@@ -111,6 +111,39 @@ def test_mfma_walks_several_chunks(K, name, kw, batch, lo, hi):
     _say(f"   worst |mfma - oracle| = {worst:.2e}")
 
 
+@pytest.mark.parametrize("name,kw,batch,lo,hi", [
+    ("batch32_32k", {}, 32, 300, 9000),                            # GQA 4
+    ("long_b4_131k", dict(split_tokens=0), 16, 1000, 12000),        # GQA 8
+    ("batch32_32k", dict(scheme="int4_channel"), 16, 300, 6000),   # 4-bit codes
+])
+def test_balanced_chunking_ragged(K, name, kw, batch, lo, hi):
+    """Automatic chunks chosen on the device from the batch's lengths (balanced chunking): ragged lengths, two of
+    them without a quantized group, put the chunk size between the 4-group floor and the longest sequence; the
+    whole output is compared with the fp32 decode of the same cache and sampled heads with the oracle."""
+    wl = synth.scaled(synth.WORKLOADS[name], batch=batch, **kw)
+    rng = np.random.default_rng(batch * 131 + lo)
+    lens = rng.integers(lo, hi + 1, size=batch)
+    lens[1] = 0
+    lens[batch - 3] = 200
+    bc = build_cache(K, wl, lens, decode_impl=K.DECODE_MFMA, seqs_per_call=8)
+    shape = K.decode_shape(bc.cfg, batch, int(lens.max()))
+    _say(f"balanced: {name} {kw} batch {batch}, lens {lens.min()}..{lens.max()}: {shape}")
+    assert shape["balanced"] == 1
+    q = synth.queries(wl)
+    out = run_decode(K, bc, q)
+    assert np.isfinite(out).all()
+    if wl.scheme == "int2_channel":  # the fp32 decode covers INT2 per channel and INT4 per token
+        bc.cfg.decode_impl = K.DECODE_F32
+        ref = run_decode(K, bc, q)
+        bc.cfg.decode_impl = K.DECODE_MFMA
+        d32 = np.abs(out - ref).max()
+        _say(f"   max |mfma - f32| over all heads = {d32:.2e}")
+        assert d32 <= TOL
+    pairs = [(b, h) for b in (0, 1, 2, batch // 2, batch - 3, batch - 1) for h in (0, wl.n_kv_heads - 1)]
+    worst = check_out(bc, out, q, pairs)
+    _say(f"   worst |mfma - oracle| = {worst:.2e}")
+
+
 def test_mfma_agrees_with_f32(K):
     """Same cache, two decodes: the matrix-core one (three-limb operands) close to the exact fp32 one."""
     for name, lens in (("tiny_1h_4k", [4096]), ("gqa_b1_32k", [2900, 1000]), ("long_b4_131k", [3000, 700])):

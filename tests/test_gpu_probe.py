@@ -30,12 +30,44 @@ def _say(msg):
     print(msg, flush=True)
 
 
+def balanced_gpc(ngs, quads, nwg, floor=4):
+    """The decode's balanced chunk size, restated from the header's rule: the smallest G >= 4 whose chunks,
+    ceil(groups / G) per (sequence, head quad), fit the nwg chunk work-groups."""
+    chunks = lambda G: sum(-(-n // G) for n in ngs) * quads
+    G = max(floor, -(-sum(ngs) * quads // nwg))
+    while chunks(G) > nwg:
+        G += 1
+    return G
+
+
+def _xor(pages, pt, b, h, groups, hb, pb):
+    acc = np.uint32(0)
+    for g in groups:
+        for p in (pt[b, 2 * g], pt[b, 2 * g + 1]):
+            blk = pages[int(p) * pb + h * hb:int(p) * pb + (h + 1) * hb]
+            acc ^= np.bitwise_xor.reduce(blk.view(np.uint32))
+    return acc
+
+
 def _expected(bc, shape, max_len):
+    """Expected slots; under balanced chunking the slots past a sequence's chunk count keep -1."""
     pages = bc.cache.pages.cpu().numpy()
     pt = bc.cache.page_table.cpu().numpy().reshape(len(bc.lens), -1)
     wl = bc.wl
     hb = head_bytes(wl.scheme)
     pb = hb * wl.n_kv_heads
+    if shape["balanced"]:
+        slots = shape["max_chunks"]
+        want = np.full((len(bc.lens), wl.n_kv_heads, slots), 0xFFFFFFFF, dtype=np.uint32)
+        cap = min(slots * 4, pt.shape[1] // 2)  # the launch bound at the 4-group floor, the page-table row
+        ngs = [min(O.n_groups(int(T), wl.n_sink, wl.n_recent), cap) for T in bc.lens]
+        nwg = shape["splitk_workgroups"] - len(bc.lens) * wl.n_kv_heads
+        G = balanced_gpc(ngs, wl.n_kv_heads // 4, nwg)
+        for b, ng in enumerate(ngs):
+            for c in range(-(-ng // G)):
+                for h in range(wl.n_kv_heads):
+                    want[b, h, c] = _xor(pages, pt, b, h, range(c * G, min((c + 1) * G, ng)), hb, pb)
+        return want
     nc, walks, gpc = shape["n_chunks"], shape["walks"], shape["chunk_units"]
     want = np.zeros((len(bc.lens), wl.n_kv_heads, walks), dtype=np.uint32)
     for b, T in enumerate(bc.lens):
@@ -44,13 +76,12 @@ def _expected(bc, shape, max_len):
             g0 = (w * nc // walks) * gpc
             g1 = min(((w + 1) * nc // walks) * gpc, ng)
             for h in range(wl.n_kv_heads):
-                acc = np.uint32(0)
-                for g in range(g0, g1):
-                    for p in (pt[b, 2 * g], pt[b, 2 * g + 1]):
-                        blk = pages[int(p) * pb + h * hb:int(p) * pb + (h + 1) * hb]
-                        acc ^= np.bitwise_xor.reduce(blk.view(np.uint32))
-                want[b, h, w] = acc
+                want[b, h, w] = _xor(pages, pt, b, h, range(g0, g1), hb, pb)
     return want
+
+
+def _slots(shape):
+    return shape["max_chunks"] if shape["balanced"] else shape["walks"]
 
 
 @pytest.mark.parametrize("name,kw,lens,split", [
@@ -58,6 +89,7 @@ def _expected(bc, shape, max_len):
     ("tiny_1h_4k", {}, [4096], 0),                                          # one kv head: walks per wave
     ("gqa_b1_32k", dict(scheme="int4_channel"), [3000, 6100], 0),           # 4-bit codes: 8704-byte head blocks
     ("batch32_32k", dict(n_q_heads=8, n_kv_heads=2), [2000, 3900, 0, 2600] * 4, 256),  # two kv heads, split
+    ("batch32_32k", {}, [9000, 700, 0, 6100, 2600, 4000, 300, 8200] * 4, 0),  # balanced: ragged, several G
 ])
 def test_probe_reads_the_decode_bytes(K, name, kw, lens, split):
     import torch
@@ -67,7 +99,7 @@ def test_probe_reads_the_decode_bytes(K, name, kw, lens, split):
     max_len = int(lens.max())
     shape = K.decode_shape(bc.cfg, len(lens), max_len)
     _say(f"probe: {name} {kw} lens {lens.tolist()} split {split}: {shape}")
-    out = torch.full((len(lens), wl.n_kv_heads, shape["walks"]), -1, dtype=torch.int32, device="cuda")
+    out = torch.full((len(lens), wl.n_kv_heads, _slots(shape)), -1, dtype=torch.int32, device="cuda")
     K.read_probe(bc.cache, out, max_len)
     torch.cuda.synchronize()
     got = out.cpu().numpy().view(np.uint32)
@@ -90,7 +122,7 @@ def test_probe_walks_several_chunks(K):
     shape = K.decode_shape(bc.cfg, batch, max_len)
     _say(f"probe: batch {batch}, lens {lens.min()}..{lens.max()}, split 512: {shape}")
     assert shape["span"] >= 2
-    out = torch.full((batch, wl.n_kv_heads, shape["walks"]), -1, dtype=torch.int32, device="cuda")
+    out = torch.full((batch, wl.n_kv_heads, _slots(shape)), -1, dtype=torch.int32, device="cuda")
     K.read_probe(bc.cache, out, max_len)
     torch.cuda.synchronize()
     got = out.cpu().numpy().view(np.uint32)

@@ -362,3 +362,20 @@ def test_read_probe_refuses_on_the_host():
     cfg4 = K.make_config(8, 32, K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0)
     cs4 = _fake_cache(cfg4, 2, K.pages_for_len(cfg4, T))
     assert probe(K.ctypes.byref(cfg4), K.ctypes.byref(cs4), f, T, None) == K.KVQ_EUNSUPPORTED
+
+
+def test_balanced_chunking_is_reported():
+    """Automatic chunks of the grouped schemes in head quads are chosen on the device from the lengths
+    (balanced); the host reports the choice for uniform lengths and the bound the workspace holds."""
+    cfg = K.make_config(8, 32)
+    sh = K.decode_shape(cfg, 32, 32768)
+    assert sh["balanced"] == 1 and sh["chunk_units"] == 32 and sh["n_chunks"] == 8
+    assert sh["max_chunks"] == -(-255 // 4)  # chunks of at least 4 groups
+    assert K.decode_workspace_bytes(cfg, 32, 32768) >= 4 * 32 * 32 * (1 + sh["max_chunks"]) * 130
+    # batch 1: the 4-group floor
+    sh1 = K.decode_shape(cfg, 1, 32768)
+    assert sh1["balanced"] == 1 and sh1["chunk_units"] == 4
+    # not balanced: an explicit split, the fp32 decode, kv heads not in fours, INT4 per token
+    for c in (K.make_config(8, 32, split_tokens=512), K.make_config(8, 32, decode_impl=K.DECODE_F32),
+              K.make_config(2, 8), K.make_config(8, 32, K.INT4_TOKEN, K.ROT_HADAMARD, 0, 0, 1.0, 1.0)):
+        assert K.decode_shape(c, 32, 32768)["balanced"] == 0
