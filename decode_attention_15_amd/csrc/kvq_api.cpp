@@ -83,7 +83,7 @@ bool uses_mfma(const kvq_config* c) {
 int wgs_per_cu(const kvq_config* c) {
   if (!uses_mfma(c)) return 4;
   const bool four = c->scheme == KVQ_INT4_CHANNEL || c->scheme == KVQ_INT4_TOKEN;
-  return gq_of(c) <= 4 ? (four ? 2 : 3) : (four ? 1 : 2);
+  return gq_of(c) <= 4 ? (four ? 2 : 3) : (four ? 1 : 3);
 }
 
 // Balanced automatic chunking: the matrix-core decode of the grouped schemes in head quads with no explicit

@@ -50,7 +50,9 @@ __device__ inline float exp2_safe_diff(float a, float b) {
 // online softmax; the waves are merged in LDS and one partial (m, l, o[128]) per q head written.
 // ---------------------------------------------------------------------------------------------
 // Per-wave LDS of the matrix-core units: the key and the value codes of a group or page pair, the metadata of
-// two of them (double-buffered, 1 KB each), and one operand plane with rows (head, limb)
+// two of them (double-buffered, 1 KB each; at GQ 8 with 2-bit codes one buffer, whose lanes take the key-side
+// words to registers and the value scales and zeros to a 512-byte side buffer before the next group's copy
+// lands, so that three work-groups fit a CU), and one operand plane with rows (head, limb)
 // of 128 bytes in k order (stride 144: consecutive rows start in different banks) and a last row that stays
 // zero for the matrix rows no head fills.  The plane holds the key-side operand while the key products read
 // it and the softmax weights while the value products read them.
@@ -58,10 +60,12 @@ template <int GQ, int KU = 256>
 struct MfmaWave {
   static constexpr int ROWS = 3 * GQ;
   static constexpr int RSTRIDE = 144;
+  static constexpr int MB = (GQ == 8 && KU == 256) ? 1 : 2;  // metadata buffers
   uint4 kst[KU];  // key codes: 4 KB (2-bit codes of a group) or 8 KB (4-bit codes of a group or page pair)
   uint4 vst[KU];  // value codes, the same size
-  uint4 mst[2][64];
+  uint4 mst[MB][64];
   uint8_t plane[(ROWS + 1) * RSTRIDE];
+  uint4 vsz[MB == 1 ? 32 : 0];  // one metadata buffer: the group's value scales and zeros
 };
 template <int GQ, bool MF, int KU>
 struct MfmaLds {};
@@ -605,6 +609,19 @@ __device__ inline void dma16_base(uint32_t lds, const void* gbase, uint32_t voff
                  : "memory");
   }
 }
+// dma16_base for the lanes of one half of the wave (HI: lanes 32..63), inside a branch on the lane's half.  The
+// two halves' blocks differ in text, so that the compiler keeps them in their branches (blocks merged after
+// the branch would take a per-lane base).
+template <bool HI>
+__device__ inline void dma16_half(uint32_t lds, const void* gbase, uint32_t voff) {
+  if constexpr (HI) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt ; upper half" ::"s"(lds), "v"(voff),
+                 "s"(gbase) : "memory");
+  } else {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt ; lower half" ::"s"(lds), "v"(voff),
+                 "s"(gbase) : "memory");
+  }
+}
 #define KVQ_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
 // The grouped schemes' code and metadata copies stream (measured on MI355X at batch 32 x 32k: the split-K
 // kernel about 10% faster than with default-policy copies); the INT4 per-token walk keeps the default policy
@@ -854,6 +871,8 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
   constexpr int RS = MfmaWave<GQ, KU>::RSTRIDE;
   constexpr int ROWS = MfmaWave<GQ, KU>::ROWS;
   constexpr float S = Limb3<BITS>::S;
+  constexpr bool M1 = MfmaWave<GQ, KU>::MB == 1;  // one metadata buffer: its words to registers first
+  static_assert(!M1 || (NCH == 16 && BITS == 2), "single metadata buffer: GQ 8, 2-bit codes");
   const Geo& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -908,15 +927,30 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
     koff[jj] = (uint32_t)(tl * 32 + 16 * (lane & 1));
   }
   const uint32_t kst_a = lds_addr(W.kst), vst_a = lds_addr(W.vst);
-  const uint32_t mst_a0 = lds_addr(W.mst[0]), mst_a1 = lds_addr(W.mst[1]);
+  const uint32_t mst_a0 = lds_addr(W.mst[0]), mst_a1 = lds_addr(W.mst[M1 ? 0 : 1]);
   const uint8_t* pages = a.pages;
   const long long pbytes = g.page_bytes, hoff = (long long)h * g.head_bytes;
   auto page_of = [&](int idx) { return pages + pool_page(g, idx) * pbytes + hoff; };
   constexpr int META = BITS == 2 ? I2_META_OFF : I4C_META_OFF;
   constexpr int KOFF = BITS == 2 ? I2_K_OFF : I4C_K_OFF, VOFF = BITS == 2 ? I2_V_OFF : I4C_V_OFF;
   auto issue_m = [&](int2 p, int buf) {
-    const uint8_t* src = (lane >= 32 ? page_of(p.y) : page_of(p.x)) + META + (lane & 31) * 16;
-    dma16<kStreamCopies>(buf ? mst_a1 : mst_a0, src);
+    if constexpr (M1) {
+      // the two pages' halves as two copies of 32 lanes each: page bases in scalar registers (taken before the
+      // branch), 32-bit lane offsets
+      auto uniform = [](const uint8_t* ptr) {
+        const uint64_t v = (uint64_t)(uintptr_t)ptr;
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+        return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+      };
+      const uint8_t* bx = uniform(page_of(p.x) + META);
+      const uint8_t* by = uniform(page_of(p.y) + META);
+      const uint32_t off = (uint32_t)(lane & 31) * 16;
+      if (lane < 32) dma16_half<false>(mst_a0, bx, off);
+      else dma16_half<true>(mst_a0, by, off);
+    } else {
+      const uint8_t* src = (lane >= 32 ? page_of(p.y) : page_of(p.x)) + META + (lane & 31) * 16;
+      dma16<kStreamCopies>(buf ? mst_a1 : mst_a0, src);
+    }
   };
   auto issue_k = [&](int2 p) {
     if constexpr (BITS == 2) {
@@ -1038,6 +1072,30 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
         vw[t][1] = *reinterpret_cast<const uint2*>(v_rd + 1024 + 128 * t);
       }
     }
+    // one metadata buffer: before the next group's copy lands there, this lane's metadata words to registers
+    // (per token: the words of step 1; per channel: the alpha step's scale/zero pairs of positions Q0 + i,
+    // i % 8 < 4) and the value scales and zeros to the side buffer
+    uint32_t mkw[M1 ? 16 : 1];
+    if constexpr (M1) {
+      const uint16_t* ms0 = reinterpret_cast<const uint16_t*>(W.mst[0]);
+      if constexpr (TOK) {
+        const uint32_t* mw = reinterpret_cast<const uint32_t*>(ms0 + 256 * (c >> 3) + 2 * (c & 7));
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mkw[4 * k + j] = mw[8 * k + 32 * j];
+      } else {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          if ((i & 4) == 0) {
+            const int ch = mf_key_channel(Q0 + i), j = 4 * (i >> 3) + (i & 3);
+            mkw[j] = reinterpret_cast<const uint32_t*>(ms0)[ch >> 1];
+            mkw[8 + j] = reinterpret_cast<const uint32_t*>(ms0 + D)[ch >> 1];
+          }
+        }
+        reinterpret_cast<uint2*>(W.vsz)[lane] = reinterpret_cast<const uint2*>(ms0 + 2 * D)[lane];
+      }
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (has_next) {
       const int2 pn = make_int2(__builtin_amdgcn_readfirstlane(pv.x), __builtin_amdgcn_readfirstlane(pv.y));
@@ -1056,7 +1114,8 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
       const uint32_t* mw = reinterpret_cast<const uint32_t*>(ms + 256 * (c >> 3) + 2 * (c & 7));
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint32_t w0 = mw[8 * k], w1 = mw[8 * k + 32], w2 = mw[8 * k + 64], w3 = mw[8 * k + 96];
+        const uint32_t w0 = M1 ? mkw[4 * k] : mw[8 * k], w1 = M1 ? mkw[4 * k + 1] : mw[8 * k + 32];
+        const uint32_t w2 = M1 ? mkw[4 * k + 2] : mw[8 * k + 64], w3 = M1 ? mkw[4 * k + 3] : mw[8 * k + 96];
         tks[k] = __uint_as_float(w0 << 16);
         tks[k + 4] = __uint_as_float(w0 & 0xffff0000u);
         tkz[k] = __uint_as_float(w1 << 16);
@@ -1078,9 +1137,9 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
           if ((i & 4) == 0) {
-            const int ch = mf_key_channel(Q0 + i);
-            const uint32_t sw = reinterpret_cast<const uint32_t*>(ms)[ch >> 1];
-            const uint32_t zw = reinterpret_cast<const uint32_t*>(ms + D)[ch >> 1];
+            const int ch = mf_key_channel(Q0 + i), j = 4 * (i >> 3) + (i & 3);
+            const uint32_t sw = M1 ? mkw[j] : reinterpret_cast<const uint32_t*>(ms)[ch >> 1];
+            const uint32_t zw = M1 ? mkw[8 + j] : reinterpret_cast<const uint32_t*>(ms + D)[ch >> 1];
             al[i] = qa[i] * __uint_as_float(sw << 16);
             al[i + 4] = qa[i + 4] * __uint_as_float(sw & 0xffff0000u);
             zk[i] = __uint_as_float(zw << 16);
@@ -1238,14 +1297,15 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int ch = c + 16 * t;
-        const float sv = bf16_to_f32(ms[2 * D + ch]), zv = bf16_to_f32(ms[3 * D + ch]);
+        const uint16_t* vsz = M1 ? reinterpret_cast<const uint16_t*>(W.vsz) - 2 * D : ms;
+        const float sv = bf16_to_f32(vsz[2 * D + ch]), zv = bf16_to_f32(vsz[3 * D + ch]);
         const float Y = fmaf(-zv, Pf, (float)limbs3_sum<GQ>(acc[t], accx[t], e));
         o[e][t] = fmaf(eg * sv, Y, o[e][t] * sc);
       }
       l[e] = fmaf(eg, Pf, l[e] * sc);
       m[e] = mnew;
     }
-    mb ^= 1;
+    if constexpr (!M1) mb ^= 1;
     if (--left == 0 || !has_next) {  // uniform: the end of a chunk
       store_partial(gi / gpc);
       left = gpc;
@@ -1581,9 +1641,9 @@ __device__ inline void splitk_unit_of(const Geo& g, int& unit, int& h, int& b) {
   b = pair / g.n_kv;
 }
 // Matrix-core launch of the grouped schemes.  Work-groups per CU, as the LDS allows (160 KB): 2-bit codes
-// three up to GQ 4 (48.5 KB each), two at GQ 8; 4-bit codes two up to GQ 4 (81 KB), one at GQ 8.
+// three (48.5 KB each up to GQ 4, 51.5 KB at GQ 8); 4-bit codes two up to GQ 4 (81 KB), one at GQ 8.
 template <int GQ, bool TOK, int BITS>
-__global__ __launch_bounds__(kThreads, GQ <= 4 ? (BITS == 2 ? 3 : 2) : (BITS == 2 ? 2 : 1)) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, GQ <= 4 ? (BITS == 2 ? 3 : 2) : (BITS == 2 ? 3 : 1)) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ DecodeLds<GQ, BITS / 2, true> L;
   const Geo& g = a.g;
   int i;

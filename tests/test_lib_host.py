@@ -323,12 +323,12 @@ def test_decode_shape_chunks_and_walks():
     assert sh["matrix_cores"] == 1 and sh["span"] == 1 and sh["walks"] == sh["n_chunks"]
     assert sh["n_chunks"] == -(-ng // sh["chunk_units"]) and 4 <= sh["chunk_units"] <= 32
     assert sh["splitk_workgroups"] == 32 * 2 * sh["n_chunks"] + 256 <= 256 * 3 and sh["band_first"] == 0
-    # 512-token split at 4 x 131k, GQA 8: 256 chunks of 4 groups in 60 walks of 4 or 5 chunks per (sequence,
-    # head quad), filling the 512 slots of one round (2 per CU) with the 32 band work-groups
+    # 512-token split at 4 x 131k, GQA 8: 256 chunks of 4 groups in 92 walks of 2 or 3 chunks per (sequence,
+    # head quad), filling the 768 slots of one round (3 per CU) with the 32 band work-groups
     cfg8 = K.make_config(8, 64, n_recent=256, split_tokens=512)
     sh = K.decode_shape(cfg8, 4, 131072)
-    assert sh["chunk_units"] == 4 and sh["n_chunks"] == 256 and sh["walks"] == 60 and sh["span"] == 5
-    assert sh["splitk_workgroups"] == 4 * 2 * 60 + 32 == 512 and sh["band_first"] == 0
+    assert sh["chunk_units"] == 4 and sh["n_chunks"] == 256 and sh["walks"] == 92 and sh["span"] == 3
+    assert sh["splitk_workgroups"] == 4 * 2 * 92 + 32 == 768 and sh["band_first"] == 0
     # the fp32 decode walks one chunk per work-group
     cfg.decode_impl = K.DECODE_F32
     sh = K.decode_shape(cfg, 32, 32768)
