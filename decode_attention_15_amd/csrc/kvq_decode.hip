@@ -797,8 +797,9 @@ __device__ __forceinline__ void store_words(uint8_t* dst, const uint32_t (&w)[N]
 }
 // The key-side operand of one head: x holds this lane's NCH positions (Q0..), the head's LPH lanes hold
 // all 128.  a = rint(x S / max|x|) over the head goes to rows rows, rows + RS, rows + 2 RS (lo, mid, hi),
-// bytes 0..NCH-1; zsum gets the head's sum of a zk; returns A = max|x| / S (logit = A sum a code).
-template <int LPH, int NCH, int RS>
+// bytes 0..NCH-1; zsum gets the head's sum of a zk (ZX: of x zk, which A a equals to 2^-23 of max|x|);
+// returns A = max|x| / S (logit = A sum a code).
+template <int LPH, int NCH, int RS, bool ZX = false>
 __device__ __forceinline__ float round_operand3(const float (&x)[NCH], const float (&zk)[NCH], float S, uint8_t* rows,
                                                 float& zsum) {
   int amx_i = 0;  // max |x| as its bit pattern (non-negative floats order as their bits)
@@ -812,7 +813,7 @@ __device__ __forceinline__ float round_operand3(const float (&x)[NCH], const flo
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     ev[i] = fmaf(x[i], inv, kRound3);
-    zs = fmaf(ev[i] - kRound3, zk[i], zs);  // ev - kRound3 = a exactly
+    zs = ZX ? fmaf(x[i], zk[i], zs) : fmaf(ev[i] - kRound3, zk[i], zs);  // ev - kRound3 = a exactly
   }
   zsum = seg_sum<LPH>(zs);
   if constexpr (NCH >= 4) {
@@ -832,12 +833,26 @@ __device__ __forceinline__ float round_operand3(const float (&x)[NCH], const flo
   }
   return amx * (1.0f / S);
 }
-// Eight weights of one head (value positions 8 c + i, already magic-rounded) to its three limb rows.
+// Non-negative weights u <= S: rounded by one FMA with the magic addend 2^23 + 0x8080, whose encoding's low
+// 23 bits are y = u + 0x8080; bytes 0 and 1 of y less 128 are lo and mid, byte 2 is hi (0 ..< 64, no sign)
+constexpr float kRoundU = 8421504.0f;  // 2^23 + 0x8080
+__device__ __forceinline__ void limbs3u(float e0, float e1, float e2, float e3, uint32_t& lo, uint32_t& mid,
+                                        uint32_t& hi) {
+  const uint32_t u0 = __float_as_uint(e0), u1 = __float_as_uint(e1), u2 = __float_as_uint(e2), u3 = __float_as_uint(e3);
+  const uint32_t a01 = __builtin_amdgcn_perm(u1, u0, 0x05010400u);  // u0.b0 u1.b0 u0.b1 u1.b1
+  const uint32_t a23 = __builtin_amdgcn_perm(u3, u2, 0x05010400u);
+  const uint32_t h01 = __builtin_amdgcn_perm(u1, u0, 0x06020602u);  // u0.b2 u1.b2 (twice)
+  const uint32_t h23 = __builtin_amdgcn_perm(u3, u2, 0x06020602u);
+  lo = __builtin_amdgcn_perm(a23, a01, 0x05040100u) ^ 0x80808080u;
+  mid = __builtin_amdgcn_perm(a23, a01, 0x07060302u) ^ 0x80808080u;
+  hi = __builtin_amdgcn_perm(h23, h01, 0x05040100u);
+}
+// Eight weights of one head (value positions 8 c + i, rounded with kRoundU) to its three limb rows.
 template <int RS>
 __device__ __forceinline__ void store_weights3(uint8_t* dst, const float (&ew)[8]) {
   uint32_t lo0, mid0, hi0, lo1, mid1, hi1;
-  limbs3(ew[0], ew[1], ew[2], ew[3], lo0, mid0, hi0);
-  limbs3(ew[4], ew[5], ew[6], ew[7], lo1, mid1, hi1);
+  limbs3u(ew[0], ew[1], ew[2], ew[3], lo0, mid0, hi0);
+  limbs3u(ew[4], ew[5], ew[6], ew[7], lo1, mid1, hi1);
   *reinterpret_cast<uint2*>(dst) = make_uint2(lo0, lo1);
   *reinterpret_cast<uint2*>(dst + RS) = make_uint2(mid0, mid1);
   *reinterpret_cast<uint2*>(dst + 2 * RS) = make_uint2(hi0, hi1);
@@ -1155,8 +1170,8 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
         }
       }
       float zs;
-      const float Ah = round_operand3<LPH, NCH, RS>(al, zk, S, a_rows, zs);
-      const float AZh = Ah * zs;
+      const float Ah = round_operand3<LPH, NCH, RS, true>(al, zk, S, a_rows, zs);
+      const float AZh = zs;
 #pragma unroll
       for (int e = 0; e < HPL; ++e) {
         Ae[e] = head_value(Ah, e);
@@ -1224,8 +1239,8 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
         float zs = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          ew[i] = fmaf(pw[i], r, kRound3);
-          zs = fmaf(ew[i] - kRound3, tvz[i], zs);
+          ew[i] = fmaf(pw[i], r, kRoundU);
+          zs = fmaf(ew[i] - kRoundU, tvz[i], zs);
         }
         Zt[e] = seg_sum<16>(zs);
       } else {
@@ -1240,7 +1255,7 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
         const float ref = Ae[e] * (float)vmx;
         mg[e] = ref - AZe[e];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ew[i] = fmaf(__builtin_amdgcn_exp2f(fmaf(Ae[e], (float)v[i], -ref)), S, kRound3);
+        for (int i = 0; i < 8; ++i) ew[i] = fmaf(__builtin_amdgcn_exp2f(fmaf(Ae[e], (float)v[i], -ref)), S, kRoundU);
       }
       const int he = q4 * HPL + e;
       if (he < GQ) store_weights3<RS>(W.plane + (3 * he) * RS + 8 * c, ew);
@@ -1566,8 +1581,8 @@ __device__ void int4tok_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int
       float zs = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        ew[i] = fmaf(pw[i], r, kRound3);
-        zs = fmaf(ew[i] - kRound3, tvz[i], zs);
+        ew[i] = fmaf(pw[i], r, kRoundU);
+        zs = fmaf(ew[i] - kRoundU, tvz[i], zs);
       }
       Zt[e] = seg_sum<16>(zs);
       const int he = q4 * HPL + e;
