@@ -1656,7 +1656,7 @@ __device__ inline void splitk_unit_of(const Geo& g, int& unit, int& h, int& b) {
   b = pair / g.n_kv;
 }
 // Matrix-core launch of the grouped schemes.  Work-groups per CU, as the LDS allows (160 KB): 2-bit codes
-// three (48.5 KB each up to GQ 4, 51.5 KB at GQ 8); 4-bit codes two up to GQ 4 (81 KB), one at GQ 8.
+// three (48.5 KB each up to GQ 4, 53.6 KB at GQ 8); 4-bit codes two up to GQ 4 (81 KB), one at GQ 8.
 template <int GQ, bool TOK, int BITS>
 __global__ __launch_bounds__(kThreads, GQ <= 4 ? (BITS == 2 ? 3 : 2) : (BITS == 2 ? 3 : 1)) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ DecodeLds<GQ, BITS / 2, true> L;
