@@ -264,6 +264,20 @@ __device__ __forceinline__ void limbs3(float e0, float e1, float e2, float e3, u
   hi = y | ((y & 0x40404040u) << 1);  // bit 6 extended into bit 7: y2 - 64 as a signed byte
 }
 
+// Non-negative operands u <= S (softmax weights): rounded by one FMA with the magic addend 2^23 + 0x8080, whose encoding's low
+// 23 bits are y = u + 0x8080; bytes 0 and 1 of y less 128 are lo and mid, byte 2 is hi (0 ..< 64, no sign)
+constexpr float kRoundU = 8421504.0f;  // 2^23 + 0x8080
+__device__ __forceinline__ void limbs3u(float e0, float e1, float e2, float e3, uint32_t& lo, uint32_t& mid,
+                                        uint32_t& hi) {
+  const uint32_t u0 = __float_as_uint(e0), u1 = __float_as_uint(e1), u2 = __float_as_uint(e2), u3 = __float_as_uint(e3);
+  const uint32_t a01 = __builtin_amdgcn_perm(u1, u0, 0x05010400u);  // u0.b0 u1.b0 u0.b1 u1.b1
+  const uint32_t a23 = __builtin_amdgcn_perm(u3, u2, 0x05010400u);
+  const uint32_t h01 = __builtin_amdgcn_perm(u1, u0, 0x06020602u);  // u0.b2 u1.b2 (twice)
+  const uint32_t h23 = __builtin_amdgcn_perm(u3, u2, 0x06020602u);
+  lo = __builtin_amdgcn_perm(a23, a01, 0x05040100u) ^ 0x80808080u;
+  mid = __builtin_amdgcn_perm(a23, a01, 0x07060302u) ^ 0x80808080u;
+  hi = __builtin_amdgcn_perm(h23, h01, 0x05040100u);
+}
 // bf16 matrix-core operands: fp32 values split into bf16 hi + lo (hi the round-to-nearest-even bf16 of x, lo
 // that of the remainder: about 16 significant bits together) for v_mfma_f32_16x16x32_bf16, whose products of
 // bf16 values are exact and whose sums are fp32

@@ -138,12 +138,17 @@ struct GroupBuf {
   uint16_t meta[512];                         // the pages' 512-byte metadata blocks, page 0 then page 1
 };
 
-// The limbs of 16 magic-rounded values ef[e] (e = 4 j + k', each fmaf(x, scale, kRound3)) as the three i8
-// operands lo, mid, hi: dword k' holds the limbs of ef[k'], ef[4 + k'], ef[8 + k'], ef[12 + k'] in bytes 0..3
+// The limbs of 16 magic-rounded values ef[e] (e = 4 j + k', each fmaf(x, scale, kRound3), or kRoundU for
+// non-negative values, U) as the three i8 operands lo, mid, hi: dword k' holds the limbs of ef[k'],
+// ef[4 + k'], ef[8 + k'], ef[12 + k'] in bytes 0..3
+template <bool U = false>
 __device__ inline void limb_operands(const float (&ef)[16], i32x4 (&op)[3]) {
   uint32_t w[4][3];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) limbs3(ef[k], ef[4 + k], ef[8 + k], ef[12 + k], w[k][0], w[k][1], w[k][2]);
+  for (int k = 0; k < 4; ++k) {
+    if constexpr (U) limbs3u(ef[k], ef[4 + k], ef[8 + k], ef[12 + k], w[k][0], w[k][1], w[k][2]);
+    else limbs3(ef[k], ef[4 + k], ef[8 + k], ef[12 + k], w[k][0], w[k][1], w[k][2]);
+  }
 #pragma unroll
   for (int lb = 0; lb < 3; ++lb) op[lb] = i32x4{(int)w[0][lb], (int)w[1][lb], (int)w[2][lb], (int)w[3][lb]};
 }
@@ -390,13 +395,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeArgs a) {
         for (int e = 0; e < 16; ++e) {
           const int c = key_channel<SCHEME>(4 * ks + q, e);
           ef[e] = fmaf(al[ks][e], inv, kRound3);
-          zs = fmaf(ef[e] - kRound3, bf16_to_f32(B.meta[D + c]), zs);
+          zs = fmaf(al[ks][e], bf16_to_f32(B.meta[D + c]), zs);  // A a equals alpha to 2^-23 of max|alpha|
         }
         limb_operands(ef, bq[ks]);
       }
       zs = col_sum(zs);
       Acol = amx * (1.0f / S);
-      AZ = Acol * zs;
+      AZ = zs;
     }
     // this lane's tokens: 16 mt + 4 q + i of the unit (page mt / 4, token 16 (mt % 4) + 4 q + i of it)
     // the scales (s) and zeros (z) of tokens 16 mt + 4 q + 0..3, K (side 0) or V (side 1), by one LDS read:
@@ -488,8 +493,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeArgs a) {
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            u[mt][i] = fmaf(pw[mt][i], r, kRound3);
-            if (FULL || lg[mt][i] != -INFINITY) zs = fmaf(u[mt][i] - kRound3, vz[mt][i], zs);
+            u[mt][i] = fmaf(pw[mt][i], r, kRoundU);
+            if (FULL || lg[mt][i] != -INFINITY) zs = fmaf(u[mt][i] - kRoundU, vz[mt][i], zs);
           }
         Zt = col_sum(zs);
       } else {
@@ -498,8 +503,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeArgs a) {
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            u[mt][i] = fmaf(weight(lg[mt][i]), S, kRound3);
-            us += u[mt][i] - kRound3;
+            u[mt][i] = fmaf(weight(lg[mt][i]), S, kRoundU);
+            us += u[mt][i] - kRoundU;
           }
         Pf = col_sum(us);
       }
@@ -521,7 +526,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeArgs a) {
         value_tok<SCHEME>(e & 3, e >> 2, J, R);
         x[e] = u[4 * kp + J][R];
       }
-      limb_operands(x, uq[kp]);
+      limb_operands<true>(x, uq[kp]);
     }
     // 4. values U^T (128 channels x 16 columns): channel 16 mt + (l % 16) is the A row
     const float mnew = fmaxf(m, gm);
