@@ -129,6 +129,47 @@ __device__ inline void wave_top_select_u32(uint32_t u0, uint32_t u1, int j, uint
   }
 }
 
+// wave_top_select_u32 for two tokens at once (a: a0, a1; b: b0, b1): the two tokens' rounds are independent, so
+// their wave reductions interleave; a token that is done keeps its results while the other finishes
+__device__ inline void wave_top_select2_u32(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, int j, uint32_t& ya,
+                                            uint32_t& ya1, uint32_t& yb, uint32_t& yb1) {
+  const int k = D - j;
+  uint32_t cura = kFull, preva = kFull, curb = kFull, prevb = kFull;
+  int abovea = 0, aboveb = 0;
+  bool da = false, db = false;
+  for (;;) {
+    const uint32_t ca0 = a0 < cura ? a0 : 0u, ca1 = a1 < cura ? a1 : 0u;
+    const uint32_t cb0 = b0 < curb ? b0 : 0u, cb1 = b1 < curb ? b1 : 0u;
+    const uint32_t ma = (uint32_t)wave_max_i32((int)(ca0 > ca1 ? ca0 : ca1));
+    const uint32_t mb = (uint32_t)wave_max_i32((int)(cb0 > cb1 ? cb0 : cb1));
+    const int cnta = wave_count(a0 == ma) + wave_count(a1 == ma);
+    const int cntb = wave_count(b0 == mb) + wave_count(b1 == mb);
+    if (!da) {
+      if (abovea + cnta >= k) {
+        ya = ma;
+        ya1 = (k - 1 > abovea) ? ma : preva;
+        da = true;
+      } else {
+        abovea += cnta;
+        preva = ma;
+        cura = ma;
+      }
+    }
+    if (!db) {
+      if (aboveb + cntb >= k) {
+        yb = mb;
+        yb1 = (k - 1 > aboveb) ? mb : prevb;
+        db = true;
+      } else {
+        aboveb += cntb;
+        prevb = mb;
+        curb = mb;
+      }
+    }
+    if (da && db) return;
+  }
+}
+
 // clip(x, -tau, tau) as two comparisons, each taking its second operand when the two compare equal, so
 // that a zero of either sign clipped at tau = 0 gives +0 as the cache format's definition does
 __device__ inline float clip_to(float x, float tau) {
@@ -157,6 +198,23 @@ __device__ inline float clip_tau(float x0, float x1, int j, float f) {
   }
   const float y0 = __uint_as_float(yj), y1 = __uint_as_float(yj1);
   return __fadd_rn(y0, __fmul_rn(f, __fsub_rn(y1, y0)));
+}
+
+// clip_tau for two tokens (a: xa0, xa1; b: xb0, xb1), the same thresholds: near the top the two selections run
+// interleaved
+__device__ inline void clip_tau2(float xa0, float xa1, float xb0, float xb1, int j, float f, float& ta, float& tb) {
+  if (j >= D - 1 || j < D - 16) {
+    ta = clip_tau(xa0, xa1, j, f);
+    tb = clip_tau(xb0, xb1, j, f);
+    return;
+  }
+  uint32_t ya, ya1, yb, yb1;
+  wave_top_select2_u32(__float_as_uint(xa0) & 0x7fffffffu, __float_as_uint(xa1) & 0x7fffffffu,
+                       __float_as_uint(xb0) & 0x7fffffffu, __float_as_uint(xb1) & 0x7fffffffu, j, ya, ya1, yb, yb1);
+  const float a_lo = __uint_as_float(ya), a_hi = __uint_as_float(ya1);
+  const float b_lo = __uint_as_float(yb), b_hi = __uint_as_float(yb1);
+  ta = __fadd_rn(a_lo, __fmul_rn(f, __fsub_rn(a_hi, a_lo)));
+  tb = __fadd_rn(b_lo, __fmul_rn(f, __fsub_rn(b_hi, b_lo)));
 }
 
 // Unnormalized radix-2 Walsh-Hadamard transform of 128 fp64 values held as (e0 = x[lane],
@@ -317,20 +375,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
       xr[tl * XS_STRIDE + lane + 64] = y1;
     }
   }
-  __syncthreads();
 
-  // 3. per-token clip
+  // 3. per-token clip, two tokens at a time (no barrier before it: every wave rotated exactly the rows it clips,
+  //    and a wave's LDS accesses stay in order)
   const int cj = which ? a.clip_j_v : a.clip_j_k;
   const float cf = which ? a.clip_f_v : a.clip_f_k;
   if (cj < D - 1) {
-    for (int tl = wave * 32; tl < wave * 32 + 32; ++tl) {
-      const float x0 = xr[tl * XS_STRIDE + lane], x1 = xr[tl * XS_STRIDE + lane + 64];
-      const float tau = clip_tau(x0, x1, cj, cf);
-      xr[tl * XS_STRIDE + lane] = clip_to(x0, tau);
-      xr[tl * XS_STRIDE + lane + 64] = clip_to(x1, tau);
+    for (int tl = wave * 32; tl < wave * 32 + 32; tl += 2) {
+      float* ra = xr + tl * XS_STRIDE;
+      float* rb = ra + XS_STRIDE;
+      const float a0 = ra[lane], a1 = ra[lane + 64], b0 = rb[lane], b1 = rb[lane + 64];
+      float ta, tb;
+      clip_tau2(a0, a1, b0, b1, cj, cf, ta, tb);
+      ra[lane] = clip_to(a0, ta);
+      ra[lane + 64] = clip_to(a1, ta);
+      rb[lane] = clip_to(b0, tb);
+      rb[lane + 64] = clip_to(b1, tb);
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   // 4. min/max per channel over the group (or per token over its channels), bf16 scale and zero
   if (tokenwise) {
