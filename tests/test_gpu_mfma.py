@@ -115,11 +115,15 @@ def test_mfma_walks_several_chunks(K, name, kw, batch, lo, hi):
     ("batch32_32k", {}, 32, 300, 9000),                            # GQA 4
     ("long_b4_131k", dict(split_tokens=0), 16, 1000, 12000),        # GQA 8
     ("batch32_32k", dict(scheme="int4_channel"), 16, 300, 6000),   # 4-bit codes
+    ("batch32_32k", {}, 256, 300, 2500),                           # GQA 4, more work-groups than one round
+    ("long_b4_131k", dict(split_tokens=0), 192, 300, 2000),         # GQA 8, likewise
 ])
 def test_balanced_chunking_ragged(K, name, kw, batch, lo, hi):
     """Automatic chunks chosen on the device from the batch's lengths (balanced chunking): ragged lengths, two of
     them without a quantized group, put the chunk size between the 4-group floor and the longest sequence; the
-    whole output is compared with the fp32 decode of the same cache and sampled heads with the oracle."""
+    whole output is compared with the fp32 decode of the same cache and sampled heads with the oracle.  The large
+    batches have more (sequence, head quad) rows than chunk slots and more work-groups than one round holds: the
+    band work-groups go first."""
     wl = synth.scaled(synth.WORKLOADS[name], batch=batch, **kw)
     rng = np.random.default_rng(batch * 131 + lo)
     lens = rng.integers(lo, hi + 1, size=batch)
@@ -129,6 +133,7 @@ def test_balanced_chunking_ragged(K, name, kw, batch, lo, hi):
     shape = K.decode_shape(bc.cfg, batch, int(lens.max()))
     _say(f"balanced: {name} {kw} batch {batch}, lens {lens.min()}..{lens.max()}: {shape}")
     assert shape["balanced"] == 1
+    assert shape["band_first"] == (1 if batch >= 128 else 0)
     q = synth.queries(wl)
     out = run_decode(K, bc, q)
     assert np.isfinite(out).all()
