@@ -340,20 +340,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
   const float* rot = which ? a.rot_v : a.rot_k;
   const int t_first = g.S0 + GROUP * grp;
 
-  // 1. gather
-  for (int e = tid; e < GROUP * D; e += 256) {
-    const int tl = e >> 7, c = e & (D - 1);
-    const int t = t_first + tl;
-    float val;
-    if (t < T0) {
-      const long long slot = band_slot_of(t, g.S0, g.W);
-      const long long off = (((long long)b * g.n_kv + h) * g.slots + slot) * 256 + which * 128 + c;
-      val = bf16_to_f32(a.band[off]);
-    } else {
-      const long long row = c0 + (t - T0);
-      val = src_as_bf16_value(src, a.src_bf16, (row * g.n_kv + h) * D + c);
+  // 1. gather: four channels per thread and step (8-byte bf16, 16-byte fp32 loads) when the band and the source
+  //    are aligned for them, else one value per step
+  const bool vec4 = (reinterpret_cast<uintptr_t>(a.band) & 7) == 0 &&
+                    (reinterpret_cast<uintptr_t>(src) & (a.src_bf16 ? 7 : 15)) == 0;
+  if (vec4) {
+    for (int e4 = tid; e4 < GROUP * D / 4; e4 += 256) {
+      const int tl = e4 >> 5, c = 4 * (e4 & 31);
+      const int t = t_first + tl;
+      float v[4];
+      if (t < T0) {
+        const long long slot = band_slot_of(t, g.S0, g.W);
+        const long long off = (((long long)b * g.n_kv + h) * g.slots + slot) * 256 + which * 128 + c;
+        const uint2 w = *reinterpret_cast<const uint2*>(a.band + off);
+        v[0] = __uint_as_float(w.x << 16);
+        v[1] = __uint_as_float(w.x & 0xffff0000u);
+        v[2] = __uint_as_float(w.y << 16);
+        v[3] = __uint_as_float(w.y & 0xffff0000u);
+      } else {
+        const long long idx = ((long long)(c0 + (t - T0)) * g.n_kv + h) * D + c;
+        if (a.src_bf16) {
+          const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(src) + idx);
+          v[0] = __uint_as_float(w.x << 16);
+          v[1] = __uint_as_float(w.x & 0xffff0000u);
+          v[2] = __uint_as_float(w.y << 16);
+          v[3] = __uint_as_float(w.y & 0xffff0000u);
+        } else {
+          const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + idx);
+          v[0] = bf16_to_f32(f32_to_bf16_rne(f.x));
+          v[1] = bf16_to_f32(f32_to_bf16_rne(f.y));
+          v[2] = bf16_to_f32(f32_to_bf16_rne(f.z));
+          v[3] = bf16_to_f32(f32_to_bf16_rne(f.w));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xs[tl * XS_STRIDE + c + i] = v[i];
     }
-    xs[tl * XS_STRIDE + c] = val;
+  } else {
+    for (int e = tid; e < GROUP * D; e += 256) {
+      const int tl = e >> 7, c = e & (D - 1);
+      const int t = t_first + tl;
+      float val;
+      if (t < T0) {
+        const long long slot = band_slot_of(t, g.S0, g.W);
+        const long long off = (((long long)b * g.n_kv + h) * g.slots + slot) * 256 + which * 128 + c;
+        val = bf16_to_f32(a.band[off]);
+      } else {
+        const long long row = c0 + (t - T0);
+        val = src_as_bf16_value(src, a.src_bf16, (row * g.n_kv + h) * D + c);
+      }
+      xs[tl * XS_STRIDE + c] = val;
+    }
   }
   __syncthreads();
 
