@@ -129,6 +129,67 @@ __device__ inline void wave_top_select_u32(uint32_t u0, uint32_t u1, int j, uint
   }
 }
 
+// wave_max_i32 of two independent values, step by step in turn, so that each step's result is not read by the
+// next instruction (a DPP read of a VGPR that the previous instruction wrote waits two cycles)
+__device__ inline void wave_max2_i32(int& x, int& y) {
+  x = max(x, KVQ_UPDDPP(x, 0xB1));
+  y = max(y, KVQ_UPDDPP(y, 0xB1));
+  x = max(x, KVQ_UPDDPP(x, 0x4E));
+  y = max(y, KVQ_UPDDPP(y, 0x4E));
+  x = max(x, KVQ_UPDDPP(x, 0x141));
+  y = max(y, KVQ_UPDDPP(y, 0x141));
+  x = max(x, KVQ_UPDDPP(x, 0x140));
+  y = max(y, KVQ_UPDDPP(y, 0x140));
+  const auto x16 = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  const auto y16 = __builtin_amdgcn_permlane16_swap((uint32_t)y, (uint32_t)y, false, false);
+  x = max((int)x16[0], (int)x16[1]);
+  y = max((int)y16[0], (int)y16[1]);
+  const auto x32 = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  const auto y32 = __builtin_amdgcn_permlane32_swap((uint32_t)y, (uint32_t)y, false, false);
+  x = max((int)x32[0], (int)x32[1]);
+  y = max((int)y32[0], (int)y32[1]);
+}
+
+// Minimum and maximum over the wave of two tokens' values (mna, mxa; mnb, mxb), the four reductions step by step
+// in turn: DPP within rows, then the row and half swaps
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ void minmax4_step(float& mna, float& mxa, float& mnb, float& mxb) {
+  mna = fminf(mna, dpp_mov_f32<CTRL>(mna));
+  mxa = fmaxf(mxa, dpp_mov_f32<CTRL>(mxa));
+  mnb = fminf(mnb, dpp_mov_f32<CTRL>(mnb));
+  mxb = fmaxf(mxb, dpp_mov_f32<CTRL>(mxb));
+}
+__device__ inline void wave_minmax2_f32(float& mna, float& mxa, float& mnb, float& mxb) {
+  minmax4_step<0xB1>(mna, mxa, mnb, mxb);   // quad_perm [1,0,3,2]
+  minmax4_step<0x4E>(mna, mxa, mnb, mxb);   // quad_perm [2,3,0,1]
+  minmax4_step<0x141>(mna, mxa, mnb, mxb);  // row_half_mirror
+  minmax4_step<0x140>(mna, mxa, mnb, mxb);  // row_mirror
+  {
+    const auto a0 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mna), __float_as_uint(mna), false, false);
+    const auto a1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mxa), __float_as_uint(mxa), false, false);
+    const auto b0 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mnb), __float_as_uint(mnb), false, false);
+    const auto b1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mxb), __float_as_uint(mxb), false, false);
+    mna = fminf(__uint_as_float(a0[0]), __uint_as_float(a0[1]));
+    mxa = fmaxf(__uint_as_float(a1[0]), __uint_as_float(a1[1]));
+    mnb = fminf(__uint_as_float(b0[0]), __uint_as_float(b0[1]));
+    mxb = fmaxf(__uint_as_float(b1[0]), __uint_as_float(b1[1]));
+  }
+  {
+    const auto a0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mna), __float_as_uint(mna), false, false);
+    const auto a1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mxa), __float_as_uint(mxa), false, false);
+    const auto b0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mnb), __float_as_uint(mnb), false, false);
+    const auto b1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mxb), __float_as_uint(mxb), false, false);
+    mna = fminf(__uint_as_float(a0[0]), __uint_as_float(a0[1]));
+    mxa = fmaxf(__uint_as_float(a1[0]), __uint_as_float(a1[1]));
+    mnb = fminf(__uint_as_float(b0[0]), __uint_as_float(b0[1]));
+    mxb = fmaxf(__uint_as_float(b1[0]), __uint_as_float(b1[1]));
+  }
+}
+
 // wave_top_select_u32 for two tokens at once (a: a0, a1; b: b0, b1): the two tokens' rounds are independent, so
 // their wave reductions interleave; a token that is done keeps its results while the other finishes
 __device__ inline void wave_top_select2_u32(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, int j, uint32_t& ya,
@@ -140,8 +201,9 @@ __device__ inline void wave_top_select2_u32(uint32_t a0, uint32_t a1, uint32_t b
   for (;;) {
     const uint32_t ca0 = a0 < cura ? a0 : 0u, ca1 = a1 < cura ? a1 : 0u;
     const uint32_t cb0 = b0 < curb ? b0 : 0u, cb1 = b1 < curb ? b1 : 0u;
-    const uint32_t ma = (uint32_t)wave_max_i32((int)(ca0 > ca1 ? ca0 : ca1));
-    const uint32_t mb = (uint32_t)wave_max_i32((int)(cb0 > cb1 ? cb0 : cb1));
+    int ia = (int)(ca0 > ca1 ? ca0 : ca1), ib = (int)(cb0 > cb1 ? cb0 : cb1);
+    wave_max2_i32(ia, ib);
+    const uint32_t ma = (uint32_t)ia, mb = (uint32_t)ib;
     const int cnta = wave_count(a0 == ma) + wave_count(a1 == ma);
     const int cntb = wave_count(b0 == mb) + wave_count(b1 == mb);
     if (!da) {
@@ -434,22 +496,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
 
   // 4. min/max per channel over the group (or per token over its channels), bf16 scale and zero
   if (tokenwise) {
-    for (int tl = wave * 32; tl < wave * 32 + 32; ++tl) {
-      const float x0 = xr[tl * XS_STRIDE + lane], x1 = xr[tl * XS_STRIDE + lane + 64];
-      const float amin = wave_min_f32(fminf(x0, x1));
-      const float bmax = wave_max_f32(fmaxf(x0, x1));
-      const float s = (bmax > amin) ? __fdiv_rn(__fsub_rn(bmax, amin), levels) : 1.0f;
-      const uint16_t s16 = f32_to_bf16_rne(s);
-      const float sp = bf16_to_f32(s16);
-      const uint16_t z16 = f32_to_bf16_rne(__fdiv_rn(-amin, sp));
-      if (lane == 0) {
-        s_rs[tl] = rcp_of_bf16(sp);
-        s_zp[tl] = bf16_to_f32(z16);
-        // page of the token: its K (which = 0) or V (which = 1) scales[64] then zeros[64]
-        const long long phys = pool_page(g, a.page_table[(long long)b * g.max_pages + 2 * grp + (tl >> 6)]);
-        uint16_t* meta = reinterpret_cast<uint16_t*>(a.pages + phys * g.page_bytes + hoff + moff) + which * 128;
-        meta[tl & 63] = s16;
-        meta[64 + (tl & 63)] = z16;
+    // two tokens at a time: their four wave reductions interleave
+    for (int tl0 = wave * 32; tl0 < wave * 32 + 32; tl0 += 2) {
+      const float* ra = xr + tl0 * XS_STRIDE;
+      const float* rb = ra + XS_STRIDE;
+      float mna = fminf(ra[lane], ra[lane + 64]), mxa = fmaxf(ra[lane], ra[lane + 64]);
+      float mnb = fminf(rb[lane], rb[lane + 64]), mxb = fmaxf(rb[lane], rb[lane + 64]);
+      wave_minmax2_f32(mna, mxa, mnb, mxb);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int tl = tl0 + k;
+        const float amin = k ? mnb : mna, bmax = k ? mxb : mxa;
+        const float s = (bmax > amin) ? __fdiv_rn(__fsub_rn(bmax, amin), levels) : 1.0f;
+        const uint16_t s16 = f32_to_bf16_rne(s);
+        const float sp = bf16_to_f32(s16);
+        const uint16_t z16 = f32_to_bf16_rne(__fdiv_rn(-amin, sp));
+        if (lane == 0) {
+          s_rs[tl] = rcp_of_bf16(sp);
+          s_zp[tl] = bf16_to_f32(z16);
+          // page of the token: its K (which = 0) or V (which = 1) scales[64] then zeros[64]
+          const long long phys = pool_page(g, a.page_table[(long long)b * g.max_pages + 2 * grp + (tl >> 6)]);
+          uint16_t* meta = reinterpret_cast<uint16_t*>(a.pages + phys * g.page_bytes + hoff + moff) + which * 128;
+          meta[tl & 63] = s16;
+          meta[64 + (tl & 63)] = z16;
+        }
       }
     }
   } else {
