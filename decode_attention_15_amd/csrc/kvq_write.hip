@@ -654,11 +654,30 @@ __global__ __launch_bounds__(256) void band_write_kernel(WriteArgs a) {
   const int ng1 = n_groups_of(T0 + n_new, g.S0, g.W);
   if (r < n_new && (t < g.S0 || t >= g.S0 + GROUP * ng1)) {
     const long long slot = band_slot_of(t, g.S0, g.W);
-    for (int e = threadIdx.x; e < g.n_kv * 256; e += 256) {
-      const int h = e >> 8, kv = (e >> 7) & 1, c = e & (D - 1);
-      const long long idx = ((long long)(c0 + r) * g.n_kv + h) * D + c;
-      a.band[(((long long)b * g.n_kv + h) * g.slots + slot) * 256 + kv * 128 + c] =
-          src_as_bf16_bits(kv ? a.v : a.k, a.src_bf16, idx);
+    const uintptr_t amask = a.src_bf16 ? 7 : 15;
+    if ((reinterpret_cast<uintptr_t>(a.band) & 7) == 0 && ((reinterpret_cast<uintptr_t>(a.k) | reinterpret_cast<uintptr_t>(a.v)) & amask) == 0) {
+      // four channels per thread and step: 8-byte bf16 stores from 8-byte bf16 or 16-byte fp32 loads
+      for (int e4 = threadIdx.x; e4 < g.n_kv * 64; e4 += 256) {
+        const int h = e4 >> 6, kv = (e4 >> 5) & 1, c = 4 * (e4 & 31);
+        const long long idx = ((long long)(c0 + r) * g.n_kv + h) * D + c;
+        const void* src = kv ? a.v : a.k;
+        uint2 w;
+        if (a.src_bf16) {
+          w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(src) + idx);
+        } else {
+          const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + idx);
+          w = make_uint2((uint32_t)f32_to_bf16_rne(f.x) | ((uint32_t)f32_to_bf16_rne(f.y) << 16),
+                         (uint32_t)f32_to_bf16_rne(f.z) | ((uint32_t)f32_to_bf16_rne(f.w) << 16));
+        }
+        *reinterpret_cast<uint2*>(a.band + (((long long)b * g.n_kv + h) * g.slots + slot) * 256 + kv * 128 + c) = w;
+      }
+    } else {
+      for (int e = threadIdx.x; e < g.n_kv * 256; e += 256) {
+        const int h = e >> 8, kv = (e >> 7) & 1, c = e & (D - 1);
+        const long long idx = ((long long)(c0 + r) * g.n_kv + h) * D + c;
+        a.band[(((long long)b * g.n_kv + h) * g.slots + slot) * 256 + kv * 128 + c] =
+            src_as_bf16_bits(kv ? a.v : a.k, a.src_bf16, idx);
+      }
     }
   }
   if constexpr (ADVANCE) {
