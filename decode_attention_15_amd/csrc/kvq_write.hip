@@ -496,7 +496,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
 
   // 4. min/max per channel over the group (or per token over its channels), bf16 scale and zero
   if (tokenwise) {
-    // two tokens at a time: their four wave reductions interleave
+    // two tokens at a time: their four wave reductions interleave.  A wave's 32 tokens lie in one page of the
+    // group, whose metadata block is looked up once
+    uint16_t* const meta_w =
+        reinterpret_cast<uint16_t*>(a.pages + pool_page(g, a.page_table[(long long)b * g.max_pages + 2 * grp + (wave >> 1)]) * g.page_bytes +
+                                    hoff + moff) + which * 128;
     for (int tl0 = wave * 32; tl0 < wave * 32 + 32; tl0 += 2) {
       const float* ra = xr + tl0 * XS_STRIDE;
       const float* rb = ra + XS_STRIDE;
@@ -514,11 +518,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
         if (lane == 0) {
           s_rs[tl] = rcp_of_bf16(sp);
           s_zp[tl] = bf16_to_f32(z16);
-          // page of the token: its K (which = 0) or V (which = 1) scales[64] then zeros[64]
-          const long long phys = pool_page(g, a.page_table[(long long)b * g.max_pages + 2 * grp + (tl >> 6)]);
-          uint16_t* meta = reinterpret_cast<uint16_t*>(a.pages + phys * g.page_bytes + hoff + moff) + which * 128;
-          meta[tl & 63] = s16;
-          meta[64 + (tl & 63)] = z16;
+          // the token's page: its K (which = 0) or V (which = 1) scales[64] then zeros[64]
+          meta_w[tl & 63] = s16;
+          meta_w[64 + (tl & 63)] = z16;
         }
       }
     }
