@@ -372,7 +372,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this path runs on one GPU; multi-GPU runs are not part of this build",
+        print(json.dumps({"error": "this decode path runs on one GPU; runs on several GPUs are not implemented",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import numpy as np
