@@ -1298,8 +1298,9 @@ __device__ void int2_unit_mfma(Lds& L, const DecodeArgs& a, int b, int h, int T,
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int ch = c + 16 * t;
-        const uint16_t* vsz = M1 ? reinterpret_cast<const uint16_t*>(W.vsz) - 2 * D : ms;
-        const float sv = bf16_to_f32(vsz[2 * D + ch]), zv = bf16_to_f32(vsz[3 * D + ch]);
+        // the value scales and zeros: the side buffer's two runs (one metadata buffer) or the metadata's second half
+        const uint16_t* vsz = M1 ? reinterpret_cast<const uint16_t*>(W.vsz) : ms + 2 * D;
+        const float sv = bf16_to_f32(vsz[ch]), zv = bf16_to_f32(vsz[D + ch]);
         const float Y = fmaf(-zv, Pf, (float)limbs3_sum<GQ>(acc[t], accx[t], e));
         o[e][t] = fmaf(eg * sv, Y, o[e][t] * sc);
       }
