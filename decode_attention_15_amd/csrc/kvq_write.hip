@@ -343,18 +343,38 @@ __device__ inline void rotate_group_mfma(float* xs, const float* rot, int wave, 
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) acc[rt][ct] = d4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 2
-  for (int s = 0; s < D / 4; ++s) {
+  // R is read from L2, one load per column tile, two steps ahead in two alternating sets (no copies between
+  // them): a step converts its set, reloads it for two steps later and multiplies
+  float bA[8], bB[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    bA[ct] = rot[lk * D + 16 * ct + li];
+    bB[ct] = rot[(4 + lk) * D + 16 * ct + li];
+    // opaque starting values: otherwise the compiler merges these loads with the loop's and issues every
+    // load right before its use
+    asm volatile("" : "+v"(bA[ct]), "+v"(bB[ct]));
+  }
+  auto step = [&](int s, float (&bs)[8]) {
     const int kk = 4 * s + lk;
-    double av[2], bv[8];
+    double bv[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) bv[ct] = (double)bs[ct];
+    // the last two steps reload row D - 1 (in bounds, never used): no branch around the loads
+    const int kn = min(kk + 8, D - 1);
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) bs[ct] = rot[kn * D + 16 * ct + li];
+    double av[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) av[rt] = (double)xs[(t0 + 16 * rt + li) * XS_STRIDE + kk];
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) bv[ct] = (double)rot[kk * D + 16 * ct + li];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) acc[rt][ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[rt], bv[ct], acc[rt][ct], 0, 0, 0);
+  };
+#pragma unroll 1
+  for (int s = 0; s < D / 4; s += 2) {
+    step(s, bA);
+    step(s + 1, bB);
   }
   // every read of these rows was consumed by the matrix cores above (a wave's LDS accesses stay in order)
 #pragma unroll
