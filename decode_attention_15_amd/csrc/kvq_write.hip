@@ -521,28 +521,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
     uint16_t* const meta_w =
         reinterpret_cast<uint16_t*>(a.pages + pool_page(g, a.page_table[(long long)b * g.max_pages + 2 * grp + (wave >> 1)]) * g.page_bytes +
                                     hoff + moff) + which * 128;
+    // lane t < 32 collects token wave * 32 + t's minimum and maximum; the scale arithmetic then runs once,
+    // one token per lane
+    float t_mn = 0.0f, t_mx = 0.0f;
     for (int tl0 = wave * 32; tl0 < wave * 32 + 32; tl0 += 2) {
       const float* ra = xr + tl0 * XS_STRIDE;
       const float* rb = ra + XS_STRIDE;
       float mna = fminf(ra[lane], ra[lane + 64]), mxa = fmaxf(ra[lane], ra[lane + 64]);
       float mnb = fminf(rb[lane], rb[lane + 64]), mxb = fmaxf(rb[lane], rb[lane + 64]);
       wave_minmax2_f32(mna, mxa, mnb, mxb);
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int tl = tl0 + k;
-        const float amin = k ? mnb : mna, bmax = k ? mxb : mxa;
-        const float s = (bmax > amin) ? __fdiv_rn(__fsub_rn(bmax, amin), levels) : 1.0f;
-        const uint16_t s16 = f32_to_bf16_rne(s);
-        const float sp = bf16_to_f32(s16);
-        const uint16_t z16 = f32_to_bf16_rne(__fdiv_rn(-amin, sp));
-        if (lane == 0) {
-          s_rs[tl] = rcp_of_bf16(sp);
-          s_zp[tl] = bf16_to_f32(z16);
-          // the token's page: its K (which = 0) or V (which = 1) scales[64] then zeros[64]
-          meta_w[tl & 63] = s16;
-          meta_w[64 + (tl & 63)] = z16;
-        }
+      const int t = tl0 - wave * 32;
+      if (lane == t) {
+        t_mn = mna;
+        t_mx = mxa;
       }
+      if (lane == t + 1) {
+        t_mn = mnb;
+        t_mx = mxb;
+      }
+    }
+    if (lane < 32) {
+      const int tl = wave * 32 + lane;
+      const float s = (t_mx > t_mn) ? __fdiv_rn(__fsub_rn(t_mx, t_mn), levels) : 1.0f;
+      const uint16_t s16 = f32_to_bf16_rne(s);
+      const float sp = bf16_to_f32(s16);
+      const uint16_t z16 = f32_to_bf16_rne(__fdiv_rn(-t_mn, sp));
+      s_rs[tl] = rcp_of_bf16(sp);
+      s_zp[tl] = bf16_to_f32(z16);
+      // the token's page: its K (which = 0) or V (which = 1) scales[64] then zeros[64]
+      meta_w[tl & 63] = s16;
+      meta_w[64 + (tl & 63)] = z16;
     }
   } else {
     const int c = tid & (D - 1), half = tid >> 7;
