@@ -150,46 +150,6 @@ __device__ inline void wave_max2_i32(int& x, int& y) {
   y = max((int)y32[0], (int)y32[1]);
 }
 
-// Minimum and maximum over the wave of two tokens' values (mna, mxa; mnb, mxb), the four reductions step by step
-// in turn: DPP within rows, then the row and half swaps
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-template <int CTRL>
-__device__ __forceinline__ void minmax4_step(float& mna, float& mxa, float& mnb, float& mxb) {
-  mna = fminf(mna, dpp_mov_f32<CTRL>(mna));
-  mxa = fmaxf(mxa, dpp_mov_f32<CTRL>(mxa));
-  mnb = fminf(mnb, dpp_mov_f32<CTRL>(mnb));
-  mxb = fmaxf(mxb, dpp_mov_f32<CTRL>(mxb));
-}
-__device__ inline void wave_minmax2_f32(float& mna, float& mxa, float& mnb, float& mxb) {
-  minmax4_step<0xB1>(mna, mxa, mnb, mxb);   // quad_perm [1,0,3,2]
-  minmax4_step<0x4E>(mna, mxa, mnb, mxb);   // quad_perm [2,3,0,1]
-  minmax4_step<0x141>(mna, mxa, mnb, mxb);  // row_half_mirror
-  minmax4_step<0x140>(mna, mxa, mnb, mxb);  // row_mirror
-  {
-    const auto a0 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mna), __float_as_uint(mna), false, false);
-    const auto a1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mxa), __float_as_uint(mxa), false, false);
-    const auto b0 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mnb), __float_as_uint(mnb), false, false);
-    const auto b1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mxb), __float_as_uint(mxb), false, false);
-    mna = fminf(__uint_as_float(a0[0]), __uint_as_float(a0[1]));
-    mxa = fmaxf(__uint_as_float(a1[0]), __uint_as_float(a1[1]));
-    mnb = fminf(__uint_as_float(b0[0]), __uint_as_float(b0[1]));
-    mxb = fmaxf(__uint_as_float(b1[0]), __uint_as_float(b1[1]));
-  }
-  {
-    const auto a0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mna), __float_as_uint(mna), false, false);
-    const auto a1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mxa), __float_as_uint(mxa), false, false);
-    const auto b0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mnb), __float_as_uint(mnb), false, false);
-    const auto b1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mxb), __float_as_uint(mxb), false, false);
-    mna = fminf(__uint_as_float(a0[0]), __uint_as_float(a0[1]));
-    mxa = fmaxf(__uint_as_float(a1[0]), __uint_as_float(a1[1]));
-    mnb = fminf(__uint_as_float(b0[0]), __uint_as_float(b0[1]));
-    mxb = fmaxf(__uint_as_float(b1[0]), __uint_as_float(b1[1]));
-  }
-}
-
 // wave_top_select_u32 for two tokens at once (a: a0, a1; b: b0, b1): the two tokens' rounds are independent, so
 // their wave reductions interleave; a token that is done keeps its results while the other finishes
 __device__ inline void wave_top_select2_u32(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, int j, uint32_t& ya,
@@ -394,6 +354,8 @@ __device__ inline void rotate_group_mfma(float* xs, const float* rot, int wave, 
 // ---------------------------------------------------------------------------------------------
 constexpr int kGroupLds = GROUP * XS_STRIDE * (int)sizeof(float);  // two work-groups per CU
 
+// TOK: per-token INT2 (its own instance, so that its per-token steps leave the per-channel schemes' code as it is)
+template <bool TOK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void int2_group_kernel(WriteArgs a) {
   extern __shared__ float lds[];
   float* xs = lds;  // [128 tokens][XS_STRIDE] inputs (bf16 values), rotated and clipped in place
@@ -477,7 +439,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
   __syncthreads();
 
   // 2. rotation (none for V under key-only rotation: the bf16 values themselves)
-  const bool tokenwise = g.scheme == KVQ_INT2_TOKEN;
+  constexpr bool tokenwise = TOK;
   const bool four = g.scheme == KVQ_INT4_CHANNEL;
   const float levels = four ? 15.0f : 3.0f;
   const long long hoff = (long long)h * g.head_bytes;
@@ -515,30 +477,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
   __syncthreads();
 
   // 4. min/max per channel over the group (or per token over its channels), bf16 scale and zero
-  if (tokenwise) {
-    // two tokens at a time: their four wave reductions interleave.  A wave's 32 tokens lie in one page of the
-    // group, whose metadata block is looked up once
+  if constexpr (tokenwise) {
+    // each wave takes 32 tokens, which lie in one page of the group, whose metadata block is looked up once
     uint16_t* const meta_w =
         reinterpret_cast<uint16_t*>(a.pages + pool_page(g, a.page_table[(long long)b * g.max_pages + 2 * grp + (wave >> 1)]) * g.page_bytes +
                                     hoff + moff) + which * 128;
-    // lane t < 32 collects token wave * 32 + t's minimum and maximum; the scale arithmetic then runs once,
-    // one token per lane
-    float t_mn = 0.0f, t_mx = 0.0f;
-    for (int tl0 = wave * 32; tl0 < wave * 32 + 32; tl0 += 2) {
-      const float* ra = xr + tl0 * XS_STRIDE;
-      const float* rb = ra + XS_STRIDE;
-      float mna = fminf(ra[lane], ra[lane + 64]), mxa = fmaxf(ra[lane], ra[lane + 64]);
-      float mnb = fminf(rb[lane], rb[lane + 64]), mxb = fmaxf(rb[lane], rb[lane + 64]);
-      wave_minmax2_f32(mna, mxa, mnb, mxb);
-      const int t = tl0 - wave * 32;
-      if (lane == t) {
-        t_mn = mna;
-        t_mx = mxa;
+    // lanes t and t + 32 take token wave * 32 + t, 64 channels each, read from its row: half 0 channels 0-63,
+    // half 1 channels 96-127 then 64-95 (on 64 banks the two halves' reads then fall on disjoint banks); one
+    // swap across the two halves completes the token's minimum and maximum
+    float t_mn, t_mx;
+    {
+      const int hf = lane >> 5;
+      const float* row = xr + (wave * 32 + (lane & 31)) * XS_STRIDE;
+      const float* r0 = row + 96 * hf;
+      const float* r1 = row + 32 + 32 * hf;
+      float mn0 = r0[0], mx0 = r0[0], mn1 = r1[0], mx1 = r1[0];
+#pragma unroll
+      for (int k = 1; k < 32; ++k) {
+        mn0 = fminf(mn0, r0[k]);
+        mx0 = fmaxf(mx0, r0[k]);
+        mn1 = fminf(mn1, r1[k]);
+        mx1 = fmaxf(mx1, r1[k]);
       }
-      if (lane == t + 1) {
-        t_mn = mnb;
-        t_mx = mxb;
-      }
+      const float mn = fminf(mn0, mn1), mx = fmaxf(mx0, mx1);
+      const auto pm = __builtin_amdgcn_permlane32_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+      const auto px = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      t_mn = fminf(__uint_as_float(pm[0]), __uint_as_float(pm[1]));
+      t_mx = fmaxf(__uint_as_float(px[0]), __uint_as_float(px[1]));
     }
     if (lane < 32) {
       const int tl = wave * 32 + lane;
@@ -1053,15 +1018,18 @@ __global__ void debug_unpack_kernel(WriteArgs a, int seq, int kv_head, int n_tok
 hipError_t launch_write_int2(const WriteArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)int2_group_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       kGroupLds);
-    if (e != hipSuccess) return e;
+    for (const void* f : {(const void*)int2_group_kernel<false>, (const void*)int2_group_kernel<true>}) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kGroupLds);
+      if (e != hipSuccess) return e;
+    }
     attr_set = true;
   }
   // n new tokens complete at most n / 128 + 1 groups of a sequence
   const int max_groups = a.max_new / GROUP + 1;
   if (a.max_new == 0) return hipSuccess;  // nothing appended: the lengths stay
-  hipLaunchKernelGGL(int2_group_kernel, dim3(max_groups, a.g.n_kv * 2, a.g.batch), dim3(256), kGroupLds, s, a);
+  const dim3 grid(max_groups, a.g.n_kv * 2, a.g.batch);
+  if (a.g.scheme == KVQ_INT2_TOKEN) hipLaunchKernelGGL(int2_group_kernel<true>, grid, dim3(256), kGroupLds, s, a);
+  else hipLaunchKernelGGL(int2_group_kernel<false>, grid, dim3(256), kGroupLds, s, a);
   if (a.max_new == 1) {
     // the decode step's append: the band write advances the lengths itself
     hipLaunchKernelGGL(band_write_kernel<true>, dim3(1, a.g.batch), dim3(256), 0, s, a);
